@@ -1,0 +1,137 @@
+/*
+ * ss_scan.h -- C ABI of the MI355X (gfx950) selective-scan library
+ * (libss_scan.so).
+ *
+ * The library computes the Mamba selective scan with a softplus step size and
+ * its single-token state-update (decode) step, entirely in HIP kernels.  The
+ * operation is the one defined by
+ *   - mhpn.cn, "PyTorch新手也能懂：手把手拆解Mamba-minimal中的selective_scan实现":
+ *     section 2 (argument shapes), sections 3, 3.1, 3.2 (exp(delta*A) for A,
+ *     delta*B*u for B), section 4 (sequential recurrence from a zero state,
+ *     readout with C after each update), section 5 (y += u*D), section 7
+ *     (A = -exp(A_log), softplus keeps delta positive);
+ *   - jiafeimiao.top, "代码连连看——mamba", the Mamba.step listing and the
+ *     selective_state_update call that follows it (bias added to dt inside the
+ *     softplus, in-place state update, gate y * silu(z) after the D skip).
+ *
+ * For every batch b, channel d and time t (h starts at zero):
+ *     delta' = softplus(delta[b,t,d] + bias[d])      (or delta + bias without softplus)
+ *     h[k]   = exp(delta' * A[d,k]) * h[k] + delta' * B[b,t,k] * u[b,t,d],  A = -exp(A_log)
+ *     y      = sum_k C[b,t,k] * h[k] + D[d] * u[b,t,d]
+ *     y      = y * z / (1 + exp(-z))                  (only when z is given)
+ *
+ * Conventions shared by every entry point:
+ *   - Every pointer is DEVICE memory owned by the caller.  Tensors are dense,
+ *     contiguous and row-major (last index fastest) with the shapes stated.
+ *   - u, delta, B, C, z and y (x, dt of the step) share one element type,
+ *     `dtype` (SS_F32 or SS_BF16).  A_log, D, the bias and the state are
+ *     always fp32.  bf16 results are rounded to nearest even.
+ *   - Nothing is allocated, no pointer is kept after return, and there is no
+ *     hidden global state apart from a per-device cache of attributes, so
+ *     calls from several host threads are safe.  Calls that share a
+ *     workspace must not overlap.
+ *   - Work is enqueued on `stream` (a hipStream_t; NULL = the default
+ *     stream) and runs asynchronously; results are valid once the stream
+ *     has been synchronised.  The library never synchronises.
+ *   - Arguments are validated before anything is enqueued; on any error
+ *     nothing is launched and nothing is written.
+ *   - Outputs must not overlap any input (SS_ERR_ALIAS); the state of the
+ *     step is the one in/out buffer and is updated in place.
+ *   - Pointers must be aligned to their element size (SS_ERR_ALIGN).
+ */
+#ifndef SS_SCAN_H
+#define SS_SCAN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Element type of u, delta, B, C, z, y (and x, dt of the step). */
+typedef enum {
+    SS_F32 = 0,
+    SS_BF16 = 1
+} ss_dtype;
+
+/* Return codes. */
+typedef enum {
+    SS_OK = 0,
+    SS_ERR_NULL = -1,        /* a required pointer is NULL                          */
+    SS_ERR_SHAPE = -2,       /* a size is <= 0 or too large to index                */
+    SS_ERR_DTYPE = -3,       /* dtype is not an ss_dtype value                      */
+    SS_ERR_UNSUPPORTED = -4, /* n (the state size) is above SS_MAX_STATE            */
+    SS_ERR_WORKSPACE = -5,   /* workspace missing or smaller than the query says    */
+    SS_ERR_HIP = -6,         /* the HIP runtime refused the launch                  */
+    SS_ERR_ALIAS = -7,       /* an output overlaps an input                         */
+    SS_ERR_ALIGN = -8        /* a pointer is not aligned to its element size        */
+} ss_status;
+
+/* Largest state size n the kernels are built for. */
+#define SS_MAX_STATE 64
+
+/*
+ * Bytes of device workspace ss_scan_fwd needs for these sizes (0 when none).
+ * The value depends only on the arguments, not on the device.  Returns 0 for
+ * invalid arguments as well; ss_scan_fwd reports those.
+ */
+size_t ss_scan_fwd_workspace_bytes(int64_t b, int64_t L, int64_t d_in, int64_t n, int dtype);
+
+/*
+ * Selective scan, forward (mhpn.cn page, sections 2-5; jiafeimiao.top page,
+ * the softplus(dt + dt_bias) of Mamba.step).
+ *
+ *   u, delta   : (b, L, d_in)  dtype
+ *   A_log      : (d_in, n)     fp32; the kernels use A = -exp(A_log).
+ *                A caller holding A (all entries < 0) passes log(-A).
+ *   B, C       : (b, L, n)     dtype; shared by all d_in channels
+ *   D          : (d_in)        fp32, required (pass zeros for no skip)
+ *   z          : (b, L, d_in)  dtype, or NULL for no gate
+ *   delta_bias : (d_in)        fp32, or NULL for no bias
+ *   delta_softplus : nonzero -> delta' = softplus(delta + bias); zero -> delta + bias
+ *   y          : (b, L, d_in)  dtype, output
+ *   last_state : (b, d_in, n)  fp32, output h after the last step, or NULL
+ *   workspace  : device memory of at least ss_scan_fwd_workspace_bytes()
+ *                bytes (may be NULL when that is 0).  Its contents need no
+ *                initialisation and are scratch after the call.
+ * Any n in 1..SS_MAX_STATE and any b, L, d_in >= 1 are accepted (no tile
+ * multiples are required).  Returns an ss_status.
+ */
+int ss_scan_fwd(const void *u, const void *delta, const float *A_log,
+                const void *B, const void *C, const float *D,
+                const void *z, const float *delta_bias, int delta_softplus,
+                void *y, float *last_state,
+                int64_t b, int64_t L, int64_t d_in, int64_t n, int dtype,
+                void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * One decode step on a persistent state (jiafeimiao.top page: Mamba.step and
+ * its selective_state_update(ssm_state, x, dt, A, B, C, D, z, dt_bias,
+ * dt_softplus) call; the state is updated in place).
+ *
+ *   state   : (b, d_in, n) fp32, read and overwritten with the new state
+ *   x, dt   : (b, d_in)    dtype (dt is the value before bias and softplus)
+ *   A_log   : (d_in, n)    fp32
+ *   B, C    : (b, n)       dtype
+ *   D       : (d_in)       fp32, required
+ *   z       : (b, d_in)    dtype, or NULL for no gate
+ *   dt_bias : (d_in)       fp32, or NULL
+ *   dt_softplus : as delta_softplus above
+ *   y       : (b, d_in)    dtype, output
+ * Returns an ss_status.
+ */
+int ss_state_update(float *state, const void *x, const void *dt,
+                    const float *A_log, const void *B, const void *C,
+                    const float *D, const void *z, const float *dt_bias,
+                    int dt_softplus, void *y,
+                    int64_t b, int64_t d_in, int64_t n, int dtype, void *stream);
+
+/* Static, NUL-terminated description of a status code. */
+const char *ss_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SS_SCAN_H */

@@ -1,0 +1,141 @@
+"""Double-precision CPU oracle of the selective scan and its state-update step.
+
+TEST INFRASTRUCTURE ONLY: imported by ``tests/``, by ``__graft_entry__.smoke()``
+and by the CPU-baseline leg of ``bench.py``; never by the library itself.
+
+The arithmetic lives in ``ss_oracle.c`` (plain C, double, sequential loops in
+the order the pages define them: the mamba-minimal ``selective_scan`` walk-through
+on the mhpn.cn page, sections 2-5 and 7, and ``Mamba.step`` on the
+jiafeimiao.top page).  This module only widens inputs to float64 and calls it
+through ctypes.  Parity of every function here is pinned by
+``tests/test_oracle_pins.py`` (brute force, closed forms, limits, invariants).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+SOURCE = os.path.join(_HERE, "ss_oracle.c")
+LIBRARY = os.path.join(_HERE, "libss_oracle.so")
+CFLAGS = ["-O2", "-std=c99", "-fPIC", "-shared", "-fno-fast-math"]
+
+_lib = None
+
+
+def build(source: str = SOURCE, output: str = LIBRARY) -> str:
+    """Compile the oracle with gcc (no HIP, no fast-math).  Returns the path."""
+    cmd = ["gcc", *CFLAGS, "-o", output, source, "-lm"]
+    subprocess.run(cmd, check=True)
+    return output
+
+
+def load(path: str | None = None) -> ctypes.CDLL:
+    """Load the compiled oracle (building it first if it was never built)."""
+    global _lib
+    if path is not None:
+        return _bind(ctypes.CDLL(path))
+    if _lib is None:
+        if not os.path.exists(LIBRARY):
+            build()
+        _lib = _bind(ctypes.CDLL(LIBRARY))
+    return _lib
+
+
+def _bind(lib: ctypes.CDLL) -> ctypes.CDLL:
+    P = ctypes.c_void_p
+    I64 = ctypes.c_int64
+    lib.ss_oracle_softplus.restype = ctypes.c_double
+    lib.ss_oracle_softplus.argtypes = [ctypes.c_double]
+    lib.ss_oracle_silu.restype = ctypes.c_double
+    lib.ss_oracle_silu.argtypes = [ctypes.c_double]
+    lib.ss_oracle_scan.restype = ctypes.c_int
+    lib.ss_oracle_scan.argtypes = [P] * 8 + [ctypes.c_int, P, P, I64, I64, I64, I64]
+    lib.ss_oracle_state_update.restype = ctypes.c_int
+    lib.ss_oracle_state_update.argtypes = [P] * 9 + [ctypes.c_int, P, I64, I64, I64]
+    return lib
+
+
+def _f64(a):
+    """Exact widening of a numpy array or torch tensor (fp32/bf16/fp16/f64) to float64."""
+    if a is None:
+        return None
+    if hasattr(a, "detach"):  # torch tensor (bf16 has no numpy dtype)
+        import torch
+
+        a = a.detach().to("cpu", torch.float64).numpy()
+    return np.ascontiguousarray(np.asarray(a, dtype=np.float64))
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def softplus(x: float, lib=None) -> float:
+    return (lib or load()).ss_oracle_softplus(float(x))
+
+
+def silu(x: float, lib=None) -> float:
+    return (lib or load()).ss_oracle_silu(float(x))
+
+
+def scan(u, delta, A_log, B, C, D, z=None, delta_bias=None, delta_softplus=True, lib=None):
+    """y (b, L, d_in) and last_state (b, d_in, n), both float64.
+
+    u, delta, z: (b, L, d_in); A_log: (d_in, n); B, C: (b, L, n); D, delta_bias: (d_in).
+    """
+    lib = lib or load()
+    u, delta, A_log, B, C, D = map(_f64, (u, delta, A_log, B, C, D))
+    z, delta_bias = _f64(z), _f64(delta_bias)
+    b, L, d_in = u.shape
+    n = A_log.shape[1]
+    assert delta.shape == u.shape and A_log.shape == (d_in, n)
+    assert B.shape == (b, L, n) and C.shape == (b, L, n) and D.shape == (d_in,)
+    assert z is None or z.shape == u.shape
+    assert delta_bias is None or delta_bias.shape == (d_in,)
+    y = np.empty((b, L, d_in), np.float64)
+    last = np.empty((b, d_in, n), np.float64)
+    rc = lib.ss_oracle_scan(_ptr(u), _ptr(delta), _ptr(A_log), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
+                            _ptr(delta_bias), int(bool(delta_softplus)), _ptr(y), _ptr(last),
+                            b, L, d_in, n)
+    if rc != 0:
+        raise ValueError(f"ss_oracle_scan returned {rc}")
+    return y, last
+
+
+def state_update(state, x, dt, A_log, B, C, D, z=None, dt_bias=None, dt_softplus=True, lib=None):
+    """One decode step on a copy of ``state``: returns (new_state (b, d_in, n), y (b, d_in))."""
+    lib = lib or load()
+    st = _f64(state).copy()
+    x, dt, A_log, B, C, D = map(_f64, (x, dt, A_log, B, C, D))
+    z, dt_bias = _f64(z), _f64(dt_bias)
+    b, d_in, n = st.shape
+    assert x.shape == (b, d_in) and dt.shape == (b, d_in) and A_log.shape == (d_in, n)
+    assert B.shape == (b, n) and C.shape == (b, n) and D.shape == (d_in,)
+    y = np.empty((b, d_in), np.float64)
+    rc = lib.ss_oracle_state_update(_ptr(st), _ptr(x), _ptr(dt), _ptr(A_log), _ptr(B), _ptr(C), _ptr(D),
+                                    _ptr(z), _ptr(dt_bias), int(bool(dt_softplus)), _ptr(y), b, d_in, n)
+    if rc != 0:
+        raise ValueError(f"ss_oracle_state_update returned {rc}")
+    return st, y
+
+
+def scan_channels(inputs: dict, channels, delta_softplus=True, lib=None):
+    """Oracle outputs for selected (batch, channel) pairs of a full-size scan.
+
+    Each pair is an independent recurrence, so its slice of the inputs is run
+    as a scan with b = 1, d_in = 1.  Returns {(bi, d): (y (L,), last_state (n,))}.
+    """
+    out = {}
+    for bi, d in channels:
+        sl = lambda t: None if t is None else t[bi:bi + 1, :, d:d + 1]  # noqa: E731
+        z = inputs.get("z")
+        bias = inputs.get("delta_bias")
+        y, last = scan(sl(inputs["u"]), sl(inputs["delta"]), inputs["A_log"][d:d + 1], inputs["B"][bi:bi + 1],
+                       inputs["C"][bi:bi + 1], inputs["D"][d:d + 1], sl(z) if z is not None else None,
+                       None if bias is None else bias[d:d + 1], delta_softplus, lib=lib)
+        out[(bi, d)] = (y[0, :, 0], last[0, 0])
+    return out

@@ -1,0 +1,141 @@
+/*
+ * ss_oracle.c -- plain, slow, double-precision CPU reference of the Mamba
+ * selective scan with a softplus step size, and of its single-token
+ * state-update step.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing on the product path may link, load or
+ * call this file: it is used by the tests, by the smoke check and by the
+ * CPU-baseline leg of the benchmark.  It shares no code, header, table or
+ * constant with the HIP library and includes no HIP header.
+ *
+ * What it computes follows the pages:
+ *   - mhpn.cn "PyTorch新手也能懂：手把手拆解Mamba-minimal中的selective_scan实现",
+ *     section 2 (argument shapes), section 3 with 3.1/3.2 (discretisation:
+ *     ZOH exp(delta*A) for A, forward Euler delta*B*u for B), section 4 (the
+ *     sequential loop: zero initial state, update then read out with C),
+ *     section 5 (the D skip), section 7 (A = -exp(A_log), softplus keeps
+ *     delta positive);
+ *   - jiafeimiao.top "代码连连看——mamba", the Mamba.step listing (dt bias
+ *     added before the softplus, A = -exp(A_log), the in-place state update,
+ *     readout with C, D skip, then the gate y * silu(z)).
+ * Every loop is written in the order of that definition; there is no
+ * blocking, fusion or reordering.  All arithmetic is in double; the caller
+ * widens its fp32 / bf16 inputs exactly.
+ *
+ * Layouts (row-major, last index fastest):
+ *   u, delta, z, y : (b, L, d_in)      B, C : (b, L, n)
+ *   A_log          : (d_in, n)         D, delta_bias : (d_in)
+ *   state          : (b, d_in, n)      x, dt, z, y of the step : (b, d_in)
+ *   B, C of the step : (b, n)
+ * Return value: 0 on success, -1 on a NULL required pointer, -2 on a
+ * non-positive size.
+ */
+#include <math.h>
+#include <stddef.h>
+#include <stdint.h>
+
+/* softplus(x) = log(1 + e^x), evaluated without overflow or cancellation:
+ * for x > 0 it is x + log(1 + e^-x).  (mhpn.cn page, section 7: softplus
+ * keeps delta positive.) */
+double ss_oracle_softplus(double x)
+{
+    if (x > 0.0)
+        return x + log1p(exp(-x));
+    return log1p(exp(x));
+}
+
+/* silu(z) = z * sigmoid(z) = z / (1 + e^-z)  (the gate act(z) of Mamba.step). */
+double ss_oracle_silu(double z)
+{
+    return z / (1.0 + exp(-z));
+}
+
+/* The step size of one (b, t, d) element: delta plus the optional bias,
+ * then the optional softplus (jiafeimiao.top page, Mamba.step: the bias is
+ * not added to dt earlier, it goes inside the softplus). */
+static double step_size(double delta, const double *bias, int64_t d, int softplus)
+{
+    double v = delta + (bias ? bias[d] : 0.0);
+    return softplus ? ss_oracle_softplus(v) : v;
+}
+
+int ss_oracle_scan(const double *u, const double *delta, const double *A_log,
+                   const double *B, const double *C, const double *D,
+                   const double *z, const double *delta_bias, int delta_softplus,
+                   double *y, double *last_state,
+                   int64_t b, int64_t L, int64_t d_in, int64_t n)
+{
+    if (!u || !delta || !A_log || !B || !C || !D || !y)
+        return -1;
+    if (b <= 0 || L <= 0 || d_in <= 0 || n <= 0)
+        return -2;
+
+    for (int64_t bi = 0; bi < b; bi++) {
+        for (int64_t d = 0; d < d_in; d++) {
+            /* h starts at zero (section 4 of the mhpn.cn page). */
+            double h[n];
+            double A[n];
+            for (int64_t k = 0; k < n; k++) {
+                h[k] = 0.0;
+                A[k] = -exp(A_log[d * n + k]);          /* A = -exp(A_log), elementwise */
+            }
+            for (int64_t t = 0; t < L; t++) {
+                int64_t e = (bi * L + t) * d_in + d;    /* (b, t, d) element */
+                int64_t r = (bi * L + t) * n;           /* row of B and C at (b, t) */
+                double dl = step_size(delta[e], delta_bias, d, delta_softplus);
+                /* state update: h = exp(delta*A) * h + delta*B*u */
+                for (int64_t k = 0; k < n; k++) {
+                    double dA = exp(dl * A[k]);
+                    double dBu = dl * B[r + k] * u[e];
+                    h[k] = dA * h[k] + dBu;
+                }
+                /* read out with C after the update, then the D skip */
+                double yt = 0.0;
+                for (int64_t k = 0; k < n; k++)
+                    yt += C[r + k] * h[k];
+                yt += D[d] * u[e];
+                /* optional gate, applied after the skip */
+                if (z)
+                    yt *= ss_oracle_silu(z[e]);
+                y[e] = yt;
+            }
+            if (last_state)
+                for (int64_t k = 0; k < n; k++)
+                    last_state[(bi * d_in + d) * n + k] = h[k];
+        }
+    }
+    return 0;
+}
+
+int ss_oracle_state_update(double *state, const double *x, const double *dt,
+                           const double *A_log, const double *B, const double *C,
+                           const double *D, const double *z, const double *dt_bias,
+                           int dt_softplus, double *y,
+                           int64_t b, int64_t d_in, int64_t n)
+{
+    if (!state || !x || !dt || !A_log || !B || !C || !D || !y)
+        return -1;
+    if (b <= 0 || d_in <= 0 || n <= 0)
+        return -2;
+
+    for (int64_t bi = 0; bi < b; bi++) {
+        for (int64_t d = 0; d < d_in; d++) {
+            int64_t e = bi * d_in + d;
+            double dl = step_size(dt[e], dt_bias, d, dt_softplus);
+            double yt = 0.0;
+            for (int64_t k = 0; k < n; k++) {
+                double A = -exp(A_log[d * n + k]);
+                double dA = exp(dl * A);
+                double dB = dl * B[bi * n + k];
+                double *h = &state[e * n + k];
+                *h = *h * dA + x[e] * dB;               /* in place */
+                yt += C[bi * n + k] * *h;
+            }
+            yt += D[d] * x[e];
+            if (z)
+                yt *= ss_oracle_silu(z[e]);
+            y[e] = yt;
+        }
+    }
+    return 0;
+}

@@ -1,0 +1,241 @@
+"""Pins of the CPU oracle to facts that do not come from the oracle itself.
+
+Every ``pin_*`` function takes a loaded oracle library (the real one or a
+deliberately broken build of it) and raises AssertionError when the oracle
+disagrees with:
+  - values worked out by hand (tests/golden/hand_worked.json);
+  - library routines in float64 (numpy.logaddexp for softplus, torch silu);
+  - the brute-force unrolled solution of the recurrence,
+        y_t = sum_n C_t,n sum_{s<=t} exp(A_n * sum_{r=s+1..t} Delta_r) Delta_s B_s,n u_s + D u_t,
+    which never runs the recurrence step by step;
+  - closed forms (the geometric sum for constant inputs at n = 1) and the
+    limits A -> 0 (a running sum) and A -> -inf (no memory);
+  - invariants: linearity in u, causality, a scan of length 1 equals one
+    step, a chain of steps equals the scan, prefill then decode equals the
+    longer scan, B = 0 leaves only the D skip.
+The definition they pin is that of the mhpn.cn selective_scan walk-through
+(sections 2-5 and 7) and of Mamba.step on the jiafeimiao.top page.
+"""
+from __future__ import annotations
+
+import json
+import math
+import os
+
+import numpy as np
+
+import oracle
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden", "hand_worked.json")
+
+
+def _rng(seed):
+    return np.random.default_rng(seed)
+
+
+def _close(a, b, rtol=1e-12, atol=1e-13, what=""):
+    a = np.asarray(a, np.float64)
+    b = np.asarray(b, np.float64)
+    assert a.shape == b.shape, f"{what}: shape {a.shape} vs {b.shape}"
+    assert np.all(np.isfinite(a)), f"{what}: non-finite values"
+    err = np.max(np.abs(a - b) / (atol + rtol * np.abs(b))) if a.size else 0.0
+    assert err <= 1.0, f"{what}: mismatch (scaled error {err:.3g})\n{a}\nvs\n{b}"
+
+
+def random_case(seed, b=2, L=9, d_in=3, n=4, gated=True, bias=True, softplus=True):
+    r = _rng(seed)
+    case = dict(
+        u=r.standard_normal((b, L, d_in)),
+        delta=r.standard_normal((b, L, d_in)) - 1.0,
+        A_log=r.uniform(-1.5, 1.5, (d_in, n)),
+        B=r.standard_normal((b, L, n)),
+        C=r.standard_normal((b, L, n)),
+        D=r.standard_normal(d_in),
+        z=r.standard_normal((b, L, d_in)) if gated else None,
+        delta_bias=r.uniform(-1.0, 0.5, d_in) if bias else None,
+        delta_softplus=softplus,
+    )
+    return case
+
+
+def brute_force(case):
+    """Unrolled closed-form solution of the recurrence (O(L^2), float64)."""
+    u, A_log, B, C, D = case["u"], case["A_log"], case["B"], case["C"], case["D"]
+    x = case["delta"] + (0.0 if case["delta_bias"] is None else case["delta_bias"])
+    Delta = np.logaddexp(0.0, x) if case["delta_softplus"] else x
+    A = -np.exp(A_log)                                   # (d_in, n)
+    b, L, d_in = u.shape
+    y = np.zeros((b, L, d_in))
+    last = np.zeros((b, d_in, A.shape[1]))
+    for bi in range(b):
+        for d in range(d_in):
+            S = np.concatenate([[0.0], np.cumsum(Delta[bi, :, d])])   # S[t+1] = sum_{r<=t} Delta_r
+            for t in range(L):
+                acc = 0.0
+                for s in range(t + 1):
+                    decay = np.exp(A[d] * (S[t + 1] - S[s + 1]))      # prod_{r=s+1..t} exp(Delta_r A)
+                    acc = acc + decay * Delta[bi, s, d] * B[bi, s] * u[bi, s, d]
+                y[bi, t, d] = np.dot(C[bi, t], acc) + D[d] * u[bi, t, d]
+                if t == L - 1:
+                    last[bi, d] = acc
+    if case["z"] is not None:
+        z = case["z"]
+        y = y * z / (1.0 + np.exp(-z))
+    return y, last
+
+
+def run(case, lib):
+    return oracle.scan(case["u"], case["delta"], case["A_log"], case["B"], case["C"], case["D"], case["z"],
+                       case["delta_bias"], case["delta_softplus"], lib=lib)
+
+
+# ----------------------------------------------------------------------------- pins
+
+def pin_softplus_silu(lib):
+    import torch
+
+    xs = np.concatenate([np.linspace(-60, 60, 241), [-745.0, -30.5, -1e-9, 0.0, 1e-9, 33.3, 700.0]])
+    for x in xs:
+        _close(oracle.softplus(x, lib), np.logaddexp(0.0, x), rtol=4e-16, atol=1e-300, what=f"softplus({x})")
+    zs = torch.linspace(-40, 40, 161, dtype=torch.float64)
+    ref = torch.nn.functional.silu(zs).numpy()
+    got = np.array([oracle.silu(float(z), lib) for z in zs])
+    _close(got, ref, rtol=4e-16, atol=1e-300, what="silu")
+
+
+def pin_hand_worked(lib):
+    g = json.load(open(GOLDEN))
+    Dl = math.log(2.0)
+    val = lambda pairs: np.array([c0 + c1 * Dl for c0, c1 in pairs])  # noqa: E731
+    s = g["scan"]
+    A_log = np.log(np.array(s["A_log_exp"]))[None, :]
+    u = np.array(s["u"])[None, :, None]
+    B = np.array(s["B"])[None]
+    C = np.array(s["C"])[None]
+    D = np.array([s["D"]])
+    for delta, bias in ((s["delta"], None), (g["scan_bias"]["delta"], np.array([g["scan_bias"]["delta_bias"]]))):
+        y, last = oracle.scan(u, np.array(delta)[None, :, None], A_log, B, C, D, None, bias, True, lib=lib)
+        _close(y[0, :, 0], val(s["y"]), what="hand-worked scan y")
+        _close(last[0, 0], val(s["last_state"]), what="hand-worked last_state")
+    st = g["step"]
+    new, y = oracle.state_update(np.array(st["state"])[None, None], np.array([[st["x"]]]), np.array([[st["dt"]]]),
+                                 np.log(np.array(st["A_log_exp"]))[None], np.array(st["B"])[None],
+                                 np.array(st["C"])[None], np.array([st["D"]]), lib=lib)
+    _close(new[0, 0], val(st["new_state"]), what="hand-worked step state")
+    _close(y[0, 0], val([st["y"]])[0], what="hand-worked step y")
+
+
+def pin_brute_force(lib):
+    for seed, kw in enumerate([dict(), dict(gated=False), dict(bias=False), dict(softplus=False, bias=False),
+                               dict(b=1, L=12, d_in=2, n=1), dict(b=2, L=5, d_in=3, n=7, bias=False)]):
+        case = random_case(100 + seed, **kw)
+        if not case["delta_softplus"]:
+            case["delta"] = np.abs(case["delta"]) + 0.05     # Delta must stay positive without softplus
+        y, last = run(case, lib)
+        yb, lb = brute_force(case)
+        _close(y, yb, rtol=1e-11, atol=1e-12, what=f"brute force y {kw}")
+        _close(last, lb, rtol=1e-11, atol=1e-12, what=f"brute force last_state {kw}")
+
+
+def pin_geometric_closed_form(lib):
+    """n = 1, constant Delta, B and u: h_t = Delta B u (1 - a^t) / (1 - a), a = exp(Delta A), t = 1..L."""
+    L = 40
+    r = _rng(7)
+    for A_exp, delta, softplus in ((3.0, 0.37, False), (0.5, -0.8, True), (1.0, 1.9, True)):
+        Delta = math.log1p(math.exp(delta)) if softplus else delta
+        Bv, uv = 0.8, -1.3
+        C = r.standard_normal((1, L, 1))
+        D = np.array([0.25])
+        y, last = oracle.scan(np.full((1, L, 1), uv), np.full((1, L, 1), delta), np.array([[math.log(A_exp)]]),
+                              np.full((1, L, 1), Bv), C, D, None, None, softplus, lib=lib)
+        a = math.exp(-A_exp * Delta)                       # A = -exp(log A_exp) = -A_exp
+        t = np.arange(1, L + 1)
+        h = Delta * Bv * uv * (1 - a ** t) / (1 - a)
+        _close(y[0, :, 0], C[0, :, 0] * h + D[0] * uv, rtol=1e-12, atol=1e-14, what="geometric y")
+        _close(last[0, 0, 0], h[-1], what="geometric last_state")
+
+
+def pin_limits(lib):
+    """A -> 0: h is the running sum of Delta B u.  A -> -inf: y = Delta u sum_n B C + D u."""
+    case = random_case(11, b=1, L=15, d_in=2, n=3, gated=False, bias=False)
+    x = case["delta"]
+    Delta = np.logaddexp(0.0, x)
+    case["A_log"] = np.full((2, 3), -40.0)                 # |A| ~ 4e-18: exp(Delta A) == 1 in double
+    y, last = run(case, lib)
+    h = np.cumsum(Delta[..., None] * case["B"][:, :, None, :] * case["u"][..., None], axis=1)  # (b, L, d, n)
+    _close(y, np.einsum("btdn,btn->btd", h, case["C"]) + case["D"] * case["u"], rtol=1e-12, atol=1e-13, what="A->0 y")
+    _close(last, h[:, -1], what="A->0 last")
+    case["A_log"] = np.full((2, 3), 10.0)                  # A = -22026: exp(Delta A) < 1e-95 for Delta >= 0.01
+    case["delta"] = np.maximum(case["delta"], -4.0)
+    Delta = np.logaddexp(0.0, case["delta"])
+    y, last = run(case, lib)
+    mem0 = Delta * case["u"] * np.einsum("btn,btn->bt", case["B"], case["C"])[..., None] + case["D"] * case["u"]
+    _close(y, mem0, rtol=1e-12, atol=1e-13, what="A->-inf y")
+
+
+def pin_skip_and_gate(lib):
+    case = random_case(12, b=2, L=6, d_in=3, n=4)
+    case["B"] = np.zeros_like(case["B"])
+    y, last = run(case, lib)
+    z = case["z"]
+    _close(y, case["D"] * case["u"] * z / (1 + np.exp(-z)), what="B=0 -> gated skip")
+    _close(last, np.zeros_like(last), what="B=0 -> zero state")
+
+
+def pin_linearity_causality(lib):
+    case = random_case(13, b=1, L=10, d_in=2, n=5, gated=False)
+    u1 = case["u"].copy()
+    u2 = _rng(14).standard_normal(u1.shape)
+    case["u"] = u1
+    y1, _ = run(case, lib)
+    case["u"] = u2
+    y2, _ = run(case, lib)
+    case["u"] = 2.5 * u1 - 0.75 * u2
+    y12, _ = run(case, lib)
+    _close(y12, 2.5 * y1 - 0.75 * y2, rtol=1e-12, atol=1e-12, what="linearity in u")
+    # Causality: changing every input at t0 onwards leaves y before t0 bit-identical.
+    case = random_case(15, b=1, L=10, d_in=2, n=5)
+    y, _ = run(case, lib)
+    t0 = 6
+    for k in ("u", "delta", "B", "C", "z"):
+        case[k] = case[k].copy()
+        case[k][:, t0:] += 1.0
+    y2, _ = run(case, lib)
+    assert np.array_equal(y[:, :t0], y2[:, :t0]), "causality"
+    assert not np.allclose(y[:, t0:], y2[:, t0:]), "later outputs must change"
+
+
+def pin_step_matches_scan(lib):
+    """L = 1 scan == one step from zero; L steps == scan; prefill + decode == longer scan."""
+    case = random_case(16, b=2, L=11, d_in=3, n=4)
+    y, last = run(case, lib)
+    b, L, d_in = case["u"].shape
+    n = case["A_log"].shape[1]
+    state = np.zeros((b, d_in, n))
+    for t in range(L):
+        state, yt = oracle.state_update(state, case["u"][:, t], case["delta"][:, t], case["A_log"], case["B"][:, t],
+                                        case["C"][:, t], case["D"], case["z"][:, t], case["delta_bias"], True, lib=lib)
+        _close(yt, y[:, t], rtol=1e-12, atol=1e-13, what=f"chain of steps y[{t}]")
+    _close(state, last, rtol=1e-12, atol=1e-13, what="chain of steps state")
+    # prefill on the first L1 steps, then decode the rest from its last_state
+    L1 = 7
+    pre = {k: (v[:, :L1] if isinstance(v, np.ndarray) and v.ndim == 3 else v) for k, v in case.items()}
+    _, st = run(pre, lib)
+    for t in range(L1, L):
+        st, yt = oracle.state_update(st, case["u"][:, t], case["delta"][:, t], case["A_log"], case["B"][:, t],
+                                     case["C"][:, t], case["D"], case["z"][:, t], case["delta_bias"], True, lib=lib)
+        _close(yt, y[:, t], rtol=1e-12, atol=1e-13, what=f"prefill->decode y[{t}]")
+
+
+def pin_bias_placement(lib):
+    """softplus(delta + bias): scanning (delta, bias) equals scanning (delta + bias, no bias)."""
+    case = random_case(17, b=1, L=8, d_in=3, n=2)
+    y1, l1 = run(case, lib)
+    c2 = dict(case, delta=case["delta"] + case["delta_bias"], delta_bias=None)
+    y2, l2 = run(c2, lib)
+    _close(y1, y2, rtol=1e-13, atol=1e-14, what="bias inside softplus")
+    _close(l1, l2, rtol=1e-13, atol=1e-14, what="bias inside softplus (state)")
+
+
+ALL_PINS = [pin_softplus_silu, pin_hand_worked, pin_brute_force, pin_geometric_closed_form, pin_limits,
+            pin_skip_and_gate, pin_linearity_causality, pin_step_matches_scan, pin_bias_placement]

@@ -1,0 +1,81 @@
+"""CPU: the oracle against its pins, and the pins against planted mistakes.
+
+The second half builds broken copies of ``oracle/ss_oracle.c`` (one planted
+mistake each: a dropped term, a wrong sign, a wrong or shifted index, a
+swapped operand, a misplaced bias or gate) and checks that every one of them
+fails at least one pin, so the pins are strong enough to catch that class
+of error in the real oracle.
+"""
+import os
+import shutil
+import subprocess
+
+import pytest
+
+import oracle
+from tests import oracle_pins
+
+pytestmark = pytest.mark.filterwarnings("ignore::RuntimeWarning")
+
+
+@pytest.mark.parametrize("pin", oracle_pins.ALL_PINS, ids=lambda p: p.__name__)
+def test_oracle_pin(pin, oracle_lib):
+    pin(oracle_lib)
+
+
+# (description, text in ss_oracle.c, replacement)
+MUTANTS = [
+    ("A sign", "A[k] = -exp(A_log[d * n + k]);", "A[k] = exp(A_log[d * n + k]);"),
+    ("A without exp", "A[k] = -exp(A_log[d * n + k]);", "A[k] = -A_log[d * n + k];"),
+    ("nonzero initial state", "h[k] = 0.0;", "h[k] = 1e-3;"),
+    ("decay without delta", "double dA = exp(dl * A[k]);", "double dA = exp(A[k]);"),
+    ("Euler decay 1 + delta*A", "double dA = exp(dl * A[k]);", "double dA = 1.0 + dl * A[k];"),
+    ("input without delta", "double dBu = dl * B[r + k] * u[e];", "double dBu = B[r + k] * u[e];"),
+    ("input uses C", "double dBu = dl * B[r + k] * u[e];", "double dBu = dl * C[r + k] * u[e];"),
+    ("dropped decay", "h[k] = dA * h[k] + dBu;", "h[k] = h[k] + dBu;"),
+    ("decayed input", "h[k] = dA * h[k] + dBu;", "h[k] = dA * (h[k] + dBu);"),
+    ("readout uses B", "yt += C[r + k] * h[k];", "yt += B[r + k] * h[k];"),
+    ("readout one state short", "for (int64_t k = 0; k < n; k++)\n                    yt += C[r + k] * h[k];",
+     "for (int64_t k = 0; k + 1 < n; k++)\n                    yt += C[r + k] * h[k];"),
+    ("B/C one step late", "int64_t r = (bi * L + t) * n;", "int64_t r = (bi * L + (t > 0 ? t - 1 : 0)) * n;"),
+    ("mirrored channel", "int64_t e = (bi * L + t) * d_in + d;", "int64_t e = (bi * L + t) * d_in + (d_in - 1 - d);"),
+    ("dropped D skip", "yt += D[d] * u[e];", "yt += 0.0 * D[d] * u[e];"),
+    ("skip uses delta", "yt += D[d] * u[e];", "yt += D[d] * delta[e];"),
+    ("gate without sigmoid", "                    yt *= ss_oracle_silu(z[e]);\n                y[e] = yt;",
+     "                    yt *= z[e];\n                y[e] = yt;"),
+    ("step gate uses x", "                yt *= ss_oracle_silu(z[e]);\n            y[e] = yt;",
+     "                yt *= ss_oracle_silu(x[e]);\n            y[e] = yt;"),
+    ("gate before skip", "yt += D[d] * u[e];\n                /* optional gate, applied after the skip */\n                if (z)\n                    yt *= ss_oracle_silu(z[e]);",
+     "if (z)\n                    yt *= ss_oracle_silu(z[e]);\n                yt += D[d] * u[e];"),
+    ("bias after softplus", "double v = delta + (bias ? bias[d] : 0.0);\n    return softplus ? ss_oracle_softplus(v) : v;",
+     "double v = softplus ? ss_oracle_softplus(delta) : delta;\n    return v + (bias ? bias[d] : 0.0);"),
+    ("softplus drops x", "return x + log1p(exp(-x));", "return log1p(exp(-x));"),
+    ("softplus is exp", "return log1p(exp(x));", "return exp(x);"),
+    ("silu sign", "return z / (1.0 + exp(-z));", "return z / (1.0 + exp(z));"),
+    ("last_state wrong slot", "last_state[(bi * d_in + d) * n + k] = h[k];", "last_state[(bi * d_in + d) * n + k] = h[n - 1 - k];"),
+    ("step without decay", "*h = *h * dA + x[e] * dB;", "*h = *h + x[e] * dB;"),
+    ("step readout before update", "*h = *h * dA + x[e] * dB;               /* in place */\n                yt += C[bi * n + k] * *h;",
+     "yt += C[bi * n + k] * *h;\n                *h = *h * dA + x[e] * dB;"),
+    ("step B index", "double dB = dl * B[bi * n + k];", "double dB = dl * B[k];"),
+    ("step dropped skip", "yt += D[d] * x[e];", "yt += 0.0 * x[e];"),
+    ("step A index", "double A = -exp(A_log[d * n + k]);", "double A = -exp(A_log[k]);"),
+]
+
+
+@pytest.mark.skipif(shutil.which("gcc") is None, reason="gcc not available")
+@pytest.mark.parametrize("desc,old,new", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_planted_mistake_is_caught(desc, old, new, tmp_path):
+    src = open(oracle.SOURCE).read()
+    assert src.count(old) == 1, f"mutation anchor not found exactly once: {old!r}"
+    mutated = tmp_path / "mutant.c"
+    mutated.write_text(src.replace(old, new))
+    so = str(tmp_path / "libmutant.so")
+    subprocess.run(["gcc", *oracle.CFLAGS, "-o", so, str(mutated), "-lm"], check=True)
+    lib = oracle.load(so)
+    failed = []
+    for pin in oracle_pins.ALL_PINS:
+        try:
+            pin(lib)
+        except (AssertionError, ValueError, FloatingPointError, OverflowError):
+            failed.append(pin.__name__)
+    assert failed, f"planted mistake '{desc}' passed every pin"
