@@ -1,0 +1,187 @@
+"""MI355X (gfx950) selective scan with a softplus step size, and its decode step.
+
+A thin ctypes binding over ``libss_scan.so`` (built from ``csrc/`` by
+``build.py``).  Every arithmetic step runs in the library's HIP kernels; this
+module only checks tensor properties, allocates outputs and workspace with
+PyTorch, and passes raw device pointers and the current HIP stream.  If the
+library is missing, importing this package raises.
+
+Entry points mirror the C ABI (``include/ss_scan.h``):
+
+  scan_fwd(u, delta, A_log, B, C, D, z=None, delta_bias=None, delta_softplus=True,
+           return_last_state=False)          -> y  or  (y, last_state)
+  state_update(state, x, dt, A_log, B, C, D, z=None, dt_bias=None, dt_softplus=True)
+                                             -> y  (state is updated in place)
+  scan_fwd_workspace_bytes(b, L, d_in, n, dtype) -> int
+  status_string(code) -> str
+
+Shapes follow the mhpn.cn selective_scan walk-through (section 2): u, delta
+(b, L, d_in); A_log (d_in, n) with A = -exp(A_log); B, C (b, L, n); D (d_in).
+The step follows jiafeimiao.top's Mamba.step / selective_state_update call:
+state (b, d_in, n) fp32 updated in place; x, dt, z (b, d_in); B, C (b, n).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIBRARY = os.path.join(_HERE, "libss_scan.so")
+
+SS_F32 = 0
+SS_BF16 = 1
+SS_MAX_STATE = 64
+STATUS = {0: "SS_OK", -1: "SS_ERR_NULL", -2: "SS_ERR_SHAPE", -3: "SS_ERR_DTYPE", -4: "SS_ERR_UNSUPPORTED",
+          -5: "SS_ERR_WORKSPACE", -6: "SS_ERR_HIP", -7: "SS_ERR_ALIAS", -8: "SS_ERR_ALIGN"}
+EXPORTS = ("ss_scan_fwd_workspace_bytes", "ss_scan_fwd", "ss_state_update", "ss_status_string")
+
+
+class SSError(RuntimeError):
+    def __init__(self, code: int, where: str):
+        self.code = code
+        super().__init__(f"{where}: {STATUS.get(code, code)} ({status_string(code)})")
+
+
+def _load() -> ctypes.CDLL:
+    if not os.path.exists(LIBRARY):
+        raise ImportError(f"{LIBRARY} is not built; run `python -m selective_state_space_softplus_amd.build` "
+                          "(or __graft_entry__.build())")
+    lib = ctypes.CDLL(LIBRARY)
+    P, I64, I = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+    lib.ss_scan_fwd_workspace_bytes.restype = ctypes.c_size_t
+    lib.ss_scan_fwd_workspace_bytes.argtypes = [I64, I64, I64, I64, I]
+    lib.ss_scan_fwd.restype = I
+    lib.ss_scan_fwd.argtypes = [P, P, P, P, P, P, P, P, I, P, P, I64, I64, I64, I64, I, P, ctypes.c_size_t, P]
+    lib.ss_state_update.restype = I
+    lib.ss_state_update.argtypes = [P, P, P, P, P, P, P, P, P, I, P, I64, I64, I64, I, P]
+    lib.ss_status_string.restype = ctypes.c_char_p
+    lib.ss_status_string.argtypes = [I]
+    return lib
+
+
+lib = _load()
+
+
+def status_string(code: int) -> str:
+    return lib.ss_status_string(int(code)).decode()
+
+
+def _dtype_code(t: torch.dtype) -> int:
+    if t == torch.float32:
+        return SS_F32
+    if t == torch.bfloat16:
+        return SS_BF16
+    raise TypeError(f"inputs must be float32 or bfloat16, got {t}")
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _check(t, name, shape, dtype, device):
+    if t is None:
+        return
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _stream(device) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def scan_fwd_workspace_bytes(b: int, L: int, d_in: int, n: int, dtype: int) -> int:
+    return int(lib.ss_scan_fwd_workspace_bytes(b, L, d_in, n, dtype))
+
+
+_workspaces: dict = {}
+
+
+def _workspace(device, nbytes: int):
+    """A cached uint8 device buffer of at least nbytes for this device (and stream)."""
+    if nbytes == 0:
+        return None
+    key = (device, torch.cuda.current_stream(device).cuda_stream)
+    ws = _workspaces.get(key)
+    if ws is None or ws.numel() < nbytes:
+        ws = torch.empty(nbytes, dtype=torch.uint8, device=device)
+        _workspaces[key] = ws
+    return ws
+
+
+def scan_fwd(u, delta, A_log, B, C, D, z=None, delta_bias=None, delta_softplus=True, return_last_state=False,
+             out=None, last_state=None, workspace=None):
+    """Selective scan forward on the GPU; returns y (and last_state if asked)."""
+    if u.dim() != 3 or A_log.dim() != 2:
+        raise ValueError("u must be (b, L, d_in) and A_log (d_in, n)")
+    b, L, d_in = u.shape
+    n = A_log.shape[1]
+    dev = u.device
+    code = _dtype_code(u.dtype)
+    _check(u, "u", (b, L, d_in), u.dtype, dev)
+    _check(delta, "delta", (b, L, d_in), u.dtype, dev)
+    _check(A_log, "A_log", (d_in, n), torch.float32, dev)
+    _check(B, "B", (b, L, n), u.dtype, dev)
+    _check(C, "C", (b, L, n), u.dtype, dev)
+    _check(D, "D", (d_in,), torch.float32, dev)
+    _check(z, "z", (b, L, d_in), u.dtype, dev)
+    _check(delta_bias, "delta_bias", (d_in,), torch.float32, dev)
+    y = torch.empty_like(u) if out is None else out
+    _check(y, "out", (b, L, d_in), u.dtype, dev)
+    if return_last_state and last_state is None:
+        last_state = torch.empty((b, d_in, n), dtype=torch.float32, device=dev)
+    _check(last_state, "last_state", (b, d_in, n), torch.float32, dev)
+    if b == 0 or L == 0 or d_in == 0:
+        # Nothing to scan: no steps leave the zero initial state.
+        if last_state is not None:
+            last_state.zero_()
+        return (y, last_state) if return_last_state else y
+    need = scan_fwd_workspace_bytes(b, L, d_in, n, code)
+    if workspace is None:
+        workspace = _workspace(dev, need)
+    ws_ptr = _ptr(workspace)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    with torch.cuda.device(dev):
+        rc = lib.ss_scan_fwd(_ptr(u), _ptr(delta), _ptr(A_log), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
+                             _ptr(delta_bias), int(bool(delta_softplus)), _ptr(y), _ptr(last_state),
+                             b, L, d_in, n, code, ws_ptr, ws_bytes, _stream(dev))
+    if rc != 0:
+        raise SSError(rc, "ss_scan_fwd")
+    return (y, last_state) if return_last_state else y
+
+
+def state_update(state, x, dt, A_log, B, C, D, z=None, dt_bias=None, dt_softplus=True, out=None):
+    """One decode step; updates ``state`` in place and returns y (b, d_in)."""
+    if state.dim() != 3:
+        raise ValueError("state must be (b, d_in, n)")
+    b, d_in, n = state.shape
+    dev = state.device
+    code = _dtype_code(x.dtype)
+    _check(state, "state", (b, d_in, n), torch.float32, dev)
+    _check(x, "x", (b, d_in), x.dtype, dev)
+    _check(dt, "dt", (b, d_in), x.dtype, dev)
+    _check(A_log, "A_log", (d_in, n), torch.float32, dev)
+    _check(B, "B", (b, n), x.dtype, dev)
+    _check(C, "C", (b, n), x.dtype, dev)
+    _check(D, "D", (d_in,), torch.float32, dev)
+    _check(z, "z", (b, d_in), x.dtype, dev)
+    _check(dt_bias, "dt_bias", (d_in,), torch.float32, dev)
+    y = torch.empty_like(x) if out is None else out
+    _check(y, "out", (b, d_in), x.dtype, dev)
+    if b == 0 or d_in == 0:
+        return y
+    with torch.cuda.device(dev):
+        rc = lib.ss_state_update(_ptr(state), _ptr(x), _ptr(dt), _ptr(A_log), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
+                                 _ptr(dt_bias), int(bool(dt_softplus)), _ptr(y), b, d_in, n, code, _stream(dev))
+    if rc != 0:
+        raise SSError(rc, "ss_state_update")
+    return y

@@ -1,0 +1,88 @@
+// ss_device.h -- device helpers shared by the selective-scan kernels (gfx950).
+//
+// Element access for the two input types (fp32 and bf16 kept as raw 16-bit
+// words), the hardware transcendental instructions, and the two pointwise
+// functions of the method: softplus for the step size (mhpn.cn selective_scan
+// walk-through, section 7; jiafeimiao.top Mamba.step: softplus(dt + dt_bias))
+// and silu for the output gate (Mamba.step: y * act(z)).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ss {
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+// v_exp_f32 / v_log_f32 / v_rcp_f32: base-2 exponential and logarithm and the
+// reciprocal, each about 1 ulp.  On gfx950 they issue at half the fp32 FMA rate.
+__device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float log2_hw(float x) { return __builtin_amdgcn_logf(x); }
+__device__ __forceinline__ float rcp_hw(float x) { return __builtin_amdgcn_rcpf(x); }
+
+// bf16 <-> fp32.  Widening is exact (the bf16 word is the high half of the
+// fp32 word).  Narrowing rounds to nearest even (v_cvt_pk_bf16_f32).
+__device__ __forceinline__ float bf16_to_f32(uint16_t v) { return __uint_as_float(uint32_t(v) << 16); }
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+    __bf16 h = (__bf16)f;
+    return __builtin_bit_cast(uint16_t, h);
+}
+
+template <typename T> struct Elem;
+
+template <> struct Elem<float> {
+    static __device__ __forceinline__ float load(const float* p, int64_t i) { return p[i]; }
+    static __device__ __forceinline__ void store(float* p, int64_t i, float v) { p[i] = v; }
+};
+
+template <> struct Elem<uint16_t> {
+    static __device__ __forceinline__ float load(const uint16_t* p, int64_t i) { return bf16_to_f32(p[i]); }
+    static __device__ __forceinline__ void store(uint16_t* p, int64_t i, float v) { p[i] = f32_to_bf16(v); }
+};
+
+// Raw input element as loaded (bf16 kept as its 16-bit word until used).
+template <typename T> struct Raw;
+template <> struct Raw<uint16_t> {
+    using type = uint32_t;
+    static __device__ __forceinline__ type load(const uint16_t* p, int64_t i) { return p[i]; }
+    static __device__ __forceinline__ float f(type v) { return __uint_as_float(v << 16); }
+};
+template <> struct Raw<float> {
+    using type = float;
+    static __device__ __forceinline__ type load(const float* p, int64_t i) { return p[i]; }
+    static __device__ __forceinline__ float f(type v) { return v; }
+};
+
+// softplus(x) = log(1 + e^x) = max(x, 0) + log1p(e) with e = exp(-|x|) in (0, 1].
+// log1p(e) is taken from its series e - e^2/2 + e^3/3 - e^4/4 when e < 2^-5
+// (truncation below 2e-7 relative) and as log2(1 + e) * ln 2 otherwise, where
+// 1 + e >= 1.03 so rounding 1 + e costs at most a few ulp.  This keeps small
+// step sizes (x << 0, e.g. softplus(-12) ~ 6e-6) accurate to fp32 rounding,
+// which a plain log(1 + exp(x)) would not.
+__device__ __forceinline__ float softplus(float x) {
+    const float e = exp2_hw(-fabsf(x) * kLog2e);
+    const float series = e * fmaf(e, fmaf(e, fmaf(e, -0.25f, 1.0f / 3.0f), -0.5f), 1.0f);
+    const float direct = log2_hw(1.0f + e) * kLn2;
+    const float r = e < 0.03125f ? series : direct;
+    return fmaxf(x, 0.0f) + r;
+}
+
+// silu(z) = z / (1 + e^-z); for z -> -inf the reciprocal of +inf is 0.
+__device__ __forceinline__ float silu(float z) {
+    return z * rcp_hw(1.0f + exp2_hw(-z * kLog2e));
+}
+
+// Step size of one (b, t, d) element: delta plus the optional bias, then the
+// optional softplus.
+__device__ __forceinline__ float step_size(float delta, float bias, int use_softplus) {
+    const float v = delta + bias;
+    return use_softplus ? softplus(v) : v;
+}
+
+// A2 = A * log2(e) with A = -exp(A_log), so that exp(delta * A) = exp2(delta * A2).
+__device__ __forceinline__ float a2_from_alog(float a_log) {
+    return -exp2_hw(a_log * kLog2e) * kLog2e;
+}
+
+}  // namespace ss

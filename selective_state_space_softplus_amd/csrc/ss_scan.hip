@@ -1,0 +1,327 @@
+// ss_scan.hip -- host side of libss_scan.so: argument validation, the choice
+// of kernel and launch shape, and the C entry points declared in ss_scan.h.
+//
+// Nothing here allocates device memory or synchronises: every launch goes on
+// the caller's stream, and the only scratch memory is the caller's workspace.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdlib>
+#include <cstring>
+
+#include "ss_scan.h"
+#include "scan_kernels.h"
+#include "state_update_kernels.h"
+
+#define SS_EXPORT extern "C" __attribute__((visibility("default")))
+
+namespace {
+
+using ss::ScanParams;
+using ss::StepParams;
+
+constexpr int kMaxSegments = 16;
+constexpr int64_t kMaxElems = int64_t(1) << 46;   // keeps every index product far from int64 overflow
+constexpr int kTparWaves = 8;
+
+// ----------------------------------------------------------------------------- validation helpers
+
+struct Range {
+    uintptr_t lo, hi;   // [lo, hi)
+};
+
+Range range_of(const void* p, int64_t count, size_t elem) {
+    const uintptr_t lo = reinterpret_cast<uintptr_t>(p);
+    return {lo, p ? lo + uintptr_t(count) * elem : lo};
+}
+
+bool overlaps(Range a, Range b) { return a.lo < b.hi && b.lo < a.hi; }
+
+bool aligned(const void* p, size_t a) { return reinterpret_cast<uintptr_t>(p) % a == 0; }
+
+size_t elem_size(int dtype) { return dtype == SS_BF16 ? 2 : 4; }
+
+// a, b, c >= 1 and a * b * c <= 2^46 (checked without forming an overflowing product).
+bool sizes_ok(int64_t a, int64_t b, int64_t c) {
+    if (a <= 0 || b <= 0 || c <= 0) return false;
+    if (a > kMaxElems / b) return false;
+    return a * b <= kMaxElems / c;
+}
+
+// ----------------------------------------------------------------------------- scan planning
+
+enum class ScanKernel { Tpar, Seq };
+
+struct SeqShape {
+    int S;     // waves per workgroup
+    int NSW;   // states per wave
+};
+
+SeqShape seq_shape(int64_t n) {
+    if (n <= 4) return {1, 4};
+    if (n <= 8) return {2, 4};
+    if (n <= 16) return {4, 4};
+    if (n <= 32) return {8, 4};
+    return {8, 8};
+}
+
+ScanKernel choose_kernel(int64_t n) {
+    const char* v = std::getenv("SS_SCAN_VARIANT");
+    if (v && std::strcmp(v, "seq") == 0) return ScanKernel::Seq;
+    if (v && std::strcmp(v, "tpar") == 0 && n <= 2) return ScanKernel::Tpar;
+    return n <= 2 ? ScanKernel::Tpar : ScanKernel::Seq;
+}
+
+// Workspace of scan_seq, in order: control words (ticket, error, one flag per
+// (segment, group)) and the states published between segments, sized for up
+// to kMaxSegments segments.
+struct SeqWorkspace {
+    size_t ctl, handoff, total;
+};
+
+SeqWorkspace seq_workspace(int64_t b, int64_t L, int64_t d_in, int64_t n) {
+    (void)L;
+    const int64_t G = b * ((d_in + 63) / 64);
+    SeqWorkspace w;
+    w.ctl = ((size_t(ss::kFlagOffset) + size_t(G) * kMaxSegments) * sizeof(uint32_t) + 255) / 256 * 256;
+    w.handoff = (size_t(kMaxSegments - 1) * size_t(G) * size_t(n) * 64 * sizeof(float) + 255) / 256 * 256;
+    w.total = w.ctl + w.handoff;
+    return w;
+}
+
+int device_cus() {
+    static int cached[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) return -1;
+    if (dev < 64 && cached[dev] > 0) return cached[dev];
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return -1;
+    if (dev < 64) cached[dev] = cus;
+    return cus;
+}
+
+// Number of segments along L for scan_seq.  SS_SCAN_SEGMENTS overrides (tests);
+// by default the whole length is one segment.
+int choose_segments(int64_t L, int T) {
+    int64_t K = 1;
+    if (const char* e = std::getenv("SS_SCAN_SEGMENTS")) {
+        const long v = std::strtol(e, nullptr, 10);
+        if (v >= 1) K = std::min<int64_t>(std::min<int64_t>(v, kMaxSegments), std::max<int64_t>(1, (L + T - 1) / T));
+    }
+    return int(K);
+}
+
+template <typename TIn, int S, int NSW>
+int launch_seq(ScanParams p, void* ws, size_t ws_bytes, hipStream_t st) {
+    constexpr int T = ss::kSeqChunk;
+    constexpr int V = T / S;
+    constexpr size_t lds = ss::seq_lds_bytes<S, NSW>();
+    const int64_t G = p.b * p.nblk_d;
+    const SeqWorkspace w = seq_workspace(p.b, p.L, p.d_in, p.n);
+    if (!ws || ws_bytes < w.total) return SS_ERR_WORKSPACE;
+    int K = choose_segments(p.L, T);
+    int64_t Lseg = (p.L + K - 1) / K;
+    Lseg = (Lseg + T - 1) / T * T;
+    K = int((p.L + Lseg - 1) / Lseg);
+    p.K = K;
+    p.Lseg = Lseg;
+    char* base = static_cast<char*>(ws);
+    p.ctl = reinterpret_cast<uint32_t*>(base);
+    p.handoff = reinterpret_cast<float*>(base + w.ctl);
+    if (K > 1) {
+        const size_t words = size_t(ss::kFlagOffset) + size_t(G) * K;
+        const int rb = int(std::min<size_t>(1024, (words + 255) / 256));
+        hipLaunchKernelGGL(ss::scan_ctl_reset, dim3(rb), dim3(256), 0, st, p.ctl, int64_t(words));
+        if (hipGetLastError() != hipSuccess) return SS_ERR_HIP;
+    }
+    const size_t va = std::min<size_t>(16, V * sizeof(TIn));
+    const bool vec = p.d_in % V == 0 && aligned(p.u, va) && aligned(p.delta, va) && aligned(p.y, va) &&
+                     (!p.z || aligned(p.z, va));
+    const dim3 grid(unsigned(G * K)), block(S * 64);
+    if (vec)
+        hipLaunchKernelGGL((ss::scan_seq<TIn, S, NSW, true>), grid, block, lds, st, p);
+    else
+        hipLaunchKernelGGL((ss::scan_seq<TIn, S, NSW, false>), grid, block, lds, st, p);
+    return hipGetLastError() == hipSuccess ? SS_OK : SS_ERR_HIP;
+}
+
+template <typename TIn>
+int dispatch_seq(const ScanParams& p, void* ws, size_t ws_bytes, hipStream_t st) {
+    const SeqShape sh = seq_shape(p.n);
+    if (sh.S == 1) return launch_seq<TIn, 1, 4>(p, ws, ws_bytes, st);
+    if (sh.S == 2) return launch_seq<TIn, 2, 4>(p, ws, ws_bytes, st);
+    if (sh.S == 4) return launch_seq<TIn, 4, 4>(p, ws, ws_bytes, st);
+    if (sh.NSW == 4) return launch_seq<TIn, 8, 4>(p, ws, ws_bytes, st);
+    return launch_seq<TIn, 8, 8>(p, ws, ws_bytes, st);
+}
+
+template <typename TIn>
+int dispatch_tpar(const ScanParams& p, hipStream_t st) {
+    const dim3 grid(unsigned(p.b * p.nblk_d));
+    if (p.n == 1)
+        hipLaunchKernelGGL((ss::scan_tpar<TIn, 1, kTparWaves>), grid, dim3(kTparWaves * 64), 0, st, p);
+    else
+        hipLaunchKernelGGL((ss::scan_tpar<TIn, 2, kTparWaves>), grid, dim3(kTparWaves * 64), 0, st, p);
+    return hipGetLastError() == hipSuccess ? SS_OK : SS_ERR_HIP;
+}
+
+}  // namespace
+
+// ============================================================================= C ABI
+
+SS_EXPORT const char* ss_status_string(int status) {
+    switch (status) {
+        case SS_OK: return "ok";
+        case SS_ERR_NULL: return "a required pointer is NULL";
+        case SS_ERR_SHAPE: return "a size is <= 0 or too large";
+        case SS_ERR_DTYPE: return "dtype is not SS_F32 or SS_BF16";
+        case SS_ERR_UNSUPPORTED: return "state size n is above SS_MAX_STATE";
+        case SS_ERR_WORKSPACE: return "workspace is missing or too small";
+        case SS_ERR_HIP: return "the HIP runtime refused the launch";
+        case SS_ERR_ALIAS: return "an output overlaps an input";
+        case SS_ERR_ALIGN: return "a pointer is not aligned to its element size";
+        default: return "unknown status";
+    }
+}
+
+SS_EXPORT size_t ss_scan_fwd_workspace_bytes(int64_t b, int64_t L, int64_t d_in, int64_t n, int dtype) {
+    if (dtype != SS_F32 && dtype != SS_BF16) return 0;
+    if (!sizes_ok(b, L, d_in) || n <= 0 || n > SS_MAX_STATE) return 0;
+    // Sized for scan_seq with the most segments; scan_tpar (n <= 2) needs none
+    // but the same size is asked for so that either kernel can be chosen.
+    return seq_workspace(b, L, d_in, n).total;
+}
+
+SS_EXPORT int ss_scan_fwd(const void* u, const void* delta, const float* A_log, const void* B, const void* C,
+                          const float* D, const void* z, const float* delta_bias, int delta_softplus, void* y,
+                          float* last_state, int64_t b, int64_t L, int64_t d_in, int64_t n, int dtype,
+                          void* workspace, size_t workspace_bytes, void* stream) {
+    if (!u || !delta || !A_log || !B || !C || !D || !y) return SS_ERR_NULL;
+    if (!sizes_ok(b, L, d_in) || n <= 0) return SS_ERR_SHAPE;
+    if (dtype != SS_F32 && dtype != SS_BF16) return SS_ERR_DTYPE;
+    if (n > SS_MAX_STATE) return SS_ERR_UNSUPPORTED;
+    const size_t es = elem_size(dtype);
+    for (const void* p : {u, delta, B, C, z, static_cast<const void*>(y)})
+        if (p && !aligned(p, es)) return SS_ERR_ALIGN;
+    for (const void* p : {static_cast<const void*>(A_log), static_cast<const void*>(D),
+                          static_cast<const void*>(delta_bias), static_cast<const void*>(last_state)})
+        if (p && !aligned(p, 4)) return SS_ERR_ALIGN;
+    const int64_t nel = b * L * d_in;
+    const Range ins[] = {range_of(u, nel, es), range_of(delta, nel, es), range_of(A_log, d_in * n, 4),
+                         range_of(B, b * L * n, es), range_of(C, b * L * n, es), range_of(D, d_in, 4),
+                         range_of(z, z ? nel : 0, es), range_of(delta_bias, delta_bias ? d_in : 0, 4)};
+    const Range ry = range_of(y, nel, es);
+    const Range rs = range_of(last_state, last_state ? b * d_in * n : 0, 4);
+    for (const Range& r : ins)
+        if (overlaps(r, ry) || overlaps(r, rs)) return SS_ERR_ALIAS;
+    if (overlaps(ry, rs)) return SS_ERR_ALIAS;
+    const size_t need = ss_scan_fwd_workspace_bytes(b, L, d_in, n, dtype);
+    if (need > 0 && (!workspace || workspace_bytes < need)) return SS_ERR_WORKSPACE;
+    if (need > 0) {
+        const Range rw = range_of(workspace, int64_t(workspace_bytes), 1);
+        for (const Range& r : ins)
+            if (overlaps(r, rw)) return SS_ERR_ALIAS;
+        if (overlaps(ry, rw) || overlaps(rs, rw)) return SS_ERR_ALIAS;
+    }
+
+    ScanParams p{};
+    p.u = u;
+    p.delta = delta;
+    p.A_log = A_log;
+    p.B = B;
+    p.C = C;
+    p.D = D;
+    p.z = z;
+    p.bias = delta_bias;
+    p.y = y;
+    p.last_state = last_state;
+    p.b = b;
+    p.L = L;
+    p.d_in = d_in;
+    p.n = n;
+    p.softplus = delta_softplus ? 1 : 0;
+    p.nblk_d = int((d_in + 63) / 64);
+    p.K = 1;
+    p.Lseg = L;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+
+    if (choose_kernel(n) == ScanKernel::Tpar)
+        return dtype == SS_BF16 ? dispatch_tpar<uint16_t>(p, st) : dispatch_tpar<float>(p, st);
+    return dtype == SS_BF16 ? dispatch_seq<uint16_t>(p, workspace, workspace_bytes, st)
+                            : dispatch_seq<float>(p, workspace, workspace_bytes, st);
+}
+
+SS_EXPORT int ss_state_update(float* state, const void* x, const void* dt, const float* A_log, const void* B,
+                              const void* C, const float* D, const void* z, const float* dt_bias, int dt_softplus,
+                              void* y, int64_t b, int64_t d_in, int64_t n, int dtype, void* stream) {
+    if (!state || !x || !dt || !A_log || !B || !C || !D || !y) return SS_ERR_NULL;
+    if (!sizes_ok(b, d_in, 1) || n <= 0 || !sizes_ok(b, d_in, n)) return SS_ERR_SHAPE;
+    if (dtype != SS_F32 && dtype != SS_BF16) return SS_ERR_DTYPE;
+    if (n > SS_MAX_STATE) return SS_ERR_UNSUPPORTED;
+    const size_t es = elem_size(dtype);
+    for (const void* p : {x, dt, B, C, z, static_cast<const void*>(y)})
+        if (p && !aligned(p, es)) return SS_ERR_ALIGN;
+    for (const void* p : {static_cast<const void*>(state), static_cast<const void*>(A_log),
+                          static_cast<const void*>(D), static_cast<const void*>(dt_bias)})
+        if (p && !aligned(p, 4)) return SS_ERR_ALIGN;
+    const int64_t nch = b * d_in;
+    const Range ins[] = {range_of(x, nch, es), range_of(dt, nch, es), range_of(A_log, d_in * n, 4),
+                         range_of(B, b * n, es), range_of(C, b * n, es), range_of(D, d_in, 4),
+                         range_of(z, z ? nch : 0, es), range_of(dt_bias, dt_bias ? d_in : 0, 4)};
+    const Range ry = range_of(y, nch, es);
+    const Range rs = range_of(state, nch * n, 4);
+    for (const Range& r : ins)
+        if (overlaps(r, ry) || overlaps(r, rs)) return SS_ERR_ALIAS;
+    if (overlaps(ry, rs)) return SS_ERR_ALIAS;
+
+    StepParams p{};
+    p.state = state;
+    p.x = x;
+    p.dt = dt;
+    p.A_log = A_log;
+    p.B = B;
+    p.C = C;
+    p.D = D;
+    p.z = z;
+    p.bias = dt_bias;
+    p.y = y;
+    p.b = b;
+    p.d_in = d_in;
+    p.n = n;
+    p.softplus = dt_softplus ? 1 : 0;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+
+    const int64_t lpc = n / 4;
+    const bool vec = n % 4 == 0 && (lpc == 1 || lpc == 2 || lpc == 4 || lpc == 8 || lpc == 16) &&
+                     aligned(state, 16) && aligned(A_log, 16) && aligned(B, 4 * es) && aligned(C, 4 * es);
+    if (vec) {
+        const int64_t threads = nch * lpc;
+        const dim3 grid(unsigned((threads + 255) / 256));
+#define SS_STEP_VEC(T_, LPC_) hipLaunchKernelGGL((ss::state_update_vec<T_, LPC_>), grid, dim3(256), 0, st, p)
+        if (dtype == SS_BF16) {
+            switch (lpc) {
+                case 1: SS_STEP_VEC(uint16_t, 1); break;
+                case 2: SS_STEP_VEC(uint16_t, 2); break;
+                case 4: SS_STEP_VEC(uint16_t, 4); break;
+                case 8: SS_STEP_VEC(uint16_t, 8); break;
+                default: SS_STEP_VEC(uint16_t, 16); break;
+            }
+        } else {
+            switch (lpc) {
+                case 1: SS_STEP_VEC(float, 1); break;
+                case 2: SS_STEP_VEC(float, 2); break;
+                case 4: SS_STEP_VEC(float, 4); break;
+                case 8: SS_STEP_VEC(float, 8); break;
+                default: SS_STEP_VEC(float, 16); break;
+            }
+        }
+#undef SS_STEP_VEC
+    } else {
+        const dim3 grid(unsigned((nch + 255) / 256));
+        if (dtype == SS_BF16)
+            hipLaunchKernelGGL((ss::state_update_any<uint16_t>), grid, dim3(256), 0, st, p);
+        else
+            hipLaunchKernelGGL((ss::state_update_any<float>), grid, dim3(256), 0, st, p);
+    }
+    return hipGetLastError() == hipSuccess ? SS_OK : SS_ERR_HIP;
+}

@@ -1,0 +1,145 @@
+"""CPU: the C ABI of libss_scan.so -- it loads, exports every declared entry
+point, and rejects bad arguments with the documented status before it touches
+the GPU (no compute call is made here; the pointers are fake addresses that
+are never dereferenced because validation fails first)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ss_scan.h")
+
+OK, NULL, SHAPE, DTYPE, UNSUP, WS, HIP, ALIAS, ALIGN = 0, -1, -2, -3, -4, -5, -6, -7, -8
+
+
+@pytest.fixture(scope="module")
+def ss():
+    import selective_state_space_softplus_amd as ss
+
+    return ss
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(ss_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_entry_points():
+    assert declared_functions() == sorted(["ss_scan_fwd", "ss_scan_fwd_workspace_bytes", "ss_state_update",
+                                           "ss_status_string"])
+
+
+def test_library_exports_every_declared_symbol(ss):
+    lib = ctypes.CDLL(ss.LIBRARY)
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+    assert set(declared_functions()) == set(ss.EXPORTS)
+
+
+def test_status_strings(ss):
+    for code in (OK, NULL, SHAPE, DTYPE, UNSUP, WS, HIP, ALIAS, ALIGN):
+        s = ss.status_string(code)
+        assert s and s != "unknown status"
+    assert ss.status_string(12345) == "unknown status"
+
+
+def test_status_codes_match_header(ss):
+    text = open(HEADER).read()
+    for name, code in (("SS_OK", OK), ("SS_ERR_NULL", NULL), ("SS_ERR_SHAPE", SHAPE), ("SS_ERR_DTYPE", DTYPE),
+                       ("SS_ERR_UNSUPPORTED", UNSUP), ("SS_ERR_WORKSPACE", WS), ("SS_ERR_HIP", HIP),
+                       ("SS_ERR_ALIAS", ALIAS), ("SS_ERR_ALIGN", ALIGN)):
+        assert re.search(rf"\b{name}\s*=\s*{code}\b", text), name
+        assert ss.STATUS[code] == name
+
+
+def test_workspace_query(ss):
+    q = ss.scan_fwd_workspace_bytes
+    assert q(4, 8192, 5120, 16, 1) > 0
+    assert q(4, 8192, 5120, 16, 1) == q(4, 8192, 5120, 16, 0)       # independent of the element type
+    assert q(4, 8192, 5120, 16, 1) == q(4, 100, 5120, 16, 1)        # and of L
+    assert q(4, 8192, 5120, 16, 1) >= 15 * 4 * 80 * 16 * 64 * 4     # room for 15 published states per group
+    for bad in ((0, 1, 1, 1, 0), (1, 0, 1, 1, 0), (1, 1, -1, 1, 0), (1, 1, 1, 0, 0), (1, 1, 1, 65, 0),
+                (1, 1, 1, 1, 2), (1 << 30, 1 << 30, 1, 1, 0)):
+        assert q(*bad) == 0, bad
+
+
+# fake, well-separated, aligned "device" addresses: validation never dereferences them
+BASE = 1 << 40
+
+
+def addr(i):
+    return BASE + i * (1 << 32)
+
+
+def scan_args(**over):
+    a = dict(u=addr(1), delta=addr(2), A_log=addr(3), B=addr(4), C=addr(5), D=addr(6), z=addr(7), bias=addr(8),
+             softplus=1, y=addr(9), last=addr(10), b=2, L=64, d_in=32, n=16, dtype=0, ws=addr(11),
+             ws_bytes=1 << 30, stream=None)
+    a.update(over)
+    return a
+
+
+def call_scan(ss, a):
+    return ss.lib.ss_scan_fwd(a["u"], a["delta"], a["A_log"], a["B"], a["C"], a["D"], a["z"], a["bias"],
+                              a["softplus"], a["y"], a["last"], a["b"], a["L"], a["d_in"], a["n"], a["dtype"],
+                              a["ws"], a["ws_bytes"], a["stream"])
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(u=None), NULL), (dict(delta=None), NULL), (dict(A_log=None), NULL), (dict(B=None), NULL),
+    (dict(C=None), NULL), (dict(D=None), NULL), (dict(y=None), NULL),
+    (dict(b=0), SHAPE), (dict(L=0), SHAPE), (dict(d_in=-3), SHAPE), (dict(n=0), SHAPE),
+    (dict(b=1 << 24, L=1 << 24, d_in=1 << 24), SHAPE),
+    (dict(dtype=2), DTYPE), (dict(dtype=-1), DTYPE),
+    (dict(n=65), UNSUP), (dict(n=1000), UNSUP),
+    (dict(ws=None), WS), (dict(ws_bytes=100), WS),
+    (dict(u=addr(1) + 2), ALIGN), (dict(dtype=1, u=addr(1) + 1), ALIGN), (dict(A_log=addr(3) + 2), ALIGN),
+    (dict(last=addr(10) + 1), ALIGN),
+    (dict(y=addr(1) + 64), ALIAS), (dict(last=addr(4)), ALIAS), (dict(y=addr(10)), ALIAS),
+    (dict(ws=addr(9)), ALIAS), (dict(ws=addr(1)), ALIAS), (dict(last=addr(8) + 4), ALIAS),
+])
+def test_scan_rejects(ss, over, code):
+    assert call_scan(ss, scan_args(**over)) == code
+
+
+def test_scan_optional_pointers_may_be_null(ss):
+    # z, bias and last_state are optional: with them NULL and a bad dtype the
+    # dtype error (not a NULL error) is what comes back.
+    assert call_scan(ss, scan_args(z=None, bias=None, last=None, dtype=9)) == DTYPE
+
+
+def step_args(**over):
+    a = dict(state=addr(1), x=addr(2), dt=addr(3), A_log=addr(4), B=addr(5), C=addr(6), D=addr(7), z=addr(8),
+             bias=addr(9), softplus=1, y=addr(10), b=256, d_in=5120, n=16, dtype=1, stream=None)
+    a.update(over)
+    return a
+
+
+def call_step(ss, a):
+    return ss.lib.ss_state_update(a["state"], a["x"], a["dt"], a["A_log"], a["B"], a["C"], a["D"], a["z"], a["bias"],
+                                  a["softplus"], a["y"], a["b"], a["d_in"], a["n"], a["dtype"], a["stream"])
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(state=None), NULL), (dict(x=None), NULL), (dict(dt=None), NULL), (dict(A_log=None), NULL),
+    (dict(B=None), NULL), (dict(C=None), NULL), (dict(D=None), NULL), (dict(y=None), NULL),
+    (dict(b=0), SHAPE), (dict(d_in=0), SHAPE), (dict(n=-1), SHAPE), (dict(dtype=3), DTYPE), (dict(n=65), UNSUP),
+    (dict(state=addr(1) + 2), ALIGN), (dict(x=addr(2) + 1), ALIGN),
+    (dict(y=addr(2)), ALIAS), (dict(state=addr(9)), ALIAS), (dict(y=addr(1) + 8), ALIAS),
+])
+def test_step_rejects(ss, over, code):
+    assert call_step(ss, step_args(**over)) == code
+
+
+def test_python_binding_checks_tensors(ss):
+    import torch
+
+    u = torch.zeros(2, 8, 4)
+    with pytest.raises((TypeError, ValueError)):
+        ss.scan_fwd(u, u, torch.zeros(4, 16), torch.zeros(2, 8, 16), torch.zeros(2, 8, 16),
+                    torch.zeros(4, dtype=torch.float64))
+    with pytest.raises((TypeError, ValueError)):
+        ss.scan_fwd(u, u[:, :4], torch.zeros(4, 16), torch.zeros(2, 8, 16), torch.zeros(2, 8, 16), torch.zeros(4))

@@ -1,0 +1,312 @@
+"""GPU: the HIP path against the CPU oracle, element by element, through the C ABI.
+
+Small shapes are compared in full; the full-size workloads are compared on
+sampled (batch, channel) recurrences, each computed by the oracle on its own
+slice of the inputs (every channel is an independent recurrence), with the
+kernel launched exactly as the benchmark launches it.  Tolerances: max
+relative error 1e-4 for fp32 inputs, 2e-2 for bf16 inputs (tests/parity.py).
+"""
+import os
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from tests.parity import TOL, assert_close, rel_err
+
+pytestmark = [pytest.mark.gpu,
+              pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU")]
+
+DEV = "cuda:0"
+F32, BF16 = torch.float32, torch.bfloat16
+
+
+@pytest.fixture(scope="module")
+def ss():
+    import selective_state_space_softplus_amd as ss
+
+    return ss
+
+
+def say(msg):
+    sys.stdout.write(f"\n[case] {msg}\n")
+    sys.stdout.flush()
+
+
+class env:
+    """Temporarily set library test hooks (kernel variant, segment count)."""
+
+    def __init__(self, **kv):
+        self.kv = {k: str(v) for k, v in kv.items() if v is not None}
+
+    def __enter__(self):
+        self.old = {k: os.environ.get(k) for k in self.kv}
+        os.environ.update(self.kv)
+
+    def __exit__(self, *a):
+        for k, v in self.old.items():
+            if v is None:
+                os.environ.pop(k, None)
+            else:
+                os.environ[k] = v
+
+
+def to_dev(inp):
+    return {k: (v.to(DEV) if isinstance(v, torch.Tensor) else v) for k, v in inp.items()}
+
+
+def gpu_scan(ss, g, last=True):
+    return ss.scan_fwd(g["u"], g["delta"], g["A_log"], g["B"], g["C"], g["D"], g["z"], g["delta_bias"],
+                       g["delta_softplus"], return_last_state=last)
+
+
+def oracle_scan(inp):
+    return oracle.scan(inp["u"], inp["delta"], inp["A_log"], inp["B"], inp["C"], inp["D"], inp["z"],
+                       inp["delta_bias"], inp["delta_softplus"])
+
+
+def check_full(ss, inp, what):
+    g = to_dev(inp)
+    y, last = gpu_scan(ss, g)
+    torch.cuda.synchronize()
+    yr, lr = oracle_scan(inp)
+    e1 = assert_close(y, yr, inp["dtype"], f"{what} y")
+    e2 = assert_close(last, lr, inp["dtype"], f"{what} last_state")
+    return e1, e2
+
+
+# ----------------------------------------------------------------------------- small shapes, full compare
+
+SMALL = [
+    # b, L, d_in, n, dtype, gated, bias, softplus
+    (2, 300, 130, 16, F32, True, True, True),
+    (2, 300, 130, 16, BF16, True, True, True),
+    (1, 1, 1, 16, F32, True, True, True),
+    (1, 2, 7, 16, F32, False, False, True),
+    (3, 63, 33, 16, BF16, True, False, True),
+    (2, 65, 64, 16, F32, False, True, True),
+    (1, 97, 65, 16, F32, True, True, False),
+    (2, 200, 40, 1, F32, False, False, True),
+    (2, 200, 40, 1, BF16, True, True, True),
+    (1, 129, 70, 2, F32, True, True, True),
+    (1, 77, 20, 3, F32, True, True, True),
+    (1, 77, 20, 4, BF16, True, True, True),
+    (2, 50, 10, 5, F32, True, False, True),
+    (1, 70, 66, 7, F32, True, True, True),
+    (1, 70, 66, 8, BF16, False, True, True),
+    (1, 70, 66, 17, F32, True, True, True),
+    (1, 70, 40, 32, F32, True, True, True),
+    (1, 70, 40, 33, F32, True, True, True),
+    (1, 70, 40, 64, F32, True, True, True),
+    (1, 70, 40, 64, BF16, True, True, True),
+]
+
+
+def small_inputs(b, L, d_in, n, dtype, gated, bias, softplus, seed):
+    inp = workloads.random_scan_inputs(b, L, d_in, n, dtype, seed, gated=gated, bias=bias)
+    if not softplus:
+        # Without softplus the step size is delta + bias itself, so keep it positive.
+        inp["delta"] = (inp["delta"].float().abs() * 0.1 + 0.01).to(dtype)
+        if inp["delta_bias"] is not None:
+            inp["delta_bias"] = inp["delta_bias"].abs() * 0.01
+        inp["delta_softplus"] = False
+    return inp
+
+
+@pytest.mark.parametrize("case", SMALL, ids=lambda c: "b{}_L{}_d{}_n{}_{}_{}{}{}".format(
+    c[0], c[1], c[2], c[3], "f32" if c[4] == F32 else "bf16", "g" if c[5] else "", "b" if c[6] else "",
+    "s" if c[7] else ""))
+def test_scan_small(ss, case):
+    say(f"scan small {case}")
+    inp = small_inputs(*case, seed=sum(case[:4]))
+    check_full(ss, inp, f"scan {case}")
+
+
+@pytest.mark.parametrize("variant,segments,n,L", [
+    ("seq", 3, 16, 300), ("seq", 16, 16, 1000), ("seq", 5, 1, 700), ("seq", 4, 2, 500), ("seq", 7, 64, 450),
+    ("tpar", None, 1, 1000), ("tpar", None, 2, 333),
+])
+def test_scan_forced_variant(ss, variant, segments, n, L):
+    say(f"forced variant={variant} segments={segments} n={n} L={L}")
+    inp = workloads.random_scan_inputs(2, L, 100, n, F32, seed=7 + n + L, gated=True, bias=True)
+    with env(SS_SCAN_VARIANT=variant, SS_SCAN_SEGMENTS=segments):
+        check_full(ss, inp, f"{variant}/{segments}")
+
+
+def test_scan_unshifted_delta_reading(ss):
+    """The alternative reading of the mid/long workloads: delta ~ N(0,1) before bias and softplus."""
+    say("unshifted delta")
+    inp = workloads.random_scan_inputs(2, 400, 96, 16, BF16, seed=99, gated=True, bias=True, delta_shift=0.0)
+    check_full(ss, inp, "unshifted delta")
+
+
+def test_scan_tiny_workload_full(ss):
+    say("scan-tiny workload, full compare")
+    inp = workloads.scan_inputs(0)
+    e1, e2 = check_full(ss, inp, "scan-tiny")
+    print(f"scan-tiny: y err {e1:.3g}, last_state err {e2:.3g}")
+
+
+def test_empty_inputs(ss):
+    say("empty inputs")
+    for shape in ((0, 5, 4), (2, 0, 4), (2, 5, 0)):
+        u = torch.zeros(shape, device=DEV)
+        b, L, d = shape
+        y, last = ss.scan_fwd(u, u, torch.zeros(d, 4, device=DEV), torch.zeros(b, L, 4, device=DEV),
+                              torch.zeros(b, L, 4, device=DEV), torch.zeros(d, device=DEV), return_last_state=True)
+        assert y.shape == shape and last.shape == (b, d, 4) and torch.all(last == 0)
+
+
+# ----------------------------------------------------------------------------- full-size workloads, sampled
+
+def sample_channels(b, d_in, count, seed):
+    r = np.random.default_rng(seed)
+    ch = {(0, 0), (b - 1, d_in - 1), (0, d_in - 1), (b - 1, 0), (0, 63 % d_in), (b // 2, min(64, d_in - 1))}
+    while len(ch) < count:
+        ch.add((int(r.integers(b)), int(r.integers(d_in))))
+    return sorted(ch)
+
+
+@pytest.mark.parametrize("index", [1, 2, 3])
+def test_scan_workload_sampled(ss, index):
+    cfg = workloads.CONFIGS[index]
+    say(f"{cfg.name} full size, sampled channels")
+    inp = workloads.scan_inputs(index)
+    g = to_dev(inp)
+    y, last = gpu_scan(ss, g)
+    torch.cuda.synchronize()
+    chans = sample_channels(cfg.b, cfg.d_in, 40, index)
+    ref = oracle.scan_channels(inp, chans)
+    yc = y[[c[0] for c in chans], :, [c[1] for c in chans]].cpu()       # (count, L)
+    lc = last[[c[0] for c in chans], [c[1] for c in chans]].cpu()      # (count, n)
+    yr = np.stack([ref[c][0] for c in chans])
+    lr = np.stack([ref[c][1] for c in chans])
+    e1 = assert_close(yc, yr, cfg.dtype, f"{cfg.name} y")
+    e2 = assert_close(lc, lr, cfg.dtype, f"{cfg.name} last_state")
+    assert torch.isfinite(y).all()
+    print(f"{cfg.name}: y err {e1:.3g}, last_state err {e2:.3g} over {len(chans)} channels")
+
+
+def test_decode_workload_sampled(ss):
+    cfg = workloads.CONFIGS[4]
+    say(f"{cfg.name}: 64 steps on the full state, sampled sequences")
+    inp = workloads.decode_inputs(4)
+    g = to_dev(inp)
+    state = g["state"].clone()
+    ys = []
+    for s in range(cfg.steps):
+        ys.append(ss.state_update(state, g["x"][s], g["dt"][s], g["A_log"], g["B"][s], g["C"][s], g["D"], g["z"][s],
+                                  g["dt_bias"], True))
+    torch.cuda.synchronize()
+    rows = [0, 37, 128, 255]
+    st = inp["state"][rows]
+    for s in range(cfg.steps):
+        st, yr = oracle.state_update(st, inp["x"][s][rows], inp["dt"][s][rows], inp["A_log"], inp["B"][s][rows],
+                                     inp["C"][s][rows], inp["D"], inp["z"][s][rows], inp["dt_bias"], True)
+        assert_close(ys[s][rows], yr, cfg.dtype, f"decode y step {s}")
+    e = assert_close(state[rows], st, cfg.dtype, "decode final state")
+    print(f"decode: final state err {e:.3g}")
+
+
+# ----------------------------------------------------------------------------- decode step, small shapes
+
+@pytest.mark.parametrize("b,d_in,n,dtype,gated,bias", [
+    (3, 33, 16, F32, True, True), (3, 33, 16, BF16, True, True), (1, 1, 1, F32, False, False),
+    (2, 10, 3, F32, True, True), (2, 10, 4, BF16, True, False), (2, 10, 8, F32, False, True),
+    (2, 10, 32, F32, True, True), (2, 10, 64, BF16, True, True), (2, 10, 5, BF16, True, True),
+    (2, 10, 48, F32, True, True),
+])
+def test_step_small(ss, b, d_in, n, dtype, gated, bias):
+    say(f"step b={b} d_in={d_in} n={n} {dtype}")
+    r = torch.Generator().manual_seed(b * 1000 + d_in * 10 + n)
+    rn = lambda *s: torch.randn(*s, generator=r)  # noqa: E731
+    state = rn(b, d_in, n) * 0.5
+    x, dt, z = rn(b, d_in).to(dtype), (rn(b, d_in) - 1).to(dtype), rn(b, d_in).to(dtype)
+    Bm, Cm = rn(b, n).to(dtype), rn(b, n).to(dtype)
+    A_log, D = torch.rand(d_in, n) * 2 - 1, rn(d_in)
+    bb = (torch.rand(d_in) - 0.5) if bias else None
+    zz = z if gated else None
+    sg = state.to(DEV)
+    dev = lambda t: None if t is None else t.to(DEV)  # noqa: E731
+    y = ss.state_update(sg, dev(x), dev(dt), dev(A_log), dev(Bm), dev(Cm), dev(D), dev(zz), dev(bb), True)
+    torch.cuda.synchronize()
+    sr, yr = oracle.state_update(state, x, dt, A_log, Bm, Cm, D, zz, bb, True)
+    assert_close(y, yr, dtype, "step y")
+    assert_close(sg, sr, dtype, "step state")
+
+
+# ----------------------------------------------------------------------------- invariants on the GPU
+
+def test_scan_L1_equals_step(ss):
+    say("scan L=1 vs step from zero")
+    inp = to_dev(workloads.random_scan_inputs(3, 1, 70, 16, F32, seed=3, gated=True, bias=True))
+    y, last = gpu_scan(ss, inp)
+    state = torch.zeros(3, 70, 16, device=DEV)
+    ys = ss.state_update(state, inp["u"][:, 0], inp["delta"][:, 0], inp["A_log"], inp["B"][:, 0], inp["C"][:, 0],
+                         inp["D"], inp["z"][:, 0], inp["delta_bias"], True)
+    assert rel_err(ys, y[:, 0]) < 1e-6
+    assert rel_err(state, last) < 1e-6
+
+
+@pytest.mark.parametrize("n,dtype", [(16, F32), (16, BF16), (1, F32)])
+def test_chain_of_steps_equals_scan(ss, n, dtype):
+    say(f"chain of steps vs scan n={n}")
+    L = 40
+    inp = to_dev(workloads.random_scan_inputs(2, L, 50, n, dtype, seed=5, gated=True, bias=True))
+    y, last = gpu_scan(ss, inp)
+    state = torch.zeros(2, 50, n, device=DEV)
+    for t in range(L):
+        yt = ss.state_update(state, inp["u"][:, t].contiguous(), inp["delta"][:, t].contiguous(), inp["A_log"],
+                             inp["B"][:, t].contiguous(), inp["C"][:, t].contiguous(), inp["D"],
+                             inp["z"][:, t].contiguous(), inp["delta_bias"], True)
+        assert rel_err(yt, y[:, t]) <= (1e-5 if dtype == F32 else 1e-2), t
+    assert rel_err(state, last) <= 1e-5
+
+
+def test_prefill_then_decode(ss):
+    say("prefill then decode")
+    L1, L = 50, 60
+    inp = workloads.random_scan_inputs(2, L, 80, 16, F32, seed=6, gated=True, bias=True)
+    g = to_dev(inp)
+    y_full = gpu_scan(ss, g, last=False)
+    pre = {k: (v[:, :L1].contiguous() if isinstance(v, torch.Tensor) and v.dim() == 3 else v) for k, v in g.items()}
+    _, st = gpu_scan(ss, pre)
+    for t in range(L1, L):
+        yt = ss.state_update(st, g["u"][:, t].contiguous(), g["delta"][:, t].contiguous(), g["A_log"],
+                             g["B"][:, t].contiguous(), g["C"][:, t].contiguous(), g["D"], g["z"][:, t].contiguous(),
+                             g["delta_bias"], True)
+        assert rel_err(yt, y_full[:, t]) <= 1e-5
+
+
+@pytest.mark.parametrize("n,segments", [(16, 6), (1, None)])
+def test_deterministic_and_causal(ss, n, segments):
+    say(f"determinism and causality n={n} segments={segments}")
+    inp = to_dev(workloads.random_scan_inputs(2, 700, 130, n, BF16, seed=8, gated=True, bias=True))
+    with env(SS_SCAN_SEGMENTS=segments):
+        y1, l1 = gpu_scan(ss, inp)
+        y2, l2 = gpu_scan(ss, inp)
+        assert torch.equal(y1, y2) and torch.equal(l1, l2), "run-to-run bitwise determinism"
+        t0 = 333
+        p = dict(inp)
+        for k in ("u", "delta", "B", "C", "z"):
+            p[k] = inp[k].clone()
+            p[k][:, t0:] = p[k][:, t0:] + 1
+        y3, _ = gpu_scan(ss, p)
+    assert torch.equal(y1[:, :t0], y3[:, :t0]), "outputs before t0 must not change"
+    assert not torch.equal(y1[:, t0:], y3[:, t0:])
+
+
+def test_nan_stays_in_its_channel(ss):
+    say("NaN isolation")
+    for n in (16, 1):
+        inp = to_dev(workloads.random_scan_inputs(2, 300, 70, n, F32, seed=9, gated=True, bias=True))
+        inp["u"] = inp["u"].clone()
+        inp["u"][1, 100, 5] = float("nan")
+        y, last = gpu_scan(ss, inp)
+        bad = ~torch.isfinite(y)
+        assert bad[1, 100:, 5].all()
+        bad[1, 100:, 5] = False
+        assert not bad.any(), f"NaN leaked out of its channel (n={n})"
