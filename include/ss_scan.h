@@ -59,7 +59,7 @@ typedef enum {
 typedef enum {
     SS_OK = 0,
     SS_ERR_NULL = -1,        /* a required pointer is NULL                          */
-    SS_ERR_SHAPE = -2,       /* a size is <= 0 or too large to index                */
+    SS_ERR_SHAPE = -2,       /* a size is <= 0, or too large to index or above SS_MAX_CHANNELS */
     SS_ERR_DTYPE = -3,       /* dtype is not an ss_dtype value                      */
     SS_ERR_UNSUPPORTED = -4, /* n (the state size) is above SS_MAX_STATE            */
     SS_ERR_WORKSPACE = -5,   /* workspace missing or smaller than the query says    */
@@ -70,6 +70,9 @@ typedef enum {
 
 /* Largest state size n the kernels are built for. */
 #define SS_MAX_STATE 64
+
+/* Largest channel count d_in of ss_scan_fwd (per-thread offsets are 24-bit products). */
+#define SS_MAX_CHANNELS ((1 << 24) - 1)
 
 /*
  * Bytes of device workspace ss_scan_fwd needs for these sizes (0 when none).
@@ -95,8 +98,10 @@ size_t ss_scan_fwd_workspace_bytes(int64_t b, int64_t L, int64_t d_in, int64_t n
  *   workspace  : device memory of at least ss_scan_fwd_workspace_bytes()
  *                bytes (may be NULL when that is 0).  Its contents need no
  *                initialisation and are scratch after the call.
- * Any n in 1..SS_MAX_STATE and any b, L, d_in >= 1 are accepted (no tile
- * multiples are required).  Returns an ss_status.
+ * Any n in 1..SS_MAX_STATE, d_in in 1..SS_MAX_CHANNELS and b, L >= 1 with
+ * b * L * d_in <= 2^46 and b * ceil(d_in / 64) < 2^23 are
+ * accepted (no tile multiples are required); other sizes give SS_ERR_SHAPE.
+ * Returns an ss_status.
  */
 int ss_scan_fwd(const void *u, const void *delta, const float *A_log,
                 const void *B, const void *C, const float *D,
@@ -119,6 +124,7 @@ int ss_scan_fwd(const void *u, const void *delta, const float *A_log,
  *   dt_bias : (d_in)       fp32, or NULL
  *   dt_softplus : as delta_softplus above
  *   y       : (b, d_in)    dtype, output
+ * Sizes: b, d_in >= 1, b * d_in < 2^28, b * d_in * n <= 2^46.
  * Returns an ss_status.
  */
 int ss_state_update(float *state, const void *x, const void *dt,

@@ -60,77 +60,81 @@ struct ScanParams {
 constexpr int kFlagOffset = 64;
 constexpr int kSpinLimit = 1 << 25;   // ~2 s of s_sleep before a wait gives up and flags an error
 
-// Chunk length of scan_seq: every wave walks T steps between barriers.
-constexpr int kSeqChunk = 32;
+// Chunk length of scan_seq: the workgroup advances T steps per barrier.
+constexpr int kSeqChunk = 16;
 
-// Steps of B/C and (delta', delta' u) a wave reads ahead of the step it computes.
+// Steps of B and C a wave reads ahead of the step it computes.
 constexpr int kSeqAhead = 4;
 
-// LDS of scan_seq: (delta', delta' u) per (t, d); the S partial readouts per
-// (t, d); B and C of the chunk as fp32, grouped per wave; 16 bytes for the
-// ticket.  Everything is one dynamic block starting 16-byte aligned: a static
-// __shared__ variable would shift the dynamic block by its size and leave the
-// 8- and 16-byte LDS accesses misaligned, which the LDS serialises.
+// LDS of scan_seq, double-buffered by chunk parity: (delta', delta' u) per
+// (t, d), two steps interleaved per channel; the S partial readouts per
+// (t, d); B and C of the chunk as fp32, grouped per wave; then 16 bytes for
+// the ticket.  It is one dynamic block that starts 16-byte aligned: a static
+// __shared__ variable would shift it by its size and leave the 8- and 16-byte
+// LDS accesses misaligned, which the LDS serialises.
 template <int S, int NSW>
 constexpr size_t seq_lds_bytes() {
-    return size_t(kSeqChunk) * (64 * (sizeof(float2) + S * sizeof(float)) + 2 * S * NSW * sizeof(float)) + 16;
+    return 2 * size_t(kSeqChunk) * (64 * (sizeof(float2) + S * sizeof(float)) + 2 * S * NSW * sizeof(float)) + 16;
 }
 
-// V consecutive input elements of one row: one wide load when VEC, else V
-// bounds-checked scalar loads (past-the-end elements read as 0).
+// V consecutive input elements of one row, kept as the raw 32-bit words that
+// were loaded (one wide load when VEC, else V bounds-checked element loads,
+// past-the-end elements reading as 0) and widened to fp32 only when used, so
+// a load stays in flight until its value is needed.
 template <typename TIn, int V, bool VEC>
 struct Span {
-    using R = Raw<TIn>;
-    typename R::type v[V];
-    __device__ __forceinline__ void load(const TIn* p, int64_t e, int valid) {
+    static constexpr bool kHalf = sizeof(TIn) == 2;
+    static constexpr int NW = VEC ? (V * int(sizeof(TIn)) + 3) / 4 : V;
+    uint32_t w[NW];
+
+    __device__ __forceinline__ void load(const TIn* base, uint32_t e, int valid) {
+        const TIn* p = base;
         if constexpr (VEC) {
-            constexpr int BYTES = V * sizeof(TIn);
-            static_assert(BYTES % 16 == 0 || BYTES == 8, "wide loads of 8 or 16k bytes");
-            if constexpr (BYTES == 8) {
-                const uint2 w = *reinterpret_cast<const uint2*>(p + e);
-                const uint32_t ww[2] = {w.x, w.y};
-                unpack(ww);
+            constexpr int BYTES = V * int(sizeof(TIn));
+            if constexpr (BYTES == 4) {
+                w[0] = *reinterpret_cast<const uint32_t*>(p + e);
+            } else if constexpr (BYTES == 8) {
+                const uint2 v = *reinterpret_cast<const uint2*>(p + e);
+                w[0] = v.x;
+                w[1] = v.y;
             } else {
-                uint32_t ww[BYTES / 4];
+                static_assert(BYTES % 16 == 0, "wide loads of 4, 8 or 16k bytes");
 #pragma unroll
                 for (int c = 0; c < BYTES / 16; c++) {
-                    const uint4 w = reinterpret_cast<const uint4*>(p + e)[c];
-                    ww[4 * c] = w.x;
-                    ww[4 * c + 1] = w.y;
-                    ww[4 * c + 2] = w.z;
-                    ww[4 * c + 3] = w.w;
+                    const uint4 v = reinterpret_cast<const uint4*>(p + e)[c];
+                    w[4 * c] = v.x;
+                    w[4 * c + 1] = v.y;
+                    w[4 * c + 2] = v.z;
+                    w[4 * c + 3] = v.w;
                 }
-                unpack(ww);
             }
         } else {
 #pragma unroll
-            for (int i = 0; i < V; i++) v[i] = i < valid ? R::load(p, e + i) : typename R::type(0);
-        }
-    }
-    template <int W>
-    __device__ __forceinline__ void unpack(const uint32_t (&ww)[W]) {
-        if constexpr (sizeof(TIn) == 2) {
-#pragma unroll
-            for (int i = 0; i < W; i++) {
-                v[2 * i] = ww[i] & 0xffffu;
-                v[2 * i + 1] = ww[i] >> 16;
+            for (int i = 0; i < V; i++) {
+                if constexpr (kHalf)
+                    w[i] = i < valid ? uint32_t(reinterpret_cast<const uint16_t*>(p)[e + i]) : 0u;
+                else
+                    w[i] = i < valid ? __float_as_uint(reinterpret_cast<const float*>(p)[e + i]) : 0u;
             }
-        } else {
-#pragma unroll
-            for (int i = 0; i < W; i++) v[i] = __uint_as_float(ww[i]);
         }
     }
-    __device__ __forceinline__ float f(int i) const { return R::f(v[i]); }
+    __device__ __forceinline__ float f(int i) const {
+        if constexpr (!kHalf) return __uint_as_float(w[i]);
+        else if constexpr (!VEC) return __uint_as_float(w[i] << 16);
+        else return (i & 1) ? __uint_as_float(w[i / 2] & 0xffff0000u) : __uint_as_float(w[i / 2] << 16);
+    }
 };
 
 template <typename TIn, int V, bool VEC>
-__device__ __forceinline__ void store_span(TIn* p, int64_t e, const float* y, int valid) {
+__device__ __forceinline__ void store_span(TIn* p, uint32_t e, const float* y, int valid) {
     if constexpr (VEC && sizeof(TIn) == 2) {
-        uint32_t ww[V / 2];
+        uint32_t ww[(V + 1) / 2];
 #pragma unroll
         for (int i = 0; i < V / 2; i++)
             ww[i] = uint32_t(f32_to_bf16(y[2 * i])) | (uint32_t(f32_to_bf16(y[2 * i + 1])) << 16);
-        if constexpr (V == 4) {
+        if constexpr (V == 2) {
+            *reinterpret_cast<uint32_t*>(p + e) = ww[0];
+        } else if constexpr (V == 4) {
             *reinterpret_cast<uint2*>(p + e) = make_uint2(ww[0], ww[1]);
         } else {
 #pragma unroll
@@ -138,9 +142,13 @@ __device__ __forceinline__ void store_span(TIn* p, int64_t e, const float* y, in
                 reinterpret_cast<uint4*>(p + e)[c] = make_uint4(ww[4 * c], ww[4 * c + 1], ww[4 * c + 2], ww[4 * c + 3]);
         }
     } else if constexpr (VEC) {
+        if constexpr (V == 2) {
+            *reinterpret_cast<float2*>(p + e) = make_float2(y[0], y[1]);
+        } else {
 #pragma unroll
-        for (int c = 0; c < V / 4; c++)
-            reinterpret_cast<float4*>(p + e)[c] = make_float4(y[4 * c], y[4 * c + 1], y[4 * c + 2], y[4 * c + 3]);
+            for (int c = 0; c < V / 4; c++)
+                reinterpret_cast<float4*>(p + e)[c] = make_float4(y[4 * c], y[4 * c + 1], y[4 * c + 2], y[4 * c + 3]);
+        }
     } else {
 #pragma unroll
         for (int i = 0; i < V; i++)
@@ -150,23 +158,42 @@ __device__ __forceinline__ void store_span(TIn* p, int64_t e, const float* y, in
 
 // VEC: d_in is a multiple of the per-thread span V and the tensors are
 // aligned for it, so the per-element phases use wide loads and stores.
-template <typename TIn, int S, int NSW, bool VEC>
+// SP: delta' = softplus(delta + bias) (else delta + bias).  GATE: z is given.
+//
+// One barrier per chunk c of T steps.  Between two barriers every wave
+//   - reads (delta', delta' u) of chunk c for its 64 lanes from LDS, and the
+//     partial readouts of chunk c-1, all up front;
+//   - runs the recurrence of chunk c from registers, reading its B and C
+//     values of each step from LDS kSeqAhead steps ahead (the only LDS
+//     accesses inside the loop, so every wait is for a read issued steps
+//     earlier);
+//   - interleaves the per-element work: phase 2 of chunk c-1 (partial sums,
+//     D skip, gate) and phase 1 of chunk c+1 (step size, delta' u), whose
+//     global loads were issued two chunks earlier;
+//   - then writes its partial readouts of chunk c, the phase-1 results and the
+//     B, C values of chunk c+1 to LDS, and stores y of chunk c-1.
+// LDS buffers alternate with the chunk parity, so no buffer is written and
+// read by different waves between two barriers.
+template <typename TIn, int S, int NSW, bool VEC, bool SP, bool GATE>
 __global__ __launch_bounds__(S * 64) void scan_seq(const ScanParams p) {
     constexpr int T = kSeqChunk;
     constexpr int NT = S * 64;                     // threads
     constexpr int V = T / S;                       // consecutive channels per thread in the per-element phases
     constexpr int TPR = 64 / V;                    // threads per step row
+    constexpr int DW_BUF = T * 64 * 2;             // floats per (delta', delta' u) buffer
+    constexpr int YP_BUF = S * T * 64;             // floats per partial-readout buffer
     constexpr int NP = S * NSW;                    // states per channel, padded
-    constexpr int EBC = T * NP / NT;               // B (and C) values each thread stages per chunk
+    constexpr int BC_BUF = T * 2 * NP;             // floats per B/C buffer
+    constexpr int EBC = (T * NP + NT - 1) / NT;    // B (and C) values each thread stages per chunk
+    constexpr int D = kSeqAhead;
+    constexpr int NR = NSW / 2;                    // float4 reads per step: NSW values of B then NSW of C
     static_assert(T % S == 0 && 64 % V == 0 && NT / TPR == T, "thread tiling of a chunk");
-    static_assert((T * NP) % NT == 0 && NSW % 4 == 0, "B/C tile splits evenly; states come in quads");
-    using R = Raw<TIn>;
+    static_assert(NSW % 2 == 0 && T % 2 == 0 && T % D == 0, "tiles split evenly");
     extern __shared__ __align__(16) float smem[];
-    float2* s_dw = reinterpret_cast<float2*>(smem);               // [T][64]  (delta', delta' u)
-    float* s_yp = smem + 2 * T * 64;                              // [S][T][64] partial readouts
-    float* s_bc = s_yp + S * T * 64;                              // [T][S][2][NSW]  B, C per wave
-    int& s_ticket = *reinterpret_cast<int*>(s_bc + T * 2 * NP);
-
+    float* s_dw = smem;                            // [2][T/2][64][4]: (delta'_j, w_j, delta'_j+1, w_j+1)
+    float* s_yp = smem + 2 * DW_BUF;               // [2][S][T][64]
+    float* s_bc = s_yp + 2 * YP_BUF;               // [2][T][S][2][NSW]
+    int& s_ticket = *reinterpret_cast<int*>(s_bc + 2 * BC_BUF);
     const TIn* __restrict__ Bm = static_cast<const TIn*>(p.B);
     const TIn* __restrict__ Cm = static_cast<const TIn*>(p.C);
 
@@ -196,14 +223,15 @@ __global__ __launch_bounds__(S * 64) void scan_seq(const ScanParams p) {
     const int64_t d = dbase + lane;               // channel of this lane in the recurrence
     const bool dv = d < d_in;
     const int64_t t_begin = seg * p.Lseg;
-    const int64_t t_end = min(L, t_begin + p.Lseg);
+    const int64_t t_end = imin(L, t_begin + p.Lseg);
+    const int nchunks = int((t_end - t_begin + T - 1) / T);
     const int n0 = wave * NSW;
 
-    // Per-element phases: thread owns step row er of the chunk, channels ec .. ec+V.
+    // Per-element phases: thread owns step row er of a chunk, channels ec .. ec+V.
     const int er = tid / TPR;
     const int ec = (tid - er * TPR) * V;
-    const int64_t ech = dbase + ec;               // first channel of the span
-    const int evalid = int(max<int64_t>(0, min<int64_t>(V, d_in - ech)));
+    const int64_t ech = dbase + ec;
+    const int evalid = int(imax(0, imin(V, d_in - ech)));
     const int64_t ech_c = evalid > 0 ? ech : 0;   // loads of an empty span stay in bounds
 
     float A2[NSW], h[NSW];
@@ -218,7 +246,6 @@ __global__ __launch_bounds__(S * 64) void scan_seq(const ScanParams p) {
         Dv[i] = i < evalid ? p.D[ech + i] : 0.0f;
         bias_v[i] = (i < evalid && p.bias) ? p.bias[ech + i] : 0.0f;
     }
-    const bool gated = zp != nullptr;
 
     if (seg > 0) {
         // Wait for the previous segment of this channel group, then take its state.
@@ -241,134 +268,221 @@ __global__ __launch_bounds__(S * 64) void scan_seq(const ScanParams p) {
             if (n0 + q < n) h[q] = src[(n0 + q) * 64 + lane];
     }
 
+    // Address arithmetic: uniform 64-bit chunk bases (scalar unit) plus
+    // per-thread 32-bit offsets; rows past the end of L are clamped to the
+    // last row (those values are masked and never stored).  The host keeps
+    // d_in < 2^24 and T * d_in below 2^31.
+    const uint32_t d_in32 = uint32_t(d_in);
+    const int64_t brow = bi * L;                  // first (b, t) row of this batch
+    auto rows_left = [&](int k) -> int { return int(imax(-1, imin(T, t_end - (t_begin + int64_t(k) * T)))); };
+    auto row_off = [&](int k) -> uint32_t {       // element offset of this thread's row in chunk k
+        const int64_t lim = imin(T - 1, L - 1 - (t_begin + int64_t(k) * T));
+        return uint32_t(__umul24(umin(uint32_t(er), uint32_t(imax(lim, 0))), d_in32)) + uint32_t(ech_c);
+    };
+    auto chunk_row = [&](int k) -> int64_t { return brow + imin(t_begin + int64_t(k) * T, L - 1); };
+
     // B/C staging: thread owns tile slots f = m*NT + tid, step f / NP, state f % NP.
-    Span<TIn, V, VEC> su, sd, sz;
-    typename R::type rb[EBC], rc[EBC];
-    auto load_ud = [&](int64_t tc) {
-        const int64_t t = min(tc + er, L - 1);
-        const int64_t e = (bi * L + t) * d_in + ech_c;
-        su.load(u, e, evalid);
-        sd.load(dlt, e, evalid);
+    const uint32_t n32 = uint32_t(n);
+    uint32_t bc_row[EBC], bc_col[EBC];
+#pragma unroll
+    for (int m = 0; m < EBC; m++) {
+        const int f = int(imin(m * NT + tid, T * NP - 1));
+        bc_row[m] = uint32_t(f / NP);
+        bc_col[m] = uint32_t(imin(f % NP, n - 1));
+    }
+    auto load_bc = [&](uint32_t* rb, uint32_t* rc, int k) {
+        const int64_t tcl = imin(t_begin + int64_t(k) * T, L - 1);
+        const uint32_t blim = uint32_t(imax(0, imin(T - 1, L - 1 - tcl)));
+        const TIn* Bc = Bm + (brow + tcl) * n;
+        const TIn* Cc = Cm + (brow + tcl) * n;
 #pragma unroll
         for (int m = 0; m < EBC; m++) {
-            const int f = m * NT + tid;
-            const int64_t tb = min(tc + f / NP, L - 1);
-            const int64_t k = min<int64_t>(f % NP, n - 1);
-            rb[m] = R::load(Bm, (bi * L + tb) * n + k);
-            rc[m] = R::load(Cm, (bi * L + tb) * n + k);
+            const uint32_t o = uint32_t(__umul24(umin(bc_row[m], blim), n32)) + bc_col[m];
+            if constexpr (sizeof(TIn) == 2) {
+                rb[m] = reinterpret_cast<const uint16_t*>(Bc)[o];
+                rc[m] = reinterpret_cast<const uint16_t*>(Cc)[o];
+            } else {
+                rb[m] = __float_as_uint(reinterpret_cast<const float*>(Bc)[o]);
+                rc[m] = __float_as_uint(reinterpret_cast<const float*>(Cc)[o]);
+            }
         }
     };
-    load_ud(t_begin);
-
-    for (int64_t tc = t_begin; tc < t_end; tc += T) {
-        const int nt = int(min<int64_t>(T, t_end - tc));
-        const bool rv = er < nt;
-
-        // Per-element phase 1: step size and delta' u, once per (t, d).
-        float uv[V];
-        {
-            float2 dwv[V];
-#pragma unroll
-            for (int i = 0; i < V; i++) {
-                const bool ok = rv && i < evalid;
-                const float dl = ok ? step_size(sd.f(i), bias_v[i], p.softplus) : 0.0f;
-                uv[i] = ok ? su.f(i) : 0.0f;
-                dwv[i] = make_float2(dl, dl * uv[i]);
-            }
-            float4* dst = reinterpret_cast<float4*>(s_dw + er * 64 + ec);
-#pragma unroll
-            for (int i = 0; i < V / 2; i++) dst[i] = make_float4(dwv[2 * i].x, dwv[2 * i].y, dwv[2 * i + 1].x, dwv[2 * i + 1].y);
-        }
+    auto stage_bc = [&](const uint32_t* rb, const uint32_t* rc, int k) {
+        const int left = rows_left(k);
 #pragma unroll
         for (int m = 0; m < EBC; m++) {
             const int f = m * NT + tid;
-            const int j = f / NP, k = f % NP;
-            const int w = k / NSW, q = k % NSW;
-            const bool ok = k < n;
-            float* dst = s_bc + ((j * S + w) * 2) * NSW + q;
-            dst[0] = ok ? R::f(rb[m]) : 0.0f;
-            dst[NSW] = ok ? R::f(rc[m]) : 0.0f;
+            if ((T * NP) % NT != 0 && f >= T * NP) break;
+            const int j = f / NP, kk = f % NP;
+            const int w = kk / NSW, q = kk % NSW;
+            const bool ok = j < left && kk < n;
+            float* dst = s_bc + (k & 1) * BC_BUF + ((j * S + w) * 2) * NSW + q;
+            dst[0] = ok ? (sizeof(TIn) == 2 ? __uint_as_float(rb[m] << 16) : __uint_as_float(rb[m])) : 0.0f;
+            dst[NSW] = ok ? (sizeof(TIn) == 2 ? __uint_as_float(rc[m] << 16) : __uint_as_float(rc[m])) : 0.0f;
+        }
+    };
+
+    auto load_chunk = [&](Span<TIn, V, VEC>& su, Span<TIn, V, VEC>& sd, int k) {
+        const int64_t base = chunk_row(k) * d_in;
+        const uint32_t off = row_off(k);
+        su.load(u + base, off, evalid);
+        sd.load(dlt + base, off, evalid);
+    };
+    auto load_z = [&](Span<TIn, V, VEC>& zs, int k) { zs.load(zp + chunk_row(k) * d_in, row_off(k), evalid); };
+
+    // Phase 1 of element i of chunk k: (delta', delta' u); returns u via uv.
+    auto phase1 = [&](const Span<TIn, V, VEC>& su, const Span<TIn, V, VEC>& sd, int k, int i, float& uv) {
+        const bool ok = er < rows_left(k) && i < evalid;
+        const float x = sd.f(i) + bias_v[i];
+        const float dl = ok ? (SP ? softplus(x) : x) : 0.0f;
+        uv = ok ? su.f(i) : 0.0f;
+        return make_float2(dl, dl * uv);
+    };
+    auto store_dw = [&](int k, const float2* dwv) {
+#pragma unroll
+        for (int i = 0; i < V; i++) {
+            float* dst = s_dw + (k & 1) * DW_BUF + ((er >> 1) * 64 + ec + i) * 4 + (er & 1) * 2;
+            *reinterpret_cast<float2*>(dst) = dwv[i];
+        }
+    };
+    auto store_y = [&](int k, const float* yv) {
+        if (k >= 0 && er < rows_left(k) && evalid > 0)
+            store_span<TIn, V, VEC>(yp + (brow + t_begin + int64_t(k) * T) * d_in, uint32_t(er) * d_in32 + uint32_t(ech),
+                                    yv, evalid);
+    };
+
+    // Pipeline fill: phase 1 of chunk 0 into LDS; loads of chunk 1 in flight.
+    Span<TIn, V, VEC> su_n, sd_n, su_n2, sd_n2, z_cur, z_prev;
+#pragma unroll
+    for (int i = 0; i < Span<TIn, V, VEC>::NW; i++) z_prev.w[i] = 0u;
+    float uv_prev[V], uv_cur[V], uv_next[V];
+    uint32_t rb_n[EBC], rc_n[EBC], rb_n2[EBC], rc_n2[EBC];
+    {
+        load_chunk(su_n, sd_n, 0);
+        load_bc(rb_n, rc_n, 0);
+        float2 dwv[V];
+#pragma unroll
+        for (int i = 0; i < V; i++) dwv[i] = phase1(su_n, sd_n, 0, i, uv_cur[i]);
+        store_dw(0, dwv);
+        stage_bc(rb_n, rc_n, 0);
+    }
+    load_chunk(su_n, sd_n, 1);
+    load_bc(rb_n, rc_n, 1);
+    if (GATE) load_z(z_cur, 0);
+#pragma unroll
+    for (int i = 0; i < V; i++) uv_prev[i] = 0.0f;
+    __syncthreads();
+
+    for (int c = 0; c < nchunks; c++) {
+        const int64_t tc = t_begin + int64_t(c) * T;
+        // Global loads two chunks ahead and the gate of the next chunk.
+        load_chunk(su_n2, sd_n2, c + 2);
+        load_bc(rb_n2, rc_n2, c + 2);
+        Span<TIn, V, VEC> z_new;
+        if (GATE) load_z(z_new, c + 1);
+
+        // All LDS reads of this chunk, up front.
+        float4 dwq[T / 2];
+        {
+            const float4* src = reinterpret_cast<const float4*>(s_dw + (c & 1) * DW_BUF) + lane;
+#pragma unroll
+            for (int pr = 0; pr < T / 2; pr++) dwq[pr] = src[pr * 64];
+        }
+        float ypv[S][V];
+        {
+            const float* src = s_yp + ((c - 1) & 1) * YP_BUF + er * 64 + ec;
+#pragma unroll
+            for (int w = 0; w < S; w++)
+#pragma unroll
+                for (int i = 0; i < V; i++) ypv[w][i] = src[w * T * 64 + i];
+        }
+
+        float ypart[T];
+        float yout[V];
+        float2 dwn[V];
+        const float* bcw = s_bc + (c & 1) * BC_BUF + wave * 2 * NSW;
+        float4 bcq[D][NR];
+        auto fetch_bc = [&](int j) {
+            const float4* r = reinterpret_cast<const float4*>(bcw + j * S * 2 * NSW);
+#pragma unroll
+            for (int qq = 0; qq < NR; qq++) bcq[j % D][qq] = r[qq];
+        };
+#pragma unroll
+        for (int j = 0; j < D; j++) fetch_bc(j);
+#pragma unroll
+        for (int j = 0; j < T; j++) {
+            const int slot = j % D;
+            const float4 dq = dwq[j / 2];
+            const float dl = (j & 1) ? dq.z : dq.x;
+            const float wv = (j & 1) ? dq.w : dq.y;
+            float bcv[2 * NSW];
+#pragma unroll
+            for (int qq = 0; qq < NR; qq++) {
+                bcv[4 * qq] = bcq[slot][qq].x;
+                bcv[4 * qq + 1] = bcq[slot][qq].y;
+                bcv[4 * qq + 2] = bcq[slot][qq].z;
+                bcv[4 * qq + 3] = bcq[slot][qq].w;
+            }
+            if (j + D < T) fetch_bc(j + D);
+            float acc = 0.0f;
+#pragma unroll
+            for (int q = 0; q < NSW; q++) {
+                const float a = exp2_hw(dl * A2[q]);
+                h[q] = fmaf(a, h[q], wv * bcv[q]);
+                acc = fmaf(bcv[NSW + q], h[q], acc);
+            }
+            ypart[j] = acc;
+            // Interleaved per-element work after every T/V steps.
+            if ((j + 1) % (T / V) == 0) {
+                const int i = (j + 1) / (T / V) - 1;
+                float acc2 = 0.0f;
+#pragma unroll
+                for (int w = 0; w < S; w++) acc2 += ypv[w][i];
+                acc2 = fmaf(Dv[i], uv_prev[i], acc2);
+                if (GATE) acc2 *= silu(z_prev.f(i));
+                yout[i] = acc2;
+                dwn[i] = phase1(su_n, sd_n, c + 1, i, uv_next[i]);
+            }
+        }
+        // LDS writes of this chunk, then the y store of chunk c-1.
+        {
+            float* dst = s_yp + (c & 1) * YP_BUF + wave * T * 64 + lane;
+#pragma unroll
+            for (int j = 0; j < T; j++) dst[j * 64] = ypart[j];
+        }
+        store_dw(c + 1, dwn);
+        stage_bc(rb_n, rc_n, c + 1);
+        store_y(c - 1, yout);
+#pragma unroll
+        for (int i = 0; i < V; i++) {
+            uv_prev[i] = uv_cur[i];
+            uv_cur[i] = uv_next[i];
+        }
+        z_prev = z_cur;
+        z_cur = z_new;
+        su_n = su_n2;
+        sd_n = sd_n2;
+#pragma unroll
+        for (int m = 0; m < EBC; m++) {
+            rb_n[m] = rb_n2[m];
+            rc_n[m] = rc_n2[m];
         }
         __syncthreads();
-
-        // Loads for the next chunk and the gate of this one, in flight during the recurrence.
-        if (gated) {
-            const int64_t t = min(tc + er, L - 1);
-            sz.load(zp, (bi * L + t) * d_in + ech_c, evalid);
+    }
+    // Pipeline drain: phase 2 of the last chunk.
+    {
+        const float* src = s_yp + ((nchunks - 1) & 1) * YP_BUF + er * 64 + ec;
+        float yout[V];
+#pragma unroll
+        for (int i = 0; i < V; i++) {
+            float acc2 = 0.0f;
+#pragma unroll
+            for (int w = 0; w < S; w++) acc2 += src[w * T * 64 + i];
+            acc2 = fmaf(Dv[i], uv_prev[i], acc2);
+            if (GATE) acc2 *= silu(z_prev.f(i));
+            yout[i] = acc2;
         }
-        if (tc + T < t_end) load_ud(tc + T);
-
-        // Recurrence over the chunk: this wave's NSW states of every channel.
-        // (delta', delta' u) and the wave's B/C values are read from LDS
-        // kSeqAhead steps before they are used.  Steps past nt have delta' = 0,
-        // which leaves the state unchanged.
-        {
-            constexpr int D = kSeqAhead;
-            constexpr int NQ = NSW / 4;
-            float2 dw[D];
-            float4 bq[D][NQ], cq[D][NQ];
-            const float* bcw = s_bc + wave * 2 * NSW;
-            auto fetch = [&](int j, int slot) {
-                dw[slot] = s_dw[j * 64 + lane];
-                const float4* r = reinterpret_cast<const float4*>(bcw + j * S * 2 * NSW);
-#pragma unroll
-                for (int qq = 0; qq < NQ; qq++) {
-                    bq[slot][qq] = r[qq];
-                    cq[slot][qq] = r[NQ + qq];
-                }
-            };
-#pragma unroll
-            for (int j = 0; j < D; j++) fetch(j, j);
-            float* ypw = s_yp + wave * T * 64;
-#pragma unroll
-            for (int j = 0; j < T; j++) {
-                const int slot = j % D;
-                const float2 dj = dw[slot];
-                float bv[NSW], cv[NSW];
-#pragma unroll
-                for (int qq = 0; qq < NQ; qq++) {
-                    bv[4 * qq] = bq[slot][qq].x; bv[4 * qq + 1] = bq[slot][qq].y;
-                    bv[4 * qq + 2] = bq[slot][qq].z; bv[4 * qq + 3] = bq[slot][qq].w;
-                    cv[4 * qq] = cq[slot][qq].x; cv[4 * qq + 1] = cq[slot][qq].y;
-                    cv[4 * qq + 2] = cq[slot][qq].z; cv[4 * qq + 3] = cq[slot][qq].w;
-                }
-                if (j + D < T) fetch(j + D, slot);
-                float acc = 0.0f;
-#pragma unroll
-                for (int q = 0; q < NSW; q++) {
-                    const float a = exp2_hw(dj.x * A2[q]);
-                    h[q] = fmaf(a, h[q], dj.y * bv[q]);
-                    acc = fmaf(cv[q], h[q], acc);
-                }
-                ypw[j * 64 + lane] = acc;
-            }
-        }
-        __syncthreads();
-
-        // Per-element phase 2: sum the partial readouts, D skip, gate, store.
-        {
-            float yv[V];
-#pragma unroll
-            for (int i = 0; i < V; i++) yv[i] = 0.0f;
-#pragma unroll
-            for (int w = 0; w < S; w++) {
-                const float4* src = reinterpret_cast<const float4*>(s_yp + (w * T + er) * 64 + ec);
-#pragma unroll
-                for (int i = 0; i < V / 4; i++) {
-                    const float4 v4 = src[i];
-                    yv[4 * i] += v4.x;
-                    yv[4 * i + 1] += v4.y;
-                    yv[4 * i + 2] += v4.z;
-                    yv[4 * i + 3] += v4.w;
-                }
-            }
-#pragma unroll
-            for (int i = 0; i < V; i++) {
-                yv[i] = fmaf(Dv[i], uv[i], yv[i]);
-                if (gated) yv[i] *= silu(sz.f(i));
-            }
-            if (rv && evalid > 0) store_span<TIn, V, VEC>(yp, (bi * L + tc + er) * d_in + ech, yv, evalid);
-        }
+        store_y(nchunks - 1, yout);
     }
 
     if (seg + 1 < p.K) {
@@ -427,7 +541,7 @@ __global__ __launch_bounds__(W * 64) void scan_tpar(const ScanParams p) {
     int parity = 0;
     for (int64_t tc = 0; tc < L; tc += int64_t(W) * TS, parity ^= 1) {
         const int64_t t0 = tc + int64_t(wave) * TS;        // first step of this wave's sub-chunk
-        const int nt = int(max<int64_t>(0, min<int64_t>(TS, L - t0)));
+        const int nt = int(imax(0, imin(TS, L - t0)));
         const int64_t row0 = bi * L + t0;
 
         float uv[TS], dv_[TS];

@@ -29,6 +29,12 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
     return __builtin_bit_cast(uint16_t, h);
 }
 
+// Integer min/max with both operands of one type.  HIP's own min/max also
+// accept mixed argument types, and those overloads compute in double.
+__device__ __forceinline__ int64_t imin(int64_t a, int64_t b) { return a < b ? a : b; }
+__device__ __forceinline__ int64_t imax(int64_t a, int64_t b) { return a > b ? a : b; }
+__device__ __forceinline__ uint32_t umin(uint32_t a, uint32_t b) { return a < b ? a : b; }
+
 template <typename T> struct Elem;
 
 template <> struct Elem<float> {
@@ -55,17 +61,18 @@ template <> struct Raw<float> {
 };
 
 // softplus(x) = log(1 + e^x) = max(x, 0) + log1p(e) with e = exp(-|x|) in (0, 1].
-// log1p(e) is taken from its series e - e^2/2 + e^3/3 - e^4/4 when e < 2^-5
-// (truncation below 2e-7 relative) and as log2(1 + e) * ln 2 otherwise, where
-// 1 + e >= 1.03 so rounding 1 + e costs at most a few ulp.  This keeps small
-// step sizes (x << 0, e.g. softplus(-12) ~ 6e-6) accurate to fp32 rounding,
-// which a plain log(1 + exp(x)) would not.
+// log1p(e) is log2(u) * ln 2 for u = 1 + e rounded to fp32, corrected by the
+// rounding error of u: log(1 + e) = log(u) - log(u / (1 + e)) and
+// log(u / (1 + e)) = ((u - 1) - e) / u to first order, where (u - 1) - e is
+// exact (Sterbenz) and dropping the division by u in [1, 2] changes the
+// result by less than 2^-24 relative.  This keeps small step sizes
+// (x << 0, e.g. softplus(-12) ~ 6e-6) accurate to a few ulp, which a plain
+// log(1 + exp(x)) would not; it costs one exp2 and one log2.
 __device__ __forceinline__ float softplus(float x) {
     const float e = exp2_hw(-fabsf(x) * kLog2e);
-    const float series = e * fmaf(e, fmaf(e, fmaf(e, -0.25f, 1.0f / 3.0f), -0.5f), 1.0f);
-    const float direct = log2_hw(1.0f + e) * kLn2;
-    const float r = e < 0.03125f ? series : direct;
-    return fmaxf(x, 0.0f) + r;
+    const float uu = 1.0f + e;
+    const float c = (uu - 1.0f) - e;
+    return fmaxf(x, 0.0f) + fmaf(log2_hw(uu), kLn2, -c);
 }
 
 // silu(z) = z / (1 + e^-z); for z -> -inf the reciprocal of +inf is 0.

@@ -6,8 +6,12 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
 #include <cstdlib>
 #include <cstring>
+#include <map>
+#include <mutex>
+#include <utility>
 
 #include "ss_scan.h"
 #include "scan_kernels.h"
@@ -23,6 +27,10 @@ using ss::StepParams;
 constexpr int kMaxSegments = 16;
 constexpr int64_t kMaxElems = int64_t(1) << 46;   // keeps every index product far from int64 overflow
 constexpr int kTparWaves = 8;
+// Largest grid in workgroups of 512 threads: a launch holds at most 2^32 - 1 work-items.
+constexpr int64_t kMaxWorkgroups = (int64_t(1) << 23) - 1;
+// Largest b * d_in of the decode step (up to 16 threads per channel in one launch).
+constexpr int64_t kMaxStepChannels = (int64_t(1) << 28) - 1;
 
 // ----------------------------------------------------------------------------- validation helpers
 
@@ -57,10 +65,14 @@ struct SeqShape {
     int NSW;   // states per wave
 };
 
+// Waves per workgroup and states per wave.  Every shape has 4 or 8 waves, so
+// the per-element work of a chunk is spread over 256 or 512 threads.
+// SS_SCAN_WAVES=4 selects the 4-wave shape at 9 <= n <= 16 (tests, tuning).
 SeqShape seq_shape(int64_t n) {
-    if (n <= 4) return {1, 4};
-    if (n <= 8) return {2, 4};
-    if (n <= 16) return {4, 4};
+    const char* w = std::getenv("SS_SCAN_WAVES");
+    const int want = w ? int(std::strtol(w, nullptr, 10)) : 0;
+    if (n <= 8) return {4, 2};
+    if (n <= 16) return want == 4 ? SeqShape{4, 4} : SeqShape{8, 2};
     if (n <= 32) return {8, 4};
     return {8, 8};
 }
@@ -89,26 +101,67 @@ SeqWorkspace seq_workspace(int64_t b, int64_t L, int64_t d_in, int64_t n) {
     return w;
 }
 
+// One chunk of B (or C) must be addressable with 32-bit offsets.
+bool bc_rows_fit(int64_t L, int64_t n) { return L >= 1 && n * ss::kSeqChunk < (int64_t(1) << 24); }
+
 int device_cus() {
-    static int cached[64];
+    static std::atomic<int> cached[64];
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0) return -1;
-    if (dev < 64 && cached[dev] > 0) return cached[dev];
+    if (dev < 64 && cached[dev].load(std::memory_order_relaxed) > 0) return cached[dev].load(std::memory_order_relaxed);
     int cus = 0;
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return -1;
-    if (dev < 64) cached[dev] = cus;
+    if (dev < 64) cached[dev].store(cus, std::memory_order_relaxed);
     return cus;
 }
 
-// Number of segments along L for scan_seq.  SS_SCAN_SEGMENTS overrides (tests);
-// by default the whole length is one segment.
-int choose_segments(int64_t L, int T) {
-    int64_t K = 1;
+// Workgroups of `fn` that fit on one compute unit at once (cached per kernel
+// and device; 0 when unknown).
+int resident_per_cu(const void* fn, int threads, size_t lds) {
+    static std::mutex mu;
+    static std::map<std::pair<const void*, int>, int> cache;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return 0;
+    const auto key = std::make_pair(fn, dev);
+    {
+        std::lock_guard<std::mutex> g(mu);
+        const auto it = cache.find(key);
+        if (it != cache.end()) return it->second;
+    }
+    int nb = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, fn, threads, lds) != hipSuccess) nb = 0;
+    std::lock_guard<std::mutex> g(mu);
+    cache[key] = nb;
+    return nb;
+}
+
+// Number of segments K along L for scan_seq.  Pieces (segment, group) are
+// taken in ticket order, segment-major, by `slots` resident workgroups.  When
+// the G groups fill the slots at least once, a piece's predecessor always ran
+// in an earlier round, so with pieces of equal length the time is
+// ceil(G K / slots) rounds of 1/K of the work each, plus a fixed cost per piece
+// (pipeline fill and drain, state handoff) taken as 2% of a whole-length
+// piece.  K minimises that.  With fewer groups than slots the segments of a
+// group would only run one after another, so K = 1.  Every segment keeps at
+// least 4 chunks.  SS_SCAN_SEGMENTS overrides (tests, tuning).
+int choose_segments(int64_t G, int64_t L, int T, int64_t slots) {
+    const int64_t max_k = std::max<int64_t>(1, std::min<int64_t>(kMaxSegments, L / (4 * int64_t(T))));
     if (const char* e = std::getenv("SS_SCAN_SEGMENTS")) {
         const long v = std::strtol(e, nullptr, 10);
-        if (v >= 1) K = std::min<int64_t>(std::min<int64_t>(v, kMaxSegments), std::max<int64_t>(1, (L + T - 1) / T));
+        if (v >= 1) return int(std::min<int64_t>(std::min<int64_t>(v, kMaxSegments), std::max<int64_t>(1, (L + T - 1) / T)));
     }
-    return int(K);
+    if (slots <= 0 || G < slots) return 1;
+    int best = 1;
+    double best_t = 0.0;
+    for (int64_t k = 1; k <= max_k; k++) {
+        const double rounds = double((G * k + slots - 1) / slots);
+        const double t = rounds * (1.0 / double(k) + 0.02);
+        if (k == 1 || t < best_t * (1.0 - 1e-9)) {
+            best = int(k);
+            best_t = t;
+        }
+    }
+    return best;
 }
 
 template <typename TIn, int S, int NSW>
@@ -116,10 +169,27 @@ int launch_seq(ScanParams p, void* ws, size_t ws_bytes, hipStream_t st) {
     constexpr int T = ss::kSeqChunk;
     constexpr int V = T / S;
     constexpr size_t lds = ss::seq_lds_bytes<S, NSW>();
+    static_assert(lds <= 160 * 1024, "LDS of one workgroup");
     const int64_t G = p.b * p.nblk_d;
     const SeqWorkspace w = seq_workspace(p.b, p.L, p.d_in, p.n);
     if (!ws || ws_bytes < w.total) return SS_ERR_WORKSPACE;
-    int K = choose_segments(p.L, T);
+
+    const size_t va = std::min<size_t>(16, V * sizeof(TIn));
+    const bool vec = p.d_in % V == 0 && aligned(p.u, va) && aligned(p.delta, va) && aligned(p.y, va) &&
+                     (!p.z || aligned(p.z, va));
+    const int variant = (vec ? 4 : 0) | (p.softplus ? 2 : 0) | (p.z ? 1 : 0);
+    using Kern = void (*)(ScanParams);
+    static constexpr Kern kernels[8] = {
+        ss::scan_seq<TIn, S, NSW, false, false, false>, ss::scan_seq<TIn, S, NSW, false, false, true>,
+        ss::scan_seq<TIn, S, NSW, false, true, false>,  ss::scan_seq<TIn, S, NSW, false, true, true>,
+        ss::scan_seq<TIn, S, NSW, true, false, false>,  ss::scan_seq<TIn, S, NSW, true, false, true>,
+        ss::scan_seq<TIn, S, NSW, true, true, false>,   ss::scan_seq<TIn, S, NSW, true, true, true>};
+    const Kern kern = kernels[variant];
+
+    const int cus = device_cus();
+    const int per_cu = resident_per_cu(reinterpret_cast<const void*>(kern), S * 64, lds);
+    int K = choose_segments(G, p.L, T, int64_t(std::max(cus, 0)) * per_cu);
+    while (K > 1 && G * K > kMaxWorkgroups) K--;   // a launch holds fewer than 2^32 work-items
     int64_t Lseg = (p.L + K - 1) / K;
     Lseg = (Lseg + T - 1) / T * T;
     K = int((p.L + Lseg - 1) / Lseg);
@@ -134,23 +204,15 @@ int launch_seq(ScanParams p, void* ws, size_t ws_bytes, hipStream_t st) {
         hipLaunchKernelGGL(ss::scan_ctl_reset, dim3(rb), dim3(256), 0, st, p.ctl, int64_t(words));
         if (hipGetLastError() != hipSuccess) return SS_ERR_HIP;
     }
-    const size_t va = std::min<size_t>(16, V * sizeof(TIn));
-    const bool vec = p.d_in % V == 0 && aligned(p.u, va) && aligned(p.delta, va) && aligned(p.y, va) &&
-                     (!p.z || aligned(p.z, va));
-    const dim3 grid(unsigned(G * K)), block(S * 64);
-    if (vec)
-        hipLaunchKernelGGL((ss::scan_seq<TIn, S, NSW, true>), grid, block, lds, st, p);
-    else
-        hipLaunchKernelGGL((ss::scan_seq<TIn, S, NSW, false>), grid, block, lds, st, p);
+    hipLaunchKernelGGL(kern, dim3(unsigned(G * K)), dim3(S * 64), lds, st, p);
     return hipGetLastError() == hipSuccess ? SS_OK : SS_ERR_HIP;
 }
 
 template <typename TIn>
 int dispatch_seq(const ScanParams& p, void* ws, size_t ws_bytes, hipStream_t st) {
     const SeqShape sh = seq_shape(p.n);
-    if (sh.S == 1) return launch_seq<TIn, 1, 4>(p, ws, ws_bytes, st);
-    if (sh.S == 2) return launch_seq<TIn, 2, 4>(p, ws, ws_bytes, st);
-    if (sh.S == 4) return launch_seq<TIn, 4, 4>(p, ws, ws_bytes, st);
+    if (sh.S == 4) return sh.NSW == 2 ? launch_seq<TIn, 4, 2>(p, ws, ws_bytes, st) : launch_seq<TIn, 4, 4>(p, ws, ws_bytes, st);
+    if (sh.NSW == 2) return launch_seq<TIn, 8, 2>(p, ws, ws_bytes, st);
     if (sh.NSW == 4) return launch_seq<TIn, 8, 4>(p, ws, ws_bytes, st);
     return launch_seq<TIn, 8, 8>(p, ws, ws_bytes, st);
 }
@@ -186,7 +248,8 @@ SS_EXPORT const char* ss_status_string(int status) {
 
 SS_EXPORT size_t ss_scan_fwd_workspace_bytes(int64_t b, int64_t L, int64_t d_in, int64_t n, int dtype) {
     if (dtype != SS_F32 && dtype != SS_BF16) return 0;
-    if (!sizes_ok(b, L, d_in) || n <= 0 || n > SS_MAX_STATE) return 0;
+    if (!sizes_ok(b, L, d_in) || n <= 0 || n > SS_MAX_STATE || d_in > SS_MAX_CHANNELS) return 0;
+    if (!bc_rows_fit(L, n) || b * ((d_in + 63) / 64) > kMaxWorkgroups) return 0;
     // Sized for scan_seq with the most segments; scan_tpar (n <= 2) needs none
     // but the same size is asked for so that either kernel can be chosen.
     return seq_workspace(b, L, d_in, n).total;
@@ -197,9 +260,10 @@ SS_EXPORT int ss_scan_fwd(const void* u, const void* delta, const float* A_log, 
                           float* last_state, int64_t b, int64_t L, int64_t d_in, int64_t n, int dtype,
                           void* workspace, size_t workspace_bytes, void* stream) {
     if (!u || !delta || !A_log || !B || !C || !D || !y) return SS_ERR_NULL;
-    if (!sizes_ok(b, L, d_in) || n <= 0) return SS_ERR_SHAPE;
+    if (!sizes_ok(b, L, d_in) || n <= 0 || d_in > SS_MAX_CHANNELS) return SS_ERR_SHAPE;
     if (dtype != SS_F32 && dtype != SS_BF16) return SS_ERR_DTYPE;
     if (n > SS_MAX_STATE) return SS_ERR_UNSUPPORTED;
+    if (!bc_rows_fit(L, n) || b * ((d_in + 63) / 64) > kMaxWorkgroups) return SS_ERR_SHAPE;
     const size_t es = elem_size(dtype);
     for (const void* p : {u, delta, B, C, z, static_cast<const void*>(y)})
         if (p && !aligned(p, es)) return SS_ERR_ALIGN;
@@ -255,7 +319,7 @@ SS_EXPORT int ss_state_update(float* state, const void* x, const void* dt, const
                               const void* C, const float* D, const void* z, const float* dt_bias, int dt_softplus,
                               void* y, int64_t b, int64_t d_in, int64_t n, int dtype, void* stream) {
     if (!state || !x || !dt || !A_log || !B || !C || !D || !y) return SS_ERR_NULL;
-    if (!sizes_ok(b, d_in, 1) || n <= 0 || !sizes_ok(b, d_in, n)) return SS_ERR_SHAPE;
+    if (!sizes_ok(b, d_in, 1) || n <= 0 || !sizes_ok(b, d_in, n) || b * d_in > kMaxStepChannels) return SS_ERR_SHAPE;
     if (dtype != SS_F32 && dtype != SS_BF16) return SS_ERR_DTYPE;
     if (n > SS_MAX_STATE) return SS_ERR_UNSUPPORTED;
     const size_t es = elem_size(dtype);
