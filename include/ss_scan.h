@@ -99,7 +99,7 @@ size_t ss_scan_fwd_workspace_bytes(int64_t b, int64_t L, int64_t d_in, int64_t n
  *                bytes (may be NULL when that is 0).  Its contents need no
  *                initialisation and are scratch after the call.
  * Any n in 1..SS_MAX_STATE, d_in in 1..SS_MAX_CHANNELS and b, L >= 1 with
- * b * L * d_in <= 2^46 and b * ceil(d_in / 64) < 2^23 are
+ * b * L * d_in <= 2^46, L < 2^31 - 1024 and b * ceil(d_in / 64) < 2^22 are
  * accepted (no tile multiples are required); other sizes give SS_ERR_SHAPE.
  * Returns an ss_status.
  */

@@ -46,7 +46,7 @@ class SSError(RuntimeError):
 
 def _load() -> ctypes.CDLL:
     if not os.path.exists(LIBRARY):
-        raise ImportError(f"{LIBRARY} is not built; run `python -m selective_state_space_softplus_amd.build` "
+        raise ImportError(f"{LIBRARY} is not built; run `python selective_state_space_softplus_amd/build.py` "
                           "(or __graft_entry__.build())")
     lib = ctypes.CDLL(LIBRARY)
     P, I64, I = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int

@@ -1,6 +1,8 @@
 """Build libss_scan.so (the HIP kernels and the C ABI) in-tree for gfx950.
 
-    python -m selective_state_space_softplus_amd.build
+    python selective_state_space_softplus_amd/build.py
+
+(run as a script: importing the package loads the library this builds).
 
 Packed-fp32 VALU instructions are switched off for all device code.
 """

@@ -32,6 +32,8 @@
 //   buys when b * d_in is small.
 #pragma once
 
+#include <type_traits>
+
 #include "ss_device.h"
 
 namespace ss {
@@ -60,71 +62,49 @@ struct ScanParams {
 constexpr int kFlagOffset = 64;
 constexpr int kSpinLimit = 1 << 25;   // ~2 s of s_sleep before a wait gives up and flags an error
 
-// Chunk length of scan_seq: the workgroup advances T steps per barrier.
-constexpr int kSeqChunk = 16;
-
-// Steps of B and C a wave reads ahead of the step it computes.
+// Steps of (delta', delta' u) a recurrence wave reads from LDS ahead of the
+// step it computes.
 constexpr int kSeqAhead = 4;
 
-// LDS of scan_seq, double-buffered by chunk parity: (delta', delta' u) per
-// (t, d), two steps interleaved per channel; the S partial readouts per
-// (t, d); B and C of the chunk as fp32, grouped per wave; then 16 bytes for
-// the ticket.  It is one dynamic block that starts 16-byte aligned: a static
-// __shared__ variable would shift it by its size and leave the 8- and 16-byte
+// Element waves per workgroup of scan_seq (one per SIMD).
+constexpr int kSeqElemWaves = 4;
+
+// Byte layout of the LDS of scan_seq<T, SC recurrence waves, NP padded
+// states, ES-byte inputs>.  All rings are indexed by chunk % 3 (partial
+// readouts: chunk % 2).  Raw inputs arrive by direct-to-LDS loads: a u, delta
+// or z tile holds T rows of 64 channels, ES bytes per element when WIDE
+// (16-byte loads) else 4 bytes per element (one element load per lane, which
+// fills a 4-byte slot); B and C hold T * NP consecutive elements of their
+// (b, L, n) array in 4-byte slots.  The block starts 16-byte aligned: a
+// static __shared__ variable would shift it by its size and leave the wide
 // LDS accesses misaligned, which the LDS serialises.
-template <int S, int NSW>
-constexpr size_t seq_lds_bytes() {
-    return 2 * size_t(kSeqChunk) * (64 * (sizeof(float2) + S * sizeof(float)) + 2 * S * NSW * sizeof(float)) + 16;
-}
-
-// V consecutive input elements of one row, kept as the raw 32-bit words that
-// were loaded (one wide load when VEC, else V bounds-checked element loads,
-// past-the-end elements reading as 0) and widened to fp32 only when used, so
-// a load stays in flight until its value is needed.
-template <typename TIn, int V, bool VEC>
-struct Span {
-    static constexpr bool kHalf = sizeof(TIn) == 2;
-    static constexpr int NW = VEC ? (V * int(sizeof(TIn)) + 3) / 4 : V;
-    uint32_t w[NW];
-
-    __device__ __forceinline__ void load(const TIn* base, uint32_t e, int valid) {
-        const TIn* p = base;
-        if constexpr (VEC) {
-            constexpr int BYTES = V * int(sizeof(TIn));
-            if constexpr (BYTES == 4) {
-                w[0] = *reinterpret_cast<const uint32_t*>(p + e);
-            } else if constexpr (BYTES == 8) {
-                const uint2 v = *reinterpret_cast<const uint2*>(p + e);
-                w[0] = v.x;
-                w[1] = v.y;
-            } else {
-                static_assert(BYTES % 16 == 0, "wide loads of 4, 8 or 16k bytes");
-#pragma unroll
-                for (int c = 0; c < BYTES / 16; c++) {
-                    const uint4 v = reinterpret_cast<const uint4*>(p + e)[c];
-                    w[4 * c] = v.x;
-                    w[4 * c + 1] = v.y;
-                    w[4 * c + 2] = v.z;
-                    w[4 * c + 3] = v.w;
-                }
-            }
-        } else {
-#pragma unroll
-            for (int i = 0; i < V; i++) {
-                if constexpr (kHalf)
-                    w[i] = i < valid ? uint32_t(reinterpret_cast<const uint16_t*>(p)[e + i]) : 0u;
-                else
-                    w[i] = i < valid ? __float_as_uint(reinterpret_cast<const float*>(p)[e + i]) : 0u;
-            }
-        }
-    }
-    __device__ __forceinline__ float f(int i) const {
-        if constexpr (!kHalf) return __uint_as_float(w[i]);
-        else if constexpr (!VEC) return __uint_as_float(w[i] << 16);
-        else return (i & 1) ? __uint_as_float(w[i / 2] & 0xffff0000u) : __uint_as_float(w[i / 2] << 16);
-    }
+template <int T, int SC, int NP, int ES, bool WIDE>
+struct SeqLds {
+    static constexpr int XES = WIDE ? ES : 4;                  // bytes per raw u/delta/z element
+    static constexpr int DW = T * 64 * 8;                      // (delta', delta' u) of a chunk
+    static constexpr int YP = SC * T * 64 * 4;                 // partial readouts of a chunk
+    static constexpr int BC = T * 2 * NP * 4;                  // B and C of a chunk as fp32, grouped per wave
+    static constexpr int RX = T * 64 * XES;                    // raw u, delta or z tile
+    static constexpr int RBC = T * NP * 4;                     // raw B or C block
+    static constexpr int off_dw = 0;
+    static constexpr int off_yp = off_dw + 3 * DW;
+    static constexpr int off_bc = off_yp + 2 * YP;
+    static constexpr int off_ru = off_bc + 3 * BC;             // [3][u, delta] tiles
+    static constexpr int off_rbc = off_ru + 6 * RX;            // [3][B, C] blocks
+    static constexpr int off_rz = off_rbc + 6 * RBC;           // [3] z tiles
+    static constexpr int off_ticket = off_rz + 3 * RX;
+    static constexpr int bytes = off_ticket + 16;
 };
 
+// Chunk length of scan_seq: 16 steps, or 8 where the LDS of 16 would not fit
+// (raw tiles of 4-byte slots with n > 32).
+template <typename TIn, int SC, int NSW, bool WIDE>
+constexpr int seq_chunk() {
+    return SeqLds<16, SC, SC * NSW, int(sizeof(TIn)), WIDE>::bytes <= 160 * 1024 ? 16 : 8;
+}
+
+// VEC-style output store of V consecutive elements (one wide store), or V
+// element stores of which the first `valid` happen.
 template <typename TIn, int V, bool VEC>
 __device__ __forceinline__ void store_span(TIn* p, uint32_t e, const float* y, int valid) {
     if constexpr (VEC && sizeof(TIn) == 2) {
@@ -156,90 +136,147 @@ __device__ __forceinline__ void store_span(TIn* p, uint32_t e, const float* y, i
     }
 }
 
-// VEC: d_in is a multiple of the per-thread span V and the tensors are
-// aligned for it, so the per-element phases use wide loads and stores.
+// V consecutive raw elements of one row of a u/delta/z tile in LDS, widened
+// to fp32.  WIDE tiles pack ES-byte elements; the others hold one element per
+// 4-byte slot (a bf16 element in its low half).
+template <typename TIn, int V, bool WIDE>
+struct RawRow {
+    static constexpr bool kHalf = sizeof(TIn) == 2;
+    static constexpr int NW = (WIDE && kHalf) ? V / 2 : V;
+    uint32_t w[NW];
+    __device__ __forceinline__ void read(const char* tile, int row, int col) {
+        constexpr int XES = WIDE ? int(sizeof(TIn)) : 4;
+        const char* src = tile + (row * 64 + col) * XES;
+        if constexpr (NW == 1) {
+            w[0] = *reinterpret_cast<const uint32_t*>(src);
+        } else if constexpr (NW == 2) {
+            const uint2 v = *reinterpret_cast<const uint2*>(src);
+            w[0] = v.x;
+            w[1] = v.y;
+        } else {
+#pragma unroll
+            for (int c = 0; c < NW / 4; c++) {
+                const uint4 v = reinterpret_cast<const uint4*>(src)[c];
+                w[4 * c] = v.x;
+                w[4 * c + 1] = v.y;
+                w[4 * c + 2] = v.z;
+                w[4 * c + 3] = v.w;
+            }
+        }
+    }
+    __device__ __forceinline__ float f(int i) const {
+        if constexpr (!kHalf) return __uint_as_float(w[i]);
+        else if constexpr (!WIDE) return __uint_as_float(w[i] << 16);
+        else return (i & 1) ? __uint_as_float(w[i / 2] & 0xffff0000u) : __uint_as_float(w[i / 2] << 16);
+    }
+};
+
+// scan_seq: WIDE = d_in * sizeof(TIn) is a multiple of 16 and u, delta, z
+// and y are aligned for 16-byte accesses, so u/delta/z tiles arrive by
+// 16-byte direct-to-LDS loads and y leaves by wide stores.
 // SP: delta' = softplus(delta + bias) (else delta + bias).  GATE: z is given.
 //
-// One barrier per chunk c of T steps.  Between two barriers every wave
-//   - reads (delta', delta' u) of chunk c for its 64 lanes from LDS, and the
-//     partial readouts of chunk c-1, all up front;
-//   - runs the recurrence of chunk c from registers, reading its B and C
-//     values of each step from LDS kSeqAhead steps ahead (the only LDS
-//     accesses inside the loop, so every wait is for a read issued steps
-//     earlier);
-//   - interleaves the per-element work: phase 2 of chunk c-1 (partial sums,
-//     D skip, gate) and phase 1 of chunk c+1 (step size, delta' u), whose
-//     global loads were issued two chunks earlier;
-//   - then writes its partial readouts of chunk c, the phase-1 results and the
-//     B, C values of chunk c+1 to LDS, and stores y of chunk c-1.
-// LDS buffers alternate with the chunk parity, so no buffer is written and
-// read by different waves between two barriers.
-template <typename TIn, int S, int NSW, bool VEC, bool SP, bool GATE>
-__global__ __launch_bounds__(S * 64) void scan_seq(const ScanParams p) {
-    constexpr int T = kSeqChunk;
-    constexpr int NT = S * 64;                     // threads
-    constexpr int V = T / S;                       // consecutive channels per thread in the per-element phases
-    constexpr int TPR = 64 / V;                    // threads per step row
-    constexpr int DW_BUF = T * 64 * 2;             // floats per (delta', delta' u) buffer
-    constexpr int YP_BUF = S * T * 64;             // floats per partial-readout buffer
-    constexpr int NP = S * NSW;                    // states per channel, padded
-    constexpr int BC_BUF = T * 2 * NP;             // floats per B/C buffer
-    constexpr int EBC = (T * NP + NT - 1) / NT;    // B (and C) values each thread stages per chunk
-    constexpr int D = kSeqAhead;
-    constexpr int NR = NSW / 2;                    // float4 reads per step: NSW values of B then NSW of C
-    static_assert(T % S == 0 && 64 % V == 0 && NT / TPR == T, "thread tiling of a chunk");
-    static_assert(NSW % 2 == 0 && T % 2 == 0 && T % D == 0, "tiles split evenly");
+// Waves 0 .. SC-1 ("recurrence waves") each hold NSW states of the 64
+// channels and run nothing but the recurrence.  Waves SC .. SC+3 ("element
+// waves") do the per-element work: step size and delta' u, the sum of the SC
+// partial readouts, the D skip, the gate, and the stores of y.  The last wave
+// (the "loader") streams u, delta, z, B and C into LDS with direct-to-LDS
+// loads and waits for them with explicit counts, so no wave ever holds data
+// that is still on its way from memory and no barrier waits for global
+// memory.  Each SIMD gets the same mix of recurrence and element waves.
+//
+// Software pipeline, one barrier per chunk c of T steps.  Between two barriers
+//   - every recurrence wave runs chunk c from registers: the (delta', delta' u)
+//     pairs and B, C values of each step are read from LDS a few steps ahead
+//     (near the end of the chunk these reads run into chunk c+1, whose LDS data
+//     was written two chunks earlier), and its partial readout of each step
+//     goes to LDS as soon as it is known;
+//   - the element waves finish chunk c-1 and prepare chunk c+2 from its raw
+//     tiles (loaded two chunks earlier);
+//   - the loader issues the loads of chunk c+4 (u, delta, B, C) and of chunk
+//     c+1 (z), then waits until those of chunk c+3 and c are complete.
+template <typename TIn, int SC, int NSW, int T, bool WIDE, bool SP, bool GATE>
+__global__ __launch_bounds__((SC + kSeqElemWaves + 1) * 64) void scan_seq(const ScanParams p) {
+    constexpr int P = kSeqElemWaves;
+    constexpr int ES = int(sizeof(TIn));
+    constexpr int NE = P * 64;                     // element threads
+    constexpr int V = T / P;                       // consecutive channels per element thread
+    constexpr int TPR = 64 / V;                    // element threads per step row
+    constexpr int NP = SC * NSW;                   // states per channel, padded
+    using Lds = SeqLds<T, SC, NP, ES, WIDE>;
+    constexpr int EBC = (T * NP + NE - 1) / NE;    // B (and C) values each element thread stages per chunk
+    constexpr int PA = kSeqAhead / 2;              // step pairs of (delta', delta' u) read ahead
+    constexpr int RDW = 4;                         // register ring of step pairs (divides T / 2)
+    constexpr int NR = NSW / 2;                    // float4 per step: NSW values of B then NSW of C
+    constexpr int RBC = NR >= 4 ? 2 : 4;           // register ring of B, C steps (divides T)
+    constexpr int LB = RBC - 1;                    // steps of B, C read ahead
+    // Loads the loader issues per chunk: u and delta, B and C, z.
+    constexpr int XI = WIDE ? T * 64 * ES / 1024 : T;          // per u, delta or z tile
+    constexpr int BI = T * NP / 64;                            // per B or C block
+    constexpr int N_UDBC = 2 * XI + 2 * BI, N_Z = GATE ? XI : 0;
+    static_assert(T % P == 0 && 64 % V == 0 && NE / TPR == T, "thread tiling of a chunk");
+    static_assert(NSW % 2 == 0 && (T / 2) % RDW == 0 && T % RBC == 0 && PA + 1 <= RDW, "tiles split evenly");
+    static_assert((T * NP) % 64 == 0 && (!WIDE || (T * 64 * ES) % 1024 == 0), "whole loads per tile");
+    static_assert(Lds::bytes <= 160 * 1024, "LDS of one workgroup");
     extern __shared__ __align__(16) float smem[];
-    float* s_dw = smem;                            // [2][T/2][64][4]: (delta'_j, w_j, delta'_j+1, w_j+1)
-    float* s_yp = smem + 2 * DW_BUF;               // [2][S][T][64]
-    float* s_bc = s_yp + 2 * YP_BUF;               // [2][T][S][2][NSW]
-    int& s_ticket = *reinterpret_cast<int*>(s_bc + 2 * BC_BUF);
-    const TIn* __restrict__ Bm = static_cast<const TIn*>(p.B);
-    const TIn* __restrict__ Cm = static_cast<const TIn*>(p.C);
-
-    const TIn* __restrict__ u = static_cast<const TIn*>(p.u);
-    const TIn* __restrict__ dlt = static_cast<const TIn*>(p.delta);
-    const TIn* __restrict__ zp = static_cast<const TIn*>(p.z);
-    TIn* __restrict__ yp = static_cast<TIn*>(p.y);
+    char* const lds = reinterpret_cast<char*>(smem);
+    float* s_dw = reinterpret_cast<float*>(lds + Lds::off_dw);   // [3][T/2][64][4]: (delta'_j, w_j, delta'_j+1, w_j+1)
+    float* s_yp = reinterpret_cast<float*>(lds + Lds::off_yp);   // [2][SC][T][64]
+    float* s_bc = reinterpret_cast<float*>(lds + Lds::off_bc);   // [3][T][SC][2][NSW]
+    int& s_ticket = *reinterpret_cast<int*>(lds + Lds::off_ticket);
+    constexpr int DW_BUF = Lds::DW / 4, YP_BUF = Lds::YP / 4, BC_BUF = Lds::BC / 4;   // floats
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int64_t L = p.L, d_in = p.d_in, n = p.n;
-    const int64_t G = p.b * p.nblk_d;
+    const bool rec = wave < SC;                    // uniform per wave
+    const bool loader = wave == SC + P;
+    // The host keeps L < 2^31, d_in < 2^24, n <= 64 and G * K < 2^22, so every
+    // per-segment index below fits 32 bits; element offsets of whole rows are
+    // formed in 64 bits.
+    const int L = int(p.L), d_in = int(p.d_in), n = int(p.n);
+    const int G = int(p.b) * p.nblk_d;
 
     int ticket;
     if (p.K == 1) {
         ticket = blockIdx.x;
     } else {
-        if (tid == 0) s_ticket = atomicAdd(p.ctl, 1u);
+        if (tid == 0) s_ticket = int(atomicAdd(p.ctl, 1u));
         __syncthreads();
-        ticket = __builtin_amdgcn_readfirstlane(s_ticket);
+        ticket = s_ticket;
     }
-    const int64_t seg = ticket / G;
-    const int64_t g = ticket - seg * G;
-    const int64_t bi = g / p.nblk_d;
-    const int64_t dbase = (g - bi * p.nblk_d) * 64;
-    const int64_t d = dbase + lane;               // channel of this lane in the recurrence
+    ticket = __builtin_amdgcn_readfirstlane(ticket);
+    int seg = 0, g = ticket;
+    while (g >= G) {                               // at most 16 rounds, uniform
+        g -= G;
+        seg++;
+    }
+    const int bi = __builtin_amdgcn_readfirstlane(g / p.nblk_d);
+    const int dbase = __builtin_amdgcn_readfirstlane((g - bi * p.nblk_d) * 64);
+    const int t_begin = seg * int(p.Lseg);
+    const int t_end = min(L, t_begin + int(p.Lseg));
+    const int nchunks = (t_end - t_begin + T - 1) / T;
+    const int nch3 = (nchunks + 2) / 3 * 3;       // chunks the loop runs (past the end: empty)
+
+    // Recurrence waves: lane = channel d, states n0 .. n0+NSW.
+    const int d = dbase + lane;
     const bool dv = d < d_in;
-    const int64_t t_begin = seg * p.Lseg;
-    const int64_t t_end = imin(L, t_begin + p.Lseg);
-    const int nchunks = int((t_end - t_begin + T - 1) / T);
     const int n0 = wave * NSW;
-
-    // Per-element phases: thread owns step row er of a chunk, channels ec .. ec+V.
-    const int er = tid / TPR;
-    const int ec = (tid - er * TPR) * V;
-    const int64_t ech = dbase + ec;
-    const int evalid = int(imax(0, imin(V, d_in - ech)));
-    const int64_t ech_c = evalid > 0 ? ech : 0;   // loads of an empty span stay in bounds
-
     float A2[NSW], h[NSW];
 #pragma unroll
     for (int q = 0; q < NSW; q++) {
-        A2[q] = (dv && n0 + q < n) ? a2_from_alog(p.A_log[d * n + n0 + q]) : 0.0f;
+        A2[q] = (rec && dv && n0 + q < n) ? a2_from_alog(p.A_log[d * n + n0 + q]) : 0.0f;
         h[q] = 0.0f;
     }
+
+    // Element waves: thread owns step row er of a chunk, channels ec .. ec+V.
+    const bool elem = !rec && !loader;
+    const int etid = elem ? tid - SC * 64 : 0;
+    const int er = etid / TPR;
+    const int ec = (etid - er * TPR) * V;
+    const int ech = dbase + ec;
+    const int evalid = elem ? max(0, min(V, d_in - ech)) : 0;
+    const uint32_t off_el = uint32_t(er) * uint32_t(d_in) + uint32_t(evalid > 0 ? ech : 0);
     float Dv[V], bias_v[V];
 #pragma unroll
     for (int i = 0; i < V; i++) {
@@ -262,168 +299,206 @@ __global__ __launch_bounds__(S * 64) void scan_seq(const ScanParams p) {
         }
         __syncthreads();
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-        const float* src = p.handoff + ((seg - 1) * G + g) * n * 64;
+        if (rec) {
+            const float* src = p.handoff + (int64_t(seg - 1) * G + g) * n * 64;
 #pragma unroll
-        for (int q = 0; q < NSW; q++)
-            if (n0 + q < n) h[q] = src[(n0 + q) * 64 + lane];
+            for (int q = 0; q < NSW; q++)
+                if (n0 + q < n) h[q] = src[(n0 + q) * 64 + lane];
+        }
     }
 
-    // Address arithmetic: uniform 64-bit chunk bases (scalar unit) plus
-    // per-thread 32-bit offsets; rows past the end of L are clamped to the
-    // last row (those values are masked and never stored).  The host keeps
-    // d_in < 2^24 and T * d_in below 2^31.
-    const uint32_t d_in32 = uint32_t(d_in);
-    const int64_t brow = bi * L;                  // first (b, t) row of this batch
-    auto rows_left = [&](int k) -> int { return int(imax(-1, imin(T, t_end - (t_begin + int64_t(k) * T)))); };
-    auto row_off = [&](int k) -> uint32_t {       // element offset of this thread's row in chunk k
-        const int64_t lim = imin(T - 1, L - 1 - (t_begin + int64_t(k) * T));
-        return uint32_t(__umul24(umin(uint32_t(er), uint32_t(imax(lim, 0))), d_in32)) + uint32_t(ech_c);
-    };
-    auto chunk_row = [&](int k) -> int64_t { return brow + imin(t_begin + int64_t(k) * T, L - 1); };
+    // Chunk k covers steps t_begin + k*T .. of this segment; rows(k) of them
+    // exist (0 for chunks past the end, whose values are masked to zero: a
+    // zero step size leaves the state unchanged).
+    const int64_t brow = int64_t(bi) * L;         // (b, t = 0) row of this batch
+    auto rows = [&](int k) -> int { return max(0, min(T, t_end - t_begin - k * T)); };
+    auto ev = [&](int k) -> int { return er < rows(k) ? evalid : 0; };   // valid channels of this thread's row
 
-    // B/C staging: thread owns tile slots f = m*NT + tid, step f / NP, state f % NP.
-    const uint32_t n32 = uint32_t(n);
-    uint32_t bc_row[EBC], bc_col[EBC];
+    // ---- loader: direct-to-LDS loads of chunk k (rows past the segment's end
+    // read its last row, channels past d_in read channel dbase; both are masked).
+    auto dma_x = [&](const TIn* src, char* tile, int k) {
+        const int t0 = t_begin + k * T;
+        if constexpr (WIDE) {
+            constexpr int EPL = 16 / ES;           // elements per lane
+            constexpr int LPR = 64 / EPL;          // lanes per row
+            constexpr int RPI = 64 / LPR;          // rows per load
+            const int q = lane % LPR;
+            const int ch = dbase + q * EPL < d_in ? dbase + q * EPL : dbase;
 #pragma unroll
-    for (int m = 0; m < EBC; m++) {
-        const int f = int(imin(m * NT + tid, T * NP - 1));
-        bc_row[m] = uint32_t(f / NP);
-        bc_col[m] = uint32_t(imin(f % NP, n - 1));
-    }
-    auto load_bc = [&](uint32_t* rb, uint32_t* rc, int k) {
-        const int64_t tcl = imin(t_begin + int64_t(k) * T, L - 1);
-        const uint32_t blim = uint32_t(imax(0, imin(T - 1, L - 1 - tcl)));
-        const TIn* Bc = Bm + (brow + tcl) * n;
-        const TIn* Cc = Cm + (brow + tcl) * n;
+            for (int ii = 0; ii < XI; ii++) {
+                const int t = min(t0 + ii * RPI + lane / LPR, t_end - 1);
+                load_to_lds<16>(src + ((brow + t) * d_in + ch), tile + ii * 1024);
+            }
+        } else {
+            const int ch = min(dbase + lane, d_in - 1);
 #pragma unroll
-        for (int m = 0; m < EBC; m++) {
-            const uint32_t o = uint32_t(__umul24(umin(bc_row[m], blim), n32)) + bc_col[m];
-            if constexpr (sizeof(TIn) == 2) {
-                rb[m] = reinterpret_cast<const uint16_t*>(Bc)[o];
-                rc[m] = reinterpret_cast<const uint16_t*>(Cc)[o];
-            } else {
-                rb[m] = __float_as_uint(reinterpret_cast<const float*>(Bc)[o]);
-                rc[m] = __float_as_uint(reinterpret_cast<const float*>(Cc)[o]);
+            for (int r = 0; r < T; r++) {
+                const int t = min(t0 + r, t_end - 1);
+                load_to_lds<ES>(src + ((brow + t) * d_in + ch), tile + r * 256);
             }
         }
     };
-    auto stage_bc = [&](const uint32_t* rb, const uint32_t* rc, int k) {
-        const int left = rows_left(k);
+    auto dma_bc = [&](const TIn* src, char* block, int k) {
+        const int t0 = min(t_begin + k * T, t_end - 1);
+        const int last = (t_end - t0) * n - 1;     // last element of the valid rows
+        const TIn* base = src + (brow + t0) * n;
 #pragma unroll
-        for (int m = 0; m < EBC; m++) {
-            const int f = m * NT + tid;
-            if ((T * NP) % NT != 0 && f >= T * NP) break;
-            const int j = f / NP, kk = f % NP;
-            const int w = kk / NSW, q = kk % NSW;
-            const bool ok = j < left && kk < n;
-            float* dst = s_bc + (k & 1) * BC_BUF + ((j * S + w) * 2) * NSW + q;
-            dst[0] = ok ? (sizeof(TIn) == 2 ? __uint_as_float(rb[m] << 16) : __uint_as_float(rb[m])) : 0.0f;
-            dst[NSW] = ok ? (sizeof(TIn) == 2 ? __uint_as_float(rc[m] << 16) : __uint_as_float(rc[m])) : 0.0f;
-        }
+        for (int ii = 0; ii < BI; ii++)
+            load_to_lds<ES>(base + min(ii * 64 + lane, last), block + ii * 256);
+    };
+    auto dma_chunk = [&](int k, int slot) {        // u, delta, B, C of chunk k into ring slot `slot`
+        char* ru = lds + Lds::off_ru + slot * 2 * Lds::RX;
+        char* rbc = lds + Lds::off_rbc + slot * 2 * Lds::RBC;
+        dma_x(static_cast<const TIn*>(p.u), ru, k);
+        dma_x(static_cast<const TIn*>(p.delta), ru + Lds::RX, k);
+        dma_bc(static_cast<const TIn*>(p.B), rbc, k);
+        dma_bc(static_cast<const TIn*>(p.C), rbc + Lds::RBC, k);
+    };
+    auto dma_z = [&](int k, int slot) {
+        if (GATE) dma_x(static_cast<const TIn*>(p.z), lds + Lds::off_rz + slot * Lds::RX, k);
     };
 
-    auto load_chunk = [&](Span<TIn, V, VEC>& su, Span<TIn, V, VEC>& sd, int k) {
-        const int64_t base = chunk_row(k) * d_in;
-        const uint32_t off = row_off(k);
-        su.load(u + base, off, evalid);
-        sd.load(dlt + base, off, evalid);
-    };
-    auto load_z = [&](Span<TIn, V, VEC>& zs, int k) { zs.load(zp + chunk_row(k) * d_in, row_off(k), evalid); };
-
-    // Phase 1 of element i of chunk k: (delta', delta' u); returns u via uv.
-    auto phase1 = [&](const Span<TIn, V, VEC>& su, const Span<TIn, V, VEC>& sd, int k, int i, float& uv) {
-        const bool ok = er < rows_left(k) && i < evalid;
-        const float x = sd.f(i) + bias_v[i];
-        const float dl = ok ? (SP ? softplus(x) : x) : 0.0f;
-        uv = ok ? su.f(i) : 0.0f;
-        return make_float2(dl, dl * uv);
-    };
-    auto store_dw = [&](int k, const float2* dwv) {
+    // ---- element waves
+    using Row = RawRow<TIn, V, WIDE>;
+    // Phase 1 of chunk k (ring slot `slot` = k % 3): (delta', delta' u) into LDS; u kept for the D skip.
+    auto phase1 = [&](int k, int slot, float* uv) {
+        const char* ru = lds + Lds::off_ru + slot * 2 * Lds::RX;
+        Row su, sd;
+        su.read(ru, er, ec);
+        sd.read(ru + Lds::RX, er, ec);
+        const int valid = ev(k);
+        float* buf = s_dw + slot * DW_BUF;
 #pragma unroll
         for (int i = 0; i < V; i++) {
-            float* dst = s_dw + (k & 1) * DW_BUF + ((er >> 1) * 64 + ec + i) * 4 + (er & 1) * 2;
-            *reinterpret_cast<float2*>(dst) = dwv[i];
+            const bool ok = i < valid;
+            const float x = sd.f(i) + bias_v[i];
+            const float dl = ok ? (SP ? softplus(x) : x) : 0.0f;
+            uv[i] = ok ? su.f(i) : 0.0f;
+            *reinterpret_cast<float2*>(buf + ((er >> 1) * 64 + ec + i) * 4 + (er & 1) * 2) = make_float2(dl, dl * uv[i]);
         }
     };
-    auto store_y = [&](int k, const float* yv) {
-        if (k >= 0 && er < rows_left(k) && evalid > 0)
-            store_span<TIn, V, VEC>(yp + (brow + t_begin + int64_t(k) * T) * d_in, uint32_t(er) * d_in32 + uint32_t(ech),
-                                    yv, evalid);
+    // B and C of chunk k (ring slot `slot` = k % 3) as fp32, zero for missing rows and states.
+    auto stage_bc = [&](int k, int slot) {
+        const uint32_t* rb = reinterpret_cast<const uint32_t*>(lds + Lds::off_rbc + slot * 2 * Lds::RBC);
+        const uint32_t* rcc = rb + Lds::RBC / 4;
+        float* buf = s_bc + slot * BC_BUF;
+        const int r = rows(k);
+#pragma unroll
+        for (int m = 0; m < EBC; m++) {
+            const int f = m * NE + etid;
+            if ((T * NP) % NE != 0 && f >= T * NP) break;
+            const int j = f / NP, kk = f % NP;
+            const bool ok = j < r && kk < n;
+            const int e = ok ? j * n + kk : 0;
+            float bv = ES == 2 ? __uint_as_float(rb[e] << 16) : __uint_as_float(rb[e]);
+            float cv = ES == 2 ? __uint_as_float(rcc[e] << 16) : __uint_as_float(rcc[e]);
+            float* dst = buf + ((j * SC + kk / NSW) * 2) * NSW + kk % NSW;
+            dst[0] = ok ? bv : 0.0f;
+            dst[NSW] = ok ? cv : 0.0f;
+        }
+    };
+    // Phase 2 of chunk k: sum of the partial readouts, D skip, gate (z slot `zslot`), store.
+    auto phase2 = [&](int k, const float* uvk, int zslot) {
+        float ypv[SC][V];
+        const float* src = s_yp + (k & 1) * YP_BUF + er * 64 + ec;
+#pragma unroll
+        for (int w = 0; w < SC; w++)
+#pragma unroll
+            for (int i = 0; i < V; i++) ypv[w][i] = src[w * T * 64 + i];
+        Row zr;
+        if (GATE) zr.read(lds + Lds::off_rz + zslot * Lds::RX, er, ec);
+        float yv[V];
+#pragma unroll
+        for (int i = 0; i < V; i++) {
+            float acc = 0.0f;
+#pragma unroll
+            for (int w = 0; w < SC; w++) acc += ypv[w][i];
+            acc = fmaf(Dv[i], uvk[i], acc);
+            if (GATE) acc *= silu(zr.f(i));
+            yv[i] = acc;
+        }
+        const int valid = ev(k);
+        TIn* yp = static_cast<TIn*>(p.y);
+        if (valid > 0)
+            store_span<TIn, V, WIDE>(yp + (brow + t_begin + int64_t(k) * T) * d_in, off_el, yv, valid);
     };
 
-    // Pipeline fill: phase 1 of chunk 0 into LDS; loads of chunk 1 in flight.
-    Span<TIn, V, VEC> su_n, sd_n, su_n2, sd_n2, z_cur, z_prev;
+    // ---- fill: loads of chunks 0 .. 2 and the gate of chunk 0; phase 1 and
+    // B/C of chunks 0 and 1.
+    float uvm1[V], uv0[V], uv1[V], uv2[V];
+    if (loader) {
+        dma_chunk(0, 0);
+        dma_chunk(1, 1);
+        dma_chunk(2, 2);
+        dma_z(0, 0);
+        wait_vmem<N_UDBC + N_Z>();   // chunks 0 and 1 are in LDS
+        __builtin_amdgcn_s_barrier();
+        wait_vmem<N_Z>();            // and chunk 2
+        __builtin_amdgcn_s_barrier();
+    } else {
+        barrier_lds();
+        if (elem) {
+            phase1(0, 0, uv0);
+            stage_bc(0, 0);
+            phase1(1, 1, uv1);
+            stage_bc(1, 1);
 #pragma unroll
-    for (int i = 0; i < Span<TIn, V, VEC>::NW; i++) z_prev.w[i] = 0u;
-    float uv_prev[V], uv_cur[V], uv_next[V];
-    uint32_t rb_n[EBC], rc_n[EBC], rb_n2[EBC], rc_n2[EBC];
-    {
-        load_chunk(su_n, sd_n, 0);
-        load_bc(rb_n, rc_n, 0);
-        float2 dwv[V];
-#pragma unroll
-        for (int i = 0; i < V; i++) dwv[i] = phase1(su_n, sd_n, 0, i, uv_cur[i]);
-        store_dw(0, dwv);
-        stage_bc(rb_n, rc_n, 0);
+            for (int i = 0; i < V; i++) uvm1[i] = 0.0f;
+        }
+        barrier_lds();
     }
-    load_chunk(su_n, sd_n, 1);
-    load_bc(rb_n, rc_n, 1);
-    if (GATE) load_z(z_cur, 0);
-#pragma unroll
-    for (int i = 0; i < V; i++) uv_prev[i] = 0.0f;
-    __syncthreads();
 
-    for (int c = 0; c < nchunks; c++) {
-        const int64_t tc = t_begin + int64_t(c) * T;
-        // Global loads two chunks ahead and the gate of the next chunk.
-        load_chunk(su_n2, sd_n2, c + 2);
-        load_bc(rb_n2, rc_n2, c + 2);
-        Span<TIn, V, VEC> z_new;
-        if (GATE) load_z(z_new, c + 1);
-
-        // All LDS reads of this chunk, up front.
-        float4 dwq[T / 2];
-        {
-            const float4* src = reinterpret_cast<const float4*>(s_dw + (c & 1) * DW_BUF) + lane;
+    // Recurrence-wave LDS read-ahead: step pairs and B/C steps.
+    float4 dwq[RDW];
+    float4 bcq[RBC][NR];
+    if (rec) {
 #pragma unroll
-            for (int pr = 0; pr < T / 2; pr++) dwq[pr] = src[pr * 64];
+        for (int pr = 0; pr < PA; pr++) dwq[pr % RDW] = reinterpret_cast<const float4*>(s_dw)[pr * 64 + lane];
+#pragma unroll
+        for (int j = 0; j < LB; j++) {
+            const float4* r = reinterpret_cast<const float4*>(s_bc + (j * SC + wave) * 2 * NSW);
+#pragma unroll
+            for (int qq = 0; qq < NR; qq++) bcq[j % RBC][qq] = r[qq];
         }
-        float ypv[S][V];
-        {
-            const float* src = s_yp + ((c - 1) & 1) * YP_BUF + er * 64 + ec;
-#pragma unroll
-            for (int w = 0; w < S; w++)
-#pragma unroll
-                for (int i = 0; i < V; i++) ypv[w][i] = src[w * T * 64 + i];
-        }
+    }
 
-        float ypart[T];
-        float yout[V];
-        float2 dwn[V];
-        const float* bcw = s_bc + (c & 1) * BC_BUF + wave * 2 * NSW;
-        float4 bcq[D][NR];
-        auto fetch_bc = [&](int j) {
-            const float4* r = reinterpret_cast<const float4*>(bcw + j * S * 2 * NSW);
-#pragma unroll
-            for (int qq = 0; qq < NR; qq++) bcq[j % D][qq] = r[qq];
-        };
-#pragma unroll
-        for (int j = 0; j < D; j++) fetch_bc(j);
+    // One chunk c of each kind of wave, with c % 3 == PH (ring slots are
+    // compile-time constants).  Each kind runs its own loop: the three never
+    // share control flow inside the loop, so the compiler's wait analysis of
+    // one (the loader's loads in flight) does not spill into the others.
+    auto rec_chunk = [&](auto ph, int c) {
+        constexpr int PH = decltype(ph)::value;
+        constexpr int K0 = PH, K1 = (PH + 1) % 3;    // ring slots of chunks c, c+1
+        float* ypw = s_yp + (c & 1) * YP_BUF + wave * T * 64 + lane;
+        const float* dw_c = s_dw + K0 * DW_BUF;
+        const float* dw_n = s_dw + K1 * DW_BUF;
+        const float* bc_c = s_bc + K0 * BC_BUF + wave * 2 * NSW;
+        const float* bc_n = s_bc + K1 * BC_BUF + wave * 2 * NSW;
+        float ylast = 0.0f;
 #pragma unroll
         for (int j = 0; j < T; j++) {
-            const int slot = j % D;
-            const float4 dq = dwq[j / 2];
+            if (j % 2 == 0) {
+                const int pr = j / 2 + PA;       // read ahead, into chunk c+1 near the end
+                const float* src = pr < T / 2 ? dw_c : dw_n;
+                dwq[pr % RDW] = reinterpret_cast<const float4*>(src)[(pr % (T / 2)) * 64 + lane];
+            }
+            {
+                const int jb = j + LB;
+                const float4* r = reinterpret_cast<const float4*>((jb < T ? bc_c : bc_n) + (jb % T) * SC * 2 * NSW);
+#pragma unroll
+                for (int qq = 0; qq < NR; qq++) bcq[jb % RBC][qq] = r[qq];
+            }
+            const float4 dq = dwq[(j / 2) % RDW];
             const float dl = (j & 1) ? dq.z : dq.x;
             const float wv = (j & 1) ? dq.w : dq.y;
             float bcv[2 * NSW];
 #pragma unroll
             for (int qq = 0; qq < NR; qq++) {
-                bcv[4 * qq] = bcq[slot][qq].x;
-                bcv[4 * qq + 1] = bcq[slot][qq].y;
-                bcv[4 * qq + 2] = bcq[slot][qq].z;
-                bcv[4 * qq + 3] = bcq[slot][qq].w;
+                bcv[4 * qq] = bcq[j % RBC][qq].x;
+                bcv[4 * qq + 1] = bcq[j % RBC][qq].y;
+                bcv[4 * qq + 2] = bcq[j % RBC][qq].z;
+                bcv[4 * qq + 3] = bcq[j % RBC][qq].w;
             }
-            if (j + D < T) fetch_bc(j + D);
             float acc = 0.0f;
 #pragma unroll
             for (int q = 0; q < NSW; q++) {
@@ -431,74 +506,81 @@ __global__ __launch_bounds__(S * 64) void scan_seq(const ScanParams p) {
                 h[q] = fmaf(a, h[q], wv * bcv[q]);
                 acc = fmaf(bcv[NSW + q], h[q], acc);
             }
-            ypart[j] = acc;
-            // Interleaved per-element work after every T/V steps.
-            if ((j + 1) % (T / V) == 0) {
-                const int i = (j + 1) / (T / V) - 1;
-                float acc2 = 0.0f;
-#pragma unroll
-                for (int w = 0; w < S; w++) acc2 += ypv[w][i];
-                acc2 = fmaf(Dv[i], uv_prev[i], acc2);
-                if (GATE) acc2 *= silu(z_prev.f(i));
-                yout[i] = acc2;
-                dwn[i] = phase1(su_n, sd_n, c + 1, i, uv_next[i]);
+            if (j & 1) {
+                ypw[(j - 1) * 64] = ylast;
+                ypw[j * 64] = acc;
+            } else {
+                ylast = acc;
             }
         }
-        // LDS writes of this chunk, then the y store of chunk c-1.
-        {
-            float* dst = s_yp + (c & 1) * YP_BUF + wave * T * 64 + lane;
-#pragma unroll
-            for (int j = 0; j < T; j++) dst[j * 64] = ypart[j];
-        }
-        store_dw(c + 1, dwn);
-        stage_bc(rb_n, rc_n, c + 1);
-        store_y(c - 1, yout);
-#pragma unroll
-        for (int i = 0; i < V; i++) {
-            uv_prev[i] = uv_cur[i];
-            uv_cur[i] = uv_next[i];
-        }
-        z_prev = z_cur;
-        z_cur = z_new;
-        su_n = su_n2;
-        sd_n = sd_n2;
-#pragma unroll
-        for (int m = 0; m < EBC; m++) {
-            rb_n[m] = rb_n2[m];
-            rc_n[m] = rc_n2[m];
-        }
-        __syncthreads();
-    }
-    // Pipeline drain: phase 2 of the last chunk.
-    {
-        const float* src = s_yp + ((nchunks - 1) & 1) * YP_BUF + er * 64 + ec;
-        float yout[V];
+        barrier_lds();
+    };
+    auto elem_chunk = [&](auto ph, int c) {
+        constexpr int PH = decltype(ph)::value;
+        constexpr int K2 = (PH + 2) % 3;         // ring slot of chunks c+2 and c-1
+        if (c > 0) phase2(c - 1, uvm1, K2);
+        phase1(c + 2, K2, uv2);
+        stage_bc(c + 2, K2);
 #pragma unroll
         for (int i = 0; i < V; i++) {
-            float acc2 = 0.0f;
-#pragma unroll
-            for (int w = 0; w < S; w++) acc2 += src[w * T * 64 + i];
-            acc2 = fmaf(Dv[i], uv_prev[i], acc2);
-            if (GATE) acc2 *= silu(z_prev.f(i));
-            yout[i] = acc2;
+            uvm1[i] = uv0[i];
+            uv0[i] = uv1[i];
+            uv1[i] = uv2[i];
         }
-        store_y(nchunks - 1, yout);
+        barrier_lds();
+    };
+    auto load_chunk = [&](auto ph, int c) {
+        constexpr int PH = decltype(ph)::value;
+        constexpr int K1 = (PH + 1) % 3;         // ring slot of chunks c+1 and c+4
+        if (c == 0) dma_chunk(3, 0);
+        dma_chunk(c + 4, K1);
+        dma_z(c + 1, K1);
+        wait_vmem<N_UDBC + N_Z>();   // chunk c+3 and z of chunk c are in LDS
+        __builtin_amdgcn_s_barrier();
+    };
+    using I0 = std::integral_constant<int, 0>;
+    using I1 = std::integral_constant<int, 1>;
+    using I2 = std::integral_constant<int, 2>;
+    if (rec) {
+        for (int c = 0; c < nch3; c += 3) {
+            rec_chunk(I0{}, c);
+            rec_chunk(I1{}, c + 1);
+            rec_chunk(I2{}, c + 2);
+        }
+    } else if (elem) {
+        for (int c = 0; c < nch3; c += 3) {
+            elem_chunk(I0{}, c);
+            elem_chunk(I1{}, c + 1);
+            elem_chunk(I2{}, c + 2);
+        }
+    } else {
+        for (int c = 0; c < nch3; c += 3) {
+            load_chunk(I0{}, c);
+            load_chunk(I1{}, c + 1);
+            load_chunk(I2{}, c + 2);
+        }
     }
 
-    if (seg + 1 < p.K) {
+    if (elem) {
+        phase2(nch3 - 1, uvm1, 2);                // drain: the last chunk's outputs (nch3 - 1 = 2 mod 3)
+    } else if (loader) {
+        wait_vmem<0>();   // no load may land after the workgroup ends
+    } else if (seg + 1 < p.K) {
         // Publish the state for the next segment.
-        float* dst = p.handoff + (seg * G + g) * n * 64;
+        float* dst = p.handoff + (int64_t(seg) * G + g) * n * 64;
 #pragma unroll
         for (int q = 0; q < NSW; q++)
             if (n0 + q < n) dst[(n0 + q) * 64 + lane] = h[q];
+    } else if (p.last_state && dv) {
+#pragma unroll
+        for (int q = 0; q < NSW; q++)
+            if (n0 + q < n) p.last_state[(int64_t(bi) * d_in + d) * n + n0 + q] = h[q];
+    }
+    if (seg + 1 < p.K) {
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
         __syncthreads();
         if (tid == 0)
             __hip_atomic_store(p.ctl + kFlagOffset + seg * G + g, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
-    } else if (p.last_state && dv) {
-#pragma unroll
-        for (int q = 0; q < NSW; q++)
-            if (n0 + q < n) p.last_state[(bi * d_in + d) * n + n0 + q] = h[q];
     }
 }
 

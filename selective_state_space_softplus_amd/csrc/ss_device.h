@@ -29,6 +29,39 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
     return __builtin_bit_cast(uint16_t, h);
 }
 
+// Workgroup barrier that orders LDS accesses only.  __syncthreads() also
+// fences global memory, which makes every wave wait for all its outstanding
+// global loads at the barrier; a software pipeline that keeps loads in flight
+// across barriers needs this narrower form.  Global memory shared between
+// waves must be ordered with explicit fences instead.
+__device__ __forceinline__ void barrier_lds() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// Direct-to-LDS load: every lane reads BYTES bytes at `src` and the wave's data
+// lands in LDS at `lds_dst` + lane * max(BYTES, 4), without passing through
+// registers.  Completion is tracked by the vector-memory counter.
+template <int BYTES>
+__device__ __forceinline__ void load_to_lds(const void* src, void* lds_dst) {
+    static_assert(BYTES == 2 || BYTES == 4 || BYTES == 16, "direct-to-LDS load size");
+    if constexpr (BYTES == 16) __builtin_amdgcn_global_load_lds(src, lds_dst, 16, 0, 0);
+    else if constexpr (BYTES == 4) __builtin_amdgcn_global_load_lds(src, lds_dst, 4, 0, 0);
+    else __builtin_amdgcn_global_load_lds(src, lds_dst, 2, 0, 0);
+}
+
+// Wait until at most N vector-memory operations of this wave are outstanding.
+template <int N>
+struct VmemWait {
+    static constexpr int n = N > 63 ? 63 : N;
+    enum : int { code = (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8) };
+};
+template <int N>
+__device__ __forceinline__ void wait_vmem() {
+    __builtin_amdgcn_s_waitcnt(VmemWait<N>::code);
+}
+
 // Integer min/max with both operands of one type.  HIP's own min/max also
 // accept mixed argument types, and those overloads compute in double.
 __device__ __forceinline__ int64_t imin(int64_t a, int64_t b) { return a < b ? a : b; }

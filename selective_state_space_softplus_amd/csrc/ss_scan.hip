@@ -27,8 +27,10 @@ using ss::StepParams;
 constexpr int kMaxSegments = 16;
 constexpr int64_t kMaxElems = int64_t(1) << 46;   // keeps every index product far from int64 overflow
 constexpr int kTparWaves = 8;
-// Largest grid in workgroups of 512 threads: a launch holds at most 2^32 - 1 work-items.
-constexpr int64_t kMaxWorkgroups = (int64_t(1) << 23) - 1;
+// Largest grid in workgroups of up to 1024 threads: a launch holds at most 2^32 - 1 work-items.
+constexpr int64_t kMaxWorkgroups = (int64_t(1) << 22) - 1;
+// Longest sequence: per-segment time indices of scan_seq are 32-bit.
+constexpr int64_t kMaxLength = (int64_t(1) << 31) - 1024;
 // Largest b * d_in of the decode step (up to 16 threads per channel in one launch).
 constexpr int64_t kMaxStepChannels = (int64_t(1) << 28) - 1;
 
@@ -61,13 +63,12 @@ bool sizes_ok(int64_t a, int64_t b, int64_t c) {
 enum class ScanKernel { Tpar, Seq };
 
 struct SeqShape {
-    int S;     // waves per workgroup
-    int NSW;   // states per wave
+    int SC;    // recurrence waves per workgroup
+    int NSW;   // states per recurrence wave
 };
 
-// Waves per workgroup and states per wave.  Every shape has 4 or 8 waves, so
-// the per-element work of a chunk is spread over 256 or 512 threads.
-// SS_SCAN_WAVES=4 selects the 4-wave shape at 9 <= n <= 16 (tests, tuning).
+// Recurrence waves and states per wave.  SS_SCAN_WAVES=4 selects 4 waves of
+// 4 states at 9 <= n <= 16 (tests, tuning).
 SeqShape seq_shape(int64_t n) {
     const char* w = std::getenv("SS_SCAN_WAVES");
     const int want = w ? int(std::strtol(w, nullptr, 10)) : 0;
@@ -100,9 +101,6 @@ SeqWorkspace seq_workspace(int64_t b, int64_t L, int64_t d_in, int64_t n) {
     w.total = w.ctl + w.handoff;
     return w;
 }
-
-// One chunk of B (or C) must be addressable with 32-bit offsets.
-bool bc_rows_fit(int64_t L, int64_t n) { return L >= 1 && n * ss::kSeqChunk < (int64_t(1) << 24); }
 
 int device_cus() {
     static std::atomic<int> cached[64];
@@ -164,30 +162,32 @@ int choose_segments(int64_t G, int64_t L, int T, int64_t slots) {
     return best;
 }
 
-template <typename TIn, int S, int NSW>
+template <typename TIn, int SC, int NSW>
 int launch_seq(ScanParams p, void* ws, size_t ws_bytes, hipStream_t st) {
-    constexpr int T = ss::kSeqChunk;
-    constexpr int V = T / S;
-    constexpr size_t lds = ss::seq_lds_bytes<S, NSW>();
-    static_assert(lds <= 160 * 1024, "LDS of one workgroup");
+    constexpr int TW = ss::seq_chunk<TIn, SC, NSW, true>(), TN = ss::seq_chunk<TIn, SC, NSW, false>();
+    constexpr int threads = (SC + ss::kSeqElemWaves + 1) * 64;
     const int64_t G = p.b * p.nblk_d;
     const SeqWorkspace w = seq_workspace(p.b, p.L, p.d_in, p.n);
     if (!ws || ws_bytes < w.total) return SS_ERR_WORKSPACE;
 
-    const size_t va = std::min<size_t>(16, V * sizeof(TIn));
-    const bool vec = p.d_in % V == 0 && aligned(p.u, va) && aligned(p.delta, va) && aligned(p.y, va) &&
-                     (!p.z || aligned(p.z, va));
-    const int variant = (vec ? 4 : 0) | (p.softplus ? 2 : 0) | (p.z ? 1 : 0);
+    // Wide path: whole 16-byte pieces per row and 16-byte aligned u, delta, z;
+    // y aligned for V-element stores.
+    const bool wide = (p.d_in * int64_t(sizeof(TIn))) % 16 == 0 && aligned(p.u, 16) && aligned(p.delta, 16) &&
+                      (!p.z || aligned(p.z, 16)) && aligned(p.y, (TW / ss::kSeqElemWaves) * sizeof(TIn));
+    const int T = wide ? TW : TN;
+    const int variant = (wide ? 4 : 0) | (p.softplus ? 2 : 0) | (p.z ? 1 : 0);
     using Kern = void (*)(ScanParams);
     static constexpr Kern kernels[8] = {
-        ss::scan_seq<TIn, S, NSW, false, false, false>, ss::scan_seq<TIn, S, NSW, false, false, true>,
-        ss::scan_seq<TIn, S, NSW, false, true, false>,  ss::scan_seq<TIn, S, NSW, false, true, true>,
-        ss::scan_seq<TIn, S, NSW, true, false, false>,  ss::scan_seq<TIn, S, NSW, true, false, true>,
-        ss::scan_seq<TIn, S, NSW, true, true, false>,   ss::scan_seq<TIn, S, NSW, true, true, true>};
+        ss::scan_seq<TIn, SC, NSW, TN, false, false, false>, ss::scan_seq<TIn, SC, NSW, TN, false, false, true>,
+        ss::scan_seq<TIn, SC, NSW, TN, false, true, false>,  ss::scan_seq<TIn, SC, NSW, TN, false, true, true>,
+        ss::scan_seq<TIn, SC, NSW, TW, true, false, false>,  ss::scan_seq<TIn, SC, NSW, TW, true, false, true>,
+        ss::scan_seq<TIn, SC, NSW, TW, true, true, false>,   ss::scan_seq<TIn, SC, NSW, TW, true, true, true>};
     const Kern kern = kernels[variant];
+    const size_t lds = wide ? ss::SeqLds<TW, SC, SC * NSW, sizeof(TIn), true>::bytes
+                            : ss::SeqLds<TN, SC, SC * NSW, sizeof(TIn), false>::bytes;
 
     const int cus = device_cus();
-    const int per_cu = resident_per_cu(reinterpret_cast<const void*>(kern), S * 64, lds);
+    const int per_cu = resident_per_cu(reinterpret_cast<const void*>(kern), threads, lds);
     int K = choose_segments(G, p.L, T, int64_t(std::max(cus, 0)) * per_cu);
     while (K > 1 && G * K > kMaxWorkgroups) K--;   // a launch holds fewer than 2^32 work-items
     int64_t Lseg = (p.L + K - 1) / K;
@@ -204,14 +204,14 @@ int launch_seq(ScanParams p, void* ws, size_t ws_bytes, hipStream_t st) {
         hipLaunchKernelGGL(ss::scan_ctl_reset, dim3(rb), dim3(256), 0, st, p.ctl, int64_t(words));
         if (hipGetLastError() != hipSuccess) return SS_ERR_HIP;
     }
-    hipLaunchKernelGGL(kern, dim3(unsigned(G * K)), dim3(S * 64), lds, st, p);
+    hipLaunchKernelGGL(kern, dim3(unsigned(G * K)), dim3(threads), lds, st, p);
     return hipGetLastError() == hipSuccess ? SS_OK : SS_ERR_HIP;
 }
 
 template <typename TIn>
 int dispatch_seq(const ScanParams& p, void* ws, size_t ws_bytes, hipStream_t st) {
     const SeqShape sh = seq_shape(p.n);
-    if (sh.S == 4) return sh.NSW == 2 ? launch_seq<TIn, 4, 2>(p, ws, ws_bytes, st) : launch_seq<TIn, 4, 4>(p, ws, ws_bytes, st);
+    if (sh.SC == 4) return sh.NSW == 2 ? launch_seq<TIn, 4, 2>(p, ws, ws_bytes, st) : launch_seq<TIn, 4, 4>(p, ws, ws_bytes, st);
     if (sh.NSW == 2) return launch_seq<TIn, 8, 2>(p, ws, ws_bytes, st);
     if (sh.NSW == 4) return launch_seq<TIn, 8, 4>(p, ws, ws_bytes, st);
     return launch_seq<TIn, 8, 8>(p, ws, ws_bytes, st);
@@ -249,7 +249,7 @@ SS_EXPORT const char* ss_status_string(int status) {
 SS_EXPORT size_t ss_scan_fwd_workspace_bytes(int64_t b, int64_t L, int64_t d_in, int64_t n, int dtype) {
     if (dtype != SS_F32 && dtype != SS_BF16) return 0;
     if (!sizes_ok(b, L, d_in) || n <= 0 || n > SS_MAX_STATE || d_in > SS_MAX_CHANNELS) return 0;
-    if (!bc_rows_fit(L, n) || b * ((d_in + 63) / 64) > kMaxWorkgroups) return 0;
+    if (b * ((d_in + 63) / 64) > kMaxWorkgroups || L > kMaxLength) return 0;
     // Sized for scan_seq with the most segments; scan_tpar (n <= 2) needs none
     // but the same size is asked for so that either kernel can be chosen.
     return seq_workspace(b, L, d_in, n).total;
@@ -263,7 +263,7 @@ SS_EXPORT int ss_scan_fwd(const void* u, const void* delta, const float* A_log, 
     if (!sizes_ok(b, L, d_in) || n <= 0 || d_in > SS_MAX_CHANNELS) return SS_ERR_SHAPE;
     if (dtype != SS_F32 && dtype != SS_BF16) return SS_ERR_DTYPE;
     if (n > SS_MAX_STATE) return SS_ERR_UNSUPPORTED;
-    if (!bc_rows_fit(L, n) || b * ((d_in + 63) / 64) > kMaxWorkgroups) return SS_ERR_SHAPE;
+    if (b * ((d_in + 63) / 64) > kMaxWorkgroups || L > kMaxLength) return SS_ERR_SHAPE;
     const size_t es = elem_size(dtype);
     for (const void* p : {u, delta, B, C, z, static_cast<const void*>(y)})
         if (p && !aligned(p, es)) return SS_ERR_ALIGN;
