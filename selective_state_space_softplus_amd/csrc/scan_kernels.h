@@ -298,12 +298,13 @@ __global__ __launch_bounds__((SC + kSeqElemWaves + 1) * 64) void scan_seq(const 
             }
         }
         __syncthreads();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
         if (rec) {
-            const float* src = p.handoff + (int64_t(seg - 1) * G + g) * n * 64;
+            const uint32_t* src = reinterpret_cast<const uint32_t*>(p.handoff) + (int64_t(seg - 1) * G + g) * n * 64;
 #pragma unroll
             for (int q = 0; q < NSW; q++)
-                if (n0 + q < n) h[q] = src[(n0 + q) * 64 + lane];
+                if (n0 + q < n)
+                    h[q] = __uint_as_float(__hip_atomic_load(src + (n0 + q) * 64 + lane, __ATOMIC_RELAXED,
+                                                             __HIP_MEMORY_SCOPE_AGENT));
         }
     }
 
@@ -567,20 +568,29 @@ __global__ __launch_bounds__((SC + kSeqElemWaves + 1) * 64) void scan_seq(const 
         wait_vmem<0>();   // no load may land after the workgroup ends
     } else if (seg + 1 < p.K) {
         // Publish the state for the next segment.
-        float* dst = p.handoff + (int64_t(seg) * G + g) * n * 64;
+        uint32_t* dst = reinterpret_cast<uint32_t*>(p.handoff) + (int64_t(seg) * G + g) * n * 64;
 #pragma unroll
         for (int q = 0; q < NSW; q++)
-            if (n0 + q < n) dst[(n0 + q) * 64 + lane] = h[q];
+            if (n0 + q < n)
+                __hip_atomic_store(dst + (n0 + q) * 64 + lane, __float_as_uint(h[q]), __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
     } else if (p.last_state && dv) {
 #pragma unroll
         for (int q = 0; q < NSW; q++)
             if (n0 + q < n) p.last_state[(int64_t(bi) * d_in + d) * n + n0 + q] = h[q];
     }
     if (seg + 1 < p.K) {
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+        // The handed-off state and the flag are device-coherent atomic
+        // accesses, ordered by the hardware: every wave waits until its state
+        // stores are acknowledged, the workgroup meets, then one thread sets
+        // the flag; the next segment reads the state only after it has seen
+        // the flag.  Release/acquire fences at device scope would write back
+        // and invalidate the whole L2 of the compute die at every segment
+        // boundary, which costs far more than this exchange.
+        __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
         if (tid == 0)
-            __hip_atomic_store(p.ctl + kFlagOffset + seg * G + g, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(p.ctl + kFlagOffset + seg * G + g, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
 }
 
