@@ -208,7 +208,7 @@ __global__ __launch_bounds__((SC + kSeqElemWaves + 1) * 64) void scan_seq(const 
     constexpr int PA = kSeqAhead / 2;              // step pairs of (delta', delta' u) read ahead
     constexpr int RDW = 4;                         // register ring of step pairs (divides T / 2)
     constexpr int NR = NSW / 2;                    // float4 per step: NSW values of B then NSW of C
-    constexpr int RBC = NR >= 4 ? 2 : 4;           // register ring of B, C steps (divides T)
+    constexpr int RBC = NR >= 2 ? 2 : 4;           // register ring of B, C steps (divides T)
     constexpr int LB = RBC - 1;                    // steps of B, C read ahead
     // Loads the loader issues per chunk: u and delta, B and C, z.
     constexpr int XI = WIDE ? T * 64 * ES / 1024 : T;          // per u, delta or z tile
@@ -221,6 +221,11 @@ __global__ __launch_bounds__((SC + kSeqElemWaves + 1) * 64) void scan_seq(const 
     extern __shared__ __align__(16) float smem[];
     char* const lds = reinterpret_cast<char*>(smem);
     float* s_dw = reinterpret_cast<float*>(lds + Lds::off_dw);   // [3][T/2][64][4]: (delta'_j, w_j, delta'_j+1, w_j+1)
+    // Channel c of a (delta', delta' u) row sits in 16-byte slot dw_slot(c): an
+    // element thread writes its V consecutive channels at a 16*V-byte stride
+    // from its neighbours, which without the swizzle would put 16 lanes of a
+    // row on 4 bank groups.
+    auto dw_slot = [](int c) { return c ^ ((c >> 4) & 3); };
     float* s_yp = reinterpret_cast<float*>(lds + Lds::off_yp);   // [2][SC][T][64]
     float* s_bc = reinterpret_cast<float*>(lds + Lds::off_bc);   // [3][T][SC][2][NSW]
     int& s_ticket = *reinterpret_cast<int*>(lds + Lds::off_ticket);
@@ -332,7 +337,7 @@ __global__ __launch_bounds__((SC + kSeqElemWaves + 1) * 64) void scan_seq(const 
             }
         } else {
             const int ch = min(dbase + lane, d_in - 1);
-#pragma unroll
+#pragma unroll 2
             for (int r = 0; r < T; r++) {
                 const int t = min(t0 + r, t_end - 1);
                 load_to_lds<ES>(src + ((brow + t) * d_in + ch), tile + r * 256);
@@ -375,7 +380,7 @@ __global__ __launch_bounds__((SC + kSeqElemWaves + 1) * 64) void scan_seq(const 
             const float x = sd.f(i) + bias_v[i];
             const float dl = ok ? (SP ? softplus(x) : x) : 0.0f;
             uv[i] = ok ? su.f(i) : 0.0f;
-            *reinterpret_cast<float2*>(buf + ((er >> 1) * 64 + ec + i) * 4 + (er & 1) * 2) = make_float2(dl, dl * uv[i]);
+            *reinterpret_cast<float2*>(buf + ((er >> 1) * 64 + dw_slot(ec + i)) * 4 + (er & 1) * 2) = make_float2(dl, dl * uv[i]);
         }
     };
     // B and C of chunk k (ring slot `slot` = k % 3) as fp32, zero for missing rows and states.
@@ -454,7 +459,7 @@ __global__ __launch_bounds__((SC + kSeqElemWaves + 1) * 64) void scan_seq(const 
     float4 bcq[RBC][NR];
     if (rec) {
 #pragma unroll
-        for (int pr = 0; pr < PA; pr++) dwq[pr % RDW] = reinterpret_cast<const float4*>(s_dw)[pr * 64 + lane];
+        for (int pr = 0; pr < PA; pr++) dwq[pr % RDW] = reinterpret_cast<const float4*>(s_dw)[pr * 64 + dw_slot(lane)];
 #pragma unroll
         for (int j = 0; j < LB; j++) {
             const float4* r = reinterpret_cast<const float4*>(s_bc + (j * SC + wave) * 2 * NSW);
@@ -481,7 +486,7 @@ __global__ __launch_bounds__((SC + kSeqElemWaves + 1) * 64) void scan_seq(const 
             if (j % 2 == 0) {
                 const int pr = j / 2 + PA;       // read ahead, into chunk c+1 near the end
                 const float* src = pr < T / 2 ? dw_c : dw_n;
-                dwq[pr % RDW] = reinterpret_cast<const float4*>(src)[(pr % (T / 2)) * 64 + lane];
+                dwq[pr % RDW] = reinterpret_cast<const float4*>(src)[(pr % (T / 2)) * 64 + dw_slot(lane)];
             }
             {
                 const int jb = j + LB;
