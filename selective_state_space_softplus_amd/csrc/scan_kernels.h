@@ -85,7 +85,7 @@ struct SeqLds {
     static constexpr int YP = SC * T * 64 * 4;                 // partial readouts of a chunk
     static constexpr int BC = T * 2 * NP * 4;                  // B and C of a chunk as fp32, grouped per wave
     static constexpr int RX = T * 64 * XES;                    // raw u, delta or z tile
-    static constexpr int RBC = T * NP * 4;                     // raw B or C block
+    static constexpr int RBC = (T * NP + 63) / 64 * 256;       // raw B or C block (whole 64-lane loads)
     static constexpr int off_dw = 0;
     static constexpr int off_yp = off_dw + 3 * DW;
     static constexpr int off_bc = off_yp + 2 * YP;
@@ -212,11 +212,11 @@ __global__ __launch_bounds__((SC + kSeqElemWaves + 1) * 64) void scan_seq(const 
     constexpr int LB = RBC - 1;                    // steps of B, C read ahead
     // Loads the loader issues per chunk: u and delta, B and C, z.
     constexpr int XI = WIDE ? T * 64 * ES / 1024 : T;          // per u, delta or z tile
-    constexpr int BI = T * NP / 64;                            // per B or C block
+    constexpr int BI = (T * NP + 63) / 64;                     // per B or C block
     constexpr int N_UDBC = 2 * XI + 2 * BI, N_Z = GATE ? XI : 0;
     static_assert(T % P == 0 && 64 % V == 0 && NE / TPR == T, "thread tiling of a chunk");
     static_assert(NSW % 2 == 0 && (T / 2) % RDW == 0 && T % RBC == 0 && PA + 1 <= RDW, "tiles split evenly");
-    static_assert((T * NP) % 64 == 0 && (!WIDE || (T * 64 * ES) % 1024 == 0), "whole loads per tile");
+    static_assert(!WIDE || (T * 64 * ES) % 1024 == 0, "whole loads per tile");
     static_assert(Lds::bytes <= 160 * 1024, "LDS of one workgroup");
     extern __shared__ __align__(16) float smem[];
     char* const lds = reinterpret_cast<char*>(smem);

@@ -72,17 +72,18 @@ struct SeqShape {
 SeqShape seq_shape(int64_t n) {
     const char* w = std::getenv("SS_SCAN_WAVES");
     const int want = w ? int(std::strtol(w, nullptr, 10)) : 0;
+    if (n <= 2) return {1, 2};
     if (n <= 8) return {4, 2};
     if (n <= 16) return want == 4 ? SeqShape{4, 4} : SeqShape{8, 2};
     if (n <= 32) return {8, 4};
     return {8, 8};
 }
 
+// scan_seq for every n; SS_SCAN_VARIANT=tpar selects scan_tpar for n <= 2 (tests).
 ScanKernel choose_kernel(int64_t n) {
     const char* v = std::getenv("SS_SCAN_VARIANT");
-    if (v && std::strcmp(v, "seq") == 0) return ScanKernel::Seq;
     if (v && std::strcmp(v, "tpar") == 0 && n <= 2) return ScanKernel::Tpar;
-    return n <= 2 ? ScanKernel::Tpar : ScanKernel::Seq;
+    return ScanKernel::Seq;
 }
 
 // Workspace of scan_seq, in order: control words (ticket, error, one flag per
@@ -211,6 +212,7 @@ int launch_seq(ScanParams p, void* ws, size_t ws_bytes, hipStream_t st) {
 template <typename TIn>
 int dispatch_seq(const ScanParams& p, void* ws, size_t ws_bytes, hipStream_t st) {
     const SeqShape sh = seq_shape(p.n);
+    if (sh.SC == 1) return launch_seq<TIn, 1, 2>(p, ws, ws_bytes, st);
     if (sh.SC == 4) return sh.NSW == 2 ? launch_seq<TIn, 4, 2>(p, ws, ws_bytes, st) : launch_seq<TIn, 4, 4>(p, ws, ws_bytes, st);
     if (sh.NSW == 2) return launch_seq<TIn, 8, 2>(p, ws, ws_bytes, st);
     if (sh.NSW == 4) return launch_seq<TIn, 8, 4>(p, ws, ws_bytes, st);
