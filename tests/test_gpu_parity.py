@@ -105,6 +105,9 @@ SMALL = [
     (1, 70, 40, 33, F32, True, True, True),
     (1, 70, 40, 64, F32, True, True, True),
     (1, 70, 40, 64, BF16, True, True, True),
+    (1, 70, 41, 64, BF16, True, True, True),     # element-wise loads, 8-step chunks
+    (2, 61, 42, 40, F32, True, False, True),     # element-wise loads, 8-step chunks, fp32
+    (2, 45, 64, 2, BF16, False, True, True),
 ]
 
 
@@ -362,3 +365,32 @@ def test_scan_seq_shapes(ss, waves, segments):
     inp = workloads.random_scan_inputs(3, 700, 200, 16, BF16, seed=31, gated=True, bias=True)
     with env(SS_SCAN_WAVES=waves, SS_SCAN_SEGMENTS=segments):
         check_full(ss, inp, f"waves={waves} segments={segments}")
+
+
+@pytest.mark.parametrize("dtype,n", [(BF16, 16), (F32, 16), (BF16, 1), (F32, 5)])
+def test_wide_and_elementwise_loads_agree(ss, dtype, n):
+    """The 16-byte direct-to-LDS path and the element-load path give bit-identical results.
+
+    Shifting every input and output by one element breaks the 16-byte alignment
+    the wide path needs, so the same values go through the element-load path.
+    """
+    say(f"wide vs element loads {dtype} n={n}")
+    b, L, d = 2, 333, 128
+    inp = to_dev(workloads.random_scan_inputs(b, L, d, n, dtype, seed=41 + n, gated=True, bias=True))
+
+    def shifted(t):
+        buf = torch.empty(t.numel() + 1, dtype=t.dtype, device=DEV)
+        v = buf[1:].view(t.shape)
+        v.copy_(t)
+        return v
+
+    y1, l1 = gpu_scan(ss, inp)
+    sh = dict(inp)
+    for k in ("u", "delta", "B", "C", "z"):
+        sh[k] = shifted(inp[k])
+    y_out = shifted(torch.zeros_like(y1))
+    y2, l2 = ss.scan_fwd(sh["u"], sh["delta"], sh["A_log"], sh["B"], sh["C"], sh["D"], sh["z"], sh["delta_bias"], True,
+                         return_last_state=True, out=y_out)
+    torch.cuda.synchronize()
+    assert y2.data_ptr() == y_out.data_ptr()
+    assert torch.equal(y1, y2) and torch.equal(l1, l2)
