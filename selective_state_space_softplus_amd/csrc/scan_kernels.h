@@ -416,9 +416,9 @@ __global__ __launch_bounds__((SC + kSeqElemWaves + 1) * 64) void scan_seq(const 
         float yv[V];
 #pragma unroll
         for (int i = 0; i < V; i++) {
-            float acc = 0.0f;
+            float acc = ypv[0][i];
 #pragma unroll
-            for (int w = 0; w < SC; w++) acc += ypv[w][i];
+            for (int w = 1; w < SC; w++) acc += ypv[w][i];
             acc = fmaf(Dv[i], uvk[i], acc);
             if (GATE) acc *= silu(zr.f(i));
             yv[i] = acc;
