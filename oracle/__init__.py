@@ -56,6 +56,10 @@ def _bind(lib: ctypes.CDLL) -> ctypes.CDLL:
     lib.ss_oracle_scan.argtypes = [P] * 8 + [ctypes.c_int, P, P, I64, I64, I64, I64]
     lib.ss_oracle_state_update.restype = ctypes.c_int
     lib.ss_oracle_state_update.argtypes = [P] * 9 + [ctypes.c_int, P, I64, I64, I64]
+    lib.ss_oracle_scan_ex.restype = ctypes.c_int
+    lib.ss_oracle_scan_ex.argtypes = [P] * 8 + [ctypes.c_int, P, ctypes.c_int, P, P, I64, I64, I64, I64]
+    lib.ss_oracle_state_update_ex.restype = ctypes.c_int
+    lib.ss_oracle_state_update_ex.argtypes = [P] * 9 + [ctypes.c_int, ctypes.c_int, P, I64, I64, I64]
     return lib
 
 
@@ -82,31 +86,33 @@ def silu(x: float, lib=None) -> float:
     return (lib or load()).ss_oracle_silu(float(x))
 
 
-def scan(u, delta, A_log, B, C, D, z=None, delta_bias=None, delta_softplus=True, lib=None):
+def scan(u, delta, A_log, B, C, D, z=None, delta_bias=None, delta_softplus=True, lib=None, h0=None, zoh=False):
     """y (b, L, d_in) and last_state (b, d_in, n), both float64.
 
-    u, delta, z: (b, L, d_in); A_log: (d_in, n); B, C: (b, L, n); D, delta_bias: (d_in).
+    u, delta, z: (b, L, d_in); A_log: (d_in, n); B, C: (b, L, n); D, delta_bias: (d_in);
+    h0: optional initial state (b, d_in, n); zoh: zero-order-hold input weight instead of Euler.
     """
     lib = lib or load()
     u, delta, A_log, B, C, D = map(_f64, (u, delta, A_log, B, C, D))
-    z, delta_bias = _f64(z), _f64(delta_bias)
+    z, delta_bias, h0 = _f64(z), _f64(delta_bias), _f64(h0)
     b, L, d_in = u.shape
     n = A_log.shape[1]
     assert delta.shape == u.shape and A_log.shape == (d_in, n)
     assert B.shape == (b, L, n) and C.shape == (b, L, n) and D.shape == (d_in,)
     assert z is None or z.shape == u.shape
     assert delta_bias is None or delta_bias.shape == (d_in,)
+    assert h0 is None or h0.shape == (b, d_in, n)
     y = np.empty((b, L, d_in), np.float64)
     last = np.empty((b, d_in, n), np.float64)
-    rc = lib.ss_oracle_scan(_ptr(u), _ptr(delta), _ptr(A_log), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
-                            _ptr(delta_bias), int(bool(delta_softplus)), _ptr(y), _ptr(last),
-                            b, L, d_in, n)
+    rc = lib.ss_oracle_scan_ex(_ptr(u), _ptr(delta), _ptr(A_log), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
+                               _ptr(delta_bias), int(bool(delta_softplus)), _ptr(h0), int(bool(zoh)),
+                               _ptr(y), _ptr(last), b, L, d_in, n)
     if rc != 0:
         raise ValueError(f"ss_oracle_scan returned {rc}")
     return y, last
 
 
-def state_update(state, x, dt, A_log, B, C, D, z=None, dt_bias=None, dt_softplus=True, lib=None):
+def state_update(state, x, dt, A_log, B, C, D, z=None, dt_bias=None, dt_softplus=True, lib=None, zoh=False):
     """One decode step on a copy of ``state``: returns (new_state (b, d_in, n), y (b, d_in))."""
     lib = lib or load()
     st = _f64(state).copy()
@@ -116,14 +122,15 @@ def state_update(state, x, dt, A_log, B, C, D, z=None, dt_bias=None, dt_softplus
     assert x.shape == (b, d_in) and dt.shape == (b, d_in) and A_log.shape == (d_in, n)
     assert B.shape == (b, n) and C.shape == (b, n) and D.shape == (d_in,)
     y = np.empty((b, d_in), np.float64)
-    rc = lib.ss_oracle_state_update(_ptr(st), _ptr(x), _ptr(dt), _ptr(A_log), _ptr(B), _ptr(C), _ptr(D),
-                                    _ptr(z), _ptr(dt_bias), int(bool(dt_softplus)), _ptr(y), b, d_in, n)
+    rc = lib.ss_oracle_state_update_ex(_ptr(st), _ptr(x), _ptr(dt), _ptr(A_log), _ptr(B), _ptr(C), _ptr(D),
+                                       _ptr(z), _ptr(dt_bias), int(bool(dt_softplus)), int(bool(zoh)), _ptr(y),
+                                       b, d_in, n)
     if rc != 0:
         raise ValueError(f"ss_oracle_state_update returned {rc}")
     return st, y
 
 
-def scan_channels(inputs: dict, channels, delta_softplus=True, lib=None):
+def scan_channels(inputs: dict, channels, delta_softplus=True, lib=None, zoh=False):
     """Oracle outputs for selected (batch, channel) pairs of a full-size scan.
 
     Each pair is an independent recurrence, so its slice of the inputs is run
@@ -136,6 +143,7 @@ def scan_channels(inputs: dict, channels, delta_softplus=True, lib=None):
         bias = inputs.get("delta_bias")
         y, last = scan(sl(inputs["u"]), sl(inputs["delta"]), inputs["A_log"][d:d + 1], inputs["B"][bi:bi + 1],
                        inputs["C"][bi:bi + 1], inputs["D"][d:d + 1], sl(z) if z is not None else None,
-                       None if bias is None else bias[d:d + 1], delta_softplus, lib=lib)
+                       None if bias is None else bias[d:d + 1], delta_softplus, lib=lib,
+                       h0=None if inputs.get("h0") is None else inputs["h0"][bi:bi + 1, d:d + 1], zoh=zoh)
         out[(bi, d)] = (y[0, :, 0], last[0, 0])
     return out

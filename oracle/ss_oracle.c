@@ -22,11 +22,15 @@
  * blocking, fusion or reordering.  All arithmetic is in double; the caller
  * widens its fp32 / bf16 inputs exactly.
  *
+ * The _ex forms add two options: an initial state h0 for the scan (instead
+ * of zero) and the zero-order-hold input weight (exp(delta*A) - 1)/A * B in
+ * place of forward Euler delta*B (mhpn.cn page, sections 3.2 and 6).
+ *
  * Layouts (row-major, last index fastest):
  *   u, delta, z, y : (b, L, d_in)      B, C : (b, L, n)
  *   A_log          : (d_in, n)         D, delta_bias : (d_in)
- *   state          : (b, d_in, n)      x, dt, z, y of the step : (b, d_in)
- *   B, C of the step : (b, n)
+ *   state, h0, last_state : (b, d_in, n)
+ *   x, dt, z, y of the step : (b, d_in)     B, C of the step : (b, n)
  * Return value: 0 on success, -1 on a NULL required pointer, -2 on a
  * non-positive size.
  */
@@ -59,11 +63,27 @@ static double step_size(double delta, const double *bias, int64_t d, int softplu
     return softplus ? ss_oracle_softplus(v) : v;
 }
 
-int ss_oracle_scan(const double *u, const double *delta, const double *A_log,
-                   const double *B, const double *C, const double *D,
-                   const double *z, const double *delta_bias, int delta_softplus,
-                   double *y, double *last_state,
-                   int64_t b, int64_t L, int64_t d_in, int64_t n)
+/* Discretised input weight of one state: forward Euler delta*B (the
+ * mamba-minimal loop, mhpn.cn page section 3.2), or with zoh != 0 the
+ * zero-order hold (exp(delta*A) - 1) / A * B that the page contrasts it with
+ * in section 6 (for a diagonal A the matrix form (delta A)^-1 (exp(delta A) - I)
+ * delta B reduces to this per state).  A = 0 exactly (A_log below about
+ * -745) takes the limit delta*B. */
+static double input_weight(double dl, double A, double Bk, int zoh)
+{
+    if (!zoh)
+        return dl * Bk;
+    if (A == 0.0)
+        return dl * Bk;
+    return expm1(dl * A) / A * Bk;
+}
+
+int ss_oracle_scan_ex(const double *u, const double *delta, const double *A_log,
+                      const double *B, const double *C, const double *D,
+                      const double *z, const double *delta_bias, int delta_softplus,
+                      const double *h0, int zoh,
+                      double *y, double *last_state,
+                      int64_t b, int64_t L, int64_t d_in, int64_t n)
 {
     if (!u || !delta || !A_log || !B || !C || !D || !y)
         return -1;
@@ -72,21 +92,22 @@ int ss_oracle_scan(const double *u, const double *delta, const double *A_log,
 
     for (int64_t bi = 0; bi < b; bi++) {
         for (int64_t d = 0; d < d_in; d++) {
-            /* h starts at zero (section 4 of the mhpn.cn page). */
+            /* h starts at zero (section 4 of the mhpn.cn page), or at the
+             * given initial state h0 (b, d_in, n). */
             double h[n];
             double A[n];
             for (int64_t k = 0; k < n; k++) {
-                h[k] = 0.0;
+                h[k] = h0 ? h0[(bi * d_in + d) * n + k] : 0.0;
                 A[k] = -exp(A_log[d * n + k]);          /* A = -exp(A_log), elementwise */
             }
             for (int64_t t = 0; t < L; t++) {
                 int64_t e = (bi * L + t) * d_in + d;    /* (b, t, d) element */
                 int64_t r = (bi * L + t) * n;           /* row of B and C at (b, t) */
                 double dl = step_size(delta[e], delta_bias, d, delta_softplus);
-                /* state update: h = exp(delta*A) * h + delta*B*u */
+                /* state update: h = exp(delta*A) * h + (input weight) * u */
                 for (int64_t k = 0; k < n; k++) {
                     double dA = exp(dl * A[k]);
-                    double dBu = dl * B[r + k] * u[e];
+                    double dBu = input_weight(dl, A[k], B[r + k], zoh) * u[e];
                     h[k] = dA * h[k] + dBu;
                 }
                 /* read out with C after the update, then the D skip */
@@ -107,11 +128,21 @@ int ss_oracle_scan(const double *u, const double *delta, const double *A_log,
     return 0;
 }
 
-int ss_oracle_state_update(double *state, const double *x, const double *dt,
-                           const double *A_log, const double *B, const double *C,
-                           const double *D, const double *z, const double *dt_bias,
-                           int dt_softplus, double *y,
-                           int64_t b, int64_t d_in, int64_t n)
+int ss_oracle_scan(const double *u, const double *delta, const double *A_log,
+                   const double *B, const double *C, const double *D,
+                   const double *z, const double *delta_bias, int delta_softplus,
+                   double *y, double *last_state,
+                   int64_t b, int64_t L, int64_t d_in, int64_t n)
+{
+    return ss_oracle_scan_ex(u, delta, A_log, B, C, D, z, delta_bias, delta_softplus, NULL, 0,
+                             y, last_state, b, L, d_in, n);
+}
+
+int ss_oracle_state_update_ex(double *state, const double *x, const double *dt,
+                              const double *A_log, const double *B, const double *C,
+                              const double *D, const double *z, const double *dt_bias,
+                              int dt_softplus, int zoh, double *y,
+                              int64_t b, int64_t d_in, int64_t n)
 {
     if (!state || !x || !dt || !A_log || !B || !C || !D || !y)
         return -1;
@@ -126,7 +157,7 @@ int ss_oracle_state_update(double *state, const double *x, const double *dt,
             for (int64_t k = 0; k < n; k++) {
                 double A = -exp(A_log[d * n + k]);
                 double dA = exp(dl * A);
-                double dB = dl * B[bi * n + k];
+                double dB = input_weight(dl, A, B[bi * n + k], zoh);
                 double *h = &state[e * n + k];
                 *h = *h * dA + x[e] * dB;               /* in place */
                 yt += C[bi * n + k] * *h;
@@ -138,4 +169,14 @@ int ss_oracle_state_update(double *state, const double *x, const double *dt,
         }
     }
     return 0;
+}
+
+int ss_oracle_state_update(double *state, const double *x, const double *dt,
+                           const double *A_log, const double *B, const double *C,
+                           const double *D, const double *z, const double *dt_bias,
+                           int dt_softplus, double *y,
+                           int64_t b, int64_t d_in, int64_t n)
+{
+    return ss_oracle_state_update_ex(state, x, dt, A_log, B, C, D, z, dt_bias, dt_softplus, 0,
+                                     y, b, d_in, n);
 }

@@ -290,26 +290,34 @@ __global__ __launch_bounds__((SC + kSeqElemWaves + 1) * 64) void scan_seq(const 
     }
 
     if (seg > 0) {
-        // Wait for the previous segment of this channel group, then take its state.
+        // Wait for the previous segment of this channel group, then take its
+        // state.  The wait cannot deadlock (the predecessor holds an earlier
+        // ticket); should it still time out, the error word is set and this
+        // piece continues from a NaN state, so its outputs show it.
+        int& s_timeout = *(reinterpret_cast<int*>(lds + Lds::off_ticket) + 1);
         if (tid == 0) {
             uint32_t* flag = p.ctl + kFlagOffset + (seg - 1) * G + g;
-            int spins = 0;
+            int spins = 0, timed_out = 0;
             while (__hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0u) {
                 __builtin_amdgcn_s_sleep(2);
                 if (++spins > kSpinLimit) {
                     atomicOr(p.ctl + 1, 1u);
+                    timed_out = 1;
                     break;
                 }
             }
+            s_timeout = timed_out;
         }
         __syncthreads();
+        const bool timed_out = __builtin_amdgcn_readfirstlane(s_timeout) != 0;
         if (rec) {
             const uint32_t* src = reinterpret_cast<const uint32_t*>(p.handoff) + (int64_t(seg - 1) * G + g) * n * 64;
 #pragma unroll
             for (int q = 0; q < NSW; q++)
                 if (n0 + q < n)
-                    h[q] = __uint_as_float(__hip_atomic_load(src + (n0 + q) * 64 + lane, __ATOMIC_RELAXED,
-                                                             __HIP_MEMORY_SCOPE_AGENT));
+                    h[q] = timed_out ? __builtin_nanf("")
+                                     : __uint_as_float(__hip_atomic_load(src + (n0 + q) * 64 + lane,
+                                                                         __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
         }
     }
 

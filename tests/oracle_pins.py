@@ -59,11 +59,18 @@ def random_case(seed, b=2, L=9, d_in=3, n=4, gated=True, bias=True, softplus=Tru
 
 
 def brute_force(case):
-    """Unrolled closed-form solution of the recurrence (O(L^2), float64)."""
+    """Unrolled closed-form solution of the recurrence (O(L^2), float64).
+
+    With case["h0"] the initial state enters as exp(A * sum_{r<=t} Delta_r) h0;
+    with case["zoh"] each input carries the zero-order-hold weight
+    expm1(Delta_s A) / A instead of Delta_s.
+    """
     u, A_log, B, C, D = case["u"], case["A_log"], case["B"], case["C"], case["D"]
     x = case["delta"] + (0.0 if case["delta_bias"] is None else case["delta_bias"])
     Delta = np.logaddexp(0.0, x) if case["delta_softplus"] else x
     A = -np.exp(A_log)                                   # (d_in, n)
+    h0 = case.get("h0")
+    zoh = case.get("zoh", False)
     b, L, d_in = u.shape
     y = np.zeros((b, L, d_in))
     last = np.zeros((b, d_in, A.shape[1]))
@@ -71,10 +78,11 @@ def brute_force(case):
         for d in range(d_in):
             S = np.concatenate([[0.0], np.cumsum(Delta[bi, :, d])])   # S[t+1] = sum_{r<=t} Delta_r
             for t in range(L):
-                acc = 0.0
+                acc = 0.0 if h0 is None else np.exp(A[d] * S[t + 1]) * h0[bi, d]
                 for s in range(t + 1):
                     decay = np.exp(A[d] * (S[t + 1] - S[s + 1]))      # prod_{r=s+1..t} exp(Delta_r A)
-                    acc = acc + decay * Delta[bi, s, d] * B[bi, s] * u[bi, s, d]
+                    w = np.expm1(Delta[bi, s, d] * A[d]) / A[d] if zoh else Delta[bi, s, d]
+                    acc = acc + decay * w * B[bi, s] * u[bi, s, d]
                 y[bi, t, d] = np.dot(C[bi, t], acc) + D[d] * u[bi, t, d]
                 if t == L - 1:
                     last[bi, d] = acc
@@ -86,7 +94,8 @@ def brute_force(case):
 
 def run(case, lib):
     return oracle.scan(case["u"], case["delta"], case["A_log"], case["B"], case["C"], case["D"], case["z"],
-                       case["delta_bias"], case["delta_softplus"], lib=lib)
+                       case["delta_bias"], case["delta_softplus"], lib=lib, h0=case.get("h0"),
+                       zoh=case.get("zoh", False))
 
 
 # ----------------------------------------------------------------------------- pins
@@ -237,5 +246,86 @@ def pin_bias_placement(lib):
     _close(l1, l2, rtol=1e-13, atol=1e-14, what="bias inside softplus (state)")
 
 
+def pin_initial_state(lib):
+    """An initial state h0: zero h0 is no h0; closed form at n = 1; brute force; a split scan is the whole scan."""
+    case = random_case(18, b=2, L=9, d_in=3, n=4)
+    y, last = run(case, lib)
+    c0 = dict(case, h0=np.zeros((2, 3, 4)))
+    y0, l0 = run(c0, lib)
+    assert np.array_equal(y, y0) and np.array_equal(last, l0), "zero h0 must equal no h0"
+    # n = 1, constant Delta, B, u: h_t = a^t h0 + Delta B u (1 - a^t) / (1 - a).
+    L = 30
+    A_exp, Delta, Bv, uv, h0v = 1.7, 0.45, -0.6, 1.1, 2.5
+    Cc = _rng(19).standard_normal((1, L, 1))
+    y1, l1 = oracle.scan(np.full((1, L, 1), uv), np.full((1, L, 1), Delta), np.array([[math.log(A_exp)]]),
+                         np.full((1, L, 1), Bv), Cc, np.array([0.0]), None, None, False, lib=lib,
+                         h0=np.array([[[h0v]]]))
+    a = math.exp(-A_exp * Delta)
+    t = np.arange(1, L + 1)
+    h = a ** t * h0v + Delta * Bv * uv * (1 - a ** t) / (1 - a)
+    _close(y1[0, :, 0], Cc[0, :, 0] * h, rtol=1e-12, atol=1e-14, what="h0 closed form")
+    _close(l1[0, 0, 0], h[-1], what="h0 closed form last")
+    for seed, kw in enumerate([dict(), dict(n=1, gated=False), dict(bias=False, n=6)]):
+        c = random_case(200 + seed, **kw)
+        c["h0"] = _rng(300 + seed).standard_normal((c["u"].shape[0], c["u"].shape[2], c["A_log"].shape[1]))
+        yb, lb = brute_force(c)
+        yo, lo = run(c, lib)
+        _close(yo, yb, rtol=1e-11, atol=1e-12, what=f"h0 brute force y {kw}")
+        _close(lo, lb, rtol=1e-11, atol=1e-12, what=f"h0 brute force last {kw}")
+    # The second part of a split scan, started from the first part's state, equals the whole scan.
+    L1 = 4
+    first = {k: (v[:, :L1] if isinstance(v, np.ndarray) and v.ndim == 3 and k not in ("h0",) else v)
+             for k, v in case.items()}
+    rest = {k: (v[:, L1:] if isinstance(v, np.ndarray) and v.ndim == 3 and k not in ("h0",) else v)
+            for k, v in case.items()}
+    _, s1 = run(first, lib)
+    rest["h0"] = s1
+    y2, l2 = run(rest, lib)
+    _close(y2, y[:, L1:], rtol=1e-12, atol=1e-13, what="split scan y")
+    _close(l2, last, rtol=1e-12, atol=1e-13, what="split scan last")
+
+
+def pin_zoh(lib):
+    """Zero-order-hold input weight: closed form at n = 1, brute force, the A -> 0 limit (Euler), step == scan."""
+    L = 30
+    for A_exp, Delta, h0v in ((1.7, 0.45, 0.0), (0.2, 1.3, -0.7), (12.0, 0.02, 3.0)):
+        Bv, uv = -0.6, 1.1
+        Cc = _rng(20).standard_normal((1, L, 1))
+        y, last = oracle.scan(np.full((1, L, 1), uv), np.full((1, L, 1), Delta), np.array([[math.log(A_exp)]]),
+                              np.full((1, L, 1), Bv), Cc, np.array([0.0]), None, None, False, lib=lib,
+                              h0=np.array([[[h0v]]]), zoh=True)
+        A = -A_exp
+        a = math.exp(A * Delta)
+        t = np.arange(1, L + 1)
+        h = a ** t * h0v - Bv * uv / A * (1 - a ** t)      # weight (a - 1)/A: the geometric sum telescopes
+        _close(y[0, :, 0], Cc[0, :, 0] * h, rtol=1e-12, atol=1e-14, what=f"zoh closed form A={A}")
+        _close(last[0, 0, 0], h[-1], rtol=1e-12, atol=1e-14, what=f"zoh closed form last A={A}")
+    for seed, kw in enumerate([dict(), dict(n=1, gated=False), dict(bias=False, n=5, softplus=False)]):
+        c = random_case(400 + seed, **kw)
+        if not c["delta_softplus"]:
+            c["delta"] = np.abs(c["delta"]) + 0.05
+        c["zoh"] = True
+        yb, lb = brute_force(c)
+        yo, lo = run(c, lib)
+        _close(yo, yb, rtol=1e-11, atol=1e-12, what=f"zoh brute force y {kw}")
+        _close(lo, lb, rtol=1e-11, atol=1e-12, what=f"zoh brute force last {kw}")
+    # A -> 0: expm1(Delta A) / A -> Delta, so ZOH equals Euler.
+    c = random_case(21, b=1, L=12, d_in=2, n=3)
+    c["A_log"] = np.full((2, 3), -40.0)
+    ye, le = run(c, lib)
+    yz, lz = run(dict(c, zoh=True), lib)
+    _close(yz, ye, rtol=1e-12, atol=1e-13, what="zoh -> Euler as A -> 0")
+    # ZOH steps chained from zero equal the ZOH scan.
+    c = random_case(22, b=2, L=7, d_in=3, n=4)
+    y, last = run(dict(c, zoh=True), lib)
+    state = np.zeros((2, 3, 4))
+    for t in range(7):
+        state, yt = oracle.state_update(state, c["u"][:, t], c["delta"][:, t], c["A_log"], c["B"][:, t], c["C"][:, t],
+                                        c["D"], c["z"][:, t], c["delta_bias"], True, lib=lib, zoh=True)
+        _close(yt, y[:, t], rtol=1e-12, atol=1e-13, what=f"zoh chain y[{t}]")
+    _close(state, last, rtol=1e-12, atol=1e-13, what="zoh chain state")
+
+
 ALL_PINS = [pin_softplus_silu, pin_hand_worked, pin_brute_force, pin_geometric_closed_form, pin_limits,
-            pin_skip_and_gate, pin_linearity_causality, pin_step_matches_scan, pin_bias_placement]
+            pin_skip_and_gate, pin_linearity_causality, pin_step_matches_scan, pin_bias_placement,
+            pin_initial_state, pin_zoh]

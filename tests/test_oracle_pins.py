@@ -27,11 +27,20 @@ def test_oracle_pin(pin, oracle_lib):
 MUTANTS = [
     ("A sign", "A[k] = -exp(A_log[d * n + k]);", "A[k] = exp(A_log[d * n + k]);"),
     ("A without exp", "A[k] = -exp(A_log[d * n + k]);", "A[k] = -A_log[d * n + k];"),
-    ("nonzero initial state", "h[k] = 0.0;", "h[k] = 1e-3;"),
+    ("nonzero initial state", "h[k] = h0 ? h0[(bi * d_in + d) * n + k] : 0.0;",
+     "h[k] = h0 ? h0[(bi * d_in + d) * n + k] : 1e-3;"),
+    ("initial state ignored", "h[k] = h0 ? h0[(bi * d_in + d) * n + k] : 0.0;", "h[k] = 0.0;"),
+    ("initial state transposed", "h[k] = h0 ? h0[(bi * d_in + d) * n + k] : 0.0;",
+     "h[k] = h0 ? h0[(bi * d_in + d) * n + (n - 1 - k)] : 0.0;"),
     ("decay without delta", "double dA = exp(dl * A[k]);", "double dA = exp(A[k]);"),
     ("Euler decay 1 + delta*A", "double dA = exp(dl * A[k]);", "double dA = 1.0 + dl * A[k];"),
-    ("input without delta", "double dBu = dl * B[r + k] * u[e];", "double dBu = B[r + k] * u[e];"),
-    ("input uses C", "double dBu = dl * B[r + k] * u[e];", "double dBu = dl * C[r + k] * u[e];"),
+    ("input without delta", "if (!zoh)\n        return dl * Bk;", "if (!zoh)\n        return Bk;"),
+    ("input uses C", "double dBu = input_weight(dl, A[k], B[r + k], zoh) * u[e];",
+     "double dBu = input_weight(dl, A[k], C[r + k], zoh) * u[e];"),
+    ("zoh weight uses exp", "return expm1(dl * A) / A * Bk;", "return exp(dl * A) / A * Bk;"),
+    ("zoh weight without 1/A", "return expm1(dl * A) / A * Bk;", "return expm1(dl * A) * Bk;"),
+    ("zoh weight sign", "return expm1(dl * A) / A * Bk;", "return -expm1(dl * A) / A * Bk;"),
+    ("zoh weight is Euler", "return expm1(dl * A) / A * Bk;", "return dl * Bk;"),
     ("dropped decay", "h[k] = dA * h[k] + dBu;", "h[k] = h[k] + dBu;"),
     ("decayed input", "h[k] = dA * h[k] + dBu;", "h[k] = dA * (h[k] + dBu);"),
     ("readout uses B", "yt += C[r + k] * h[k];", "yt += B[r + k] * h[k];"),
@@ -56,7 +65,10 @@ MUTANTS = [
     ("step without decay", "*h = *h * dA + x[e] * dB;", "*h = *h + x[e] * dB;"),
     ("step readout before update", "*h = *h * dA + x[e] * dB;               /* in place */\n                yt += C[bi * n + k] * *h;",
      "yt += C[bi * n + k] * *h;\n                *h = *h * dA + x[e] * dB;"),
-    ("step B index", "double dB = dl * B[bi * n + k];", "double dB = dl * B[k];"),
+    ("step B index", "double dB = input_weight(dl, A, B[bi * n + k], zoh);",
+     "double dB = input_weight(dl, A, B[k], zoh);"),
+    ("step ignores zoh", "double dB = input_weight(dl, A, B[bi * n + k], zoh);",
+     "double dB = input_weight(dl, A, B[bi * n + k], 0);"),
     ("step dropped skip", "yt += D[d] * x[e];", "yt += 0.0 * x[e];"),
     ("step A index", "double A = -exp(A_log[d * n + k]);", "double A = -exp(A_log[k]);"),
 ]
