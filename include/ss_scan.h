@@ -14,11 +14,17 @@
  *     selective_state_update call that follows it (bias added to dt inside the
  *     softplus, in-place state update, gate y * silu(z) after the D skip).
  *
- * For every batch b, channel d and time t (h starts at zero):
+ * For every batch b, channel d and time t (h starts at zero, or at a given
+ * initial state with the _ex entry points):
  *     delta' = softplus(delta[b,t,d] + bias[d])      (or delta + bias without softplus)
  *     h[k]   = exp(delta' * A[d,k]) * h[k] + delta' * B[b,t,k] * u[b,t,d],  A = -exp(A_log)
  *     y      = sum_k C[b,t,k] * h[k] + D[d] * u[b,t,d]
  *     y      = y * z / (1 + exp(-z))                  (only when z is given)
+ * The _ex entry points can instead weight the input term with the zero-order
+ * hold (mhpn.cn page, section 6: the exact discretisation of the B term, which
+ * the simplified delta' * B above approximates; A is diagonal, so it acts per
+ * state):
+ *     h[k]   = exp(delta' * A[d,k]) * h[k] + (exp(delta' * A[d,k]) - 1) / A[d,k] * B[b,t,k] * u[b,t,d]
  *
  * Conventions shared by every entry point:
  *   - Every pointer is DEVICE memory owned by the caller.  Tensors are dense,
@@ -36,7 +42,8 @@
  *   - Arguments are validated before anything is enqueued; on any error
  *     nothing is launched and nothing is written.
  *   - Outputs must not overlap any input (SS_ERR_ALIAS); the state of the
- *     step is the one in/out buffer and is updated in place.
+ *     step is the one in/out buffer and is updated in place, and the
+ *     initial_state of ss_scan_fwd_ex may be its last_state buffer itself.
  *   - Pointers must be aligned to their element size (SS_ERR_ALIGN).
  */
 #ifndef SS_SCAN_H
@@ -65,8 +72,15 @@ typedef enum {
     SS_ERR_WORKSPACE = -5,   /* workspace missing or smaller than the query says    */
     SS_ERR_HIP = -6,         /* the HIP runtime refused the launch                  */
     SS_ERR_ALIAS = -7,       /* an output overlaps an input                         */
-    SS_ERR_ALIGN = -8        /* a pointer is not aligned to its element size        */
+    SS_ERR_ALIGN = -8,       /* a pointer is not aligned to its element size        */
+    SS_ERR_MODE = -9         /* discretization is not an ss_discretization value    */
 } ss_status;
+
+/* Input term of the recurrence (the _ex entry points). */
+typedef enum {
+    SS_DISC_EULER = 0,       /* delta' * B * u, as ss_scan_fwd and ss_state_update  */
+    SS_DISC_ZOH = 1          /* (exp(delta' * A) - 1) / A * B * u, the zero-order hold */
+} ss_discretization;
 
 /* Largest state size n the kernels are built for. */
 #define SS_MAX_STATE 64
@@ -111,6 +125,29 @@ int ss_scan_fwd(const void *u, const void *delta, const float *A_log,
                 void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * ss_scan_fwd with two more inputs (mhpn.cn page: section 4 starts the
+ * recurrence from a zero state, section 6 gives the zero-order hold):
+ *
+ *   initial_state  : (b, d_in, n) fp32, the state before the first step, or
+ *                    NULL for zero.  It may be the same buffer as last_state
+ *                    (the state is then carried over in place); any other
+ *                    overlap with an output gives SS_ERR_ALIAS.
+ *   discretization : an ss_discretization value (else SS_ERR_MODE).
+ * Splitting a sequence into consecutive parts and passing each part's
+ * last_state as the next part's initial_state gives the outputs of one scan
+ * over the whole sequence (up to rounding).  All other arguments, sizes and
+ * errors are those of ss_scan_fwd, which is this call with NULL and
+ * SS_DISC_EULER.  Returns an ss_status.
+ */
+int ss_scan_fwd_ex(const void *u, const void *delta, const float *A_log,
+                   const void *B, const void *C, const float *D,
+                   const void *z, const float *delta_bias, int delta_softplus,
+                   const float *initial_state, int discretization,
+                   void *y, float *last_state,
+                   int64_t b, int64_t L, int64_t d_in, int64_t n, int dtype,
+                   void *workspace, size_t workspace_bytes, void *stream);
+
+/*
  * One decode step on a persistent state (jiafeimiao.top page: Mamba.step and
  * its selective_state_update(ssm_state, x, dt, A, B, C, D, z, dt_bias,
  * dt_softplus) call; the state is updated in place).
@@ -132,6 +169,19 @@ int ss_state_update(float *state, const void *x, const void *dt,
                     const float *D, const void *z, const float *dt_bias,
                     int dt_softplus, void *y,
                     int64_t b, int64_t d_in, int64_t n, int dtype, void *stream);
+
+/*
+ * ss_state_update with the input term chosen by `discretization` (an
+ * ss_discretization value, else SS_ERR_MODE; mhpn.cn page, section 6).  The
+ * zero-order-hold step is one step of ss_scan_fwd_ex with SS_DISC_ZOH.  All
+ * other arguments, sizes and errors are those of ss_state_update, which is
+ * this call with SS_DISC_EULER.  Returns an ss_status.
+ */
+int ss_state_update_ex(float *state, const void *x, const void *dt,
+                       const float *A_log, const void *B, const void *C,
+                       const float *D, const void *z, const float *dt_bias,
+                       int dt_softplus, int discretization, void *y,
+                       int64_t b, int64_t d_in, int64_t n, int dtype, void *stream);
 
 /* Static, NUL-terminated description of a status code. */
 const char *ss_status_string(int status);

@@ -9,9 +9,10 @@ library is missing, importing this package raises.
 Entry points mirror the C ABI (``include/ss_scan.h``):
 
   scan_fwd(u, delta, A_log, B, C, D, z=None, delta_bias=None, delta_softplus=True,
-           return_last_state=False)          -> y  or  (y, last_state)
-  state_update(state, x, dt, A_log, B, C, D, z=None, dt_bias=None, dt_softplus=True)
-                                             -> y  (state is updated in place)
+           return_last_state=False, initial_state=None, zoh=False)
+                                             -> y  or  (y, last_state)
+  state_update(state, x, dt, A_log, B, C, D, z=None, dt_bias=None, dt_softplus=True,
+               zoh=False)                    -> y  (state is updated in place)
   scan_fwd_workspace_bytes(b, L, d_in, n, dtype) -> int
   status_string(code) -> str
 
@@ -19,6 +20,9 @@ Shapes follow the mhpn.cn selective_scan walk-through (section 2): u, delta
 (b, L, d_in); A_log (d_in, n) with A = -exp(A_log); B, C (b, L, n); D (d_in).
 The step follows jiafeimiao.top's Mamba.step / selective_state_update call:
 state (b, d_in, n) fp32 updated in place; x, dt, z (b, d_in); B, C (b, n).
+``initial_state`` (b, d_in, n) fp32 starts the scan from a given state and
+``zoh=True`` selects the zero-order-hold input term (mhpn.cn, section 6); calls
+that use either go through ``ss_scan_fwd_ex`` / ``ss_state_update_ex``.
 """
 from __future__ import annotations
 
@@ -33,9 +37,12 @@ LIBRARY = os.path.join(_HERE, "libss_scan.so")
 SS_F32 = 0
 SS_BF16 = 1
 SS_MAX_STATE = 64
+SS_DISC_EULER = 0
+SS_DISC_ZOH = 1
 STATUS = {0: "SS_OK", -1: "SS_ERR_NULL", -2: "SS_ERR_SHAPE", -3: "SS_ERR_DTYPE", -4: "SS_ERR_UNSUPPORTED",
-          -5: "SS_ERR_WORKSPACE", -6: "SS_ERR_HIP", -7: "SS_ERR_ALIAS", -8: "SS_ERR_ALIGN"}
-EXPORTS = ("ss_scan_fwd_workspace_bytes", "ss_scan_fwd", "ss_state_update", "ss_status_string")
+          -5: "SS_ERR_WORKSPACE", -6: "SS_ERR_HIP", -7: "SS_ERR_ALIAS", -8: "SS_ERR_ALIGN", -9: "SS_ERR_MODE"}
+EXPORTS = ("ss_scan_fwd_workspace_bytes", "ss_scan_fwd", "ss_scan_fwd_ex", "ss_state_update", "ss_state_update_ex",
+           "ss_status_string")
 
 
 class SSError(RuntimeError):
@@ -54,8 +61,12 @@ def _load() -> ctypes.CDLL:
     lib.ss_scan_fwd_workspace_bytes.argtypes = [I64, I64, I64, I64, I]
     lib.ss_scan_fwd.restype = I
     lib.ss_scan_fwd.argtypes = [P, P, P, P, P, P, P, P, I, P, P, I64, I64, I64, I64, I, P, ctypes.c_size_t, P]
+    lib.ss_scan_fwd_ex.restype = I
+    lib.ss_scan_fwd_ex.argtypes = [P, P, P, P, P, P, P, P, I, P, I, P, P, I64, I64, I64, I64, I, P, ctypes.c_size_t, P]
     lib.ss_state_update.restype = I
     lib.ss_state_update.argtypes = [P, P, P, P, P, P, P, P, P, I, P, I64, I64, I64, I, P]
+    lib.ss_state_update_ex.restype = I
+    lib.ss_state_update_ex.argtypes = [P, P, P, P, P, P, P, P, P, I, I, P, I64, I64, I64, I, P]
     lib.ss_status_string.restype = ctypes.c_char_p
     lib.ss_status_string.argtypes = [I]
     return lib
@@ -119,8 +130,11 @@ def _workspace(device, nbytes: int):
 
 
 def scan_fwd(u, delta, A_log, B, C, D, z=None, delta_bias=None, delta_softplus=True, return_last_state=False,
-             out=None, last_state=None, workspace=None):
-    """Selective scan forward on the GPU; returns y (and last_state if asked)."""
+             out=None, last_state=None, workspace=None, initial_state=None, zoh=False):
+    """Selective scan forward on the GPU; returns y (and last_state if asked).
+
+    ``initial_state`` may be the ``last_state`` buffer itself (carried over in place).
+    """
     if u.dim() != 3 or A_log.dim() != 2:
         raise ValueError("u must be (b, L, d_in) and A_log (d_in, n)")
     b, L, d_in = u.shape
@@ -140,10 +154,14 @@ def scan_fwd(u, delta, A_log, B, C, D, z=None, delta_bias=None, delta_softplus=T
     if return_last_state and last_state is None:
         last_state = torch.empty((b, d_in, n), dtype=torch.float32, device=dev)
     _check(last_state, "last_state", (b, d_in, n), torch.float32, dev)
+    _check(initial_state, "initial_state", (b, d_in, n), torch.float32, dev)
     if b == 0 or L == 0 or d_in == 0:
-        # Nothing to scan: no steps leave the zero initial state.
+        # Nothing to scan: no steps leave the initial state as it is.
         if last_state is not None:
-            last_state.zero_()
+            if initial_state is None:
+                last_state.zero_()
+            elif initial_state.data_ptr() != last_state.data_ptr():
+                last_state.copy_(initial_state)
         return (y, last_state) if return_last_state else y
     need = scan_fwd_workspace_bytes(b, L, d_in, n, code)
     if workspace is None:
@@ -151,15 +169,23 @@ def scan_fwd(u, delta, A_log, B, C, D, z=None, delta_bias=None, delta_softplus=T
     ws_ptr = _ptr(workspace)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     with torch.cuda.device(dev):
-        rc = lib.ss_scan_fwd(_ptr(u), _ptr(delta), _ptr(A_log), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
-                             _ptr(delta_bias), int(bool(delta_softplus)), _ptr(y), _ptr(last_state),
-                             b, L, d_in, n, code, ws_ptr, ws_bytes, _stream(dev))
+        if initial_state is None and not zoh:
+            where = "ss_scan_fwd"
+            rc = lib.ss_scan_fwd(_ptr(u), _ptr(delta), _ptr(A_log), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
+                                 _ptr(delta_bias), int(bool(delta_softplus)), _ptr(y), _ptr(last_state),
+                                 b, L, d_in, n, code, ws_ptr, ws_bytes, _stream(dev))
+        else:
+            where = "ss_scan_fwd_ex"
+            rc = lib.ss_scan_fwd_ex(_ptr(u), _ptr(delta), _ptr(A_log), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
+                                    _ptr(delta_bias), int(bool(delta_softplus)), _ptr(initial_state),
+                                    SS_DISC_ZOH if zoh else SS_DISC_EULER, _ptr(y), _ptr(last_state),
+                                    b, L, d_in, n, code, ws_ptr, ws_bytes, _stream(dev))
     if rc != 0:
-        raise SSError(rc, "ss_scan_fwd")
+        raise SSError(rc, where)
     return (y, last_state) if return_last_state else y
 
 
-def state_update(state, x, dt, A_log, B, C, D, z=None, dt_bias=None, dt_softplus=True, out=None):
+def state_update(state, x, dt, A_log, B, C, D, z=None, dt_bias=None, dt_softplus=True, out=None, zoh=False):
     """One decode step; updates ``state`` in place and returns y (b, d_in)."""
     if state.dim() != 3:
         raise ValueError("state must be (b, d_in, n)")
@@ -180,8 +206,16 @@ def state_update(state, x, dt, A_log, B, C, D, z=None, dt_bias=None, dt_softplus
     if b == 0 or d_in == 0:
         return y
     with torch.cuda.device(dev):
-        rc = lib.ss_state_update(_ptr(state), _ptr(x), _ptr(dt), _ptr(A_log), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
-                                 _ptr(dt_bias), int(bool(dt_softplus)), _ptr(y), b, d_in, n, code, _stream(dev))
+        if not zoh:
+            where = "ss_state_update"
+            rc = lib.ss_state_update(_ptr(state), _ptr(x), _ptr(dt), _ptr(A_log), _ptr(B), _ptr(C), _ptr(D),
+                                     _ptr(z), _ptr(dt_bias), int(bool(dt_softplus)), _ptr(y), b, d_in, n, code,
+                                     _stream(dev))
+        else:
+            where = "ss_state_update_ex"
+            rc = lib.ss_state_update_ex(_ptr(state), _ptr(x), _ptr(dt), _ptr(A_log), _ptr(B), _ptr(C), _ptr(D),
+                                        _ptr(z), _ptr(dt_bias), int(bool(dt_softplus)), SS_DISC_ZOH, _ptr(y),
+                                        b, d_in, n, code, _stream(dev))
     if rc != 0:
-        raise SSError(rc, "ss_state_update")
+        raise SSError(rc, where)
     return y

@@ -7,6 +7,8 @@
 //     h[k]   = exp(delta' A[d,k]) h[k] + delta' B[b,t,k] u      (A = -exp(A_log))
 //     y      = sum_k C[b,t,k] h[k] + D[d] u,   then y *= silu(z) if z is given.
 // exp(delta' A) and delta' B u are formed in registers and never stored.
+// scan_seq also takes a given initial state h0 and the zero-order-hold input
+// term (exp(delta' A) - 1) / A B u of the same page's section 6.
 //
 // scan_seq  (state sizes n >= 3).  One lane per channel d, 64 channels per
 //   workgroup; the n states of a channel are split across the S waves of the
@@ -49,6 +51,7 @@ struct ScanParams {
     const float* bias;
     void* y;
     float* last_state;
+    const float* h0;     // (b, d_in, n) initial state, or null for zero (scan_seq)
     int64_t b, L, d_in, n;
     int softplus;
     // plan
@@ -175,6 +178,8 @@ struct RawRow {
 // and y are aligned for 16-byte accesses, so u/delta/z tiles arrive by
 // 16-byte direct-to-LDS loads and y leaves by wide stores.
 // SP: delta' = softplus(delta + bias) (else delta + bias).  GATE: z is given.
+// ZOH: the input term is the zero-order hold's (exp(delta' A) - 1) / A B u
+// (else delta' B u).
 //
 // Waves 0 .. SC-1 ("recurrence waves") each hold NSW states of the 64
 // channels and run nothing but the recurrence.  Waves SC .. SC+3 ("element
@@ -195,7 +200,7 @@ struct RawRow {
 //     tiles (loaded two chunks earlier);
 //   - the loader issues the loads of chunk c+4 (u, delta, B, C) and of chunk
 //     c+1 (z), then waits until those of chunk c+3 and c are complete.
-template <typename TIn, int SC, int NSW, int T, bool WIDE, bool SP, bool GATE>
+template <typename TIn, int SC, int NSW, int T, bool WIDE, bool SP, bool GATE, bool ZOH>
 __global__ __launch_bounds__((SC + kSeqElemWaves + 1) * 64) void scan_seq(const ScanParams p) {
     constexpr int P = kSeqElemWaves;
     constexpr int ES = int(sizeof(TIn));
@@ -268,10 +273,12 @@ __global__ __launch_bounds__((SC + kSeqElemWaves + 1) * 64) void scan_seq(const 
     const bool dv = d < d_in;
     const int n0 = wave * NSW;
     float A2[NSW], h[NSW];
+    const float* h0 = (seg == 0 && p.h0) ? p.h0 + (int64_t(bi) * d_in + d) * n + n0 : nullptr;
 #pragma unroll
     for (int q = 0; q < NSW; q++) {
-        A2[q] = (rec && dv && n0 + q < n) ? a2_from_alog(p.A_log[d * n + n0 + q]) : 0.0f;
-        h[q] = 0.0f;
+        const bool ok = rec && dv && n0 + q < n;
+        A2[q] = ok ? a2_from_alog(p.A_log[d * n + n0 + q]) : 0.0f;
+        h[q] = (ok && h0) ? h0[q] : 0.0f;
     }
 
     // Element waves: thread owns step row er of a chunk, channels ec .. ec+V.
@@ -374,7 +381,8 @@ __global__ __launch_bounds__((SC + kSeqElemWaves + 1) * 64) void scan_seq(const 
 
     // ---- element waves
     using Row = RawRow<TIn, V, WIDE>;
-    // Phase 1 of chunk k (ring slot `slot` = k % 3): (delta', delta' u) into LDS; u kept for the D skip.
+    // Phase 1 of chunk k (ring slot `slot` = k % 3): (delta', delta' u) into LDS,
+    // or (delta', u) with the zero-order hold; u kept for the D skip.
     auto phase1 = [&](int k, int slot, float* uv) {
         const char* ru = lds + Lds::off_ru + slot * 2 * Lds::RX;
         Row su, sd;
@@ -388,7 +396,8 @@ __global__ __launch_bounds__((SC + kSeqElemWaves + 1) * 64) void scan_seq(const 
             const float x = sd.f(i) + bias_v[i];
             const float dl = ok ? (SP ? softplus(x) : x) : 0.0f;
             uv[i] = ok ? su.f(i) : 0.0f;
-            *reinterpret_cast<float2*>(buf + ((er >> 1) * 64 + dw_slot(ec + i)) * 4 + (er & 1) * 2) = make_float2(dl, dl * uv[i]);
+            *reinterpret_cast<float2*>(buf + ((er >> 1) * 64 + dw_slot(ec + i)) * 4 + (er & 1) * 2) =
+                make_float2(dl, ZOH ? uv[i] : dl * uv[i]);
         }
     };
     // B and C of chunk k (ring slot `slot` = k % 3) as fp32, zero for missing rows and states.
@@ -480,6 +489,11 @@ __global__ __launch_bounds__((SC + kSeqElemWaves + 1) * 64) void scan_seq(const 
     // compile-time constants).  Each kind runs its own loop: the three never
     // share control flow inside the loop, so the compiler's wait analysis of
     // one (the loader's loads in flight) does not spill into the others.
+    // ZOH: the input weight is the zero-order hold's (invA[q] = 1 / A).
+    float invA[NSW];
+#pragma unroll
+    for (int q = 0; q < NSW; q++)
+        invA[q] = (ZOH && rec && dv && n0 + q < n) ? inv_a_from_alog(p.A_log[d * n + n0 + q]) : 0.0f;
     auto rec_chunk = [&](auto ph, int c) {
         constexpr int PH = decltype(ph)::value;
         constexpr int K0 = PH, K1 = (PH + 1) % 3;    // ring slots of chunks c, c+1
@@ -516,8 +530,12 @@ __global__ __launch_bounds__((SC + kSeqElemWaves + 1) * 64) void scan_seq(const 
             float acc = 0.0f;
 #pragma unroll
             for (int q = 0; q < NSW; q++) {
-                const float a = exp2_hw(dl * A2[q]);
-                h[q] = fmaf(a, h[q], wv * bcv[q]);
+                const float x2 = dl * A2[q];
+                const float a = exp2_hw(x2);
+                if constexpr (ZOH)
+                    h[q] = fmaf(a, h[q], zoh_weight(dl, x2, a, invA[q]) * (wv * bcv[q]));
+                else
+                    h[q] = fmaf(a, h[q], wv * bcv[q]);
                 acc = fmaf(bcv[NSW + q], h[q], acc);
             }
             if (j & 1) {

@@ -125,4 +125,34 @@ __device__ __forceinline__ float a2_from_alog(float a_log) {
     return -exp2_hw(a_log * kLog2e) * kLog2e;
 }
 
+// 1 / A = -exp(-A_log).
+__device__ __forceinline__ float inv_a_from_alog(float a_log) {
+    return -exp2_hw(-a_log * kLog2e);
+}
+
+// Zero-order-hold input weight (exp(delta' A) - 1) / A of one state (mhpn.cn
+// selective_scan walk-through, section 6: the exact discretisation of the B
+// term, which for a diagonal A acts state by state), given x2 = delta' A2,
+// a = exp2(x2) and invA = 1 / A.
+//   |x2| >= 1/2: |a - 1| > 0.29, so (a - 1) / A loses less than 2^-22 to the
+//     cancellation and is used as it stands.
+//   |x2| <  1/2: the weight is delta' E(x) with E(x) = expm1(x) / x and
+//     x = x2 ln 2, |x| < 0.35, from its Taylor series sum_k x^k / (k+1)! cut
+//     after x^6 (the first dropped term is below 1.6e-8 relative), written in
+//     powers of x2 and evaluated by Horner's rule; in fp32 the result is
+//     within 8e-8 relative of E.
+__device__ __forceinline__ float zoh_weight(float dl, float x2, float a, float invA) {
+    constexpr double l = 0.6931471805599453;   // ln 2; c_k = ln2^k / (k+1)!
+    constexpr float c6 = float(l * l * l * l * l * l / 5040.0), c5 = float(l * l * l * l * l / 720.0),
+                    c4 = float(l * l * l * l / 120.0), c3 = float(l * l * l / 24.0), c2 = float(l * l / 6.0),
+                    c1 = float(l / 2.0);
+    float e = fmaf(c6, x2, c5);
+    e = fmaf(e, x2, c4);
+    e = fmaf(e, x2, c3);
+    e = fmaf(e, x2, c2);
+    e = fmaf(e, x2, c1);
+    e = fmaf(e, x2, 1.0f);
+    return fabsf(x2) < 0.5f ? dl * e : (a - 1.0f) * invA;
+}
+
 }  // namespace ss

@@ -79,10 +79,11 @@ SeqShape seq_shape(int64_t n) {
     return {8, 8};
 }
 
-// scan_seq for every n; SS_SCAN_VARIANT=tpar selects scan_tpar for n <= 2 (tests).
-ScanKernel choose_kernel(int64_t n) {
+// scan_seq for every n; SS_SCAN_VARIANT=tpar selects scan_tpar for n <= 2
+// (tests), which starts from a zero state with the delta' input weight only.
+ScanKernel choose_kernel(const ScanParams& p, bool zoh) {
     const char* v = std::getenv("SS_SCAN_VARIANT");
-    if (v && std::strcmp(v, "tpar") == 0 && n <= 2) return ScanKernel::Tpar;
+    if (v && std::strcmp(v, "tpar") == 0 && p.n <= 2 && !p.h0 && !zoh) return ScanKernel::Tpar;
     return ScanKernel::Seq;
 }
 
@@ -164,7 +165,7 @@ int choose_segments(int64_t G, int64_t L, int T, int64_t slots) {
 }
 
 template <typename TIn, int SC, int NSW>
-int launch_seq(ScanParams p, void* ws, size_t ws_bytes, hipStream_t st) {
+int launch_seq(ScanParams p, bool zoh, void* ws, size_t ws_bytes, hipStream_t st) {
     constexpr int TW = ss::seq_chunk<TIn, SC, NSW, true>(), TN = ss::seq_chunk<TIn, SC, NSW, false>();
     constexpr int threads = (SC + ss::kSeqElemWaves + 1) * 64;
     const int64_t G = p.b * p.nblk_d;
@@ -172,17 +173,28 @@ int launch_seq(ScanParams p, void* ws, size_t ws_bytes, hipStream_t st) {
     if (!ws || ws_bytes < w.total) return SS_ERR_WORKSPACE;
 
     // Wide path: whole 16-byte pieces per row and 16-byte aligned u, delta, z;
-    // y aligned for V-element stores.
-    const bool wide = (p.d_in * int64_t(sizeof(TIn))) % 16 == 0 && aligned(p.u, 16) && aligned(p.delta, 16) &&
-                      (!p.z || aligned(p.z, 16)) && aligned(p.y, (TW / ss::kSeqElemWaves) * sizeof(TIn));
+    // y aligned for V-element stores.  The zero-order-hold kernels exist in
+    // the element-load form only: their recurrence costs about three times
+    // the Euler one, which hides the difference in load width.
+    const bool wide = !zoh && (p.d_in * int64_t(sizeof(TIn))) % 16 == 0 && aligned(p.u, 16) &&
+                      aligned(p.delta, 16) && (!p.z || aligned(p.z, 16)) &&
+                      aligned(p.y, (TW / ss::kSeqElemWaves) * sizeof(TIn));
     const int T = wide ? TW : TN;
-    const int variant = (wide ? 4 : 0) | (p.softplus ? 2 : 0) | (p.z ? 1 : 0);
+    const int variant = (zoh ? 8 : wide ? 4 : 0) | (p.softplus ? 2 : 0) | (p.z ? 1 : 0);
     using Kern = void (*)(ScanParams);
-    static constexpr Kern kernels[8] = {
-        ss::scan_seq<TIn, SC, NSW, TN, false, false, false>, ss::scan_seq<TIn, SC, NSW, TN, false, false, true>,
-        ss::scan_seq<TIn, SC, NSW, TN, false, true, false>,  ss::scan_seq<TIn, SC, NSW, TN, false, true, true>,
-        ss::scan_seq<TIn, SC, NSW, TW, true, false, false>,  ss::scan_seq<TIn, SC, NSW, TW, true, false, true>,
-        ss::scan_seq<TIn, SC, NSW, TW, true, true, false>,   ss::scan_seq<TIn, SC, NSW, TW, true, true, true>};
+    static constexpr Kern kernels[12] = {
+        ss::scan_seq<TIn, SC, NSW, TN, false, false, false, false>,
+        ss::scan_seq<TIn, SC, NSW, TN, false, false, true, false>,
+        ss::scan_seq<TIn, SC, NSW, TN, false, true, false, false>,
+        ss::scan_seq<TIn, SC, NSW, TN, false, true, true, false>,
+        ss::scan_seq<TIn, SC, NSW, TW, true, false, false, false>,
+        ss::scan_seq<TIn, SC, NSW, TW, true, false, true, false>,
+        ss::scan_seq<TIn, SC, NSW, TW, true, true, false, false>,
+        ss::scan_seq<TIn, SC, NSW, TW, true, true, true, false>,
+        ss::scan_seq<TIn, SC, NSW, TN, false, false, false, true>,
+        ss::scan_seq<TIn, SC, NSW, TN, false, false, true, true>,
+        ss::scan_seq<TIn, SC, NSW, TN, false, true, false, true>,
+        ss::scan_seq<TIn, SC, NSW, TN, false, true, true, true>};
     const Kern kern = kernels[variant];
     const size_t lds = wide ? ss::SeqLds<TW, SC, SC * NSW, sizeof(TIn), true>::bytes
                             : ss::SeqLds<TN, SC, SC * NSW, sizeof(TIn), false>::bytes;
@@ -210,13 +222,15 @@ int launch_seq(ScanParams p, void* ws, size_t ws_bytes, hipStream_t st) {
 }
 
 template <typename TIn>
-int dispatch_seq(const ScanParams& p, void* ws, size_t ws_bytes, hipStream_t st) {
+int dispatch_seq(const ScanParams& p, bool zoh, void* ws, size_t ws_bytes, hipStream_t st) {
     const SeqShape sh = seq_shape(p.n);
-    if (sh.SC == 1) return launch_seq<TIn, 1, 2>(p, ws, ws_bytes, st);
-    if (sh.SC == 4) return sh.NSW == 2 ? launch_seq<TIn, 4, 2>(p, ws, ws_bytes, st) : launch_seq<TIn, 4, 4>(p, ws, ws_bytes, st);
-    if (sh.NSW == 2) return launch_seq<TIn, 8, 2>(p, ws, ws_bytes, st);
-    if (sh.NSW == 4) return launch_seq<TIn, 8, 4>(p, ws, ws_bytes, st);
-    return launch_seq<TIn, 8, 8>(p, ws, ws_bytes, st);
+    if (sh.SC == 1) return launch_seq<TIn, 1, 2>(p, zoh, ws, ws_bytes, st);
+    if (sh.SC == 4)
+        return sh.NSW == 2 ? launch_seq<TIn, 4, 2>(p, zoh, ws, ws_bytes, st)
+                           : launch_seq<TIn, 4, 4>(p, zoh, ws, ws_bytes, st);
+    if (sh.NSW == 2) return launch_seq<TIn, 8, 2>(p, zoh, ws, ws_bytes, st);
+    if (sh.NSW == 4) return launch_seq<TIn, 8, 4>(p, zoh, ws, ws_bytes, st);
+    return launch_seq<TIn, 8, 8>(p, zoh, ws, ws_bytes, st);
 }
 
 template <typename TIn>
@@ -244,6 +258,7 @@ SS_EXPORT const char* ss_status_string(int status) {
         case SS_ERR_HIP: return "the HIP runtime refused the launch";
         case SS_ERR_ALIAS: return "an output overlaps an input";
         case SS_ERR_ALIGN: return "a pointer is not aligned to its element size";
+        case SS_ERR_MODE: return "discretization is not SS_DISC_EULER or SS_DISC_ZOH";
         default: return "unknown status";
     }
 }
@@ -257,20 +272,23 @@ SS_EXPORT size_t ss_scan_fwd_workspace_bytes(int64_t b, int64_t L, int64_t d_in,
     return seq_workspace(b, L, d_in, n).total;
 }
 
-SS_EXPORT int ss_scan_fwd(const void* u, const void* delta, const float* A_log, const void* B, const void* C,
-                          const float* D, const void* z, const float* delta_bias, int delta_softplus, void* y,
-                          float* last_state, int64_t b, int64_t L, int64_t d_in, int64_t n, int dtype,
-                          void* workspace, size_t workspace_bytes, void* stream) {
+SS_EXPORT int ss_scan_fwd_ex(const void* u, const void* delta, const float* A_log, const void* B, const void* C,
+                             const float* D, const void* z, const float* delta_bias, int delta_softplus,
+                             const float* initial_state, int discretization, void* y, float* last_state, int64_t b,
+                             int64_t L, int64_t d_in, int64_t n, int dtype, void* workspace, size_t workspace_bytes,
+                             void* stream) {
     if (!u || !delta || !A_log || !B || !C || !D || !y) return SS_ERR_NULL;
     if (!sizes_ok(b, L, d_in) || n <= 0 || d_in > SS_MAX_CHANNELS) return SS_ERR_SHAPE;
     if (dtype != SS_F32 && dtype != SS_BF16) return SS_ERR_DTYPE;
     if (n > SS_MAX_STATE) return SS_ERR_UNSUPPORTED;
     if (b * ((d_in + 63) / 64) > kMaxWorkgroups || L > kMaxLength) return SS_ERR_SHAPE;
+    if (discretization != SS_DISC_EULER && discretization != SS_DISC_ZOH) return SS_ERR_MODE;
     const size_t es = elem_size(dtype);
     for (const void* p : {u, delta, B, C, z, static_cast<const void*>(y)})
         if (p && !aligned(p, es)) return SS_ERR_ALIGN;
     for (const void* p : {static_cast<const void*>(A_log), static_cast<const void*>(D),
-                          static_cast<const void*>(delta_bias), static_cast<const void*>(last_state)})
+                          static_cast<const void*>(delta_bias), static_cast<const void*>(initial_state),
+                          static_cast<const void*>(last_state)})
         if (p && !aligned(p, 4)) return SS_ERR_ALIGN;
     const int64_t nel = b * L * d_in;
     const Range ins[] = {range_of(u, nel, es), range_of(delta, nel, es), range_of(A_log, d_in * n, 4),
@@ -278,16 +296,21 @@ SS_EXPORT int ss_scan_fwd(const void* u, const void* delta, const float* A_log, 
                          range_of(z, z ? nel : 0, es), range_of(delta_bias, delta_bias ? d_in : 0, 4)};
     const Range ry = range_of(y, nel, es);
     const Range rs = range_of(last_state, last_state ? b * d_in * n : 0, 4);
+    // The initial state may be read and overwritten in place as last_state
+    // (each workgroup reads its own states before it, or the last segment of
+    // its channels, writes them); any other overlap with an output is refused.
+    const Range rh = range_of(initial_state, initial_state ? b * d_in * n : 0, 4);
+    const bool in_place = initial_state && static_cast<const void*>(initial_state) == last_state;
     for (const Range& r : ins)
         if (overlaps(r, ry) || overlaps(r, rs)) return SS_ERR_ALIAS;
-    if (overlaps(ry, rs)) return SS_ERR_ALIAS;
+    if (overlaps(ry, rs) || overlaps(rh, ry) || (!in_place && overlaps(rh, rs))) return SS_ERR_ALIAS;
     const size_t need = ss_scan_fwd_workspace_bytes(b, L, d_in, n, dtype);
     if (need > 0 && (!workspace || workspace_bytes < need)) return SS_ERR_WORKSPACE;
     if (need > 0) {
         const Range rw = range_of(workspace, int64_t(workspace_bytes), 1);
         for (const Range& r : ins)
             if (overlaps(r, rw)) return SS_ERR_ALIAS;
-        if (overlaps(ry, rw) || overlaps(rs, rw)) return SS_ERR_ALIAS;
+        if (overlaps(ry, rw) || overlaps(rs, rw) || overlaps(rh, rw)) return SS_ERR_ALIAS;
     }
 
     ScanParams p{};
@@ -301,6 +324,7 @@ SS_EXPORT int ss_scan_fwd(const void* u, const void* delta, const float* A_log, 
     p.bias = delta_bias;
     p.y = y;
     p.last_state = last_state;
+    p.h0 = initial_state;
     p.b = b;
     p.L = L;
     p.d_in = d_in;
@@ -311,19 +335,30 @@ SS_EXPORT int ss_scan_fwd(const void* u, const void* delta, const float* A_log, 
     p.Lseg = L;
     hipStream_t st = static_cast<hipStream_t>(stream);
 
-    if (choose_kernel(n) == ScanKernel::Tpar)
+    const bool zoh = discretization == SS_DISC_ZOH;
+    if (choose_kernel(p, zoh) == ScanKernel::Tpar)
         return dtype == SS_BF16 ? dispatch_tpar<uint16_t>(p, st) : dispatch_tpar<float>(p, st);
-    return dtype == SS_BF16 ? dispatch_seq<uint16_t>(p, workspace, workspace_bytes, st)
-                            : dispatch_seq<float>(p, workspace, workspace_bytes, st);
+    return dtype == SS_BF16 ? dispatch_seq<uint16_t>(p, zoh, workspace, workspace_bytes, st)
+                            : dispatch_seq<float>(p, zoh, workspace, workspace_bytes, st);
 }
 
-SS_EXPORT int ss_state_update(float* state, const void* x, const void* dt, const float* A_log, const void* B,
-                              const void* C, const float* D, const void* z, const float* dt_bias, int dt_softplus,
-                              void* y, int64_t b, int64_t d_in, int64_t n, int dtype, void* stream) {
+SS_EXPORT int ss_scan_fwd(const void* u, const void* delta, const float* A_log, const void* B, const void* C,
+                          const float* D, const void* z, const float* delta_bias, int delta_softplus, void* y,
+                          float* last_state, int64_t b, int64_t L, int64_t d_in, int64_t n, int dtype,
+                          void* workspace, size_t workspace_bytes, void* stream) {
+    return ss_scan_fwd_ex(u, delta, A_log, B, C, D, z, delta_bias, delta_softplus, nullptr, SS_DISC_EULER, y,
+                          last_state, b, L, d_in, n, dtype, workspace, workspace_bytes, stream);
+}
+
+SS_EXPORT int ss_state_update_ex(float* state, const void* x, const void* dt, const float* A_log, const void* B,
+                                 const void* C, const float* D, const void* z, const float* dt_bias, int dt_softplus,
+                                 int discretization, void* y, int64_t b, int64_t d_in, int64_t n, int dtype,
+                                 void* stream) {
     if (!state || !x || !dt || !A_log || !B || !C || !D || !y) return SS_ERR_NULL;
     if (!sizes_ok(b, d_in, 1) || n <= 0 || !sizes_ok(b, d_in, n) || b * d_in > kMaxStepChannels) return SS_ERR_SHAPE;
     if (dtype != SS_F32 && dtype != SS_BF16) return SS_ERR_DTYPE;
     if (n > SS_MAX_STATE) return SS_ERR_UNSUPPORTED;
+    if (discretization != SS_DISC_EULER && discretization != SS_DISC_ZOH) return SS_ERR_MODE;
     const size_t es = elem_size(dtype);
     for (const void* p : {x, dt, B, C, z, static_cast<const void*>(y)})
         if (p && !aligned(p, es)) return SS_ERR_ALIGN;
@@ -355,6 +390,7 @@ SS_EXPORT int ss_state_update(float* state, const void* x, const void* dt, const
     p.d_in = d_in;
     p.n = n;
     p.softplus = dt_softplus ? 1 : 0;
+    p.zoh = discretization == SS_DISC_ZOH ? 1 : 0;
     hipStream_t st = static_cast<hipStream_t>(stream);
 
     const int64_t lpc = n / 4;
@@ -390,4 +426,11 @@ SS_EXPORT int ss_state_update(float* state, const void* x, const void* dt, const
             hipLaunchKernelGGL((ss::state_update_any<float>), grid, dim3(256), 0, st, p);
     }
     return hipGetLastError() == hipSuccess ? SS_OK : SS_ERR_HIP;
+}
+
+SS_EXPORT int ss_state_update(float* state, const void* x, const void* dt, const float* A_log, const void* B,
+                              const void* C, const float* D, const void* z, const float* dt_bias, int dt_softplus,
+                              void* y, int64_t b, int64_t d_in, int64_t n, int dtype, void* stream) {
+    return ss_state_update_ex(state, x, dt, A_log, B, C, D, z, dt_bias, dt_softplus, SS_DISC_EULER, y, b, d_in, n,
+                              dtype, stream);
 }

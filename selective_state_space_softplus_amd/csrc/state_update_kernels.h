@@ -3,6 +3,8 @@
 //     delta' = softplus(dt + dt_bias)
 //     state[k] = exp(delta' A[d,k]) state[k] + delta' B[b,k] x      (in place)
 //     y = sum_k C[b,k] state[k] + D[d] x,   then y *= silu(z) if z is given.
+// With the zero-order hold (mhpn.cn selective_scan walk-through, section 6)
+// the input term is (exp(delta' A[d,k]) - 1) / A[d,k] * B[b,k] x instead.
 // The step reads and writes the whole fp32 state once, so it is bound by HBM
 // bandwidth; everything else is small.
 //
@@ -32,7 +34,17 @@ struct StepParams {
     void* y;
     int64_t b, d_in, n;
     int softplus;
+    int zoh;             // zero-order-hold input weight instead of delta'
 };
+
+// New value of one state: exp(delta' A) s + w B x, where w is delta' or the
+// zero-order-hold weight (exp(delta' A) - 1) / A.
+__device__ __forceinline__ float step_state(float s, float dl, float xv, float a_log, float Bk, int zoh) {
+    const float x2 = dl * a2_from_alog(a_log);
+    const float a = exp2_hw(x2);
+    const float w = zoh ? zoh_weight(dl, x2, a, inv_a_from_alog(a_log)) : dl;
+    return fmaf(a, s, (w * xv) * Bk);
+}
 
 template <typename TIn>
 __device__ __forceinline__ float4 load4(const TIn* p, int64_t i);
@@ -71,7 +83,6 @@ __global__ __launch_bounds__(256) void state_update_vec(const StepParams p) {
 
     const float xv = Elem<TIn>::load(xp, ch);
     const float dl = step_size(Elem<TIn>::load(dtp, ch), p.bias ? p.bias[d] : 0.0f, p.softplus);
-    const float wv = dl * xv;
 
     float4* sp = reinterpret_cast<float4*>(p.state) + ch * LPC + q;
     float4 s = *sp;
@@ -79,10 +90,10 @@ __global__ __launch_bounds__(256) void state_update_vec(const StepParams p) {
     const float4 Bv = load4<TIn>(Bm, bi * n + 4 * q);
     const float4 Cv = load4<TIn>(Cm, bi * n + 4 * q);
 
-    s.x = fmaf(exp2_hw(dl * a2_from_alog(al.x)), s.x, wv * Bv.x);
-    s.y = fmaf(exp2_hw(dl * a2_from_alog(al.y)), s.y, wv * Bv.y);
-    s.z = fmaf(exp2_hw(dl * a2_from_alog(al.z)), s.z, wv * Bv.z);
-    s.w = fmaf(exp2_hw(dl * a2_from_alog(al.w)), s.w, wv * Bv.w);
+    s.x = step_state(s.x, dl, xv, al.x, Bv.x, p.zoh);
+    s.y = step_state(s.y, dl, xv, al.y, Bv.y, p.zoh);
+    s.z = step_state(s.z, dl, xv, al.z, Bv.z, p.zoh);
+    s.w = step_state(s.w, dl, xv, al.w, Bv.w, p.zoh);
     *sp = s;
 
     float acc = fmaf(Cv.x, s.x, fmaf(Cv.y, s.y, fmaf(Cv.z, s.z, Cv.w * s.w)));
@@ -112,12 +123,10 @@ __global__ __launch_bounds__(256) void state_update_any(const StepParams p) {
 
     const float xv = Elem<TIn>::load(xp, ch);
     const float dl = step_size(Elem<TIn>::load(dtp, ch), p.bias ? p.bias[d] : 0.0f, p.softplus);
-    const float wv = dl * xv;
     float acc = 0.0f;
     for (int64_t k = 0; k < n; k++) {
-        const float a = exp2_hw(dl * a2_from_alog(p.A_log[d * n + k]));
-        float s = p.state[ch * n + k];
-        s = fmaf(a, s, wv * Elem<TIn>::load(Bm, bi * n + k));
+        const float s = step_state(p.state[ch * n + k], dl, xv, p.A_log[d * n + k], Elem<TIn>::load(Bm, bi * n + k),
+                                   p.zoh);
         p.state[ch * n + k] = s;
         acc = fmaf(Elem<TIn>::load(Cm, bi * n + k), s, acc);
     }

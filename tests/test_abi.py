@@ -11,7 +11,7 @@ import pytest
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "ss_scan.h")
 
-OK, NULL, SHAPE, DTYPE, UNSUP, WS, HIP, ALIAS, ALIGN = 0, -1, -2, -3, -4, -5, -6, -7, -8
+OK, NULL, SHAPE, DTYPE, UNSUP, WS, HIP, ALIAS, ALIGN, MODE = 0, -1, -2, -3, -4, -5, -6, -7, -8, -9
 
 
 @pytest.fixture(scope="module")
@@ -28,8 +28,8 @@ def declared_functions():
 
 
 def test_header_declares_the_entry_points():
-    assert declared_functions() == sorted(["ss_scan_fwd", "ss_scan_fwd_workspace_bytes", "ss_state_update",
-                                           "ss_status_string"])
+    assert declared_functions() == sorted(["ss_scan_fwd", "ss_scan_fwd_ex", "ss_scan_fwd_workspace_bytes",
+                                           "ss_state_update", "ss_state_update_ex", "ss_status_string"])
 
 
 def test_library_exports_every_declared_symbol(ss):
@@ -40,7 +40,7 @@ def test_library_exports_every_declared_symbol(ss):
 
 
 def test_status_strings(ss):
-    for code in (OK, NULL, SHAPE, DTYPE, UNSUP, WS, HIP, ALIAS, ALIGN):
+    for code in (OK, NULL, SHAPE, DTYPE, UNSUP, WS, HIP, ALIAS, ALIGN, MODE):
         s = ss.status_string(code)
         assert s and s != "unknown status"
     assert ss.status_string(12345) == "unknown status"
@@ -50,9 +50,11 @@ def test_status_codes_match_header(ss):
     text = open(HEADER).read()
     for name, code in (("SS_OK", OK), ("SS_ERR_NULL", NULL), ("SS_ERR_SHAPE", SHAPE), ("SS_ERR_DTYPE", DTYPE),
                        ("SS_ERR_UNSUPPORTED", UNSUP), ("SS_ERR_WORKSPACE", WS), ("SS_ERR_HIP", HIP),
-                       ("SS_ERR_ALIAS", ALIAS), ("SS_ERR_ALIGN", ALIGN)):
+                       ("SS_ERR_ALIAS", ALIAS), ("SS_ERR_ALIGN", ALIGN), ("SS_ERR_MODE", MODE)):
         assert re.search(rf"\b{name}\s*=\s*{code}\b", text), name
         assert ss.STATUS[code] == name
+    for name, code in (("SS_DISC_EULER", ss.SS_DISC_EULER), ("SS_DISC_ZOH", ss.SS_DISC_ZOH)):
+        assert re.search(rf"\b{name}\s*=\s*{code}\b", text), name
 
 
 def test_workspace_query(ss):
@@ -143,3 +145,50 @@ def test_python_binding_checks_tensors(ss):
                     torch.zeros(4, dtype=torch.float64))
     with pytest.raises((TypeError, ValueError)):
         ss.scan_fwd(u, u[:, :4], torch.zeros(4, 16), torch.zeros(2, 8, 16), torch.zeros(2, 8, 16), torch.zeros(4))
+
+
+def call_scan_ex(ss, a, h0=None, disc=0):
+    return ss.lib.ss_scan_fwd_ex(a["u"], a["delta"], a["A_log"], a["B"], a["C"], a["D"], a["z"], a["bias"],
+                                 a["softplus"], h0, disc, a["y"], a["last"], a["b"], a["L"], a["d_in"], a["n"],
+                                 a["dtype"], a["ws"], a["ws_bytes"], a["stream"])
+
+
+@pytest.mark.parametrize("over,h0,disc,code", [
+    ({}, None, 2, MODE), ({}, None, -1, MODE), ({}, addr(12), 7, MODE),
+    ({}, addr(12) + 2, 0, ALIGN),
+    ({}, addr(9), 1, ALIAS),                      # initial state on top of y
+    ({}, addr(10) + 4, 0, ALIAS),                 # initial state partly over last_state
+    ({}, addr(11) + 64, 1, ALIAS),                # initial state inside the workspace
+    (dict(ws_bytes=100), addr(10), 1, WS),        # in place (== last_state) passes the alias check
+    (dict(ws_bytes=100), addr(12), 1, WS),
+    (dict(n=0), addr(12), 1, SHAPE), (dict(u=None), addr(12), 1, NULL),
+])
+def test_scan_ex_rejects(ss, over, h0, disc, code):
+    assert call_scan_ex(ss, scan_args(**over), h0, disc) == code
+
+
+def test_scan_ex_is_scan_with_defaults(ss):
+    # With no initial state and Euler weights, every rejection matches ss_scan_fwd's.
+    for over in (dict(u=None), dict(b=0), dict(dtype=2), dict(n=65), dict(ws=None), dict(u=addr(1) + 2),
+                 dict(y=addr(10)), dict(ws_bytes=100)):
+        a = scan_args(**over)
+        assert call_scan_ex(ss, a) == call_scan(ss, a), over
+
+
+def test_step_ex_rejects(ss):
+    a = step_args()
+    args = lambda a, disc: (a["state"], a["x"], a["dt"], a["A_log"], a["B"], a["C"], a["D"], a["z"],  # noqa: E731
+                            a["bias"], a["softplus"], disc, a["y"], a["b"], a["d_in"], a["n"], a["dtype"], a["stream"])
+    assert ss.lib.ss_state_update_ex(*args(a, 2)) == MODE
+    assert ss.lib.ss_state_update_ex(*args(a, -3)) == MODE
+    for over, code in ((dict(x=None), NULL), (dict(n=65), UNSUP), (dict(y=addr(2)), ALIAS)):
+        assert ss.lib.ss_state_update_ex(*args(step_args(**over), 1)) == code, over
+
+
+def test_python_binding_checks_initial_state(ss):
+    import torch
+
+    u = torch.zeros(2, 8, 4)
+    with pytest.raises((TypeError, ValueError)):
+        ss.scan_fwd(u, u, torch.zeros(4, 16), torch.zeros(2, 8, 16), torch.zeros(2, 8, 16), torch.zeros(4),
+                    initial_state=torch.zeros(2, 4, 15))
