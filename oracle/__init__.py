@@ -6,7 +6,7 @@ and by the CPU-baseline leg of ``bench.py``; never by the library itself.
 The arithmetic lives in ``ss_oracle.c`` (plain C, double, sequential loops in
 the order the pages define them: the mamba-minimal ``selective_scan`` walk-through
 on the mhpn.cn page, sections 2-5 and 7, and ``Mamba.step`` on the
-jiafeimiao.top page).  This module only widens inputs to float64 and calls it
+jiafeimiao.top page, including its convolution step).  This module only widens inputs to float64 and calls it
 through ctypes.  Parity of every function here is pinned by
 ``tests/test_oracle_pins.py`` (brute force, closed forms, limits, invariants).
 """
@@ -60,6 +60,8 @@ def _bind(lib: ctypes.CDLL) -> ctypes.CDLL:
     lib.ss_oracle_scan_ex.argtypes = [P] * 8 + [ctypes.c_int, P, ctypes.c_int, P, P, I64, I64, I64, I64]
     lib.ss_oracle_state_update_ex.restype = ctypes.c_int
     lib.ss_oracle_state_update_ex.argtypes = [P] * 9 + [ctypes.c_int, ctypes.c_int, P, I64, I64, I64]
+    lib.ss_oracle_conv_update.restype = ctypes.c_int
+    lib.ss_oracle_conv_update.argtypes = [P] * 4 + [ctypes.c_int, P, I64, I64, I64]
     return lib
 
 
@@ -147,3 +149,22 @@ def scan_channels(inputs: dict, channels, delta_softplus=True, lib=None, zoh=Fal
                        h0=None if inputs.get("h0") is None else inputs["h0"][bi:bi + 1, d:d + 1], zoh=zoh)
         out[(bi, d)] = (y[0, :, 0], last[0, 0])
     return out
+
+
+def conv_update(conv_state, x, weight, bias=None, act=True, lib=None):
+    """One convolution step on a copy of ``conv_state``: returns (new_state (b, d_in, W), out (b, d_in)).
+
+    conv_state: (b, d_in, W); x: (b, d_in); weight: (d_in, W); bias: (d_in) or None; act: apply silu.
+    """
+    lib = lib or load()
+    st = _f64(conv_state).copy()
+    x, weight, bias = _f64(x), _f64(weight), _f64(bias)
+    b, d_in, W = st.shape
+    assert x.shape == (b, d_in) and weight.shape == (d_in, W)
+    assert bias is None or bias.shape == (d_in,)
+    out = np.empty((b, d_in), np.float64)
+    rc = lib.ss_oracle_conv_update(_ptr(st), _ptr(x), _ptr(weight), _ptr(bias), int(bool(act)), _ptr(out),
+                                   b, d_in, W)
+    if rc != 0:
+        raise ValueError(f"ss_oracle_conv_update returned {rc}")
+    return st, out

@@ -26,11 +26,17 @@
  * of zero) and the zero-order-hold input weight (exp(delta*A) - 1)/A * B in
  * place of forward Euler delta*B (mhpn.cn page, sections 3.2 and 6).
  *
+ * ss_oracle_conv_update is the convolution step that Mamba.step runs before
+ * the SSM step (jiafeimiao.top page, the "Conv step" branch written out in
+ * torch): a rolling window of the last W inputs per channel, a depthwise dot
+ * product with the channel's W weights, the bias, then silu.
+ *
  * Layouts (row-major, last index fastest):
  *   u, delta, z, y : (b, L, d_in)      B, C : (b, L, n)
  *   A_log          : (d_in, n)         D, delta_bias : (d_in)
  *   state, h0, last_state : (b, d_in, n)
  *   x, dt, z, y of the step : (b, d_in)     B, C of the step : (b, n)
+ *   conv_state : (b, d_in, W)   conv weight : (d_in, W)   conv bias : (d_in)
  * Return value: 0 on success, -1 on a NULL required pointer, -2 on a
  * non-positive size.
  */
@@ -179,4 +185,38 @@ int ss_oracle_state_update(double *state, const double *x, const double *dt,
 {
     return ss_oracle_state_update_ex(state, x, dt, A_log, B, C, D, z, dt_bias, dt_softplus, 0,
                                      y, b, d_in, n);
+}
+
+/* One convolution step of Mamba.step (jiafeimiao.top page, "Conv step"):
+ *   1. the window conv_state[b, d, 0..W-1] moves one place towards index 0
+ *      (torch.roll by -1 along the last axis; the value at index 0 leaves),
+ *   2. the new input x[b, d] is written at index W-1,
+ *   3. out = sum_w conv_state[b, d, w] * weight[d, w], plus bias[d] when a
+ *      bias is given,
+ *   4. out = silu(out) when act != 0 (the block's activation).
+ * conv_state is updated in place. */
+int ss_oracle_conv_update(double *conv_state, const double *x, const double *weight,
+                          const double *bias, int act, double *out,
+                          int64_t b, int64_t d_in, int64_t W)
+{
+    if (!conv_state || !x || !weight || !out)
+        return -1;
+    if (b <= 0 || d_in <= 0 || W <= 0)
+        return -2;
+
+    for (int64_t bi = 0; bi < b; bi++) {
+        for (int64_t d = 0; d < d_in; d++) {
+            double *win = &conv_state[(bi * d_in + d) * W];
+            for (int64_t w = 0; w + 1 < W; w++)          /* roll by -1 */
+                win[w] = win[w + 1];
+            win[W - 1] = x[bi * d_in + d];              /* newest input last */
+            double acc = 0.0;
+            for (int64_t w = 0; w < W; w++)
+                acc += win[w] * weight[d * W + w];
+            if (bias)
+                acc += bias[d];
+            out[bi * d_in + d] = act ? ss_oracle_silu(acc) : acc;
+        }
+    }
+    return 0;
 }

@@ -14,7 +14,8 @@ disagrees with:
     step, a chain of steps equals the scan, prefill then decode equals the
     longer scan, B = 0 leaves only the D skip.
 The definition they pin is that of the mhpn.cn selective_scan walk-through
-(sections 2-5 and 7) and of Mamba.step on the jiafeimiao.top page.
+(sections 2-5 and 7) and of Mamba.step on the jiafeimiao.top page, whose
+convolution step is pinned to torch's depthwise conv1d and a delay line.
 """
 from __future__ import annotations
 
@@ -40,6 +41,12 @@ def _close(a, b, rtol=1e-12, atol=1e-13, what=""):
     assert np.all(np.isfinite(a)), f"{what}: non-finite values"
     err = np.max(np.abs(a - b) / (atol + rtol * np.abs(b))) if a.size else 0.0
     assert err <= 1.0, f"{what}: mismatch (scaled error {err:.3g})\n{a}\nvs\n{b}"
+
+
+def _exact(a, b, what=""):
+    a = np.asarray(a, np.float64)
+    b = np.asarray(b, np.float64)
+    assert a.shape == b.shape and np.array_equal(a, b), f"{what}: not identical\n{a}\nvs\n{b}"
 
 
 def random_case(seed, b=2, L=9, d_in=3, n=4, gated=True, bias=True, softplus=True):
@@ -326,6 +333,55 @@ def pin_zoh(lib):
     _close(state, last, rtol=1e-12, atol=1e-13, what="zoh chain state")
 
 
+def pin_conv_update(lib):
+    """The convolution step before the SSM step in Mamba.step (jiafeimiao.top page, "Conv step").
+
+    - Chained over a sequence from a zero window, the steps equal torch's
+      depthwise conv1d with W - 1 zeros of left padding (a causal filter,
+      out_t = sum_w weight[w] x_(t-W+1+w)), plus the bias, then silu -- for
+      W = 1 .. 4;
+    - with a one-hot weight at index j (no bias, no silu) the output is the
+      input W-1-j steps back: a delay line;
+    - after each step the window holds the last W inputs, oldest first;
+    - a case worked by hand.
+    """
+    import torch
+
+    r = _rng(23)
+    b, d_in, L = 2, 3, 11
+    for W in (1, 2, 3, 4):
+        xs = r.standard_normal((L, b, d_in))
+        weight = r.standard_normal((d_in, W))
+        bias = r.standard_normal(d_in)
+        st = np.zeros((b, d_in, W))
+        outs = []
+        for t in range(L):
+            st, o = oracle.conv_update(st, xs[t], weight, bias, True, lib=lib)
+            outs.append(o)
+            want = np.stack([xs[t - W + 1 + w] if t - W + 1 + w >= 0 else np.zeros((b, d_in)) for w in range(W)], -1)
+            _exact(st, want, what=f"conv window W={W} t={t}")
+        xt = torch.from_numpy(np.ascontiguousarray(xs.transpose(1, 2, 0)))           # (b, d_in, L)
+        ref = torch.nn.functional.conv1d(xt, torch.from_numpy(weight)[:, None, :], torch.from_numpy(bias),
+                                         padding=W - 1, groups=d_in)[..., :L]
+        ref = torch.nn.functional.silu(ref).numpy().transpose(2, 0, 1)              # (L, b, d_in)
+        _close(np.stack(outs), ref, rtol=1e-12, atol=1e-13, what=f"conv chain vs conv1d W={W}")
+    W = 4
+    xs = r.standard_normal((L, b, d_in))
+    for j in range(W):
+        weight = np.zeros((d_in, W))
+        weight[:, j] = 1.0
+        st = np.zeros((b, d_in, W))
+        for t in range(L):
+            st, o = oracle.conv_update(st, xs[t], weight, None, False, lib=lib)
+            lag = W - 1 - j
+            _exact(o, xs[t - lag] if t >= lag else np.zeros((b, d_in)), what=f"delay j={j} t={t}")
+    st, o = oracle.conv_update(np.array([[[1.0, 2.0, 3.0, 4.0]]]), np.array([[5.0]]), np.array([[1.0, 0.0, -1.0, 2.0]]),
+                               np.array([0.5]), True, lib=lib)
+    # window [2, 3, 4, 5]; 2*1 + 3*0 + 4*(-1) + 5*2 + 0.5 = 8.5; silu(8.5) = 8.5 / (1 + e^-8.5)
+    _exact(st, [[[2.0, 3.0, 4.0, 5.0]]], what="hand-worked window")
+    _close(o, [[8.5 / (1.0 + math.exp(-8.5))]], what="hand-worked output")
+
+
 ALL_PINS = [pin_softplus_silu, pin_hand_worked, pin_brute_force, pin_geometric_closed_form, pin_limits,
             pin_skip_and_gate, pin_linearity_causality, pin_step_matches_scan, pin_bias_placement,
-            pin_initial_state, pin_zoh]
+            pin_initial_state, pin_zoh, pin_conv_update]

@@ -71,6 +71,15 @@ MUTANTS = [
      "double dB = input_weight(dl, A, B[bi * n + k], 0);"),
     ("step dropped skip", "yt += D[d] * x[e];", "yt += 0.0 * x[e];"),
     ("step A index", "double A = -exp(A_log[d * n + k]);", "double A = -exp(A_log[k]);"),
+    ("conv rolls the other way", "for (int64_t w = 0; w + 1 < W; w++)          /* roll by -1 */\n                win[w] = win[w + 1];",
+     "for (int64_t w = W - 1; w > 0; w--)\n                win[w] = win[w - 1];"),
+    ("conv without roll", "win[w] = win[w + 1];", "(void)0;"),
+    ("conv newest input first", "win[W - 1] = x[bi * d_in + d];", "win[0] = x[bi * d_in + d];"),
+    ("conv weight reversed", "acc += win[w] * weight[d * W + w];", "acc += win[w] * weight[d * W + (W - 1 - w)];"),
+    ("conv weight of channel 0", "acc += win[w] * weight[d * W + w];", "acc += win[w] * weight[w];"),
+    ("conv bias after silu", "if (bias)\n                acc += bias[d];\n            out[bi * d_in + d] = act ? ss_oracle_silu(acc) : acc;",
+     "out[bi * d_in + d] = (act ? ss_oracle_silu(acc) : acc) + (bias ? bias[d] : 0.0);"),
+    ("conv silu ignored", "out[bi * d_in + d] = act ? ss_oracle_silu(acc) : acc;", "out[bi * d_in + d] = acc;"),
 ]
 
 
