@@ -7,12 +7,15 @@ n=16, bf16 inputs/outputs, fp32 state, gated, delta bias, last state
 written), with every input already resident in HBM.  The value is achieved
 algorithmic HBM bandwidth in GB/s; state updates/s and the fraction of the
 8 TB/s HBM peak are reported beside it.  The decode step (b=256, d_in=5120,
-n=16, 64 back-to-back single-token steps) is timed in the same run.
+n=16, 64 back-to-back single-token steps) and the convolution step that
+precedes it in a decode step (same b and d_in, width 4, bf16) are timed in the
+same run.
 
 Algorithmic bytes are what the fused method must move (the (b, L, d_in, n)
 intermediates are never stored):
   scan   = s*(3 bLd [u, delta, y] + bLd [z] + 2 bLn [B, C]) + 4*(d n [A_log] + d [D] + d [bias]) + 4 b d n [last state]
   decode = 8 b d n [state read + write] + s*(4 b d [x, dt, z, y] + 2 b n [B, C]) + 4*(d n + 2 d)
+  conv   = s*b d (2 W [window read + write] + 2 [x, out]) + 4*(d W + d) [weight, bias]
 with s the input element size.
 
 The dominant kernel at n = 16 is bound by VALU issue, not by HBM: each state
@@ -55,6 +58,10 @@ def scan_bytes(b, L, d, n, s, gated=True, bias=True, last=True):
 
 def decode_bytes(b, d, n, s, gated=True, bias=True):
     return 8 * b * d * n + s * ((4 if gated else 3) * b * d + 2 * b * n) + 4 * (d * n + d + (d if bias else 0))
+
+
+def conv_bytes(b, d, W, s, bias=True):
+    return s * b * d * (2 * W + 2) + 4 * (d * W + (d if bias else 0))
 
 
 def kernel_source_hash() -> str:
@@ -234,6 +241,63 @@ def main(argv=None):
             "hbm_frac": round(db / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
             "updates_per_s": float(f"{dcfg.b * dcfg.d_in * dcfg.n / (ms * 1e-3):.4g}"),
             "algorithmic_bytes_per_step": db,
+        }
+        # The convolution step of the same decode step (width 4, bf16 window).
+        W = 4
+        gen = torch.Generator(device=dev).manual_seed(4)
+        cst = torch.randn(dcfg.b, dcfg.d_in, W, device=dev, generator=gen).to(torch.bfloat16)
+        cx = torch.randn(dcfg.steps, dcfg.b, dcfg.d_in, device=dev, generator=gen).to(torch.bfloat16)
+        cw = torch.randn(dcfg.d_in, W, device=dev, generator=gen) * 0.5
+        cb = torch.randn(dcfg.d_in, device=dev, generator=gen) * 0.1
+        cout = torch.empty(dcfg.b, dcfg.d_in, device=dev, dtype=torch.bfloat16)
+
+        def conv64():
+            for t in range(dcfg.steps):
+                ss.conv_update(cst, cx[t], cw, cb, silu=True, out=cout)
+
+        conv64()
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(reps):
+            conv64()
+        e1.record()
+        torch.cuda.synchronize()
+        cms = e0.elapsed_time(e1) / (reps * dcfg.steps)
+        cbytes = conv_bytes(dcfg.b, dcfg.d_in, W, 2)
+
+        # Both steps again as HIP graphs of 64 launches each: what a decode loop
+        # that captures its steps sees, without the per-call host overhead.
+        def graphed(fn):
+            side = torch.cuda.Stream(device=dev)
+            side.wait_stream(torch.cuda.current_stream(dev))
+            with torch.cuda.stream(side):
+                fn()
+            torch.cuda.current_stream(dev).wait_stream(side)
+            torch.cuda.synchronize()
+            graph = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(graph):
+                fn()
+            graph.replay()
+            torch.cuda.synchronize()
+            e0.record()
+            for _ in range(reps):
+                graph.replay()
+            e1.record()
+            torch.cuda.synchronize()
+            return e0.elapsed_time(e1) / (reps * dcfg.steps)
+
+        ms_g = graphed(run64)
+        cms_g = graphed(conv64)
+        result["decode"]["us_per_step_graph"] = round(ms_g * 1e3, 2)
+        result["decode"]["GBps_graph"] = round(db / (ms_g * 1e-3) / 1e9, 1)
+        result["decode"]["conv_step"] = {
+            "workload": f"conv step: b={dcfg.b} d_in={dcfg.d_in} W={W}, bf16 window/x/out, fp32 weight and bias, "
+                        f"silu, {dcfg.steps} back-to-back steps",
+            "us_per_step": round(cms * 1e3, 2),
+            "GBps": round(cbytes / (cms * 1e-3) / 1e9, 1),
+            "us_per_step_graph": round(cms_g * 1e3, 2),
+            "GBps_graph": round(cbytes / (cms_g * 1e-3) / 1e9, 1),
+            "algorithmic_bytes_per_step": cbytes,
         }
 
     if not args.no_cpu:

@@ -12,7 +12,8 @@
  *     (A = -exp(A_log), softplus keeps delta positive);
  *   - jiafeimiao.top, "代码连连看——mamba", the Mamba.step listing and the
  *     selective_state_update call that follows it (bias added to dt inside the
- *     softplus, in-place state update, gate y * silu(z) after the D skip).
+ *     softplus, in-place state update, gate y * silu(z) after the D skip),
+ *     and the convolution step that comes before it (ss_conv_update).
  *
  * For every batch b, channel d and time t (h starts at zero, or at a given
  * initial state with the _ex entry points):
@@ -182,6 +183,33 @@ int ss_state_update_ex(float *state, const void *x, const void *dt,
                        const float *D, const void *z, const float *dt_bias,
                        int dt_softplus, int discretization, void *y,
                        int64_t b, int64_t d_in, int64_t n, int dtype, void *stream);
+
+/* Largest convolution width W of ss_conv_update. */
+#define SS_MAX_CONV_WIDTH 8
+
+/*
+ * The convolution step that precedes the SSM step of a decode step
+ * (jiafeimiao.top page, Mamba.step, "Conv step": the causal depthwise
+ * convolution of the block applied to one new token).  Per (b, d) channel:
+ *     window[0 .. W-2] = window[1 .. W-1];  window[W-1] = x[b, d]
+ *     out[b, d] = sum_w window[w] * weight[d, w] + bias[d]      (bias optional)
+ *     out[b, d] = silu(out[b, d])                               (when silu != 0)
+ *
+ *   conv_state : (b, d_in, W)  dtype, the window, read and overwritten in place
+ *   x          : (b, d_in)     dtype, the new input
+ *   weight     : (d_in, W)     fp32 (the conv1d weight (d_in, 1, W) without its middle axis)
+ *   bias       : (d_in)        fp32, or NULL
+ *   silu       : nonzero -> apply silu to the output
+ *   out        : (b, d_in)     dtype, output (the x of the SSM step, after
+ *                              the caller's projections have produced dt, B, C from it)
+ * Sizes: b, d_in >= 1, b * d_in < 2^28, 1 <= W <= SS_MAX_CONV_WIDTH
+ * (else SS_ERR_SHAPE / SS_ERR_UNSUPPORTED).  out must not overlap any input
+ * and conv_state must not overlap x, weight or bias (SS_ERR_ALIAS).
+ * Returns an ss_status.
+ */
+int ss_conv_update(void *conv_state, const void *x, const float *weight,
+                   const float *bias, int silu, void *out,
+                   int64_t b, int64_t d_in, int64_t W, int dtype, void *stream);
 
 /* Static, NUL-terminated description of a status code. */
 const char *ss_status_string(int status);

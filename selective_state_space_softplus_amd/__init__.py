@@ -13,6 +13,8 @@ Entry points mirror the C ABI (``include/ss_scan.h``):
                                              -> y  or  (y, last_state)
   state_update(state, x, dt, A_log, B, C, D, z=None, dt_bias=None, dt_softplus=True,
                zoh=False)                    -> y  (state is updated in place)
+  conv_update(conv_state, x, weight, bias=None, silu=True)
+                                             -> out (b, d_in)  (conv_state is updated in place)
   scan_fwd_workspace_bytes(b, L, d_in, n, dtype) -> int
   status_string(code) -> str
 
@@ -23,6 +25,8 @@ state (b, d_in, n) fp32 updated in place; x, dt, z (b, d_in); B, C (b, n).
 ``initial_state`` (b, d_in, n) fp32 starts the scan from a given state and
 ``zoh=True`` selects the zero-order-hold input term (mhpn.cn, section 6); calls
 that use either go through ``ss_scan_fwd_ex`` / ``ss_state_update_ex``.
+``conv_update`` is the convolution step of Mamba.step (jiafeimiao.top): conv_state
+(b, d_in, W) in the dtype of x, weight (d_in, W) and bias (d_in) fp32.
 """
 from __future__ import annotations
 
@@ -37,12 +41,13 @@ LIBRARY = os.path.join(_HERE, "libss_scan.so")
 SS_F32 = 0
 SS_BF16 = 1
 SS_MAX_STATE = 64
+SS_MAX_CONV_WIDTH = 8
 SS_DISC_EULER = 0
 SS_DISC_ZOH = 1
 STATUS = {0: "SS_OK", -1: "SS_ERR_NULL", -2: "SS_ERR_SHAPE", -3: "SS_ERR_DTYPE", -4: "SS_ERR_UNSUPPORTED",
           -5: "SS_ERR_WORKSPACE", -6: "SS_ERR_HIP", -7: "SS_ERR_ALIAS", -8: "SS_ERR_ALIGN", -9: "SS_ERR_MODE"}
 EXPORTS = ("ss_scan_fwd_workspace_bytes", "ss_scan_fwd", "ss_scan_fwd_ex", "ss_state_update", "ss_state_update_ex",
-           "ss_status_string")
+           "ss_conv_update", "ss_status_string")
 
 
 class SSError(RuntimeError):
@@ -67,6 +72,8 @@ def _load() -> ctypes.CDLL:
     lib.ss_state_update.argtypes = [P, P, P, P, P, P, P, P, P, I, P, I64, I64, I64, I, P]
     lib.ss_state_update_ex.restype = I
     lib.ss_state_update_ex.argtypes = [P, P, P, P, P, P, P, P, P, I, I, P, I64, I64, I64, I, P]
+    lib.ss_conv_update.restype = I
+    lib.ss_conv_update.argtypes = [P, P, P, P, I, P, I64, I64, I64, I, P]
     lib.ss_status_string.restype = ctypes.c_char_p
     lib.ss_status_string.argtypes = [I]
     return lib
@@ -218,4 +225,27 @@ def state_update(state, x, dt, A_log, B, C, D, z=None, dt_bias=None, dt_softplus
                                         b, d_in, n, code, _stream(dev))
     if rc != 0:
         raise SSError(rc, where)
+    return y
+
+
+def conv_update(conv_state, x, weight, bias=None, silu=True, out=None):
+    """One convolution step; updates ``conv_state`` (b, d_in, W) in place and returns out (b, d_in)."""
+    if conv_state.dim() != 3:
+        raise ValueError("conv_state must be (b, d_in, W)")
+    b, d_in, W = conv_state.shape
+    dev = conv_state.device
+    code = _dtype_code(x.dtype)
+    _check(conv_state, "conv_state", (b, d_in, W), x.dtype, dev)
+    _check(x, "x", (b, d_in), x.dtype, dev)
+    _check(weight, "weight", (d_in, W), torch.float32, dev)
+    _check(bias, "bias", (d_in,), torch.float32, dev)
+    y = torch.empty_like(x) if out is None else out
+    _check(y, "out", (b, d_in), x.dtype, dev)
+    if b == 0 or d_in == 0:
+        return y
+    with torch.cuda.device(dev):
+        rc = lib.ss_conv_update(_ptr(conv_state), _ptr(x), _ptr(weight), _ptr(bias), int(bool(silu)), _ptr(y),
+                                b, d_in, W, code, _stream(dev))
+    if rc != 0:
+        raise SSError(rc, "ss_conv_update")
     return y

@@ -14,6 +14,7 @@
 #include <utility>
 
 #include "ss_scan.h"
+#include "conv_kernels.h"
 #include "scan_kernels.h"
 #include "state_update_kernels.h"
 
@@ -21,6 +22,7 @@
 
 namespace {
 
+using ss::ConvParams;
 using ss::ScanParams;
 using ss::StepParams;
 
@@ -243,6 +245,34 @@ int dispatch_tpar(const ScanParams& p, hipStream_t st) {
     return hipGetLastError() == hipSuccess ? SS_OK : SS_ERR_HIP;
 }
 
+template <typename TIn, int W>
+void launch_conv(const ConvParams& p, bool vec, hipStream_t st) {
+    const dim3 grid(unsigned((p.b * p.d_in + 255) / 256));
+    constexpr int NW = sizeof(TIn) == 2 ? (W + 1) / 2 : W;
+    constexpr bool can_vec = (NW == 2 || NW == 4) && W * int(sizeof(TIn)) == 4 * NW;
+    if constexpr (can_vec) {
+        if (vec) {
+            hipLaunchKernelGGL((ss::conv_update<TIn, W, true>), grid, dim3(256), 0, st, p);
+            return;
+        }
+    }
+    hipLaunchKernelGGL((ss::conv_update<TIn, W, false>), grid, dim3(256), 0, st, p);
+}
+
+template <typename TIn>
+void dispatch_conv(const ConvParams& p, int W, bool vec, hipStream_t st) {
+    switch (W) {
+        case 1: launch_conv<TIn, 1>(p, vec, st); break;
+        case 2: launch_conv<TIn, 2>(p, vec, st); break;
+        case 3: launch_conv<TIn, 3>(p, vec, st); break;
+        case 4: launch_conv<TIn, 4>(p, vec, st); break;
+        case 5: launch_conv<TIn, 5>(p, vec, st); break;
+        case 6: launch_conv<TIn, 6>(p, vec, st); break;
+        case 7: launch_conv<TIn, 7>(p, vec, st); break;
+        default: launch_conv<TIn, 8>(p, vec, st); break;
+    }
+}
+
 }  // namespace
 
 // ============================================================================= C ABI
@@ -433,4 +463,42 @@ SS_EXPORT int ss_state_update(float* state, const void* x, const void* dt, const
                               void* y, int64_t b, int64_t d_in, int64_t n, int dtype, void* stream) {
     return ss_state_update_ex(state, x, dt, A_log, B, C, D, z, dt_bias, dt_softplus, SS_DISC_EULER, y, b, d_in, n,
                               dtype, stream);
+}
+
+SS_EXPORT int ss_conv_update(void* conv_state, const void* x, const float* weight, const float* bias, int silu,
+                             void* out, int64_t b, int64_t d_in, int64_t W, int dtype, void* stream) {
+    if (!conv_state || !x || !weight || !out) return SS_ERR_NULL;
+    if (!sizes_ok(b, d_in, 1) || W <= 0 || b * d_in > kMaxStepChannels) return SS_ERR_SHAPE;
+    if (dtype != SS_F32 && dtype != SS_BF16) return SS_ERR_DTYPE;
+    if (W > SS_MAX_CONV_WIDTH) return SS_ERR_UNSUPPORTED;
+    const size_t es = elem_size(dtype);
+    for (const void* p : {static_cast<const void*>(conv_state), x, static_cast<const void*>(out)})
+        if (!aligned(p, es)) return SS_ERR_ALIGN;
+    for (const void* p : {static_cast<const void*>(weight), static_cast<const void*>(bias)})
+        if (p && !aligned(p, 4)) return SS_ERR_ALIGN;
+    const int64_t nch = b * d_in;
+    const Range rs = range_of(conv_state, nch * W, es);
+    const Range ro = range_of(out, nch, es);
+    const Range ins[] = {range_of(x, nch, es), range_of(weight, d_in * W, 4), range_of(bias, bias ? d_in : 0, 4)};
+    for (const Range& r : ins)
+        if (overlaps(r, rs) || overlaps(r, ro)) return SS_ERR_ALIAS;
+    if (overlaps(rs, ro)) return SS_ERR_ALIAS;
+
+    ConvParams p{};
+    p.state = conv_state;
+    p.x = x;
+    p.weight = weight;
+    p.bias = bias;
+    p.out = out;
+    p.b = b;
+    p.d_in = d_in;
+    p.silu = silu ? 1 : 0;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    // A channel's window is one 8- or 16-byte access when it is that long and so aligned.
+    const bool vec = aligned(conv_state, size_t(W) * es);
+    if (dtype == SS_BF16)
+        dispatch_conv<uint16_t>(p, int(W), vec, st);
+    else
+        dispatch_conv<float>(p, int(W), vec, st);
+    return hipGetLastError() == hipSuccess ? SS_OK : SS_ERR_HIP;
 }

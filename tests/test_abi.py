@@ -28,8 +28,9 @@ def declared_functions():
 
 
 def test_header_declares_the_entry_points():
-    assert declared_functions() == sorted(["ss_scan_fwd", "ss_scan_fwd_ex", "ss_scan_fwd_workspace_bytes",
-                                           "ss_state_update", "ss_state_update_ex", "ss_status_string"])
+    assert declared_functions() == sorted(["ss_conv_update", "ss_scan_fwd", "ss_scan_fwd_ex",
+                                           "ss_scan_fwd_workspace_bytes", "ss_state_update", "ss_state_update_ex",
+                                           "ss_status_string"])
 
 
 def test_library_exports_every_declared_symbol(ss):
@@ -192,3 +193,31 @@ def test_python_binding_checks_initial_state(ss):
     with pytest.raises((TypeError, ValueError)):
         ss.scan_fwd(u, u, torch.zeros(4, 16), torch.zeros(2, 8, 16), torch.zeros(2, 8, 16), torch.zeros(4),
                     initial_state=torch.zeros(2, 4, 15))
+
+
+def conv_args(**over):
+    a = dict(state=addr(1), x=addr(2), weight=addr(3), bias=addr(4), silu=1, out=addr(5), b=256, d_in=5120, W=4,
+             dtype=1, stream=None)
+    a.update(over)
+    return a
+
+
+def call_conv(ss, a):
+    return ss.lib.ss_conv_update(a["state"], a["x"], a["weight"], a["bias"], a["silu"], a["out"], a["b"], a["d_in"],
+                                 a["W"], a["dtype"], a["stream"])
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(state=None), NULL), (dict(x=None), NULL), (dict(weight=None), NULL), (dict(out=None), NULL),
+    (dict(b=0), SHAPE), (dict(d_in=-1), SHAPE), (dict(W=0), SHAPE), (dict(b=1 << 20, d_in=1 << 10), SHAPE),
+    (dict(dtype=2), DTYPE), (dict(W=9), UNSUP),
+    (dict(state=addr(1) + 1), ALIGN), (dict(dtype=0, x=addr(2) + 2), ALIGN), (dict(weight=addr(3) + 2), ALIGN),
+    (dict(out=addr(1) + 8), ALIAS), (dict(out=addr(2)), ALIAS), (dict(state=addr(3)), ALIAS),
+    (dict(state=addr(4) - 8), ALIAS), (dict(out=addr(4)), ALIAS),
+])
+def test_conv_rejects(ss, over, code):
+    assert call_conv(ss, conv_args(**over)) == code
+
+
+def test_conv_bias_is_optional(ss):
+    assert call_conv(ss, conv_args(bias=None, dtype=7)) == DTYPE
