@@ -60,6 +60,8 @@ def _bind(lib: ctypes.CDLL) -> ctypes.CDLL:
     lib.ss_oracle_scan_ex.argtypes = [P] * 8 + [ctypes.c_int, P, ctypes.c_int, P, P, I64, I64, I64, I64]
     lib.ss_oracle_state_update_ex.restype = ctypes.c_int
     lib.ss_oracle_state_update_ex.argtypes = [P] * 9 + [ctypes.c_int, ctypes.c_int, P, I64, I64, I64]
+    lib.ss_oracle_cross_scan.restype = ctypes.c_int
+    lib.ss_oracle_cross_scan.argtypes = [P] * 7 + [ctypes.c_int, P, P, I64, I64, I64, I64, I64]
     lib.ss_oracle_conv_update.restype = ctypes.c_int
     lib.ss_oracle_conv_update.argtypes = [P] * 4 + [ctypes.c_int, P, I64, I64, I64]
     return lib
@@ -168,3 +170,28 @@ def conv_update(conv_state, x, weight, bias=None, act=True, lib=None):
     if rc != 0:
         raise ValueError(f"ss_oracle_conv_update returned {rc}")
     return st, out
+
+
+def cross_scan(x, delta, A_log, B, C, D, delta_bias=None, delta_softplus=True, lib=None):
+    """VMamba cross scan + merge: returns (y (maps, H, W, d_in), last_state (maps, 4, d_in, n)), float64.
+
+    x: (maps, H, W, d_in); delta: (maps, 4, H*W, d_in); B, C: (maps, 4, H*W, n);
+    A_log: (4, d_in, n); D, delta_bias: (4, d_in).  Directions: 0 row-major,
+    1 column-major, 2 and 3 those two backwards.
+    """
+    lib = lib or load()
+    x, delta, A_log, B, C, D = map(_f64, (x, delta, A_log, B, C, D))
+    delta_bias = _f64(delta_bias)
+    maps, H, W, d_in = x.shape
+    n = A_log.shape[2]
+    L = H * W
+    assert delta.shape == (maps, 4, L, d_in) and A_log.shape == (4, d_in, n)
+    assert B.shape == (maps, 4, L, n) and C.shape == (maps, 4, L, n) and D.shape == (4, d_in)
+    assert delta_bias is None or delta_bias.shape == (4, d_in)
+    y = np.empty((maps, H, W, d_in), np.float64)
+    last = np.empty((maps, 4, d_in, n), np.float64)
+    rc = lib.ss_oracle_cross_scan(_ptr(x), _ptr(delta), _ptr(A_log), _ptr(B), _ptr(C), _ptr(D), _ptr(delta_bias),
+                                  int(bool(delta_softplus)), _ptr(y), _ptr(last), maps, H, W, d_in, n)
+    if rc != 0:
+        raise ValueError(f"ss_oracle_cross_scan returned {rc}")
+    return y, last

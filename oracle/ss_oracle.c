@@ -31,6 +31,13 @@
  * torch): a rolling window of the last W inputs per channel, a depthwise dot
  * product with the channel's W weights, the bias, then silu.
  *
+ * ss_oracle_cross_scan is VMamba's CrossScan / scan / CrossMerge
+ * (githubissues.com VMamba issue 206: the cross operations only arrange the
+ * sequence): each feature map is read as four sequences -- row-major,
+ * column-major, and both of those backwards -- each scanned as its own
+ * sequence, and the four outputs are added back at the positions they came
+ * from.
+ *
  * Layouts (row-major, last index fastest):
  *   u, delta, z, y : (b, L, d_in)      B, C : (b, L, n)
  *   A_log          : (d_in, n)         D, delta_bias : (d_in)
@@ -43,6 +50,7 @@
 #include <math.h>
 #include <stddef.h>
 #include <stdint.h>
+#include <stdlib.h>
 
 /* softplus(x) = log(1 + e^x), evaluated without overflow or cancellation:
  * for x > 0 it is x + log(1 + e^-x).  (mhpn.cn page, section 7: softplus
@@ -219,4 +227,69 @@ int ss_oracle_conv_update(double *conv_state, const double *x, const double *wei
         }
     }
     return 0;
+}
+
+/* Map position (row-major index h*W + w of an H x W map) of step t of
+ * traversal direction k: 0 row-major, 1 column-major (step t = w*H + h),
+ * 2 and 3 the same two orders run backwards. */
+static int64_t cross_position(int k, int64_t t, int64_t H, int64_t W)
+{
+    int64_t s = (k >= 2) ? H * W - 1 - t : t;
+    if (k % 2 == 0)
+        return s;
+    int64_t w = s / H, h = s % H;
+    return h * W + w;
+}
+
+/* CrossScan, the selective scan of each direction, CrossMerge.
+ *   x           : (maps, H, W, d_in)   the feature map, channels last
+ *   delta, B, C : (maps, 4, H*W, d_in) and (maps, 4, H*W, n): direction k's
+ *                 values in its own step order
+ *   A_log       : (4, d_in, n)   D, delta_bias : (4, d_in)   per direction
+ *   y           : (maps, H, W, d_in)   sum over the four directions
+ *   last_state  : (maps, 4, d_in, n) or NULL
+ * Direction k of map m is the scan (ss_oracle_scan_ex, b = 1, zero initial
+ * state, Euler input term) of u_k[t] = x[m, position_k(t)]. */
+int ss_oracle_cross_scan(const double *x, const double *delta, const double *A_log,
+                         const double *B, const double *C, const double *D,
+                         const double *delta_bias, int delta_softplus,
+                         double *y, double *last_state,
+                         int64_t maps, int64_t H, int64_t W, int64_t d_in, int64_t n)
+{
+    if (!x || !delta || !A_log || !B || !C || !D || !y)
+        return -1;
+    if (maps <= 0 || H <= 0 || W <= 0 || d_in <= 0 || n <= 0)
+        return -2;
+    const int64_t L = H * W;
+    double *uk = malloc(sizeof(double) * (size_t)(L * d_in));
+    double *yk = malloc(sizeof(double) * (size_t)(L * d_in));
+    if (!uk || !yk) {
+        free(uk);
+        free(yk);
+        return -3;
+    }
+    for (int64_t i = 0; i < maps * L * d_in; i++)
+        y[i] = 0.0;
+    int rc = 0;
+    for (int64_t m = 0; m < maps && rc == 0; m++) {
+        for (int k = 0; k < 4 && rc == 0; k++) {
+            /* CrossScan: direction k's sequence of map positions */
+            for (int64_t t = 0; t < L; t++)
+                for (int64_t d = 0; d < d_in; d++)
+                    uk[t * d_in + d] = x[(m * L + cross_position(k, t, H, W)) * d_in + d];
+            int64_t seq = m * 4 + k;
+            rc = ss_oracle_scan_ex(uk, delta + seq * L * d_in, A_log + k * d_in * n,
+                                   B + seq * L * n, C + seq * L * n, D + k * d_in, NULL,
+                                   delta_bias ? delta_bias + k * d_in : NULL, delta_softplus,
+                                   NULL, 0, yk, last_state ? last_state + seq * d_in * n : NULL,
+                                   1, L, d_in, n);
+            /* CrossMerge: add the outputs back where their inputs came from */
+            for (int64_t t = 0; t < L; t++)
+                for (int64_t d = 0; d < d_in; d++)
+                    y[(m * L + cross_position(k, t, H, W)) * d_in + d] += yk[t * d_in + d];
+        }
+    }
+    free(uk);
+    free(yk);
+    return rc;
 }

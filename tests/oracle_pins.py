@@ -382,6 +382,55 @@ def pin_conv_update(lib):
     _close(o, [[8.5 / (1.0 + math.exp(-8.5))]], what="hand-worked output")
 
 
+def _cross_case(seed, maps=2, H=3, W=5, d_in=3, n=2):
+    r = _rng(seed)
+    L = H * W
+    return dict(x=r.standard_normal((maps, H, W, d_in)), delta=r.standard_normal((maps, 4, L, d_in)) - 1.0,
+                A_log=r.uniform(-1.5, 1.5, (4, d_in, n)), B=r.standard_normal((maps, 4, L, n)),
+                C=r.standard_normal((maps, 4, L, n)), D=r.standard_normal((4, d_in)),
+                delta_bias=r.uniform(-1.0, 0.5, (4, d_in)))
+
+
+def pin_cross_scan(lib):
+    """VMamba's cross scan and merge (githubissues.com VMamba issue 206: they only arrange the sequence).
+
+    - The four sequences arranged with torch (reshape, transpose, flip) rather than
+      index arithmetic, each scanned with the plain scan, and merged back through the
+      inverse arrangement, give the same y and last states;
+    - B = 0: every direction returns D_k u, so y = (sum_k D_k) x everywhere;
+    - transposing the map swaps the row- and column-major directions: the cross
+      scan of x^T with directions (1, 0, 3, 2) is the transposed cross scan of x.
+    """
+    import torch
+
+    for (H, W, n) in ((3, 5, 2), (4, 1, 1), (1, 6, 3), (5, 5, 1)):
+        c = _cross_case(31 + H * W, H=H, W=W, n=n)
+        y, last = oracle.cross_scan(c["x"], c["delta"], c["A_log"], c["B"], c["C"], c["D"], c["delta_bias"], True, lib=lib)
+        x = torch.from_numpy(c["x"])
+        maps, d_in, L = x.shape[0], x.shape[3], H * W
+        row = x.reshape(maps, L, d_in)
+        col = x.transpose(1, 2).reshape(maps, L, d_in)
+        seqs = [row, col, row.flip(1), col.flip(1)]
+        ys = []
+        for k in range(4):
+            yk, lk = oracle.scan(seqs[k].numpy(), c["delta"][:, k], c["A_log"][k], c["B"][:, k], c["C"][:, k], c["D"][k],
+                                 None, c["delta_bias"][k], True, lib=lib)
+            _close(last[:, k], lk, rtol=1e-13, atol=1e-14, what=f"cross last state k={k} {H}x{W}")
+            ys.append(torch.from_numpy(yk))
+        want = (ys[0].reshape(maps, H, W, d_in) + ys[1].reshape(maps, W, H, d_in).transpose(1, 2)
+                + ys[2].flip(1).reshape(maps, H, W, d_in) + ys[3].flip(1).reshape(maps, W, H, d_in).transpose(1, 2))
+        _close(y, want.numpy(), rtol=1e-12, atol=1e-13, what=f"cross scan vs torch arrangement {H}x{W}")
+        sw = [1, 0, 3, 2]
+        yT, lT = oracle.cross_scan(np.ascontiguousarray(c["x"].transpose(0, 2, 1, 3)), c["delta"][:, sw], c["A_log"][sw],
+                                   c["B"][:, sw], c["C"][:, sw], c["D"][sw], c["delta_bias"][sw], True, lib=lib)
+        _close(yT, y.transpose(0, 2, 1, 3), rtol=1e-12, atol=1e-13, what=f"cross scan transposed {H}x{W}")
+        _close(lT, last[:, sw], rtol=1e-13, atol=1e-14, what=f"cross last transposed {H}x{W}")
+    c = _cross_case(41)
+    y, _ = oracle.cross_scan(c["x"], c["delta"], c["A_log"], np.zeros_like(c["B"]), c["C"], c["D"], c["delta_bias"], True,
+                             lib=lib)
+    _close(y, c["x"] * c["D"].sum(0), rtol=1e-13, atol=1e-14, what="cross scan with B = 0")
+
+
 ALL_PINS = [pin_softplus_silu, pin_hand_worked, pin_brute_force, pin_geometric_closed_form, pin_limits,
             pin_skip_and_gate, pin_linearity_causality, pin_step_matches_scan, pin_bias_placement,
-            pin_initial_state, pin_zoh, pin_conv_update]
+            pin_initial_state, pin_zoh, pin_conv_update, pin_cross_scan]

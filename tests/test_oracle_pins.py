@@ -9,6 +9,7 @@ of error in the real oracle.
 import os
 import shutil
 import subprocess
+import sys
 
 import pytest
 
@@ -23,7 +24,11 @@ def test_oracle_pin(pin, oracle_lib):
     pin(oracle_lib)
 
 
-# (description, text in ss_oracle.c, replacement)
+# A mutant whose wrong index can write outside its buffers runs its pins in a
+# child process: a crash there counts as caught.
+ISOLATE = "isolate"
+
+# (description, text in ss_oracle.c, replacement[, ISOLATE])
 MUTANTS = [
     ("A sign", "A[k] = -exp(A_log[d * n + k]);", "A[k] = exp(A_log[d * n + k]);"),
     ("A without exp", "A[k] = -exp(A_log[d * n + k]);", "A[k] = -A_log[d * n + k];"),
@@ -79,24 +84,56 @@ MUTANTS = [
     ("conv weight of channel 0", "acc += win[w] * weight[d * W + w];", "acc += win[w] * weight[w];"),
     ("conv bias after silu", "if (bias)\n                acc += bias[d];\n            out[bi * d_in + d] = act ? ss_oracle_silu(acc) : acc;",
      "out[bi * d_in + d] = (act ? ss_oracle_silu(acc) : acc) + (bias ? bias[d] : 0.0);"),
+    ("cross column-major by W", "int64_t w = s / H, h = s % H;", "int64_t w = s / W, h = s % W;", ISOLATE),
+    ("cross reversed directions run forwards", "int64_t s = (k >= 2) ? H * W - 1 - t : t;", "int64_t s = t;"),
+    ("cross column-major reversed only", "int64_t s = (k >= 2) ? H * W - 1 - t : t;", "int64_t s = (k == 3) ? H * W - 1 - t : t;"),
+    ("cross merge overwrites", "y[(m * L + cross_position(k, t, H, W)) * d_in + d] += yk[t * d_in + d];",
+     "y[(m * L + cross_position(k, t, H, W)) * d_in + d] = yk[t * d_in + d];"),
+    ("cross merge at the step index", "y[(m * L + cross_position(k, t, H, W)) * d_in + d] += yk[t * d_in + d];",
+     "y[(m * L + t) * d_in + d] += yk[t * d_in + d];"),
+    ("cross parameters of direction 0", "rc = ss_oracle_scan_ex(uk, delta + seq * L * d_in, A_log + k * d_in * n,",
+     "rc = ss_oracle_scan_ex(uk, delta + seq * L * d_in, A_log,"),
+    ("cross D of direction 0", "B + seq * L * n, C + seq * L * n, D + k * d_in, NULL,", "B + seq * L * n, C + seq * L * n, D, NULL,"),
+    ("cross inputs of direction 0", "rc = ss_oracle_scan_ex(uk, delta + seq * L * d_in,", "rc = ss_oracle_scan_ex(uk, delta + m * 4 * L * d_in,"),
     ("conv silu ignored", "out[bi * d_in + d] = act ? ss_oracle_silu(acc) : acc;", "out[bi * d_in + d] = acc;"),
 ]
 
 
-@pytest.mark.skipif(shutil.which("gcc") is None, reason="gcc not available")
-@pytest.mark.parametrize("desc,old,new", MUTANTS, ids=[m[0] for m in MUTANTS])
-def test_planted_mistake_is_caught(desc, old, new, tmp_path):
-    src = open(oracle.SOURCE).read()
-    assert src.count(old) == 1, f"mutation anchor not found exactly once: {old!r}"
-    mutated = tmp_path / "mutant.c"
-    mutated.write_text(src.replace(old, new))
-    so = str(tmp_path / "libmutant.so")
-    subprocess.run(["gcc", *oracle.CFLAGS, "-o", so, str(mutated), "-lm"], check=True)
-    lib = oracle.load(so)
+def failing_pins(lib):
     failed = []
     for pin in oracle_pins.ALL_PINS:
         try:
             pin(lib)
         except (AssertionError, ValueError, FloatingPointError, OverflowError):
             failed.append(pin.__name__)
+    return failed
+
+
+CHILD = (
+    "import sys, warnings\n"
+    "warnings.simplefilter('ignore')\n"
+    "sys.path.insert(0, sys.argv[2])\n"
+    "import oracle\n"
+    "from tests.test_oracle_pins import failing_pins\n"
+    "print(','.join(failing_pins(oracle.load(sys.argv[1]))))\n"
+)
+
+
+@pytest.mark.skipif(shutil.which("gcc") is None, reason="gcc not available")
+@pytest.mark.parametrize("mutant", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_planted_mistake_is_caught(mutant, tmp_path):
+    desc, old, new = mutant[:3]
+    src = open(oracle.SOURCE).read()
+    assert src.count(old) == 1, f"mutation anchor not found exactly once: {old!r}"
+    mutated = tmp_path / "mutant.c"
+    mutated.write_text(src.replace(old, new))
+    so = str(tmp_path / "libmutant.so")
+    subprocess.run(["gcc", *oracle.CFLAGS, "-o", so, str(mutated), "-lm"], check=True)
+    if ISOLATE in mutant[3:]:
+        root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+        r = subprocess.run([sys.executable, "-c", CHILD, so, root], capture_output=True, text=True, timeout=300)
+        failed = r.stdout.strip().split(",") if r.returncode == 0 else [f"crashed ({r.returncode})"]
+        failed = [f for f in failed if f]
+    else:
+        failed = failing_pins(oracle.load(so))
     assert failed, f"planted mistake '{desc}' passed every pin"
