@@ -64,6 +64,11 @@ def conv_bytes(b, d, W, s, bias=True):
     return s * b * d * (2 * W + 2) + 4 * (d * W + (d if bias else 0))
 
 
+def cross_bytes(maps, L, d, n, s, bias=False):
+    """Fused cross scan: the map once, per-direction delta, B, C, the fp32 output map, parameters."""
+    return s * (maps * L * d + 4 * maps * L * d + 8 * maps * L * n) + 4 * maps * L * d + 4 * (4 * d * n + 4 * d * (2 if bias else 1))
+
+
 def kernel_source_hash() -> str:
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "selective_state_space_softplus_amd", "csrc")
@@ -143,6 +148,7 @@ def main(argv=None):
     ap.add_argument("--prewarm", type=float, default=0.3, help="seconds of untimed scans before the warm-up steps")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-decode", action="store_true", help="skip the decode-step measurement")
+    ap.add_argument("--no-cross", action="store_true", help="skip the VMamba cross-scan measurement")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target duration of the CPU baseline sample")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy (calibrates the HBM byte counters)")
@@ -298,6 +304,56 @@ def main(argv=None):
             "us_per_step_graph": round(cms_g * 1e3, 2),
             "GBps_graph": round(cbytes / (cms_g * 1e-3) / 1e9, 1),
             "algorithmic_bytes_per_step": cbytes,
+        }
+
+    if not args.no_cross:
+        # VMamba's cross scan on the scan-vmamba maps: the fused kernel against
+        # the same work done the unfused way (the four traversal copies made
+        # with torch, the plain scan, the merge with torch).
+        vcfg = workloads.CONFIGS[3]
+        ci = {k: (v.to(dev) if isinstance(v, torch.Tensor) else v) for k, v in workloads.cross_scan_inputs(3).items()}
+        maps, H, L, d, n = vcfg.maps, vcfg.side, vcfg.L, vcfg.d_in, vcfg.n
+        yout = torch.empty(maps, H, H, d, device=dev)
+
+        def fused():
+            ss.cross_scan_fwd(ci["x"], ci["delta"], ci["A_log"], ci["B"], ci["C"], ci["D"], None, True, out=yout)
+
+        dl2, B2, C2 = ci["delta"].reshape(maps * 4, L, d), ci["B"].reshape(maps * 4, L, n), ci["C"].reshape(maps * 4, L, n)
+
+        def unfused():
+            u = workloads.vmamba_unroll(ci["x"])
+            yd = ss.scan_fwd(u, dl2, ci["A_log"][0], B2, C2, ci["D"][0], None, None, True).reshape(maps, 4, L, d)
+            return (yd[:, 0].reshape(maps, H, H, d) + yd[:, 1].reshape(maps, H, H, d).transpose(1, 2)
+                    + yd[:, 2].flip(1).reshape(maps, H, H, d) + yd[:, 3].flip(1).reshape(maps, H, H, d).transpose(1, 2))
+
+        u_pre = workloads.vmamba_unroll(ci["x"])
+
+        def scan_only():
+            ss.scan_fwd(u_pre, dl2, ci["A_log"][0], B2, C2, ci["D"][0], None, None, True)
+
+        def timed(fn, reps=10):
+            for _ in range(3):
+                fn()
+            torch.cuda.synchronize()
+            a0, a1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a0.record()
+            for _ in range(reps):
+                fn()
+            a1.record()
+            torch.cuda.synchronize()
+            return a0.elapsed_time(a1) / reps
+
+        ms_f, ms_u, ms_s = timed(fused), timed(unfused), timed(scan_only)
+        xb = cross_bytes(maps, L, d, n, 4)
+        result["vmamba_cross"] = {
+            "workload": f"{vcfg.name}: {maps} maps of {H}x{H}x{d}, 4 traversal orders, n={n}, fp32, softplus, no gate",
+            "fused_ms": round(ms_f, 4),
+            "fused_GBps": round(xb / (ms_f * 1e-3) / 1e9, 1),
+            "algorithmic_bytes": xb,
+            "unfused_ms": round(ms_u, 4),
+            "unfused_scan_only_ms": round(ms_s, 4),
+            "note": "unfused = four traversal copies made with torch + ss_scan_fwd + torch merge; "
+                    "scan_only = ss_scan_fwd on copies made beforehand",
         }
 
     if not args.no_cpu:

@@ -184,6 +184,45 @@ int ss_state_update_ex(float *state, const void *x, const void *dt,
                        int dt_softplus, int discretization, void *y,
                        int64_t b, int64_t d_in, int64_t n, int dtype, void *stream);
 
+/*
+ * VMamba's cross scan, fused (githubissues.com VMamba issue 206: CrossScan and
+ * CrossMerge only arrange the sequence around the selective scan).  Each
+ * H x W feature map is read as four sequences of L = H * W steps --
+ * direction 0 row-major (step t = h*W + w), 1 column-major (t = w*H + h),
+ * 2 and 3 the same two orders backwards -- each scanned as ss_scan_fwd scans
+ * one batch row (zero initial state, delta' B u input term, no gate), and the
+ * four outputs are added back at the positions they came from:
+ *     y[m, p, d] = sum_k y_k[m, t_k(p), d]
+ * The map is read in place by every direction (no unrolled copies); the
+ * four outputs go to workspace and a second kernel adds them back, in the
+ * order k = 0, 1, 2, 3, so y is the same bit for bit on every run.
+ *
+ *   x          : (maps, H, W, d_in)    dtype; u of all four directions
+ *   delta      : (maps, 4, L, d_in)    dtype; direction k's values in its own step order
+ *   A_log      : (4, d_in, n)          fp32, one set per direction
+ *   B, C       : (maps, 4, L, n)       dtype
+ *   D          : (4, d_in)             fp32
+ *   delta_bias : (4, d_in)             fp32, or NULL
+ *   delta_softplus : as for ss_scan_fwd
+ *   y          : (maps, H, W, d_in)    fp32 output (whatever dtype the inputs have)
+ *   last_state : (maps, 4, d_in, n)    fp32 output, or NULL
+ *   workspace  : device memory of ss_cross_scan_fwd_workspace_bytes() bytes,
+ *                256-byte aligned (SS_ERR_ALIGN otherwise); it holds the four
+ *                directions' outputs, 16 * maps * L * d_in bytes, and the
+ *                scan's own workspace.
+ * Sizes: those of ss_scan_fwd with b = 4 * maps and L = H * W.  Errors as
+ * for ss_scan_fwd.
+ */
+size_t ss_cross_scan_fwd_workspace_bytes(int64_t maps, int64_t H, int64_t W,
+                                         int64_t d_in, int64_t n, int dtype);
+
+int ss_cross_scan_fwd(const void *x, const void *delta, const float *A_log,
+                      const void *B, const void *C, const float *D,
+                      const float *delta_bias, int delta_softplus,
+                      float *y, float *last_state,
+                      int64_t maps, int64_t H, int64_t W, int64_t d_in, int64_t n,
+                      int dtype, void *workspace, size_t workspace_bytes, void *stream);
+
 /* Largest convolution width W of ss_conv_update. */
 #define SS_MAX_CONV_WIDTH 8
 

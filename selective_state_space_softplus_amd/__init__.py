@@ -13,6 +13,8 @@ Entry points mirror the C ABI (``include/ss_scan.h``):
                                              -> y  or  (y, last_state)
   state_update(state, x, dt, A_log, B, C, D, z=None, dt_bias=None, dt_softplus=True,
                zoh=False)                    -> y  (state is updated in place)
+  cross_scan_fwd(x, delta, A_log, B, C, D, delta_bias=None, delta_softplus=True,
+                 return_last_state=False)    -> y (maps, H, W, d_in) fp32  or  (y, last_state)
   conv_update(conv_state, x, weight, bias=None, silu=True)
                                              -> out (b, d_in)  (conv_state is updated in place)
   scan_fwd_workspace_bytes(b, L, d_in, n, dtype) -> int
@@ -25,6 +27,10 @@ state (b, d_in, n) fp32 updated in place; x, dt, z (b, d_in); B, C (b, n).
 ``initial_state`` (b, d_in, n) fp32 starts the scan from a given state and
 ``zoh=True`` selects the zero-order-hold input term (mhpn.cn, section 6); calls
 that use either go through ``ss_scan_fwd_ex`` / ``ss_state_update_ex``.
+``cross_scan_fwd`` is VMamba's CrossScan + scan + CrossMerge in one pass (githubissues.com
+VMamba #206): x (maps, H, W, d_in); delta (maps, 4, H*W, d_in); B, C (maps, 4, H*W, n);
+A_log (4, d_in, n); D, delta_bias (4, d_in); directions 0 row-major, 1 column-major,
+2 and 3 those reversed; y is the fp32 sum of the four directions at each position.
 ``conv_update`` is the convolution step of Mamba.step (jiafeimiao.top): conv_state
 (b, d_in, W) in the dtype of x, weight (d_in, W) and bias (d_in) fp32.
 """
@@ -47,7 +53,7 @@ SS_DISC_ZOH = 1
 STATUS = {0: "SS_OK", -1: "SS_ERR_NULL", -2: "SS_ERR_SHAPE", -3: "SS_ERR_DTYPE", -4: "SS_ERR_UNSUPPORTED",
           -5: "SS_ERR_WORKSPACE", -6: "SS_ERR_HIP", -7: "SS_ERR_ALIAS", -8: "SS_ERR_ALIGN", -9: "SS_ERR_MODE"}
 EXPORTS = ("ss_scan_fwd_workspace_bytes", "ss_scan_fwd", "ss_scan_fwd_ex", "ss_state_update", "ss_state_update_ex",
-           "ss_conv_update", "ss_status_string")
+           "ss_cross_scan_fwd", "ss_cross_scan_fwd_workspace_bytes", "ss_conv_update", "ss_status_string")
 
 
 class SSError(RuntimeError):
@@ -72,6 +78,10 @@ def _load() -> ctypes.CDLL:
     lib.ss_state_update.argtypes = [P, P, P, P, P, P, P, P, P, I, P, I64, I64, I64, I, P]
     lib.ss_state_update_ex.restype = I
     lib.ss_state_update_ex.argtypes = [P, P, P, P, P, P, P, P, P, I, I, P, I64, I64, I64, I, P]
+    lib.ss_cross_scan_fwd_workspace_bytes.restype = ctypes.c_size_t
+    lib.ss_cross_scan_fwd_workspace_bytes.argtypes = [I64, I64, I64, I64, I64, I]
+    lib.ss_cross_scan_fwd.restype = I
+    lib.ss_cross_scan_fwd.argtypes = [P, P, P, P, P, P, P, I, P, P, I64, I64, I64, I64, I64, I, P, ctypes.c_size_t, P]
     lib.ss_conv_update.restype = I
     lib.ss_conv_update.argtypes = [P, P, P, P, I, P, I64, I64, I64, I, P]
     lib.ss_status_string.restype = ctypes.c_char_p
@@ -249,3 +259,43 @@ def conv_update(conv_state, x, weight, bias=None, silu=True, out=None):
     if rc != 0:
         raise SSError(rc, "ss_conv_update")
     return y
+
+
+def cross_scan_fwd(x, delta, A_log, B, C, D, delta_bias=None, delta_softplus=True, return_last_state=False,
+                   out=None, last_state=None, workspace=None):
+    """VMamba cross scan + merge on the GPU; returns y (maps, H, W, d_in) fp32 (and last_state (maps, 4, d_in, n))."""
+    if x.dim() != 4 or A_log.dim() != 3:
+        raise ValueError("x must be (maps, H, W, d_in) and A_log (4, d_in, n)")
+    maps, H, W, d_in = x.shape
+    n = A_log.shape[2]
+    L = H * W
+    dev = x.device
+    code = _dtype_code(x.dtype)
+    _check(x, "x", (maps, H, W, d_in), x.dtype, dev)
+    _check(delta, "delta", (maps, 4, L, d_in), x.dtype, dev)
+    _check(A_log, "A_log", (4, d_in, n), torch.float32, dev)
+    _check(B, "B", (maps, 4, L, n), x.dtype, dev)
+    _check(C, "C", (maps, 4, L, n), x.dtype, dev)
+    _check(D, "D", (4, d_in), torch.float32, dev)
+    _check(delta_bias, "delta_bias", (4, d_in), torch.float32, dev)
+    y = torch.empty((maps, H, W, d_in), dtype=torch.float32, device=dev) if out is None else out
+    _check(y, "out", (maps, H, W, d_in), torch.float32, dev)
+    if return_last_state and last_state is None:
+        last_state = torch.empty((maps, 4, d_in, n), dtype=torch.float32, device=dev)
+    _check(last_state, "last_state", (maps, 4, d_in, n), torch.float32, dev)
+    if maps == 0 or L == 0 or d_in == 0:
+        y.zero_()
+        if last_state is not None:
+            last_state.zero_()
+        return (y, last_state) if return_last_state else y
+    need = int(lib.ss_cross_scan_fwd_workspace_bytes(maps, H, W, d_in, n, code))
+    if workspace is None:
+        workspace = _workspace(dev, need)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    with torch.cuda.device(dev):
+        rc = lib.ss_cross_scan_fwd(_ptr(x), _ptr(delta), _ptr(A_log), _ptr(B), _ptr(C), _ptr(D), _ptr(delta_bias),
+                                   int(bool(delta_softplus)), _ptr(y), _ptr(last_state), maps, H, W, d_in, n, code,
+                                   _ptr(workspace), ws_bytes, _stream(dev))
+    if rc != 0:
+        raise SSError(rc, "ss_cross_scan_fwd")
+    return (y, last_state) if return_last_state else y

@@ -8,7 +8,10 @@
 //     y      = sum_k C[b,t,k] h[k] + D[d] u,   then y *= silu(z) if z is given.
 // exp(delta' A) and delta' B u are formed in registers and never stored.
 // scan_seq also takes a given initial state h0 and the zero-order-hold input
-// term (exp(delta' A) - 1) / A B u of the same page's section 6.
+// term (exp(delta' A) - 1) / A B u of the same page's section 6, and runs
+// VMamba's cross scan (githubissues.com VMamba issue 206): batch row 4m + k is
+// traversal direction k of feature map m, whose u rows are read from the map
+// in that direction's order; cross_merge then adds the four outputs back.
 //
 // scan_seq  (state sizes n >= 3).  One lane per channel d, 64 channels per
 //   workgroup; the n states of a channel are split across the S waves of the
@@ -54,6 +57,7 @@ struct ScanParams {
     const float* h0;     // (b, d_in, n) initial state, or null for zero (scan_seq)
     int64_t b, L, d_in, n;
     int softplus;
+    int cross_h, cross_w; // cross scan: map height and width (L = cross_h * cross_w)
     // plan
     int nblk_d;          // ceil(d_in / 64)
     int K;               // segments along L (scan_seq)
@@ -179,7 +183,10 @@ struct RawRow {
 // 16-byte direct-to-LDS loads and y leaves by wide stores.
 // SP: delta' = softplus(delta + bias) (else delta + bias).  GATE: z is given.
 // ZOH: the input term is the zero-order hold's (exp(delta' A) - 1) / A B u
-// (else delta' B u).
+// (else delta' B u).  CROSS: cross scan -- batch row bi is direction bi % 4
+// (0 row-major, 1 column-major, 2 and 3 those backwards) of map bi / 4; u is
+// the (maps, H, W, d_in) map, A_log, D and the bias hold one set per
+// direction, and y is fp32 (b, L, d_in), each direction in its own step order.
 //
 // Waves 0 .. SC-1 ("recurrence waves") each hold NSW states of the 64
 // channels and run nothing but the recurrence.  Waves SC .. SC+3 ("element
@@ -200,10 +207,11 @@ struct RawRow {
 //     tiles (loaded two chunks earlier);
 //   - the loader issues the loads of chunk c+4 (u, delta, B, C) and of chunk
 //     c+1 (z), then waits until those of chunk c+3 and c are complete.
-template <typename TIn, int SC, int NSW, int T, bool WIDE, bool SP, bool GATE, bool ZOH>
+template <typename TIn, int SC, int NSW, int T, bool WIDE, bool SP, bool GATE, bool ZOH, bool CROSS>
 __global__ __launch_bounds__((SC + kSeqElemWaves + 1) * 64) void scan_seq(const ScanParams p) {
     constexpr int P = kSeqElemWaves;
     constexpr int ES = int(sizeof(TIn));
+    using TOut = std::conditional_t<CROSS, float, TIn>;   // element type of y
     constexpr int NE = P * 64;                     // element threads
     constexpr int V = T / P;                       // consecutive channels per element thread
     constexpr int TPR = 64 / V;                    // element threads per step row
@@ -268,6 +276,19 @@ __global__ __launch_bounds__((SC + kSeqElemWaves + 1) * 64) void scan_seq(const 
     const int nchunks = (t_end - t_begin + T - 1) / T;
     const int nch3 = (nchunks + 2) / 3 * 3;       // chunks the loop runs (past the end: empty)
 
+    // Cross scan: direction and map of this batch row, and the map position of
+    // step t of that direction (the host keeps H * W < 2^31).
+    const int dir = CROSS ? bi % 4 : 0;
+    const int64_t mrow = CROSS ? int64_t(bi / 4) * L : 0;
+    auto cross_pos = [&](int t) -> int {
+        const int s = dir >= 2 ? L - 1 - t : t;
+        if (!(dir & 1)) return s;
+        const uint32_t w = uint32_t(s) / uint32_t(p.cross_h);
+        const int h = s - int(w) * p.cross_h;
+        return h * p.cross_w + int(w);
+    };
+    const int64_t prow = int64_t(dir) * d_in;     // this direction's row of A_log, D, bias
+
     // Recurrence waves: lane = channel d, states n0 .. n0+NSW.
     const int d = dbase + lane;
     const bool dv = d < d_in;
@@ -277,7 +298,7 @@ __global__ __launch_bounds__((SC + kSeqElemWaves + 1) * 64) void scan_seq(const 
 #pragma unroll
     for (int q = 0; q < NSW; q++) {
         const bool ok = rec && dv && n0 + q < n;
-        A2[q] = ok ? a2_from_alog(p.A_log[d * n + n0 + q]) : 0.0f;
+        A2[q] = ok ? a2_from_alog(p.A_log[(prow + d) * n + n0 + q]) : 0.0f;
         h[q] = (ok && h0) ? h0[q] : 0.0f;
     }
 
@@ -292,8 +313,8 @@ __global__ __launch_bounds__((SC + kSeqElemWaves + 1) * 64) void scan_seq(const 
     float Dv[V], bias_v[V];
 #pragma unroll
     for (int i = 0; i < V; i++) {
-        Dv[i] = i < evalid ? p.D[ech + i] : 0.0f;
-        bias_v[i] = (i < evalid && p.bias) ? p.bias[ech + i] : 0.0f;
+        Dv[i] = i < evalid ? p.D[prow + ech + i] : 0.0f;
+        bias_v[i] = (i < evalid && p.bias) ? p.bias[prow + ech + i] : 0.0f;
     }
 
     if (seg > 0) {
@@ -337,7 +358,9 @@ __global__ __launch_bounds__((SC + kSeqElemWaves + 1) * 64) void scan_seq(const 
 
     // ---- loader: direct-to-LDS loads of chunk k (rows past the segment's end
     // read its last row, channels past d_in read channel dbase; both are masked).
-    auto dma_x = [&](const TIn* src, char* tile, int k) {
+    // `mapped`: rows of the cross scan's map (u), else rows of this batch row.
+    auto xrow = [&](bool mapped, int t) -> int64_t { return CROSS && mapped ? mrow + cross_pos(t) : brow + t; };
+    auto dma_x = [&](const TIn* src, char* tile, int k, bool mapped) {
         const int t0 = t_begin + k * T;
         if constexpr (WIDE) {
             constexpr int EPL = 16 / ES;           // elements per lane
@@ -348,14 +371,14 @@ __global__ __launch_bounds__((SC + kSeqElemWaves + 1) * 64) void scan_seq(const 
 #pragma unroll
             for (int ii = 0; ii < XI; ii++) {
                 const int t = min(t0 + ii * RPI + lane / LPR, t_end - 1);
-                load_to_lds<16>(src + ((brow + t) * d_in + ch), tile + ii * 1024);
+                load_to_lds<16>(src + (xrow(mapped, t) * d_in + ch), tile + ii * 1024);
             }
         } else {
             const int ch = min(dbase + lane, d_in - 1);
 #pragma unroll 2
             for (int r = 0; r < T; r++) {
                 const int t = min(t0 + r, t_end - 1);
-                load_to_lds<ES>(src + ((brow + t) * d_in + ch), tile + r * 256);
+                load_to_lds<ES>(src + (xrow(mapped, t) * d_in + ch), tile + r * 256);
             }
         }
     };
@@ -370,13 +393,13 @@ __global__ __launch_bounds__((SC + kSeqElemWaves + 1) * 64) void scan_seq(const 
     auto dma_chunk = [&](int k, int slot) {        // u, delta, B, C of chunk k into ring slot `slot`
         char* ru = lds + Lds::off_ru + slot * 2 * Lds::RX;
         char* rbc = lds + Lds::off_rbc + slot * 2 * Lds::RBC;
-        dma_x(static_cast<const TIn*>(p.u), ru, k);
-        dma_x(static_cast<const TIn*>(p.delta), ru + Lds::RX, k);
+        dma_x(static_cast<const TIn*>(p.u), ru, k, true);
+        dma_x(static_cast<const TIn*>(p.delta), ru + Lds::RX, k, false);
         dma_bc(static_cast<const TIn*>(p.B), rbc, k);
         dma_bc(static_cast<const TIn*>(p.C), rbc + Lds::RBC, k);
     };
     auto dma_z = [&](int k, int slot) {
-        if (GATE) dma_x(static_cast<const TIn*>(p.z), lds + Lds::off_rz + slot * Lds::RX, k);
+        if (GATE) dma_x(static_cast<const TIn*>(p.z), lds + Lds::off_rz + slot * Lds::RX, k, false);
     };
 
     // ---- element waves
@@ -441,9 +464,9 @@ __global__ __launch_bounds__((SC + kSeqElemWaves + 1) * 64) void scan_seq(const 
             yv[i] = acc;
         }
         const int valid = ev(k);
-        TIn* yp = static_cast<TIn*>(p.y);
+        TOut* yp = static_cast<TOut*>(p.y);
         if (valid > 0)
-            store_span<TIn, V, WIDE>(yp + (brow + t_begin + int64_t(k) * T) * d_in, off_el, yv, valid);
+            store_span<TOut, V, WIDE>(yp + (brow + t_begin + int64_t(k) * T) * d_in, off_el, yv, valid);
     };
 
     // ---- fill: loads of chunks 0 .. 2 and the gate of chunk 0; phase 1 and
@@ -493,7 +516,7 @@ __global__ __launch_bounds__((SC + kSeqElemWaves + 1) * 64) void scan_seq(const 
     float invA[NSW];
 #pragma unroll
     for (int q = 0; q < NSW; q++)
-        invA[q] = (ZOH && rec && dv && n0 + q < n) ? inv_a_from_alog(p.A_log[d * n + n0 + q]) : 0.0f;
+        invA[q] = (ZOH && rec && dv && n0 + q < n) ? inv_a_from_alog(p.A_log[(prow + d) * n + n0 + q]) : 0.0f;
     auto rec_chunk = [&](auto ph, int c) {
         constexpr int PH = decltype(ph)::value;
         constexpr int K0 = PH, K1 = (PH + 1) % 3;    // ring slots of chunks c, c+1
@@ -623,6 +646,46 @@ __global__ __launch_bounds__((SC + kSeqElemWaves + 1) * 64) void scan_seq(const 
         if (tid == 0)
             __hip_atomic_store(p.ctl + kFlagOffset + seg * G + g, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
+}
+
+// CrossMerge: y[m, p, :] = sum over the four directions k of ys[m, k, t_k(p), :],
+// t_k(p) the step at which direction k visits map position p (the inverse of
+// the cross scan's traversal), added in the order k = 0, 1, 2, 3.  One thread
+// per VEC consecutive channels of a position; every read and the write are
+// whole rows of d_in channels.
+template <int VEC>
+__global__ __launch_bounds__(256) void cross_merge(const float* __restrict__ ys, float* __restrict__ y, int64_t maps,
+                                                   int H, int W, int64_t d_in) {
+    const int64_t L = int64_t(H) * W;
+    const int64_t cpr = d_in / VEC;                           // thread columns per row
+    const int64_t i = blockIdx.x * int64_t(blockDim.x) + threadIdx.x;
+    if (i >= maps * L * cpr) return;
+    const int64_t row = i / cpr;                              // (m, p)
+    const int64_t c = (i - row * cpr) * VEC;
+    const int64_t m = row / L;
+    const int64_t pos = row - m * L;
+    const int64_t h = pos / W, w = pos - h * W;
+    const int64_t tc = w * H + h;                             // step of the column-major direction
+    const int64_t steps[4] = {pos, tc, L - 1 - pos, L - 1 - tc};
+    float acc[VEC];
+#pragma unroll
+    for (int v = 0; v < VEC; v++) acc[v] = 0.0f;
+#pragma unroll
+    for (int k = 0; k < 4; k++) {
+        const float* src = ys + ((m * 4 + k) * L + steps[k]) * d_in + c;
+        if constexpr (VEC == 4) {
+            const float4 q = *reinterpret_cast<const float4*>(src);
+            acc[0] += q.x;
+            acc[1] += q.y;
+            acc[2] += q.z;
+            acc[3] += q.w;
+        } else {
+            acc[0] += src[0];
+        }
+    }
+    float* dst = y + row * d_in + c;
+    if constexpr (VEC == 4) *reinterpret_cast<float4*>(dst) = make_float4(acc[0], acc[1], acc[2], acc[3]);
+    else dst[0] = acc[0];
 }
 
 // Clears the ticket counter, the error word and the segment flags.

@@ -166,8 +166,11 @@ int choose_segments(int64_t G, int64_t L, int T, int64_t slots) {
     return best;
 }
 
+// Which family of scan_seq kernels a call needs.
+enum class SeqMode { Euler, Zoh, Cross };
+
 template <typename TIn, int SC, int NSW>
-int launch_seq(ScanParams p, bool zoh, void* ws, size_t ws_bytes, hipStream_t st) {
+int launch_seq(ScanParams p, SeqMode mode, void* ws, size_t ws_bytes, hipStream_t st) {
     constexpr int TW = ss::seq_chunk<TIn, SC, NSW, true>(), TN = ss::seq_chunk<TIn, SC, NSW, false>();
     constexpr int threads = (SC + ss::kSeqElemWaves + 1) * 64;
     const int64_t G = p.b * p.nblk_d;
@@ -175,28 +178,35 @@ int launch_seq(ScanParams p, bool zoh, void* ws, size_t ws_bytes, hipStream_t st
     if (!ws || ws_bytes < w.total) return SS_ERR_WORKSPACE;
 
     // Wide path: whole 16-byte pieces per row and 16-byte aligned u, delta, z;
-    // y aligned for V-element stores.  The zero-order-hold kernels exist in
-    // the element-load form only: their recurrence costs about three times
-    // the Euler one, which hides the difference in load width.
-    const bool wide = !zoh && (p.d_in * int64_t(sizeof(TIn))) % 16 == 0 && aligned(p.u, 16) &&
+    // y aligned for V-element stores (the cross scan adds to y element by
+    // element).  The zero-order-hold kernels exist in the element-load form
+    // only: their recurrence costs about three times the Euler one, which
+    // hides the difference in load width.  The cross scan has no gate.
+    const bool wide = mode != SeqMode::Zoh && (p.d_in * int64_t(sizeof(TIn))) % 16 == 0 && aligned(p.u, 16) &&
                       aligned(p.delta, 16) && (!p.z || aligned(p.z, 16)) &&
-                      aligned(p.y, (TW / ss::kSeqElemWaves) * sizeof(TIn));
+                      (mode == SeqMode::Cross || aligned(p.y, (TW / ss::kSeqElemWaves) * sizeof(TIn)));
     const int T = wide ? TW : TN;
-    const int variant = (zoh ? 8 : wide ? 4 : 0) | (p.softplus ? 2 : 0) | (p.z ? 1 : 0);
+    const int variant = mode == SeqMode::Cross ? 12 + (wide ? 2 : 0) + (p.softplus ? 1 : 0)
+                                               : ((mode == SeqMode::Zoh ? 8 : wide ? 4 : 0) | (p.softplus ? 2 : 0) |
+                                                  (p.z ? 1 : 0));
     using Kern = void (*)(ScanParams);
-    static constexpr Kern kernels[12] = {
-        ss::scan_seq<TIn, SC, NSW, TN, false, false, false, false>,
-        ss::scan_seq<TIn, SC, NSW, TN, false, false, true, false>,
-        ss::scan_seq<TIn, SC, NSW, TN, false, true, false, false>,
-        ss::scan_seq<TIn, SC, NSW, TN, false, true, true, false>,
-        ss::scan_seq<TIn, SC, NSW, TW, true, false, false, false>,
-        ss::scan_seq<TIn, SC, NSW, TW, true, false, true, false>,
-        ss::scan_seq<TIn, SC, NSW, TW, true, true, false, false>,
-        ss::scan_seq<TIn, SC, NSW, TW, true, true, true, false>,
-        ss::scan_seq<TIn, SC, NSW, TN, false, false, false, true>,
-        ss::scan_seq<TIn, SC, NSW, TN, false, false, true, true>,
-        ss::scan_seq<TIn, SC, NSW, TN, false, true, false, true>,
-        ss::scan_seq<TIn, SC, NSW, TN, false, true, true, true>};
+    static constexpr Kern kernels[16] = {
+        ss::scan_seq<TIn, SC, NSW, TN, false, false, false, false, false>,
+        ss::scan_seq<TIn, SC, NSW, TN, false, false, true, false, false>,
+        ss::scan_seq<TIn, SC, NSW, TN, false, true, false, false, false>,
+        ss::scan_seq<TIn, SC, NSW, TN, false, true, true, false, false>,
+        ss::scan_seq<TIn, SC, NSW, TW, true, false, false, false, false>,
+        ss::scan_seq<TIn, SC, NSW, TW, true, false, true, false, false>,
+        ss::scan_seq<TIn, SC, NSW, TW, true, true, false, false, false>,
+        ss::scan_seq<TIn, SC, NSW, TW, true, true, true, false, false>,
+        ss::scan_seq<TIn, SC, NSW, TN, false, false, false, true, false>,
+        ss::scan_seq<TIn, SC, NSW, TN, false, false, true, true, false>,
+        ss::scan_seq<TIn, SC, NSW, TN, false, true, false, true, false>,
+        ss::scan_seq<TIn, SC, NSW, TN, false, true, true, true, false>,
+        ss::scan_seq<TIn, SC, NSW, TN, false, false, false, false, true>,
+        ss::scan_seq<TIn, SC, NSW, TN, false, true, false, false, true>,
+        ss::scan_seq<TIn, SC, NSW, TW, true, false, false, false, true>,
+        ss::scan_seq<TIn, SC, NSW, TW, true, true, false, false, true>};
     const Kern kern = kernels[variant];
     const size_t lds = wide ? ss::SeqLds<TW, SC, SC * NSW, sizeof(TIn), true>::bytes
                             : ss::SeqLds<TN, SC, SC * NSW, sizeof(TIn), false>::bytes;
@@ -224,15 +234,15 @@ int launch_seq(ScanParams p, bool zoh, void* ws, size_t ws_bytes, hipStream_t st
 }
 
 template <typename TIn>
-int dispatch_seq(const ScanParams& p, bool zoh, void* ws, size_t ws_bytes, hipStream_t st) {
+int dispatch_seq(const ScanParams& p, SeqMode mode, void* ws, size_t ws_bytes, hipStream_t st) {
     const SeqShape sh = seq_shape(p.n);
-    if (sh.SC == 1) return launch_seq<TIn, 1, 2>(p, zoh, ws, ws_bytes, st);
+    if (sh.SC == 1) return launch_seq<TIn, 1, 2>(p, mode, ws, ws_bytes, st);
     if (sh.SC == 4)
-        return sh.NSW == 2 ? launch_seq<TIn, 4, 2>(p, zoh, ws, ws_bytes, st)
-                           : launch_seq<TIn, 4, 4>(p, zoh, ws, ws_bytes, st);
-    if (sh.NSW == 2) return launch_seq<TIn, 8, 2>(p, zoh, ws, ws_bytes, st);
-    if (sh.NSW == 4) return launch_seq<TIn, 8, 4>(p, zoh, ws, ws_bytes, st);
-    return launch_seq<TIn, 8, 8>(p, zoh, ws, ws_bytes, st);
+        return sh.NSW == 2 ? launch_seq<TIn, 4, 2>(p, mode, ws, ws_bytes, st)
+                           : launch_seq<TIn, 4, 4>(p, mode, ws, ws_bytes, st);
+    if (sh.NSW == 2) return launch_seq<TIn, 8, 2>(p, mode, ws, ws_bytes, st);
+    if (sh.NSW == 4) return launch_seq<TIn, 8, 4>(p, mode, ws, ws_bytes, st);
+    return launch_seq<TIn, 8, 8>(p, mode, ws, ws_bytes, st);
 }
 
 template <typename TIn>
@@ -368,8 +378,9 @@ SS_EXPORT int ss_scan_fwd_ex(const void* u, const void* delta, const float* A_lo
     const bool zoh = discretization == SS_DISC_ZOH;
     if (choose_kernel(p, zoh) == ScanKernel::Tpar)
         return dtype == SS_BF16 ? dispatch_tpar<uint16_t>(p, st) : dispatch_tpar<float>(p, st);
-    return dtype == SS_BF16 ? dispatch_seq<uint16_t>(p, zoh, workspace, workspace_bytes, st)
-                            : dispatch_seq<float>(p, zoh, workspace, workspace_bytes, st);
+    const SeqMode mode = zoh ? SeqMode::Zoh : SeqMode::Euler;
+    return dtype == SS_BF16 ? dispatch_seq<uint16_t>(p, mode, workspace, workspace_bytes, st)
+                            : dispatch_seq<float>(p, mode, workspace, workspace_bytes, st);
 }
 
 SS_EXPORT int ss_scan_fwd(const void* u, const void* delta, const float* A_log, const void* B, const void* C,
@@ -500,5 +511,96 @@ SS_EXPORT int ss_conv_update(void* conv_state, const void* x, const float* weigh
         dispatch_conv<uint16_t>(p, int(W), vec, st);
     else
         dispatch_conv<float>(p, int(W), vec, st);
+    return hipGetLastError() == hipSuccess ? SS_OK : SS_ERR_HIP;
+}
+
+// Per-direction outputs of the cross scan, (4 maps, L, d_in) fp32, placed
+// before the scan's own workspace.
+size_t cross_ys_bytes(int64_t maps, int64_t L, int64_t d_in) {
+    return (size_t(4 * maps) * size_t(L) * size_t(d_in) * sizeof(float) + 255) / 256 * 256;
+}
+
+bool cross_sizes_ok(int64_t maps, int64_t H, int64_t W, int64_t d_in, int64_t n) {
+    if (!sizes_ok(maps, H, W) || d_in <= 0 || n <= 0 || d_in > SS_MAX_CHANNELS || maps > kMaxElems / 4) return false;
+    const int64_t b = 4 * maps, L = H * W;
+    return sizes_ok(b, L, d_in) && b * ((d_in + 63) / 64) <= kMaxWorkgroups && L <= kMaxLength;
+}
+
+SS_EXPORT size_t ss_cross_scan_fwd_workspace_bytes(int64_t maps, int64_t H, int64_t W, int64_t d_in, int64_t n,
+                                                   int dtype) {
+    if (dtype != SS_F32 && dtype != SS_BF16) return 0;
+    if (!cross_sizes_ok(maps, H, W, d_in, n) || n > SS_MAX_STATE) return 0;
+    return cross_ys_bytes(maps, H * W, d_in) + ss_scan_fwd_workspace_bytes(4 * maps, H * W, d_in, n, dtype);
+}
+
+SS_EXPORT int ss_cross_scan_fwd(const void* x, const void* delta, const float* A_log, const void* B, const void* C,
+                                const float* D, const float* delta_bias, int delta_softplus, float* y,
+                                float* last_state, int64_t maps, int64_t H, int64_t W, int64_t d_in, int64_t n,
+                                int dtype, void* workspace, size_t workspace_bytes, void* stream) {
+    if (!x || !delta || !A_log || !B || !C || !D || !y) return SS_ERR_NULL;
+    if (!cross_sizes_ok(maps, H, W, d_in, n)) return SS_ERR_SHAPE;
+    if (dtype != SS_F32 && dtype != SS_BF16) return SS_ERR_DTYPE;
+    if (n > SS_MAX_STATE) return SS_ERR_UNSUPPORTED;
+    const int64_t b = 4 * maps, L = H * W;
+    const size_t es = elem_size(dtype);
+    for (const void* p : {x, delta, B, C})
+        if (!aligned(p, es)) return SS_ERR_ALIGN;
+    for (const void* p : {static_cast<const void*>(A_log), static_cast<const void*>(D),
+                          static_cast<const void*>(delta_bias), static_cast<const void*>(y),
+                          static_cast<const void*>(last_state)})
+        if (p && !aligned(p, 4)) return SS_ERR_ALIGN;
+    if (!aligned(workspace, 256)) return workspace ? SS_ERR_ALIGN : SS_ERR_WORKSPACE;
+    const Range ins[] = {range_of(x, maps * L * d_in, es), range_of(delta, b * L * d_in, es),
+                         range_of(A_log, 4 * d_in * n, 4), range_of(B, b * L * n, es), range_of(C, b * L * n, es),
+                         range_of(D, 4 * d_in, 4), range_of(delta_bias, delta_bias ? 4 * d_in : 0, 4)};
+    const Range ry = range_of(y, maps * L * d_in, 4);
+    const Range rs = range_of(last_state, last_state ? b * d_in * n : 0, 4);
+    for (const Range& r : ins)
+        if (overlaps(r, ry) || overlaps(r, rs)) return SS_ERR_ALIAS;
+    if (overlaps(ry, rs)) return SS_ERR_ALIAS;
+    const size_t need = ss_cross_scan_fwd_workspace_bytes(maps, H, W, d_in, n, dtype);
+    if (!workspace || workspace_bytes < need) return SS_ERR_WORKSPACE;
+    const Range rw = range_of(workspace, int64_t(workspace_bytes), 1);
+    for (const Range& r : ins)
+        if (overlaps(r, rw)) return SS_ERR_ALIAS;
+    if (overlaps(ry, rw) || overlaps(rs, rw)) return SS_ERR_ALIAS;
+
+    const size_t ys_bytes = cross_ys_bytes(maps, L, d_in);
+    float* ys = static_cast<float*>(workspace);
+    ScanParams p{};
+    p.u = x;
+    p.delta = delta;
+    p.A_log = A_log;
+    p.B = B;
+    p.C = C;
+    p.D = D;
+    p.z = nullptr;
+    p.bias = delta_bias;
+    p.y = ys;
+    p.last_state = last_state;
+    p.b = b;
+    p.L = L;
+    p.d_in = d_in;
+    p.n = n;
+    p.softplus = delta_softplus ? 1 : 0;
+    p.cross_h = int(H);
+    p.cross_w = int(W);
+    p.nblk_d = int((d_in + 63) / 64);
+    p.K = 1;
+    p.Lseg = L;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    void* scan_ws = static_cast<char*>(workspace) + ys_bytes;
+    const int rc = dtype == SS_BF16
+                       ? dispatch_seq<uint16_t>(p, SeqMode::Cross, scan_ws, workspace_bytes - ys_bytes, st)
+                       : dispatch_seq<float>(p, SeqMode::Cross, scan_ws, workspace_bytes - ys_bytes, st);
+    if (rc != SS_OK) return rc;
+    // CrossMerge: the four directions' outputs added back at their positions.
+    const bool vec = d_in % 4 == 0 && aligned(y, 16);
+    const int64_t threads = maps * L * (vec ? d_in / 4 : d_in);
+    const dim3 grid(unsigned((threads + 255) / 256));
+    if (vec)
+        hipLaunchKernelGGL((ss::cross_merge<4>), grid, dim3(256), 0, st, ys, y, maps, int(H), int(W), d_in);
+    else
+        hipLaunchKernelGGL((ss::cross_merge<1>), grid, dim3(256), 0, st, ys, y, maps, int(H), int(W), d_in);
     return hipGetLastError() == hipSuccess ? SS_OK : SS_ERR_HIP;
 }

@@ -28,7 +28,8 @@ def declared_functions():
 
 
 def test_header_declares_the_entry_points():
-    assert declared_functions() == sorted(["ss_conv_update", "ss_scan_fwd", "ss_scan_fwd_ex",
+    assert declared_functions() == sorted(["ss_conv_update", "ss_cross_scan_fwd", "ss_cross_scan_fwd_workspace_bytes",
+                                           "ss_scan_fwd", "ss_scan_fwd_ex",
                                            "ss_scan_fwd_workspace_bytes", "ss_state_update", "ss_state_update_ex",
                                            "ss_status_string"])
 
@@ -221,3 +222,47 @@ def test_conv_rejects(ss, over, code):
 
 def test_conv_bias_is_optional(ss):
     assert call_conv(ss, conv_args(bias=None, dtype=7)) == DTYPE
+
+
+def cross_args(**over):
+    a = dict(x=addr(1), delta=addr(2), A_log=addr(3), B=addr(4), C=addr(5), D=addr(6), bias=addr(7), softplus=1,
+             y=addr(8), last=addr(9), maps=16, H=56, W=56, d_in=384, n=1, dtype=0, ws=addr(10), ws_bytes=1 << 30,
+             stream=None)
+    a.update(over)
+    return a
+
+
+def call_cross(ss, a):
+    return ss.lib.ss_cross_scan_fwd(a["x"], a["delta"], a["A_log"], a["B"], a["C"], a["D"], a["bias"], a["softplus"],
+                                    a["y"], a["last"], a["maps"], a["H"], a["W"], a["d_in"], a["n"], a["dtype"],
+                                    a["ws"], a["ws_bytes"], a["stream"])
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(x=None), NULL), (dict(delta=None), NULL), (dict(A_log=None), NULL), (dict(B=None), NULL),
+    (dict(C=None), NULL), (dict(D=None), NULL), (dict(y=None), NULL),
+    (dict(maps=0), SHAPE), (dict(H=0), SHAPE), (dict(W=-2), SHAPE), (dict(d_in=0), SHAPE), (dict(n=0), SHAPE),
+    (dict(H=1 << 16, W=1 << 16), SHAPE), (dict(maps=1 << 45), SHAPE),
+    (dict(dtype=3), DTYPE), (dict(n=65), UNSUP),
+    (dict(ws=None), WS), (dict(ws_bytes=10), WS), (dict(ws_bytes=16 * 16 * 3136 * 384 - 1), WS),
+    (dict(x=addr(1) + 2), ALIGN), (dict(y=addr(8) + 2), ALIGN), (dict(last=addr(9) + 1), ALIGN),
+    (dict(ws=addr(10) + 16), ALIGN),
+    (dict(y=addr(1)), ALIAS), (dict(last=addr(3)), ALIAS), (dict(y=addr(9)), ALIAS), (dict(ws=addr(8)), ALIAS),
+    (dict(bias=addr(9) + 8), ALIAS),
+])
+def test_cross_rejects(ss, over, code):
+    assert call_cross(ss, cross_args(**over)) == code
+
+
+def test_cross_optional_pointers_may_be_null(ss):
+    assert call_cross(ss, cross_args(bias=None, last=None, dtype=5)) == DTYPE
+
+
+def test_cross_workspace_query(ss):
+    q = ss.lib.ss_cross_scan_fwd_workspace_bytes
+    q.restype = ctypes.c_size_t
+    full = q(16, 56, 56, 384, 1, 0)
+    assert full >= 16 * 16 * 3136 * 384 + ss.scan_fwd_workspace_bytes(64, 3136, 384, 1, 0)
+    assert full == q(16, 56, 56, 384, 1, 1)
+    for bad in ((0, 5, 5, 8, 1, 0), (1, 0, 5, 8, 1, 0), (1, 5, 5, 8, 65, 0), (1, 5, 5, 8, 1, 2)):
+        assert q(*bad) == 0, bad

@@ -146,6 +146,34 @@ def scan_inputs(cfg: ScanConfig | int, seed: int | None = None) -> dict:
             "z": None, "delta_bias": None, "delta_softplus": True, "dtype": cfg.dtype}
 
 
+def cross_scan_inputs(cfg: ScanConfig | int = 3, seed: int | None = None) -> dict:
+    """A map workload in the layout of the fused cross scan (CPU tensors).
+
+    The same draws as scan_inputs for that workload, kept as the feature map
+    x (maps, H, W, d_in) instead of its four unrolled copies; delta, B, C
+    become (maps, 4, L, .) and A_log, D one set per direction (the shared
+    values repeated), so the fused cross scan of these inputs merges exactly
+    the four scans of scan_inputs(cfg).
+    """
+    if isinstance(cfg, int):
+        cfg = CONFIGS[cfg]
+    assert cfg.vmamba
+    seed = 1000 + cfg.index if seed is None else seed
+    g = _gen(seed)
+    r = lambda *s: torch.randn(*s, generator=g, dtype=F32)  # noqa: E731
+    fmap = r(cfg.maps, cfg.side, cfg.side, cfg.d_in)
+    delta = r(cfg.b, cfg.L, cfg.d_in) - 2.0
+    Bm = r(cfg.b, cfg.L, cfg.n)
+    Cm = r(cfg.b, cfg.L, cfg.n)
+    D = r(cfg.d_in)
+    m = cfg.maps
+    cast = lambda t: t.to(cfg.dtype).contiguous()  # noqa: E731
+    return {"x": cast(fmap), "delta": cast(delta.reshape(m, 4, cfg.L, cfg.d_in)),
+            "A_log": torch.zeros(4, cfg.d_in, cfg.n, dtype=F32), "B": cast(Bm.reshape(m, 4, cfg.L, cfg.n)),
+            "C": cast(Cm.reshape(m, 4, cfg.L, cfg.n)), "D": D.expand(4, cfg.d_in).contiguous(), "delta_bias": None,
+            "delta_softplus": True, "dtype": cfg.dtype}
+
+
 def decode_inputs(cfg: DecodeConfig | int = 4, seed: int | None = None, steps: int | None = None,
                   b: int | None = None) -> dict:
     """Initial state and pre-drawn per-step inputs of the decode workload (CPU tensors).
