@@ -60,6 +60,8 @@ def _bind(lib: ctypes.CDLL) -> ctypes.CDLL:
     lib.ss_oracle_scan_ex.argtypes = [P] * 8 + [ctypes.c_int, P, ctypes.c_int, P, P, I64, I64, I64, I64]
     lib.ss_oracle_state_update_ex.restype = ctypes.c_int
     lib.ss_oracle_state_update_ex.argtypes = [P] * 9 + [ctypes.c_int, ctypes.c_int, P, I64, I64, I64]
+    lib.ss_oracle_scan_bwd.restype = ctypes.c_int
+    lib.ss_oracle_scan_bwd.argtypes = [P] * 8 + [ctypes.c_int] + [P] * 12 + [I64, I64, I64, I64]
     lib.ss_oracle_cross_scan.restype = ctypes.c_int
     lib.ss_oracle_cross_scan.argtypes = [P] * 7 + [ctypes.c_int, P, P, I64, I64, I64, I64, I64]
     lib.ss_oracle_conv_update.restype = ctypes.c_int
@@ -195,3 +197,34 @@ def cross_scan(x, delta, A_log, B, C, D, delta_bias=None, delta_softplus=True, l
     if rc != 0:
         raise ValueError(f"ss_oracle_cross_scan returned {rc}")
     return y, last
+
+
+def scan_bwd(u, delta, A_log, B, C, D, z=None, delta_bias=None, delta_softplus=True, h0=None, dy=None, dlast=None,
+             lib=None):
+    """Gradients of the scan (Euler input term) for output gradients dy (b, L, d_in) and dlast (b, d_in, n).
+
+    Returns a dict of float64 arrays: du, ddelta, dA_log, dB, dC, dD, and dz, ddelta_bias, dh0 when z,
+    delta_bias, h0 are given.
+    """
+    lib = lib or load()
+    u, delta, A_log, B, C, D, dy = map(_f64, (u, delta, A_log, B, C, D, dy))
+    z, delta_bias, h0, dlast = _f64(z), _f64(delta_bias), _f64(h0), _f64(dlast)
+    b, L, d_in = u.shape
+    n = A_log.shape[1]
+    assert dy.shape == u.shape and (dlast is None or dlast.shape == (b, d_in, n))
+    out = dict(du=np.empty_like(u), ddelta=np.empty_like(u), dA_log=np.empty((d_in, n)), dB=np.empty((b, L, n)),
+               dC=np.empty((b, L, n)), dD=np.empty(d_in))
+    if z is not None:
+        out["dz"] = np.empty_like(u)
+    if delta_bias is not None:
+        out["ddelta_bias"] = np.empty(d_in)
+    if h0 is not None:
+        out["dh0"] = np.empty((b, d_in, n))
+    rc = lib.ss_oracle_scan_bwd(_ptr(u), _ptr(delta), _ptr(A_log), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
+                                _ptr(delta_bias), int(bool(delta_softplus)), _ptr(h0), _ptr(dy), _ptr(dlast),
+                                _ptr(out["du"]), _ptr(out["ddelta"]), _ptr(out["dA_log"]), _ptr(out["dB"]),
+                                _ptr(out["dC"]), _ptr(out["dD"]), _ptr(out.get("dz")), _ptr(out.get("ddelta_bias")),
+                                _ptr(out.get("dh0")), b, L, d_in, n)
+    if rc != 0:
+        raise ValueError(f"ss_oracle_scan_bwd returned {rc}")
+    return out

@@ -31,6 +31,12 @@
  * torch): a rolling window of the last W inputs per channel, a depthwise dot
  * product with the channel's W weights, the bias, then silu.
  *
+ * ss_oracle_scan_bwd is the gradient of ss_oracle_scan_ex (Euler input term)
+ * with respect to every input, for a given gradient of y and of last_state.
+ * The pages only name the autograd wrappers, so the formulas are derived
+ * here by the chain rule and written out step by step below; they are pinned
+ * to torch autograd and to finite differences of the forward.
+ *
  * ss_oracle_cross_scan is VMamba's CrossScan / scan / CrossMerge
  * (githubissues.com VMamba issue 206: the cross operations only arrange the
  * sequence): each feature map is read as four sequences -- row-major,
@@ -292,4 +298,110 @@ int ss_oracle_cross_scan(const double *x, const double *delta, const double *A_l
     free(uk);
     free(yk);
     return rc;
+}
+
+/* Gradient of the scan (Euler input term, optional h0) for given dy (b, L,
+ * d_in) and dlast (b, d_in, n, or NULL for zero).  Per (b, d) channel, with
+ * w_t = Delta_t u_t, a_tk = exp(Delta_t A_k), the pre-gate output
+ * y'_t = sum_k C_tk h_tk + D u_t and y_t = y'_t silu(z_t):
+ *   dz_t    = dy_t y'_t silu'(z_t),  dy'_t = dy_t silu(z_t)     (dy'_t = dy_t without z)
+ *   g_tk    = dL/dh_tk = dy'_t C_tk + a_(t+1)k g_(t+1)k,  g_(L)k = dlast_k
+ *   du_t    = dy'_t D + sum_k g_tk Delta_t B_tk
+ *   dDelta_t= sum_k g_tk (A_k a_tk h_(t-1)k + B_tk u_t)
+ *   ddelta_t= dDelta_t softplus'(delta_t + bias) = dDelta_t sigmoid(delta_t + bias)  (dDelta_t without softplus)
+ *   dB_tk  += sum_d g_tk Delta_t u_t,   dC_tk += sum_d dy'_t h_tk
+ *   dA_log_dk += sum_(b,t) g_tk Delta_t a_tk h_(t-1)k A_k       (dA/dA_log = A)
+ *   dD_d   += sum_(b,t) dy'_t u_t,      dbias_d += sum_(b,t) ddelta_t
+ *   dh0_k   = a_0k g_0k
+ * Outputs are overwritten (the sums start from zero); dz, ddelta_bias and
+ * dh0 may be NULL when z, the bias or h0 are absent. */
+int ss_oracle_scan_bwd(const double *u, const double *delta, const double *A_log,
+                       const double *B, const double *C, const double *D,
+                       const double *z, const double *delta_bias, int delta_softplus,
+                       const double *h0, const double *dy, const double *dlast,
+                       double *du, double *ddelta, double *dA_log, double *dB, double *dC,
+                       double *dD, double *dz, double *ddelta_bias, double *dh0,
+                       int64_t b, int64_t L, int64_t d_in, int64_t n)
+{
+    if (!u || !delta || !A_log || !B || !C || !D || !dy || !du || !ddelta || !dA_log || !dB || !dC || !dD)
+        return -1;
+    if (b <= 0 || L <= 0 || d_in <= 0 || n <= 0)
+        return -2;
+    double *hs = malloc(sizeof(double) * (size_t)((L + 1) * n));   /* h_(t-1) for t = 0 .. L */
+    double *g = malloc(sizeof(double) * (size_t)n);
+    double *A = malloc(sizeof(double) * (size_t)n);
+    if (!hs || !g || !A) {
+        free(hs);
+        free(g);
+        free(A);
+        return -3;
+    }
+    for (int64_t i = 0; i < b * L * n; i++)
+        dB[i] = dC[i] = 0.0;
+    for (int64_t i = 0; i < d_in * n; i++)
+        dA_log[i] = 0.0;
+    for (int64_t d = 0; d < d_in; d++) {
+        dD[d] = 0.0;
+        if (ddelta_bias)
+            ddelta_bias[d] = 0.0;
+    }
+    for (int64_t bi = 0; bi < b; bi++) {
+        for (int64_t d = 0; d < d_in; d++) {
+            /* forward again, keeping every state: hs[(t+1) n + k] = h_tk */
+            for (int64_t k = 0; k < n; k++) {
+                A[k] = -exp(A_log[d * n + k]);
+                hs[k] = h0 ? h0[(bi * d_in + d) * n + k] : 0.0;
+            }
+            for (int64_t t = 0; t < L; t++) {
+                int64_t e = (bi * L + t) * d_in + d, r = (bi * L + t) * n;
+                double dl = step_size(delta[e], delta_bias, d, delta_softplus);
+                for (int64_t k = 0; k < n; k++)
+                    hs[(t + 1) * n + k] = exp(dl * A[k]) * hs[t * n + k] + dl * B[r + k] * u[e];
+            }
+            /* backward in time */
+            for (int64_t k = 0; k < n; k++)
+                g[k] = dlast ? dlast[(bi * d_in + d) * n + k] : 0.0;
+            for (int64_t t = L - 1; t >= 0; t--) {
+                int64_t e = (bi * L + t) * d_in + d, r = (bi * L + t) * n;
+                double x = delta[e] + (delta_bias ? delta_bias[d] : 0.0);
+                double dl = delta_softplus ? ss_oracle_softplus(x) : x;
+                /* the gate: y = y' silu(z) */
+                double dyp = dy[e];
+                if (z) {
+                    double yp = D[d] * u[e];
+                    for (int64_t k = 0; k < n; k++)
+                        yp += C[r + k] * hs[(t + 1) * n + k];
+                    double sg = 1.0 / (1.0 + exp(-z[e]));                  /* sigmoid(z) */
+                    dz[e] = dy[e] * yp * sg * (1.0 + z[e] * (1.0 - sg));    /* silu'(z) = s (1 + z (1 - s)) */
+                    dyp = dy[e] * z[e] * sg;                                /* dy * silu(z) */
+                }
+                double dut = dyp * D[d];
+                double ddl = 0.0;
+                dD[d] += dyp * u[e];
+                for (int64_t k = 0; k < n; k++) {
+                    double a = exp(dl * A[k]);
+                    double hprev = hs[t * n + k];
+                    g[k] += dyp * C[r + k];                   /* dL/dh_tk */
+                    dC[r + k] += dyp * hs[(t + 1) * n + k];
+                    dB[r + k] += g[k] * dl * u[e];
+                    dut += g[k] * dl * B[r + k];
+                    ddl += g[k] * (A[k] * a * hprev + B[r + k] * u[e]);
+                    dA_log[d * n + k] += g[k] * dl * a * hprev * A[k];
+                    g[k] *= a;                                /* on to h_(t-1) */
+                }
+                du[e] = dut;
+                double dd = delta_softplus ? ddl / (1.0 + exp(-x)) : ddl;   /* softplus' = sigmoid */
+                ddelta[e] = dd;
+                if (ddelta_bias)
+                    ddelta_bias[d] += dd;
+            }
+            if (dh0)
+                for (int64_t k = 0; k < n; k++)
+                    dh0[(bi * d_in + d) * n + k] = g[k];
+        }
+    }
+    free(hs);
+    free(g);
+    free(A);
+    return 0;
 }

@@ -30,8 +30,9 @@ ISOLATE = "isolate"
 
 # (description, text in ss_oracle.c, replacement[, ISOLATE])
 MUTANTS = [
-    ("A sign", "A[k] = -exp(A_log[d * n + k]);", "A[k] = exp(A_log[d * n + k]);"),
-    ("A without exp", "A[k] = -exp(A_log[d * n + k]);", "A[k] = -A_log[d * n + k];"),
+    ("A sign", "A[k] = -exp(A_log[d * n + k]);          /*", "A[k] = exp(A_log[d * n + k]);          /*"),
+    ("A without exp", "A[k] = -exp(A_log[d * n + k]);          /*", "A[k] = -A_log[d * n + k];          /*"),
+    ("bwd A sign", "A[k] = -exp(A_log[d * n + k]);\n                hs[k]", "A[k] = exp(A_log[d * n + k]);\n                hs[k]"),
     ("nonzero initial state", "h[k] = h0 ? h0[(bi * d_in + d) * n + k] : 0.0;",
      "h[k] = h0 ? h0[(bi * d_in + d) * n + k] : 1e-3;"),
     ("initial state ignored", "h[k] = h0 ? h0[(bi * d_in + d) * n + k] : 0.0;", "h[k] = 0.0;"),
@@ -95,6 +96,24 @@ MUTANTS = [
      "rc = ss_oracle_scan_ex(uk, delta + seq * L * d_in, A_log,"),
     ("cross D of direction 0", "B + seq * L * n, C + seq * L * n, D + k * d_in, NULL,", "B + seq * L * n, C + seq * L * n, D, NULL,"),
     ("cross inputs of direction 0", "rc = ss_oracle_scan_ex(uk, delta + seq * L * d_in,", "rc = ss_oracle_scan_ex(uk, delta + m * 4 * L * d_in,"),
+    ("bwd adjoint not decayed", "g[k] *= a;                                /* on to h_(t-1) */", "(void)a;"),
+    ("bwd adjoint misses the readout", "g[k] += dyp * C[r + k];                   /* dL/dh_tk */", "g[k] += 0.0 * C[r + k];"),
+    ("bwd dC from the previous state", "dC[r + k] += dyp * hs[(t + 1) * n + k];", "dC[r + k] += dyp * hs[t * n + k];"),
+    ("bwd dB without delta", "dB[r + k] += g[k] * dl * u[e];", "dB[r + k] += g[k] * u[e];"),
+    ("bwd du without the skip", "double dut = dyp * D[d];", "double dut = 0.0;"),
+    ("bwd dDelta without the decay term", "ddl += g[k] * (A[k] * a * hprev + B[r + k] * u[e]);", "ddl += g[k] * B[r + k] * u[e];"),
+    ("bwd dDelta uses the new state", "ddl += g[k] * (A[k] * a * hprev + B[r + k] * u[e]);",
+     "ddl += g[k] * (A[k] * a * hs[(t + 1) * n + k] + B[r + k] * u[e]);"),
+    ("bwd dA_log without A", "dA_log[d * n + k] += g[k] * dl * a * hprev * A[k];", "dA_log[d * n + k] += g[k] * dl * a * hprev;"),
+    ("bwd softplus derivative", "double dd = delta_softplus ? ddl / (1.0 + exp(-x)) : ddl;",
+     "double dd = delta_softplus ? ddl / (1.0 + exp(x)) : ddl;"),
+    ("bwd dz without y'", "dz[e] = dy[e] * yp * sg * (1.0 + z[e] * (1.0 - sg));", "dz[e] = dy[e] * sg * (1.0 + z[e] * (1.0 - sg));"),
+    ("bwd silu derivative", "dz[e] = dy[e] * yp * sg * (1.0 + z[e] * (1.0 - sg));", "dz[e] = dy[e] * yp * sg;"),
+    ("bwd gate ignored", "dyp = dy[e] * z[e] * sg;                                /* dy * silu(z) */", "(void)sg;"),
+    ("bwd dD uses dy", "dD[d] += dyp * u[e];", "dD[d] += dy[e] * u[e];"),
+    ("bwd bias gradient missing", "ddelta_bias[d] += dd;", "ddelta_bias[d] += 0.0;"),
+    ("bwd last-state gradient ignored", "g[k] = dlast ? dlast[(bi * d_in + d) * n + k] : 0.0;", "g[k] = 0.0;"),
+    ("bwd forward ignores h0", "hs[k] = h0 ? h0[(bi * d_in + d) * n + k] : 0.0;", "hs[k] = 0.0;"),
     ("conv silu ignored", "out[bi * d_in + d] = act ? ss_oracle_silu(acc) : acc;", "out[bi * d_in + d] = acc;"),
 ]
 
