@@ -223,6 +223,43 @@ int ss_cross_scan_fwd(const void *x, const void *delta, const float *A_log,
                       int64_t maps, int64_t H, int64_t W, int64_t d_in, int64_t n,
                       int dtype, void *workspace, size_t workspace_bytes, void *stream);
 
+/* Largest state size n of ss_scan_bwd. */
+#define SS_MAX_BWD_STATE 32
+
+/* Bytes of device workspace ss_scan_bwd needs (0 for invalid arguments). */
+size_t ss_scan_bwd_workspace_bytes(int64_t b, int64_t L, int64_t d_in, int64_t n, int dtype);
+
+/*
+ * Gradient of ss_scan_fwd_ex with the delta' * B * u input term (the pages
+ * only name the autograd wrappers of the scan; the formulas are the chain
+ * rule of the forward definition above).  Given the forward's inputs and
+ * the gradients dy of y and dlast_state of last_state, writes the gradients
+ * of every input:
+ *   dy          : (b, L, d_in) dtype
+ *   dlast_state : (b, d_in, n) fp32, or NULL (zero)
+ *   du, ddelta  : (b, L, d_in) dtype      ddelta is with respect to delta before bias and softplus
+ *   dA_log      : (d_in, n)    fp32       dB, dC : (b, L, n) dtype
+ *   dD          : (d_in)       fp32       dz : (b, L, d_in) dtype, required when z is given
+ *   ddelta_bias : (d_in) fp32, or NULL (only written when delta_bias is given)
+ *   dinitial_state : (b, d_in, n) fp32, or NULL
+ * The call runs the forward scan again (saving the state every 8 steps in
+ * the workspace) and then the adjoint backwards in time; sums over channels,
+ * batch rows and time are formed from per-workgroup partials in a fixed
+ * order, so the results are the same bit for bit on every run.  Sizes as for
+ * ss_scan_fwd with n <= SS_MAX_BWD_STATE (else SS_ERR_UNSUPPORTED); the
+ * workspace must be 256-byte aligned and ss_scan_bwd_workspace_bytes() long.
+ * No output may overlap an input, another output or the workspace
+ * (SS_ERR_ALIAS).  Returns an ss_status.
+ */
+int ss_scan_bwd(const void *u, const void *delta, const float *A_log,
+                const void *B, const void *C, const float *D,
+                const void *z, const float *delta_bias, int delta_softplus,
+                const float *initial_state, const void *dy, const float *dlast_state,
+                void *du, void *ddelta, float *dA_log, void *dB, void *dC,
+                float *dD, void *dz, float *ddelta_bias, float *dinitial_state,
+                int64_t b, int64_t L, int64_t d_in, int64_t n, int dtype,
+                void *workspace, size_t workspace_bytes, void *stream);
+
 /* Largest convolution width W of ss_conv_update. */
 #define SS_MAX_CONV_WIDTH 8
 

@@ -13,6 +13,11 @@ Entry points mirror the C ABI (``include/ss_scan.h``):
                                              -> y  or  (y, last_state)
   state_update(state, x, dt, A_log, B, C, D, z=None, dt_bias=None, dt_softplus=True,
                zoh=False)                    -> y  (state is updated in place)
+  scan_bwd(u, delta, A_log, B, C, D, dy, z=None, delta_bias=None, delta_softplus=True,
+           initial_state=None, dlast_state=None)  -> dict of gradients
+  selective_scan(u, delta, A_log, B, C, D, z=None, delta_bias=None, delta_softplus=True,
+                 initial_state=None)          -> y, differentiable (torch.autograd.Function
+                                                 calling scan_fwd / scan_bwd)
   cross_scan_fwd(x, delta, A_log, B, C, D, delta_bias=None, delta_softplus=True,
                  return_last_state=False)    -> y (maps, H, W, d_in) fp32  or  (y, last_state)
   conv_update(conv_state, x, weight, bias=None, silu=True)
@@ -48,12 +53,14 @@ SS_F32 = 0
 SS_BF16 = 1
 SS_MAX_STATE = 64
 SS_MAX_CONV_WIDTH = 8
+SS_MAX_BWD_STATE = 32
 SS_DISC_EULER = 0
 SS_DISC_ZOH = 1
 STATUS = {0: "SS_OK", -1: "SS_ERR_NULL", -2: "SS_ERR_SHAPE", -3: "SS_ERR_DTYPE", -4: "SS_ERR_UNSUPPORTED",
           -5: "SS_ERR_WORKSPACE", -6: "SS_ERR_HIP", -7: "SS_ERR_ALIAS", -8: "SS_ERR_ALIGN", -9: "SS_ERR_MODE"}
 EXPORTS = ("ss_scan_fwd_workspace_bytes", "ss_scan_fwd", "ss_scan_fwd_ex", "ss_state_update", "ss_state_update_ex",
-           "ss_cross_scan_fwd", "ss_cross_scan_fwd_workspace_bytes", "ss_conv_update", "ss_status_string")
+           "ss_scan_bwd", "ss_scan_bwd_workspace_bytes", "ss_cross_scan_fwd", "ss_cross_scan_fwd_workspace_bytes",
+           "ss_conv_update", "ss_status_string")
 
 
 class SSError(RuntimeError):
@@ -78,6 +85,10 @@ def _load() -> ctypes.CDLL:
     lib.ss_state_update.argtypes = [P, P, P, P, P, P, P, P, P, I, P, I64, I64, I64, I, P]
     lib.ss_state_update_ex.restype = I
     lib.ss_state_update_ex.argtypes = [P, P, P, P, P, P, P, P, P, I, I, P, I64, I64, I64, I, P]
+    lib.ss_scan_bwd_workspace_bytes.restype = ctypes.c_size_t
+    lib.ss_scan_bwd_workspace_bytes.argtypes = [I64, I64, I64, I64, I]
+    lib.ss_scan_bwd.restype = I
+    lib.ss_scan_bwd.argtypes = [P] * 8 + [I] + [P] * 12 + [I64, I64, I64, I64, I, P, ctypes.c_size_t, P]
     lib.ss_cross_scan_fwd_workspace_bytes.restype = ctypes.c_size_t
     lib.ss_cross_scan_fwd_workspace_bytes.argtypes = [I64, I64, I64, I64, I64, I]
     lib.ss_cross_scan_fwd.restype = I
@@ -299,3 +310,79 @@ def cross_scan_fwd(x, delta, A_log, B, C, D, delta_bias=None, delta_softplus=Tru
     if rc != 0:
         raise SSError(rc, "ss_cross_scan_fwd")
     return (y, last_state) if return_last_state else y
+
+
+def scan_bwd(u, delta, A_log, B, C, D, dy, z=None, delta_bias=None, delta_softplus=True, initial_state=None,
+             dlast_state=None, workspace=None):
+    """Gradients of the scan (delta' B u input term) for output gradients dy (and dlast_state).
+
+    Returns a dict: du, ddelta, dz (dtype of u; dz only with z), dA_log, dD, ddelta_bias (fp32; only
+    with delta_bias), dB, dC (dtype of u), dinitial_state (fp32; only with initial_state).
+    """
+    if u.dim() != 3 or A_log.dim() != 2:
+        raise ValueError("u must be (b, L, d_in) and A_log (d_in, n)")
+    b, L, d_in = u.shape
+    n = A_log.shape[1]
+    dev = u.device
+    code = _dtype_code(u.dtype)
+    for t, name, shape, dt in ((u, "u", (b, L, d_in), u.dtype), (delta, "delta", (b, L, d_in), u.dtype),
+                               (A_log, "A_log", (d_in, n), torch.float32), (B, "B", (b, L, n), u.dtype),
+                               (C, "C", (b, L, n), u.dtype), (D, "D", (d_in,), torch.float32),
+                               (z, "z", (b, L, d_in), u.dtype), (delta_bias, "delta_bias", (d_in,), torch.float32),
+                               (initial_state, "initial_state", (b, d_in, n), torch.float32),
+                               (dy, "dy", (b, L, d_in), u.dtype),
+                               (dlast_state, "dlast_state", (b, d_in, n), torch.float32)):
+        _check(t, name, shape, dt, dev)
+    g = dict(du=torch.empty_like(u), ddelta=torch.empty_like(u),
+             dA_log=torch.empty((d_in, n), dtype=torch.float32, device=dev),
+             dB=torch.empty_like(B), dC=torch.empty_like(C), dD=torch.empty(d_in, dtype=torch.float32, device=dev))
+    if z is not None:
+        g["dz"] = torch.empty_like(z)
+    if delta_bias is not None:
+        g["ddelta_bias"] = torch.empty(d_in, dtype=torch.float32, device=dev)
+    if initial_state is not None:
+        g["dinitial_state"] = torch.empty((b, d_in, n), dtype=torch.float32, device=dev)
+    if b == 0 or L == 0 or d_in == 0:
+        for k, v in g.items():
+            if k == "dinitial_state" and dlast_state is not None:
+                v.copy_(dlast_state)
+            else:
+                v.zero_()
+        return g
+    need = int(lib.ss_scan_bwd_workspace_bytes(b, L, d_in, n, code))
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev) if need else None
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    with torch.cuda.device(dev):
+        rc = lib.ss_scan_bwd(_ptr(u), _ptr(delta), _ptr(A_log), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(delta_bias),
+                             int(bool(delta_softplus)), _ptr(initial_state), _ptr(dy), _ptr(dlast_state),
+                             _ptr(g["du"]), _ptr(g["ddelta"]), _ptr(g["dA_log"]), _ptr(g["dB"]), _ptr(g["dC"]),
+                             _ptr(g["dD"]), _ptr(g.get("dz")), _ptr(g.get("ddelta_bias")),
+                             _ptr(g.get("dinitial_state")), b, L, d_in, n, code, _ptr(workspace), ws_bytes,
+                             _stream(dev))
+    if rc != 0:
+        raise SSError(rc, "ss_scan_bwd")
+    return g
+
+
+class _SelectiveScan(torch.autograd.Function):
+    """The scan as an autograd function: forward ss_scan_fwd(_ex), backward ss_scan_bwd."""
+
+    @staticmethod
+    def forward(ctx, u, delta, A_log, B, C, D, z, delta_bias, delta_softplus, initial_state):
+        y = scan_fwd(u, delta, A_log, B, C, D, z, delta_bias, delta_softplus, initial_state=initial_state)
+        ctx.delta_softplus = delta_softplus
+        ctx.save_for_backward(u, delta, A_log, B, C, D, z, delta_bias, initial_state)
+        return y
+
+    @staticmethod
+    def backward(ctx, dy):
+        u, delta, A_log, B, C, D, z, delta_bias, initial_state = ctx.saved_tensors
+        g = scan_bwd(u, delta, A_log, B, C, D, dy.contiguous(), z, delta_bias, ctx.delta_softplus, initial_state)
+        return (g["du"], g["ddelta"], g["dA_log"], g["dB"], g["dC"], g["dD"], g.get("dz"), g.get("ddelta_bias"),
+                None, g.get("dinitial_state"))
+
+
+def selective_scan(u, delta, A_log, B, C, D, z=None, delta_bias=None, delta_softplus=True, initial_state=None):
+    """y of the scan, differentiable with respect to every tensor argument (torch autograd)."""
+    return _SelectiveScan.apply(u, delta, A_log, B, C, D, z, delta_bias, delta_softplus, initial_state)

@@ -1,0 +1,434 @@
+// scan_bwd_kernels.h -- gradient of the selective scan (Euler input term) on
+// gfx950.  The pages only name the autograd wrappers around the scan; the
+// formulas below are the chain rule applied to the forward recurrence
+// (mhpn.cn selective_scan walk-through, sections 3-5 and 7; jiafeimiao.top
+// Mamba.step for the bias and the gate).  Per (b, d) channel, with
+// w_t = Delta_t u_t, a_tk = exp(Delta_t A_k), y'_t = sum_k C_tk h_tk + D u_t:
+//     dy'_t    = dy_t silu(z_t)                   (dy_t without a gate)
+//     g_tk     = dL/dh_tk = dy'_t C_tk + a_(t+1)k g_(t+1)k,   g_Lk = dlast_k
+//     S1_t     = sum_k g_tk B_tk,   S2_t = sum_k g_tk A_k a_tk h_(t-1)k
+//     du_t     = Delta_t S1_t + dy'_t D
+//     dDelta_t = S2_t + u_t S1_t,   ddelta_t = dDelta_t sigmoid(delta_t + bias)  (softplus' = sigmoid)
+//     dz_t     = dy_t y'_t silu'(z_t)
+//     dB_tk    = sum_d g_tk w_t,    dC_tk = sum_d dy'_t h_tk
+//     dA_log_k = sum_(b,t) g_tk Delta_t a_tk h_(t-1)k A_k,   dD = sum dy' u,   dbias = sum ddelta
+//     dh0_k    = a_0k g_0k
+//
+// scan_bwd<TIn, SC, NSW, SP, GATE>: one workgroup per (b, 64-channel group)
+// walks L backwards in chunks of kCkptSteps = 8 steps.  The forward pass
+// saved the state every 8 steps; the SC recurrence waves (NSW states of the
+// 64 channels each) reload the state entering the chunk, run the chunk's 8
+// steps forward again keeping every h and decay in registers, then run the
+// adjoint back through them.  The 4 element waves load and prepare the next
+// chunk (delta', delta' u, dy', the fp32 B and C rows, the entering state;
+// their global loads are issued one chunk earlier still), and finish the
+// previous one (sums of the waves' S1, S2 and readout partials, du, ddelta,
+// dz, and the chunk's dB, dC rows).  Sums over the 64 channels (dB, dC) are
+// DPP reductions inside each recurrence wave; sums over the channel groups,
+// batch rows and time (dB, dC, dA_log, dD, dbias) go through per-workgroup
+// partials that reduce_groups adds in a fixed order, so every gradient is
+// the same bit for bit on every run.
+#pragma once
+
+#include <type_traits>
+
+#include "scan_kernels.h"
+#include "ss_device.h"
+
+namespace ss {
+
+struct BwdParams {
+    const void* u;
+    const void* delta;
+    const float* A_log;
+    const void* B;
+    const void* C;
+    const float* D;
+    const void* z;
+    const float* bias;
+    const float* h0;          // (b, d_in, n) or null
+    const void* dy;           // (b, L, d_in)
+    const float* dlast;       // (b, d_in, n) or null
+    const float* ckpt;        // (b, nck, n, d_in): state after steps 8 (i + 1)
+    void* du;
+    void* ddelta;
+    void* dz;                 // null without a gate
+    float* dh0;               // null unless asked
+    float* part_B;            // (nblk_d, b, L, n) dB per channel group
+    float* part_C;            // (nblk_d, b, L, n)
+    float* part_A;            // (b, d_in, n) dA_log per batch row
+    float* part_D;            // (b, d_in)
+    float* part_bias;         // (b, d_in)
+    int64_t b, L, d_in, n;
+    int nck, nblk_d, softplus;
+};
+
+// v moved from another lane by a DPP control (row_shr, row_bcast); lanes the
+// control leaves out, or whose row is not in ROW_MASK, read 0.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ float dpp_take(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, ROW_MASK, 0xf, true));
+}
+
+// Sum of v over the 64 lanes of the wave, complete in lane 63: prefix sums
+// inside each row of 16 lanes (row_shr 1, 2, 4, 8), then lane 15 of rows 0
+// and 2 added into rows 1 and 3 (row_bcast:15), then lane 31 into rows 2 and
+// 3 (row_bcast:31).  Every lane of the wave must be active.
+__device__ __forceinline__ float wave_sum_last(float v) {
+    v += dpp_take<0x111, 0xf>(v);
+    v += dpp_take<0x112, 0xf>(v);
+    v += dpp_take<0x114, 0xf>(v);
+    v += dpp_take<0x118, 0xf>(v);
+    v += dpp_take<0x142, 0xa>(v);
+    v += dpp_take<0x143, 0xc>(v);
+    return v;
+}
+
+// LDS of scan_bwd<SC recurrence waves, NP padded states>, T = 8 steps.
+template <int SC, int NP, bool GATE>
+struct BwdLds {
+    static constexpr int T = kCkptSteps;
+    static constexpr int PREP = T * 64 * 16;                  // (Delta, w, dy', u) per (step, channel)
+    static constexpr int PART = SC * T * 64 * 8;              // (S1, S2) per (wave, step, channel)
+    static constexpr int YP = GATE ? SC * T * 64 * 4 : 0;     // readout partials
+    static constexpr int CK = NP * 64 * 4;                    // state entering the chunk
+    static constexpr int BC = T * 2 * NP * 4;                 // B, C rows as fp32, grouped per wave
+    static constexpr int DBC = T * 2 * NP * 4;                // dB, dC sums of the chunk
+    static constexpr int off_prep = 0;                        // [3]
+    static constexpr int off_part = off_prep + 3 * PREP;      // [2]
+    static constexpr int off_yp = off_part + 2 * PART;        // [2]
+    static constexpr int off_ck = off_yp + 2 * YP;            // [2]
+    static constexpr int off_bc = off_ck + 2 * CK;            // [2]
+    static constexpr int off_dbc = off_bc + 2 * BC;           // [2]
+    static constexpr int bytes = off_dbc + 2 * DBC;
+};
+
+template <typename TIn, int SC, int NSW, bool SP, bool GATE>
+__global__ __launch_bounds__((SC + 4) * 64) void scan_bwd(const BwdParams p) {
+    constexpr int T = kCkptSteps;
+    constexpr int NE = 4 * 64;                     // element threads
+    constexpr int V = T * 64 / NE;                 // consecutive channels per element thread
+    constexpr int TPR = 64 / V;                    // element threads per step row
+    constexpr int NP = SC * NSW;
+    constexpr int EBC = (T * NP + NE - 1) / NE;    // B (and C) values each element thread stages per chunk
+    constexpr int ECK = (NP * 64 + NE - 1) / NE;   // entering-state values each element thread stages
+    using Lds = BwdLds<SC, NP, GATE>;
+    static_assert(Lds::bytes <= 160 * 1024, "LDS of one workgroup");
+    static_assert(NE / TPR == T, "thread tiling of a chunk");
+    extern __shared__ __align__(16) float smem[];
+    char* const lds = reinterpret_cast<char*>(smem);
+    float4* s_prep = reinterpret_cast<float4*>(lds + Lds::off_prep);   // [3][T][64]
+    float2* s_part = reinterpret_cast<float2*>(lds + Lds::off_part);   // [2][SC][T][64]
+    float* s_yp = reinterpret_cast<float*>(lds + Lds::off_yp);         // [2][SC][T][64]
+    float* s_ck = reinterpret_cast<float*>(lds + Lds::off_ck);         // [2][NP][64]
+    float* s_bc = reinterpret_cast<float*>(lds + Lds::off_bc);         // [2][T][SC][2][NSW]
+    float* s_dbc = reinterpret_cast<float*>(lds + Lds::off_dbc);       // [2][T][2][NP]
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const bool rec = wave < SC;
+    const int L = int(p.L), d_in = int(p.d_in), n = int(p.n);
+    const int bi = __builtin_amdgcn_readfirstlane(int(blockIdx.x) / p.nblk_d);
+    const int grp = __builtin_amdgcn_readfirstlane(int(blockIdx.x) - bi * p.nblk_d);
+    const int dbase = grp * 64;
+    const int nchunks = (L + T - 1) / T;
+    const int64_t brow = int64_t(bi) * L;
+
+    // Recurrence waves: lane = channel d, states n0 .. n0 + NSW.
+    const int d = dbase + lane;
+    const bool dv = d < d_in;
+    const int n0 = wave * NSW;
+    float A2[NSW], An[NSW], g[NSW], dA[NSW];
+#pragma unroll
+    for (int q = 0; q < NSW; q++) {
+        const bool ok = rec && dv && n0 + q < n;
+        A2[q] = ok ? a2_from_alog(p.A_log[int64_t(d) * n + n0 + q]) : 0.0f;
+        An[q] = A2[q] * kLn2;                                          // A itself
+        g[q] = (ok && p.dlast) ? p.dlast[(int64_t(bi) * d_in + d) * n + n0 + q] : 0.0f;
+        dA[q] = 0.0f;
+    }
+
+    // Element waves: thread owns step row er of a chunk, channels ech .. ech + V.
+    const int etid = rec ? 0 : tid - SC * 64;
+    const int er = etid / TPR;
+    const int ec = (etid - er * TPR) * V;
+    const int ech = dbase + ec;
+    const int evalid = rec ? 0 : max(0, min(V, d_in - ech));
+    float Dv[V], bias_v[V], accD[V], accBias[V];
+#pragma unroll
+    for (int i = 0; i < V; i++) {
+        Dv[i] = i < evalid ? p.D[ech + i] : 0.0f;
+        bias_v[i] = (i < evalid && p.bias) ? p.bias[ech + i] : 0.0f;
+        accD[i] = accBias[i] = 0.0f;
+    }
+
+    // Raw global values of one chunk as loaded by an element thread.
+    struct Raw {
+        float u[V], dl[V], z[V], dy[V];
+        float b[EBC], c[EBC];
+        float ck[ECK];
+    };
+    // Values an element thread keeps from preparing a chunk to finishing it.
+    struct Keep {
+        float x[V], z[V], dy[V];                   // delta + bias, z, dy
+    };
+    Raw raw[3];
+    Keep keep[3];
+
+    auto load_chunk = [&](Raw& r, int k) __attribute__((always_inline)) {         // issue the global loads of chunk k
+        const int t = k * T + er;
+        const bool rv = k >= 0 && t < L;
+#pragma unroll
+        for (int i = 0; i < V; i++) {
+            const bool ok = rv && i < evalid;
+            const int64_t e = (brow + t) * d_in + ech + i;
+            r.u[i] = ok ? Elem<TIn>::load(static_cast<const TIn*>(p.u), e) : 0.0f;
+            r.dl[i] = ok ? Elem<TIn>::load(static_cast<const TIn*>(p.delta), e) : 0.0f;
+            r.z[i] = (GATE && ok) ? Elem<TIn>::load(static_cast<const TIn*>(p.z), e) : 0.0f;
+            r.dy[i] = ok ? Elem<TIn>::load(static_cast<const TIn*>(p.dy), e) : 0.0f;
+        }
+#pragma unroll
+        for (int m = 0; m < EBC; m++) {
+            const int f = m * NE + etid;
+            const int j = f / NP, kk = f - (f / NP) * NP;
+            const bool ok = k >= 0 && f < T * NP && k * T + j < L && kk < n;
+            const int64_t e = (brow + k * T + j) * n + kk;
+            r.b[m] = ok ? Elem<TIn>::load(static_cast<const TIn*>(p.B), e) : 0.0f;
+            r.c[m] = ok ? Elem<TIn>::load(static_cast<const TIn*>(p.C), e) : 0.0f;
+        }
+#pragma unroll
+        for (int m = 0; m < ECK; m++) {
+            const int f = m * NE + etid;
+            const int kk = f / 64, l = f & 63;
+            const int dd = dbase + l;
+            const bool ok = k >= 0 && f < NP * 64 && kk < n && dd < d_in;
+            float v = 0.0f;
+            if (ok) {
+                if (k > 0)
+                    v = p.ckpt[((int64_t(bi) * p.nck + k - 1) * n + kk) * d_in + dd];
+                else if (p.h0)
+                    v = p.h0[(int64_t(bi) * d_in + dd) * n + kk];
+            }
+            r.ck[m] = v;
+        }
+    };
+    // Prepare chunk k from its raw values: LDS ring slots s3 (of 3) and s2 (of 2).
+    auto prepare = [&](const Raw& r, Keep& kp, int k, int s3, int s2) __attribute__((always_inline)) {
+        const int t = k * T + er;
+        const bool rv = t < L;
+#pragma unroll
+        for (int i = 0; i < V; i++) {
+            const bool ok = rv && i < evalid;
+            const float x = r.dl[i] + bias_v[i];
+            const float dl = ok ? (SP ? softplus(x) : x) : 0.0f;
+            const float dyp = GATE ? r.dy[i] * silu(r.z[i]) : r.dy[i];
+            s_prep[(s3 * T + er) * 64 + ec + i] = make_float4(dl, dl * r.u[i], ok ? dyp : 0.0f, r.u[i]);
+            kp.x[i] = x;
+            kp.z[i] = r.z[i];
+            kp.dy[i] = r.dy[i];
+        }
+#pragma unroll
+        for (int m = 0; m < EBC; m++) {
+            const int f = m * NE + etid;
+            if ((T * NP) % NE != 0 && f >= T * NP) break;
+            const int j = f / NP, kk = f - (f / NP) * NP;
+            float* dst = s_bc + s2 * (T * 2 * NP) + ((j * SC + kk / NSW) * 2) * NSW + kk % NSW;
+            dst[0] = r.b[m];
+            dst[NSW] = r.c[m];
+        }
+#pragma unroll
+        for (int m = 0; m < ECK; m++) {
+            const int f = m * NE + etid;
+            if ((NP * 64) % NE != 0 && f >= NP * 64) break;
+            s_ck[s2 * NP * 64 + f] = r.ck[m];
+        }
+    };
+    // Finish chunk k: sums of the recurrence waves' partials, the per-element
+    // gradients, and the chunk's dB, dC rows of this channel group.
+    auto finalize = [&](const Keep& kp, int k, int s3, int s2) __attribute__((always_inline)) {
+        const int t = k * T + er;
+        const bool rv = t < L;
+        const int64_t e0 = (brow + t) * d_in + ech;
+#pragma unroll
+        for (int i = 0; i < V; i++) {
+            const float4 pr = s_prep[(s3 * T + er) * 64 + ec + i];    // (Delta, w, dy', u)
+            float S1 = 0.0f, S2 = 0.0f, yp = 0.0f;
+#pragma unroll
+            for (int w = 0; w < SC; w++) {
+                const float2 q = s_part[((s2 * SC + w) * T + er) * 64 + ec + i];
+                S1 += q.x;
+                S2 += q.y;
+                if (GATE) yp += s_yp[((s2 * SC + w) * T + er) * 64 + ec + i];
+            }
+            const float dDelta = fmaf(pr.w, S1, S2);
+            const float ddl = SP ? dDelta * rcp_hw(1.0f + exp2_hw(-kp.x[i] * kLog2e)) : dDelta;
+            const float du = fmaf(pr.x, S1, pr.z * Dv[i]);
+            if (rv && i < evalid) {
+                Elem<TIn>::store(static_cast<TIn*>(p.du), e0 + i, du);
+                Elem<TIn>::store(static_cast<TIn*>(p.ddelta), e0 + i, ddl);
+                if (GATE) {
+                    const float ypre = fmaf(Dv[i], pr.w, yp);
+                    const float sg = rcp_hw(1.0f + exp2_hw(-kp.z[i] * kLog2e));
+                    const float dz = kp.dy[i] * ypre * sg * fmaf(kp.z[i], 1.0f - sg, 1.0f);
+                    Elem<TIn>::store(static_cast<TIn*>(p.dz), e0 + i, dz);
+                }
+                accD[i] = fmaf(pr.z, pr.w, accD[i]);
+                accBias[i] += ddl;
+            }
+        }
+        // dB, dC of the chunk's rows: T * n consecutive values of each.
+        const int64_t prow = (int64_t(grp) * p.b + bi) * L;
+        for (int f = etid; f < T * n; f += NE) {
+            const int j = f / n, kk = f - (f / n) * n;
+            if (k * T + j < L) {
+                const int64_t o = (prow + k * T + j) * n + kk;
+                p.part_B[o] = s_dbc[((s2 * T + j) * 2 + 0) * NP + kk];
+                p.part_C[o] = s_dbc[((s2 * T + j) * 2 + 1) * NP + kk];
+            }
+        }
+    };
+    // Recurrence waves, chunk c: recompute its states, then the adjoint back through them.
+    auto process = [&](int c, int s3, int s2) __attribute__((always_inline)) {
+        float hstart[NSW], h[NSW];
+#pragma unroll
+        for (int q = 0; q < NSW; q++) h[q] = hstart[q] = s_ck[(s2 * NP + n0 + q) * 64 + lane];
+        const float* bcw = s_bc + s2 * (T * 2 * NP) + wave * 2 * NSW;
+        float hs[T][NSW], as[T][NSW];
+#pragma unroll
+        for (int j = 0; j < T; j++) {
+            const float4 pr = s_prep[(s3 * T + j) * 64 + lane];
+            float acc = 0.0f;
+#pragma unroll
+            for (int q = 0; q < NSW; q++) {
+                const float a = exp2_hw(pr.x * A2[q]);
+                h[q] = fmaf(a, h[q], pr.y * bcw[j * SC * 2 * NSW + q]);
+                hs[j][q] = h[q];
+                as[j][q] = a;
+                acc = fmaf(bcw[j * SC * 2 * NSW + NSW + q], h[q], acc);
+            }
+            if (GATE) s_yp[((s2 * SC + wave) * T + j) * 64 + lane] = acc;
+        }
+#pragma unroll
+        for (int j = T - 1; j >= 0; j--) {
+            const float4 pr = s_prep[(s3 * T + j) * 64 + lane];
+            float S1 = 0.0f, S2 = 0.0f, dBv[NSW], dCv[NSW];
+#pragma unroll
+            for (int q = 0; q < NSW; q++) {
+                const float Bq = bcw[j * SC * 2 * NSW + q], Cq = bcw[j * SC * 2 * NSW + NSW + q];
+                g[q] = fmaf(pr.z, Cq, g[q]);
+                const float hp = j > 0 ? hs[j - 1][q] : hstart[q];
+                const float gah = g[q] * as[j][q] * hp;
+                S1 = fmaf(g[q], Bq, S1);
+                S2 = fmaf(gah, An[q], S2);
+                dA[q] = fmaf(gah, pr.x, dA[q]);
+                dBv[q] = g[q] * pr.y;
+                dCv[q] = pr.z * hs[j][q];
+                g[q] *= as[j][q];
+            }
+            s_part[((s2 * SC + wave) * T + j) * 64 + lane] = make_float2(S1, S2);
+#pragma unroll
+            for (int q = 0; q < NSW; q++) {
+                const float sB = wave_sum_last(dBv[q]);
+                const float sC = wave_sum_last(dCv[q]);
+                if (lane == 63) {
+                    s_dbc[((s2 * T + j) * 2 + 0) * NP + n0 + q] = sB;
+                    s_dbc[((s2 * T + j) * 2 + 1) * NP + n0 + q] = sC;
+                }
+            }
+        }
+    };
+
+    // (The lambdas are forced inline: called from three unrolled copies, the
+    // compiler would otherwise emit them as functions, with their arrays in
+    // scratch memory and LDS reached through generic pointers.)
+    // Iteration i: the recurrence waves take chunk c = nchunks - 1 - i; the
+    // element waves issue the loads of chunk c - 2, finish chunk c + 1 and
+    // prepare chunk c - 1.  Ring slots: LDS (Delta, w, dy', u) and the kept
+    // values by i % 3 (compile-time: the loops are unrolled by three), the raw
+    // loads by the iteration that issued them, the two-slot LDS rings by i & 1.
+    const int niter = (nchunks + 1 + 2) / 3 * 3;
+    using I0 = std::integral_constant<int, 0>;
+    using I1 = std::integral_constant<int, 1>;
+    using I2 = std::integral_constant<int, 2>;
+    if (!rec) {
+        load_chunk(raw[1], nchunks - 1);
+        prepare(raw[1], keep[0], nchunks - 1, 0, 0);
+        load_chunk(raw[2], nchunks - 2);
+    }
+    barrier_lds();
+    auto rec_iter = [&](auto ph, int i) __attribute__((always_inline)) {
+        constexpr int PH = decltype(ph)::value;
+        const int c = nchunks - 1 - i;
+        if (c >= 0) process(c, PH, i & 1);
+        barrier_lds();
+    };
+    auto elem_iter = [&](auto ph, int i) __attribute__((always_inline)) {
+        constexpr int PH = decltype(ph)::value;
+        const int c = nchunks - 1 - i;
+        load_chunk(raw[PH], c - 2);
+        if (c + 1 >= 0 && c + 1 < nchunks) finalize(keep[(PH + 2) % 3], c + 1, (PH + 2) % 3, (i + 1) & 1);
+        if (c - 1 >= 0) prepare(raw[(PH + 2) % 3], keep[(PH + 1) % 3], c - 1, (PH + 1) % 3, (i + 1) & 1);
+        barrier_lds();
+    };
+    if (rec) {
+        for (int i = 0; i < niter; i += 3) {
+            rec_iter(I0{}, i);
+            rec_iter(I1{}, i + 1);
+            rec_iter(I2{}, i + 2);
+        }
+    } else {
+        for (int i = 0; i < niter; i += 3) {
+            elem_iter(I0{}, i);
+            elem_iter(I1{}, i + 1);
+            elem_iter(I2{}, i + 2);
+        }
+    }
+
+    if (rec) {
+        if (dv) {
+#pragma unroll
+            for (int q = 0; q < NSW; q++) {
+                if (n0 + q >= n) continue;
+                const int64_t o = (int64_t(bi) * d_in + d) * n + n0 + q;
+                p.part_A[o] = dA[q] * An[q];
+                if (p.dh0) p.dh0[o] = g[q];
+            }
+        }
+        barrier_lds();
+        barrier_lds();
+    } else {
+        // dD and dbias: sum the T step rows of each channel (fixed order).
+        float* s_red = reinterpret_cast<float*>(lds + Lds::off_prep);   // [T][64][2]
+#pragma unroll
+        for (int i = 0; i < V; i++) {
+            s_red[(er * 64 + ec + i) * 2] = accD[i];
+            s_red[(er * 64 + ec + i) * 2 + 1] = accBias[i];
+        }
+        barrier_lds();
+        if (etid < 64 && dbase + etid < d_in) {
+            float sD = 0.0f, sB = 0.0f;
+            for (int r = 0; r < T; r++) {
+                sD += s_red[(r * 64 + etid) * 2];
+                sB += s_red[(r * 64 + etid) * 2 + 1];
+            }
+            p.part_D[int64_t(bi) * d_in + dbase + etid] = sD;
+            p.part_bias[int64_t(bi) * d_in + dbase + etid] = sB;
+        }
+        barrier_lds();
+    }
+}
+
+// out[i] = scale_i * sum over g of part[g * count + i], added in the order
+// g = 0, 1, ...; scale_i = 1, written as TOut (fp32 or bf16 words).
+template <typename TOut>
+__global__ __launch_bounds__(256) void reduce_groups(const float* __restrict__ part, TOut* __restrict__ out,
+                                                     int64_t count, int groups) {
+    const int64_t i = blockIdx.x * int64_t(blockDim.x) + threadIdx.x;
+    if (i >= count) return;
+    float s = 0.0f;
+    for (int g = 0; g < groups; g++) s += part[int64_t(g) * count + i];
+    Elem<TOut>::store(out, i, s);
+}
+
+}  // namespace ss

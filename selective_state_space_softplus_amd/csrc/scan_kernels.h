@@ -55,6 +55,8 @@ struct ScanParams {
     void* y;
     float* last_state;
     const float* h0;     // (b, d_in, n) initial state, or null for zero (scan_seq)
+    float* ckpt;         // (b, nck, n, d_in) states after every kCkptSteps steps, or null (scan_seq)
+    int nck;             // checkpoints per batch row: (L - 1) / kCkptSteps
     int64_t b, L, d_in, n;
     int softplus;
     int cross_h, cross_w; // cross scan: map height and width (L = cross_h * cross_w)
@@ -67,6 +69,10 @@ struct ScanParams {
 };
 
 constexpr int kFlagOffset = 64;
+
+// Steps between the states the forward scan saves for the backward pass, and
+// the chunk length of the backward pass.
+constexpr int kCkptSteps = 8;
 constexpr int kSpinLimit = 1 << 25;   // ~2 s of s_sleep before a wait gives up and flags an error
 
 // Steps of (delta', delta' u) a recurrence wave reads from LDS ahead of the
@@ -231,6 +237,7 @@ __global__ __launch_bounds__((SC + kSeqElemWaves + 1) * 64) void scan_seq(const 
     static_assert(NSW % 2 == 0 && (T / 2) % RDW == 0 && T % RBC == 0 && PA + 1 <= RDW, "tiles split evenly");
     static_assert(!WIDE || (T * 64 * ES) % 1024 == 0, "whole loads per tile");
     static_assert(Lds::bytes <= 160 * 1024, "LDS of one workgroup");
+    static_assert(T % kCkptSteps == 0, "checkpoints fall at chunk-internal step boundaries");
     extern __shared__ __align__(16) float smem[];
     char* const lds = reinterpret_cast<char*>(smem);
     float* s_dw = reinterpret_cast<float*>(lds + Lds::off_dw);   // [3][T/2][64][4]: (delta'_j, w_j, delta'_j+1, w_j+1)
@@ -465,7 +472,7 @@ __global__ __launch_bounds__((SC + kSeqElemWaves + 1) * 64) void scan_seq(const 
         }
         const int valid = ev(k);
         TOut* yp = static_cast<TOut*>(p.y);
-        if (valid > 0)
+        if (valid > 0 && yp)
             store_span<TOut, V, WIDE>(yp + (brow + t_begin + int64_t(k) * T) * d_in, off_el, yv, valid);
     };
 
@@ -517,6 +524,9 @@ __global__ __launch_bounds__((SC + kSeqElemWaves + 1) * 64) void scan_seq(const 
 #pragma unroll
     for (int q = 0; q < NSW; q++)
         invA[q] = (ZOH && rec && dv && n0 + q < n) ? inv_a_from_alog(p.A_log[(prow + d) * n + n0 + q]) : 0.0f;
+    // Checkpoints for the backward pass: state n0 of channel dbase in checkpoint 0 (wave-uniform).
+    float* const ck0 = p.ckpt ? p.ckpt + (int64_t(bi) * p.nck * n + n0) * d_in + dbase : nullptr;
+    const int64_t ck_stride = int64_t(n) * d_in;   // floats between consecutive checkpoints
     auto rec_chunk = [&](auto ph, int c) {
         constexpr int PH = decltype(ph)::value;
         constexpr int K0 = PH, K1 = (PH + 1) % 3;    // ring slots of chunks c, c+1
@@ -566,6 +576,17 @@ __global__ __launch_bounds__((SC + kSeqElemWaves + 1) * 64) void scan_seq(const 
                 ypw[j * 64] = acc;
             } else {
                 ylast = acc;
+            }
+            if (j % kCkptSteps == kCkptSteps - 1 && ck0) {
+                // The state after step t + 1 = kCkptSteps (i + 1), for the backward pass;
+                // only for steps of this segment (past its end the state is not its own).
+                const int t = t_begin + c * T + j;
+                if (t < t_end && t + 1 < L && dv) {
+                    float* dst = ck0 + int64_t((t + 1) / kCkptSteps - 1) * ck_stride + lane;
+#pragma unroll
+                    for (int q = 0; q < NSW; q++)
+                        if (n0 + q < n) dst[int64_t(q) * d_in] = h[q];
+                }
             }
         }
         barrier_lds();

@@ -15,6 +15,7 @@
 
 #include "ss_scan.h"
 #include "conv_kernels.h"
+#include "scan_bwd_kernels.h"
 #include "scan_kernels.h"
 #include "state_update_kernels.h"
 
@@ -603,4 +604,207 @@ SS_EXPORT int ss_cross_scan_fwd(const void* x, const void* delta, const float* A
     else
         hipLaunchKernelGGL((ss::cross_merge<1>), grid, dim3(256), 0, st, ys, y, maps, int(H), int(W), d_in);
     return hipGetLastError() == hipSuccess ? SS_OK : SS_ERR_HIP;
+}
+
+// ============================================================================= backward
+
+namespace {
+
+using ss::BwdParams;
+
+// Recurrence waves and states per wave of scan_bwd (n <= 32).
+SeqShape bwd_shape(int64_t n) {
+    if (n <= 2) return {1, 2};
+    if (n <= 8) return {4, 2};
+    if (n <= 16) return {8, 2};
+    return {8, 4};
+}
+
+// Workspace of ss_scan_bwd, in order: the forward's checkpoints, the dB and dC
+// partials per channel group, the dA_log, dD and dbias partials per batch
+// row, then the forward scan's own workspace.
+struct BwdWorkspace {
+    size_t ckpt, part_B, part_C, part_A, part_D, part_bias, fwd, total;
+};
+
+size_t round256(size_t x) { return (x + 255) / 256 * 256; }
+
+BwdWorkspace bwd_workspace(int64_t b, int64_t L, int64_t d_in, int64_t n) {
+    const int64_t nck = (L - 1) / ss::kCkptSteps;
+    const int64_t nblk = (d_in + 63) / 64;
+    BwdWorkspace w;
+    w.ckpt = round256(size_t(b) * size_t(nck) * size_t(n) * size_t(d_in) * 4);
+    w.part_B = w.part_C = round256(size_t(nblk) * size_t(b) * size_t(L) * size_t(n) * 4);
+    w.part_A = round256(size_t(b) * size_t(d_in) * size_t(n) * 4);
+    w.part_D = w.part_bias = round256(size_t(b) * size_t(d_in) * 4);
+    w.fwd = seq_workspace(b, L, d_in, n).total;
+    w.total = w.ckpt + w.part_B + w.part_C + w.part_A + w.part_D + w.part_bias + w.fwd;
+    return w;
+}
+
+template <typename TIn, int SC, int NSW>
+int launch_bwd(const BwdParams& p, bool gate, hipStream_t st) {
+    constexpr int threads = (SC + 4) * 64;
+    using Kern = void (*)(BwdParams);
+    static constexpr Kern kernels[4] = {ss::scan_bwd<TIn, SC, NSW, false, false>, ss::scan_bwd<TIn, SC, NSW, false, true>,
+                                        ss::scan_bwd<TIn, SC, NSW, true, false>, ss::scan_bwd<TIn, SC, NSW, true, true>};
+    const Kern kern = kernels[(p.softplus ? 2 : 0) | (gate ? 1 : 0)];
+    const size_t lds = gate ? ss::BwdLds<SC, SC * NSW, true>::bytes : ss::BwdLds<SC, SC * NSW, false>::bytes;
+    hipLaunchKernelGGL(kern, dim3(unsigned(p.b * p.nblk_d)), dim3(threads), lds, st, p);
+    return hipGetLastError() == hipSuccess ? SS_OK : SS_ERR_HIP;
+}
+
+template <typename TIn>
+int dispatch_bwd(const BwdParams& p, bool gate, hipStream_t st) {
+    const SeqShape sh = bwd_shape(p.n);
+    if (sh.SC == 1) return launch_bwd<TIn, 1, 2>(p, gate, st);
+    if (sh.SC == 4) return launch_bwd<TIn, 4, 2>(p, gate, st);
+    if (sh.NSW == 2) return launch_bwd<TIn, 8, 2>(p, gate, st);
+    return launch_bwd<TIn, 8, 4>(p, gate, st);
+}
+
+template <typename TOut>
+int reduce(const float* part, void* out, int64_t count, int64_t groups, hipStream_t st) {
+    hipLaunchKernelGGL((ss::reduce_groups<TOut>), dim3(unsigned((count + 255) / 256)), dim3(256), 0, st, part,
+                       static_cast<TOut*>(out), count, int(groups));
+    return hipGetLastError() == hipSuccess ? SS_OK : SS_ERR_HIP;
+}
+
+}  // namespace
+
+SS_EXPORT size_t ss_scan_bwd_workspace_bytes(int64_t b, int64_t L, int64_t d_in, int64_t n, int dtype) {
+    if (dtype != SS_F32 && dtype != SS_BF16) return 0;
+    if (!sizes_ok(b, L, d_in) || n <= 0 || n > SS_MAX_BWD_STATE || d_in > SS_MAX_CHANNELS) return 0;
+    if (b * ((d_in + 63) / 64) > kMaxWorkgroups || L > kMaxLength) return 0;
+    return bwd_workspace(b, L, d_in, n).total;
+}
+
+SS_EXPORT int ss_scan_bwd(const void* u, const void* delta, const float* A_log, const void* B, const void* C,
+                          const float* D, const void* z, const float* delta_bias, int delta_softplus,
+                          const float* initial_state, const void* dy, const float* dlast_state, void* du,
+                          void* ddelta, float* dA_log, void* dB, void* dC, float* dD, void* dz, float* ddelta_bias,
+                          float* dinitial_state, int64_t b, int64_t L, int64_t d_in, int64_t n, int dtype,
+                          void* workspace, size_t workspace_bytes, void* stream) {
+    if (!u || !delta || !A_log || !B || !C || !D || !dy || !du || !ddelta || !dA_log || !dB || !dC || !dD)
+        return SS_ERR_NULL;
+    if (z && !dz) return SS_ERR_NULL;
+    if (!sizes_ok(b, L, d_in) || n <= 0 || d_in > SS_MAX_CHANNELS) return SS_ERR_SHAPE;
+    if (dtype != SS_F32 && dtype != SS_BF16) return SS_ERR_DTYPE;
+    if (n > SS_MAX_BWD_STATE) return SS_ERR_UNSUPPORTED;
+    if (b * ((d_in + 63) / 64) > kMaxWorkgroups || L > kMaxLength) return SS_ERR_SHAPE;
+    const size_t es = elem_size(dtype);
+    for (const void* p : {u, delta, B, C, z, dy, static_cast<const void*>(du), static_cast<const void*>(ddelta),
+                          static_cast<const void*>(dB), static_cast<const void*>(dC), static_cast<const void*>(dz)})
+        if (p && !aligned(p, es)) return SS_ERR_ALIGN;
+    for (const void* p : {static_cast<const void*>(A_log), static_cast<const void*>(D),
+                          static_cast<const void*>(delta_bias), static_cast<const void*>(initial_state),
+                          static_cast<const void*>(dlast_state), static_cast<const void*>(dA_log),
+                          static_cast<const void*>(dD), static_cast<const void*>(ddelta_bias),
+                          static_cast<const void*>(dinitial_state)})
+        if (p && !aligned(p, 4)) return SS_ERR_ALIGN;
+    if (!aligned(workspace, 256)) return workspace ? SS_ERR_ALIGN : SS_ERR_WORKSPACE;
+    const int64_t nel = b * L * d_in, nst = b * d_in * n;
+    const Range ins[] = {range_of(u, nel, es), range_of(delta, nel, es), range_of(A_log, d_in * n, 4),
+                         range_of(B, b * L * n, es), range_of(C, b * L * n, es), range_of(D, d_in, 4),
+                         range_of(z, z ? nel : 0, es), range_of(delta_bias, delta_bias ? d_in : 0, 4),
+                         range_of(initial_state, initial_state ? nst : 0, 4), range_of(dy, nel, es),
+                         range_of(dlast_state, dlast_state ? nst : 0, 4)};
+    const Range outs[] = {range_of(du, nel, es), range_of(ddelta, nel, es), range_of(dA_log, d_in * n, 4),
+                          range_of(dB, b * L * n, es), range_of(dC, b * L * n, es), range_of(dD, d_in, 4),
+                          range_of(dz, z ? nel : 0, es), range_of(ddelta_bias, ddelta_bias ? d_in : 0, 4),
+                          range_of(dinitial_state, dinitial_state ? nst : 0, 4)};
+    const size_t need = ss_scan_bwd_workspace_bytes(b, L, d_in, n, dtype);
+    if (!workspace || workspace_bytes < need) return SS_ERR_WORKSPACE;
+    const Range rw = range_of(workspace, int64_t(workspace_bytes), 1);
+    for (size_t i = 0; i < sizeof(outs) / sizeof(outs[0]); i++) {
+        for (const Range& r : ins)
+            if (overlaps(r, outs[i])) return SS_ERR_ALIAS;
+        for (size_t j = i + 1; j < sizeof(outs) / sizeof(outs[0]); j++)
+            if (overlaps(outs[i], outs[j])) return SS_ERR_ALIAS;
+        if (overlaps(outs[i], rw)) return SS_ERR_ALIAS;
+    }
+    for (const Range& r : ins)
+        if (overlaps(r, rw)) return SS_ERR_ALIAS;
+
+    const BwdWorkspace w = bwd_workspace(b, L, d_in, n);
+    char* base = static_cast<char*>(workspace);
+    float* ckpt = reinterpret_cast<float*>(base);
+    float* part_B = reinterpret_cast<float*>(base + w.ckpt);
+    float* part_C = reinterpret_cast<float*>(base + w.ckpt + w.part_B);
+    float* part_A = reinterpret_cast<float*>(base + w.ckpt + w.part_B + w.part_C);
+    float* part_D = reinterpret_cast<float*>(base + w.ckpt + w.part_B + w.part_C + w.part_A);
+    float* part_bias = reinterpret_cast<float*>(base + w.ckpt + w.part_B + w.part_C + w.part_A + w.part_D);
+    void* fwd_ws = base + w.total - w.fwd;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    const int nblk = int((d_in + 63) / 64);
+
+    // 1. The forward scan again, saving the state every kCkptSteps steps (no y).
+    ScanParams f{};
+    f.u = u;
+    f.delta = delta;
+    f.A_log = A_log;
+    f.B = B;
+    f.C = C;
+    f.D = D;
+    f.z = z;
+    f.bias = delta_bias;
+    f.y = nullptr;
+    f.last_state = nullptr;
+    f.h0 = initial_state;
+    f.ckpt = ckpt;
+    f.nck = int((L - 1) / ss::kCkptSteps);
+    f.b = b;
+    f.L = L;
+    f.d_in = d_in;
+    f.n = n;
+    f.softplus = delta_softplus ? 1 : 0;
+    f.nblk_d = nblk;
+    f.K = 1;
+    f.Lseg = L;
+    int rc = dtype == SS_BF16 ? dispatch_seq<uint16_t>(f, SeqMode::Euler, fwd_ws, w.fwd, st)
+                              : dispatch_seq<float>(f, SeqMode::Euler, fwd_ws, w.fwd, st);
+    if (rc != SS_OK) return rc;
+
+    // 2. Backward through every chunk.
+    BwdParams p{};
+    p.u = u;
+    p.delta = delta;
+    p.A_log = A_log;
+    p.B = B;
+    p.C = C;
+    p.D = D;
+    p.z = z;
+    p.bias = delta_bias;
+    p.h0 = initial_state;
+    p.dy = dy;
+    p.dlast = dlast_state;
+    p.ckpt = ckpt;
+    p.du = du;
+    p.ddelta = ddelta;
+    p.dz = z ? dz : nullptr;
+    p.dh0 = dinitial_state;
+    p.part_B = part_B;
+    p.part_C = part_C;
+    p.part_A = part_A;
+    p.part_D = part_D;
+    p.part_bias = part_bias;
+    p.b = b;
+    p.L = L;
+    p.d_in = d_in;
+    p.n = n;
+    p.nck = f.nck;
+    p.nblk_d = nblk;
+    p.softplus = f.softplus;
+    rc = dtype == SS_BF16 ? dispatch_bwd<uint16_t>(p, z != nullptr, st) : dispatch_bwd<float>(p, z != nullptr, st);
+    if (rc != SS_OK) return rc;
+
+    // 3. Sums over channel groups (dB, dC) and batch rows (dA_log, dD, dbias), in a fixed order.
+    const int64_t nbc = b * L * n;
+    rc = dtype == SS_BF16 ? reduce<uint16_t>(part_B, dB, nbc, nblk, st) : reduce<float>(part_B, dB, nbc, nblk, st);
+    if (rc == SS_OK)
+        rc = dtype == SS_BF16 ? reduce<uint16_t>(part_C, dC, nbc, nblk, st) : reduce<float>(part_C, dC, nbc, nblk, st);
+    if (rc == SS_OK) rc = reduce<float>(part_A, dA_log, d_in * n, b, st);
+    if (rc == SS_OK) rc = reduce<float>(part_D, dD, d_in, b, st);
+    if (rc == SS_OK && ddelta_bias && delta_bias) rc = reduce<float>(part_bias, ddelta_bias, d_in, b, st);
+    return rc;
 }

@@ -29,7 +29,7 @@ def declared_functions():
 
 def test_header_declares_the_entry_points():
     assert declared_functions() == sorted(["ss_conv_update", "ss_cross_scan_fwd", "ss_cross_scan_fwd_workspace_bytes",
-                                           "ss_scan_fwd", "ss_scan_fwd_ex",
+                                           "ss_scan_bwd", "ss_scan_bwd_workspace_bytes", "ss_scan_fwd", "ss_scan_fwd_ex",
                                            "ss_scan_fwd_workspace_bytes", "ss_state_update", "ss_state_update_ex",
                                            "ss_status_string"])
 
@@ -266,3 +266,41 @@ def test_cross_workspace_query(ss):
     assert full == q(16, 56, 56, 384, 1, 1)
     for bad in ((0, 5, 5, 8, 1, 0), (1, 0, 5, 8, 1, 0), (1, 5, 5, 8, 65, 0), (1, 5, 5, 8, 1, 2)):
         assert q(*bad) == 0, bad
+
+
+def bwd_args(**over):
+    a = dict(u=addr(1), delta=addr(2), A_log=addr(3), B=addr(4), C=addr(5), D=addr(6), z=addr(7), bias=addr(8),
+             softplus=1, h0=addr(9), dy=addr(10), dlast=addr(11), du=addr(12), ddelta=addr(13), dA=addr(14),
+             dB=addr(15), dC=addr(16), dD=addr(17), dz=addr(18), dbias=addr(19), dh0=addr(20), b=2, L=64, d_in=32,
+             n=16, dtype=1, ws=addr(21), ws_bytes=1 << 30, stream=None)
+    a.update(over)
+    return a
+
+
+def call_bwd(ss, a):
+    k = ("u", "delta", "A_log", "B", "C", "D", "z", "bias", "softplus", "h0", "dy", "dlast", "du", "ddelta", "dA",
+         "dB", "dC", "dD", "dz", "dbias", "dh0", "b", "L", "d_in", "n", "dtype", "ws", "ws_bytes", "stream")
+    return ss.lib.ss_scan_bwd(*[a[x] for x in k])
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(u=None), NULL), (dict(dy=None), NULL), (dict(du=None), NULL), (dict(dA=None), NULL), (dict(dC=None), NULL),
+    (dict(dz=None), NULL), (dict(b=0), SHAPE), (dict(L=-1), SHAPE), (dict(n=0), SHAPE), (dict(dtype=2), DTYPE),
+    (dict(n=33), UNSUP), (dict(ws=None), WS), (dict(ws_bytes=100), WS), (dict(ws=addr(21) + 128), ALIGN),
+    (dict(du=addr(12) + 1), ALIGN), (dict(dA=addr(14) + 2), ALIGN), (dict(dh0=addr(20) + 1), ALIGN),
+    (dict(du=addr(1)), ALIAS), (dict(dB=addr(12)), ALIAS), (dict(dA=addr(3)), ALIAS), (dict(dh0=addr(9)), ALIAS),
+    (dict(ws=addr(12)), ALIAS), (dict(dD=addr(19) - 8), ALIAS), (dict(dz=addr(21)), ALIAS),
+])
+def test_bwd_rejects(ss, over, code):
+    assert call_bwd(ss, bwd_args(**over)) == code
+
+
+def test_bwd_optional_pointers_may_be_null(ss):
+    # No gate (then dz may be NULL), no bias, no h0, no dlast, no dh0: only the dtype error remains.
+    assert call_bwd(ss, bwd_args(z=None, dz=None, bias=None, dbias=None, h0=None, dlast=None, dh0=None, dtype=7)) == DTYPE
+
+
+def test_bwd_workspace_query(ss):
+    q = ss.lib.ss_scan_bwd_workspace_bytes
+    assert q(4, 8192, 5120, 16, 1) > 4 * 1023 * 16 * 5120 * 4
+    assert q(4, 8192, 5120, 33, 1) == 0 and q(0, 1, 1, 1, 0) == 0 and q(1, 1, 1, 1, 3) == 0
