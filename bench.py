@@ -69,10 +69,15 @@ def cross_bytes(maps, L, d, n, s, bias=False):
     return s * (maps * L * d + 4 * maps * L * d + 8 * maps * L * n) + 4 * maps * L * d + 4 * (4 * d * n + 4 * d * (2 if bias else 1))
 
 
+# Sources of the forward scan kernel (scan_seq) and its launch: the measured
+# traffic in profiles/traffic.json is used only while these are unchanged.
+SCAN_KERNEL_SOURCES = ("scan_kernels.h", "ss_device.h", "ss_scan.hip")
+
+
 def kernel_source_hash() -> str:
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "selective_state_space_softplus_amd", "csrc")
-    for name in sorted(os.listdir(csrc)):
+    for name in SCAN_KERNEL_SOURCES:
         with open(os.path.join(csrc, name), "rb") as f:
             h.update(name.encode() + f.read())
     return h.hexdigest()[:16]
@@ -149,6 +154,7 @@ def main(argv=None):
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-decode", action="store_true", help="skip the decode-step measurement")
     ap.add_argument("--no-cross", action="store_true", help="skip the VMamba cross-scan measurement")
+    ap.add_argument("--no-bwd", action="store_true", help="skip the backward-pass measurement")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target duration of the CPU baseline sample")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy (calibrates the HBM byte counters)")
@@ -304,6 +310,36 @@ def main(argv=None):
             "us_per_step_graph": round(cms_g * 1e3, 2),
             "GBps_graph": round(cbytes / (cms_g * 1e-3) / 1e9, 1),
             "algorithmic_bytes_per_step": cbytes,
+        }
+
+    if not args.no_bwd:
+        # The gradient of the same scan-long scan (ss_scan_bwd: the forward
+        # again with state checkpoints every 8 steps, the adjoint pass, the
+        # fixed-order sums), for an output gradient dy of y's shape.
+        dyb = torch.randn(g["u"].shape, device=dev, generator=torch.Generator(device=dev).manual_seed(5)).to(g["u"].dtype)
+        bws = torch.empty(ss.lib.ss_scan_bwd_workspace_bytes(cfg.b, cfg.L, cfg.d_in, cfg.n, 1), dtype=torch.uint8,
+                          device=dev)
+
+        def bwd():
+            ss.scan_bwd(g["u"], g["delta"], g["A_log"], g["B"], g["C"], g["D"], dyb, g["z"], g["delta_bias"], True,
+                        workspace=bws)
+
+        for _ in range(2):
+            bwd()
+        torch.cuda.synchronize()
+        b0, b1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        b0.record()
+        for _ in range(5):
+            bwd()
+        b1.record()
+        torch.cuda.synchronize()
+        bms = b0.elapsed_time(b1) / 5
+        result["backward"] = {
+            "workload": f"{cfg.name}: gradient of the scan above for a given dy (du, ddelta, dz, dA_log, dB, dC, dD, "
+                        "dbias), forward recomputed inside with state checkpoints every 8 steps",
+            "ms": round(bms, 4),
+            "updates_per_s": float(f"{cfg.updates / (bms * 1e-3):.4g}"),
+            "vs_forward": round(bms / ms_step, 2),
         }
 
     if not args.no_cross:
