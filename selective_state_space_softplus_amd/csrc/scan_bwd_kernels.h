@@ -14,8 +14,11 @@
 //     dA_log_k = sum_(b,t) g_tk Delta_t a_tk h_(t-1)k A_k,   dD = sum dy' u,   dbias = sum ddelta
 //     dh0_k    = a_0k g_0k
 //
-// scan_bwd<TIn, SC, NSW, SP, GATE>: one workgroup per (b, 64-channel group)
-// walks L backwards in chunks of kCkptSteps = 8 steps.  The forward pass
+// scan_bwd<TIn, SC, NSW, SP, GATE>: one workgroup per (b, 64-channel group,
+// segment of L) walks its segment backwards in chunks of kCkptSteps = 8
+// steps; segments are taken last first, each starting from the adjoint the
+// later one handed on (as the forward hands on states), which balances the
+// workgroups over the compute units.  The forward pass
 // saved the state every 8 steps; the SC recurrence waves (NSW states of the
 // 64 channels each) reload the state entering the chunk, run the chunk's 8
 // steps forward again keeping every h and decay in registers, then run the
@@ -24,7 +27,7 @@
 // their global loads are issued one chunk earlier still), and finish the
 // previous one (sums of the waves' S1, S2 and readout partials, du, ddelta,
 // dz, and the chunk's dB, dC rows).  Sums over the 64 channels (dB, dC) are
-// DPP reductions inside each recurrence wave; sums over the channel groups,
+// cross-lane reductions inside each recurrence wave; sums over the channel groups,
 // batch rows and time (dB, dC, dA_log, dD, dbias) go through per-workgroup
 // partials that reduce_groups adds in a fixed order, so every gradient is
 // the same bit for bit on every run.
@@ -56,32 +59,47 @@ struct BwdParams {
     float* dh0;               // null unless asked
     float* part_B;            // (nblk_d, b, L, n) dB per channel group
     float* part_C;            // (nblk_d, b, L, n)
-    float* part_A;            // (b, d_in, n) dA_log per batch row
-    float* part_D;            // (b, d_in)
-    float* part_bias;         // (b, d_in)
+    float* part_A;            // (K, b, d_in, n) dA_log per segment and batch row
+    float* part_D;            // (K, b, d_in)
+    float* part_bias;         // (K, b, d_in)
     int64_t b, L, d_in, n;
     int nck, nblk_d, softplus;
+    // L segments: pieces taken in ticket order, last segment first; a piece
+    // starts from the adjoint its successor segment handed on.
+    int K;
+    int64_t Lseg;             // steps per segment, a multiple of kCkptSteps
+    uint32_t* ctl;            // [0] ticket counter, [1] error word, [kFlagOffset + s G + g] flags
+    float* handoff;           // (K - 1, G, n, 64) adjoints handed between segments
 };
 
-// v moved from another lane by a DPP control (row_shr, row_bcast); lanes the
-// control leaves out, or whose row is not in ROW_MASK, read 0.
+// v moved from another lane of the same row by a DPP control (row_shr);
+// lanes the control leaves out, or whose row is not in ROW_MASK, read 0.
 template <int CTRL, int ROW_MASK>
 __device__ __forceinline__ float dpp_take(float v) {
     return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, ROW_MASK, 0xf, true));
 }
 
-// Sum of v over the 64 lanes of the wave, complete in lane 63: prefix sums
-// inside each row of 16 lanes (row_shr 1, 2, 4, 8), then lane 15 of rows 0
-// and 2 added into rows 1 and 3 (row_bcast:15), then lane 31 into rows 2 and
-// 3 (row_bcast:31).  Every lane of the wave must be active.
-__device__ __forceinline__ float wave_sum_last(float v) {
-    v += dpp_take<0x111, 0xf>(v);
-    v += dpp_take<0x112, 0xf>(v);
-    v += dpp_take<0x114, 0xf>(v);
-    v += dpp_take<0x118, 0xf>(v);
-    v += dpp_take<0x142, 0xa>(v);
-    v += dpp_take<0x143, 0xc>(v);
-    return v;
+// Sums over the 64 lanes of the wave of four values at once (a transposing
+// butterfly; every lane of the wave must be active):
+//   1. v_permlane32_swap pairs the lower halves of (v0, v1) and of (v2, v3):
+//      a = [v0_lo + v0_hi | v1_lo + v1_hi], b likewise for v2, v3;
+//   2. v_permlane16_swap pairs odd rows of a with even rows of b: t holds in
+//      its rows 0, 1, 2, 3 partial sums (over 4 lanes) of v0, v2, v1, v3;
+//   3. prefix sums inside each row of 16 lanes (DPP row_shr 1, 2, 4, 8).
+// Lanes 15, 31, 47, 63 then hold the sums of v0, v2, v1, v3 -- 10 VALU
+// instructions instead of 24 for four separate six-step reductions.
+__device__ __forceinline__ float wave_sum4(float v0, float v1, float v2, float v3) {
+    const auto x = __builtin_amdgcn_permlane32_swap(__float_as_uint(v0), __float_as_uint(v1), false, false);
+    const auto y = __builtin_amdgcn_permlane32_swap(__float_as_uint(v2), __float_as_uint(v3), false, false);
+    const float a = __uint_as_float(x[0]) + __uint_as_float(x[1]);
+    const float b = __uint_as_float(y[0]) + __uint_as_float(y[1]);
+    const auto z = __builtin_amdgcn_permlane16_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+    float t = __uint_as_float(z[0]) + __uint_as_float(z[1]);
+    t += dpp_take<0x111, 0xf>(t);
+    t += dpp_take<0x112, 0xf>(t);
+    t += dpp_take<0x114, 0xf>(t);
+    t += dpp_take<0x118, 0xf>(t);
+    return t;
 }
 
 // LDS of scan_bwd<SC recurrence waves, NP padded states>, T = 8 steps.
@@ -100,7 +118,8 @@ struct BwdLds {
     static constexpr int off_ck = off_yp + 2 * YP;            // [2]
     static constexpr int off_bc = off_ck + 2 * CK;            // [2]
     static constexpr int off_dbc = off_bc + 2 * BC;           // [2]
-    static constexpr int bytes = off_dbc + 2 * DBC;
+    static constexpr int off_ticket = off_dbc + 2 * DBC;      // ticket, timeout flag
+    static constexpr int bytes = off_ticket + 16;
 };
 
 template <typename TIn, int SC, int NSW, bool SP, bool GATE>
@@ -115,6 +134,7 @@ __global__ __launch_bounds__((SC + 4) * 64) void scan_bwd(const BwdParams p) {
     using Lds = BwdLds<SC, NP, GATE>;
     static_assert(Lds::bytes <= 160 * 1024, "LDS of one workgroup");
     static_assert(NE / TPR == T, "thread tiling of a chunk");
+    static_assert(NSW % 2 == 0, "states reduced two at a time");
     extern __shared__ __align__(16) float smem[];
     char* const lds = reinterpret_cast<char*>(smem);
     float4* s_prep = reinterpret_cast<float4*>(lds + Lds::off_prep);   // [3][T][64]
@@ -129,10 +149,29 @@ __global__ __launch_bounds__((SC + 4) * 64) void scan_bwd(const BwdParams p) {
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const bool rec = wave < SC;
     const int L = int(p.L), d_in = int(p.d_in), n = int(p.n);
-    const int bi = __builtin_amdgcn_readfirstlane(int(blockIdx.x) / p.nblk_d);
-    const int grp = __builtin_amdgcn_readfirstlane(int(blockIdx.x) - bi * p.nblk_d);
+    const int G = int(p.b) * p.nblk_d;
+    int& s_ticket = *reinterpret_cast<int*>(lds + Lds::off_ticket);
+    int ticket;
+    if (p.K == 1) {
+        ticket = blockIdx.x;
+    } else {
+        if (tid == 0) s_ticket = int(atomicAdd(p.ctl, 1u));
+        __syncthreads();
+        ticket = s_ticket;
+    }
+    ticket = __builtin_amdgcn_readfirstlane(ticket);
+    int seg = p.K - 1, gi = ticket;                // later segments take the earlier tickets
+    while (gi >= G) {                              // at most 16 rounds, uniform
+        gi -= G;
+        seg--;
+    }
+    const int bi = __builtin_amdgcn_readfirstlane(gi / p.nblk_d);
+    const int grp = __builtin_amdgcn_readfirstlane(gi - bi * p.nblk_d);
     const int dbase = grp * 64;
-    const int nchunks = (L + T - 1) / T;
+    const int t_begin = seg * int(p.Lseg);
+    const int t_end = min(L, t_begin + int(p.Lseg));
+    const int kc0 = t_begin / T;                   // first and last chunk of this segment
+    const int kcl = (t_end + T - 1) / T - 1;
     const int64_t brow = int64_t(bi) * L;
 
     // Recurrence waves: lane = channel d, states n0 .. n0 + NSW.
@@ -145,8 +184,38 @@ __global__ __launch_bounds__((SC + 4) * 64) void scan_bwd(const BwdParams p) {
         const bool ok = rec && dv && n0 + q < n;
         A2[q] = ok ? a2_from_alog(p.A_log[int64_t(d) * n + n0 + q]) : 0.0f;
         An[q] = A2[q] * kLn2;                                          // A itself
-        g[q] = (ok && p.dlast) ? p.dlast[(int64_t(bi) * d_in + d) * n + n0 + q] : 0.0f;
+        g[q] = (ok && p.dlast && seg == p.K - 1) ? p.dlast[(int64_t(bi) * d_in + d) * n + n0 + q] : 0.0f;
         dA[q] = 0.0f;
+    }
+    if (seg < p.K - 1) {
+        // Wait for the adjoint of the later segment of these channels (it holds
+        // an earlier ticket, so the wait cannot deadlock; on a timeout the error
+        // word is set and this piece goes on from NaN, so its outputs show it).
+        int& s_timeout = *(reinterpret_cast<int*>(lds + Lds::off_ticket) + 1);
+        if (tid == 0) {
+            uint32_t* flag = p.ctl + kFlagOffset + seg * G + gi;
+            int spins = 0, timed_out = 0;
+            while (__hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0u) {
+                __builtin_amdgcn_s_sleep(2);
+                if (++spins > kSpinLimit) {
+                    atomicOr(p.ctl + 1, 1u);
+                    timed_out = 1;
+                    break;
+                }
+            }
+            s_timeout = timed_out;
+        }
+        __syncthreads();
+        const bool timed_out = __builtin_amdgcn_readfirstlane(s_timeout) != 0;
+        if (rec) {
+            const uint32_t* src = reinterpret_cast<const uint32_t*>(p.handoff) + (int64_t(seg) * G + gi) * n * 64;
+#pragma unroll
+            for (int q = 0; q < NSW; q++)
+                if (n0 + q < n)
+                    g[q] = timed_out ? __builtin_nanf("")
+                                     : __uint_as_float(__hip_atomic_load(src + (n0 + q) * 64 + lane,
+                                                                         __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+        }
     }
 
     // Element waves: thread owns step row er of a chunk, channels ech .. ech + V.
@@ -178,7 +247,7 @@ __global__ __launch_bounds__((SC + 4) * 64) void scan_bwd(const BwdParams p) {
 
     auto load_chunk = [&](Raw& r, int k) __attribute__((always_inline)) {         // issue the global loads of chunk k
         const int t = k * T + er;
-        const bool rv = k >= 0 && t < L;
+        const bool rv = k >= kc0 && t < L;
 #pragma unroll
         for (int i = 0; i < V; i++) {
             const bool ok = rv && i < evalid;
@@ -192,7 +261,7 @@ __global__ __launch_bounds__((SC + 4) * 64) void scan_bwd(const BwdParams p) {
         for (int m = 0; m < EBC; m++) {
             const int f = m * NE + etid;
             const int j = f / NP, kk = f - (f / NP) * NP;
-            const bool ok = k >= 0 && f < T * NP && k * T + j < L && kk < n;
+            const bool ok = k >= kc0 && f < T * NP && k * T + j < L && kk < n;
             const int64_t e = (brow + k * T + j) * n + kk;
             r.b[m] = ok ? Elem<TIn>::load(static_cast<const TIn*>(p.B), e) : 0.0f;
             r.c[m] = ok ? Elem<TIn>::load(static_cast<const TIn*>(p.C), e) : 0.0f;
@@ -202,7 +271,7 @@ __global__ __launch_bounds__((SC + 4) * 64) void scan_bwd(const BwdParams p) {
             const int f = m * NE + etid;
             const int kk = f / 64, l = f & 63;
             const int dd = dbase + l;
-            const bool ok = k >= 0 && f < NP * 64 && kk < n && dd < d_in;
+            const bool ok = k >= kc0 && f < NP * 64 && kk < n && dd < d_in;
             float v = 0.0f;
             if (ok) {
                 if (k > 0)
@@ -327,13 +396,14 @@ __global__ __launch_bounds__((SC + 4) * 64) void scan_bwd(const BwdParams p) {
                 g[q] *= as[j][q];
             }
             s_part[((s2 * SC + wave) * T + j) * 64 + lane] = make_float2(S1, S2);
+            // dB, dC of this step summed over the 64 channels, two states at a time:
+            // lane 15 holds dB[q], 31 dC[q], 47 dB[q + 1], 63 dC[q + 1].
 #pragma unroll
-            for (int q = 0; q < NSW; q++) {
-                const float sB = wave_sum_last(dBv[q]);
-                const float sC = wave_sum_last(dCv[q]);
-                if (lane == 63) {
-                    s_dbc[((s2 * T + j) * 2 + 0) * NP + n0 + q] = sB;
-                    s_dbc[((s2 * T + j) * 2 + 1) * NP + n0 + q] = sC;
+            for (int q = 0; q < NSW; q += 2) {
+                const float sum = wave_sum4(dBv[q], dBv[q + 1], dCv[q], dCv[q + 1]);
+                if ((lane & 15) == 15) {
+                    const int r = lane >> 4;
+                    s_dbc[((s2 * T + j) * 2 + (r & 1)) * NP + n0 + q + (r >> 1)] = sum;
                 }
             }
         }
@@ -342,33 +412,33 @@ __global__ __launch_bounds__((SC + 4) * 64) void scan_bwd(const BwdParams p) {
     // (The lambdas are forced inline: called from three unrolled copies, the
     // compiler would otherwise emit them as functions, with their arrays in
     // scratch memory and LDS reached through generic pointers.)
-    // Iteration i: the recurrence waves take chunk c = nchunks - 1 - i; the
+    // Iteration i: the recurrence waves take chunk c = kcl - i; the
     // element waves issue the loads of chunk c - 2, finish chunk c + 1 and
     // prepare chunk c - 1.  Ring slots: LDS (Delta, w, dy', u) and the kept
     // values by i % 3 (compile-time: the loops are unrolled by three), the raw
     // loads by the iteration that issued them, the two-slot LDS rings by i & 1.
-    const int niter = (nchunks + 1 + 2) / 3 * 3;
+    const int niter = (kcl - kc0 + 2 + 2) / 3 * 3;
     using I0 = std::integral_constant<int, 0>;
     using I1 = std::integral_constant<int, 1>;
     using I2 = std::integral_constant<int, 2>;
     if (!rec) {
-        load_chunk(raw[1], nchunks - 1);
-        prepare(raw[1], keep[0], nchunks - 1, 0, 0);
-        load_chunk(raw[2], nchunks - 2);
+        load_chunk(raw[1], kcl);
+        prepare(raw[1], keep[0], kcl, 0, 0);
+        load_chunk(raw[2], kcl - 1);
     }
     barrier_lds();
     auto rec_iter = [&](auto ph, int i) __attribute__((always_inline)) {
         constexpr int PH = decltype(ph)::value;
-        const int c = nchunks - 1 - i;
-        if (c >= 0) process(c, PH, i & 1);
+        const int c = kcl - i;
+        if (c >= kc0) process(c, PH, i & 1);
         barrier_lds();
     };
     auto elem_iter = [&](auto ph, int i) __attribute__((always_inline)) {
         constexpr int PH = decltype(ph)::value;
-        const int c = nchunks - 1 - i;
+        const int c = kcl - i;
         load_chunk(raw[PH], c - 2);
-        if (c + 1 >= 0 && c + 1 < nchunks) finalize(keep[(PH + 2) % 3], c + 1, (PH + 2) % 3, (i + 1) & 1);
-        if (c - 1 >= 0) prepare(raw[(PH + 2) % 3], keep[(PH + 1) % 3], c - 1, (PH + 1) % 3, (i + 1) & 1);
+        if (c + 1 >= kc0 && c + 1 <= kcl) finalize(keep[(PH + 2) % 3], c + 1, (PH + 2) % 3, (i + 1) & 1);
+        if (c - 1 >= kc0) prepare(raw[(PH + 2) % 3], keep[(PH + 1) % 3], c - 1, (PH + 1) % 3, (i + 1) & 1);
         barrier_lds();
     };
     if (rec) {
@@ -385,15 +455,24 @@ __global__ __launch_bounds__((SC + 4) * 64) void scan_bwd(const BwdParams p) {
         }
     }
 
+    const int64_t pb = int64_t(seg) * p.b + bi;    // partials of this segment and batch row
     if (rec) {
         if (dv) {
 #pragma unroll
             for (int q = 0; q < NSW; q++) {
                 if (n0 + q >= n) continue;
-                const int64_t o = (int64_t(bi) * d_in + d) * n + n0 + q;
-                p.part_A[o] = dA[q] * An[q];
-                if (p.dh0) p.dh0[o] = g[q];
+                p.part_A[(pb * d_in + d) * n + n0 + q] = dA[q] * An[q];
+                if (p.dh0 && seg == 0) p.dh0[(int64_t(bi) * d_in + d) * n + n0 + q] = g[q];
             }
+        }
+        if (seg > 0) {
+            // Hand the adjoint on to the earlier segment.
+            uint32_t* dst = reinterpret_cast<uint32_t*>(p.handoff) + (int64_t(seg - 1) * G + gi) * n * 64;
+#pragma unroll
+            for (int q = 0; q < NSW; q++)
+                if (n0 + q < n)
+                    __hip_atomic_store(dst + (n0 + q) * 64 + lane, __float_as_uint(g[q]), __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_AGENT);
         }
         barrier_lds();
         barrier_lds();
@@ -412,10 +491,19 @@ __global__ __launch_bounds__((SC + 4) * 64) void scan_bwd(const BwdParams p) {
                 sD += s_red[(r * 64 + etid) * 2];
                 sB += s_red[(r * 64 + etid) * 2 + 1];
             }
-            p.part_D[int64_t(bi) * d_in + dbase + etid] = sD;
-            p.part_bias[int64_t(bi) * d_in + dbase + etid] = sB;
+            p.part_D[pb * d_in + dbase + etid] = sD;
+            p.part_bias[pb * d_in + dbase + etid] = sB;
         }
         barrier_lds();
+    }
+    if (seg > 0) {
+        // As in the forward hand-off: every wave's stores acknowledged, the
+        // workgroup met, then one thread sets the flag.
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        if (tid == 0)
+            __hip_atomic_store(p.ctl + kFlagOffset + (seg - 1) * G + gi, 1u, __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
     }
 }
 

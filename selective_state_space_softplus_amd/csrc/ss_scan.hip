@@ -621,10 +621,11 @@ SeqShape bwd_shape(int64_t n) {
 }
 
 // Workspace of ss_scan_bwd, in order: the forward's checkpoints, the dB and dC
-// partials per channel group, the dA_log, dD and dbias partials per batch
-// row, then the forward scan's own workspace.
+// partials per channel group, the dA_log, dD and dbias partials per segment
+// and batch row, the control words and adjoints of the backward's segments,
+// then the forward scan's own workspace.
 struct BwdWorkspace {
-    size_t ckpt, part_B, part_C, part_A, part_D, part_bias, fwd, total;
+    size_t ckpt, part_B, part_C, part_A, part_D, part_bias, ctl, handoff, fwd, total;
 };
 
 size_t round256(size_t x) { return (x + 255) / 256 * 256; }
@@ -635,32 +636,56 @@ BwdWorkspace bwd_workspace(int64_t b, int64_t L, int64_t d_in, int64_t n) {
     BwdWorkspace w;
     w.ckpt = round256(size_t(b) * size_t(nck) * size_t(n) * size_t(d_in) * 4);
     w.part_B = w.part_C = round256(size_t(nblk) * size_t(b) * size_t(L) * size_t(n) * 4);
-    w.part_A = round256(size_t(b) * size_t(d_in) * size_t(n) * 4);
-    w.part_D = w.part_bias = round256(size_t(b) * size_t(d_in) * 4);
+    w.part_A = round256(size_t(kMaxSegments) * size_t(b) * size_t(d_in) * size_t(n) * 4);
+    w.part_D = w.part_bias = round256(size_t(kMaxSegments) * size_t(b) * size_t(d_in) * 4);
+    const int64_t G = b * nblk;
+    w.ctl = round256((size_t(ss::kFlagOffset) + size_t(G) * kMaxSegments) * sizeof(uint32_t));
+    w.handoff = round256(size_t(kMaxSegments - 1) * size_t(G) * size_t(n) * 64 * sizeof(float));
     w.fwd = seq_workspace(b, L, d_in, n).total;
-    w.total = w.ckpt + w.part_B + w.part_C + w.part_A + w.part_D + w.part_bias + w.fwd;
+    w.total = w.ckpt + w.part_B + w.part_C + w.part_A + w.part_D + w.part_bias + w.ctl + w.handoff + w.fwd;
     return w;
 }
 
+// Launches scan_bwd, cut into segments along L as the forward is (same rule:
+// balance the resident workgroups); p.K and p.Lseg are set here and the
+// number of segments is returned in *segments.
 template <typename TIn, int SC, int NSW>
-int launch_bwd(const BwdParams& p, bool gate, hipStream_t st) {
+int launch_bwd(BwdParams p, bool gate, hipStream_t st, int* segments) {
     constexpr int threads = (SC + 4) * 64;
+    constexpr int T = ss::kCkptSteps;
     using Kern = void (*)(BwdParams);
     static constexpr Kern kernels[4] = {ss::scan_bwd<TIn, SC, NSW, false, false>, ss::scan_bwd<TIn, SC, NSW, false, true>,
                                         ss::scan_bwd<TIn, SC, NSW, true, false>, ss::scan_bwd<TIn, SC, NSW, true, true>};
     const Kern kern = kernels[(p.softplus ? 2 : 0) | (gate ? 1 : 0)];
     const size_t lds = gate ? ss::BwdLds<SC, SC * NSW, true>::bytes : ss::BwdLds<SC, SC * NSW, false>::bytes;
-    hipLaunchKernelGGL(kern, dim3(unsigned(p.b * p.nblk_d)), dim3(threads), lds, st, p);
+    const int64_t G = p.b * p.nblk_d;
+    const int cus = device_cus();
+    const int per_cu = resident_per_cu(reinterpret_cast<const void*>(kern), threads, lds);
+    int K = choose_segments(G, p.L, T, int64_t(std::max(cus, 0)) * per_cu);
+    while (K > 1 && G * K > kMaxWorkgroups) K--;
+    int64_t Lseg = (p.L + K - 1) / K;
+    Lseg = (Lseg + T - 1) / T * T;
+    K = int((p.L + Lseg - 1) / Lseg);
+    p.K = K;
+    p.Lseg = Lseg;
+    *segments = K;
+    if (K > 1) {
+        const size_t words = size_t(ss::kFlagOffset) + size_t(G) * K;
+        const int rb = int(std::min<size_t>(1024, (words + 255) / 256));
+        hipLaunchKernelGGL(ss::scan_ctl_reset, dim3(rb), dim3(256), 0, st, p.ctl, int64_t(words));
+        if (hipGetLastError() != hipSuccess) return SS_ERR_HIP;
+    }
+    hipLaunchKernelGGL(kern, dim3(unsigned(G * K)), dim3(threads), lds, st, p);
     return hipGetLastError() == hipSuccess ? SS_OK : SS_ERR_HIP;
 }
 
 template <typename TIn>
-int dispatch_bwd(const BwdParams& p, bool gate, hipStream_t st) {
+int dispatch_bwd(const BwdParams& p, bool gate, hipStream_t st, int* segments) {
     const SeqShape sh = bwd_shape(p.n);
-    if (sh.SC == 1) return launch_bwd<TIn, 1, 2>(p, gate, st);
-    if (sh.SC == 4) return launch_bwd<TIn, 4, 2>(p, gate, st);
-    if (sh.NSW == 2) return launch_bwd<TIn, 8, 2>(p, gate, st);
-    return launch_bwd<TIn, 8, 4>(p, gate, st);
+    if (sh.SC == 1) return launch_bwd<TIn, 1, 2>(p, gate, st, segments);
+    if (sh.SC == 4) return launch_bwd<TIn, 4, 2>(p, gate, st, segments);
+    if (sh.NSW == 2) return launch_bwd<TIn, 8, 2>(p, gate, st, segments);
+    return launch_bwd<TIn, 8, 4>(p, gate, st, segments);
 }
 
 template <typename TOut>
@@ -734,6 +759,9 @@ SS_EXPORT int ss_scan_bwd(const void* u, const void* delta, const float* A_log, 
     float* part_A = reinterpret_cast<float*>(base + w.ckpt + w.part_B + w.part_C);
     float* part_D = reinterpret_cast<float*>(base + w.ckpt + w.part_B + w.part_C + w.part_A);
     float* part_bias = reinterpret_cast<float*>(base + w.ckpt + w.part_B + w.part_C + w.part_A + w.part_D);
+    uint32_t* bctl = reinterpret_cast<uint32_t*>(base + w.ckpt + w.part_B + w.part_C + w.part_A + w.part_D +
+                                                 w.part_bias);
+    float* handoff = reinterpret_cast<float*>(reinterpret_cast<char*>(bctl) + w.ctl);
     void* fwd_ws = base + w.total - w.fwd;
     hipStream_t st = static_cast<hipStream_t>(stream);
     const int nblk = int((d_in + 63) / 64);
@@ -795,16 +823,20 @@ SS_EXPORT int ss_scan_bwd(const void* u, const void* delta, const float* A_log, 
     p.nck = f.nck;
     p.nblk_d = nblk;
     p.softplus = f.softplus;
-    rc = dtype == SS_BF16 ? dispatch_bwd<uint16_t>(p, z != nullptr, st) : dispatch_bwd<float>(p, z != nullptr, st);
+    p.ctl = bctl;
+    p.handoff = handoff;
+    int K = 1;
+    rc = dtype == SS_BF16 ? dispatch_bwd<uint16_t>(p, z != nullptr, st, &K)
+                          : dispatch_bwd<float>(p, z != nullptr, st, &K);
     if (rc != SS_OK) return rc;
 
-    // 3. Sums over channel groups (dB, dC) and batch rows (dA_log, dD, dbias), in a fixed order.
+    // 3. Sums over channel groups (dB, dC) and segments and batch rows (dA_log, dD, dbias), in a fixed order.
     const int64_t nbc = b * L * n;
     rc = dtype == SS_BF16 ? reduce<uint16_t>(part_B, dB, nbc, nblk, st) : reduce<float>(part_B, dB, nbc, nblk, st);
     if (rc == SS_OK)
         rc = dtype == SS_BF16 ? reduce<uint16_t>(part_C, dC, nbc, nblk, st) : reduce<float>(part_C, dC, nbc, nblk, st);
-    if (rc == SS_OK) rc = reduce<float>(part_A, dA_log, d_in * n, b, st);
-    if (rc == SS_OK) rc = reduce<float>(part_D, dD, d_in, b, st);
-    if (rc == SS_OK && ddelta_bias && delta_bias) rc = reduce<float>(part_bias, ddelta_bias, d_in, b, st);
+    if (rc == SS_OK) rc = reduce<float>(part_A, dA_log, d_in * n, int64_t(K) * b, st);
+    if (rc == SS_OK) rc = reduce<float>(part_D, dD, d_in, int64_t(K) * b, st);
+    if (rc == SS_OK && ddelta_bias && delta_bias) rc = reduce<float>(part_bias, ddelta_bias, d_in, int64_t(K) * b, st);
     return rc;
 }
