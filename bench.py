@@ -300,6 +300,24 @@ def main(argv=None):
 
         ms_g = graphed(run64)
         cms_g = graphed(conv64)
+
+        # One step at a time with the last-level cache flushed before each
+        # (512 MB written between the timed steps): the state then comes from HBM.
+        flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+        fl = []
+        for t in range(16):
+            flush.fill_(t)
+            f0, f1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            f0.record()
+            ss.state_update(state, d["x"][t], d["dt"][t], d["A_log"], d["B"][t], d["C"][t], d["D"], d["z"][t],
+                            d["dt_bias"], True)
+            f1.record()
+            torch.cuda.synchronize()
+            fl.append(f0.elapsed_time(f1))
+        del flush
+        ms_f = sorted(fl)[len(fl) // 2]
+        result["decode"]["us_per_step_flushed"] = round(ms_f * 1e3, 2)
+        result["decode"]["GBps_flushed"] = round(db / (ms_f * 1e-3) / 1e9, 1)
         result["decode"]["us_per_step_graph"] = round(ms_g * 1e3, 2)
         result["decode"]["GBps_graph"] = round(db / (ms_g * 1e-3) / 1e9, 1)
         result["decode"]["conv_step"] = {
@@ -311,6 +329,25 @@ def main(argv=None):
             "GBps_graph": round(cbytes / (cms_g * 1e-3) / 1e9, 1),
             "algorithmic_bytes_per_step": cbytes,
         }
+
+    # A plain device copy of 1 GiB (torch's copy kernel): what this machine's HBM
+    # delivers to a streaming kernel, the practical ceiling beside the 8 TB/s
+    # specification.
+    csrc_t = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+    cdst_t = torch.empty_like(csrc_t)
+    for _ in range(3):
+        cdst_t.copy_(csrc_t)
+    torch.cuda.synchronize()
+    c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    c0.record()
+    for _ in range(5):
+        cdst_t.copy_(csrc_t)
+    c1.record()
+    torch.cuda.synchronize()
+    copy_gbps = 2 * (1 << 30) / (c0.elapsed_time(c1) / 5 * 1e-3) / 1e9
+    del csrc_t, cdst_t
+    result["copy_GBps"] = round(copy_gbps, 1)
+    result["hbm_frac_of_copy"] = round(gbps / copy_gbps, 4)
 
     if not args.no_bwd:
         # The gradient of the same scan-long scan (ss_scan_bwd: the forward

@@ -497,6 +497,34 @@ def pin_scan_bwd(lib):
             assert abs(fd - an) <= 1e-6 * (1 + abs(an)), f"finite differences {kw}: {fd} vs {an}"
 
 
+def pin_einsum_transcription(lib):
+    """A second, independent formulation in torch float64: the discretised tensors formed whole with einsum
+    (mhpn.cn page, section 3: exp(delta A) over (b, l, d_in, n) and delta B u), then the update-then-read-out
+    loop of section 4 and the skip of section 5 -- the unfused method the kernels avoid materialising."""
+    import torch
+
+    for seed, kw in enumerate([dict(), dict(n=1, gated=False, bias=False), dict(b=3, L=11, d_in=5, n=6)]):
+        c = random_case(700 + seed, **kw)
+        t = {k: (None if c[k] is None else torch.tensor(c[k])) for k in ("u", "delta", "A_log", "B", "C", "D", "z",
+                                                                        "delta_bias")}
+        dl = t["delta"] + (t["delta_bias"] if t["delta_bias"] is not None else 0.0)
+        dl = torch.nn.functional.softplus(dl)
+        A = -torch.exp(t["A_log"])
+        dA = torch.exp(torch.einsum("bld,dn->bldn", dl, A))
+        dBu = torch.einsum("bld,bln,bld->bldn", dl, t["B"], t["u"])
+        x = torch.zeros(dA.shape[0], dA.shape[2], dA.shape[3], dtype=torch.float64)
+        ys = []
+        for i in range(dA.shape[1]):
+            x = dA[:, i] * x + dBu[:, i]
+            ys.append(torch.einsum("bdn,bn->bd", x, t["C"][:, i]))
+        y = torch.stack(ys, dim=1) + t["u"] * t["D"]
+        if t["z"] is not None:
+            y = y * torch.nn.functional.silu(t["z"])
+        yo, lo = run(c, lib)
+        _close(yo, y.numpy(), rtol=1e-12, atol=1e-13, what=f"einsum transcription y {kw}")
+        _close(lo, x.numpy(), rtol=1e-12, atol=1e-13, what=f"einsum transcription last state {kw}")
+
+
 ALL_PINS = [pin_softplus_silu, pin_hand_worked, pin_brute_force, pin_geometric_closed_form, pin_limits,
             pin_skip_and_gate, pin_linearity_causality, pin_step_matches_scan, pin_bias_placement,
-            pin_initial_state, pin_zoh, pin_conv_update, pin_cross_scan, pin_scan_bwd]
+            pin_initial_state, pin_zoh, pin_conv_update, pin_cross_scan, pin_scan_bwd, pin_einsum_transcription]
