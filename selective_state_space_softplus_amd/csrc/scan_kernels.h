@@ -420,16 +420,28 @@ __global__ __launch_bounds__((SC + kSeqElemWaves + 1) * 64) void scan_seq(const 
         sd.read(ru + Lds::RX, er, ec);
         const int valid = ev(k);
         float* buf = s_dw + slot * DW_BUF;
+        if (valid == V) {                          // a whole row: nothing to mask
 #pragma unroll
-        for (int i = 0; i < V; i++) {
-            const bool ok = i < valid;
-            const float x = sd.f(i) + bias_v[i];
-            const float dl = ok ? (SP ? softplus(x) : x) : 0.0f;
-            uv[i] = ok ? su.f(i) : 0.0f;
-            *reinterpret_cast<float2*>(buf + ((er >> 1) * 64 + dw_slot(ec + i)) * 4 + (er & 1) * 2) =
-                make_float2(dl, ZOH ? uv[i] : dl * uv[i]);
+            for (int i = 0; i < V; i++) {
+                const float x = sd.f(i) + bias_v[i];
+                const float dl = SP ? softplus(x) : x;
+                uv[i] = su.f(i);
+                *reinterpret_cast<float2*>(buf + ((er >> 1) * 64 + dw_slot(ec + i)) * 4 + (er & 1) * 2) =
+                    make_float2(dl, ZOH ? uv[i] : dl * uv[i]);
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < V; i++) {
+                const bool ok = i < valid;
+                const float x = sd.f(i) + bias_v[i];
+                const float dl = ok ? (SP ? softplus(x) : x) : 0.0f;
+                uv[i] = ok ? su.f(i) : 0.0f;
+                *reinterpret_cast<float2*>(buf + ((er >> 1) * 64 + dw_slot(ec + i)) * 4 + (er & 1) * 2) =
+                    make_float2(dl, ZOH ? uv[i] : dl * uv[i]);
+            }
         }
     };
+
     // B and C of chunk k (ring slot `slot` = k % 3) as fp32, zero for missing rows and states.
     auto stage_bc = [&](int k, int slot) {
         const uint32_t* rb = reinterpret_cast<const uint32_t*>(lds + Lds::off_rbc + slot * 2 * Lds::RBC);
