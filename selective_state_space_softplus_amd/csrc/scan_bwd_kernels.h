@@ -232,85 +232,99 @@ __global__ __launch_bounds__((SC + 4) * 64) void scan_bwd(const BwdParams p) {
         accD[i] = accBias[i] = 0.0f;
     }
 
-    // Raw global values of one chunk as loaded by an element thread.
-    struct Raw {
-        float u[V], dl[V], z[V], dy[V];
-        float b[EBC], c[EBC];
+    // Global words of one chunk as loaded by an element thread.  Every load is
+    // issued unconditionally (an element outside the tensor reads element 0 of
+    // a valid array instead) and kept as loaded; masking and the bf16 widening
+    // happen when the chunk is prepared, one iteration later, so the loads stay
+    // in flight across the recurrence waves' work on the current chunk.
+    using RawIn = Raw<TIn>;
+    using Word = typename RawIn::type;
+    struct Chunk {
+        Word u[V], dl[V], z[V], dy[V];
+        Word b[EBC], c[EBC];
         float ck[ECK];
     };
     // Values an element thread keeps from preparing a chunk to finishing it.
     struct Keep {
         float x[V], z[V], dy[V];                   // delta + bias, z, dy
     };
-    Raw raw[3];
+    Chunk raw[3];
     Keep keep[3];
 
-    auto load_chunk = [&](Raw& r, int k) __attribute__((always_inline)) {         // issue the global loads of chunk k
-        const int t = k * T + er;
-        const bool rv = k >= kc0 && t < L;
+    // Which loads of chunk k fall inside the tensors (shared by load_chunk and prepare).
+    auto row_ok = [&](int k) __attribute__((always_inline)) { return k >= kc0 && k * T + er < L; };
+    auto bc_ok = [&](int k, int f) __attribute__((always_inline)) {
+        const int j = f / NP, kk = f - (f / NP) * NP;
+        return k >= kc0 && f < T * NP && k * T + j < L && kk < n;
+    };
+    auto ck_ok = [&](int k, int f) __attribute__((always_inline)) {
+        const int kk = f / 64, dd = dbase + (f & 63);
+        return k >= kc0 && f < NP * 64 && kk < n && dd < d_in && (k > 0 || p.h0 != nullptr);
+    };
+    auto load_chunk = [&](Chunk& r, int k) __attribute__((always_inline)) {       // issue the global loads of chunk k
+        const bool rv = row_ok(k);
+        const int64_t row = (brow + k * T + er) * d_in + ech;
 #pragma unroll
         for (int i = 0; i < V; i++) {
-            const bool ok = rv && i < evalid;
-            const int64_t e = (brow + t) * d_in + ech + i;
-            r.u[i] = ok ? Elem<TIn>::load(static_cast<const TIn*>(p.u), e) : 0.0f;
-            r.dl[i] = ok ? Elem<TIn>::load(static_cast<const TIn*>(p.delta), e) : 0.0f;
-            r.z[i] = (GATE && ok) ? Elem<TIn>::load(static_cast<const TIn*>(p.z), e) : 0.0f;
-            r.dy[i] = ok ? Elem<TIn>::load(static_cast<const TIn*>(p.dy), e) : 0.0f;
+            const int64_t e = (rv && i < evalid) ? row + i : 0;
+            r.u[i] = RawIn::load(static_cast<const TIn*>(p.u), e);
+            r.dl[i] = RawIn::load(static_cast<const TIn*>(p.delta), e);
+            if (GATE) r.z[i] = RawIn::load(static_cast<const TIn*>(p.z), e);
+            r.dy[i] = RawIn::load(static_cast<const TIn*>(p.dy), e);
         }
 #pragma unroll
         for (int m = 0; m < EBC; m++) {
             const int f = m * NE + etid;
             const int j = f / NP, kk = f - (f / NP) * NP;
-            const bool ok = k >= kc0 && f < T * NP && k * T + j < L && kk < n;
-            const int64_t e = (brow + k * T + j) * n + kk;
-            r.b[m] = ok ? Elem<TIn>::load(static_cast<const TIn*>(p.B), e) : 0.0f;
-            r.c[m] = ok ? Elem<TIn>::load(static_cast<const TIn*>(p.C), e) : 0.0f;
+            const int64_t e = bc_ok(k, f) ? (brow + k * T + j) * n + kk : 0;
+            r.b[m] = RawIn::load(static_cast<const TIn*>(p.B), e);
+            r.c[m] = RawIn::load(static_cast<const TIn*>(p.C), e);
         }
 #pragma unroll
         for (int m = 0; m < ECK; m++) {
             const int f = m * NE + etid;
-            const int kk = f / 64, l = f & 63;
-            const int dd = dbase + l;
-            const bool ok = k >= kc0 && f < NP * 64 && kk < n && dd < d_in;
-            float v = 0.0f;
-            if (ok) {
-                if (k > 0)
-                    v = p.ckpt[((int64_t(bi) * p.nck + k - 1) * n + kk) * d_in + dd];
-                else if (p.h0)
-                    v = p.h0[(int64_t(bi) * d_in + dd) * n + kk];
+            const int kk = f / 64, dd = dbase + (f & 63);
+            const float* src = p.A_log;           // any valid word when the value is not used
+            int64_t e = 0;
+            if (ck_ok(k, f)) {
+                src = k > 0 ? p.ckpt : p.h0;
+                e = k > 0 ? ((int64_t(bi) * p.nck + k - 1) * n + kk) * d_in + dd : (int64_t(bi) * d_in + dd) * n + kk;
             }
-            r.ck[m] = v;
+            r.ck[m] = src[e];
         }
     };
     // Prepare chunk k from its raw values: LDS ring slots s3 (of 3) and s2 (of 2).
-    auto prepare = [&](const Raw& r, Keep& kp, int k, int s3, int s2) __attribute__((always_inline)) {
-        const int t = k * T + er;
-        const bool rv = t < L;
+    auto prepare = [&](const Chunk& r, Keep& kp, int k, int s3, int s2) __attribute__((always_inline)) {
+        const bool rv = row_ok(k);
 #pragma unroll
         for (int i = 0; i < V; i++) {
             const bool ok = rv && i < evalid;
-            const float x = r.dl[i] + bias_v[i];
+            const float u = ok ? RawIn::f(r.u[i]) : 0.0f;
+            const float x = (ok ? RawIn::f(r.dl[i]) : 0.0f) + bias_v[i];
+            const float z = (GATE && ok) ? RawIn::f(r.z[i]) : 0.0f;
+            const float dy = ok ? RawIn::f(r.dy[i]) : 0.0f;
             const float dl = ok ? (SP ? softplus(x) : x) : 0.0f;
-            const float dyp = GATE ? r.dy[i] * silu(r.z[i]) : r.dy[i];
-            s_prep[(s3 * T + er) * 64 + ec + i] = make_float4(dl, dl * r.u[i], ok ? dyp : 0.0f, r.u[i]);
+            const float dyp = GATE ? dy * silu(z) : dy;
+            s_prep[(s3 * T + er) * 64 + ec + i] = make_float4(dl, dl * u, dyp, u);
             kp.x[i] = x;
-            kp.z[i] = r.z[i];
-            kp.dy[i] = r.dy[i];
+            kp.z[i] = z;
+            kp.dy[i] = dy;
         }
 #pragma unroll
         for (int m = 0; m < EBC; m++) {
             const int f = m * NE + etid;
             if ((T * NP) % NE != 0 && f >= T * NP) break;
             const int j = f / NP, kk = f - (f / NP) * NP;
+            const bool ok = bc_ok(k, f);
             float* dst = s_bc + s2 * (T * 2 * NP) + ((j * SC + kk / NSW) * 2) * NSW + kk % NSW;
-            dst[0] = r.b[m];
-            dst[NSW] = r.c[m];
+            dst[0] = ok ? RawIn::f(r.b[m]) : 0.0f;
+            dst[NSW] = ok ? RawIn::f(r.c[m]) : 0.0f;
         }
 #pragma unroll
         for (int m = 0; m < ECK; m++) {
             const int f = m * NE + etid;
             if ((NP * 64) % NE != 0 && f >= NP * 64) break;
-            s_ck[s2 * NP * 64 + f] = r.ck[m];
+            s_ck[s2 * NP * 64 + f] = ck_ok(k, f) ? r.ck[m] : 0.0f;
         }
     };
     // Finish chunk k: sums of the recurrence waves' partials, the per-element
