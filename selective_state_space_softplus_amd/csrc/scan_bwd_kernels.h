@@ -233,12 +233,15 @@ __global__ __launch_bounds__((SC + 4) * 64) void scan_bwd(const BwdParams p) {
     }
 
     // Global words of one chunk as loaded by an element thread.  Every load is
-    // issued unconditionally (an element outside the tensor reads element 0 of
-    // a valid array instead) and kept as loaded; masking and the bf16 widening
-    // happen when the chunk is prepared, one iteration later, so the loads stay
-    // in flight across the recurrence waves' work on the current chunk.
+    // issued unconditionally (an element outside the tensor reads a valid word
+    // of the same array instead) and kept as loaded; masking and the bf16
+    // widening happen when the chunk is prepared, one iteration later, so the
+    // loads stay in flight across the recurrence waves' work on the current
+    // chunk.  Addresses are a per-chunk base, uniform over the workgroup, plus
+    // a 32-bit byte offset fixed per thread.
     using RawIn = Raw<TIn>;
     using Word = typename RawIn::type;
+    constexpr int ES = int(sizeof(TIn));
     struct Chunk {
         Word u[V], dl[V], z[V], dy[V];
         Word b[EBC], c[EBC];
@@ -251,46 +254,75 @@ __global__ __launch_bounds__((SC + 4) * 64) void scan_bwd(const BwdParams p) {
     Chunk raw[3];
     Keep keep[3];
 
-    // Which loads of chunk k fall inside the tensors (shared by load_chunk and prepare).
-    auto row_ok = [&](int k) __attribute__((always_inline)) { return k >= kc0 && k * T + er < L; };
-    auto bc_ok = [&](int k, int f) __attribute__((always_inline)) {
+    // Per-thread parts of the element, B/C and entering-state addresses, and
+    // which of them exist whatever the chunk.
+    uint32_t off_row[V];                           // (er, ech + i) from (chunk row 0, dbase)
+#pragma unroll
+    for (int i = 0; i < V; i++) off_row[i] = i < evalid ? uint32_t(er * d_in + ec + i) * uint32_t(ES) : 0u;
+    int bc_row[EBC];                               // step row j of the B/C word, -1 if none
+    uint32_t off_bc[EBC];                          // (j, kk) from (chunk row 0, state 0)
+#pragma unroll
+    for (int m = 0; m < EBC; m++) {
+        const int f = m * NE + etid;
         const int j = f / NP, kk = f - (f / NP) * NP;
-        return k >= kc0 && f < T * NP && k * T + j < L && kk < n;
-    };
-    auto ck_ok = [&](int k, int f) __attribute__((always_inline)) {
+        const bool ok = !rec && f < T * NP && kk < n;
+        bc_row[m] = ok ? j : -1;
+        off_bc[m] = ok ? uint32_t((j * n + kk) * ES) : 0u;
+    }
+    uint32_t off_ck[ECK], off_h0[ECK];             // (kk, dd) in a checkpoint and in h0
+    bool ck_has[ECK];
+#pragma unroll
+    for (int m = 0; m < ECK; m++) {
+        const int f = m * NE + etid;
         const int kk = f / 64, dd = dbase + (f & 63);
-        return k >= kc0 && f < NP * 64 && kk < n && dd < d_in && (k > 0 || p.h0 != nullptr);
+        ck_has[m] = !rec && f < NP * 64 && kk < n && dd < d_in;
+        off_ck[m] = ck_has[m] ? uint32_t(kk * d_in + dd) * 4u : 0u;
+        off_h0[m] = ck_has[m] ? uint32_t(dd * n + kk) * 4u : 0u;
+    }
+    // Element threads that write a dB, dC word of a chunk (T n <= T NP <= NE).
+    const int pf_j = etid / max(n, 1), pf_kk = etid - pf_j * max(n, 1);
+    const bool pf_has = !rec && etid < T * n;
+
+    // Uniform bases of chunk k (clamped into the segment, so always inside the tensors).
+    auto row_base = [&](int k) __attribute__((always_inline)) {
+        return (brow + int64_t(max(k, kc0)) * T) * d_in + dbase;      // element index
+    };
+    auto ld = [&](const void* base, int64_t idx, uint32_t boff) __attribute__((always_inline)) {
+        const TIn* q = static_cast<const TIn*>(base) + idx;
+        return RawIn::load(reinterpret_cast<const TIn*>(reinterpret_cast<const char*>(q) + boff), 0);
+    };
+    auto row_ok = [&](int k) __attribute__((always_inline)) { return k >= kc0 && k * T + er < L; };
+    auto bc_ok = [&](int k, int m) __attribute__((always_inline)) {
+        return k >= kc0 && bc_row[m] >= 0 && k * T + bc_row[m] < L;
+    };
+    auto ck_ok = [&](int k, int m) __attribute__((always_inline)) {
+        return k >= kc0 && ck_has[m] && (k > 0 || p.h0 != nullptr);
     };
     auto load_chunk = [&](Chunk& r, int k) __attribute__((always_inline)) {       // issue the global loads of chunk k
         const bool rv = row_ok(k);
-        const int64_t row = (brow + k * T + er) * d_in + ech;
+        const int64_t rb = row_base(k);
 #pragma unroll
         for (int i = 0; i < V; i++) {
-            const int64_t e = (rv && i < evalid) ? row + i : 0;
-            r.u[i] = RawIn::load(static_cast<const TIn*>(p.u), e);
-            r.dl[i] = RawIn::load(static_cast<const TIn*>(p.delta), e);
-            if (GATE) r.z[i] = RawIn::load(static_cast<const TIn*>(p.z), e);
-            r.dy[i] = RawIn::load(static_cast<const TIn*>(p.dy), e);
+            const uint32_t o = rv ? off_row[i] : 0u;
+            r.u[i] = ld(p.u, rb, o);
+            r.dl[i] = ld(p.delta, rb, o);
+            if (GATE) r.z[i] = ld(p.z, rb, o);
+            r.dy[i] = ld(p.dy, rb, o);
         }
+        const int64_t bb = (brow + int64_t(max(k, kc0)) * T) * n;
 #pragma unroll
         for (int m = 0; m < EBC; m++) {
-            const int f = m * NE + etid;
-            const int j = f / NP, kk = f - (f / NP) * NP;
-            const int64_t e = bc_ok(k, f) ? (brow + k * T + j) * n + kk : 0;
-            r.b[m] = RawIn::load(static_cast<const TIn*>(p.B), e);
-            r.c[m] = RawIn::load(static_cast<const TIn*>(p.C), e);
+            const uint32_t o = bc_ok(k, m) ? off_bc[m] : 0u;
+            r.b[m] = ld(p.B, bb, o);
+            r.c[m] = ld(p.C, bb, o);
         }
+        // Entering state: checkpoint k - 1, or h0 for the first chunk.
+        const float* cb = k > 0 ? p.ckpt + (int64_t(bi) * p.nck + k - 1) * n * d_in
+                                : (p.h0 ? p.h0 + int64_t(bi) * d_in * n : p.A_log);
 #pragma unroll
         for (int m = 0; m < ECK; m++) {
-            const int f = m * NE + etid;
-            const int kk = f / 64, dd = dbase + (f & 63);
-            const float* src = p.A_log;           // any valid word when the value is not used
-            int64_t e = 0;
-            if (ck_ok(k, f)) {
-                src = k > 0 ? p.ckpt : p.h0;
-                e = k > 0 ? ((int64_t(bi) * p.nck + k - 1) * n + kk) * d_in + dd : (int64_t(bi) * d_in + dd) * n + kk;
-            }
-            r.ck[m] = src[e];
+            const uint32_t o = ck_ok(k, m) ? (k > 0 ? off_ck[m] : off_h0[m]) : 0u;
+            r.ck[m] = *reinterpret_cast<const float*>(reinterpret_cast<const char*>(k >= kc0 ? cb : p.A_log) + o);
         }
     };
     // Prepare chunk k from its raw values: LDS ring slots s3 (of 3) and s2 (of 2).
@@ -315,7 +347,7 @@ __global__ __launch_bounds__((SC + 4) * 64) void scan_bwd(const BwdParams p) {
             const int f = m * NE + etid;
             if ((T * NP) % NE != 0 && f >= T * NP) break;
             const int j = f / NP, kk = f - (f / NP) * NP;
-            const bool ok = bc_ok(k, f);
+            const bool ok = bc_ok(k, m);
             float* dst = s_bc + s2 * (T * 2 * NP) + ((j * SC + kk / NSW) * 2) * NSW + kk % NSW;
             dst[0] = ok ? RawIn::f(r.b[m]) : 0.0f;
             dst[NSW] = ok ? RawIn::f(r.c[m]) : 0.0f;
@@ -324,51 +356,60 @@ __global__ __launch_bounds__((SC + 4) * 64) void scan_bwd(const BwdParams p) {
         for (int m = 0; m < ECK; m++) {
             const int f = m * NE + etid;
             if ((NP * 64) % NE != 0 && f >= NP * 64) break;
-            s_ck[s2 * NP * 64 + f] = ck_ok(k, f) ? r.ck[m] : 0.0f;
+            s_ck[s2 * NP * 64 + f] = ck_ok(k, m) ? r.ck[m] : 0.0f;
         }
     };
     // Finish chunk k: sums of the recurrence waves' partials, the per-element
     // gradients, and the chunk's dB, dC rows of this channel group.
     auto finalize = [&](const Keep& kp, int k, int s3, int s2) __attribute__((always_inline)) {
-        const int t = k * T + er;
-        const bool rv = t < L;
-        const int64_t e0 = (brow + t) * d_in + ech;
+        const bool rv = row_ok(k);
+        const int64_t rb = row_base(k);
+        // This thread's (step row, channel) in the partials of wave 0; wave w at + w T 64.
+        const float2* pp = s_part + (s2 * SC * T + er) * 64 + ec;
+        const float* py = s_yp + (s2 * SC * T + er) * 64 + ec;
+        float2 q[SC][V];
+        float yq[SC][V];
+#pragma unroll
+        for (int w = 0; w < SC; w++)
+#pragma unroll
+            for (int i = 0; i < V; i++) {
+                q[w][i] = pp[w * T * 64 + i];
+                yq[w][i] = GATE ? py[w * T * 64 + i] : 0.0f;
+            }
 #pragma unroll
         for (int i = 0; i < V; i++) {
             const float4 pr = s_prep[(s3 * T + er) * 64 + ec + i];    // (Delta, w, dy', u)
-            float S1 = 0.0f, S2 = 0.0f, yp = 0.0f;
+            float S1 = q[0][i].x, S2 = q[0][i].y, yp = yq[0][i];
 #pragma unroll
-            for (int w = 0; w < SC; w++) {
-                const float2 q = s_part[((s2 * SC + w) * T + er) * 64 + ec + i];
-                S1 += q.x;
-                S2 += q.y;
-                if (GATE) yp += s_yp[((s2 * SC + w) * T + er) * 64 + ec + i];
+            for (int w = 1; w < SC; w++) {
+                S1 += q[w][i].x;
+                S2 += q[w][i].y;
+                if (GATE) yp += yq[w][i];
             }
             const float dDelta = fmaf(pr.w, S1, S2);
             const float ddl = SP ? dDelta * rcp_hw(1.0f + exp2_hw(-kp.x[i] * kLog2e)) : dDelta;
             const float du = fmaf(pr.x, S1, pr.z * Dv[i]);
             if (rv && i < evalid) {
-                Elem<TIn>::store(static_cast<TIn*>(p.du), e0 + i, du);
-                Elem<TIn>::store(static_cast<TIn*>(p.ddelta), e0 + i, ddl);
+                auto st = [&](void* base, float v) __attribute__((always_inline)) {
+                    TIn* q = static_cast<TIn*>(base) + rb;
+                    Elem<TIn>::store(reinterpret_cast<TIn*>(reinterpret_cast<char*>(q) + off_row[i]), 0, v);
+                };
+                st(p.du, du);
+                st(p.ddelta, ddl);
                 if (GATE) {
                     const float ypre = fmaf(Dv[i], pr.w, yp);
                     const float sg = rcp_hw(1.0f + exp2_hw(-kp.z[i] * kLog2e));
-                    const float dz = kp.dy[i] * ypre * sg * fmaf(kp.z[i], 1.0f - sg, 1.0f);
-                    Elem<TIn>::store(static_cast<TIn*>(p.dz), e0 + i, dz);
+                    st(p.dz, kp.dy[i] * ypre * sg * fmaf(kp.z[i], 1.0f - sg, 1.0f));
                 }
                 accD[i] = fmaf(pr.z, pr.w, accD[i]);
                 accBias[i] += ddl;
             }
         }
         // dB, dC of the chunk's rows: T * n consecutive values of each.
-        const int64_t prow = (int64_t(grp) * p.b + bi) * L;
-        for (int f = etid; f < T * n; f += NE) {
-            const int j = f / n, kk = f - (f / n) * n;
-            if (k * T + j < L) {
-                const int64_t o = (prow + k * T + j) * n + kk;
-                p.part_B[o] = s_dbc[((s2 * T + j) * 2 + 0) * NP + kk];
-                p.part_C[o] = s_dbc[((s2 * T + j) * 2 + 1) * NP + kk];
-            }
+        if (pf_has && k * T + pf_j < L) {
+            const int64_t o = ((int64_t(grp) * p.b + bi) * L + int64_t(k) * T) * n + etid;
+            p.part_B[o] = s_dbc[((s2 * T + pf_j) * 2 + 0) * NP + pf_kk];
+            p.part_C[o] = s_dbc[((s2 * T + pf_j) * 2 + 1) * NP + pf_kk];
         }
     };
     // Recurrence waves, chunk c: recompute its states, then the adjoint back through them.
