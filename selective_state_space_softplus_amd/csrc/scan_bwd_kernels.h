@@ -25,8 +25,10 @@
 // adjoint back through them.  The 4 element waves load and prepare the next
 // chunk (delta', delta' u, dy', the fp32 B and C rows, the entering state;
 // their global loads are issued one chunk earlier still), and finish the
-// previous one (sums of the waves' S1, S2 and readout partials, du, ddelta,
-// dz, and the chunk's dB, dC rows).  Sums over the 64 channels (dB, dC) are
+// previous one (sums of the waves' S1, S2 partials, du, ddelta, and the
+// chunk's dB, dC rows).  dz needs the readout y'_t and nothing else does:
+// the forward pass that saves the states writes it (scan_seq with DZ), so
+// the readout is never recomputed here.  Sums over the 64 channels (dB, dC) are
 // cross-lane reductions inside each recurrence wave; sums over the channel groups,
 // batch rows and time (dB, dC, dA_log, dD, dbias) go through per-workgroup
 // partials that reduce_groups adds in a fixed order, so every gradient is
@@ -55,7 +57,6 @@ struct BwdParams {
     const float* ckpt;        // (b, nck, n, d_in): state after steps 8 (i + 1)
     void* du;
     void* ddelta;
-    void* dz;                 // null without a gate
     float* dh0;               // null unless asked
     float* part_B;            // (nblk_d, b, L, n) dB per channel group
     float* part_C;            // (nblk_d, b, L, n)
@@ -103,19 +104,17 @@ __device__ __forceinline__ float wave_sum4(float v0, float v1, float v2, float v
 }
 
 // LDS of scan_bwd<SC recurrence waves, NP padded states>, T = 8 steps.
-template <int SC, int NP, bool GATE>
+template <int SC, int NP>
 struct BwdLds {
     static constexpr int T = kCkptSteps;
     static constexpr int PREP = T * 64 * 16;                  // (Delta, w, dy', u) per (step, channel)
     static constexpr int PART = SC * T * 64 * 8;              // (S1, S2) per (wave, step, channel)
-    static constexpr int YP = GATE ? SC * T * 64 * 4 : 0;     // readout partials
     static constexpr int CK = NP * 64 * 4;                    // state entering the chunk
     static constexpr int BC = T * 2 * NP * 4;                 // B, C rows as fp32, grouped per wave
     static constexpr int DBC = T * 2 * NP * 4;                // dB, dC sums of the chunk
     static constexpr int off_prep = 0;                        // [3]
     static constexpr int off_part = off_prep + 3 * PREP;      // [2]
-    static constexpr int off_yp = off_part + 2 * PART;        // [2]
-    static constexpr int off_ck = off_yp + 2 * YP;            // [2]
+    static constexpr int off_ck = off_part + 2 * PART;        // [2]
     static constexpr int off_bc = off_ck + 2 * CK;            // [2]
     static constexpr int off_dbc = off_bc + 2 * BC;           // [2]
     static constexpr int off_ticket = off_dbc + 2 * DBC;      // ticket, timeout flag
@@ -131,7 +130,7 @@ __global__ __launch_bounds__((SC + 4) * 64) void scan_bwd(const BwdParams p) {
     constexpr int NP = SC * NSW;
     constexpr int EBC = (T * NP + NE - 1) / NE;    // B (and C) values each element thread stages per chunk
     constexpr int ECK = (NP * 64 + NE - 1) / NE;   // entering-state values each element thread stages
-    using Lds = BwdLds<SC, NP, GATE>;
+    using Lds = BwdLds<SC, NP>;
     static_assert(Lds::bytes <= 160 * 1024, "LDS of one workgroup");
     static_assert(NE / TPR == T, "thread tiling of a chunk");
     static_assert(NSW % 2 == 0, "states reduced two at a time");
@@ -139,7 +138,6 @@ __global__ __launch_bounds__((SC + 4) * 64) void scan_bwd(const BwdParams p) {
     char* const lds = reinterpret_cast<char*>(smem);
     float4* s_prep = reinterpret_cast<float4*>(lds + Lds::off_prep);   // [3][T][64]
     float2* s_part = reinterpret_cast<float2*>(lds + Lds::off_part);   // [2][SC][T][64]
-    float* s_yp = reinterpret_cast<float*>(lds + Lds::off_yp);         // [2][SC][T][64]
     float* s_ck = reinterpret_cast<float*>(lds + Lds::off_ck);         // [2][NP][64]
     float* s_bc = reinterpret_cast<float*>(lds + Lds::off_bc);         // [2][T][SC][2][NSW]
     float* s_dbc = reinterpret_cast<float*>(lds + Lds::off_dbc);       // [2][T][2][NP]
@@ -249,7 +247,7 @@ __global__ __launch_bounds__((SC + 4) * 64) void scan_bwd(const BwdParams p) {
     };
     // Values an element thread keeps from preparing a chunk to finishing it.
     struct Keep {
-        float x[V], z[V], dy[V];                   // delta + bias, z, dy
+        float x[V];                                // delta + bias
     };
     Chunk raw[3];
     Keep keep[3];
@@ -339,8 +337,6 @@ __global__ __launch_bounds__((SC + 4) * 64) void scan_bwd(const BwdParams p) {
             const float dyp = GATE ? dy * silu(z) : dy;
             s_prep[(s3 * T + er) * 64 + ec + i] = make_float4(dl, dl * u, dyp, u);
             kp.x[i] = x;
-            kp.z[i] = z;
-            kp.dy[i] = dy;
         }
 #pragma unroll
         for (int m = 0; m < EBC; m++) {
@@ -366,25 +362,19 @@ __global__ __launch_bounds__((SC + 4) * 64) void scan_bwd(const BwdParams p) {
         const int64_t rb = row_base(k);
         // This thread's (step row, channel) in the partials of wave 0; wave w at + w T 64.
         const float2* pp = s_part + (s2 * SC * T + er) * 64 + ec;
-        const float* py = s_yp + (s2 * SC * T + er) * 64 + ec;
         float2 q[SC][V];
-        float yq[SC][V];
 #pragma unroll
         for (int w = 0; w < SC; w++)
 #pragma unroll
-            for (int i = 0; i < V; i++) {
-                q[w][i] = pp[w * T * 64 + i];
-                yq[w][i] = GATE ? py[w * T * 64 + i] : 0.0f;
-            }
+            for (int i = 0; i < V; i++) q[w][i] = pp[w * T * 64 + i];
 #pragma unroll
         for (int i = 0; i < V; i++) {
             const float4 pr = s_prep[(s3 * T + er) * 64 + ec + i];    // (Delta, w, dy', u)
-            float S1 = q[0][i].x, S2 = q[0][i].y, yp = yq[0][i];
+            float S1 = q[0][i].x, S2 = q[0][i].y;
 #pragma unroll
             for (int w = 1; w < SC; w++) {
                 S1 += q[w][i].x;
                 S2 += q[w][i].y;
-                if (GATE) yp += yq[w][i];
             }
             const float dDelta = fmaf(pr.w, S1, S2);
             const float ddl = SP ? dDelta * rcp_hw(1.0f + exp2_hw(-kp.x[i] * kLog2e)) : dDelta;
@@ -396,11 +386,6 @@ __global__ __launch_bounds__((SC + 4) * 64) void scan_bwd(const BwdParams p) {
                 };
                 st(p.du, du);
                 st(p.ddelta, ddl);
-                if (GATE) {
-                    const float ypre = fmaf(Dv[i], pr.w, yp);
-                    const float sg = rcp_hw(1.0f + exp2_hw(-kp.z[i] * kLog2e));
-                    st(p.dz, kp.dy[i] * ypre * sg * fmaf(kp.z[i], 1.0f - sg, 1.0f));
-                }
                 accD[i] = fmaf(pr.z, pr.w, accD[i]);
                 accBias[i] += ddl;
             }
@@ -422,16 +407,13 @@ __global__ __launch_bounds__((SC + 4) * 64) void scan_bwd(const BwdParams p) {
 #pragma unroll
         for (int j = 0; j < T; j++) {
             const float4 pr = s_prep[(s3 * T + j) * 64 + lane];
-            float acc = 0.0f;
 #pragma unroll
             for (int q = 0; q < NSW; q++) {
                 const float a = exp2_hw(pr.x * A2[q]);
                 h[q] = fmaf(a, h[q], pr.y * bcw[j * SC * 2 * NSW + q]);
                 hs[j][q] = h[q];
                 as[j][q] = a;
-                acc = fmaf(bcw[j * SC * 2 * NSW + NSW + q], h[q], acc);
             }
-            if (GATE) s_yp[((s2 * SC + wave) * T + j) * 64 + lane] = acc;
         }
 #pragma unroll
         for (int j = T - 1; j >= 0; j--) {

@@ -56,6 +56,8 @@ struct ScanParams {
     float* last_state;
     const float* h0;     // (b, d_in, n) initial state, or null for zero (scan_seq)
     float* ckpt;         // (b, nck, n, d_in) states after every kCkptSteps steps, or null (scan_seq)
+    const void* dy;      // gradient of y: with dz, scan_seq writes dz in place of y (gated scans)
+    void* dz;
     int nck;             // checkpoints per batch row: (L - 1) / kCkptSteps
     int64_t b, L, d_in, n;
     int softplus;
@@ -177,6 +179,37 @@ struct RawRow {
             }
         }
     }
+    // The same V elements from a row in global memory at `src`: one vector
+    // load when WIDE (src aligned to V elements), else element loads, of
+    // which those past `valid` read element 0 again.
+    __device__ __forceinline__ void load(const TIn* src, int valid) {
+        if constexpr (WIDE) {
+            const char* c = reinterpret_cast<const char*>(src);
+            if constexpr (NW == 1) {
+                w[0] = *reinterpret_cast<const uint32_t*>(c);
+            } else if constexpr (NW == 2) {
+                const uint2 v = *reinterpret_cast<const uint2*>(c);
+                w[0] = v.x;
+                w[1] = v.y;
+            } else {
+#pragma unroll
+                for (int q = 0; q < NW / 4; q++) {
+                    const uint4 v = reinterpret_cast<const uint4*>(c)[q];
+                    w[4 * q] = v.x;
+                    w[4 * q + 1] = v.y;
+                    w[4 * q + 2] = v.z;
+                    w[4 * q + 3] = v.w;
+                }
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < V; i++) {
+                const int e = i < valid ? i : 0;
+                if constexpr (kHalf) w[i] = reinterpret_cast<const uint16_t*>(src)[e];
+                else w[i] = __float_as_uint(reinterpret_cast<const float*>(src)[e]);
+            }
+        }
+    }
     __device__ __forceinline__ float f(int i) const {
         if constexpr (!kHalf) return __uint_as_float(w[i]);
         else if constexpr (!WIDE) return __uint_as_float(w[i] << 16);
@@ -193,6 +226,9 @@ struct RawRow {
 // (0 row-major, 1 column-major, 2 and 3 those backwards) of map bi / 4; u is
 // the (maps, H, W, d_in) map, A_log, D and the bias hold one set per
 // direction, and y is fp32 (b, L, d_in), each direction in its own step order.
+// DZ (with GATE): the pass inside the backward -- instead of y it writes the
+// gradient of the gate input, dz = dy y_pre silu'(z), y_pre = sum C h + D u
+// (dy read by the element waves one chunk ahead of its use).
 //
 // Waves 0 .. SC-1 ("recurrence waves") each hold NSW states of the 64
 // channels and run nothing but the recurrence.  Waves SC .. SC+3 ("element
@@ -213,7 +249,7 @@ struct RawRow {
 //     tiles (loaded two chunks earlier);
 //   - the loader issues the loads of chunk c+4 (u, delta, B, C) and of chunk
 //     c+1 (z), then waits until those of chunk c+3 and c are complete.
-template <typename TIn, int SC, int NSW, int T, bool WIDE, bool SP, bool GATE, bool ZOH, bool CROSS>
+template <typename TIn, int SC, int NSW, int T, bool WIDE, bool SP, bool GATE, bool ZOH, bool CROSS, bool DZ = false>
 __global__ __launch_bounds__((SC + kSeqElemWaves + 1) * 64) void scan_seq(const ScanParams p) {
     constexpr int P = kSeqElemWaves;
     constexpr int ES = int(sizeof(TIn));
@@ -238,6 +274,7 @@ __global__ __launch_bounds__((SC + kSeqElemWaves + 1) * 64) void scan_seq(const 
     static_assert(!WIDE || (T * 64 * ES) % 1024 == 0, "whole loads per tile");
     static_assert(Lds::bytes <= 160 * 1024, "LDS of one workgroup");
     static_assert(T % kCkptSteps == 0, "checkpoints fall at chunk-internal step boundaries");
+    static_assert(!DZ || (GATE && !ZOH && !CROSS), "dz is the gradient of a gated Euler scan");
     extern __shared__ __align__(16) float smem[];
     char* const lds = reinterpret_cast<char*>(smem);
     float* s_dw = reinterpret_cast<float*>(lds + Lds::off_dw);   // [3][T/2][64][4]: (delta'_j, w_j, delta'_j+1, w_j+1)
@@ -462,8 +499,16 @@ __global__ __launch_bounds__((SC + kSeqElemWaves + 1) * 64) void scan_seq(const 
             dst[NSW] = ok ? cv : 0.0f;
         }
     };
-    // Phase 2 of chunk k: sum of the partial readouts, D skip, gate (z slot `zslot`), store.
-    auto phase2 = [&](int k, const float* uvk, int zslot) {
+    // dy of chunk k (DZ): this thread's V channels of its step row, issued one
+    // chunk before phase 2 uses them (rows past the segment read its last row).
+    auto load_dy = [&](int k, Row& r) {
+        const int t = min(t_begin + k * T + er, t_end - 1);
+        const int valid = max(evalid, 1);
+        r.load(static_cast<const TIn*>(p.dy) + (brow + t) * d_in + (evalid > 0 ? ech : dbase), valid);
+    };
+    // Phase 2 of chunk k: sum of the partial readouts, D skip, gate (z slot `zslot`), store
+    // (DZ: dz from that sum, z and dy row `dyk`).
+    auto phase2 = [&](int k, const float* uvk, int zslot, const Row& dyk) {
         float ypv[SC][V];
         const float* src = s_yp + (k & 1) * YP_BUF + er * 64 + ec;
 #pragma unroll
@@ -479,11 +524,17 @@ __global__ __launch_bounds__((SC + kSeqElemWaves + 1) * 64) void scan_seq(const 
 #pragma unroll
             for (int w = 1; w < SC; w++) acc += ypv[w][i];
             acc = fmaf(Dv[i], uvk[i], acc);
-            if (GATE) acc *= silu(zr.f(i));
+            if constexpr (DZ) {
+                const float z = zr.f(i);
+                const float sg = rcp_hw(1.0f + exp2_hw(-z * kLog2e));
+                acc = dyk.f(i) * acc * sg * fmaf(z, 1.0f - sg, 1.0f);
+            } else if (GATE) {
+                acc *= silu(zr.f(i));
+            }
             yv[i] = acc;
         }
         const int valid = ev(k);
-        TOut* yp = static_cast<TOut*>(p.y);
+        TOut* yp = static_cast<TOut*>(DZ ? p.dz : p.y);
         if (valid > 0 && yp)
             store_span<TOut, V, WIDE>(yp + (brow + t_begin + int64_t(k) * T) * d_in, off_el, yv, valid);
     };
@@ -491,6 +542,7 @@ __global__ __launch_bounds__((SC + kSeqElemWaves + 1) * 64) void scan_seq(const 
     // ---- fill: loads of chunks 0 .. 2 and the gate of chunk 0; phase 1 and
     // B/C of chunks 0 and 1.
     float uvm1[V], uv0[V], uv1[V], uv2[V];
+    Row dyr[3];                                   // DZ: dy of chunk c in dyr[c % 3]
     if (loader) {
         dma_chunk(0, 0);
         dma_chunk(1, 1);
@@ -606,7 +658,8 @@ __global__ __launch_bounds__((SC + kSeqElemWaves + 1) * 64) void scan_seq(const 
     auto elem_chunk = [&](auto ph, int c) {
         constexpr int PH = decltype(ph)::value;
         constexpr int K2 = (PH + 2) % 3;         // ring slot of chunks c+2 and c-1
-        if (c > 0) phase2(c - 1, uvm1, K2);
+        if (DZ) load_dy(c, dyr[PH]);
+        if (c > 0) phase2(c - 1, uvm1, K2, dyr[K2]);
         phase1(c + 2, K2, uv2);
         stage_bc(c + 2, K2);
 #pragma unroll
@@ -650,7 +703,7 @@ __global__ __launch_bounds__((SC + kSeqElemWaves + 1) * 64) void scan_seq(const 
     }
 
     if (elem) {
-        phase2(nch3 - 1, uvm1, 2);                // drain: the last chunk's outputs (nch3 - 1 = 2 mod 3)
+        phase2(nch3 - 1, uvm1, 2, dyr[2]);        // drain: the last chunk's outputs (nch3 - 1 = 2 mod 3)
     } else if (loader) {
         wait_vmem<0>();   // no load may land after the workgroup ends
     } else if (seg + 1 < p.K) {

@@ -167,8 +167,18 @@ int choose_segments(int64_t G, int64_t L, int T, int64_t slots) {
     return best;
 }
 
-// Which family of scan_seq kernels a call needs.
-enum class SeqMode { Euler, Zoh, Cross };
+// Which family of scan_seq kernels a call needs.  Dz: the gated Euler scan
+// inside the backward, writing dz in place of y.
+enum class SeqMode { Euler, Zoh, Cross, Dz };
+
+// scan_seq writing dz, for the state sizes the backward takes (none above).
+template <typename TIn, int SC, int NSW, int T, bool WIDE, bool SP>
+constexpr void (*dz_kernel())(ss::ScanParams) {
+    if constexpr (SC * NSW <= SS_MAX_BWD_STATE)
+        return ss::scan_seq<TIn, SC, NSW, T, WIDE, SP, true, false, false, true>;
+    else
+        return nullptr;
+}
 
 template <typename TIn, int SC, int NSW>
 int launch_seq(ScanParams p, SeqMode mode, void* ws, size_t ws_bytes, hipStream_t st) {
@@ -183,15 +193,18 @@ int launch_seq(ScanParams p, SeqMode mode, void* ws, size_t ws_bytes, hipStream_
     // element).  The zero-order-hold kernels exist in the element-load form
     // only: their recurrence costs about three times the Euler one, which
     // hides the difference in load width.  The cross scan has no gate.
+    const void* out = mode == SeqMode::Dz ? p.dz : p.y;
     const bool wide = mode != SeqMode::Zoh && (p.d_in * int64_t(sizeof(TIn))) % 16 == 0 && aligned(p.u, 16) &&
                       aligned(p.delta, 16) && (!p.z || aligned(p.z, 16)) &&
-                      (mode == SeqMode::Cross || aligned(p.y, (TW / ss::kSeqElemWaves) * sizeof(TIn)));
+                      (mode != SeqMode::Dz || aligned(p.dy, 16)) &&
+                      (mode == SeqMode::Cross || aligned(out, (TW / ss::kSeqElemWaves) * sizeof(TIn)));
     const int T = wide ? TW : TN;
     const int variant = mode == SeqMode::Cross ? 12 + (wide ? 2 : 0) + (p.softplus ? 1 : 0)
+                        : mode == SeqMode::Dz  ? 16 + (wide ? 2 : 0) + (p.softplus ? 1 : 0)
                                                : ((mode == SeqMode::Zoh ? 8 : wide ? 4 : 0) | (p.softplus ? 2 : 0) |
                                                   (p.z ? 1 : 0));
     using Kern = void (*)(ScanParams);
-    static constexpr Kern kernels[16] = {
+    static constexpr Kern kernels[20] = {
         ss::scan_seq<TIn, SC, NSW, TN, false, false, false, false, false>,
         ss::scan_seq<TIn, SC, NSW, TN, false, false, true, false, false>,
         ss::scan_seq<TIn, SC, NSW, TN, false, true, false, false, false>,
@@ -207,8 +220,13 @@ int launch_seq(ScanParams p, SeqMode mode, void* ws, size_t ws_bytes, hipStream_
         ss::scan_seq<TIn, SC, NSW, TN, false, false, false, false, true>,
         ss::scan_seq<TIn, SC, NSW, TN, false, true, false, false, true>,
         ss::scan_seq<TIn, SC, NSW, TW, true, false, false, false, true>,
-        ss::scan_seq<TIn, SC, NSW, TW, true, true, false, false, true>};
+        ss::scan_seq<TIn, SC, NSW, TW, true, true, false, false, true>,
+        dz_kernel<TIn, SC, NSW, TN, false, false>(),
+        dz_kernel<TIn, SC, NSW, TN, false, true>(),
+        dz_kernel<TIn, SC, NSW, TW, true, false>(),
+        dz_kernel<TIn, SC, NSW, TW, true, true>()};
     const Kern kern = kernels[variant];
+    if (!kern) return SS_ERR_UNSUPPORTED;
     const size_t lds = wide ? ss::SeqLds<TW, SC, SC * NSW, sizeof(TIn), true>::bytes
                             : ss::SeqLds<TN, SC, SC * NSW, sizeof(TIn), false>::bytes;
 
@@ -657,7 +675,7 @@ int launch_bwd(BwdParams p, bool gate, hipStream_t st, int* segments) {
     static constexpr Kern kernels[4] = {ss::scan_bwd<TIn, SC, NSW, false, false>, ss::scan_bwd<TIn, SC, NSW, false, true>,
                                         ss::scan_bwd<TIn, SC, NSW, true, false>, ss::scan_bwd<TIn, SC, NSW, true, true>};
     const Kern kern = kernels[(p.softplus ? 2 : 0) | (gate ? 1 : 0)];
-    const size_t lds = gate ? ss::BwdLds<SC, SC * NSW, true>::bytes : ss::BwdLds<SC, SC * NSW, false>::bytes;
+    const size_t lds = ss::BwdLds<SC, SC * NSW>::bytes;
     const int64_t G = p.b * p.nblk_d;
     const int cus = device_cus();
     const int per_cu = resident_per_cu(reinterpret_cast<const void*>(kern), threads, lds);
@@ -766,7 +784,9 @@ SS_EXPORT int ss_scan_bwd(const void* u, const void* delta, const float* A_log, 
     hipStream_t st = static_cast<hipStream_t>(stream);
     const int nblk = int((d_in + 63) / 64);
 
-    // 1. The forward scan again, saving the state every kCkptSteps steps (no y).
+    // 1. The forward scan again, saving the state every kCkptSteps steps.  No
+    //    y; with a gate it writes dz, the one gradient that needs the readout
+    //    sum C h + D u (so the backward pass never recomputes the readout).
     ScanParams f{};
     f.u = u;
     f.delta = delta;
@@ -780,6 +800,8 @@ SS_EXPORT int ss_scan_bwd(const void* u, const void* delta, const float* A_log, 
     f.last_state = nullptr;
     f.h0 = initial_state;
     f.ckpt = ckpt;
+    f.dy = z ? dy : nullptr;
+    f.dz = z ? dz : nullptr;
     f.nck = int((L - 1) / ss::kCkptSteps);
     f.b = b;
     f.L = L;
@@ -789,8 +811,9 @@ SS_EXPORT int ss_scan_bwd(const void* u, const void* delta, const float* A_log, 
     f.nblk_d = nblk;
     f.K = 1;
     f.Lseg = L;
-    int rc = dtype == SS_BF16 ? dispatch_seq<uint16_t>(f, SeqMode::Euler, fwd_ws, w.fwd, st)
-                              : dispatch_seq<float>(f, SeqMode::Euler, fwd_ws, w.fwd, st);
+    const SeqMode fm = z ? SeqMode::Dz : SeqMode::Euler;
+    int rc = dtype == SS_BF16 ? dispatch_seq<uint16_t>(f, fm, fwd_ws, w.fwd, st)
+                              : dispatch_seq<float>(f, fm, fwd_ws, w.fwd, st);
     if (rc != SS_OK) return rc;
 
     // 2. Backward through every chunk.
@@ -809,7 +832,6 @@ SS_EXPORT int ss_scan_bwd(const void* u, const void* delta, const float* A_log, 
     p.ckpt = ckpt;
     p.du = du;
     p.ddelta = ddelta;
-    p.dz = z ? dz : nullptr;
     p.dh0 = dinitial_state;
     p.part_B = part_B;
     p.part_C = part_C;
