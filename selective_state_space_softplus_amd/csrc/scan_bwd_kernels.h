@@ -89,13 +89,19 @@ __device__ __forceinline__ float dpp_take(float v) {
 //   3. prefix sums inside each row of 16 lanes (DPP row_shr 1, 2, 4, 8).
 // Lanes 15, 31, 47, 63 then hold the sums of v0, v2, v1, v3 -- 10 VALU
 // instructions instead of 24 for four separate six-step reductions.
-__device__ __forceinline__ float wave_sum4(float v0, float v1, float v2, float v3) {
+// Steps 1 and 2 alone: rows 0, 1, 2, 3 of the result hold 16 partial sums
+// (over 4 lanes each) of v0, v2, v1, v3.
+__device__ __forceinline__ float wave_part4(float v0, float v1, float v2, float v3) {
     const auto x = __builtin_amdgcn_permlane32_swap(__float_as_uint(v0), __float_as_uint(v1), false, false);
     const auto y = __builtin_amdgcn_permlane32_swap(__float_as_uint(v2), __float_as_uint(v3), false, false);
     const float a = __uint_as_float(x[0]) + __uint_as_float(x[1]);
     const float b = __uint_as_float(y[0]) + __uint_as_float(y[1]);
     const auto z = __builtin_amdgcn_permlane16_swap(__float_as_uint(a), __float_as_uint(b), false, false);
-    float t = __uint_as_float(z[0]) + __uint_as_float(z[1]);
+    return __uint_as_float(z[0]) + __uint_as_float(z[1]);
+}
+
+__device__ __forceinline__ float wave_sum4(float v0, float v1, float v2, float v3) {
+    float t = wave_part4(v0, v1, v2, v3);
     t += dpp_take<0x111, 0xf>(t);
     t += dpp_take<0x112, 0xf>(t);
     t += dpp_take<0x114, 0xf>(t);
@@ -104,14 +110,21 @@ __device__ __forceinline__ float wave_sum4(float v0, float v1, float v2, float v
 }
 
 // LDS of scan_bwd<SC recurrence waves, NP padded states>, T = 8 steps.
+// RL (NP <= 16): the recurrence waves leave the dB, dC sums over the 64
+// channels at 16 partials per (step, state) -- a row of RS floats (16 and 4
+// of padding against bank conflicts) -- and the element waves add them up;
+// above, the sums are finished in the wave (the rows would not fit).
 template <int SC, int NP>
 struct BwdLds {
     static constexpr int T = kCkptSteps;
+    static constexpr bool RL = NP <= 16;
+    static constexpr int RS = 20;
+    static constexpr int ROWS = T * 2 * NP;                   // (step, state, B or C) rows of a chunk
     static constexpr int PREP = T * 64 * 16;                  // (Delta, w, dy', u) per (step, channel)
     static constexpr int PART = SC * T * 64 * 8;              // (S1, S2) per (wave, step, channel)
     static constexpr int CK = NP * 64 * 4;                    // state entering the chunk
     static constexpr int BC = T * 2 * NP * 4;                 // B, C rows as fp32, grouped per wave
-    static constexpr int DBC = T * 2 * NP * 4;                // dB, dC sums of the chunk
+    static constexpr int DBC = RL ? ROWS * RS * 4 : T * 2 * NP * 4;   // dB, dC partial rows, or sums, of the chunk
     static constexpr int off_prep = 0;                        // [3]
     static constexpr int off_part = off_prep + 3 * PREP;      // [2]
     static constexpr int off_ck = off_part + 2 * PART;        // [2]
@@ -140,7 +153,10 @@ __global__ __launch_bounds__((SC + 4) * 64) void scan_bwd(const BwdParams p) {
     float2* s_part = reinterpret_cast<float2*>(lds + Lds::off_part);   // [2][SC][T][64]
     float* s_ck = reinterpret_cast<float*>(lds + Lds::off_ck);         // [2][NP][64]
     float* s_bc = reinterpret_cast<float*>(lds + Lds::off_bc);         // [2][T][SC][2][NSW]
-    float* s_dbc = reinterpret_cast<float*>(lds + Lds::off_dbc);       // [2][T][2][NP]
+    float* s_dbc = reinterpret_cast<float*>(lds + Lds::off_dbc);       // [2][T][2][NP], or [2][ROWS][RS] rows
+    constexpr bool RL = Lds::RL;
+    constexpr int RS = Lds::RS, ROWS = Lds::ROWS;
+    constexpr int RPT = (ROWS + NE - 1) / NE;      // partial rows each element thread adds up per chunk
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -280,6 +296,24 @@ __global__ __launch_bounds__((SC + 4) * 64) void scan_bwd(const BwdParams p) {
     // Element threads that write a dB, dC word of a chunk (T n <= T NP <= NE).
     const int pf_j = etid / max(n, 1), pf_kk = etid - pf_j * max(n, 1);
     const bool pf_has = !rec && etid < T * n;
+    // RL: partial row g = ((j SC + w) NSW/2 + pair) 4 + r of a chunk holds,
+    // for r = 0, 1, 2, 3, dB of state 2 pair, its dC, dB of the next state,
+    // its dC (the row order of wave_part4); element thread etid adds rows
+    // etid, etid + NE, ...
+    int red_j[RPT], red_off[RPT];
+    bool red_c[RPT], red_ok[RPT];
+#pragma unroll
+    for (int m = 0; m < RPT; m++) {
+        const int g = m * NE + etid;
+        const int r = g & 3, pq = (g >> 2) % (NSW / 2), w = (g / (2 * NSW)) % SC, j = g / (2 * NP);
+        const int kk = w * NSW + pq * 2 + (r >> 1);
+        red_ok[m] = RL && !rec && g < ROWS && kk < n;
+        red_c[m] = (r & 1) != 0;
+        red_j[m] = j;
+        red_off[m] = j * n + kk;
+    }
+    // Recurrence lane's place in a partial row group: row lane / 16, column lane % 16.
+    const int red_lane = (lane >> 4) * RS + (lane & 15);
 
     // Uniform bases of chunk k (clamped into the segment, so always inside the tensors).
     auto row_base = [&](int k) __attribute__((always_inline)) {
@@ -391,10 +425,23 @@ __global__ __launch_bounds__((SC + 4) * 64) void scan_bwd(const BwdParams p) {
             }
         }
         // dB, dC of the chunk's rows: T * n consecutive values of each.
-        if (pf_has && k * T + pf_j < L) {
-            const int64_t o = ((int64_t(grp) * p.b + bi) * L + int64_t(k) * T) * n + etid;
-            p.part_B[o] = s_dbc[((s2 * T + pf_j) * 2 + 0) * NP + pf_kk];
-            p.part_C[o] = s_dbc[((s2 * T + pf_j) * 2 + 1) * NP + pf_kk];
+        const int64_t ob = ((int64_t(grp) * p.b + bi) * L + int64_t(k) * T) * n;
+        if constexpr (RL) {
+#pragma unroll
+            for (int m = 0; m < RPT; m++) {
+                if (!red_ok[m] || k * T + red_j[m] >= L) continue;
+                const float4* src = reinterpret_cast<const float4*>(s_dbc + (s2 * ROWS + m * NE + etid) * RS);
+                const float4 a = src[0], b = src[1], c = src[2], e = src[3];
+                float sum = a.x;                   // the 16 partials in row order
+                sum += a.y; sum += a.z; sum += a.w;
+                sum += b.x; sum += b.y; sum += b.z; sum += b.w;
+                sum += c.x; sum += c.y; sum += c.z; sum += c.w;
+                sum += e.x; sum += e.y; sum += e.z; sum += e.w;
+                (red_c[m] ? p.part_C : p.part_B)[ob + red_off[m]] = sum;
+            }
+        } else if (pf_has && k * T + pf_j < L) {
+            p.part_B[ob + etid] = s_dbc[((s2 * T + pf_j) * 2 + 0) * NP + pf_kk];
+            p.part_C[ob + etid] = s_dbc[((s2 * T + pf_j) * 2 + 1) * NP + pf_kk];
         }
     };
     // Recurrence waves, chunk c: recompute its states, then the adjoint back through them.
@@ -433,14 +480,22 @@ __global__ __launch_bounds__((SC + 4) * 64) void scan_bwd(const BwdParams p) {
                 g[q] *= as[j][q];
             }
             s_part[((s2 * SC + wave) * T + j) * 64 + lane] = make_float2(S1, S2);
-            // dB, dC of this step summed over the 64 channels, two states at a time:
-            // lane 15 holds dB[q], 31 dC[q], 47 dB[q + 1], 63 dC[q + 1].
+            // dB, dC of this step over the 64 channels, two states at a time.
+            if constexpr (RL) {
+                // 16 partials each, to LDS for the element waves to add up.
+                float* dst = s_dbc + ((s2 * T + j) * SC + wave) * (NSW / 2) * 4 * RS + red_lane;
 #pragma unroll
-            for (int q = 0; q < NSW; q += 2) {
-                const float sum = wave_sum4(dBv[q], dBv[q + 1], dCv[q], dCv[q + 1]);
-                if ((lane & 15) == 15) {
-                    const int r = lane >> 4;
-                    s_dbc[((s2 * T + j) * 2 + (r & 1)) * NP + n0 + q + (r >> 1)] = sum;
+                for (int q = 0; q < NSW; q += 2)
+                    dst[(q / 2) * 4 * RS] = wave_part4(dBv[q], dBv[q + 1], dCv[q], dCv[q + 1]);
+            } else {
+                // Whole sums: lane 15 holds dB[q], 31 dC[q], 47 dB[q + 1], 63 dC[q + 1].
+#pragma unroll
+                for (int q = 0; q < NSW; q += 2) {
+                    const float sum = wave_sum4(dBv[q], dBv[q + 1], dCv[q], dCv[q + 1]);
+                    if ((lane & 15) == 15) {
+                        const int r = lane >> 4;
+                        s_dbc[((s2 * T + j) * 2 + (r & 1)) * NP + n0 + q + (r >> 1)] = sum;
+                    }
                 }
             }
         }
