@@ -111,20 +111,25 @@ __device__ __forceinline__ float wave_sum4(float v0, float v1, float v2, float v
 
 // LDS of scan_bwd<SC recurrence waves, NP padded states>, T = 8 steps.
 // RL (NP <= 16): the recurrence waves leave the dB, dC sums over the 64
-// channels at 16 partials per (step, state) -- a row of RS floats (16 and 4
-// of padding against bank conflicts) -- and the element waves add them up;
-// above, the sums are finished in the wave (the rows would not fit).
+// channels at 16 partials per (step, state) -- a row of 16 floats -- and the
+// element waves add them up; above, the sums are finished in the wave (the
+// rows would not fit).
 template <int SC, int NP>
 struct BwdLds {
     static constexpr int T = kCkptSteps;
     static constexpr bool RL = NP <= 16;
-    static constexpr int RS = 20;
+    static constexpr int RS = 18;                             // mean floats per row: pairs of rows padded by 4
     static constexpr int ROWS = T * 2 * NP;                   // (step, state, B or C) rows of a chunk
     static constexpr int PREP = T * 64 * 16;                  // (Delta, w, dy', u) per (step, channel)
     static constexpr int PART = SC * T * 64 * 8;              // (S1, S2) per (wave, step, channel)
     static constexpr int CK = NP * 64 * 4;                    // state entering the chunk
     static constexpr int BC = T * 2 * NP * 4;                 // B, C rows as fp32, grouped per wave
     static constexpr int DBC = RL ? ROWS * RS * 4 : T * 2 * NP * 4;   // dB, dC partial rows, or sums, of the chunk
+    // Row g of the partial rows starts at float g 16 + (g / 2) 4: a recurrence
+    // wave's four rows are two contiguous 32-float runs (bank-conflict-free
+    // writes), and 8 consecutive rows start on 8 different 4-bank groups
+    // (conflict-free 16-byte reads of one row per lane).
+    static constexpr int row_off(int g) { return g * 16 + (g >> 1) * 4; }
     static constexpr int off_prep = 0;                        // [3]
     static constexpr int off_part = off_prep + 3 * PREP;      // [2]
     static constexpr int off_ck = off_part + 2 * PART;        // [2]
@@ -156,6 +161,7 @@ __global__ __launch_bounds__((SC + 4) * 64) void scan_bwd(const BwdParams p) {
     float* s_dbc = reinterpret_cast<float*>(lds + Lds::off_dbc);       // [2][T][2][NP], or [2][ROWS][RS] rows
     constexpr bool RL = Lds::RL;
     constexpr int RS = Lds::RS, ROWS = Lds::ROWS;
+    static_assert(Lds::row_off(4) == 4 * RS && ROWS % 4 == 0, "groups of 4 partial rows at 4 RS floats");
     constexpr int RPT = (ROWS + NE - 1) / NE;      // partial rows each element thread adds up per chunk
 
     const int tid = threadIdx.x;
@@ -232,17 +238,19 @@ __global__ __launch_bounds__((SC + 4) * 64) void scan_bwd(const BwdParams p) {
         }
     }
 
-    // Element waves: thread owns step row er of a chunk, channels ech .. ech + V.
+    // Element waves: thread owns step row er of a chunk and channels ec + i TPR
+    // (i < V) of the group, so consecutive lanes take consecutive channels.
     const int etid = rec ? 0 : tid - SC * 64;
     const int er = etid / TPR;
-    const int ec = (etid - er * TPR) * V;
-    const int ech = dbase + ec;
-    const int evalid = rec ? 0 : max(0, min(V, d_in - ech));
+    const int ec = etid - er * TPR;
+    bool evok[V];
+#pragma unroll
+    for (int i = 0; i < V; i++) evok[i] = !rec && dbase + ec + i * TPR < d_in;
     float Dv[V], bias_v[V], accD[V], accBias[V];
 #pragma unroll
     for (int i = 0; i < V; i++) {
-        Dv[i] = i < evalid ? p.D[ech + i] : 0.0f;
-        bias_v[i] = (i < evalid && p.bias) ? p.bias[ech + i] : 0.0f;
+        Dv[i] = evok[i] ? p.D[dbase + ec + i * TPR] : 0.0f;
+        bias_v[i] = (evok[i] && p.bias) ? p.bias[dbase + ec + i * TPR] : 0.0f;
         accD[i] = accBias[i] = 0.0f;
     }
 
@@ -270,9 +278,9 @@ __global__ __launch_bounds__((SC + 4) * 64) void scan_bwd(const BwdParams p) {
 
     // Per-thread parts of the element, B/C and entering-state addresses, and
     // which of them exist whatever the chunk.
-    uint32_t off_row[V];                           // (er, ech + i) from (chunk row 0, dbase)
+    uint32_t off_row[V];                           // (er, dbase + ec + i TPR) from (chunk row 0, dbase)
 #pragma unroll
-    for (int i = 0; i < V; i++) off_row[i] = i < evalid ? uint32_t(er * d_in + ec + i) * uint32_t(ES) : 0u;
+    for (int i = 0; i < V; i++) off_row[i] = evok[i] ? uint32_t(er * d_in + ec + i * TPR) * uint32_t(ES) : 0u;
     int bc_row[EBC];                               // step row j of the B/C word, -1 if none
     uint32_t off_bc[EBC];                          // (j, kk) from (chunk row 0, state 0)
 #pragma unroll
@@ -312,8 +320,8 @@ __global__ __launch_bounds__((SC + 4) * 64) void scan_bwd(const BwdParams p) {
         red_j[m] = j;
         red_off[m] = j * n + kk;
     }
-    // Recurrence lane's place in a partial row group: row lane / 16, column lane % 16.
-    const int red_lane = (lane >> 4) * RS + (lane & 15);
+    // Recurrence lane's place in a group of 4 partial rows: row lane / 16, column lane % 16.
+    const int red_lane = lane + (lane >> 5) * 4;
 
     // Uniform bases of chunk k (clamped into the segment, so always inside the tensors).
     auto row_base = [&](int k) __attribute__((always_inline)) {
@@ -362,14 +370,14 @@ __global__ __launch_bounds__((SC + 4) * 64) void scan_bwd(const BwdParams p) {
         const bool rv = row_ok(k);
 #pragma unroll
         for (int i = 0; i < V; i++) {
-            const bool ok = rv && i < evalid;
+            const bool ok = rv && evok[i];
             const float u = ok ? RawIn::f(r.u[i]) : 0.0f;
             const float x = (ok ? RawIn::f(r.dl[i]) : 0.0f) + bias_v[i];
             const float z = (GATE && ok) ? RawIn::f(r.z[i]) : 0.0f;
             const float dy = ok ? RawIn::f(r.dy[i]) : 0.0f;
             const float dl = ok ? (SP ? softplus(x) : x) : 0.0f;
             const float dyp = GATE ? dy * silu(z) : dy;
-            s_prep[(s3 * T + er) * 64 + ec + i] = make_float4(dl, dl * u, dyp, u);
+            s_prep[(s3 * T + er) * 64 + ec + i * TPR] = make_float4(dl, dl * u, dyp, u);
             kp.x[i] = x;
         }
 #pragma unroll
@@ -400,10 +408,10 @@ __global__ __launch_bounds__((SC + 4) * 64) void scan_bwd(const BwdParams p) {
 #pragma unroll
         for (int w = 0; w < SC; w++)
 #pragma unroll
-            for (int i = 0; i < V; i++) q[w][i] = pp[w * T * 64 + i];
+            for (int i = 0; i < V; i++) q[w][i] = pp[w * T * 64 + i * TPR];
 #pragma unroll
         for (int i = 0; i < V; i++) {
-            const float4 pr = s_prep[(s3 * T + er) * 64 + ec + i];    // (Delta, w, dy', u)
+            const float4 pr = s_prep[(s3 * T + er) * 64 + ec + i * TPR];    // (Delta, w, dy', u)
             float S1 = q[0][i].x, S2 = q[0][i].y;
 #pragma unroll
             for (int w = 1; w < SC; w++) {
@@ -413,7 +421,7 @@ __global__ __launch_bounds__((SC + 4) * 64) void scan_bwd(const BwdParams p) {
             const float dDelta = fmaf(pr.w, S1, S2);
             const float ddl = SP ? dDelta * rcp_hw(1.0f + exp2_hw(-kp.x[i] * kLog2e)) : dDelta;
             const float du = fmaf(pr.x, S1, pr.z * Dv[i]);
-            if (rv && i < evalid) {
+            if (rv && evok[i]) {
                 auto st = [&](void* base, float v) __attribute__((always_inline)) {
                     TIn* q = static_cast<TIn*>(base) + rb;
                     Elem<TIn>::store(reinterpret_cast<TIn*>(reinterpret_cast<char*>(q) + off_row[i]), 0, v);
@@ -430,7 +438,7 @@ __global__ __launch_bounds__((SC + 4) * 64) void scan_bwd(const BwdParams p) {
 #pragma unroll
             for (int m = 0; m < RPT; m++) {
                 if (!red_ok[m] || k * T + red_j[m] >= L) continue;
-                const float4* src = reinterpret_cast<const float4*>(s_dbc + (s2 * ROWS + m * NE + etid) * RS);
+                const float4* src = reinterpret_cast<const float4*>(s_dbc + Lds::row_off(s2 * ROWS + m * NE + etid));
                 const float4 a = src[0], b = src[1], c = src[2], e = src[3];
                 float sum = a.x;                   // the 16 partials in row order
                 sum += a.y; sum += a.z; sum += a.w;
@@ -573,8 +581,8 @@ __global__ __launch_bounds__((SC + 4) * 64) void scan_bwd(const BwdParams p) {
         float* s_red = reinterpret_cast<float*>(lds + Lds::off_prep);   // [T][64][2]
 #pragma unroll
         for (int i = 0; i < V; i++) {
-            s_red[(er * 64 + ec + i) * 2] = accD[i];
-            s_red[(er * 64 + ec + i) * 2 + 1] = accBias[i];
+            s_red[(er * 64 + ec + i * TPR) * 2] = accD[i];
+            s_red[(er * 64 + ec + i * TPR) * 2 + 1] = accBias[i];
         }
         barrier_lds();
         if (etid < 64 && dbase + etid < d_in) {
