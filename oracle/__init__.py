@@ -62,6 +62,8 @@ def _bind(lib: ctypes.CDLL) -> ctypes.CDLL:
     lib.ss_oracle_state_update_ex.argtypes = [P] * 9 + [ctypes.c_int, ctypes.c_int, P, I64, I64, I64]
     lib.ss_oracle_scan_bwd.restype = ctypes.c_int
     lib.ss_oracle_scan_bwd.argtypes = [P] * 8 + [ctypes.c_int] + [P] * 12 + [I64, I64, I64, I64]
+    lib.ss_oracle_scan_bwd_ex.restype = ctypes.c_int
+    lib.ss_oracle_scan_bwd_ex.argtypes = [P] * 8 + [ctypes.c_int, P, ctypes.c_int] + [P] * 11 + [I64, I64, I64, I64]
     lib.ss_oracle_cross_scan.restype = ctypes.c_int
     lib.ss_oracle_cross_scan.argtypes = [P] * 7 + [ctypes.c_int, P, P, I64, I64, I64, I64, I64]
     lib.ss_oracle_conv_update.restype = ctypes.c_int
@@ -200,8 +202,9 @@ def cross_scan(x, delta, A_log, B, C, D, delta_bias=None, delta_softplus=True, l
 
 
 def scan_bwd(u, delta, A_log, B, C, D, z=None, delta_bias=None, delta_softplus=True, h0=None, dy=None, dlast=None,
-             lib=None):
-    """Gradients of the scan (Euler input term) for output gradients dy (b, L, d_in) and dlast (b, d_in, n).
+             lib=None, zoh=False):
+    """Gradients of the scan for output gradients dy (b, L, d_in) and dlast (b, d_in, n); zoh: the
+    zero-order-hold input term instead of Euler.
 
     Returns a dict of float64 arrays: du, ddelta, dA_log, dB, dC, dD, and dz, ddelta_bias, dh0 when z,
     delta_bias, h0 are given.
@@ -220,8 +223,9 @@ def scan_bwd(u, delta, A_log, B, C, D, z=None, delta_bias=None, delta_softplus=T
         out["ddelta_bias"] = np.empty(d_in)
     if h0 is not None:
         out["dh0"] = np.empty((b, d_in, n))
-    rc = lib.ss_oracle_scan_bwd(_ptr(u), _ptr(delta), _ptr(A_log), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
-                                _ptr(delta_bias), int(bool(delta_softplus)), _ptr(h0), _ptr(dy), _ptr(dlast),
+    rc = lib.ss_oracle_scan_bwd_ex(_ptr(u), _ptr(delta), _ptr(A_log), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
+                                _ptr(delta_bias), int(bool(delta_softplus)), _ptr(h0), int(bool(zoh)), _ptr(dy),
+                                _ptr(dlast),
                                 _ptr(out["du"]), _ptr(out["ddelta"]), _ptr(out["dA_log"]), _ptr(out["dB"]),
                                 _ptr(out["dC"]), _ptr(out["dD"]), _ptr(out.get("dz")), _ptr(out.get("ddelta_bias")),
                                 _ptr(out.get("dh0")), b, L, d_in, n)

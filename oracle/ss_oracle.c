@@ -31,8 +31,9 @@
  * torch): a rolling window of the last W inputs per channel, a depthwise dot
  * product with the channel's W weights, the bias, then silu.
  *
- * ss_oracle_scan_bwd is the gradient of ss_oracle_scan_ex (Euler input term)
- * with respect to every input, for a given gradient of y and of last_state.
+ * ss_oracle_scan_bwd_ex is the gradient of ss_oracle_scan_ex (Euler or
+ * zero-order-hold input term) with respect to every input, for a given
+ * gradient of y and of last_state; ss_oracle_scan_bwd is its Euler form.
  * The pages only name the autograd wrappers, so the formulas are derived
  * here by the chain rule and written out step by step below; they are pinned
  * to torch autograd and to finite differences of the forward.
@@ -300,28 +301,32 @@ int ss_oracle_cross_scan(const double *x, const double *delta, const double *A_l
     return rc;
 }
 
-/* Gradient of the scan (Euler input term, optional h0) for given dy (b, L,
- * d_in) and dlast (b, d_in, n, or NULL for zero).  Per (b, d) channel, with
- * w_t = Delta_t u_t, a_tk = exp(Delta_t A_k), the pre-gate output
- * y'_t = sum_k C_tk h_tk + D u_t and y_t = y'_t silu(z_t):
+/* Gradient of the scan (optional h0) for given dy (b, L, d_in) and dlast
+ * (b, d_in, n, or NULL for zero).  Per (b, d) channel, with
+ * a_tk = exp(Delta_t A_k), the input weight beta_tk (B-bar = beta B:
+ * Euler beta = Delta, zero-order hold beta = (exp(Delta A) - 1)/A, mhpn.cn
+ * page sections 3.2 and 6), h_tk = a_tk h_(t-1)k + beta_tk B_tk u_t, the
+ * pre-gate output y'_t = sum_k C_tk h_tk + D u_t and y_t = y'_t silu(z_t):
  *   dz_t    = dy_t y'_t silu'(z_t),  dy'_t = dy_t silu(z_t)     (dy'_t = dy_t without z)
  *   g_tk    = dL/dh_tk = dy'_t C_tk + a_(t+1)k g_(t+1)k,  g_(L)k = dlast_k
- *   du_t    = dy'_t D + sum_k g_tk Delta_t B_tk
- *   dDelta_t= sum_k g_tk (A_k a_tk h_(t-1)k + B_tk u_t)
+ *   du_t    = dy'_t D + sum_k g_tk beta_tk B_tk
+ *   dDelta_t= sum_k g_tk (A_k a_tk h_(t-1)k + dbeta/dDelta B_tk u_t)
+ *             (dbeta/dDelta = 1 for Euler, a_tk for the hold)
  *   ddelta_t= dDelta_t softplus'(delta_t + bias) = dDelta_t sigmoid(delta_t + bias)  (dDelta_t without softplus)
- *   dB_tk  += sum_d g_tk Delta_t u_t,   dC_tk += sum_d dy'_t h_tk
- *   dA_log_dk += sum_(b,t) g_tk Delta_t a_tk h_(t-1)k A_k       (dA/dA_log = A)
+ *   dB_tk  += sum_d g_tk beta_tk u_t,   dC_tk += sum_d dy'_t h_tk
+ *   dA_log_dk += sum_(b,t) g_tk (Delta_t a_tk h_(t-1)k + dbeta/dA B_tk u_t) A_k   (dA/dA_log = A;
+ *             dbeta/dA = 0 for Euler, (Delta a_tk - beta_tk)/A_k for the hold)
  *   dD_d   += sum_(b,t) dy'_t u_t,      dbias_d += sum_(b,t) ddelta_t
  *   dh0_k   = a_0k g_0k
  * Outputs are overwritten (the sums start from zero); dz, ddelta_bias and
  * dh0 may be NULL when z, the bias or h0 are absent. */
-int ss_oracle_scan_bwd(const double *u, const double *delta, const double *A_log,
-                       const double *B, const double *C, const double *D,
-                       const double *z, const double *delta_bias, int delta_softplus,
-                       const double *h0, const double *dy, const double *dlast,
-                       double *du, double *ddelta, double *dA_log, double *dB, double *dC,
-                       double *dD, double *dz, double *ddelta_bias, double *dh0,
-                       int64_t b, int64_t L, int64_t d_in, int64_t n)
+int ss_oracle_scan_bwd_ex(const double *u, const double *delta, const double *A_log,
+                          const double *B, const double *C, const double *D,
+                          const double *z, const double *delta_bias, int delta_softplus,
+                          const double *h0, int zoh, const double *dy, const double *dlast,
+                          double *du, double *ddelta, double *dA_log, double *dB, double *dC,
+                          double *dD, double *dz, double *ddelta_bias, double *dh0,
+                          int64_t b, int64_t L, int64_t d_in, int64_t n)
 {
     if (!u || !delta || !A_log || !B || !C || !D || !dy || !du || !ddelta || !dA_log || !dB || !dC || !dD)
         return -1;
@@ -356,7 +361,7 @@ int ss_oracle_scan_bwd(const double *u, const double *delta, const double *A_log
                 int64_t e = (bi * L + t) * d_in + d, r = (bi * L + t) * n;
                 double dl = step_size(delta[e], delta_bias, d, delta_softplus);
                 for (int64_t k = 0; k < n; k++)
-                    hs[(t + 1) * n + k] = exp(dl * A[k]) * hs[t * n + k] + dl * B[r + k] * u[e];
+                    hs[(t + 1) * n + k] = exp(dl * A[k]) * hs[t * n + k] + input_weight(dl, A[k], B[r + k], zoh) * u[e];
             }
             /* backward in time */
             for (int64_t k = 0; k < n; k++)
@@ -381,12 +386,16 @@ int ss_oracle_scan_bwd(const double *u, const double *delta, const double *A_log
                 for (int64_t k = 0; k < n; k++) {
                     double a = exp(dl * A[k]);
                     double hprev = hs[t * n + k];
+                    /* the input weight and its derivatives in Delta and in A */
+                    double beta = zoh ? expm1(dl * A[k]) / A[k] : dl;
+                    double dbeta_ddl = zoh ? a : 1.0;
+                    double dbeta_dA = zoh ? (dl * a - beta) / A[k] : 0.0;
                     g[k] += dyp * C[r + k];                   /* dL/dh_tk */
                     dC[r + k] += dyp * hs[(t + 1) * n + k];
-                    dB[r + k] += g[k] * dl * u[e];
-                    dut += g[k] * dl * B[r + k];
-                    ddl += g[k] * (A[k] * a * hprev + B[r + k] * u[e]);
-                    dA_log[d * n + k] += g[k] * dl * a * hprev * A[k];
+                    dB[r + k] += g[k] * beta * u[e];
+                    dut += g[k] * beta * B[r + k];
+                    ddl += g[k] * (A[k] * a * hprev + dbeta_ddl * B[r + k] * u[e]);
+                    dA_log[d * n + k] += g[k] * (dl * a * hprev + dbeta_dA * B[r + k] * u[e]) * A[k];
                     g[k] *= a;                                /* on to h_(t-1) */
                 }
                 du[e] = dut;
@@ -404,4 +413,16 @@ int ss_oracle_scan_bwd(const double *u, const double *delta, const double *A_log
     free(g);
     free(A);
     return 0;
+}
+
+int ss_oracle_scan_bwd(const double *u, const double *delta, const double *A_log,
+                       const double *B, const double *C, const double *D,
+                       const double *z, const double *delta_bias, int delta_softplus,
+                       const double *h0, const double *dy, const double *dlast,
+                       double *du, double *ddelta, double *dA_log, double *dB, double *dC,
+                       double *dD, double *dz, double *ddelta_bias, double *dh0,
+                       int64_t b, int64_t L, int64_t d_in, int64_t n)
+{
+    return ss_oracle_scan_bwd_ex(u, delta, A_log, B, C, D, z, delta_bias, delta_softplus, h0, 0, dy, dlast,
+                                 du, ddelta, dA_log, dB, dC, dD, dz, ddelta_bias, dh0, b, L, d_in, n);
 }

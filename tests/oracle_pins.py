@@ -431,8 +431,9 @@ def pin_cross_scan(lib):
     _close(y, c["x"] * c["D"].sum(0), rtol=1e-13, atol=1e-14, what="cross scan with B = 0")
 
 
-def _torch_scan_loss(c, dy, dlast, softplus=True):
-    """The scan written with torch float64 operations, and <y, dy> + <last state, dlast>."""
+def _torch_scan_loss(c, dy, dlast, softplus=True, zoh=False):
+    """The scan written with torch float64 operations, and <y, dy> + <last state, dlast>; zoh: the input
+    weight (exp(delta A) - 1)/A of the zero-order hold in place of Euler's delta."""
     import torch
 
     u, delta, A_log, B, C, D = (c[k] for k in ("u", "delta", "A_log", "B", "C", "D"))
@@ -443,7 +444,10 @@ def _torch_scan_loss(c, dy, dlast, softplus=True):
     for t in range(L):
         x = delta[:, t] + (c["delta_bias"] if c.get("delta_bias") is not None else 0.0)
         dl = torch.nn.functional.softplus(x) if softplus else x
-        h = torch.exp(dl[..., None] * A) * h + (dl * u[:, t])[..., None] * B[:, t, None, :]
+        if zoh:
+            h = torch.exp(dl[..., None] * A) * h + torch.expm1(dl[..., None] * A) / A * (u[:, t, :, None] * B[:, t, None, :])
+        else:
+            h = torch.exp(dl[..., None] * A) * h + (dl * u[:, t])[..., None] * B[:, t, None, :]
         y = (h * C[:, t, None, :]).sum(-1) + D * u[:, t]
         if c.get("z") is not None:
             y = y * torch.nn.functional.silu(c["z"][:, t])
@@ -454,16 +458,20 @@ def _torch_scan_loss(c, dy, dlast, softplus=True):
 
 
 def pin_scan_bwd(lib):
-    """Gradients of the scan (Euler input term): torch autograd of the scan written with torch ops, and
-    central finite differences of the oracle's own forward along random directions."""
+    """Gradients of the scan (Euler and zero-order-hold input terms): torch autograd of the scan written
+    with torch ops, and central finite differences of the oracle's own forward along random directions."""
     import torch
 
     names = ("u", "delta", "A_log", "B", "C", "D", "z", "delta_bias", "h0")
     grad_of = dict(u="du", delta="ddelta", A_log="dA_log", B="dB", C="dC", D="dD", z="dz", delta_bias="ddelta_bias",
                    h0="dh0")
-    for seed, kw, with_h0, with_dlast, sp in ((50, dict(), True, True, True), (51, dict(n=1, gated=False), False, True, True),
-                                              (52, dict(bias=False, n=3), True, False, True),
-                                              (53, dict(softplus=False, L=6), False, False, False)):
+    for seed, kw, with_h0, with_dlast, sp, zoh in ((50, dict(), True, True, True, False),
+                                                   (51, dict(n=1, gated=False), False, True, True, False),
+                                                   (52, dict(bias=False, n=3), True, False, True, False),
+                                                   (53, dict(softplus=False, L=6), False, False, False, False),
+                                                   (54, dict(), True, True, True, True),
+                                                   (55, dict(n=2, gated=False, bias=False), False, True, True, True),
+                                                   (56, dict(softplus=False, L=7), True, False, False, True)):
         c = random_case(seed, **kw)
         if not sp:
             c["delta"] = np.abs(c["delta"]) * 0.3 + 0.05
@@ -474,18 +482,18 @@ def pin_scan_bwd(lib):
         dy = r.standard_normal((b, L, d_in))
         dlast = r.standard_normal((b, d_in, n)) if with_dlast else None
         got = oracle.scan_bwd(c["u"], c["delta"], c["A_log"], c["B"], c["C"], c["D"], c["z"], c["delta_bias"], sp,
-                              c["h0"], dy, dlast, lib=lib)
+                              c["h0"], dy, dlast, lib=lib, zoh=zoh)
         tc = {k: (None if c.get(k) is None else torch.tensor(c[k], dtype=torch.float64, requires_grad=True))
               for k in names}
-        loss = _torch_scan_loss(tc, torch.tensor(dy), None if dlast is None else torch.tensor(dlast), sp)
+        loss = _torch_scan_loss(tc, torch.tensor(dy), None if dlast is None else torch.tensor(dlast), sp, zoh)
         loss.backward()
         for k in names:
             if tc[k] is not None:
-                _close(got[grad_of[k]], tc[k].grad.numpy(), rtol=1e-10, atol=1e-11, what=f"d{k} vs autograd {kw}")
+                _close(got[grad_of[k]], tc[k].grad.numpy(), rtol=1e-10, atol=1e-11, what=f"d{k} vs autograd {kw} zoh={zoh}")
         # finite differences: <grad, v> = (L(x + e v) - L(x - e v)) / 2e
         def loss_at(cc):
             y, last = oracle.scan(cc["u"], cc["delta"], cc["A_log"], cc["B"], cc["C"], cc["D"], cc["z"],
-                                  cc["delta_bias"], sp, lib=lib, h0=cc["h0"])
+                                  cc["delta_bias"], sp, lib=lib, h0=cc["h0"], zoh=zoh)
             return float((y * dy).sum() + ((last * dlast).sum() if dlast is not None else 0.0))
         for j in range(3):
             v = {k: (None if c.get(k) is None else r.standard_normal(np.shape(c[k]))) for k in names}
@@ -494,7 +502,7 @@ def pin_scan_bwd(lib):
             minus = {k: (None if c.get(k) is None else c[k] - eps * v[k]) for k in names}
             fd = (loss_at(plus) - loss_at(minus)) / (2 * eps)
             an = sum(float((got[grad_of[k]] * v[k]).sum()) for k in names if c.get(k) is not None)
-            assert abs(fd - an) <= 1e-6 * (1 + abs(an)), f"finite differences {kw}: {fd} vs {an}"
+            assert abs(fd - an) <= 1e-6 * (1 + abs(an)), f"finite differences {kw} zoh={zoh}: {fd} vs {an}"
 
 
 def pin_einsum_transcription(lib):

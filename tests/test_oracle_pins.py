@@ -99,12 +99,23 @@ MUTANTS = [
     ("bwd adjoint not decayed", "g[k] *= a;                                /* on to h_(t-1) */", "(void)a;"),
     ("bwd adjoint misses the readout", "g[k] += dyp * C[r + k];                   /* dL/dh_tk */", "g[k] += 0.0 * C[r + k];"),
     ("bwd dC from the previous state", "dC[r + k] += dyp * hs[(t + 1) * n + k];", "dC[r + k] += dyp * hs[t * n + k];"),
-    ("bwd dB without delta", "dB[r + k] += g[k] * dl * u[e];", "dB[r + k] += g[k] * u[e];"),
+    ("bwd dB without delta", "dB[r + k] += g[k] * beta * u[e];", "dB[r + k] += g[k] * u[e];"),
+    ("bwd du without the input weight", "dut += g[k] * beta * B[r + k];", "dut += g[k] * B[r + k];"),
+    ("bwd zoh weight taken as Euler", "double beta = zoh ? expm1(dl * A[k]) / A[k] : dl;", "double beta = dl;"),
+    ("bwd zoh dDelta input term without the decay", "double dbeta_ddl = zoh ? a : 1.0;", "double dbeta_ddl = 1.0;"),
+    ("bwd zoh dA_log misses the weight's term", "double dbeta_dA = zoh ? (dl * a - beta) / A[k] : 0.0;",
+     "double dbeta_dA = 0.0;"),
+    ("bwd zoh weight derivative sign", "double dbeta_dA = zoh ? (dl * a - beta) / A[k] : 0.0;",
+     "double dbeta_dA = zoh ? (beta - dl * a) / A[k] : 0.0;"),
+    ("bwd zoh forward recomputed with Euler", "hs[t * n + k] + input_weight(dl, A[k], B[r + k], zoh) * u[e];",
+     "hs[t * n + k] + input_weight(dl, A[k], B[r + k], 0) * u[e];"),
     ("bwd du without the skip", "double dut = dyp * D[d];", "double dut = 0.0;"),
-    ("bwd dDelta without the decay term", "ddl += g[k] * (A[k] * a * hprev + B[r + k] * u[e]);", "ddl += g[k] * B[r + k] * u[e];"),
-    ("bwd dDelta uses the new state", "ddl += g[k] * (A[k] * a * hprev + B[r + k] * u[e]);",
-     "ddl += g[k] * (A[k] * a * hs[(t + 1) * n + k] + B[r + k] * u[e]);"),
-    ("bwd dA_log without A", "dA_log[d * n + k] += g[k] * dl * a * hprev * A[k];", "dA_log[d * n + k] += g[k] * dl * a * hprev;"),
+    ("bwd dDelta without the decay term", "ddl += g[k] * (A[k] * a * hprev + dbeta_ddl * B[r + k] * u[e]);",
+     "ddl += g[k] * dbeta_ddl * B[r + k] * u[e];"),
+    ("bwd dDelta uses the new state", "ddl += g[k] * (A[k] * a * hprev + dbeta_ddl * B[r + k] * u[e]);",
+     "ddl += g[k] * (A[k] * a * hs[(t + 1) * n + k] + dbeta_ddl * B[r + k] * u[e]);"),
+    ("bwd dA_log without A", "dA_log[d * n + k] += g[k] * (dl * a * hprev + dbeta_dA * B[r + k] * u[e]) * A[k];",
+     "dA_log[d * n + k] += g[k] * (dl * a * hprev + dbeta_dA * B[r + k] * u[e]);"),
     ("bwd softplus derivative", "double dd = delta_softplus ? ddl / (1.0 + exp(-x)) : ddl;",
      "double dd = delta_softplus ? ddl / (1.0 + exp(x)) : ddl;"),
     ("bwd dz without y'", "dz[e] = dy[e] * yp * sg * (1.0 + z[e] * (1.0 - sg));", "dz[e] = dy[e] * sg * (1.0 + z[e] * (1.0 - sg));"),
