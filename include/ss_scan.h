@@ -260,6 +260,25 @@ int ss_scan_bwd(const void *u, const void *delta, const float *A_log,
                 int64_t b, int64_t L, int64_t d_in, int64_t n, int dtype,
                 void *workspace, size_t workspace_bytes, void *stream);
 
+/*
+ * ss_scan_bwd for either input term of ss_scan_fwd_ex: discretization is
+ * SS_DISC_EULER (the same as ss_scan_bwd) or SS_DISC_ZOH, the gradient of the
+ * zero-order-hold scan with input weight beta = (exp(delta' A) - 1) / A
+ * (mhpn.cn page, section 6), whose derivatives are exp(delta' A) in delta'
+ * and (delta' exp(delta' A) - beta) / A in A.  Arguments, workspace and
+ * results otherwise as for ss_scan_bwd; another discretization value is
+ * SS_ERR_MODE.
+ */
+int ss_scan_bwd_ex(const void *u, const void *delta, const float *A_log,
+                   const void *B, const void *C, const float *D,
+                   const void *z, const float *delta_bias, int delta_softplus,
+                   const float *initial_state, int discretization,
+                   const void *dy, const float *dlast_state,
+                   void *du, void *ddelta, float *dA_log, void *dB, void *dC,
+                   float *dD, void *dz, float *ddelta_bias, float *dinitial_state,
+                   int64_t b, int64_t L, int64_t d_in, int64_t n, int dtype,
+                   void *workspace, size_t workspace_bytes, void *stream);
+
 /* Largest convolution width W of ss_conv_update. */
 #define SS_MAX_CONV_WIDTH 8
 

@@ -14,9 +14,9 @@ Entry points mirror the C ABI (``include/ss_scan.h``):
   state_update(state, x, dt, A_log, B, C, D, z=None, dt_bias=None, dt_softplus=True,
                zoh=False)                    -> y  (state is updated in place)
   scan_bwd(u, delta, A_log, B, C, D, dy, z=None, delta_bias=None, delta_softplus=True,
-           initial_state=None, dlast_state=None)  -> dict of gradients
+           initial_state=None, dlast_state=None, zoh=False)  -> dict of gradients
   selective_scan(u, delta, A_log, B, C, D, z=None, delta_bias=None, delta_softplus=True,
-                 initial_state=None)          -> y, differentiable (torch.autograd.Function
+                 initial_state=None, zoh=False) -> y, differentiable (torch.autograd.Function
                                                  calling scan_fwd / scan_bwd)
   cross_scan_fwd(x, delta, A_log, B, C, D, delta_bias=None, delta_softplus=True,
                  return_last_state=False)    -> y (maps, H, W, d_in) fp32  or  (y, last_state)
@@ -31,7 +31,8 @@ The step follows jiafeimiao.top's Mamba.step / selective_state_update call:
 state (b, d_in, n) fp32 updated in place; x, dt, z (b, d_in); B, C (b, n).
 ``initial_state`` (b, d_in, n) fp32 starts the scan from a given state and
 ``zoh=True`` selects the zero-order-hold input term (mhpn.cn, section 6); calls
-that use either go through ``ss_scan_fwd_ex`` / ``ss_state_update_ex``.
+that use either go through ``ss_scan_fwd_ex`` / ``ss_state_update_ex`` (``ss_scan_bwd_ex`` for the
+gradient of a zero-order-hold scan).
 ``cross_scan_fwd`` is VMamba's CrossScan + scan + CrossMerge in one pass (githubissues.com
 VMamba #206): x (maps, H, W, d_in); delta (maps, 4, H*W, d_in); B, C (maps, 4, H*W, n);
 A_log (4, d_in, n); D, delta_bias (4, d_in); directions 0 row-major, 1 column-major,
@@ -59,8 +60,8 @@ SS_DISC_ZOH = 1
 STATUS = {0: "SS_OK", -1: "SS_ERR_NULL", -2: "SS_ERR_SHAPE", -3: "SS_ERR_DTYPE", -4: "SS_ERR_UNSUPPORTED",
           -5: "SS_ERR_WORKSPACE", -6: "SS_ERR_HIP", -7: "SS_ERR_ALIAS", -8: "SS_ERR_ALIGN", -9: "SS_ERR_MODE"}
 EXPORTS = ("ss_scan_fwd_workspace_bytes", "ss_scan_fwd", "ss_scan_fwd_ex", "ss_state_update", "ss_state_update_ex",
-           "ss_scan_bwd", "ss_scan_bwd_workspace_bytes", "ss_cross_scan_fwd", "ss_cross_scan_fwd_workspace_bytes",
-           "ss_conv_update", "ss_status_string")
+           "ss_scan_bwd", "ss_scan_bwd_ex", "ss_scan_bwd_workspace_bytes", "ss_cross_scan_fwd",
+           "ss_cross_scan_fwd_workspace_bytes", "ss_conv_update", "ss_status_string")
 
 
 class SSError(RuntimeError):
@@ -89,6 +90,8 @@ def _load() -> ctypes.CDLL:
     lib.ss_scan_bwd_workspace_bytes.argtypes = [I64, I64, I64, I64, I]
     lib.ss_scan_bwd.restype = I
     lib.ss_scan_bwd.argtypes = [P] * 8 + [I] + [P] * 12 + [I64, I64, I64, I64, I, P, ctypes.c_size_t, P]
+    lib.ss_scan_bwd_ex.restype = I
+    lib.ss_scan_bwd_ex.argtypes = [P] * 8 + [I, P, I] + [P] * 11 + [I64, I64, I64, I64, I, P, ctypes.c_size_t, P]
     lib.ss_cross_scan_fwd_workspace_bytes.restype = ctypes.c_size_t
     lib.ss_cross_scan_fwd_workspace_bytes.argtypes = [I64, I64, I64, I64, I64, I]
     lib.ss_cross_scan_fwd.restype = I
@@ -313,8 +316,9 @@ def cross_scan_fwd(x, delta, A_log, B, C, D, delta_bias=None, delta_softplus=Tru
 
 
 def scan_bwd(u, delta, A_log, B, C, D, dy, z=None, delta_bias=None, delta_softplus=True, initial_state=None,
-             dlast_state=None, workspace=None):
-    """Gradients of the scan (delta' B u input term) for output gradients dy (and dlast_state).
+             dlast_state=None, workspace=None, zoh=False):
+    """Gradients of the scan for output gradients dy (and dlast_state): the delta' B u input term, or
+    with zoh=True the zero-order hold's (ss_scan_bwd_ex).
 
     Returns a dict: du, ddelta, dz (dtype of u; dz only with z), dA_log, dD, ddelta_bias (fp32; only
     with delta_bias), dB, dC (dtype of u), dinitial_state (fp32; only with initial_state).
@@ -354,35 +358,42 @@ def scan_bwd(u, delta, A_log, B, C, D, dy, z=None, delta_bias=None, delta_softpl
         workspace = torch.empty(need, dtype=torch.uint8, device=dev) if need else None
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     with torch.cuda.device(dev):
-        rc = lib.ss_scan_bwd(_ptr(u), _ptr(delta), _ptr(A_log), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(delta_bias),
-                             int(bool(delta_softplus)), _ptr(initial_state), _ptr(dy), _ptr(dlast_state),
-                             _ptr(g["du"]), _ptr(g["ddelta"]), _ptr(g["dA_log"]), _ptr(g["dB"]), _ptr(g["dC"]),
-                             _ptr(g["dD"]), _ptr(g.get("dz")), _ptr(g.get("ddelta_bias")),
-                             _ptr(g.get("dinitial_state")), b, L, d_in, n, code, _ptr(workspace), ws_bytes,
-                             _stream(dev))
+        head = (_ptr(u), _ptr(delta), _ptr(A_log), _ptr(B), _ptr(C), _ptr(D), _ptr(z), _ptr(delta_bias),
+                int(bool(delta_softplus)), _ptr(initial_state))
+        tail = (_ptr(dy), _ptr(dlast_state), _ptr(g["du"]), _ptr(g["ddelta"]), _ptr(g["dA_log"]), _ptr(g["dB"]),
+                _ptr(g["dC"]), _ptr(g["dD"]), _ptr(g.get("dz")), _ptr(g.get("ddelta_bias")),
+                _ptr(g.get("dinitial_state")), b, L, d_in, n, code, _ptr(workspace), ws_bytes, _stream(dev))
+        if zoh:
+            rc = lib.ss_scan_bwd_ex(*head, SS_DISC_ZOH, *tail)
+        else:
+            rc = lib.ss_scan_bwd(*head, *tail)
     if rc != 0:
-        raise SSError(rc, "ss_scan_bwd")
+        raise SSError(rc, "ss_scan_bwd_ex" if zoh else "ss_scan_bwd")
     return g
 
 
 class _SelectiveScan(torch.autograd.Function):
-    """The scan as an autograd function: forward ss_scan_fwd(_ex), backward ss_scan_bwd."""
+    """The scan as an autograd function: forward ss_scan_fwd(_ex), backward ss_scan_bwd(_ex)."""
 
     @staticmethod
-    def forward(ctx, u, delta, A_log, B, C, D, z, delta_bias, delta_softplus, initial_state):
-        y = scan_fwd(u, delta, A_log, B, C, D, z, delta_bias, delta_softplus, initial_state=initial_state)
+    def forward(ctx, u, delta, A_log, B, C, D, z, delta_bias, delta_softplus, initial_state, zoh):
+        y = scan_fwd(u, delta, A_log, B, C, D, z, delta_bias, delta_softplus, initial_state=initial_state, zoh=zoh)
         ctx.delta_softplus = delta_softplus
+        ctx.zoh = zoh
         ctx.save_for_backward(u, delta, A_log, B, C, D, z, delta_bias, initial_state)
         return y
 
     @staticmethod
     def backward(ctx, dy):
         u, delta, A_log, B, C, D, z, delta_bias, initial_state = ctx.saved_tensors
-        g = scan_bwd(u, delta, A_log, B, C, D, dy.contiguous(), z, delta_bias, ctx.delta_softplus, initial_state)
+        g = scan_bwd(u, delta, A_log, B, C, D, dy.contiguous(), z, delta_bias, ctx.delta_softplus, initial_state,
+                     zoh=ctx.zoh)
         return (g["du"], g["ddelta"], g["dA_log"], g["dB"], g["dC"], g["dD"], g.get("dz"), g.get("ddelta_bias"),
-                None, g.get("dinitial_state"))
+                None, g.get("dinitial_state"), None)
 
 
-def selective_scan(u, delta, A_log, B, C, D, z=None, delta_bias=None, delta_softplus=True, initial_state=None):
-    """y of the scan, differentiable with respect to every tensor argument (torch autograd)."""
-    return _SelectiveScan.apply(u, delta, A_log, B, C, D, z, delta_bias, delta_softplus, initial_state)
+def selective_scan(u, delta, A_log, B, C, D, z=None, delta_bias=None, delta_softplus=True, initial_state=None,
+                   zoh=False):
+    """y of the scan, differentiable with respect to every tensor argument (torch autograd); zoh selects
+    the zero-order-hold input term."""
+    return _SelectiveScan.apply(u, delta, A_log, B, C, D, z, delta_bias, delta_softplus, initial_state, bool(zoh))

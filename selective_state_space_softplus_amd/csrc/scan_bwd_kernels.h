@@ -14,7 +14,12 @@
 //     dA_log_k = sum_(b,t) g_tk Delta_t a_tk h_(t-1)k A_k,   dD = sum dy' u,   dbias = sum ddelta
 //     dh0_k    = a_0k g_0k
 //
-// scan_bwd<TIn, SC, NSW, SP, GATE>: one workgroup per (b, 64-channel group,
+// ZOH: the zero-order-hold input weight beta = (exp(Delta A) - 1)/A in place
+// of Delta (mhpn.cn page, section 6): du_t = dy'_t D + sum_k g_tk beta_tk B_tk,
+// dDelta_t gains a_tk where Euler has 1 in its input term, dB = g beta u, and
+// dA_k gains g_tk B_tk u_t (Delta_t a_tk - beta_tk)/A_k.
+//
+// scan_bwd<TIn, SC, NSW, SP, GATE, ZOH>: one workgroup per (b, 64-channel group,
 // segment of L) walks its segment backwards in chunks of kCkptSteps = 8
 // steps; segments are taken last first, each starting from the adjoint the
 // later one handed on (as the forward hands on states), which balances the
@@ -139,7 +144,7 @@ struct BwdLds {
     static constexpr int bytes = off_ticket + 16;
 };
 
-template <typename TIn, int SC, int NSW, bool SP, bool GATE>
+template <typename TIn, int SC, int NSW, bool SP, bool GATE, bool ZOH>
 __global__ __launch_bounds__((SC + 4) * 64) void scan_bwd(const BwdParams p) {
     constexpr int T = kCkptSteps;
     constexpr int NE = 4 * 64;                     // element threads
@@ -198,12 +203,13 @@ __global__ __launch_bounds__((SC + 4) * 64) void scan_bwd(const BwdParams p) {
     const int d = dbase + lane;
     const bool dv = d < d_in;
     const int n0 = wave * NSW;
-    float A2[NSW], An[NSW], g[NSW], dA[NSW];
+    float A2[NSW], An[NSW], g[NSW], dA[NSW], invA[NSW];
 #pragma unroll
     for (int q = 0; q < NSW; q++) {
         const bool ok = rec && dv && n0 + q < n;
         A2[q] = ok ? a2_from_alog(p.A_log[int64_t(d) * n + n0 + q]) : 0.0f;
         An[q] = A2[q] * kLn2;                                          // A itself
+        invA[q] = (ZOH && ok) ? inv_a_from_alog(p.A_log[int64_t(d) * n + n0 + q]) : 0.0f;
         g[q] = (ok && p.dlast && seg == p.K - 1) ? p.dlast[(int64_t(bi) * d_in + d) * n + n0 + q] : 0.0f;
         dA[q] = 0.0f;
     }
@@ -377,7 +383,7 @@ __global__ __launch_bounds__((SC + 4) * 64) void scan_bwd(const BwdParams p) {
             const float dy = ok ? RawIn::f(r.dy[i]) : 0.0f;
             const float dl = ok ? (SP ? softplus(x) : x) : 0.0f;
             const float dyp = GATE ? dy * silu(z) : dy;
-            s_prep[(s3 * T + er) * 64 + ec + i * TPR] = make_float4(dl, dl * u, dyp, u);
+            s_prep[(s3 * T + er) * 64 + ec + i * TPR] = make_float4(dl, ZOH ? u : dl * u, dyp, u);
             kp.x[i] = x;
         }
 #pragma unroll
@@ -418,9 +424,11 @@ __global__ __launch_bounds__((SC + 4) * 64) void scan_bwd(const BwdParams p) {
                 S1 += q[w][i].x;
                 S2 += q[w][i].y;
             }
-            const float dDelta = fmaf(pr.w, S1, S2);
+            // Euler: S1 = sum g B, dDelta = S2 + u S1, du = Delta S1 + dy' D; the hold:
+            // S1 = sum g beta B, S2 already holds the input term, du = S1 + dy' D.
+            const float dDelta = ZOH ? S2 : fmaf(pr.w, S1, S2);
             const float ddl = SP ? dDelta * rcp_hw(1.0f + exp2_hw(-kp.x[i] * kLog2e)) : dDelta;
-            const float du = fmaf(pr.x, S1, pr.z * Dv[i]);
+            const float du = ZOH ? fmaf(pr.z, Dv[i], S1) : fmaf(pr.x, S1, pr.z * Dv[i]);
             if (rv && evok[i]) {
                 auto st = [&](void* base, float v) __attribute__((always_inline)) {
                     TIn* q = static_cast<TIn*>(base) + rb;
@@ -458,14 +466,21 @@ __global__ __launch_bounds__((SC + 4) * 64) void scan_bwd(const BwdParams p) {
 #pragma unroll
         for (int q = 0; q < NSW; q++) h[q] = hstart[q] = s_ck[(s2 * NP + n0 + q) * 64 + lane];
         const float* bcw = s_bc + s2 * (T * 2 * NP) + wave * 2 * NSW;
-        float hs[T][NSW], as[T][NSW];
+        float hs[T][NSW], as[T][NSW], bs[ZOH ? T : 1][NSW];   // states, decays, hold weights
 #pragma unroll
         for (int j = 0; j < T; j++) {
             const float4 pr = s_prep[(s3 * T + j) * 64 + lane];
 #pragma unroll
             for (int q = 0; q < NSW; q++) {
-                const float a = exp2_hw(pr.x * A2[q]);
-                h[q] = fmaf(a, h[q], pr.y * bcw[j * SC * 2 * NSW + q]);
+                const float x2 = pr.x * A2[q];
+                const float a = exp2_hw(x2);
+                if constexpr (ZOH) {
+                    const float beta = zoh_weight(pr.x, x2, a, invA[q]);
+                    h[q] = fmaf(a, h[q], beta * (pr.y * bcw[j * SC * 2 * NSW + q]));
+                    bs[j][q] = beta;
+                } else {
+                    h[q] = fmaf(a, h[q], pr.y * bcw[j * SC * 2 * NSW + q]);
+                }
                 hs[j][q] = h[q];
                 as[j][q] = a;
             }
@@ -473,20 +488,32 @@ __global__ __launch_bounds__((SC + 4) * 64) void scan_bwd(const BwdParams p) {
 #pragma unroll
         for (int j = T - 1; j >= 0; j--) {
             const float4 pr = s_prep[(s3 * T + j) * 64 + lane];
-            float S1 = 0.0f, S2 = 0.0f, dBv[NSW], dCv[NSW];
+            float S1 = 0.0f, S2 = 0.0f, S3 = 0.0f, dBv[NSW], dCv[NSW];
 #pragma unroll
             for (int q = 0; q < NSW; q++) {
                 const float Bq = bcw[j * SC * 2 * NSW + q], Cq = bcw[j * SC * 2 * NSW + NSW + q];
                 g[q] = fmaf(pr.z, Cq, g[q]);
                 const float hp = j > 0 ? hs[j - 1][q] : hstart[q];
-                const float gah = g[q] * as[j][q] * hp;
-                S1 = fmaf(g[q], Bq, S1);
+                const float ga = g[q] * as[j][q];
+                const float gah = ga * hp;
                 S2 = fmaf(gah, An[q], S2);
                 dA[q] = fmaf(gah, pr.x, dA[q]);
-                dBv[q] = g[q] * pr.y;
                 dCv[q] = pr.z * hs[j][q];
-                g[q] *= as[j][q];
+                if constexpr (ZOH) {
+                    // beta = (a - 1)/A: d beta/dDelta = a, d beta/dA = (Delta a - beta)/A.
+                    const float beta = bs[j][q];
+                    const float gb = g[q] * beta;
+                    S1 = fmaf(gb, Bq, S1);
+                    S3 = fmaf(ga, Bq, S3);
+                    dA[q] = fmaf(g[q] * (pr.y * Bq), fmaf(pr.x, as[j][q], -beta) * invA[q], dA[q]);
+                    dBv[q] = gb * pr.y;
+                } else {
+                    S1 = fmaf(g[q], Bq, S1);
+                    dBv[q] = g[q] * pr.y;
+                }
+                g[q] = ga;
             }
+            if constexpr (ZOH) S2 = fmaf(pr.w, S3, S2);   // the input term of dDelta: u sum g a B
             s_part[((s2 * SC + wave) * T + j) * 64 + lane] = make_float2(S1, S2);
             // dB, dC of this step over the 64 channels, two states at a time.
             if constexpr (RL) {

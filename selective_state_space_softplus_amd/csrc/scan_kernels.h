@@ -274,7 +274,7 @@ __global__ __launch_bounds__((SC + kSeqElemWaves + 1) * 64) void scan_seq(const 
     static_assert(!WIDE || (T * 64 * ES) % 1024 == 0, "whole loads per tile");
     static_assert(Lds::bytes <= 160 * 1024, "LDS of one workgroup");
     static_assert(T % kCkptSteps == 0, "checkpoints fall at chunk-internal step boundaries");
-    static_assert(!DZ || (GATE && !ZOH && !CROSS), "dz is the gradient of a gated Euler scan");
+    static_assert(!DZ || (GATE && !CROSS), "dz is the gradient of a gated scan");
     extern __shared__ __align__(16) float smem[];
     char* const lds = reinterpret_cast<char*>(smem);
     float* s_dw = reinterpret_cast<float*>(lds + Lds::off_dw);   // [3][T/2][64][4]: (delta'_j, w_j, delta'_j+1, w_j+1)

@@ -167,15 +167,15 @@ int choose_segments(int64_t G, int64_t L, int T, int64_t slots) {
     return best;
 }
 
-// Which family of scan_seq kernels a call needs.  Dz: the gated Euler scan
+// Which family of scan_seq kernels a call needs.  Dz, ZohDz: the gated scan
 // inside the backward, writing dz in place of y.
-enum class SeqMode { Euler, Zoh, Cross, Dz };
+enum class SeqMode { Euler, Zoh, Cross, Dz, ZohDz };
 
 // scan_seq writing dz, for the state sizes the backward takes (none above).
-template <typename TIn, int SC, int NSW, int T, bool WIDE, bool SP>
+template <typename TIn, int SC, int NSW, int T, bool WIDE, bool SP, bool ZOH = false>
 constexpr void (*dz_kernel())(ss::ScanParams) {
     if constexpr (SC * NSW <= SS_MAX_BWD_STATE)
-        return ss::scan_seq<TIn, SC, NSW, T, WIDE, SP, true, false, false, true>;
+        return ss::scan_seq<TIn, SC, NSW, T, WIDE, SP, true, ZOH, false, true>;
     else
         return nullptr;
 }
@@ -193,18 +193,21 @@ int launch_seq(ScanParams p, SeqMode mode, void* ws, size_t ws_bytes, hipStream_
     // element).  The zero-order-hold kernels exist in the element-load form
     // only: their recurrence costs about three times the Euler one, which
     // hides the difference in load width.  The cross scan has no gate.
-    const void* out = mode == SeqMode::Dz ? p.dz : p.y;
-    const bool wide = mode != SeqMode::Zoh && (p.d_in * int64_t(sizeof(TIn))) % 16 == 0 && aligned(p.u, 16) &&
+    const bool dz = mode == SeqMode::Dz || mode == SeqMode::ZohDz;
+    const void* out = dz ? p.dz : p.y;
+    const bool wide = mode != SeqMode::Zoh && mode != SeqMode::ZohDz && (p.d_in * int64_t(sizeof(TIn))) % 16 == 0 &&
+                      aligned(p.u, 16) &&
                       aligned(p.delta, 16) && (!p.z || aligned(p.z, 16)) &&
-                      (mode != SeqMode::Dz || aligned(p.dy, 16)) &&
+                      (!dz || aligned(p.dy, 16)) &&
                       (mode == SeqMode::Cross || aligned(out, (TW / ss::kSeqElemWaves) * sizeof(TIn)));
     const int T = wide ? TW : TN;
-    const int variant = mode == SeqMode::Cross ? 12 + (wide ? 2 : 0) + (p.softplus ? 1 : 0)
-                        : mode == SeqMode::Dz  ? 16 + (wide ? 2 : 0) + (p.softplus ? 1 : 0)
+    const int variant = mode == SeqMode::Cross   ? 12 + (wide ? 2 : 0) + (p.softplus ? 1 : 0)
+                        : mode == SeqMode::Dz    ? 16 + (wide ? 2 : 0) + (p.softplus ? 1 : 0)
+                        : mode == SeqMode::ZohDz ? 20 + (p.softplus ? 1 : 0)
                                                : ((mode == SeqMode::Zoh ? 8 : wide ? 4 : 0) | (p.softplus ? 2 : 0) |
                                                   (p.z ? 1 : 0));
     using Kern = void (*)(ScanParams);
-    static constexpr Kern kernels[20] = {
+    static constexpr Kern kernels[22] = {
         ss::scan_seq<TIn, SC, NSW, TN, false, false, false, false, false>,
         ss::scan_seq<TIn, SC, NSW, TN, false, false, true, false, false>,
         ss::scan_seq<TIn, SC, NSW, TN, false, true, false, false, false>,
@@ -224,7 +227,9 @@ int launch_seq(ScanParams p, SeqMode mode, void* ws, size_t ws_bytes, hipStream_
         dz_kernel<TIn, SC, NSW, TN, false, false>(),
         dz_kernel<TIn, SC, NSW, TN, false, true>(),
         dz_kernel<TIn, SC, NSW, TW, true, false>(),
-        dz_kernel<TIn, SC, NSW, TW, true, true>()};
+        dz_kernel<TIn, SC, NSW, TW, true, true>(),
+        dz_kernel<TIn, SC, NSW, TN, false, false, true>(),
+        dz_kernel<TIn, SC, NSW, TN, false, true, true>()};
     const Kern kern = kernels[variant];
     if (!kern) return SS_ERR_UNSUPPORTED;
     const size_t lds = wide ? ss::SeqLds<TW, SC, SC * NSW, sizeof(TIn), true>::bytes
@@ -668,13 +673,16 @@ BwdWorkspace bwd_workspace(int64_t b, int64_t L, int64_t d_in, int64_t n) {
 // balance the resident workgroups); p.K and p.Lseg are set here and the
 // number of segments is returned in *segments.
 template <typename TIn, int SC, int NSW>
-int launch_bwd(BwdParams p, bool gate, hipStream_t st, int* segments) {
+int launch_bwd(BwdParams p, bool gate, bool zoh, hipStream_t st, int* segments) {
     constexpr int threads = (SC + 4) * 64;
     constexpr int T = ss::kCkptSteps;
     using Kern = void (*)(BwdParams);
-    static constexpr Kern kernels[4] = {ss::scan_bwd<TIn, SC, NSW, false, false>, ss::scan_bwd<TIn, SC, NSW, false, true>,
-                                        ss::scan_bwd<TIn, SC, NSW, true, false>, ss::scan_bwd<TIn, SC, NSW, true, true>};
-    const Kern kern = kernels[(p.softplus ? 2 : 0) | (gate ? 1 : 0)];
+    static constexpr Kern kernels[8] = {
+        ss::scan_bwd<TIn, SC, NSW, false, false, false>, ss::scan_bwd<TIn, SC, NSW, false, true, false>,
+        ss::scan_bwd<TIn, SC, NSW, true, false, false>,  ss::scan_bwd<TIn, SC, NSW, true, true, false>,
+        ss::scan_bwd<TIn, SC, NSW, false, false, true>,  ss::scan_bwd<TIn, SC, NSW, false, true, true>,
+        ss::scan_bwd<TIn, SC, NSW, true, false, true>,   ss::scan_bwd<TIn, SC, NSW, true, true, true>};
+    const Kern kern = kernels[(zoh ? 4 : 0) | (p.softplus ? 2 : 0) | (gate ? 1 : 0)];
     const size_t lds = ss::BwdLds<SC, SC * NSW>::bytes;
     const int64_t G = p.b * p.nblk_d;
     const int cus = device_cus();
@@ -698,12 +706,12 @@ int launch_bwd(BwdParams p, bool gate, hipStream_t st, int* segments) {
 }
 
 template <typename TIn>
-int dispatch_bwd(const BwdParams& p, bool gate, hipStream_t st, int* segments) {
+int dispatch_bwd(const BwdParams& p, bool gate, bool zoh, hipStream_t st, int* segments) {
     const SeqShape sh = bwd_shape(p.n);
-    if (sh.SC == 1) return launch_bwd<TIn, 1, 2>(p, gate, st, segments);
-    if (sh.SC == 4) return launch_bwd<TIn, 4, 2>(p, gate, st, segments);
-    if (sh.NSW == 2) return launch_bwd<TIn, 8, 2>(p, gate, st, segments);
-    return launch_bwd<TIn, 8, 4>(p, gate, st, segments);
+    if (sh.SC == 1) return launch_bwd<TIn, 1, 2>(p, gate, zoh, st, segments);
+    if (sh.SC == 4) return launch_bwd<TIn, 4, 2>(p, gate, zoh, st, segments);
+    if (sh.NSW == 2) return launch_bwd<TIn, 8, 2>(p, gate, zoh, st, segments);
+    return launch_bwd<TIn, 8, 4>(p, gate, zoh, st, segments);
 }
 
 template <typename TOut>
@@ -722,15 +730,18 @@ SS_EXPORT size_t ss_scan_bwd_workspace_bytes(int64_t b, int64_t L, int64_t d_in,
     return bwd_workspace(b, L, d_in, n).total;
 }
 
-SS_EXPORT int ss_scan_bwd(const void* u, const void* delta, const float* A_log, const void* B, const void* C,
-                          const float* D, const void* z, const float* delta_bias, int delta_softplus,
-                          const float* initial_state, const void* dy, const float* dlast_state, void* du,
-                          void* ddelta, float* dA_log, void* dB, void* dC, float* dD, void* dz, float* ddelta_bias,
-                          float* dinitial_state, int64_t b, int64_t L, int64_t d_in, int64_t n, int dtype,
-                          void* workspace, size_t workspace_bytes, void* stream) {
+SS_EXPORT int ss_scan_bwd_ex(const void* u, const void* delta, const float* A_log, const void* B, const void* C,
+                             const float* D, const void* z, const float* delta_bias, int delta_softplus,
+                             const float* initial_state, int discretization, const void* dy,
+                             const float* dlast_state, void* du, void* ddelta, float* dA_log, void* dB, void* dC,
+                             float* dD, void* dz, float* ddelta_bias, float* dinitial_state, int64_t b, int64_t L,
+                             int64_t d_in, int64_t n, int dtype, void* workspace, size_t workspace_bytes,
+                             void* stream) {
     if (!u || !delta || !A_log || !B || !C || !D || !dy || !du || !ddelta || !dA_log || !dB || !dC || !dD)
         return SS_ERR_NULL;
     if (z && !dz) return SS_ERR_NULL;
+    if (discretization != SS_DISC_EULER && discretization != SS_DISC_ZOH) return SS_ERR_MODE;
+    const bool zoh = discretization == SS_DISC_ZOH;
     if (!sizes_ok(b, L, d_in) || n <= 0 || d_in > SS_MAX_CHANNELS) return SS_ERR_SHAPE;
     if (dtype != SS_F32 && dtype != SS_BF16) return SS_ERR_DTYPE;
     if (n > SS_MAX_BWD_STATE) return SS_ERR_UNSUPPORTED;
@@ -811,7 +822,7 @@ SS_EXPORT int ss_scan_bwd(const void* u, const void* delta, const float* A_log, 
     f.nblk_d = nblk;
     f.K = 1;
     f.Lseg = L;
-    const SeqMode fm = z ? SeqMode::Dz : SeqMode::Euler;
+    const SeqMode fm = zoh ? (z ? SeqMode::ZohDz : SeqMode::Zoh) : (z ? SeqMode::Dz : SeqMode::Euler);
     int rc = dtype == SS_BF16 ? dispatch_seq<uint16_t>(f, fm, fwd_ws, w.fwd, st)
                               : dispatch_seq<float>(f, fm, fwd_ws, w.fwd, st);
     if (rc != SS_OK) return rc;
@@ -848,8 +859,8 @@ SS_EXPORT int ss_scan_bwd(const void* u, const void* delta, const float* A_log, 
     p.ctl = bctl;
     p.handoff = handoff;
     int K = 1;
-    rc = dtype == SS_BF16 ? dispatch_bwd<uint16_t>(p, z != nullptr, st, &K)
-                          : dispatch_bwd<float>(p, z != nullptr, st, &K);
+    rc = dtype == SS_BF16 ? dispatch_bwd<uint16_t>(p, z != nullptr, zoh, st, &K)
+                          : dispatch_bwd<float>(p, z != nullptr, zoh, st, &K);
     if (rc != SS_OK) return rc;
 
     // 3. Sums over channel groups (dB, dC) and segments and batch rows (dA_log, dD, dbias), in a fixed order.
@@ -861,4 +872,15 @@ SS_EXPORT int ss_scan_bwd(const void* u, const void* delta, const float* A_log, 
     if (rc == SS_OK) rc = reduce<float>(part_D, dD, d_in, int64_t(K) * b, st);
     if (rc == SS_OK && ddelta_bias && delta_bias) rc = reduce<float>(part_bias, ddelta_bias, d_in, int64_t(K) * b, st);
     return rc;
+}
+
+SS_EXPORT int ss_scan_bwd(const void* u, const void* delta, const float* A_log, const void* B, const void* C,
+                          const float* D, const void* z, const float* delta_bias, int delta_softplus,
+                          const float* initial_state, const void* dy, const float* dlast_state, void* du,
+                          void* ddelta, float* dA_log, void* dB, void* dC, float* dD, void* dz, float* ddelta_bias,
+                          float* dinitial_state, int64_t b, int64_t L, int64_t d_in, int64_t n, int dtype,
+                          void* workspace, size_t workspace_bytes, void* stream) {
+    return ss_scan_bwd_ex(u, delta, A_log, B, C, D, z, delta_bias, delta_softplus, initial_state, SS_DISC_EULER, dy,
+                          dlast_state, du, ddelta, dA_log, dB, dC, dD, dz, ddelta_bias, dinitial_state, b, L, d_in, n,
+                          dtype, workspace, workspace_bytes, stream);
 }

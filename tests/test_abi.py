@@ -29,7 +29,8 @@ def declared_functions():
 
 def test_header_declares_the_entry_points():
     assert declared_functions() == sorted(["ss_conv_update", "ss_cross_scan_fwd", "ss_cross_scan_fwd_workspace_bytes",
-                                           "ss_scan_bwd", "ss_scan_bwd_workspace_bytes", "ss_scan_fwd", "ss_scan_fwd_ex",
+                                           "ss_scan_bwd", "ss_scan_bwd_ex", "ss_scan_bwd_workspace_bytes", "ss_scan_fwd",
+                                           "ss_scan_fwd_ex",
                                            "ss_scan_fwd_workspace_bytes", "ss_state_update", "ss_state_update_ex",
                                            "ss_status_string"])
 
@@ -293,6 +294,27 @@ def call_bwd(ss, a):
 ])
 def test_bwd_rejects(ss, over, code):
     assert call_bwd(ss, bwd_args(**over)) == code
+
+
+def call_bwd_ex(ss, a, mode):
+    k1 = ("u", "delta", "A_log", "B", "C", "D", "z", "bias", "softplus", "h0")
+    k2 = ("dy", "dlast", "du", "ddelta", "dA", "dB", "dC", "dD", "dz", "dbias", "dh0", "b", "L", "d_in", "n", "dtype",
+          "ws", "ws_bytes", "stream")
+    return ss.lib.ss_scan_bwd_ex(*[a[x] for x in k1], mode, *[a[x] for x in k2])
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(u=None), NULL), (dict(dz=None), NULL), (dict(b=0), SHAPE), (dict(dtype=2), DTYPE), (dict(n=33), UNSUP),
+    (dict(ws_bytes=100), WS), (dict(du=addr(12) + 1), ALIGN), (dict(du=addr(1)), ALIAS),
+])
+@pytest.mark.parametrize("mode", [0, 1])
+def test_bwd_ex_rejects(ss, over, code, mode):
+    assert call_bwd_ex(ss, bwd_args(**over), mode) == code
+
+
+@pytest.mark.parametrize("mode", [-1, 2, 7])
+def test_bwd_ex_rejects_unknown_discretization(ss, mode):
+    assert call_bwd_ex(ss, bwd_args(), mode) == MODE
 
 
 def test_bwd_optional_pointers_may_be_null(ss):

@@ -1,4 +1,5 @@
-"""GPU: the gradient of the scan (ss_scan_bwd) against the oracle's gradient.
+"""GPU: the gradient of the scan (ss_scan_bwd, and ss_scan_bwd_ex with the
+zero-order-hold input term) against the oracle's gradient.
 
 The oracle's backward is pinned to torch autograd and to finite differences of
 its forward (tests/oracle_pins.py).  Every gradient is compared element by
@@ -28,16 +29,16 @@ def ss():
     return ss
 
 
-def grads_gpu(ss, g, dy, h0=None, dlast=None):
+def grads_gpu(ss, g, dy, h0=None, dlast=None, zoh=False):
     out = ss.scan_bwd(g["u"], g["delta"], g["A_log"], g["B"], g["C"], g["D"], dy, g["z"], g["delta_bias"],
-                      g["delta_softplus"], initial_state=h0, dlast_state=dlast)
+                      g["delta_softplus"], initial_state=h0, dlast_state=dlast, zoh=zoh)
     torch.cuda.synchronize()
     return out
 
 
-def grads_oracle(inp, dy, h0=None, dlast=None):
+def grads_oracle(inp, dy, h0=None, dlast=None, zoh=False):
     return oracle.scan_bwd(inp["u"], inp["delta"], inp["A_log"], inp["B"], inp["C"], inp["D"], inp["z"],
-                           inp["delta_bias"], inp["delta_softplus"], h0, dy, dlast)
+                           inp["delta_bias"], inp["delta_softplus"], h0, dy, dlast, zoh=zoh)
 
 
 def compare(got, ref, dtype, what):
@@ -161,3 +162,92 @@ def test_autograd_function(ss):
     for k, v in leaves.items():
         assert torch.equal(v.grad, ref[names[k]]), k
     assert torch.equal(h0.grad, ref["dinitial_state"])
+
+
+# ---- zero-order-hold input term (ss_scan_bwd_ex)
+
+ZOH_CASES = [c for c in CASES if c[:4] in ((2, 300, 130, 16), (1, 1, 1, 16), (1, 97, 65, 16), (2, 200, 40, 1),
+                                          (1, 129, 70, 2), (2, 90, 24, 3), (1, 70, 66, 8), (2, 61, 42, 32),
+                                          (1, 64, 128, 32))]
+
+
+@pytest.mark.parametrize("case", ZOH_CASES, ids=[_id(c) for c in ZOH_CASES])
+@pytest.mark.parametrize("h0,dlast", [(False, False), (True, True)])
+def test_bwd_zoh_small(ss, case, h0, dlast):
+    say(f"bwd zoh {case} h0={h0} dlast={dlast}")
+    b, L, d_in, n, dtype = case[:5]
+    inp = small_inputs(*case, seed=sum(case[:4]) + 5)
+    dy, hh, dl = extras(b, L, d_in, n, dtype, seed=b + L + d_in + n + 1, h0=h0, dlast=dlast)
+    got = grads_gpu(ss, to_dev(inp), dy.to(DEV), None if hh is None else hh.to(DEV), None if dl is None else dl.to(DEV),
+                    zoh=True)
+    compare(got, grads_oracle(inp, dy, hh, dl, zoh=True), dtype, f"zoh {case}")
+
+
+@pytest.mark.parametrize("segments,n,dtype", [(4, 16, BF16), (3, 5, F32)])
+def test_bwd_zoh_with_segments(ss, segments, n, dtype):
+    say(f"bwd zoh with {segments} segments n={n}")
+    inp = workloads.random_scan_inputs(2, 1000, 100, n, dtype, seed=80 + n, gated=True, bias=True)
+    dy, hh, dl = extras(2, 1000, 100, n, dtype, seed=81, h0=True, dlast=True)
+    with env(SS_SCAN_SEGMENTS=segments):
+        got = grads_gpu(ss, to_dev(inp), dy.to(DEV), hh.to(DEV), dl.to(DEV), zoh=True)
+    compare(got, grads_oracle(inp, dy, hh, dl, zoh=True), dtype, f"zoh segments={segments}")
+
+
+def test_bwd_zoh_mid_workload_full(ss):
+    """The scan-mid workload with the zero-order hold, every gradient compared in full."""
+    cfg = workloads.CONFIGS[1]
+    say(f"bwd zoh at {cfg.name} size, full compare")
+    inp = workloads.scan_inputs(1)
+    dy, _, _ = extras(cfg.b, cfg.L, cfg.d_in, cfg.n, cfg.dtype, seed=79, h0=False, dlast=False)
+    got = grads_gpu(ss, to_dev(inp), dy.to(DEV), zoh=True)
+    errs = compare(got, grads_oracle(inp, dy, zoh=True), cfg.dtype, f"zoh {cfg.name}")
+    print(f"{cfg.name} zoh bwd errors: " + ", ".join(f"{k} {v:.3g}" for k, v in errs.items()))
+
+
+def test_bwd_zoh_long_workload_sampled(ss):
+    """scan-long with the zero-order hold: per-channel gradients on sampled channels (as for Euler)."""
+    cfg = workloads.CONFIGS[2]
+    say(f"bwd zoh at {cfg.name} size, sampled channels")
+    inp = workloads.scan_inputs(2)
+    dy, _, _ = extras(cfg.b, cfg.L, cfg.d_in, cfg.n, cfg.dtype, seed=82, h0=False, dlast=False)
+    got = grads_gpu(ss, to_dev(inp), dy.to(DEV), zoh=True)
+    for d in (0, 65, 3000, cfg.d_in - 1):
+        sl = lambda t: t[:, :, d:d + 1].contiguous()  # noqa: E731
+        ref = oracle.scan_bwd(sl(inp["u"]), sl(inp["delta"]), inp["A_log"][d:d + 1], inp["B"], inp["C"],
+                              inp["D"][d:d + 1], sl(inp["z"]), inp["delta_bias"][d:d + 1], True, None, sl(dy), None,
+                              zoh=True)
+        for k in ("du", "ddelta", "dz"):
+            assert_close(got[k][:, :, d:d + 1], ref[k], cfg.dtype, f"zoh {cfg.name} {k} channel {d}")
+        for k in ("dA_log", "dD", "ddelta_bias"):
+            assert_close(got[k][d:d + 1], ref[k], cfg.dtype, f"zoh {cfg.name} {k} channel {d}")
+
+
+def test_bwd_zoh_is_deterministic(ss):
+    say("bwd zoh run-to-run determinism")
+    inp = to_dev(workloads.random_scan_inputs(2, 500, 200, 16, BF16, seed=6, gated=True, bias=True))
+    dy = torch.randn(2, 500, 200, device=DEV).to(BF16)
+    a = grads_gpu(ss, inp, dy, zoh=True)
+    b = grads_gpu(ss, inp, dy, zoh=True)
+    for k in a:
+        assert torch.equal(a[k], b[k]), k
+
+
+def test_autograd_function_zoh(ss):
+    """selective_scan(..., zoh=True) under torch autograd: y.backward(dy) gives scan_bwd's hold gradients,
+    and y is the hold forward's."""
+    say("autograd function, zero-order hold")
+    inp = to_dev(workloads.random_scan_inputs(2, 100, 64, 16, F32, seed=10, gated=True, bias=True))
+    leaves = {k: inp[k].clone().requires_grad_(True) for k in ("u", "delta", "A_log", "B", "C", "D", "z",
+                                                                  "delta_bias")}
+    y = ss.selective_scan(leaves["u"], leaves["delta"], leaves["A_log"], leaves["B"], leaves["C"], leaves["D"],
+                          leaves["z"], leaves["delta_bias"], True, zoh=True)
+    y_fwd = ss.scan_fwd(inp["u"], inp["delta"], inp["A_log"], inp["B"], inp["C"], inp["D"], inp["z"],
+                        inp["delta_bias"], True, zoh=True)
+    assert torch.equal(y.detach(), y_fwd)
+    dy = torch.randn_like(y)
+    y.backward(dy)
+    ref = ss.scan_bwd(inp["u"], inp["delta"], inp["A_log"], inp["B"], inp["C"], inp["D"], dy, inp["z"],
+                      inp["delta_bias"], True, zoh=True)
+    names = dict(u="du", delta="ddelta", A_log="dA_log", B="dB", C="dC", D="dD", z="dz", delta_bias="ddelta_bias")
+    for k, v in leaves.items():
+        assert torch.equal(v.grad, ref[names[k]]), k
