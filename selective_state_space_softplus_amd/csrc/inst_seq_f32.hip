@@ -1,0 +1,11 @@
+// The scan_seq launchers for f32 inputs, one per launch shape.
+#include "launch_seq.h"
+
+namespace ss_host {
+template int launch_seq<float, 1, 2>(ss::ScanParams, SeqMode, void*, size_t, hipStream_t);
+template int launch_seq<float, 4, 2>(ss::ScanParams, SeqMode, void*, size_t, hipStream_t);
+template int launch_seq<float, 4, 4>(ss::ScanParams, SeqMode, void*, size_t, hipStream_t);
+template int launch_seq<float, 8, 2>(ss::ScanParams, SeqMode, void*, size_t, hipStream_t);
+template int launch_seq<float, 8, 4>(ss::ScanParams, SeqMode, void*, size_t, hipStream_t);
+template int launch_seq<float, 8, 8>(ss::ScanParams, SeqMode, void*, size_t, hipStream_t);
+}  // namespace ss_host

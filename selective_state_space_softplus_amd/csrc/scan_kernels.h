@@ -775,7 +775,7 @@ __global__ __launch_bounds__(256) void cross_merge(const float* __restrict__ ys,
 }
 
 // Clears the ticket counter, the error word and the segment flags.
-__global__ void scan_ctl_reset(uint32_t* ctl, int64_t words) {
+static __global__ void scan_ctl_reset(uint32_t* ctl, int64_t words) {
     for (int64_t i = blockIdx.x * int64_t(blockDim.x) + threadIdx.x; i < words; i += int64_t(gridDim.x) * blockDim.x)
         ctl[i] = 0u;
 }

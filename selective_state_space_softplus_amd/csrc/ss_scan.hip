@@ -17,25 +17,18 @@
 #include "conv_kernels.h"
 #include "scan_bwd_kernels.h"
 #include "scan_kernels.h"
+#include "ss_host.h"
 #include "state_update_kernels.h"
 
 #define SS_EXPORT extern "C" __attribute__((visibility("default")))
 
 namespace {
 
+using namespace ss_host;
 using ss::ConvParams;
 using ss::ScanParams;
 using ss::StepParams;
 
-constexpr int kMaxSegments = 16;
-constexpr int64_t kMaxElems = int64_t(1) << 46;   // keeps every index product far from int64 overflow
-constexpr int kTparWaves = 8;
-// Largest grid in workgroups of up to 1024 threads: a launch holds at most 2^32 - 1 work-items.
-constexpr int64_t kMaxWorkgroups = (int64_t(1) << 22) - 1;
-// Longest sequence: per-segment time indices of scan_seq are 32-bit.
-constexpr int64_t kMaxLength = (int64_t(1) << 31) - 1024;
-// Largest b * d_in of the decode step (up to 16 threads per channel in one launch).
-constexpr int64_t kMaxStepChannels = (int64_t(1) << 28) - 1;
 
 // ----------------------------------------------------------------------------- validation helpers
 
@@ -50,8 +43,6 @@ Range range_of(const void* p, int64_t count, size_t elem) {
 
 bool overlaps(Range a, Range b) { return a.lo < b.hi && b.lo < a.hi; }
 
-bool aligned(const void* p, size_t a) { return reinterpret_cast<uintptr_t>(p) % a == 0; }
-
 size_t elem_size(int dtype) { return dtype == SS_BF16 ? 2 : 4; }
 
 // a, b, c >= 1 and a * b * c <= 2^46 (checked without forming an overflowing product).
@@ -65,196 +56,12 @@ bool sizes_ok(int64_t a, int64_t b, int64_t c) {
 
 enum class ScanKernel { Tpar, Seq };
 
-struct SeqShape {
-    int SC;    // recurrence waves per workgroup
-    int NSW;   // states per recurrence wave
-};
-
-// Recurrence waves and states per wave.  SS_SCAN_WAVES=4 selects 4 waves of
-// 4 states at 9 <= n <= 16 (tests, tuning).
-SeqShape seq_shape(int64_t n) {
-    const char* w = std::getenv("SS_SCAN_WAVES");
-    const int want = w ? int(std::strtol(w, nullptr, 10)) : 0;
-    if (n <= 2) return {1, 2};
-    if (n <= 8) return {4, 2};
-    if (n <= 16) return want == 4 ? SeqShape{4, 4} : SeqShape{8, 2};
-    if (n <= 32) return {8, 4};
-    return {8, 8};
-}
-
 // scan_seq for every n; SS_SCAN_VARIANT=tpar selects scan_tpar for n <= 2
 // (tests), which starts from a zero state with the delta' input weight only.
 ScanKernel choose_kernel(const ScanParams& p, bool zoh) {
     const char* v = std::getenv("SS_SCAN_VARIANT");
     if (v && std::strcmp(v, "tpar") == 0 && p.n <= 2 && !p.h0 && !zoh) return ScanKernel::Tpar;
     return ScanKernel::Seq;
-}
-
-// Workspace of scan_seq, in order: control words (ticket, error, one flag per
-// (segment, group)) and the states published between segments, sized for up
-// to kMaxSegments segments.
-struct SeqWorkspace {
-    size_t ctl, handoff, total;
-};
-
-SeqWorkspace seq_workspace(int64_t b, int64_t L, int64_t d_in, int64_t n) {
-    (void)L;
-    const int64_t G = b * ((d_in + 63) / 64);
-    SeqWorkspace w;
-    w.ctl = ((size_t(ss::kFlagOffset) + size_t(G) * kMaxSegments) * sizeof(uint32_t) + 255) / 256 * 256;
-    w.handoff = (size_t(kMaxSegments - 1) * size_t(G) * size_t(n) * 64 * sizeof(float) + 255) / 256 * 256;
-    w.total = w.ctl + w.handoff;
-    return w;
-}
-
-int device_cus() {
-    static std::atomic<int> cached[64];
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0) return -1;
-    if (dev < 64 && cached[dev].load(std::memory_order_relaxed) > 0) return cached[dev].load(std::memory_order_relaxed);
-    int cus = 0;
-    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return -1;
-    if (dev < 64) cached[dev].store(cus, std::memory_order_relaxed);
-    return cus;
-}
-
-// Workgroups of `fn` that fit on one compute unit at once (cached per kernel
-// and device; 0 when unknown).
-int resident_per_cu(const void* fn, int threads, size_t lds) {
-    static std::mutex mu;
-    static std::map<std::pair<const void*, int>, int> cache;
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess) return 0;
-    const auto key = std::make_pair(fn, dev);
-    {
-        std::lock_guard<std::mutex> g(mu);
-        const auto it = cache.find(key);
-        if (it != cache.end()) return it->second;
-    }
-    int nb = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, fn, threads, lds) != hipSuccess) nb = 0;
-    std::lock_guard<std::mutex> g(mu);
-    cache[key] = nb;
-    return nb;
-}
-
-// Number of segments K along L for scan_seq.  Pieces (segment, group) are
-// taken in ticket order, segment-major, by `slots` resident workgroups.  When
-// the G groups fill the slots at least once, a piece's predecessor always ran
-// in an earlier round, so with pieces of equal length the time is
-// ceil(G K / slots) rounds of 1/K of the work each, plus a fixed cost per piece
-// (pipeline fill and drain, state handoff) taken as 2% of a whole-length
-// piece.  K minimises that.  With fewer groups than slots the segments of a
-// group would only run one after another, so K = 1.  Every segment keeps at
-// least 4 chunks.  SS_SCAN_SEGMENTS overrides (tests, tuning).
-int choose_segments(int64_t G, int64_t L, int T, int64_t slots) {
-    const int64_t max_k = std::max<int64_t>(1, std::min<int64_t>(kMaxSegments, L / (4 * int64_t(T))));
-    if (const char* e = std::getenv("SS_SCAN_SEGMENTS")) {
-        const long v = std::strtol(e, nullptr, 10);
-        if (v >= 1) return int(std::min<int64_t>(std::min<int64_t>(v, kMaxSegments), std::max<int64_t>(1, (L + T - 1) / T)));
-    }
-    if (slots <= 0 || G < slots) return 1;
-    int best = 1;
-    double best_t = 0.0;
-    for (int64_t k = 1; k <= max_k; k++) {
-        const double rounds = double((G * k + slots - 1) / slots);
-        const double t = rounds * (1.0 / double(k) + 0.02);
-        if (k == 1 || t < best_t * (1.0 - 1e-9)) {
-            best = int(k);
-            best_t = t;
-        }
-    }
-    return best;
-}
-
-// Which family of scan_seq kernels a call needs.  Dz, ZohDz: the gated scan
-// inside the backward, writing dz in place of y.
-enum class SeqMode { Euler, Zoh, Cross, Dz, ZohDz };
-
-// scan_seq writing dz, for the state sizes the backward takes (none above).
-template <typename TIn, int SC, int NSW, int T, bool WIDE, bool SP, bool ZOH = false>
-constexpr void (*dz_kernel())(ss::ScanParams) {
-    if constexpr (SC * NSW <= SS_MAX_BWD_STATE)
-        return ss::scan_seq<TIn, SC, NSW, T, WIDE, SP, true, ZOH, false, true>;
-    else
-        return nullptr;
-}
-
-template <typename TIn, int SC, int NSW>
-int launch_seq(ScanParams p, SeqMode mode, void* ws, size_t ws_bytes, hipStream_t st) {
-    constexpr int TW = ss::seq_chunk<TIn, SC, NSW, true>(), TN = ss::seq_chunk<TIn, SC, NSW, false>();
-    constexpr int threads = (SC + ss::kSeqElemWaves + 1) * 64;
-    const int64_t G = p.b * p.nblk_d;
-    const SeqWorkspace w = seq_workspace(p.b, p.L, p.d_in, p.n);
-    if (!ws || ws_bytes < w.total) return SS_ERR_WORKSPACE;
-
-    // Wide path: whole 16-byte pieces per row and 16-byte aligned u, delta, z;
-    // y aligned for V-element stores (the cross scan adds to y element by
-    // element).  The zero-order-hold kernels exist in the element-load form
-    // only: their recurrence costs about three times the Euler one, which
-    // hides the difference in load width.  The cross scan has no gate.
-    const bool dz = mode == SeqMode::Dz || mode == SeqMode::ZohDz;
-    const void* out = dz ? p.dz : p.y;
-    const bool wide = mode != SeqMode::Zoh && mode != SeqMode::ZohDz && (p.d_in * int64_t(sizeof(TIn))) % 16 == 0 &&
-                      aligned(p.u, 16) &&
-                      aligned(p.delta, 16) && (!p.z || aligned(p.z, 16)) &&
-                      (!dz || aligned(p.dy, 16)) &&
-                      (mode == SeqMode::Cross || aligned(out, (TW / ss::kSeqElemWaves) * sizeof(TIn)));
-    const int T = wide ? TW : TN;
-    const int variant = mode == SeqMode::Cross   ? 12 + (wide ? 2 : 0) + (p.softplus ? 1 : 0)
-                        : mode == SeqMode::Dz    ? 16 + (wide ? 2 : 0) + (p.softplus ? 1 : 0)
-                        : mode == SeqMode::ZohDz ? 20 + (p.softplus ? 1 : 0)
-                                               : ((mode == SeqMode::Zoh ? 8 : wide ? 4 : 0) | (p.softplus ? 2 : 0) |
-                                                  (p.z ? 1 : 0));
-    using Kern = void (*)(ScanParams);
-    static constexpr Kern kernels[22] = {
-        ss::scan_seq<TIn, SC, NSW, TN, false, false, false, false, false>,
-        ss::scan_seq<TIn, SC, NSW, TN, false, false, true, false, false>,
-        ss::scan_seq<TIn, SC, NSW, TN, false, true, false, false, false>,
-        ss::scan_seq<TIn, SC, NSW, TN, false, true, true, false, false>,
-        ss::scan_seq<TIn, SC, NSW, TW, true, false, false, false, false>,
-        ss::scan_seq<TIn, SC, NSW, TW, true, false, true, false, false>,
-        ss::scan_seq<TIn, SC, NSW, TW, true, true, false, false, false>,
-        ss::scan_seq<TIn, SC, NSW, TW, true, true, true, false, false>,
-        ss::scan_seq<TIn, SC, NSW, TN, false, false, false, true, false>,
-        ss::scan_seq<TIn, SC, NSW, TN, false, false, true, true, false>,
-        ss::scan_seq<TIn, SC, NSW, TN, false, true, false, true, false>,
-        ss::scan_seq<TIn, SC, NSW, TN, false, true, true, true, false>,
-        ss::scan_seq<TIn, SC, NSW, TN, false, false, false, false, true>,
-        ss::scan_seq<TIn, SC, NSW, TN, false, true, false, false, true>,
-        ss::scan_seq<TIn, SC, NSW, TW, true, false, false, false, true>,
-        ss::scan_seq<TIn, SC, NSW, TW, true, true, false, false, true>,
-        dz_kernel<TIn, SC, NSW, TN, false, false>(),
-        dz_kernel<TIn, SC, NSW, TN, false, true>(),
-        dz_kernel<TIn, SC, NSW, TW, true, false>(),
-        dz_kernel<TIn, SC, NSW, TW, true, true>(),
-        dz_kernel<TIn, SC, NSW, TN, false, false, true>(),
-        dz_kernel<TIn, SC, NSW, TN, false, true, true>()};
-    const Kern kern = kernels[variant];
-    if (!kern) return SS_ERR_UNSUPPORTED;
-    const size_t lds = wide ? ss::SeqLds<TW, SC, SC * NSW, sizeof(TIn), true>::bytes
-                            : ss::SeqLds<TN, SC, SC * NSW, sizeof(TIn), false>::bytes;
-
-    const int cus = device_cus();
-    const int per_cu = resident_per_cu(reinterpret_cast<const void*>(kern), threads, lds);
-    int K = choose_segments(G, p.L, T, int64_t(std::max(cus, 0)) * per_cu);
-    while (K > 1 && G * K > kMaxWorkgroups) K--;   // a launch holds fewer than 2^32 work-items
-    int64_t Lseg = (p.L + K - 1) / K;
-    Lseg = (Lseg + T - 1) / T * T;
-    K = int((p.L + Lseg - 1) / Lseg);
-    p.K = K;
-    p.Lseg = Lseg;
-    char* base = static_cast<char*>(ws);
-    p.ctl = reinterpret_cast<uint32_t*>(base);
-    p.handoff = reinterpret_cast<float*>(base + w.ctl);
-    if (K > 1) {
-        const size_t words = size_t(ss::kFlagOffset) + size_t(G) * K;
-        const int rb = int(std::min<size_t>(1024, (words + 255) / 256));
-        hipLaunchKernelGGL(ss::scan_ctl_reset, dim3(rb), dim3(256), 0, st, p.ctl, int64_t(words));
-        if (hipGetLastError() != hipSuccess) return SS_ERR_HIP;
-    }
-    hipLaunchKernelGGL(kern, dim3(unsigned(G * K)), dim3(threads), lds, st, p);
-    return hipGetLastError() == hipSuccess ? SS_OK : SS_ERR_HIP;
 }
 
 template <typename TIn>
@@ -633,15 +440,8 @@ SS_EXPORT int ss_cross_scan_fwd(const void* x, const void* delta, const float* A
 
 namespace {
 
+using namespace ss_host;
 using ss::BwdParams;
-
-// Recurrence waves and states per wave of scan_bwd (n <= 32).
-SeqShape bwd_shape(int64_t n) {
-    if (n <= 2) return {1, 2};
-    if (n <= 8) return {4, 2};
-    if (n <= 16) return {8, 2};
-    return {8, 4};
-}
 
 // Workspace of ss_scan_bwd, in order: the forward's checkpoints, the dB and dC
 // partials per channel group, the dA_log, dD and dbias partials per segment
@@ -667,42 +467,6 @@ BwdWorkspace bwd_workspace(int64_t b, int64_t L, int64_t d_in, int64_t n) {
     w.fwd = seq_workspace(b, L, d_in, n).total;
     w.total = w.ckpt + w.part_B + w.part_C + w.part_A + w.part_D + w.part_bias + w.ctl + w.handoff + w.fwd;
     return w;
-}
-
-// Launches scan_bwd, cut into segments along L as the forward is (same rule:
-// balance the resident workgroups); p.K and p.Lseg are set here and the
-// number of segments is returned in *segments.
-template <typename TIn, int SC, int NSW>
-int launch_bwd(BwdParams p, bool gate, bool zoh, hipStream_t st, int* segments) {
-    constexpr int threads = (SC + 4) * 64;
-    constexpr int T = ss::kCkptSteps;
-    using Kern = void (*)(BwdParams);
-    static constexpr Kern kernels[8] = {
-        ss::scan_bwd<TIn, SC, NSW, false, false, false>, ss::scan_bwd<TIn, SC, NSW, false, true, false>,
-        ss::scan_bwd<TIn, SC, NSW, true, false, false>,  ss::scan_bwd<TIn, SC, NSW, true, true, false>,
-        ss::scan_bwd<TIn, SC, NSW, false, false, true>,  ss::scan_bwd<TIn, SC, NSW, false, true, true>,
-        ss::scan_bwd<TIn, SC, NSW, true, false, true>,   ss::scan_bwd<TIn, SC, NSW, true, true, true>};
-    const Kern kern = kernels[(zoh ? 4 : 0) | (p.softplus ? 2 : 0) | (gate ? 1 : 0)];
-    const size_t lds = ss::BwdLds<SC, SC * NSW>::bytes;
-    const int64_t G = p.b * p.nblk_d;
-    const int cus = device_cus();
-    const int per_cu = resident_per_cu(reinterpret_cast<const void*>(kern), threads, lds);
-    int K = choose_segments(G, p.L, T, int64_t(std::max(cus, 0)) * per_cu);
-    while (K > 1 && G * K > kMaxWorkgroups) K--;
-    int64_t Lseg = (p.L + K - 1) / K;
-    Lseg = (Lseg + T - 1) / T * T;
-    K = int((p.L + Lseg - 1) / Lseg);
-    p.K = K;
-    p.Lseg = Lseg;
-    *segments = K;
-    if (K > 1) {
-        const size_t words = size_t(ss::kFlagOffset) + size_t(G) * K;
-        const int rb = int(std::min<size_t>(1024, (words + 255) / 256));
-        hipLaunchKernelGGL(ss::scan_ctl_reset, dim3(rb), dim3(256), 0, st, p.ctl, int64_t(words));
-        if (hipGetLastError() != hipSuccess) return SS_ERR_HIP;
-    }
-    hipLaunchKernelGGL(kern, dim3(unsigned(G * K)), dim3(threads), lds, st, p);
-    return hipGetLastError() == hipSuccess ? SS_OK : SS_ERR_HIP;
 }
 
 template <typename TIn>
