@@ -81,11 +81,14 @@ __global__ __launch_bounds__(256) void state_update_vec(const StepParams p) {
     const int64_t d = ch - bi * p.d_in;
     const int64_t n = p.n;
 
+    // The state is read once and written once per step: non-temporal
+    // accesses (the state is the bulk of the traffic and no other access of
+    // this step reuses it), issued first, as the longest wait.
+    typedef float f4v __attribute__((ext_vector_type(4)));
+    f4v* sp = reinterpret_cast<f4v*>(p.state) + ch * LPC + q;
+    f4v s = __builtin_nontemporal_load(sp);
     const float xv = Elem<TIn>::load(xp, ch);
     const float dl = step_size(Elem<TIn>::load(dtp, ch), p.bias ? p.bias[d] : 0.0f, p.softplus);
-
-    float4* sp = reinterpret_cast<float4*>(p.state) + ch * LPC + q;
-    float4 s = *sp;
     const float4 al = reinterpret_cast<const float4*>(p.A_log)[d * LPC + q];
     const float4 Bv = load4<TIn>(Bm, bi * n + 4 * q);
     const float4 Cv = load4<TIn>(Cm, bi * n + 4 * q);
@@ -94,7 +97,7 @@ __global__ __launch_bounds__(256) void state_update_vec(const StepParams p) {
     s.y = step_state(s.y, dl, xv, al.y, Bv.y, p.zoh);
     s.z = step_state(s.z, dl, xv, al.z, Bv.z, p.zoh);
     s.w = step_state(s.w, dl, xv, al.w, Bv.w, p.zoh);
-    *sp = s;
+    __builtin_nontemporal_store(s, sp);
 
     float acc = fmaf(Cv.x, s.x, fmaf(Cv.y, s.y, fmaf(Cv.z, s.z, Cv.w * s.w)));
 #pragma unroll
