@@ -71,7 +71,7 @@ def cross_bytes(maps, L, d, n, s, bias=False):
 
 # Sources of the forward scan kernel (scan_seq) and its launch: the measured
 # traffic in profiles/traffic.json is used only while these are unchanged.
-SCAN_KERNEL_SOURCES = ("scan_kernels.h", "ss_device.h", "ss_scan.hip")
+SCAN_KERNEL_SOURCES = ("scan_kernels.h", "ss_device.h", "ss_host.h", "launch_seq.h")
 
 
 def kernel_source_hash() -> str:
