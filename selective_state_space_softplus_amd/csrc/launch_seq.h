@@ -25,26 +25,22 @@ int launch_seq(ss::ScanParams p, SeqMode mode, void* ws, size_t ws_bytes, hipStr
     const SeqWorkspace w = seq_workspace(p.b, p.L, p.d_in, p.n);
     if (!ws || ws_bytes < w.total) return SS_ERR_WORKSPACE;
 
-    // Wide path: whole 16-byte pieces per row and 16-byte aligned u, delta, z;
-    // y aligned for V-element stores (the cross scan adds to y element by
-    // element).  The zero-order-hold kernels exist in the element-load form
-    // only: their recurrence costs about three times the Euler one, which
-    // hides the difference in load width.  The cross scan has no gate.
+    // Wide path: whole 16-byte pieces per row and 16-byte aligned u, delta, z
+    // (and dy); y (dz) aligned for V-element stores (the cross scan adds to y
+    // element by element).  The cross scan has no gate.
     const bool dz = mode == SeqMode::Dz || mode == SeqMode::ZohDz;
     const void* out = dz ? p.dz : p.y;
-    const bool wide = mode != SeqMode::Zoh && mode != SeqMode::ZohDz && (p.d_in * int64_t(sizeof(TIn))) % 16 == 0 &&
-                      aligned(p.u, 16) &&
+    const bool wide = (p.d_in * int64_t(sizeof(TIn))) % 16 == 0 && aligned(p.u, 16) &&
                       aligned(p.delta, 16) && (!p.z || aligned(p.z, 16)) &&
                       (!dz || aligned(p.dy, 16)) &&
                       (mode == SeqMode::Cross || aligned(out, (TW / ss::kSeqElemWaves) * sizeof(TIn)));
     const int T = wide ? TW : TN;
     const int variant = mode == SeqMode::Cross   ? 12 + (wide ? 2 : 0) + (p.softplus ? 1 : 0)
                         : mode == SeqMode::Dz    ? 16 + (wide ? 2 : 0) + (p.softplus ? 1 : 0)
-                        : mode == SeqMode::ZohDz ? 20 + (p.softplus ? 1 : 0)
-                                               : ((mode == SeqMode::Zoh ? 8 : wide ? 4 : 0) | (p.softplus ? 2 : 0) |
-                                                  (p.z ? 1 : 0));
+                        : mode == SeqMode::ZohDz ? 20 + (wide ? 2 : 0) + (p.softplus ? 1 : 0)
+                        : ((mode == SeqMode::Zoh ? (wide ? 24 : 8) : wide ? 4 : 0) | (p.softplus ? 2 : 0) | (p.z ? 1 : 0));
     using Kern = void (*)(ss::ScanParams);
-    static constexpr Kern kernels[22] = {
+    static constexpr Kern kernels[28] = {
         ss::scan_seq<TIn, SC, NSW, TN, false, false, false, false, false>,
         ss::scan_seq<TIn, SC, NSW, TN, false, false, true, false, false>,
         ss::scan_seq<TIn, SC, NSW, TN, false, true, false, false, false>,
@@ -66,7 +62,13 @@ int launch_seq(ss::ScanParams p, SeqMode mode, void* ws, size_t ws_bytes, hipStr
         dz_kernel<TIn, SC, NSW, TW, true, false>(),
         dz_kernel<TIn, SC, NSW, TW, true, true>(),
         dz_kernel<TIn, SC, NSW, TN, false, false, true>(),
-        dz_kernel<TIn, SC, NSW, TN, false, true, true>()};
+        dz_kernel<TIn, SC, NSW, TN, false, true, true>(),
+        dz_kernel<TIn, SC, NSW, TW, true, false, true>(),
+        dz_kernel<TIn, SC, NSW, TW, true, true, true>(),
+        ss::scan_seq<TIn, SC, NSW, TW, true, false, false, true, false>,
+        ss::scan_seq<TIn, SC, NSW, TW, true, false, true, true, false>,
+        ss::scan_seq<TIn, SC, NSW, TW, true, true, false, true, false>,
+        ss::scan_seq<TIn, SC, NSW, TW, true, true, true, true, false>};
     const Kern kern = kernels[variant];
     if (!kern) return SS_ERR_UNSUPPORTED;
     const size_t lds = wide ? ss::SeqLds<TW, SC, SC * NSW, sizeof(TIn), true>::bytes
