@@ -540,10 +540,13 @@ __global__ __launch_bounds__((SC + 4) * 64) void scan_bwd(const BwdParams p) {
     // compiler would otherwise emit them as functions, with their arrays in
     // scratch memory and LDS reached through generic pointers.)
     // Iteration i: the recurrence waves take chunk c = kcl - i; the
-    // element waves issue the loads of chunk c - 2, finish chunk c + 1 and
-    // prepare chunk c - 1.  Ring slots: LDS (Delta, w, dy', u) and the kept
+    // element waves issue the loads of chunk c - 1 - AHEAD, finish chunk c + 1
+    // and prepare chunk c - 1.  Ring slots: LDS (Delta, w, dy', u) and the kept
     // values by i % 3 (compile-time: the loops are unrolled by three), the raw
-    // loads by the iteration that issued them, the two-slot LDS rings by i & 1.
+    // words of chunk x in slot (kcl - x - 2) % 3, the two-slot LDS rings by
+    // i & 1.  AHEAD = 2 (loads two iterations before their use) where the
+    // registers allow the third chunk in flight, else 1.
+    constexpr int AHEAD = NP <= 16 ? 2 : 1;
     const int niter = (kcl - kc0 + 2 + 2) / 3 * 3;
     using I0 = std::integral_constant<int, 0>;
     using I1 = std::integral_constant<int, 1>;
@@ -552,6 +555,7 @@ __global__ __launch_bounds__((SC + 4) * 64) void scan_bwd(const BwdParams p) {
         load_chunk(raw[1], kcl);
         prepare(raw[1], keep[0], kcl, 0, 0);
         load_chunk(raw[2], kcl - 1);
+        if (AHEAD == 2) load_chunk(raw[0], kcl - 2);
     }
     barrier_lds();
     auto rec_iter = [&](auto ph, int i) __attribute__((always_inline)) {
@@ -563,7 +567,7 @@ __global__ __launch_bounds__((SC + 4) * 64) void scan_bwd(const BwdParams p) {
     auto elem_iter = [&](auto ph, int i) __attribute__((always_inline)) {
         constexpr int PH = decltype(ph)::value;
         const int c = kcl - i;
-        load_chunk(raw[PH], c - 2);
+        load_chunk(raw[(PH + AHEAD - 1) % 3], c - 1 - AHEAD);
         if (c + 1 >= kc0 && c + 1 <= kcl) finalize(keep[(PH + 2) % 3], c + 1, (PH + 2) % 3, (i + 1) & 1);
         if (c - 1 >= kc0) prepare(raw[(PH + 2) % 3], keep[(PH + 1) % 3], c - 1, (PH + 1) % 3, (i + 1) & 1);
         barrier_lds();
