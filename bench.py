@@ -196,7 +196,8 @@ def main(argv=None):
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16 in/out, fp32 state and math",
+        "dtype": "f32",                           # the arithmetic: state, recurrence and readout in fp32
+        "io_dtype": "bf16",                       # u, delta, z, B, C read and y written as bf16
         "data": "synthetic (seeded N(0,1) inputs, delta ~ N(0,1)-2 plus bias ~ U(log 1e-3, log 1e-1), A_log = log(1..16))",
         "config": {"workload": f"{cfg.name}: selective scan fwd b={cfg.b} L={cfg.L} d_in={cfg.d_in} n={cfg.n}, "
                                "bf16, gated, delta bias + softplus, last state written",
