@@ -224,7 +224,7 @@ int ss_cross_scan_fwd(const void *x, const void *delta, const float *A_log,
                       int dtype, void *workspace, size_t workspace_bytes, void *stream);
 
 /* Largest state size n of ss_scan_bwd. */
-#define SS_MAX_BWD_STATE 32
+#define SS_MAX_BWD_STATE 64
 
 /* Bytes of device workspace ss_scan_bwd needs (0 for invalid arguments). */
 size_t ss_scan_bwd_workspace_bytes(int64_t b, int64_t L, int64_t d_in, int64_t n, int dtype);

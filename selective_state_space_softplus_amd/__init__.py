@@ -54,7 +54,7 @@ SS_F32 = 0
 SS_BF16 = 1
 SS_MAX_STATE = 64
 SS_MAX_CONV_WIDTH = 8
-SS_MAX_BWD_STATE = 32
+SS_MAX_BWD_STATE = 64
 SS_DISC_EULER = 0
 SS_DISC_ZOH = 1
 STATUS = {0: "SS_OK", -1: "SS_ERR_NULL", -2: "SS_ERR_SHAPE", -3: "SS_ERR_DTYPE", -4: "SS_ERR_UNSUPPORTED",

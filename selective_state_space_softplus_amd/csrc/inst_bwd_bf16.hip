@@ -6,4 +6,5 @@ template int launch_bwd<uint16_t, 1, 2>(ss::BwdParams, bool, bool, hipStream_t, 
 template int launch_bwd<uint16_t, 4, 2>(ss::BwdParams, bool, bool, hipStream_t, int*);
 template int launch_bwd<uint16_t, 8, 2>(ss::BwdParams, bool, bool, hipStream_t, int*);
 template int launch_bwd<uint16_t, 8, 4>(ss::BwdParams, bool, bool, hipStream_t, int*);
+template int launch_bwd<uint16_t, 8, 8>(ss::BwdParams, bool, bool, hipStream_t, int*);
 }  // namespace ss_host

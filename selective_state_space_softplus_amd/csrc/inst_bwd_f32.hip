@@ -6,4 +6,5 @@ template int launch_bwd<float, 1, 2>(ss::BwdParams, bool, bool, hipStream_t, int
 template int launch_bwd<float, 4, 2>(ss::BwdParams, bool, bool, hipStream_t, int*);
 template int launch_bwd<float, 8, 2>(ss::BwdParams, bool, bool, hipStream_t, int*);
 template int launch_bwd<float, 8, 4>(ss::BwdParams, bool, bool, hipStream_t, int*);
+template int launch_bwd<float, 8, 8>(ss::BwdParams, bool, bool, hipStream_t, int*);
 }  // namespace ss_host

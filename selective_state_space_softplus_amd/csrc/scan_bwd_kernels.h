@@ -307,9 +307,18 @@ __global__ __launch_bounds__((SC + 4) * 64) void scan_bwd(const BwdParams p) {
         off_ck[m] = ck_has[m] ? uint32_t(kk * d_in + dd) * 4u : 0u;
         off_h0[m] = ck_has[m] ? uint32_t(dd * n + kk) * 4u : 0u;
     }
-    // Element threads that write a dB, dC word of a chunk (T n <= T NP <= NE).
-    const int pf_j = etid / max(n, 1), pf_kk = etid - pf_j * max(n, 1);
-    const bool pf_has = !rec && etid < T * n;
+    // dB, dC words of a chunk written by this element thread (without the
+    // partial rows): word f = m NE + etid < T n is (step f / n, state f % n).
+    constexpr int PFN = (T * NP + NE - 1) / NE;
+    int pf_j[PFN], pf_kk[PFN];
+    bool pf_has[PFN];
+#pragma unroll
+    for (int m = 0; m < PFN; m++) {
+        const int f = m * NE + etid;
+        pf_j[m] = f / max(n, 1);
+        pf_kk[m] = f - pf_j[m] * max(n, 1);
+        pf_has[m] = !rec && f < T * n;
+    }
     // RL: partial row g = ((j SC + w) NSW/2 + pair) 4 + r of a chunk holds,
     // for r = 0, 1, 2, 3, dB of state 2 pair, its dC, dB of the next state,
     // its dC (the row order of wave_part4); element thread etid adds rows
@@ -455,20 +464,36 @@ __global__ __launch_bounds__((SC + 4) * 64) void scan_bwd(const BwdParams p) {
                 sum += e.x; sum += e.y; sum += e.z; sum += e.w;
                 (red_c[m] ? p.part_C : p.part_B)[ob + red_off[m]] = sum;
             }
-        } else if (pf_has && k * T + pf_j < L) {
-            p.part_B[ob + etid] = s_dbc[((s2 * T + pf_j) * 2 + 0) * NP + pf_kk];
-            p.part_C[ob + etid] = s_dbc[((s2 * T + pf_j) * 2 + 1) * NP + pf_kk];
+        } else {
+#pragma unroll
+            for (int m = 0; m < PFN; m++) {
+                if (!pf_has[m] || k * T + pf_j[m] >= L) continue;
+                p.part_B[ob + m * NE + etid] = s_dbc[((s2 * T + pf_j[m]) * 2 + 0) * NP + pf_kk[m]];
+                p.part_C[ob + m * NE + etid] = s_dbc[((s2 * T + pf_j[m]) * 2 + 1) * NP + pf_kk[m]];
+            }
         }
     };
     // Recurrence waves, chunk c: recompute its states, then the adjoint back through them.
+    // The recurrence waves keep TH steps of states and decays (and hold
+    // weights) in registers at once and run a chunk in T / TH passes, latest
+    // first: each pass recomputes the chunk from its entering state up to the
+    // end of its steps, then takes the adjoint back through them.  TH < T
+    // only with 8 states per wave (n > 32), where a whole chunk's values would
+    // not fit the register file.
+    constexpr int TH = NSW >= 8 ? T / 2 : T;
     auto process = [&](int c, int s3, int s2) __attribute__((always_inline)) {
-        float hstart[NSW], h[NSW];
+        float hstart[NSW];
 #pragma unroll
-        for (int q = 0; q < NSW; q++) h[q] = hstart[q] = s_ck[(s2 * NP + n0 + q) * 64 + lane];
+        for (int q = 0; q < NSW; q++) hstart[q] = s_ck[(s2 * NP + n0 + q) * 64 + lane];
         const float* bcw = s_bc + s2 * (T * 2 * NP) + wave * 2 * NSW;
-        float hs[T][NSW], as[T][NSW], bs[ZOH ? T : 1][NSW];   // states, decays, hold weights
 #pragma unroll
-        for (int j = 0; j < T; j++) {
+        for (int j0 = T - TH; j0 >= 0; j0 -= TH) {
+        float h[NSW], hin[NSW];                                     // running state; state entering step j0
+        float hs[TH][NSW], as[TH][NSW], bs[ZOH ? TH : 1][NSW];   // states, decays, hold weights of steps j0 ..
+#pragma unroll
+        for (int q = 0; q < NSW; q++) h[q] = hin[q] = hstart[q];
+#pragma unroll
+        for (int j = 0; j < j0 + TH; j++) {
             const float4 pr = s_prep[(s3 * T + j) * 64 + lane];
 #pragma unroll
             for (int q = 0; q < NSW; q++) {
@@ -477,35 +502,38 @@ __global__ __launch_bounds__((SC + 4) * 64) void scan_bwd(const BwdParams p) {
                 if constexpr (ZOH) {
                     const float beta = zoh_weight(pr.x, x2, a, invA[q]);
                     h[q] = fmaf(a, h[q], beta * (pr.y * bcw[j * SC * 2 * NSW + q]));
-                    bs[j][q] = beta;
+                    if (j >= j0) bs[j - j0][q] = beta;
                 } else {
                     h[q] = fmaf(a, h[q], pr.y * bcw[j * SC * 2 * NSW + q]);
                 }
-                hs[j][q] = h[q];
-                as[j][q] = a;
+                if (j >= j0) {
+                    hs[j - j0][q] = h[q];
+                    as[j - j0][q] = a;
+                }
+                if (j == j0 - 1) hin[q] = h[q];
             }
         }
 #pragma unroll
-        for (int j = T - 1; j >= 0; j--) {
+        for (int j = j0 + TH - 1; j >= j0; j--) {
             const float4 pr = s_prep[(s3 * T + j) * 64 + lane];
             float S1 = 0.0f, S2 = 0.0f, S3 = 0.0f, dBv[NSW], dCv[NSW];
 #pragma unroll
             for (int q = 0; q < NSW; q++) {
                 const float Bq = bcw[j * SC * 2 * NSW + q], Cq = bcw[j * SC * 2 * NSW + NSW + q];
                 g[q] = fmaf(pr.z, Cq, g[q]);
-                const float hp = j > 0 ? hs[j - 1][q] : hstart[q];
-                const float ga = g[q] * as[j][q];
+                const float hp = j > j0 ? hs[j - j0 - 1][q] : hin[q];
+                const float ga = g[q] * as[j - j0][q];
                 const float gah = ga * hp;
                 S2 = fmaf(gah, An[q], S2);
                 dA[q] = fmaf(gah, pr.x, dA[q]);
-                dCv[q] = pr.z * hs[j][q];
+                dCv[q] = pr.z * hs[j - j0][q];
                 if constexpr (ZOH) {
                     // beta = (a - 1)/A: d beta/dDelta = a, d beta/dA = (Delta a - beta)/A.
-                    const float beta = bs[j][q];
+                    const float beta = bs[j - j0][q];
                     const float gb = g[q] * beta;
                     S1 = fmaf(gb, Bq, S1);
                     S3 = fmaf(ga, Bq, S3);
-                    dA[q] = fmaf(g[q] * (pr.y * Bq), fmaf(pr.x, as[j][q], -beta) * invA[q], dA[q]);
+                    dA[q] = fmaf(g[q] * (pr.y * Bq), fmaf(pr.x, as[j - j0][q], -beta) * invA[q], dA[q]);
                     dBv[q] = gb * pr.y;
                 } else {
                     S1 = fmaf(g[q], Bq, S1);
@@ -533,6 +561,7 @@ __global__ __launch_bounds__((SC + 4) * 64) void scan_bwd(const BwdParams p) {
                     }
                 }
             }
+        }
         }
     };
 

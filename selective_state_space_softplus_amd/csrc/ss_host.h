@@ -50,12 +50,13 @@ inline SeqShape seq_shape(int64_t n) {
     return {8, 8};
 }
 
-// Recurrence waves and states per wave of scan_bwd (n <= 32).
+// Recurrence waves and states per wave of scan_bwd (n <= 64).
 inline SeqShape bwd_shape(int64_t n) {
     if (n <= 2) return {1, 2};
     if (n <= 8) return {4, 2};
     if (n <= 16) return {8, 2};
-    return {8, 4};
+    if (n <= 32) return {8, 4};
+    return {8, 8};
 }
 
 // Workspace of scan_seq, in order: control words (ticket, error, one flag per

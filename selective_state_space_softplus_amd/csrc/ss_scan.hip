@@ -475,7 +475,8 @@ int dispatch_bwd(const BwdParams& p, bool gate, bool zoh, hipStream_t st, int* s
     if (sh.SC == 1) return launch_bwd<TIn, 1, 2>(p, gate, zoh, st, segments);
     if (sh.SC == 4) return launch_bwd<TIn, 4, 2>(p, gate, zoh, st, segments);
     if (sh.NSW == 2) return launch_bwd<TIn, 8, 2>(p, gate, zoh, st, segments);
-    return launch_bwd<TIn, 8, 4>(p, gate, zoh, st, segments);
+    if (sh.NSW == 4) return launch_bwd<TIn, 8, 4>(p, gate, zoh, st, segments);
+    return launch_bwd<TIn, 8, 8>(p, gate, zoh, st, segments);
 }
 
 template <typename TOut>

@@ -287,7 +287,7 @@ def call_bwd(ss, a):
 @pytest.mark.parametrize("over,code", [
     (dict(u=None), NULL), (dict(dy=None), NULL), (dict(du=None), NULL), (dict(dA=None), NULL), (dict(dC=None), NULL),
     (dict(dz=None), NULL), (dict(b=0), SHAPE), (dict(L=-1), SHAPE), (dict(n=0), SHAPE), (dict(dtype=2), DTYPE),
-    (dict(n=33), UNSUP), (dict(ws=None), WS), (dict(ws_bytes=100), WS), (dict(ws=addr(21) + 128), ALIGN),
+    (dict(n=65), UNSUP), (dict(ws=None), WS), (dict(ws_bytes=100), WS), (dict(ws=addr(21) + 128), ALIGN),
     (dict(du=addr(12) + 1), ALIGN), (dict(dA=addr(14) + 2), ALIGN), (dict(dh0=addr(20) + 1), ALIGN),
     (dict(du=addr(1)), ALIAS), (dict(dB=addr(12)), ALIAS), (dict(dA=addr(3)), ALIAS), (dict(dh0=addr(9)), ALIAS),
     (dict(ws=addr(12)), ALIAS), (dict(dD=addr(19) - 8), ALIAS), (dict(dz=addr(21)), ALIAS),
@@ -304,7 +304,7 @@ def call_bwd_ex(ss, a, mode):
 
 
 @pytest.mark.parametrize("over,code", [
-    (dict(u=None), NULL), (dict(dz=None), NULL), (dict(b=0), SHAPE), (dict(dtype=2), DTYPE), (dict(n=33), UNSUP),
+    (dict(u=None), NULL), (dict(dz=None), NULL), (dict(b=0), SHAPE), (dict(dtype=2), DTYPE), (dict(n=65), UNSUP),
     (dict(ws_bytes=100), WS), (dict(du=addr(12) + 1), ALIGN), (dict(du=addr(1)), ALIAS),
 ])
 @pytest.mark.parametrize("mode", [0, 1])
@@ -325,4 +325,4 @@ def test_bwd_optional_pointers_may_be_null(ss):
 def test_bwd_workspace_query(ss):
     q = ss.lib.ss_scan_bwd_workspace_bytes
     assert q(4, 8192, 5120, 16, 1) > 4 * 1023 * 16 * 5120 * 4
-    assert q(4, 8192, 5120, 33, 1) == 0 and q(0, 1, 1, 1, 0) == 0 and q(1, 1, 1, 1, 3) == 0
+    assert q(4, 8192, 5120, 65, 1) == 0 and q(0, 1, 1, 1, 0) == 0 and q(1, 1, 1, 1, 3) == 0

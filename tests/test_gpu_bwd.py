@@ -71,6 +71,9 @@ CASES = [
     (1, 70, 66, 17, F32, True, True, True),
     (2, 61, 42, 32, F32, True, False, True),
     (1, 64, 128, 32, BF16, True, True, True),
+    (1, 70, 66, 40, F32, True, True, True),
+    (2, 61, 42, 64, F32, True, False, True),
+    (1, 64, 128, 64, BF16, True, True, True),
 ]
 
 
@@ -124,7 +127,7 @@ def test_bwd_long_workload_sampled(ss):
         assert_close(got["ddelta_bias"][d:d + 1], ref["ddelta_bias"], cfg.dtype, f"{cfg.name} dbias channel {d}")
 
 
-@pytest.mark.parametrize("segments,n,dtype", [(4, 16, BF16), (7, 1, F32), (3, 32, F32)])
+@pytest.mark.parametrize("segments,n,dtype", [(4, 16, BF16), (7, 1, F32), (3, 32, F32), (5, 64, F32)])
 def test_bwd_with_segments(ss, segments, n, dtype):
     """The forward pass inside the backward cut into segments: each piece saves only its own states."""
     say(f"bwd with {segments} forward segments n={n}")
@@ -168,7 +171,7 @@ def test_autograd_function(ss):
 
 ZOH_CASES = [c for c in CASES if c[:4] in ((2, 300, 130, 16), (1, 1, 1, 16), (1, 97, 65, 16), (2, 200, 40, 1),
                                           (1, 129, 70, 2), (2, 90, 24, 3), (1, 70, 66, 8), (2, 61, 42, 32),
-                                          (1, 64, 128, 32))]
+                                          (1, 64, 128, 32), (1, 70, 66, 40), (2, 61, 42, 64))]
 
 
 @pytest.mark.parametrize("case", ZOH_CASES, ids=[_id(c) for c in ZOH_CASES])
