@@ -667,16 +667,17 @@ __global__ __launch_bounds__((SC + 4) * 64) void scan_bwd(const BwdParams p) {
     }
 }
 
-// out[i] = scale_i * sum over g of part[g * count + i], added in the order
-// g = 0, 1, ...; scale_i = 1, written as TOut (fp32 or bf16 words).
+// out[i] = sum over g of part[g * count + i], added in the order g = 0, 1, ...
+// and written as TOut (fp32 or bf16 words); grid-stride, so the host may cap
+// the grid.
 template <typename TOut>
 __global__ __launch_bounds__(256) void reduce_groups(const float* __restrict__ part, TOut* __restrict__ out,
                                                      int64_t count, int groups) {
-    const int64_t i = blockIdx.x * int64_t(blockDim.x) + threadIdx.x;
-    if (i >= count) return;
-    float s = 0.0f;
-    for (int g = 0; g < groups; g++) s += part[int64_t(g) * count + i];
-    Elem<TOut>::store(out, i, s);
+    for (int64_t i = blockIdx.x * int64_t(blockDim.x) + threadIdx.x; i < count; i += int64_t(gridDim.x) * blockDim.x) {
+        float s = 0.0f;
+        for (int g = 0; g < groups; g++) s += part[int64_t(g) * count + i];
+        Elem<TOut>::store(out, i, s);
+    }
 }
 
 }  // namespace ss

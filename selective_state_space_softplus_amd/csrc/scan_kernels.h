@@ -14,12 +14,12 @@
 // in that direction's order; cross_merge then adds the four outputs back.
 //
 // scan_seq  (state sizes n >= 3).  One lane per channel d, 64 channels per
-//   workgroup; the n states of a channel are split across the S waves of the
-//   workgroup, NSW states per wave (4, or 8 above n = 32), so the B and C values a wave needs at
-//   step t are the same for all its lanes and come through scalar loads.
-//   The per-(b,t,d) work -- softplus, delta' u, the D skip, the gate and the
-//   sum of the S partial readouts -- is done once per element by the whole
-//   workgroup through LDS, not once per wave.  Time is walked in chunks of T
+//   workgroup; the n states of a channel are split across the SC recurrence
+//   waves of the workgroup, NSW states per wave (2, 4 or 8), so the B and C
+//   values a wave needs at step t are the same for all its lanes (wave-uniform
+//   LDS reads).  The per-(b,t,d) work -- softplus, delta' u, the D skip, the
+//   gate and the sum of the SC partial readouts -- is done once per element by
+//   the workgroup's element waves, not once per recurrence wave.  Time is walked in chunks of T
 //   steps.  L may be cut into K segments ("pieces"); workgroups take pieces in
 //   ticket order (an atomic counter), segment-major, and a piece starts from
 //   the state its predecessor segment published.  A piece therefore waits
@@ -428,7 +428,9 @@ __global__ __launch_bounds__((SC + kSeqElemWaves + 1) * 64) void scan_seq(const 
     };
     auto dma_bc = [&](const TIn* src, char* block, int k) {
         const int t0 = min(t_begin + k * T, t_end - 1);
-        const int last = (t_end - t0) * n - 1;     // last element of the valid rows
+        // Last element of the chunk's valid rows (at most T of them: the rows
+        // left in a long segment times n would overflow 32 bits).
+        const int last = min(T, t_end - t0) * n - 1;
         const TIn* base = src + (brow + t0) * n;
 #pragma unroll
         for (int ii = 0; ii < BI; ii++)
@@ -737,41 +739,43 @@ __global__ __launch_bounds__((SC + kSeqElemWaves + 1) * 64) void scan_seq(const 
 // CrossMerge: y[m, p, :] = sum over the four directions k of ys[m, k, t_k(p), :],
 // t_k(p) the step at which direction k visits map position p (the inverse of
 // the cross scan's traversal), added in the order k = 0, 1, 2, 3.  One thread
-// per VEC consecutive channels of a position; every read and the write are
-// whole rows of d_in channels.
+// per VEC consecutive channels of a position, grid-stride (the host caps the
+// grid, so any size launches); every read and the write are whole rows of
+// d_in channels.
 template <int VEC>
 __global__ __launch_bounds__(256) void cross_merge(const float* __restrict__ ys, float* __restrict__ y, int64_t maps,
                                                    int H, int W, int64_t d_in) {
     const int64_t L = int64_t(H) * W;
     const int64_t cpr = d_in / VEC;                           // thread columns per row
-    const int64_t i = blockIdx.x * int64_t(blockDim.x) + threadIdx.x;
-    if (i >= maps * L * cpr) return;
-    const int64_t row = i / cpr;                              // (m, p)
-    const int64_t c = (i - row * cpr) * VEC;
-    const int64_t m = row / L;
-    const int64_t pos = row - m * L;
-    const int64_t h = pos / W, w = pos - h * W;
-    const int64_t tc = w * H + h;                             // step of the column-major direction
-    const int64_t steps[4] = {pos, tc, L - 1 - pos, L - 1 - tc};
-    float acc[VEC];
+    const int64_t total = maps * L * cpr;
+    for (int64_t i = blockIdx.x * int64_t(blockDim.x) + threadIdx.x; i < total; i += int64_t(gridDim.x) * blockDim.x) {
+        const int64_t row = i / cpr;                          // (m, p)
+        const int64_t c = (i - row * cpr) * VEC;
+        const int64_t m = row / L;
+        const int64_t pos = row - m * L;
+        const int64_t h = pos / W, w = pos - h * W;
+        const int64_t tc = w * H + h;                         // step of the column-major direction
+        const int64_t steps[4] = {pos, tc, L - 1 - pos, L - 1 - tc};
+        float acc[VEC];
 #pragma unroll
-    for (int v = 0; v < VEC; v++) acc[v] = 0.0f;
+        for (int v = 0; v < VEC; v++) acc[v] = 0.0f;
 #pragma unroll
-    for (int k = 0; k < 4; k++) {
-        const float* src = ys + ((m * 4 + k) * L + steps[k]) * d_in + c;
-        if constexpr (VEC == 4) {
-            const float4 q = *reinterpret_cast<const float4*>(src);
-            acc[0] += q.x;
-            acc[1] += q.y;
-            acc[2] += q.z;
-            acc[3] += q.w;
-        } else {
-            acc[0] += src[0];
+        for (int k = 0; k < 4; k++) {
+            const float* src = ys + ((m * 4 + k) * L + steps[k]) * d_in + c;
+            if constexpr (VEC == 4) {
+                const float4 q = *reinterpret_cast<const float4*>(src);
+                acc[0] += q.x;
+                acc[1] += q.y;
+                acc[2] += q.z;
+                acc[3] += q.w;
+            } else {
+                acc[0] += src[0];
+            }
         }
+        float* dst = y + row * d_in + c;
+        if constexpr (VEC == 4) *reinterpret_cast<float4*>(dst) = make_float4(acc[0], acc[1], acc[2], acc[3]);
+        else dst[0] = acc[0];
     }
-    float* dst = y + row * d_in + c;
-    if constexpr (VEC == 4) *reinterpret_cast<float4*>(dst) = make_float4(acc[0], acc[1], acc[2], acc[3]);
-    else dst[0] = acc[0];
 }
 
 // Clears the ticket counter, the error word and the segment flags.

@@ -33,6 +33,13 @@ constexpr int64_t kMaxStepChannels = (int64_t(1) << 28) - 1;
 
 inline bool aligned(const void* p, size_t a) { return reinterpret_cast<uintptr_t>(p) % a == 0; }
 
+// Grid of a grid-stride kernel of 256-thread workgroups over `items` items:
+// one item per thread up to 2^20 workgroups, so the launch stays far below
+// the 2^32 - 1 work-items a launch may hold.
+inline dim3 grid_1d(int64_t items) {
+    return dim3(unsigned(std::max<int64_t>(1, std::min<int64_t>((items + 255) / 256, int64_t(1) << 20))));
+}
+
 struct SeqShape {
     int SC;    // recurrence waves per workgroup
     int NSW;   // states per recurrence wave

@@ -428,7 +428,7 @@ SS_EXPORT int ss_cross_scan_fwd(const void* x, const void* delta, const float* A
     // CrossMerge: the four directions' outputs added back at their positions.
     const bool vec = d_in % 4 == 0 && aligned(y, 16);
     const int64_t threads = maps * L * (vec ? d_in / 4 : d_in);
-    const dim3 grid(unsigned((threads + 255) / 256));
+    const dim3 grid = grid_1d(threads);
     if (vec)
         hipLaunchKernelGGL((ss::cross_merge<4>), grid, dim3(256), 0, st, ys, y, maps, int(H), int(W), d_in);
     else
@@ -481,7 +481,7 @@ int dispatch_bwd(const BwdParams& p, bool gate, bool zoh, hipStream_t st, int* s
 
 template <typename TOut>
 int reduce(const float* part, void* out, int64_t count, int64_t groups, hipStream_t st) {
-    hipLaunchKernelGGL((ss::reduce_groups<TOut>), dim3(unsigned((count + 255) / 256)), dim3(256), 0, st, part,
+    hipLaunchKernelGGL((ss::reduce_groups<TOut>), grid_1d(count), dim3(256), 0, st, part,
                        static_cast<TOut*>(out), count, int(groups));
     return hipGetLastError() == hipSuccess ? SS_OK : SS_ERR_HIP;
 }
