@@ -46,6 +46,15 @@
  *     step is the one in/out buffer and is updated in place, and the
  *     initial_state of ss_scan_fwd_ex may be its last_state buffer itself.
  *   - Pointers must be aligned to their element size (SS_ERR_ALIGN).
+ *   - Three environment variables, read at each call, change how the work
+ *     is split but not what is computed (tests and tuning use them):
+ *     SS_SCAN_SEGMENTS=K cuts L into K pieces (1..16) instead of the
+ *     occupancy-based choice; SS_SCAN_WAVES=4 takes 4 recurrence waves of
+ *     4 states for 9 <= n <= 16 (forward); SS_SCAN_VARIANT=tpar takes the
+ *     time-parallel forward kernel for n <= 2 (Euler input term, zero
+ *     initial state).  Results agree with the default
+ *     within the stated tolerances (the order of the fp32 additions
+ *     changes); each setting is deterministic run to run.
  */
 #ifndef SS_SCAN_H
 #define SS_SCAN_H
