@@ -1,9 +1,9 @@
 """GPU: a seeded sweep of random shapes and options against the oracle.
 
-Each case draws its sizes (b, L, d_in, n), the input type and the options
-(gate, bias, softplus, zero-order hold, initial state, final-state gradient,
-forced L segments) from its own seed, so a failure names a case that can be
-run again as it is.  Sizes stay small enough for the oracle to finish at once;
+Each case draws its sizes (b, L, d_in, n; the map sizes of the cross scan),
+the input type and the options (gate, bias, softplus, zero-order hold,
+initial state, final-state gradient, forced L segments) from its own seed, so
+a failure names a case that can be run again as it is.  Sizes stay small enough for the oracle to finish at once;
 they are chosen around the tile edges (chunks of 8 and 16 steps, groups of 64
 channels, 2, 4 and 8 states per recurrence wave).  Tolerances as everywhere:
 max relative error 1e-4 for fp32 inputs, 2e-2 for bf16 inputs.
@@ -16,6 +16,7 @@ import torch
 import oracle
 from tests.parity import assert_close
 from tests.test_gpu_bwd import compare, grads_gpu, grads_oracle
+from tests.test_gpu_cross import check as cross_check, cross_inputs
 from tests.test_gpu_parity import BF16, DEV, F32, env, say, small_inputs, to_dev
 
 pytestmark = [pytest.mark.gpu,
@@ -52,7 +53,7 @@ def dev(t):
     return None if t is None else t.to(DEV)
 
 
-@pytest.mark.parametrize("seed", range(3000, 3040))
+@pytest.mark.parametrize("seed", range(3000, 3200))
 def test_scan_sweep(ss, seed):
     c = draw(seed)
     say(f"scan sweep seed={seed} {c}")
@@ -68,7 +69,7 @@ def test_scan_sweep(ss, seed):
     assert_close(last, lr, c["dtype"], f"seed {seed} last_state")
 
 
-@pytest.mark.parametrize("seed", range(4000, 4030))
+@pytest.mark.parametrize("seed", range(4000, 4120))
 def test_bwd_sweep(ss, seed):
     c = draw(seed)
     say(f"bwd sweep seed={seed} {c}")
@@ -82,7 +83,7 @@ def test_bwd_sweep(ss, seed):
     compare(got, ref, c["dtype"], f"seed {seed}")
 
 
-@pytest.mark.parametrize("seed", range(5000, 5020))
+@pytest.mark.parametrize("seed", range(5000, 5060))
 def test_step_sweep(ss, seed):
     r = random.Random(seed)
     b, d_in, n = r.randint(1, 70), r.choice(CHANNELS), r.choice(STATES)
@@ -102,3 +103,12 @@ def test_step_sweep(ss, seed):
     sr, yr = oracle.state_update(state, x, dt, A_log, Bm, Cm, D, zz, bb, True, zoh=zoh)
     assert_close(y, yr, dtype, f"seed {seed} step y")
     assert_close(sg, sr, dtype, f"seed {seed} step state")
+
+
+@pytest.mark.parametrize("seed", range(6000, 6030))
+def test_cross_sweep(ss, seed):
+    r = random.Random(seed)
+    maps, H, W = r.randint(1, 3), r.randint(1, 12), r.randint(1, 12)
+    d_in, n, dtype, bias = r.choice(CHANNELS), r.choice(STATES), r.choice([F32, BF16]), r.random() < 0.6
+    say(f"cross sweep seed={seed} maps={maps} {H}x{W} d_in={d_in} n={n} {dtype} bias={bias}")
+    cross_check(ss, cross_inputs(maps, H, W, d_in, n, dtype, seed, bias=bias), f"seed {seed}")
