@@ -325,8 +325,30 @@ def main(argv=None):
         torch.cuda.synchronize()
         ms_h = e0.elapsed_time(e1) / (reps * dcfg.steps)
         del rot
+        # A plain device copy (torch) of one state, rotated over 6 buffer pairs
+        # in the same way: what a kernel of this size that reads and writes
+        # the state once reaches, beside the step's own rate.
+        src = [state.clone() for _ in range(nrot)]
+        dst = [torch.empty_like(state) for _ in range(nrot)]
+
+        def copy64():
+            for t in range(dcfg.steps):
+                dst[t % nrot].copy_(src[t % nrot])
+
+        copy64()
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(reps):
+            copy64()
+        e1.record()
+        torch.cuda.synchronize()
+        ms_c = e0.elapsed_time(e1) / (reps * dcfg.steps)
+        del src, dst
+        copy_gbps = 2 * state.numel() * state.element_size() / (ms_c * 1e-3) / 1e9
         result["decode"]["us_per_step_hbm"] = round(ms_h * 1e3, 2)
         result["decode"]["GBps_hbm"] = round(db / (ms_h * 1e-3) / 1e9, 1)
+        result["decode"]["state_copy_GBps"] = round(copy_gbps, 1)
+        result["decode"]["hbm_frac_of_state_copy"] = round(db / (ms_h * 1e-3) / 1e9 / copy_gbps, 3)
         result["decode"]["us_per_step_graph"] = round(ms_g * 1e3, 2)
         result["decode"]["GBps_graph"] = round(db / (ms_g * 1e-3) / 1e9, 1)
         result["decode"]["conv_step"] = {
