@@ -145,6 +145,55 @@ def copy_probe(torch, dev, nbytes=1 << 30, reps=5):
     return 0
 
 
+def shape_sweep(torch, ss, workloads, dev):
+    """Forward (and backward) throughput over state sizes, input types and the
+    zero-order hold at b=4, L=8192, d_in=5120, plus the b=8, L=2048, d_in=1536
+    scan: one JSON line per case, HIP events over 10 launches (5 for the
+    backward) after 0.3 s of untimed ones."""
+    cases = [(4, 8192, 5120, n, torch.bfloat16, False) for n in (1, 2, 4, 8, 16, 32, 64)]
+    cases += [(4, 8192, 5120, 16, torch.float32, False), (4, 8192, 5120, 16, torch.bfloat16, True),
+              (8, 2048, 1536, 16, torch.bfloat16, False)]
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+    def timed(fn, reps=10, settle_s=0.3):
+        # Untimed launches for settle_s seconds first: the GPU idles while the
+        # next case's inputs are generated and must raise its clocks again.
+        t0 = time.perf_counter()
+        while time.perf_counter() - t0 < settle_s:
+            fn()
+            torch.cuda.synchronize()
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    for b, L, d, n, dt, zoh in cases:
+        inp = workloads.random_scan_inputs(b, L, d, n, dtype=dt, seed=7, gated=True, bias=True)
+        g = {k: (v.to(dev) if isinstance(v, torch.Tensor) else v) for k, v in inp.items()}
+        del inp
+        args = (g["u"], g["delta"], g["A_log"], g["B"], g["C"], g["D"], g["z"], g["delta_bias"], True)
+        ms = timed(lambda: ss.scan_fwd(*args, return_last_state=True, zoh=zoh))
+        s = 2 if dt == torch.bfloat16 else 4
+        upd = b * L * d * n
+        row = {"b": b, "L": L, "d_in": d, "n": n, "io_dtype": "bf16" if s == 2 else "f32", "zoh": zoh,
+               "fwd_ms": round(ms, 4), "fwd_updates_per_s": float(f"{upd / (ms * 1e-3):.4g}"),
+               "fwd_GBps": round(scan_bytes(b, L, d, n, s) / (ms * 1e-3) / 1e9, 1)}
+        if n in (1, 16, 64) and not zoh:
+            dy = torch.randn_like(g["u"])
+            mb = timed(lambda: ss.scan_bwd(*args[:6], dy, g["z"], g["delta_bias"], True), reps=5)
+            row.update(bwd_ms=round(mb, 4), bwd_updates_per_s=float(f"{upd / (mb * 1e-3):.4g}"))
+            del dy
+        print(json.dumps(row), flush=True)
+        del g, args
+        torch.cuda.empty_cache()
+    return 0
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -158,6 +207,8 @@ def main(argv=None):
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target duration of the CPU baseline sample")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy (calibrates the HBM byte counters)")
+    ap.add_argument("--sweep", action="store_true",
+                    help="only time the forward and backward over state sizes, input types and shapes")
     args = ap.parse_args(argv)
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only: the scan shards over batch and channels with no communication, "
@@ -173,6 +224,8 @@ def main(argv=None):
     torch.cuda.set_device(0)
     if args.copy_probe:
         return copy_probe(torch, dev)
+    if args.sweep:
+        return shape_sweep(torch, ss, workloads, dev)
     cfg = workloads.CONFIGS[2]
     inp = workloads.scan_inputs(2)
     g = {k: (v.to(dev) if isinstance(v, torch.Tensor) else v) for k, v in inp.items()}
