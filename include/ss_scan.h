@@ -45,16 +45,12 @@
  *   - Outputs must not overlap any input (SS_ERR_ALIAS); the state of the
  *     step is the one in/out buffer and is updated in place, and the
  *     initial_state of ss_scan_fwd_ex may be its last_state buffer itself.
- *   - Pointers must be aligned to their element size (SS_ERR_ALIGN).
- *   - Three environment variables, read at each call, change how the work
- *     is split but not what is computed (tests and tuning use them):
- *     SS_SCAN_SEGMENTS=K cuts L into K pieces (1..16) instead of the
- *     occupancy-based choice; SS_SCAN_WAVES=4 takes 4 recurrence waves of
- *     4 states for 9 <= n <= 16 (forward); SS_SCAN_VARIANT=tpar takes the
- *     time-parallel forward kernel for n <= 2 (Euler input term, zero
- *     initial state).  Results agree with the default
- *     within the stated tolerances (the order of the fp32 additions
- *     changes); each setting is deterministic run to run.
+ *   - Pointers must be aligned to their element size (SS_ERR_ALIGN), and
+ *     workspaces to 256 bytes.
+ *   - A long scan is cut into segments along L that hand the state on
+ *     through the workspace; a segment waits (bounded) for its predecessor.
+ *     Such a wait cannot deadlock, but should one give up, the scan goes on
+ *     from NaN and records it: ss_scan_status then reports SS_ERR_TIMEOUT.
  */
 #ifndef SS_SCAN_H
 #define SS_SCAN_H
@@ -83,7 +79,8 @@ typedef enum {
     SS_ERR_HIP = -6,         /* the HIP runtime refused the launch                  */
     SS_ERR_ALIAS = -7,       /* an output overlaps an input                         */
     SS_ERR_ALIGN = -8,       /* a pointer is not aligned to its element size        */
-    SS_ERR_MODE = -9         /* discretization is not an ss_discretization value    */
+    SS_ERR_MODE = -9,        /* discretization is not an ss_discretization value    */
+    SS_ERR_TIMEOUT = -10     /* (ss_scan_status) a wait between segments gave up    */
 } ss_status;
 
 /* Input term of the recurrence (the _ex entry points). */
@@ -120,8 +117,9 @@ size_t ss_scan_fwd_workspace_bytes(int64_t b, int64_t L, int64_t d_in, int64_t n
  *   y          : (b, L, d_in)  dtype, output
  *   last_state : (b, d_in, n)  fp32, output h after the last step, or NULL
  *   workspace  : device memory of at least ss_scan_fwd_workspace_bytes()
- *                bytes (may be NULL when that is 0).  Its contents need no
- *                initialisation and are scratch after the call.
+ *                bytes, 256-byte aligned (SS_ERR_ALIGN otherwise).  Its
+ *                contents need no initialisation; after the call it holds
+ *                the call's status (ss_scan_status) and scratch.
  * Any n in 1..SS_MAX_STATE, d_in in 1..SS_MAX_CHANNELS and b, L >= 1 with
  * b * L * d_in <= 2^46, L < 2^31 - 1024 and b * ceil(d_in / 64) < 2^22 are
  * accepted (no tile multiples are required); other sizes give SS_ERR_SHAPE.
@@ -156,6 +154,16 @@ int ss_scan_fwd_ex(const void *u, const void *delta, const float *A_log,
                    void *y, float *last_state,
                    int64_t b, int64_t L, int64_t d_in, int64_t n, int dtype,
                    void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * Status a scan call left in its workspace, copied on `stream` (after that
+ * call, in stream order) to *status, one int32 in device memory (or host
+ * memory the device can write): SS_OK, or SS_ERR_TIMEOUT when a wait between
+ * segments of L gave up, in which case the outputs of that call hold NaN.
+ * workspace is the workspace passed to ss_scan_fwd(_ex), ss_cross_scan_fwd
+ * or ss_scan_bwd(_ex).  Returns an ss_status.
+ */
+int ss_scan_status(const void *workspace, size_t workspace_bytes, int32_t *status, void *stream);
 
 /*
  * One decode step on a persistent state (jiafeimiao.top page: Mamba.step and
@@ -317,6 +325,23 @@ int ss_conv_update(void *conv_state, const void *x, const float *weight,
 
 /* Static, NUL-terminated description of a status code. */
 const char *ss_status_string(int status);
+
+/*
+ * For tests and tuning only; never needed for correct results.  Overrides,
+ * process-wide and for every later call, how the scans split their work
+ * (each argument 0 = the library's own choice):
+ *   segments      : cut L into this many segments (1..16)
+ *   waves         : 4 = 4 recurrence waves of 4 states at 9 <= n <= 16
+ *   time_parallel : 1 = the time-parallel forward kernel for n <= 2
+ *                   (Euler input term, zero initial state)
+ *   spin_limit    : polls before a segment wait gives up
+ *   wait_never    : 1 = segment waits poll a word nothing sets, so each
+ *                   gives up after spin_limit polls (exercises SS_ERR_TIMEOUT)
+ * Results agree with the default within the stated tolerances (the order of
+ * fp32 additions may change) and are deterministic for each setting.
+ * Returns SS_OK, or SS_ERR_SHAPE for an argument out of range.
+ */
+int ss_set_test_plan(int segments, int waves, int time_parallel, int spin_limit, int wait_never);
 
 #ifdef __cplusplus
 }

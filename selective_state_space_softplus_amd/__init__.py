@@ -23,7 +23,14 @@ Entry points mirror the C ABI (``include/ss_scan.h``):
   conv_update(conv_state, x, weight, bias=None, silu=True)
                                              -> out (b, d_in)  (conv_state is updated in place)
   scan_fwd_workspace_bytes(b, L, d_in, n, dtype) -> int
+  scan_status(workspace) -> int    (SS_OK, or SS_ERR_TIMEOUT if a segment wait gave up)
   status_string(code) -> str
+  test_plan(segments=0, waves=0, time_parallel=0, spin_limit=0, wait_never=0)
+                                             context manager over ss_set_test_plan (tests, tuning)
+
+scan_fwd, cross_scan_fwd and scan_bwd take ``check=True`` to synchronise and
+raise SSError(SS_ERR_TIMEOUT) when the call's status says a wait between
+segments gave up (its outputs then hold NaN).
 
 Shapes follow the mhpn.cn selective_scan walk-through (section 2): u, delta
 (b, L, d_in); A_log (d_in, n) with A = -exp(A_log); B, C (b, L, n); D (d_in).
@@ -42,6 +49,7 @@ A_log (4, d_in, n); D, delta_bias (4, d_in); directions 0 row-major, 1 column-ma
 """
 from __future__ import annotations
 
+import contextlib
 import ctypes
 import os
 
@@ -57,11 +65,14 @@ SS_MAX_CONV_WIDTH = 8
 SS_MAX_BWD_STATE = 64
 SS_DISC_EULER = 0
 SS_DISC_ZOH = 1
+SS_ERR_TIMEOUT = -10
 STATUS = {0: "SS_OK", -1: "SS_ERR_NULL", -2: "SS_ERR_SHAPE", -3: "SS_ERR_DTYPE", -4: "SS_ERR_UNSUPPORTED",
-          -5: "SS_ERR_WORKSPACE", -6: "SS_ERR_HIP", -7: "SS_ERR_ALIAS", -8: "SS_ERR_ALIGN", -9: "SS_ERR_MODE"}
-EXPORTS = ("ss_scan_fwd_workspace_bytes", "ss_scan_fwd", "ss_scan_fwd_ex", "ss_state_update", "ss_state_update_ex",
-           "ss_scan_bwd", "ss_scan_bwd_ex", "ss_scan_bwd_workspace_bytes", "ss_cross_scan_fwd",
-           "ss_cross_scan_fwd_workspace_bytes", "ss_conv_update", "ss_status_string")
+          -5: "SS_ERR_WORKSPACE", -6: "SS_ERR_HIP", -7: "SS_ERR_ALIAS", -8: "SS_ERR_ALIGN", -9: "SS_ERR_MODE",
+          -10: "SS_ERR_TIMEOUT"}
+EXPORTS = ("ss_scan_fwd_workspace_bytes", "ss_scan_fwd", "ss_scan_fwd_ex", "ss_scan_status",
+           "ss_state_update", "ss_state_update_ex", "ss_scan_bwd", "ss_scan_bwd_ex", "ss_scan_bwd_workspace_bytes",
+           "ss_cross_scan_fwd", "ss_cross_scan_fwd_workspace_bytes", "ss_conv_update", "ss_status_string",
+           "ss_set_test_plan")
 
 
 class SSError(RuntimeError):
@@ -82,6 +93,10 @@ def _load() -> ctypes.CDLL:
     lib.ss_scan_fwd.argtypes = [P, P, P, P, P, P, P, P, I, P, P, I64, I64, I64, I64, I, P, ctypes.c_size_t, P]
     lib.ss_scan_fwd_ex.restype = I
     lib.ss_scan_fwd_ex.argtypes = [P, P, P, P, P, P, P, P, I, P, I, P, P, I64, I64, I64, I64, I, P, ctypes.c_size_t, P]
+    lib.ss_scan_status.restype = I
+    lib.ss_scan_status.argtypes = [P, ctypes.c_size_t, P, P]
+    lib.ss_set_test_plan.restype = I
+    lib.ss_set_test_plan.argtypes = [I, I, I, I, I]
     lib.ss_state_update.restype = I
     lib.ss_state_update.argtypes = [P, P, P, P, P, P, P, P, P, I, P, I64, I64, I64, I, P]
     lib.ss_state_update_ex.restype = I
@@ -145,6 +160,36 @@ def scan_fwd_workspace_bytes(b: int, L: int, d_in: int, n: int, dtype: int) -> i
     return int(lib.ss_scan_fwd_workspace_bytes(b, L, d_in, n, dtype))
 
 
+def scan_status(workspace) -> int:
+    """Status the last scan call with ``workspace`` left: SS_OK or SS_ERR_TIMEOUT.  Synchronises the stream."""
+    dev = workspace.device
+    out = torch.empty(1, dtype=torch.int32, device=dev)
+    nbytes = workspace.numel() * workspace.element_size()
+    with torch.cuda.device(dev):
+        rc = lib.ss_scan_status(_ptr(workspace), nbytes, _ptr(out), _stream(dev))
+    if rc != 0:
+        raise SSError(rc, "ss_scan_status")
+    return int(out.item())
+
+
+def _raise_on_timeout(workspace, where):
+    code = scan_status(workspace)
+    if code != 0:
+        raise SSError(code, where)
+
+
+@contextlib.contextmanager
+def test_plan(segments=0, waves=0, time_parallel=0, spin_limit=0, wait_never=0):
+    """Override how the scans split their work (ss_set_test_plan) inside a with block."""
+    rc = lib.ss_set_test_plan(int(segments), int(waves), int(time_parallel), int(spin_limit), int(wait_never))
+    if rc != 0:
+        raise SSError(rc, "ss_set_test_plan")
+    try:
+        yield
+    finally:
+        lib.ss_set_test_plan(0, 0, 0, 0, 0)
+
+
 _workspaces: dict = {}
 
 
@@ -161,10 +206,11 @@ def _workspace(device, nbytes: int):
 
 
 def scan_fwd(u, delta, A_log, B, C, D, z=None, delta_bias=None, delta_softplus=True, return_last_state=False,
-             out=None, last_state=None, workspace=None, initial_state=None, zoh=False):
+             out=None, last_state=None, workspace=None, initial_state=None, zoh=False, check=False):
     """Selective scan forward on the GPU; returns y (and last_state if asked).
 
     ``initial_state`` may be the ``last_state`` buffer itself (carried over in place).
+    ``check``: synchronise and raise if a wait between segments gave up.
     """
     if u.dim() != 3 or A_log.dim() != 2:
         raise ValueError("u must be (b, L, d_in) and A_log (d_in, n)")
@@ -213,6 +259,8 @@ def scan_fwd(u, delta, A_log, B, C, D, z=None, delta_bias=None, delta_softplus=T
                                     b, L, d_in, n, code, ws_ptr, ws_bytes, _stream(dev))
     if rc != 0:
         raise SSError(rc, where)
+    if check:
+        _raise_on_timeout(workspace, where)
     return (y, last_state) if return_last_state else y
 
 
@@ -276,7 +324,7 @@ def conv_update(conv_state, x, weight, bias=None, silu=True, out=None):
 
 
 def cross_scan_fwd(x, delta, A_log, B, C, D, delta_bias=None, delta_softplus=True, return_last_state=False,
-                   out=None, last_state=None, workspace=None):
+                   out=None, last_state=None, workspace=None, check=False):
     """VMamba cross scan + merge on the GPU; returns y (maps, H, W, d_in) fp32 (and last_state (maps, 4, d_in, n))."""
     if x.dim() != 4 or A_log.dim() != 3:
         raise ValueError("x must be (maps, H, W, d_in) and A_log (4, d_in, n)")
@@ -312,11 +360,13 @@ def cross_scan_fwd(x, delta, A_log, B, C, D, delta_bias=None, delta_softplus=Tru
                                    _ptr(workspace), ws_bytes, _stream(dev))
     if rc != 0:
         raise SSError(rc, "ss_cross_scan_fwd")
+    if check:
+        _raise_on_timeout(workspace, "ss_cross_scan_fwd")
     return (y, last_state) if return_last_state else y
 
 
 def scan_bwd(u, delta, A_log, B, C, D, dy, z=None, delta_bias=None, delta_softplus=True, initial_state=None,
-             dlast_state=None, workspace=None, zoh=False):
+             dlast_state=None, workspace=None, zoh=False, check=False):
     """Gradients of the scan for output gradients dy (and dlast_state): the delta' B u input term, or
     with zoh=True the zero-order hold's (ss_scan_bwd_ex).
 
@@ -369,6 +419,8 @@ def scan_bwd(u, delta, A_log, B, C, D, dy, z=None, delta_bias=None, delta_softpl
             rc = lib.ss_scan_bwd(*head, *tail)
     if rc != 0:
         raise SSError(rc, "ss_scan_bwd_ex" if zoh else "ss_scan_bwd")
+    if check:
+        _raise_on_timeout(workspace, "ss_scan_bwd_ex" if zoh else "ss_scan_bwd")
     return g
 
 

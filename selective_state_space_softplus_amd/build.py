@@ -20,10 +20,14 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIBRARY = os.path.join(PKG, "libss_scan.so")
-# The C ABI and the small kernels, then the scan_seq and scan_bwd launchers
-# per input type: separate translation units, compiled in parallel.
-SOURCES = [os.path.join(CSRC, name) for name in ("ss_scan.hip", "inst_seq_bf16.hip", "inst_seq_f32.hip",
-                                                 "inst_bwd_bf16.hip", "inst_bwd_f32.hip")]
+# The C ABI and the small kernels in one translation unit; the scan_seq and
+# scan_bwd launchers (launch_seq.h, launch_bwd.h) are instantiated once per
+# input type and launch shape, each in a small generated unit of its own, so
+# that the kernels compile in parallel.
+SOURCES = [os.path.join(CSRC, "ss_scan.hip")]
+INPUT_TYPES = ("uint16_t", "float")
+SEQ_SHAPES = ((1, 2), (4, 2), (4, 4), (8, 2), (8, 4), (8, 8))   # must cover ss_host::seq_shape
+BWD_SHAPES = ((1, 2), (4, 2), (8, 2), (8, 4), (8, 8))           # must cover ss_host::bwd_shape
 ARCH = os.environ.get("SS_OFFLOAD_ARCH", "gfx950")
 FLAGS = ["-O3", "-std=c++17", "-fPIC", "-fvisibility=hidden", "-Xclang", "-target-feature", "-Xclang",
          "-packed-fp32-ops"]
@@ -51,13 +55,33 @@ def _run(cmd: list[str], verbose: bool) -> None:
         raise RuntimeError(f"hipcc failed with status {res.returncode}: {' '.join(cmd[-3:])}")
 
 
+def instantiation_units(objdir: str) -> list[str]:
+    """Write one source per (launcher, input type, shape) into objdir; returns their paths."""
+    units = []
+    for ty in INPUT_TYPES:
+        for header, fn, shapes, sig in (
+                ("launch_seq.h", "launch_seq", SEQ_SHAPES, "ss::ScanParams, SeqMode, void*, size_t, hipStream_t"),
+                ("launch_bwd.h", "launch_bwd", BWD_SHAPES, "ss::BwdParams, bool, bool, hipStream_t, int*")):
+            for sc, nsw in shapes:
+                path = os.path.join(objdir, f"{fn}_{ty}_{sc}x{nsw}.hip")
+                with open(path, "w") as f:
+                    f.write(f'#include "{header}"\nnamespace ss_host {{\n'
+                            f"template int {fn}<{ty}, {sc}, {nsw}>({sig});\n}}\n")
+                units.append(path)
+    return units
+
+
 def build(output: str = LIBRARY, verbose: bool = False) -> str:
     objdir = tempfile.mkdtemp(prefix="ss_build_")
     try:
-        objects = [os.path.join(objdir, os.path.basename(src) + ".o") for src in SOURCES]
-        workers = max(1, min(len(SOURCES), os.cpu_count() or 1))
+        sources = SOURCES + instantiation_units(objdir)
+        objects = [os.path.join(objdir, os.path.basename(src) + ".o") for src in sources]
+        workers = max(1, min(len(sources), os.cpu_count() or 1))
         with concurrent.futures.ThreadPoolExecutor(workers) as pool:
-            for f in [pool.submit(_run, compile_command(src, obj), verbose) for src, obj in zip(SOURCES, objects)]:
+            # The largest units first, so the pool does not end on one of them.
+            order = sorted(range(len(sources)), key=lambda i: "_8x" not in sources[i] and "ss_scan" not in sources[i])
+            futures = [pool.submit(_run, compile_command(sources[i], objects[i]), verbose) for i in order]
+            for f in futures:
                 f.result()
         tmp = output + ".tmp"
         _run(link_command(objects, tmp), verbose)

@@ -31,11 +31,14 @@ int launch_bwd(ss::BwdParams p, bool gate, bool zoh, hipStream_t st, int* segmen
     K = int((p.L + Lseg - 1) / Lseg);
     p.K = K;
     p.Lseg = Lseg;
+    p.spin_limit = spin_limit();
+    p.wait_never = test_plan().wait_never.load(std::memory_order_relaxed);
     *segments = K;
     if (K > 1) {
+        // The status words were cleared by the forward pass of this call.
         const size_t words = size_t(ss::kFlagOffset) + size_t(G) * K;
         const int rb = int(std::min<size_t>(1024, (words + 255) / 256));
-        hipLaunchKernelGGL(ss::scan_ctl_reset, dim3(rb), dim3(256), 0, st, p.ctl, int64_t(words));
+        hipLaunchKernelGGL(ss::scan_ctl_reset, dim3(rb), dim3(256), 0, st, p.ctl, int64_t(words), nullptr);
         if (hipGetLastError() != hipSuccess) return SS_ERR_HIP;
     }
     hipLaunchKernelGGL(kern, dim3(unsigned(G * K)), dim3(threads), lds, st, p);

@@ -22,8 +22,7 @@ int launch_seq(ss::ScanParams p, SeqMode mode, void* ws, size_t ws_bytes, hipStr
     constexpr int TW = ss::seq_chunk<TIn, SC, NSW, true>(), TN = ss::seq_chunk<TIn, SC, NSW, false>();
     constexpr int threads = (SC + ss::kSeqElemWaves + 1) * 64;
     const int64_t G = p.b * p.nblk_d;
-    const SeqWorkspace w = seq_workspace(p.b, p.L, p.d_in, p.n);
-    if (!ws || ws_bytes < w.total) return SS_ERR_WORKSPACE;
+    if (!ws || ws_bytes < seq_workspace(p.b, p.d_in, p.n, 1).total) return SS_ERR_WORKSPACE;
 
     // Wide path: whole 16-byte pieces per row and 16-byte aligned u, delta, z
     // (and dy); y (dz) aligned for V-element stores (the cross scan adds to y
@@ -78,18 +77,25 @@ int launch_seq(ss::ScanParams p, SeqMode mode, void* ws, size_t ws_bytes, hipStr
     const int per_cu = resident_per_cu(reinterpret_cast<const void*>(kern), threads, lds);
     int K = choose_segments(G, p.L, T, int64_t(std::max(cus, 0)) * per_cu);
     while (K > 1 && G * K > kMaxWorkgroups) K--;   // a launch holds fewer than 2^32 work-items
+    // Fewer segments where the workspace is smaller than the query asks:
+    // results are the same, since every segment starts from the exact state
+    // its predecessor ended with.
+    while (K > 1 && seq_workspace(p.b, p.d_in, p.n, K).total > ws_bytes) K--;
     int64_t Lseg = (p.L + K - 1) / K;
     Lseg = (Lseg + T - 1) / T * T;
     K = int((p.L + Lseg - 1) / Lseg);
     p.K = K;
     p.Lseg = Lseg;
+    const SeqWorkspace w = seq_workspace(p.b, p.d_in, p.n, K);
     char* base = static_cast<char*>(ws);
     p.ctl = reinterpret_cast<uint32_t*>(base);
     p.handoff = reinterpret_cast<float*>(base + w.ctl);
+    p.spin_limit = spin_limit();
+    p.wait_never = test_plan().wait_never.load(std::memory_order_relaxed);
     if (K > 1) {
         const size_t words = size_t(ss::kFlagOffset) + size_t(G) * K;
         const int rb = int(std::min<size_t>(1024, (words + 255) / 256));
-        hipLaunchKernelGGL(ss::scan_ctl_reset, dim3(rb), dim3(256), 0, st, p.ctl, int64_t(words));
+        hipLaunchKernelGGL(ss::scan_ctl_reset, dim3(rb), dim3(256), 0, st, p.ctl, int64_t(words), p.err);
         if (hipGetLastError() != hipSuccess) return SS_ERR_HIP;
     }
     hipLaunchKernelGGL(kern, dim3(unsigned(G * K)), dim3(threads), lds, st, p);

@@ -74,8 +74,11 @@ struct BwdParams {
     // starts from the adjoint its successor segment handed on.
     int K;
     int64_t Lseg;             // steps per segment, a multiple of kCkptSteps
-    uint32_t* ctl;            // [0] ticket counter, [1] error word, [kFlagOffset + s G + g] flags
+    uint32_t* ctl;            // [0] ticket counter, [kFlagOffset + s G + g] flags
     float* handoff;           // (K - 1, G, n, 64) adjoints handed between segments
+    uint32_t* err;            // status words of the call (as ScanParams::err; cleared by the forward pass)
+    int spin_limit;           // polls before a segment wait gives up
+    int wait_never;           // nonzero: waits poll err[1] (never set) and give up after spin_limit polls
 };
 
 // v moved from another lane of the same row by a DPP control (row_shr);
@@ -215,21 +218,12 @@ __global__ __launch_bounds__((SC + 4) * 64) void scan_bwd(const BwdParams p) {
     }
     if (seg < p.K - 1) {
         // Wait for the adjoint of the later segment of these channels (it holds
-        // an earlier ticket, so the wait cannot deadlock; on a timeout the error
+        // an earlier ticket, so the wait cannot deadlock; on a timeout the status
         // word is set and this piece goes on from NaN, so its outputs show it).
         int& s_timeout = *(reinterpret_cast<int*>(lds + Lds::off_ticket) + 1);
         if (tid == 0) {
-            uint32_t* flag = p.ctl + kFlagOffset + seg * G + gi;
-            int spins = 0, timed_out = 0;
-            while (__hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0u) {
-                __builtin_amdgcn_s_sleep(2);
-                if (++spins > kSpinLimit) {
-                    atomicOr(p.ctl + 1, 1u);
-                    timed_out = 1;
-                    break;
-                }
-            }
-            s_timeout = timed_out;
+            const uint32_t* flag = p.wait_never ? p.err + 1 : p.ctl + kFlagOffset + seg * G + gi;
+            s_timeout = wait_segment_flag(flag, p.err, p.spin_limit) ? 1 : 0;
         }
         __syncthreads();
         const bool timed_out = __builtin_amdgcn_readfirstlane(s_timeout) != 0;

@@ -66,8 +66,11 @@ struct ScanParams {
     int nblk_d;          // ceil(d_in / 64)
     int K;               // segments along L (scan_seq)
     int64_t Lseg;        // steps per segment (a multiple of the chunk length)
-    uint32_t* ctl;       // [0] ticket counter, [1] error word, [kFlagOffset + i] segment-done flags
+    uint32_t* ctl;       // [0] ticket counter, [kFlagOffset + i] segment-done flags
     float* handoff;      // (K - 1) * G * n * 64 states published between segments
+    uint32_t* err;       // status words of the call: [0] nonzero once a segment wait gave up, [1] never set
+    int spin_limit;      // polls before a segment wait gives up
+    int wait_never;      // nonzero: segment waits poll err[1] (never set), so each gives up after spin_limit polls
 };
 
 constexpr int kFlagOffset = 64;
@@ -76,6 +79,21 @@ constexpr int kFlagOffset = 64;
 // the chunk length of the backward pass.
 constexpr int kCkptSteps = 8;
 constexpr int kSpinLimit = 1 << 25;   // ~2 s of s_sleep before a wait gives up and flags an error
+
+// One thread waits until the segment flag `flag` is set, or gives up after
+// `limit` polls: then it sets err[0] and returns true.  The flag and the
+// state it guards are device-coherent atomics (see the end of scan_seq).
+__device__ __forceinline__ bool wait_segment_flag(const uint32_t* flag, uint32_t* err, int limit) {
+    int spins = 0;
+    while (__hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0u) {
+        __builtin_amdgcn_s_sleep(2);
+        if (++spins > limit) {
+            atomicOr(err, 1u);
+            return true;
+        }
+    }
+    return false;
+}
 
 // Steps of (delta', delta' u) a recurrence wave reads from LDS ahead of the
 // step it computes.
@@ -302,6 +320,9 @@ __global__ __launch_bounds__((SC + kSeqElemWaves + 1) * 64) void scan_seq(const 
     int ticket;
     if (p.K == 1) {
         ticket = blockIdx.x;
+        // Without segments nothing waits, so nothing can set the status word
+        // while it is cleared here (with segments scan_ctl_reset clears it).
+        if (blockIdx.x == 0 && tid < 2 && p.err) p.err[tid] = 0u;
     } else {
         if (tid == 0) s_ticket = int(atomicAdd(p.ctl, 1u));
         __syncthreads();
@@ -364,21 +385,12 @@ __global__ __launch_bounds__((SC + kSeqElemWaves + 1) * 64) void scan_seq(const 
     if (seg > 0) {
         // Wait for the previous segment of this channel group, then take its
         // state.  The wait cannot deadlock (the predecessor holds an earlier
-        // ticket); should it still time out, the error word is set and this
+        // ticket); should it still time out, the status word is set and this
         // piece continues from a NaN state, so its outputs show it.
         int& s_timeout = *(reinterpret_cast<int*>(lds + Lds::off_ticket) + 1);
         if (tid == 0) {
-            uint32_t* flag = p.ctl + kFlagOffset + (seg - 1) * G + g;
-            int spins = 0, timed_out = 0;
-            while (__hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0u) {
-                __builtin_amdgcn_s_sleep(2);
-                if (++spins > kSpinLimit) {
-                    atomicOr(p.ctl + 1, 1u);
-                    timed_out = 1;
-                    break;
-                }
-            }
-            s_timeout = timed_out;
+            const uint32_t* flag = p.wait_never ? p.err + 1 : p.ctl + kFlagOffset + (seg - 1) * G + g;
+            s_timeout = wait_segment_flag(flag, p.err, p.spin_limit) ? 1 : 0;
         }
         __syncthreads();
         const bool timed_out = __builtin_amdgcn_readfirstlane(s_timeout) != 0;
@@ -778,10 +790,18 @@ __global__ __launch_bounds__(256) void cross_merge(const float* __restrict__ ys,
     }
 }
 
-// Clears the ticket counter, the error word and the segment flags.
-static __global__ void scan_ctl_reset(uint32_t* ctl, int64_t words) {
+// Clears the ticket counter and the segment flags (ctl[0 .. words)) and, when
+// err is given, the call's two status words.
+static __global__ void scan_ctl_reset(uint32_t* ctl, int64_t words, uint32_t* err) {
     for (int64_t i = blockIdx.x * int64_t(blockDim.x) + threadIdx.x; i < words; i += int64_t(gridDim.x) * blockDim.x)
         ctl[i] = 0u;
+    if (err && blockIdx.x == 0 && threadIdx.x < 2) err[threadIdx.x] = 0u;
+}
+
+// The status code a call left in its status word: SS_OK (0), or
+// SS_ERR_TIMEOUT (-10) once a segment wait gave up.
+static __global__ void scan_status_copy(const uint32_t* err, int32_t* status) {
+    if (threadIdx.x == 0) *status = __hip_atomic_load(err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ? -10 : 0;
 }
 
 constexpr int kTparSteps = 16;   // TS: steps per wave per chunk

@@ -9,7 +9,6 @@
 
 #include <algorithm>
 #include <atomic>
-#include <cstdlib>
 #include <cstring>
 #include <map>
 #include <mutex>
@@ -40,16 +39,36 @@ inline dim3 grid_1d(int64_t items) {
     return dim3(unsigned(std::max<int64_t>(1, std::min<int64_t>((items + 255) / 256, int64_t(1) << 20))));
 }
 
+// Overrides of the launch plan set by ss_set_test_plan (tests and tuning
+// only; every field 0 = the library's own choice).  Each changes how the work
+// is split, never what is computed.
+struct TestPlan {
+    std::atomic<int> segments{0};    // segments along L, 1..kMaxSegments
+    std::atomic<int> waves{0};       // 4: 4 recurrence waves of 4 states at 9 <= n <= 16
+    std::atomic<int> tpar{0};        // 1: scan_tpar for n <= 2 (zero initial state, Euler)
+    std::atomic<int> spin_limit{0};  // polls before a segment wait gives up
+    std::atomic<int> wait_never{0};  // 1: segment waits poll a word nothing sets (they all give up)
+};
+
+inline TestPlan& test_plan() {
+    static TestPlan plan;
+    return plan;
+}
+
+inline int spin_limit() {
+    const int v = test_plan().spin_limit.load(std::memory_order_relaxed);
+    return v > 0 ? v : ss::kSpinLimit;
+}
+
 struct SeqShape {
     int SC;    // recurrence waves per workgroup
     int NSW;   // states per recurrence wave
 };
 
-// Recurrence waves and states per wave.  SS_SCAN_WAVES=4 selects 4 waves of
-// 4 states at 9 <= n <= 16 (tests, tuning).
+// Recurrence waves and states per wave (the test plan may take 4 waves of 4
+// states at 9 <= n <= 16).
 inline SeqShape seq_shape(int64_t n) {
-    const char* w = std::getenv("SS_SCAN_WAVES");
-    const int want = w ? int(std::strtol(w, nullptr, 10)) : 0;
+    const int want = test_plan().waves.load(std::memory_order_relaxed);
     if (n <= 2) return {1, 2};
     if (n <= 8) return {4, 2};
     if (n <= 16) return want == 4 ? SeqShape{4, 4} : SeqShape{8, 2};
@@ -66,19 +85,18 @@ inline SeqShape bwd_shape(int64_t n) {
     return {8, 8};
 }
 
-// Workspace of scan_seq, in order: control words (ticket, error, one flag per
-// (segment, group)) and the states published between segments, sized for up
-// to kMaxSegments segments.
+// Workspace of scan_seq cut into K segments, in order: control words (ticket
+// counter, one flag per (segment, group)) and the states published between
+// segments.  The size asked of callers is that for kMaxSegments.
 struct SeqWorkspace {
     size_t ctl, handoff, total;
 };
 
-inline SeqWorkspace seq_workspace(int64_t b, int64_t L, int64_t d_in, int64_t n) {
-    (void)L;
+inline SeqWorkspace seq_workspace(int64_t b, int64_t d_in, int64_t n, int K = kMaxSegments) {
     const int64_t G = b * ((d_in + 63) / 64);
     SeqWorkspace w;
-    w.ctl = ((size_t(ss::kFlagOffset) + size_t(G) * kMaxSegments) * sizeof(uint32_t) + 255) / 256 * 256;
-    w.handoff = (size_t(kMaxSegments - 1) * size_t(G) * size_t(n) * 64 * sizeof(float) + 255) / 256 * 256;
+    w.ctl = ((size_t(ss::kFlagOffset) + (K > 1 ? size_t(G) * size_t(K) : 0)) * sizeof(uint32_t) + 255) / 256 * 256;
+    w.handoff = (size_t(K - 1) * size_t(G) * size_t(n) * 64 * sizeof(float) + 255) / 256 * 256;
     w.total = w.ctl + w.handoff;
     return w;
 }
@@ -122,13 +140,11 @@ inline int resident_per_cu(const void* fn, int threads, size_t lds) {
 // (pipeline fill and drain, state handoff) taken as 2% of a whole-length
 // piece.  K minimises that.  With fewer groups than slots the segments of a
 // group would only run one after another, so K = 1.  Every segment keeps at
-// least 4 chunks.  SS_SCAN_SEGMENTS overrides (tests, tuning).
+// least 4 chunks.  The test plan may fix K.
 inline int choose_segments(int64_t G, int64_t L, int T, int64_t slots) {
     const int64_t max_k = std::max<int64_t>(1, std::min<int64_t>(kMaxSegments, L / (4 * int64_t(T))));
-    if (const char* e = std::getenv("SS_SCAN_SEGMENTS")) {
-        const long v = std::strtol(e, nullptr, 10);
-        if (v >= 1) return int(std::min<int64_t>(std::min<int64_t>(v, kMaxSegments), std::max<int64_t>(1, (L + T - 1) / T)));
-    }
+    if (const int v = test_plan().segments.load(std::memory_order_relaxed); v >= 1)
+        return int(std::min<int64_t>(std::min<int64_t>(v, kMaxSegments), std::max<int64_t>(1, (L + T - 1) / T)));
     if (slots <= 0 || G < slots) return 1;
     int best = 1;
     double best_t = 0.0;

@@ -7,7 +7,6 @@
 
 #include <algorithm>
 #include <atomic>
-#include <cstdlib>
 #include <cstring>
 #include <map>
 #include <mutex>
@@ -45,6 +44,11 @@ bool overlaps(Range a, Range b) { return a.lo < b.hi && b.lo < a.hi; }
 
 size_t elem_size(int dtype) { return dtype == SS_BF16 ? 2 : 4; }
 
+// Every scan workspace (ss_scan_fwd, ss_cross_scan_fwd, ss_scan_bwd) starts
+// with the forward scan's control words; the call's status words are words
+// kStatusWord and kStatusWord + 1 of it (ss_scan_status reads the first).
+constexpr int kStatusWord = 1;
+
 // a, b, c >= 1 and a * b * c <= 2^46 (checked without forming an overflowing product).
 bool sizes_ok(int64_t a, int64_t b, int64_t c) {
     if (a <= 0 || b <= 0 || c <= 0) return false;
@@ -56,11 +60,10 @@ bool sizes_ok(int64_t a, int64_t b, int64_t c) {
 
 enum class ScanKernel { Tpar, Seq };
 
-// scan_seq for every n; SS_SCAN_VARIANT=tpar selects scan_tpar for n <= 2
-// (tests), which starts from a zero state with the delta' input weight only.
+// scan_seq for every n; the test plan may select scan_tpar for n <= 2, which
+// starts from a zero state with the delta' input weight only.
 ScanKernel choose_kernel(const ScanParams& p, bool zoh) {
-    const char* v = std::getenv("SS_SCAN_VARIANT");
-    if (v && std::strcmp(v, "tpar") == 0 && p.n <= 2 && !p.h0 && !zoh) return ScanKernel::Tpar;
+    if (test_plan().tpar.load(std::memory_order_relaxed) && p.n <= 2 && !p.h0 && !zoh) return ScanKernel::Tpar;
     return ScanKernel::Seq;
 }
 
@@ -130,6 +133,7 @@ SS_EXPORT const char* ss_status_string(int status) {
         case SS_ERR_ALIAS: return "an output overlaps an input";
         case SS_ERR_ALIGN: return "a pointer is not aligned to its element size";
         case SS_ERR_MODE: return "discretization is not SS_DISC_EULER or SS_DISC_ZOH";
+        case SS_ERR_TIMEOUT: return "a wait between sequence segments gave up; the outputs hold NaN";
         default: return "unknown status";
     }
 }
@@ -140,14 +144,18 @@ SS_EXPORT size_t ss_scan_fwd_workspace_bytes(int64_t b, int64_t L, int64_t d_in,
     if (b * ((d_in + 63) / 64) > kMaxWorkgroups || L > kMaxLength) return 0;
     // Sized for scan_seq with the most segments; scan_tpar (n <= 2) needs none
     // but the same size is asked for so that either kernel can be chosen.
-    return seq_workspace(b, L, d_in, n).total;
+    return seq_workspace(b, d_in, n).total;
 }
 
-SS_EXPORT int ss_scan_fwd_ex(const void* u, const void* delta, const float* A_log, const void* B, const void* C,
-                             const float* D, const void* z, const float* delta_bias, int delta_softplus,
-                             const float* initial_state, int discretization, void* y, float* last_state, int64_t b,
-                             int64_t L, int64_t d_in, int64_t n, int dtype, void* workspace, size_t workspace_bytes,
-                             void* stream) {
+namespace {
+
+// The scan forward behind ss_scan_fwd_ex: the caller's workspace must be as
+// large as the query says.
+int scan_fwd_impl(const void* u, const void* delta, const float* A_log, const void* B, const void* C,
+                  const float* D, const void* z, const float* delta_bias, int delta_softplus,
+                  const float* initial_state, int discretization, void* y, float* last_state, int64_t b, int64_t L,
+                  int64_t d_in, int64_t n, int dtype, void* workspace, size_t workspace_bytes,
+                  void* stream) {
     if (!u || !delta || !A_log || !B || !C || !D || !y) return SS_ERR_NULL;
     if (!sizes_ok(b, L, d_in) || n <= 0 || d_in > SS_MAX_CHANNELS) return SS_ERR_SHAPE;
     if (dtype != SS_F32 && dtype != SS_BF16) return SS_ERR_DTYPE;
@@ -176,13 +184,13 @@ SS_EXPORT int ss_scan_fwd_ex(const void* u, const void* delta, const float* A_lo
         if (overlaps(r, ry) || overlaps(r, rs)) return SS_ERR_ALIAS;
     if (overlaps(ry, rs) || overlaps(rh, ry) || (!in_place && overlaps(rh, rs))) return SS_ERR_ALIAS;
     const size_t need = ss_scan_fwd_workspace_bytes(b, L, d_in, n, dtype);
-    if (need > 0 && (!workspace || workspace_bytes < need)) return SS_ERR_WORKSPACE;
-    if (need > 0) {
-        const Range rw = range_of(workspace, int64_t(workspace_bytes), 1);
-        for (const Range& r : ins)
-            if (overlaps(r, rw)) return SS_ERR_ALIAS;
-        if (overlaps(ry, rw) || overlaps(rs, rw) || overlaps(rh, rw)) return SS_ERR_ALIAS;
-    }
+    if (!workspace || workspace_bytes < need) return SS_ERR_WORKSPACE;
+    // The workspace starts with 32-bit words updated by device atomics.
+    if (!aligned(workspace, 256)) return SS_ERR_ALIGN;
+    const Range rw = range_of(workspace, int64_t(workspace_bytes), 1);
+    for (const Range& r : ins)
+        if (overlaps(r, rw)) return SS_ERR_ALIAS;
+    if (overlaps(ry, rw) || overlaps(rs, rw) || overlaps(rh, rw)) return SS_ERR_ALIAS;
 
     ScanParams p{};
     p.u = u;
@@ -204,14 +212,52 @@ SS_EXPORT int ss_scan_fwd_ex(const void* u, const void* delta, const float* A_lo
     p.nblk_d = int((d_in + 63) / 64);
     p.K = 1;
     p.Lseg = L;
+    p.err = static_cast<uint32_t*>(workspace) + kStatusWord;
     hipStream_t st = static_cast<hipStream_t>(stream);
 
     const bool zoh = discretization == SS_DISC_ZOH;
-    if (choose_kernel(p, zoh) == ScanKernel::Tpar)
+    if (choose_kernel(p, zoh) == ScanKernel::Tpar) {
+        // No segment waits: only the status words need clearing.
+        hipLaunchKernelGGL(ss::scan_ctl_reset, dim3(1), dim3(64), 0, st, p.err, int64_t(0), p.err);
+        if (hipGetLastError() != hipSuccess) return SS_ERR_HIP;
         return dtype == SS_BF16 ? dispatch_tpar<uint16_t>(p, st) : dispatch_tpar<float>(p, st);
+    }
     const SeqMode mode = zoh ? SeqMode::Zoh : SeqMode::Euler;
     return dtype == SS_BF16 ? dispatch_seq<uint16_t>(p, mode, workspace, workspace_bytes, st)
                             : dispatch_seq<float>(p, mode, workspace, workspace_bytes, st);
+}
+
+}  // namespace
+
+SS_EXPORT int ss_scan_fwd_ex(const void* u, const void* delta, const float* A_log, const void* B, const void* C,
+                             const float* D, const void* z, const float* delta_bias, int delta_softplus,
+                             const float* initial_state, int discretization, void* y, float* last_state, int64_t b,
+                             int64_t L, int64_t d_in, int64_t n, int dtype, void* workspace, size_t workspace_bytes,
+                             void* stream) {
+    return scan_fwd_impl(u, delta, A_log, B, C, D, z, delta_bias, delta_softplus, initial_state, discretization, y,
+                         last_state, b, L, d_in, n, dtype, workspace, workspace_bytes, stream);
+}
+
+SS_EXPORT int ss_scan_status(const void* workspace, size_t workspace_bytes, int32_t* status, void* stream) {
+    if (!workspace || !status) return SS_ERR_NULL;
+    if (workspace_bytes < 256) return SS_ERR_WORKSPACE;
+    if (!aligned(workspace, 256) || !aligned(status, 4)) return SS_ERR_ALIGN;
+    hipLaunchKernelGGL(ss::scan_status_copy, dim3(1), dim3(64), 0, static_cast<hipStream_t>(stream),
+                       static_cast<const uint32_t*>(workspace) + kStatusWord, status);
+    return hipGetLastError() == hipSuccess ? SS_OK : SS_ERR_HIP;
+}
+
+SS_EXPORT int ss_set_test_plan(int segments, int waves, int time_parallel, int spin_limit, int wait_never) {
+    if (segments < 0 || segments > kMaxSegments || (waves != 0 && waves != 4) || spin_limit < 0 ||
+        (time_parallel != 0 && time_parallel != 1) || (wait_never != 0 && wait_never != 1))
+        return SS_ERR_SHAPE;
+    TestPlan& t = test_plan();
+    t.segments.store(segments);
+    t.waves.store(waves);
+    t.tpar.store(time_parallel);
+    t.spin_limit.store(spin_limit);
+    t.wait_never.store(wait_never);
+    return SS_OK;
 }
 
 SS_EXPORT int ss_scan_fwd(const void* u, const void* delta, const float* A_log, const void* B, const void* C,
@@ -361,7 +407,7 @@ SS_EXPORT size_t ss_cross_scan_fwd_workspace_bytes(int64_t maps, int64_t H, int6
                                                    int dtype) {
     if (dtype != SS_F32 && dtype != SS_BF16) return 0;
     if (!cross_sizes_ok(maps, H, W, d_in, n) || n > SS_MAX_STATE) return 0;
-    return cross_ys_bytes(maps, H * W, d_in) + ss_scan_fwd_workspace_bytes(4 * maps, H * W, d_in, n, dtype);
+    return ss_scan_fwd_workspace_bytes(4 * maps, H * W, d_in, n, dtype) + cross_ys_bytes(maps, H * W, d_in);
 }
 
 SS_EXPORT int ss_cross_scan_fwd(const void* x, const void* delta, const float* A_log, const void* B, const void* C,
@@ -396,8 +442,10 @@ SS_EXPORT int ss_cross_scan_fwd(const void* x, const void* delta, const float* A
         if (overlaps(r, rw)) return SS_ERR_ALIAS;
     if (overlaps(ry, rw) || overlaps(rs, rw)) return SS_ERR_ALIAS;
 
-    const size_t ys_bytes = cross_ys_bytes(maps, L, d_in);
-    float* ys = static_cast<float*>(workspace);
+    // The scan's own workspace first (so the status words lead the workspace),
+    // then the four directions' outputs.
+    const size_t scan_ws_bytes = ss_scan_fwd_workspace_bytes(b, L, d_in, n, dtype);
+    float* ys = reinterpret_cast<float*>(static_cast<char*>(workspace) + scan_ws_bytes);
     ScanParams p{};
     p.u = x;
     p.delta = delta;
@@ -419,11 +467,10 @@ SS_EXPORT int ss_cross_scan_fwd(const void* x, const void* delta, const float* A
     p.nblk_d = int((d_in + 63) / 64);
     p.K = 1;
     p.Lseg = L;
+    p.err = static_cast<uint32_t*>(workspace) + kStatusWord;
     hipStream_t st = static_cast<hipStream_t>(stream);
-    void* scan_ws = static_cast<char*>(workspace) + ys_bytes;
-    const int rc = dtype == SS_BF16
-                       ? dispatch_seq<uint16_t>(p, SeqMode::Cross, scan_ws, workspace_bytes - ys_bytes, st)
-                       : dispatch_seq<float>(p, SeqMode::Cross, scan_ws, workspace_bytes - ys_bytes, st);
+    const int rc = dtype == SS_BF16 ? dispatch_seq<uint16_t>(p, SeqMode::Cross, workspace, scan_ws_bytes, st)
+                                    : dispatch_seq<float>(p, SeqMode::Cross, workspace, scan_ws_bytes, st);
     if (rc != SS_OK) return rc;
     // CrossMerge: the four directions' outputs added back at their positions.
     const bool vec = d_in % 4 == 0 && aligned(y, 16);
@@ -443,12 +490,13 @@ namespace {
 using namespace ss_host;
 using ss::BwdParams;
 
-// Workspace of ss_scan_bwd, in order: the forward's checkpoints, the dB and dC
-// partials per channel group, the dA_log, dD and dbias partials per segment
-// and batch row, the control words and adjoints of the backward's segments,
-// then the forward scan's own workspace.
+// Workspace of ss_scan_bwd, in order: the forward scan's own workspace (whose
+// control words lead with the call's status words), the forward's
+// checkpoints, the dB and dC partials per channel group, the dA_log, dD and
+// dbias partials per segment and batch row, then the control words and
+// adjoints of the backward's segments.
 struct BwdWorkspace {
-    size_t ckpt, part_B, part_C, part_A, part_D, part_bias, ctl, handoff, fwd, total;
+    size_t fwd, ckpt, part_B, part_C, part_A, part_D, part_bias, ctl, handoff, total;
 };
 
 size_t round256(size_t x) { return (x + 255) / 256 * 256; }
@@ -464,8 +512,8 @@ BwdWorkspace bwd_workspace(int64_t b, int64_t L, int64_t d_in, int64_t n) {
     const int64_t G = b * nblk;
     w.ctl = round256((size_t(ss::kFlagOffset) + size_t(G) * kMaxSegments) * sizeof(uint32_t));
     w.handoff = round256(size_t(kMaxSegments - 1) * size_t(G) * size_t(n) * 64 * sizeof(float));
-    w.fwd = seq_workspace(b, L, d_in, n).total;
-    w.total = w.ckpt + w.part_B + w.part_C + w.part_A + w.part_D + w.part_bias + w.ctl + w.handoff + w.fwd;
+    w.fwd = seq_workspace(b, d_in, n).total;
+    w.total = w.fwd + w.ckpt + w.part_B + w.part_C + w.part_A + w.part_D + w.part_bias + w.ctl + w.handoff;
     return w;
 }
 
@@ -546,17 +594,18 @@ SS_EXPORT int ss_scan_bwd_ex(const void* u, const void* delta, const float* A_lo
         if (overlaps(r, rw)) return SS_ERR_ALIAS;
 
     const BwdWorkspace w = bwd_workspace(b, L, d_in, n);
-    char* base = static_cast<char*>(workspace);
-    float* ckpt = reinterpret_cast<float*>(base);
-    float* part_B = reinterpret_cast<float*>(base + w.ckpt);
-    float* part_C = reinterpret_cast<float*>(base + w.ckpt + w.part_B);
-    float* part_A = reinterpret_cast<float*>(base + w.ckpt + w.part_B + w.part_C);
-    float* part_D = reinterpret_cast<float*>(base + w.ckpt + w.part_B + w.part_C + w.part_A);
-    float* part_bias = reinterpret_cast<float*>(base + w.ckpt + w.part_B + w.part_C + w.part_A + w.part_D);
-    uint32_t* bctl = reinterpret_cast<uint32_t*>(base + w.ckpt + w.part_B + w.part_C + w.part_A + w.part_D +
-                                                 w.part_bias);
-    float* handoff = reinterpret_cast<float*>(reinterpret_cast<char*>(bctl) + w.ctl);
-    void* fwd_ws = base + w.total - w.fwd;
+    char* const base = static_cast<char*>(workspace);
+    void* fwd_ws = base;
+    char* at = base + w.fwd;
+    float* ckpt = reinterpret_cast<float*>(at);
+    float* part_B = reinterpret_cast<float*>(at += w.ckpt);
+    float* part_C = reinterpret_cast<float*>(at += w.part_B);
+    float* part_A = reinterpret_cast<float*>(at += w.part_C);
+    float* part_D = reinterpret_cast<float*>(at += w.part_A);
+    float* part_bias = reinterpret_cast<float*>(at += w.part_D);
+    uint32_t* bctl = reinterpret_cast<uint32_t*>(at += w.part_bias);
+    float* handoff = reinterpret_cast<float*>(at += w.ctl);
+    uint32_t* err = static_cast<uint32_t*>(workspace) + kStatusWord;
     hipStream_t st = static_cast<hipStream_t>(stream);
     const int nblk = int((d_in + 63) / 64);
 
@@ -587,6 +636,7 @@ SS_EXPORT int ss_scan_bwd_ex(const void* u, const void* delta, const float* A_lo
     f.nblk_d = nblk;
     f.K = 1;
     f.Lseg = L;
+    f.err = err;
     const SeqMode fm = zoh ? (z ? SeqMode::ZohDz : SeqMode::Zoh) : (z ? SeqMode::Dz : SeqMode::Euler);
     int rc = dtype == SS_BF16 ? dispatch_seq<uint16_t>(f, fm, fwd_ws, w.fwd, st)
                               : dispatch_seq<float>(f, fm, fwd_ws, w.fwd, st);
@@ -623,6 +673,7 @@ SS_EXPORT int ss_scan_bwd_ex(const void* u, const void* delta, const float* A_lo
     p.softplus = f.softplus;
     p.ctl = bctl;
     p.handoff = handoff;
+    p.err = err;
     int K = 1;
     rc = dtype == SS_BF16 ? dispatch_bwd<uint16_t>(p, z != nullptr, zoh, st, &K)
                           : dispatch_bwd<float>(p, z != nullptr, zoh, st, &K);

@@ -11,7 +11,7 @@ import pytest
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "ss_scan.h")
 
-OK, NULL, SHAPE, DTYPE, UNSUP, WS, HIP, ALIAS, ALIGN, MODE = 0, -1, -2, -3, -4, -5, -6, -7, -8, -9
+OK, NULL, SHAPE, DTYPE, UNSUP, WS, HIP, ALIAS, ALIGN, MODE, TIMEOUT = 0, -1, -2, -3, -4, -5, -6, -7, -8, -9, -10
 
 
 @pytest.fixture(scope="module")
@@ -30,9 +30,9 @@ def declared_functions():
 def test_header_declares_the_entry_points():
     assert declared_functions() == sorted(["ss_conv_update", "ss_cross_scan_fwd", "ss_cross_scan_fwd_workspace_bytes",
                                            "ss_scan_bwd", "ss_scan_bwd_ex", "ss_scan_bwd_workspace_bytes", "ss_scan_fwd",
-                                           "ss_scan_fwd_ex",
-                                           "ss_scan_fwd_workspace_bytes", "ss_state_update", "ss_state_update_ex",
-                                           "ss_status_string"])
+                                           "ss_scan_fwd_ex", "ss_scan_status",
+                                           "ss_scan_fwd_workspace_bytes", "ss_set_test_plan", "ss_state_update",
+                                           "ss_state_update_ex", "ss_status_string"])
 
 
 def test_library_exports_every_declared_symbol(ss):
@@ -43,7 +43,7 @@ def test_library_exports_every_declared_symbol(ss):
 
 
 def test_status_strings(ss):
-    for code in (OK, NULL, SHAPE, DTYPE, UNSUP, WS, HIP, ALIAS, ALIGN, MODE):
+    for code in (OK, NULL, SHAPE, DTYPE, UNSUP, WS, HIP, ALIAS, ALIGN, MODE, TIMEOUT):
         s = ss.status_string(code)
         assert s and s != "unknown status"
     assert ss.status_string(12345) == "unknown status"
@@ -53,7 +53,8 @@ def test_status_codes_match_header(ss):
     text = open(HEADER).read()
     for name, code in (("SS_OK", OK), ("SS_ERR_NULL", NULL), ("SS_ERR_SHAPE", SHAPE), ("SS_ERR_DTYPE", DTYPE),
                        ("SS_ERR_UNSUPPORTED", UNSUP), ("SS_ERR_WORKSPACE", WS), ("SS_ERR_HIP", HIP),
-                       ("SS_ERR_ALIAS", ALIAS), ("SS_ERR_ALIGN", ALIGN), ("SS_ERR_MODE", MODE)):
+                       ("SS_ERR_ALIAS", ALIAS), ("SS_ERR_ALIGN", ALIGN), ("SS_ERR_MODE", MODE),
+                       ("SS_ERR_TIMEOUT", TIMEOUT)):
         assert re.search(rf"\b{name}\s*=\s*{code}\b", text), name
         assert ss.STATUS[code] == name
     for name, code in (("SS_DISC_EULER", ss.SS_DISC_EULER), ("SS_DISC_ZOH", ss.SS_DISC_ZOH)):
@@ -105,9 +106,31 @@ def call_scan(ss, a):
     (dict(last=addr(10) + 1), ALIGN),
     (dict(y=addr(1) + 64), ALIAS), (dict(last=addr(4)), ALIAS), (dict(y=addr(10)), ALIAS),
     (dict(ws=addr(9)), ALIAS), (dict(ws=addr(1)), ALIAS), (dict(last=addr(8) + 4), ALIAS),
+    (dict(ws=addr(11) + 4), ALIGN), (dict(ws=addr(11) + 128), ALIGN),
 ])
 def test_scan_rejects(ss, over, code):
     assert call_scan(ss, scan_args(**over)) == code
+
+
+def test_scan_status_rejects(ss):
+    out = ctypes.c_void_p(addr(20))
+    assert ss.lib.ss_scan_status(addr(11), 1 << 20, None, None) == NULL
+    assert ss.lib.ss_scan_status(addr(11), 100, out, None) == WS
+    assert ss.lib.ss_scan_status(addr(11) + 4, 1 << 20, out, None) == ALIGN
+    assert ss.lib.ss_scan_status(addr(11), 1 << 20, ctypes.c_void_p(addr(20) + 2), None) == ALIGN
+
+
+def test_test_plan_validates_and_resets(ss):
+    bad = ((-1, 0, 0, 0, 0), (17, 0, 0, 0, 0), (0, 2, 0, 0, 0), (0, 0, 2, 0, 0), (0, 0, 0, -5, 0), (0, 0, 0, 0, 3))
+    for args in bad:
+        assert ss.lib.ss_set_test_plan(*args) == SHAPE, args
+    assert ss.lib.ss_set_test_plan(4, 4, 1, 100, 1) == OK
+    assert ss.lib.ss_set_test_plan(0, 0, 0, 0, 0) == OK
+    with ss.test_plan(segments=3):
+        pass
+    with pytest.raises(ss.SSError):
+        with ss.test_plan(segments=99):
+            pass
 
 
 def test_scan_optional_pointers_may_be_null(ss):

@@ -13,7 +13,7 @@ import torch
 import oracle
 import workloads
 from tests.parity import TOL, assert_close
-from tests.test_gpu_parity import BF16, DEV, F32, env, say, small_inputs, to_dev
+from tests.test_gpu_parity import BF16, DEV, F32, plan, say, small_inputs, to_dev
 
 pytestmark = [pytest.mark.gpu,
               pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU")]
@@ -133,7 +133,7 @@ def test_bwd_with_segments(ss, segments, n, dtype):
     say(f"bwd with {segments} forward segments n={n}")
     inp = workloads.random_scan_inputs(2, 1000, 100, n, dtype, seed=60 + n, gated=True, bias=True)
     dy, hh, dl = extras(2, 1000, 100, n, dtype, seed=61, h0=True, dlast=True)
-    with env(SS_SCAN_SEGMENTS=segments):
+    with plan(segments=segments):
         got = grads_gpu(ss, to_dev(inp), dy.to(DEV), hh.to(DEV), dl.to(DEV))
     compare(got, grads_oracle(inp, dy, hh, dl), dtype, f"segments={segments}")
 
@@ -191,7 +191,7 @@ def test_bwd_zoh_with_segments(ss, segments, n, dtype):
     say(f"bwd zoh with {segments} segments n={n}")
     inp = workloads.random_scan_inputs(2, 1000, 100, n, dtype, seed=80 + n, gated=True, bias=True)
     dy, hh, dl = extras(2, 1000, 100, n, dtype, seed=81, h0=True, dlast=True)
-    with env(SS_SCAN_SEGMENTS=segments):
+    with plan(segments=segments):
         got = grads_gpu(ss, to_dev(inp), dy.to(DEV), hh.to(DEV), dl.to(DEV), zoh=True)
     compare(got, grads_oracle(inp, dy, hh, dl, zoh=True), dtype, f"zoh segments={segments}")
 

@@ -16,7 +16,7 @@ import torch
 import oracle
 import workloads
 from tests.parity import assert_close
-from tests.test_gpu_parity import BF16, DEV, F32, env, say
+from tests.test_gpu_parity import BF16, DEV, F32, plan, say
 
 pytestmark = [pytest.mark.gpu,
               pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU")]
@@ -80,7 +80,7 @@ def test_cross_without_softplus_or_bias(ss):
 def test_cross_segments(ss, segments, n):
     say(f"cross with {segments} segments n={n}")
     c = cross_inputs(1, 20, 30, 64, n, F32, seed=9 + n)
-    with env(SS_SCAN_SEGMENTS=segments):
+    with plan(segments=segments):
         check(ss, c, f"segments={segments}")
 
 

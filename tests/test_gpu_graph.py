@@ -11,7 +11,7 @@ import pytest
 import torch
 
 import workloads
-from tests.test_gpu_parity import BF16, DEV, env, say, to_dev
+from tests.test_gpu_parity import BF16, DEV, plan, say, to_dev
 
 pytestmark = [pytest.mark.gpu,
               pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU")]
@@ -43,7 +43,7 @@ def test_scan_fwd_graph_replays(ss, zoh):
     g = to_dev(workloads.random_scan_inputs(2, 3000, 256, 16, BF16, seed=31, gated=True, bias=True))
     other = to_dev(workloads.random_scan_inputs(1, 500, 128, 16, BF16, seed=32, gated=True, bias=True))
     args = (g["u"], g["delta"], g["A_log"], g["B"], g["C"], g["D"], g["z"], g["delta_bias"], True)
-    with env(SS_SCAN_SEGMENTS=4):
+    with plan(segments=4):
         y_e, last_e = ss.scan_fwd(*args, return_last_state=True, zoh=zoh)
         y_g, last_g = torch.empty_like(y_e), torch.empty_like(last_e)
         ws = torch.empty(ss.scan_fwd_workspace_bytes(2, 3000, 256, 16, 1), dtype=torch.uint8, device=DEV)
@@ -66,7 +66,7 @@ def test_scan_bwd_graph_replays(ss, zoh):
     g = to_dev(workloads.random_scan_inputs(2, 2000, 192, 16, BF16, seed=33, gated=True, bias=True))
     dy = torch.randn(2, 2000, 192, device=DEV, generator=torch.Generator(device=DEV).manual_seed(34)).to(BF16)
     args = (g["u"], g["delta"], g["A_log"], g["B"], g["C"], g["D"], dy, g["z"], g["delta_bias"], True)
-    with env(SS_SCAN_SEGMENTS=3):
+    with plan(segments=3):
         ref = ss.scan_bwd(*args, zoh=zoh)
         ws = torch.empty(ss.lib.ss_scan_bwd_workspace_bytes(2, 2000, 192, 16, 1), dtype=torch.uint8, device=DEV)
         graph, got = _capture(lambda: ss.scan_bwd(*args, workspace=ws, zoh=zoh))

@@ -6,7 +6,6 @@ slice of the inputs (every channel is an independent recurrence), with the
 kernel launched exactly as the benchmark launches it.  Tolerances: max
 relative error 1e-4 for fp32 inputs, 2e-2 for bf16 inputs (tests/parity.py).
 """
-import os
 import sys
 
 import numpy as np
@@ -36,22 +35,12 @@ def say(msg):
     sys.stdout.flush()
 
 
-class env:
-    """Temporarily set library test hooks (kernel variant, segment count)."""
+def plan(variant=None, segments=None, waves=None):
+    """Context manager: the library's test plan (kernel variant, segment count, wave layout)."""
+    import selective_state_space_softplus_amd as ss
 
-    def __init__(self, **kv):
-        self.kv = {k: str(v) for k, v in kv.items() if v is not None}
-
-    def __enter__(self):
-        self.old = {k: os.environ.get(k) for k in self.kv}
-        os.environ.update(self.kv)
-
-    def __exit__(self, *a):
-        for k, v in self.old.items():
-            if v is None:
-                os.environ.pop(k, None)
-            else:
-                os.environ[k] = v
+    return ss.test_plan(segments=segments or 0, waves=4 if waves == 4 else 0,
+                        time_parallel=1 if variant == "tpar" else 0)
 
 
 def to_dev(inp):
@@ -142,7 +131,7 @@ def test_scan_small(ss, case):
 def test_scan_forced_variant(ss, variant, segments, n, L):
     say(f"forced variant={variant} segments={segments} n={n} L={L}")
     inp = workloads.random_scan_inputs(2, L, 100, n, F32, seed=7 + n + L, gated=True, bias=True)
-    with env(SS_SCAN_VARIANT=variant, SS_SCAN_SEGMENTS=segments):
+    with plan(variant=variant, segments=segments):
         check_full(ss, inp, f"{variant}/{segments}")
 
 
@@ -295,7 +284,7 @@ def test_prefill_then_decode(ss):
 def test_deterministic_and_causal(ss, n, segments):
     say(f"determinism and causality n={n} segments={segments}")
     inp = to_dev(workloads.random_scan_inputs(2, 700, 130, n, BF16, seed=8, gated=True, bias=True))
-    with env(SS_SCAN_SEGMENTS=segments):
+    with plan(segments=segments):
         y1, l1 = gpu_scan(ss, inp)
         y2, l2 = gpu_scan(ss, inp)
         assert torch.equal(y1, y2) and torch.equal(l1, l2), "run-to-run bitwise determinism"
@@ -363,7 +352,7 @@ def test_scan_seq_shapes(ss, waves, segments):
     """Both wave layouts of scan_seq at n = 16 (8 waves x 2 states, 4 waves x 4 states), with segments."""
     say(f"scan_seq waves={waves} segments={segments}")
     inp = workloads.random_scan_inputs(3, 700, 200, 16, BF16, seed=31, gated=True, bias=True)
-    with env(SS_SCAN_WAVES=waves, SS_SCAN_SEGMENTS=segments):
+    with plan(waves=waves, segments=segments):
         check_full(ss, inp, f"waves={waves} segments={segments}")
 
 

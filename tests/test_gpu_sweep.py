@@ -17,7 +17,7 @@ import oracle
 from tests.parity import assert_close
 from tests.test_gpu_bwd import compare, grads_gpu, grads_oracle
 from tests.test_gpu_cross import check as cross_check, cross_inputs
-from tests.test_gpu_parity import BF16, DEV, F32, env, say, small_inputs, to_dev
+from tests.test_gpu_parity import BF16, DEV, F32, plan, say, small_inputs, to_dev
 
 pytestmark = [pytest.mark.gpu,
               pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU")]
@@ -59,7 +59,7 @@ def test_scan_sweep(ss, seed):
     say(f"scan sweep seed={seed} {c}")
     inp, h0 = inputs(c, seed)
     g = to_dev(inp)
-    with env(SS_SCAN_SEGMENTS=c["segments"]):
+    with plan(segments=c["segments"]):
         y, last = ss.scan_fwd(g["u"], g["delta"], g["A_log"], g["B"], g["C"], g["D"], g["z"], g["delta_bias"],
                               g["delta_softplus"], return_last_state=True, initial_state=dev(h0), zoh=c["zoh"])
         torch.cuda.synchronize()
@@ -77,7 +77,7 @@ def test_bwd_sweep(ss, seed):
     g = torch.Generator().manual_seed(seed + 2)
     dy = torch.randn(c["b"], c["L"], c["d_in"], generator=g).to(c["dtype"])
     dl = torch.randn(c["b"], c["d_in"], c["n"], generator=g) if c["dlast"] else None
-    with env(SS_SCAN_SEGMENTS=c["segments"]):
+    with plan(segments=c["segments"]):
         got = grads_gpu(ss, to_dev(inp), dy.to(DEV), dev(h0), dev(dl), zoh=c["zoh"])
     ref = grads_oracle(inp, dy, h0, dl, zoh=c["zoh"])
     compare(got, ref, c["dtype"], f"seed {seed}")

@@ -13,7 +13,7 @@ import torch
 import oracle
 import workloads
 from tests.parity import assert_close, rel_err
-from tests.test_gpu_parity import BF16, DEV, F32, env, sample_channels, say, small_inputs, to_dev
+from tests.test_gpu_parity import BF16, DEV, F32, plan, sample_channels, say, small_inputs, to_dev
 
 pytestmark = [pytest.mark.gpu,
               pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU")]
@@ -87,7 +87,7 @@ def test_scan_segments(ss, segments, n, L, zoh):
     say(f"segments={segments} n={n} L={L} zoh={zoh}")
     inp = workloads.random_scan_inputs(2, L, 100, n, F32, seed=70 + n + L, gated=True, bias=True)
     h0 = initial_state(2, 100, n, seed=n + L)
-    with env(SS_SCAN_SEGMENTS=segments):
+    with plan(segments=segments):
         check(ss, inp, h0, zoh, f"segments={segments} zoh={zoh}")
 
 
