@@ -161,9 +161,35 @@ int ss_scan_fwd_ex(const void *u, const void *delta, const float *A_log,
  * memory the device can write): SS_OK, or SS_ERR_TIMEOUT when a wait between
  * segments of L gave up, in which case the outputs of that call hold NaN.
  * workspace is the workspace passed to ss_scan_fwd(_ex), ss_cross_scan_fwd
- * or ss_scan_bwd(_ex).  Returns an ss_status.
+ * or ss_scan_bwd(_ex); NULL reads the static scratch of the last
+ * ss_scan_fwd_noalloc call on the current device.  Returns an ss_status.
  */
 int ss_scan_status(const void *workspace, size_t workspace_bytes, int32_t *status, void *stream);
+
+/* Size of the static device array that ss_scan_fwd_noalloc works in. */
+#define SS_NOALLOC_SCRATCH_BYTES (8u << 20)
+
+/*
+ * ss_scan_fwd_ex without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  The scratch is a static device array of
+ * SS_NOALLOC_SCRATCH_BYTES bytes, one per device, looked up on the first call
+ * on a device and held until the process ends; nothing is allocated or freed.
+ * Where the segments along L that ss_scan_fwd_ex would use need more than
+ * that, fewer segments are used (the results are the same, bit for bit;
+ * only the speed differs), so every size ss_scan_fwd_ex accepts is accepted.
+ * All calls on one device share the array: calls that overlap in time on
+ * one device (several streams or host threads) race and must be avoided.
+ * Arguments, sizes and errors otherwise as for ss_scan_fwd_ex.
+ * Returns an ss_status.
+ */
+int ss_scan_fwd_noalloc(const void *u, const void *delta, const float *A_log,
+                        const void *B, const void *C, const float *D,
+                        const void *z, const float *delta_bias, int delta_softplus,
+                        const float *initial_state, int discretization,
+                        void *y, float *last_state,
+                        int64_t b, int64_t L, int64_t d_in, int64_t n, int dtype,
+                        void *stream);
 
 /*
  * One decode step on a persistent state (jiafeimiao.top page: Mamba.step and

@@ -30,7 +30,9 @@ Entry points mirror the C ABI (``include/ss_scan.h``):
 
 scan_fwd, cross_scan_fwd and scan_bwd take ``check=True`` to synchronise and
 raise SSError(SS_ERR_TIMEOUT) when the call's status says a wait between
-segments gave up (its outputs then hold NaN).
+segments gave up (its outputs then hold NaN).  ``scan_fwd(noalloc=True)`` runs
+ss_scan_fwd_noalloc, which works in the library's static scratch instead of a
+workspace.
 
 Shapes follow the mhpn.cn selective_scan walk-through (section 2): u, delta
 (b, L, d_in); A_log (d_in, n) with A = -exp(A_log); B, C (b, L, n); D (d_in).
@@ -66,10 +68,11 @@ SS_MAX_BWD_STATE = 64
 SS_DISC_EULER = 0
 SS_DISC_ZOH = 1
 SS_ERR_TIMEOUT = -10
+SS_NOALLOC_SCRATCH_BYTES = 8 << 20
 STATUS = {0: "SS_OK", -1: "SS_ERR_NULL", -2: "SS_ERR_SHAPE", -3: "SS_ERR_DTYPE", -4: "SS_ERR_UNSUPPORTED",
           -5: "SS_ERR_WORKSPACE", -6: "SS_ERR_HIP", -7: "SS_ERR_ALIAS", -8: "SS_ERR_ALIGN", -9: "SS_ERR_MODE",
           -10: "SS_ERR_TIMEOUT"}
-EXPORTS = ("ss_scan_fwd_workspace_bytes", "ss_scan_fwd", "ss_scan_fwd_ex", "ss_scan_status",
+EXPORTS = ("ss_scan_fwd_workspace_bytes", "ss_scan_fwd", "ss_scan_fwd_ex", "ss_scan_fwd_noalloc", "ss_scan_status",
            "ss_state_update", "ss_state_update_ex", "ss_scan_bwd", "ss_scan_bwd_ex", "ss_scan_bwd_workspace_bytes",
            "ss_cross_scan_fwd", "ss_cross_scan_fwd_workspace_bytes", "ss_conv_update", "ss_status_string",
            "ss_set_test_plan")
@@ -93,6 +96,8 @@ def _load() -> ctypes.CDLL:
     lib.ss_scan_fwd.argtypes = [P, P, P, P, P, P, P, P, I, P, P, I64, I64, I64, I64, I, P, ctypes.c_size_t, P]
     lib.ss_scan_fwd_ex.restype = I
     lib.ss_scan_fwd_ex.argtypes = [P, P, P, P, P, P, P, P, I, P, I, P, P, I64, I64, I64, I64, I, P, ctypes.c_size_t, P]
+    lib.ss_scan_fwd_noalloc.restype = I
+    lib.ss_scan_fwd_noalloc.argtypes = [P, P, P, P, P, P, P, P, I, P, I, P, P, I64, I64, I64, I64, I, P]
     lib.ss_scan_status.restype = I
     lib.ss_scan_status.argtypes = [P, ctypes.c_size_t, P, P]
     lib.ss_set_test_plan.restype = I
@@ -160,11 +165,12 @@ def scan_fwd_workspace_bytes(b: int, L: int, d_in: int, n: int, dtype: int) -> i
     return int(lib.ss_scan_fwd_workspace_bytes(b, L, d_in, n, dtype))
 
 
-def scan_status(workspace) -> int:
-    """Status the last scan call with ``workspace`` left: SS_OK or SS_ERR_TIMEOUT.  Synchronises the stream."""
-    dev = workspace.device
+def scan_status(workspace, device=None) -> int:
+    """Status the last scan call with ``workspace`` (None: the static scratch of the last
+    noalloc scan on ``device``) left: SS_OK or SS_ERR_TIMEOUT.  Synchronises the stream."""
+    dev = workspace.device if workspace is not None else torch.device(device if device is not None else "cuda")
     out = torch.empty(1, dtype=torch.int32, device=dev)
-    nbytes = workspace.numel() * workspace.element_size()
+    nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     with torch.cuda.device(dev):
         rc = lib.ss_scan_status(_ptr(workspace), nbytes, _ptr(out), _stream(dev))
     if rc != 0:
@@ -172,8 +178,8 @@ def scan_status(workspace) -> int:
     return int(out.item())
 
 
-def _raise_on_timeout(workspace, where):
-    code = scan_status(workspace)
+def _raise_on_timeout(workspace, where, device=None):
+    code = scan_status(workspace, device)
     if code != 0:
         raise SSError(code, where)
 
@@ -206,10 +212,11 @@ def _workspace(device, nbytes: int):
 
 
 def scan_fwd(u, delta, A_log, B, C, D, z=None, delta_bias=None, delta_softplus=True, return_last_state=False,
-             out=None, last_state=None, workspace=None, initial_state=None, zoh=False, check=False):
+             out=None, last_state=None, workspace=None, initial_state=None, zoh=False, noalloc=False, check=False):
     """Selective scan forward on the GPU; returns y (and last_state if asked).
 
     ``initial_state`` may be the ``last_state`` buffer itself (carried over in place).
+    ``noalloc``: ss_scan_fwd_noalloc (the library's static scratch; no workspace).
     ``check``: synchronise and raise if a wait between segments gave up.
     """
     if u.dim() != 3 or A_log.dim() != 2:
@@ -239,6 +246,17 @@ def scan_fwd(u, delta, A_log, B, C, D, z=None, delta_bias=None, delta_softplus=T
                 last_state.zero_()
             elif initial_state.data_ptr() != last_state.data_ptr():
                 last_state.copy_(initial_state)
+        return (y, last_state) if return_last_state else y
+    if noalloc:
+        with torch.cuda.device(dev):
+            rc = lib.ss_scan_fwd_noalloc(_ptr(u), _ptr(delta), _ptr(A_log), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
+                                         _ptr(delta_bias), int(bool(delta_softplus)), _ptr(initial_state),
+                                         SS_DISC_ZOH if zoh else SS_DISC_EULER, _ptr(y), _ptr(last_state),
+                                         b, L, d_in, n, code, _stream(dev))
+        if rc != 0:
+            raise SSError(rc, "ss_scan_fwd_noalloc")
+        if check:
+            _raise_on_timeout(None, "ss_scan_fwd_noalloc", dev)
         return (y, last_state) if return_last_state else y
     need = scan_fwd_workspace_bytes(b, L, d_in, n, code)
     if workspace is None:

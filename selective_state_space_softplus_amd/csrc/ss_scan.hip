@@ -2,7 +2,8 @@
 // of kernel and launch shape, and the C entry points declared in ss_scan.h.
 //
 // Nothing here allocates device memory or synchronises: every launch goes on
-// the caller's stream, and the only scratch memory is the caller's workspace.
+// the caller's stream, and the only scratch memory is the caller's workspace
+// or, for ss_scan_fwd_noalloc, a static device array of fixed size.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -147,14 +148,40 @@ SS_EXPORT size_t ss_scan_fwd_workspace_bytes(int64_t b, int64_t L, int64_t d_in,
     return seq_workspace(b, d_in, n).total;
 }
 
+// Static scratch of ss_scan_fwd_noalloc, one copy per device, kept until the
+// process ends.  Host code reaches it only through the address
+// hipGetSymbolAddress returns for the current device (in host code the
+// array's own name is a host-side stand-in, not a device address).
+static __device__ __align__(256) unsigned char scratch[SS_NOALLOC_SCRATCH_BYTES];
+
 namespace {
 
-// The scan forward behind ss_scan_fwd_ex: the caller's workspace must be as
-// large as the query says.
+// Device address of `scratch` on the current device, looked up once per
+// device; null if the lookup fails.
+void* scratch_address() {
+    static std::mutex mu;
+    static void* addr[64] = {};
+    static bool done[64] = {};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
+    std::lock_guard<std::mutex> g(mu);
+    if (!done[dev]) {
+        void* ptr = nullptr;
+        if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess) return nullptr;
+        addr[dev] = ptr;
+        done[dev] = true;
+    }
+    return addr[dev];
+}
+
+// The scan forward behind ss_scan_fwd_ex and ss_scan_fwd_noalloc.  `own_ws`:
+// the workspace is the caller's, which must be as large as the query says;
+// otherwise it is the library's static scratch, and the segment count is
+// lowered until the scan fits in it.
 int scan_fwd_impl(const void* u, const void* delta, const float* A_log, const void* B, const void* C,
                   const float* D, const void* z, const float* delta_bias, int delta_softplus,
                   const float* initial_state, int discretization, void* y, float* last_state, int64_t b, int64_t L,
-                  int64_t d_in, int64_t n, int dtype, void* workspace, size_t workspace_bytes,
+                  int64_t d_in, int64_t n, int dtype, void* workspace, size_t workspace_bytes, bool own_ws,
                   void* stream) {
     if (!u || !delta || !A_log || !B || !C || !D || !y) return SS_ERR_NULL;
     if (!sizes_ok(b, L, d_in) || n <= 0 || d_in > SS_MAX_CHANNELS) return SS_ERR_SHAPE;
@@ -183,14 +210,22 @@ int scan_fwd_impl(const void* u, const void* delta, const float* A_log, const vo
     for (const Range& r : ins)
         if (overlaps(r, ry) || overlaps(r, rs)) return SS_ERR_ALIAS;
     if (overlaps(ry, rs) || overlaps(rh, ry) || (!in_place && overlaps(rh, rs))) return SS_ERR_ALIAS;
-    const size_t need = ss_scan_fwd_workspace_bytes(b, L, d_in, n, dtype);
-    if (!workspace || workspace_bytes < need) return SS_ERR_WORKSPACE;
-    // The workspace starts with 32-bit words updated by device atomics.
-    if (!aligned(workspace, 256)) return SS_ERR_ALIGN;
-    const Range rw = range_of(workspace, int64_t(workspace_bytes), 1);
-    for (const Range& r : ins)
-        if (overlaps(r, rw)) return SS_ERR_ALIAS;
-    if (overlaps(ry, rw) || overlaps(rs, rw) || overlaps(rh, rw)) return SS_ERR_ALIAS;
+    if (own_ws) {
+        const size_t need = ss_scan_fwd_workspace_bytes(b, L, d_in, n, dtype);
+        if (!workspace || workspace_bytes < need) return SS_ERR_WORKSPACE;
+        // The workspace starts with 32-bit words updated by device atomics.
+        if (!aligned(workspace, 256)) return SS_ERR_ALIGN;
+        const Range rw = range_of(workspace, int64_t(workspace_bytes), 1);
+        for (const Range& r : ins)
+            if (overlaps(r, rw)) return SS_ERR_ALIAS;
+        if (overlaps(ry, rw) || overlaps(rs, rw) || overlaps(rh, rw)) return SS_ERR_ALIAS;
+    } else {
+        // Validation is done: only now is the device touched.
+        workspace = scratch_address();
+        if (!workspace) return SS_ERR_HIP;
+        workspace_bytes = SS_NOALLOC_SCRATCH_BYTES;
+        if (workspace_bytes < seq_workspace(b, d_in, n, 1).total) return SS_ERR_WORKSPACE;
+    }
 
     ScanParams p{};
     p.u = u;
@@ -235,11 +270,26 @@ SS_EXPORT int ss_scan_fwd_ex(const void* u, const void* delta, const float* A_lo
                              int64_t L, int64_t d_in, int64_t n, int dtype, void* workspace, size_t workspace_bytes,
                              void* stream) {
     return scan_fwd_impl(u, delta, A_log, B, C, D, z, delta_bias, delta_softplus, initial_state, discretization, y,
-                         last_state, b, L, d_in, n, dtype, workspace, workspace_bytes, stream);
+                         last_state, b, L, d_in, n, dtype, workspace, workspace_bytes, true, stream);
+}
+
+SS_EXPORT int ss_scan_fwd_noalloc(const void* u, const void* delta, const float* A_log, const void* B,
+                                  const void* C, const float* D, const void* z, const float* delta_bias,
+                                  int delta_softplus, const float* initial_state, int discretization, void* y,
+                                  float* last_state, int64_t b, int64_t L, int64_t d_in, int64_t n, int dtype,
+                                  void* stream) {
+    return scan_fwd_impl(u, delta, A_log, B, C, D, z, delta_bias, delta_softplus, initial_state, discretization, y,
+                         last_state, b, L, d_in, n, dtype, nullptr, 0, false, stream);
 }
 
 SS_EXPORT int ss_scan_status(const void* workspace, size_t workspace_bytes, int32_t* status, void* stream) {
-    if (!workspace || !status) return SS_ERR_NULL;
+    if (!status) return SS_ERR_NULL;
+    if (!workspace) {
+        // The static scratch of ss_scan_fwd_noalloc on the current device.
+        workspace = scratch_address();
+        if (!workspace) return SS_ERR_HIP;
+        workspace_bytes = SS_NOALLOC_SCRATCH_BYTES;
+    }
     if (workspace_bytes < 256) return SS_ERR_WORKSPACE;
     if (!aligned(workspace, 256) || !aligned(status, 4)) return SS_ERR_ALIGN;
     hipLaunchKernelGGL(ss::scan_status_copy, dim3(1), dim3(64), 0, static_cast<hipStream_t>(stream),

@@ -30,7 +30,7 @@ def declared_functions():
 def test_header_declares_the_entry_points():
     assert declared_functions() == sorted(["ss_conv_update", "ss_cross_scan_fwd", "ss_cross_scan_fwd_workspace_bytes",
                                            "ss_scan_bwd", "ss_scan_bwd_ex", "ss_scan_bwd_workspace_bytes", "ss_scan_fwd",
-                                           "ss_scan_fwd_ex", "ss_scan_status",
+                                           "ss_scan_fwd_ex", "ss_scan_fwd_noalloc", "ss_scan_status",
                                            "ss_scan_fwd_workspace_bytes", "ss_set_test_plan", "ss_state_update",
                                            "ss_state_update_ex", "ss_status_string"])
 
@@ -110,6 +110,22 @@ def call_scan(ss, a):
 ])
 def test_scan_rejects(ss, over, code):
     assert call_scan(ss, scan_args(**over)) == code
+
+
+def call_scan_noalloc(ss, a, h0=None, disc=0):
+    return ss.lib.ss_scan_fwd_noalloc(a["u"], a["delta"], a["A_log"], a["B"], a["C"], a["D"], a["z"], a["bias"],
+                                      a["softplus"], h0, disc, a["y"], a["last"], a["b"], a["L"], a["d_in"], a["n"],
+                                      a["dtype"], a["stream"])
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(u=None), NULL), (dict(y=None), NULL), (dict(b=0), SHAPE), (dict(dtype=2), DTYPE), (dict(n=65), UNSUP),
+    (dict(u=addr(1) + 2), ALIGN), (dict(y=addr(1) + 64), ALIAS), (dict(last=addr(4)), ALIAS),
+])
+def test_scan_noalloc_rejects_before_touching_the_device(ss, over, code):
+    # The static scratch is looked up only after validation, so these run without a GPU.
+    assert call_scan_noalloc(ss, scan_args(**over)) == code
+    assert call_scan_noalloc(ss, scan_args(), disc=7) == MODE
 
 
 def test_scan_status_rejects(ss):
