@@ -143,8 +143,7 @@ __device__ __forceinline__ void store_span(TIn* p, uint32_t e, const float* y, i
     if constexpr (VEC && sizeof(TIn) == 2) {
         uint32_t ww[(V + 1) / 2];
 #pragma unroll
-        for (int i = 0; i < V / 2; i++)
-            ww[i] = uint32_t(f32_to_bf16(y[2 * i])) | (uint32_t(f32_to_bf16(y[2 * i + 1])) << 16);
+        for (int i = 0; i < V / 2; i++) ww[i] = f32x2_to_bf16x2(y[2 * i], y[2 * i + 1]);
         if constexpr (V == 2) {
             *reinterpret_cast<uint32_t*>(p + e) = ww[0];
         } else if constexpr (V == 4) {
@@ -374,6 +373,7 @@ __global__ __launch_bounds__((SC + kSeqElemWaves + 1) * 64) void scan_seq(const 
     const int ec = (etid - er * TPR) * V;
     const int ech = dbase + ec;
     const int evalid = elem ? max(0, min(V, d_in - ech)) : 0;
+    const bool whole_span = evalid == V;           // all V channels of this thread exist
     const uint32_t off_el = uint32_t(er) * uint32_t(d_in) + uint32_t(evalid > 0 ? ech : 0);
     float Dv[V], bias_v[V];
 #pragma unroll
@@ -448,16 +448,72 @@ __global__ __launch_bounds__((SC + kSeqElemWaves + 1) * 64) void scan_seq(const 
         for (int ii = 0; ii < BI; ii++)
             load_to_lds<ES>(base + min(ii * 64 + lane, last), block + ii * 256);
     };
+    // Whole chunks (all T rows inside the segment, and the B/C block within
+    // the segment's rows) are loaded through buffer descriptors based at the
+    // chunk's first row: per-lane byte offsets fixed at the start, per-load
+    // offsets in scalar registers, so the loader issues no vector
+    // instruction for them.  Each descriptor covers exactly the bytes its
+    // loads read.  The other chunks take the clamped loads above.
+    // The forms for whole chunks below (loads, the step-size phase, the B/C
+    // staging) are taken by the Euler forward only: in the zero-order-hold
+    // and dz forms, whose recurrence waves already fill the register file,
+    // they made one fp32 build (8 x 4 states, zero-order hold, dz) compute a
+    // wrong dz, though the same source run on the host is correct.
+    constexpr bool kWholeForms = !ZOH && !DZ && !CROSS;
+    constexpr bool kFastLoads = WIDE && kWholeForms;
+    constexpr int XEPL = 16 / ES, XLPR = 64 / XEPL, XRPI = 64 / XLPR;   // elements, lanes, rows per 16-byte load
+    uint32_t vo_x = 0;
+    if constexpr (kFastLoads) {
+        const int q = lane % XLPR;
+        vo_x = uint32_t(lane / XLPR) * uint32_t(d_in) * ES + uint32_t(dbase + q * XEPL < d_in ? q * XEPL : 0) * ES;
+    }
+    // The LDS block as an LDS-space pointer.  scan_seq declares no static
+    // LDS, so the 16-byte-aligned dynamic block starts at the static size.
+    const lds_ptr lds3 = dynamic_lds_base();
+    const bool lds3_ok = __builtin_amdgcn_groupstaticsize() == 0;
+    auto whole_chunk = [&](int k) -> bool {
+        const int t0 = t_begin + k * T;
+        return lds3_ok && t0 + T <= t_end && BI * 64 <= (t_end - t0) * n;
+    };
+    auto fast_x = [&](const TIn* src, lds_ptr tile, int k) {
+        const int64_t row0 = brow + t_begin + int64_t(k) * T;
+        const auto rs = buffer_rsrc(src + row0 * d_in + dbase, uint32_t(T) * uint32_t(d_in) * ES);
+#pragma unroll
+        for (int ii = 0; ii < XI; ii++)
+            buffer_load_to_lds<16>(rs, tile + ii * 1024, vo_x, uint32_t(ii * XRPI) * uint32_t(d_in) * ES);
+    };
+    auto fast_bc = [&](const TIn* src, lds_ptr block, int k) {
+        const int64_t row0 = brow + t_begin + int64_t(k) * T;
+        const auto rs = buffer_rsrc(src + row0 * n, uint32_t(BI * 64 * ES));
+#pragma unroll
+        for (int ii = 0; ii < BI; ii++)
+            buffer_load_to_lds<ES>(rs, block + ii * 256, uint32_t(lane * ES), uint32_t(ii * 64 * ES));
+    };
     auto dma_chunk = [&](int k, int slot) {        // u, delta, B, C of chunk k into ring slot `slot`
         char* ru = lds + Lds::off_ru + slot * 2 * Lds::RX;
         char* rbc = lds + Lds::off_rbc + slot * 2 * Lds::RBC;
-        dma_x(static_cast<const TIn*>(p.u), ru, k, true);
-        dma_x(static_cast<const TIn*>(p.delta), ru + Lds::RX, k, false);
-        dma_bc(static_cast<const TIn*>(p.B), rbc, k);
-        dma_bc(static_cast<const TIn*>(p.C), rbc + Lds::RBC, k);
+        if (kFastLoads && whole_chunk(k)) {
+            // (LDS offsets formed here: hoisted, the 3 ring slots' dozen
+            // destination addresses would not fit the scalar registers.)
+            const lds_ptr ru3 = lds3 + opaque_scalar(Lds::off_ru + slot * 2 * Lds::RX);
+            const lds_ptr rbc3 = lds3 + opaque_scalar(Lds::off_rbc + slot * 2 * Lds::RBC);
+            fast_x(static_cast<const TIn*>(p.u), ru3, k);
+            fast_x(static_cast<const TIn*>(p.delta), ru3 + Lds::RX, k);
+            fast_bc(static_cast<const TIn*>(p.B), rbc3, k);
+            fast_bc(static_cast<const TIn*>(p.C), rbc3 + Lds::RBC, k);
+        } else {
+            dma_x(static_cast<const TIn*>(p.u), ru, k, true);
+            dma_x(static_cast<const TIn*>(p.delta), ru + Lds::RX, k, false);
+            dma_bc(static_cast<const TIn*>(p.B), rbc, k);
+            dma_bc(static_cast<const TIn*>(p.C), rbc + Lds::RBC, k);
+        }
     };
     auto dma_z = [&](int k, int slot) {
-        if (GATE) dma_x(static_cast<const TIn*>(p.z), lds + Lds::off_rz + slot * Lds::RX, k, false);
+        if (!GATE) return;
+        if (kFastLoads && whole_chunk(k))
+            fast_x(static_cast<const TIn*>(p.z), lds3 + opaque_scalar(Lds::off_rz + slot * Lds::RX), k);
+        else
+            dma_x(static_cast<const TIn*>(p.z), lds + Lds::off_rz + slot * Lds::RX, k, false);
     };
 
     // ---- element waves
@@ -469,9 +525,9 @@ __global__ __launch_bounds__((SC + kSeqElemWaves + 1) * 64) void scan_seq(const 
         Row su, sd;
         su.read(ru, er, ec);
         sd.read(ru + Lds::RX, er, ec);
-        const int valid = ev(k);
         float* buf = s_dw + slot * DW_BUF;
-        if (valid == V) {                          // a whole row: nothing to mask
+        // A whole row (for the Euler forward: of a whole chunk) has nothing to mask.
+        if (kWholeForms ? rows(k) == T && whole_span : ev(k) == V) {
 #pragma unroll
             for (int i = 0; i < V; i++) {
                 const float x = sd.f(i) + bias_v[i];
@@ -481,6 +537,7 @@ __global__ __launch_bounds__((SC + kSeqElemWaves + 1) * 64) void scan_seq(const 
                     make_float2(dl, ZOH ? uv[i] : dl * uv[i]);
             }
         } else {
+            const int valid = ev(k);
 #pragma unroll
             for (int i = 0; i < V; i++) {
                 const bool ok = i < valid;
@@ -499,6 +556,21 @@ __global__ __launch_bounds__((SC + kSeqElemWaves + 1) * 64) void scan_seq(const 
         const uint32_t* rcc = rb + Lds::RBC / 4;
         float* buf = s_bc + slot * BC_BUF;
         const int r = rows(k);
+        auto widen = [](uint32_t w) { return ES == 2 ? __uint_as_float(w << 16) : __uint_as_float(w); };
+        // Every row and state exists: no masks.  (Not in the 8-state-per-wave
+        // shape, where this form makes the compiler emit an invalid compare.)
+        if (kWholeForms && NSW <= 4 && r == T && n == NP) {
+#pragma unroll
+            for (int m = 0; m < EBC; m++) {
+                const int f = m * NE + etid;
+                if ((T * NP) % NE != 0 && f >= T * NP) break;
+                const int j = f / NP, kk = f % NP;
+                float* dst = buf + ((j * SC + kk / NSW) * 2) * NSW + kk % NSW;
+                dst[0] = widen(rb[f]);
+                dst[NSW] = widen(rcc[f]);
+            }
+            return;
+        }
 #pragma unroll
         for (int m = 0; m < EBC; m++) {
             const int f = m * NE + etid;

@@ -28,6 +28,13 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
     __bf16 h = (__bf16)f;
     return __builtin_bit_cast(uint16_t, h);
 }
+// Two values narrowed at once (one v_cvt_pk_bf16_f32): lo in bits 0-15.
+__device__ __forceinline__ uint32_t f32x2_to_bf16x2(float lo, float hi) {
+    typedef float f32x2 __attribute__((ext_vector_type(2)));
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    const f32x2 v = {lo, hi};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
+}
 
 // Workgroup barrier that orders LDS accesses only.  __syncthreads() also
 // fences global memory, which makes every wave wait for all its outstanding
@@ -49,6 +56,46 @@ __device__ __forceinline__ void load_to_lds(const void* src, void* lds_dst) {
     if constexpr (BYTES == 16) __builtin_amdgcn_global_load_lds(src, lds_dst, 16, 0, 0);
     else if constexpr (BYTES == 4) __builtin_amdgcn_global_load_lds(src, lds_dst, 4, 0, 0);
     else __builtin_amdgcn_global_load_lds(src, lds_dst, 2, 0, 0);
+}
+
+// Direct-to-LDS load through a buffer descriptor: every lane reads BYTES bytes
+// at byte offset voff + soff of the descriptor's base and the wave's data
+// lands in LDS at `lds_dst` + lane * max(BYTES, 4).  `soff` is wave-uniform
+// (a scalar register), so a stream of such loads whose per-lane offsets are
+// fixed costs no vector instruction.  Lanes whose voff is at or beyond the
+// descriptor's byte count read zeros instead of memory.
+using lds_ptr = __attribute__((address_space(3))) char*;
+
+// LDS-space pointer to the start of a kernel's dynamic LDS (extern
+// __shared__), which begins where the static allocation ends; a kernel that
+// declares no static LDS gets 0.  Formed from the LDS address itself: a cast
+// of the generic pointer would add a null check of it.
+__device__ __forceinline__ lds_ptr dynamic_lds_base() {
+    return (lds_ptr)(uintptr_t)__builtin_amdgcn_groupstaticsize();
+}
+
+// `v` unchanged, but opaque to the optimiser: a constant passed through here
+// is formed where it is used (one scalar instruction) instead of being
+// hoisted into a register of its own for a whole loop.
+__device__ __forceinline__ uint32_t opaque_scalar(uint32_t v) {
+    asm volatile("" : "+s"(v));
+    return v;
+}
+
+template <int BYTES>
+__device__ __forceinline__ void buffer_load_to_lds(__amdgpu_buffer_rsrc_t rsrc, lds_ptr lds_dst, uint32_t voff,
+                                                   uint32_t soff) {
+    static_assert(BYTES == 2 || BYTES == 4 || BYTES == 16, "direct-to-LDS load size");
+    auto* dst = (__attribute__((address_space(3))) void*)lds_dst;
+    if constexpr (BYTES == 16) __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, dst, 16, voff, soff, 0, 0);
+    else if constexpr (BYTES == 4) __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, dst, 4, voff, soff, 0, 0);
+    else __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, dst, 2, voff, soff, 0, 0);
+}
+
+// Buffer descriptor of `bytes` bytes at `base` (wave-uniform): untyped, no
+// stride, the data-format word that raw buffer accesses take on gfx9 parts.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, int(bytes), 0x00020000);
 }
 
 // Wait until at most N vector-memory operations of this wave are outstanding.

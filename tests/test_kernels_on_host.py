@@ -1,0 +1,136 @@
+"""CPU: the library's own HIP sources run on the host (tests/host_kernels.py).
+
+Every entry point here goes through the real C ABI code (validation, launch
+planning, segments) and the real kernel source, compiled for the CPU against
+a stand-in of the HIP device API with AddressSanitizer and
+UndefinedBehaviorSanitizer: each tensor is an allocation of exactly its
+size, and the bytes of LDS past a launch's dynamic size are poisoned, so a
+load, store or direct-to-LDS copy outside its tensor or outside the
+workgroup's LDS -- including one through a clamped index or a ring slot --
+ends the run with a report.  Outputs are compared with the oracle at the
+usual tolerances.  The cases cover every launch shape of the forward
+(1x2, 4x2, 8x2, 4x4, 8x4, 8x8 states), both load forms (16-byte and element),
+ragged L and d_in, segments along L, the zero-order hold, an initial state,
+the backward pass, the decode step and the cross scan; among them is the
+case (b=1, L=77, d_in=20, n=3, fp32, gated) that a one-wave shape of the
+forward, no longer built, once faulted on.
+"""
+import shutil
+
+import pytest
+import torch
+
+import oracle
+import workloads
+from tests import host_kernels as hk
+from tests.parity import TOL, assert_close
+
+F32, BF16 = torch.float32, torch.bfloat16
+
+pytestmark = pytest.mark.skipif(not shutil.which(hk.CLANG) and not __import__("os").path.exists(hk.CLANG),
+                                reason="needs the ROCm host clang")
+
+
+def _code(dt):
+    return 1 if dt == BF16 else 0
+
+
+def fwd_case(b, L, d, n, dt, gated=True, bias=True, softplus=True, zoh=False, h0=False, segments=0, waves=0,
+             seed=0, misalign=False, mode="fwd"):
+    inp = workloads.random_scan_inputs(b, L, d, n, dt, seed=seed, gated=gated, bias=bias)
+    if not softplus:
+        # Without softplus the step size is delta + bias itself, so keep it positive.
+        inp["delta"] = (inp["delta"].float().abs() * 0.1 + 0.01).to(dt)
+        if inp["delta_bias"] is not None:
+            inp["delta_bias"] = inp["delta_bias"].abs() * 0.01
+    h = torch.randn(b, d, n, generator=torch.Generator().manual_seed(seed + 1)) * 0.5 if h0 else None
+    t = dict(u=inp["u"], delta=inp["delta"], A_log=inp["A_log"], B=inp["B"], C=inp["C"], D=inp["D"], z=inp["z"],
+             delta_bias=inp["delta_bias"], h0=h)
+    args = dict(b=b, L=L, d_in=d, n=n, dtype=_code(dt), softplus=int(softplus), zoh=int(zoh), segments=segments,
+                waves=waves)
+    got = hk.run(mode, t, args, dict(y=((b, L, d), dt), last_state=((b, d, n), F32)))
+    yr, lr = oracle.scan(inp["u"], inp["delta"], inp["A_log"], inp["B"], inp["C"], inp["D"], inp["z"],
+                         inp["delta_bias"], softplus, h0=h, zoh=zoh)
+    assert_close(got["y"], yr, dt, "host y")
+    assert_close(got["last_state"], lr, dt, "host last_state")
+
+
+FWD = [
+    # b, L, d_in, n, dtype, options
+    (1, 77, 20, 3, F32, {}),                            # the case the removed one-wave shape faulted on
+    (2, 90, 24, 3, F32, {}),
+    (1, 77, 20, 4, BF16, {}),
+    (2, 61, 66, 8, BF16, dict(gated=False)),
+    (2, 130, 96, 16, BF16, dict(segments=3)),           # 8 x 2 states, 16-byte loads, whole and ragged chunks
+    (1, 100, 130, 16, F32, dict(segments=2, h0=True)),
+    (2, 97, 64, 16, BF16, dict(waves=4)),               # 4 x 4 states
+    (1, 70, 41, 16, BF16, {}),                          # element loads (d_in * 2 not a multiple of 16)
+    (1, 70, 40, 32, F32, dict(zoh=True)),               # 8 x 4 states, zero-order hold
+    (1, 64, 96, 32, F32, dict(zoh=True, segments=2)),
+    (1, 45, 40, 64, BF16, {}),                          # 8 x 8 states
+    (2, 33, 10, 1, F32, dict(softplus=False)),          # 1 x 2 states
+    (1, 129, 70, 2, BF16, dict(h0=True, zoh=True)),
+]
+
+
+@pytest.mark.parametrize("case", FWD, ids=lambda c: f"b{c[0]}L{c[1]}d{c[2]}n{c[3]}{'bf16' if c[4] == BF16 else 'f32'}"
+                         + "".join(f"-{k}{v}" for k, v in c[5].items()) if isinstance(c, tuple) else str(c))
+def test_forward_on_host(case):
+    b, L, d, n, dt, opt = case
+    fwd_case(b, L, d, n, dt, seed=b + L + d + n, **opt)
+
+
+def test_noalloc_on_host():
+    fwd_case(2, 150, 70, 16, BF16, segments=4, seed=5, mode="noalloc")
+
+
+@pytest.mark.parametrize("case", [(1, 64, 96, 32, F32, True), (2, 50, 70, 16, BF16, False), (1, 40, 64, 64, F32, False)],
+                         ids=["n32-f32-zoh", "n16-bf16", "n64-f32"])
+def test_backward_on_host(case):
+    b, L, d, n, dt, zoh = case
+    inp = workloads.random_scan_inputs(b, L, d, n, dt, seed=11, gated=True, bias=True)
+    g = torch.Generator().manual_seed(12)
+    dy = torch.randn(b, L, d, generator=g).to(dt)
+    t = dict(u=inp["u"], delta=inp["delta"], A_log=inp["A_log"], B=inp["B"], C=inp["C"], D=inp["D"], z=inp["z"],
+             delta_bias=inp["delta_bias"], dy=dy)
+    args = dict(b=b, L=L, d_in=d, n=n, dtype=_code(dt), softplus=1, zoh=int(zoh), segments=2)
+    outs = dict(du=((b, L, d), dt), ddelta=((b, L, d), dt), dA_log=((d, n), F32), dB=((b, L, n), dt),
+                dC=((b, L, n), dt), dD=((d,), F32), dz=((b, L, d), dt), ddelta_bias=((d,), F32))
+    got = hk.run("bwd", t, args, outs)
+    ref = oracle.scan_bwd(inp["u"], inp["delta"], inp["A_log"], inp["B"], inp["C"], inp["D"], inp["z"],
+                          inp["delta_bias"], True, None, dy, None, zoh=zoh)
+    for k in outs:
+        assert_close(got[k], ref[k], dt, f"host {k}")
+
+
+@pytest.mark.parametrize("b,d,n,dt", [(3, 70, 16, BF16), (2, 33, 5, F32)])
+def test_step_on_host(b, d, n, dt):
+    dec = workloads.decode_inputs(4, steps=1, b=b)
+    g = torch.Generator().manual_seed(b + d)
+    state = torch.randn(b, d, n, generator=g) * 0.1
+    x, dtv, z = (torch.randn(b, d, generator=g).to(dt) for _ in range(3))
+    B, C = (torch.randn(b, n, generator=g).to(dt) for _ in range(2))
+    A_log = workloads.s4d_real_A_log(d, n)
+    D, bias = torch.randn(d, generator=g), dec["dt_bias"][:d].contiguous()
+    t = dict(state=state, x=x, dt=dtv, A_log=A_log, B=B, C=C, D=D, z=z, dt_bias=bias)
+    got = hk.run("step", t, dict(b=b, d_in=d, n=n, dtype=_code(dt), softplus=1, zoh=0),
+                 dict(y=((b, d), dt), state=((b, d, n), F32)))
+    sr, yr = oracle.state_update(state, x, dtv, A_log, B, C, D, z, bias, True)
+    assert_close(got["y"], yr, dt, "host step y")
+    assert_close(got["state"], sr, dt, "host step state")
+
+
+def test_cross_on_host():
+    maps, H, W, d, n = 2, 5, 7, 24, 1
+    g = torch.Generator().manual_seed(3)
+    x = torch.randn(maps, H, W, d, generator=g)
+    delta = torch.randn(maps, 4, H * W, d, generator=g) - 2
+    B, C = (torch.randn(maps, 4, H * W, n, generator=g) for _ in range(2))
+    A_log = torch.zeros(4, d, n)
+    D = torch.randn(4, d, generator=g)
+    t = dict(x=x, delta=delta, A_log=A_log, B=B, C=C, D=D)
+    got = hk.run("cross", t, dict(maps=maps, H=H, W=W, d_in=d, n=n, dtype=0, softplus=1, segments=2),
+                 dict(y=((maps, H, W, d), F32), last_state=((maps, 4, d, n), F32)))
+    yr, lr = oracle.cross_scan(x, delta, A_log, B, C, D, None, True)
+    assert_close(got["y"], yr, F32, "host cross y")
+    assert_close(got["last_state"], lr, F32, "host cross last_state")
