@@ -294,6 +294,7 @@ __global__ __launch_bounds__((SC + kSeqElemWaves + 1) * 64) void scan_seq(const 
     static_assert(!DZ || (GATE && !CROSS), "dz is the gradient of a gated scan");
     extern __shared__ __align__(16) float smem[];
     char* const lds = reinterpret_cast<char*>(smem);
+    const lds_ptr lds3 = dynamic_lds_base();       // the same block as an LDS-space pointer (direct-to-LDS loads)
     float* s_dw = reinterpret_cast<float*>(lds + Lds::off_dw);   // [3][T/2][64][4]: (delta'_j, w_j, delta'_j+1, w_j+1)
     // Channel c of a (delta', delta' u) row sits in 16-byte slot dw_slot(c): an
     // element thread writes its V consecutive channels at a 16*V-byte stride
@@ -416,7 +417,7 @@ __global__ __launch_bounds__((SC + kSeqElemWaves + 1) * 64) void scan_seq(const 
     // read its last row, channels past d_in read channel dbase; both are masked).
     // `mapped`: rows of the cross scan's map (u), else rows of this batch row.
     auto xrow = [&](bool mapped, int t) -> int64_t { return CROSS && mapped ? mrow + cross_pos(t) : brow + t; };
-    auto dma_x = [&](const TIn* src, char* tile, int k, bool mapped) {
+    auto dma_x = [&](const TIn* src, lds_ptr tile, int k, bool mapped) {
         const int t0 = t_begin + k * T;
         if constexpr (WIDE) {
             constexpr int EPL = 16 / ES;           // elements per lane
@@ -438,7 +439,7 @@ __global__ __launch_bounds__((SC + kSeqElemWaves + 1) * 64) void scan_seq(const 
             }
         }
     };
-    auto dma_bc = [&](const TIn* src, char* block, int k) {
+    auto dma_bc = [&](const TIn* src, lds_ptr block, int k) {
         const int t0 = min(t_begin + k * T, t_end - 1);
         // Last element of the chunk's valid rows (at most T of them: the rows
         // left in a long segment times n would overflow 32 bits).
@@ -467,13 +468,9 @@ __global__ __launch_bounds__((SC + kSeqElemWaves + 1) * 64) void scan_seq(const 
         const int q = lane % XLPR;
         vo_x = uint32_t(lane / XLPR) * uint32_t(d_in) * ES + uint32_t(dbase + q * XEPL < d_in ? q * XEPL : 0) * ES;
     }
-    // The LDS block as an LDS-space pointer.  scan_seq declares no static
-    // LDS, so the 16-byte-aligned dynamic block starts at the static size.
-    const lds_ptr lds3 = dynamic_lds_base();
-    const bool lds3_ok = __builtin_amdgcn_groupstaticsize() == 0;
     auto whole_chunk = [&](int k) -> bool {
         const int t0 = t_begin + k * T;
-        return lds3_ok && t0 + T <= t_end && BI * 64 <= (t_end - t0) * n;
+        return t0 + T <= t_end && BI * 64 <= (t_end - t0) * n;
     };
     auto fast_x = [&](const TIn* src, lds_ptr tile, int k) {
         const int64_t row0 = brow + t_begin + int64_t(k) * T;
@@ -490,17 +487,15 @@ __global__ __launch_bounds__((SC + kSeqElemWaves + 1) * 64) void scan_seq(const 
             buffer_load_to_lds<ES>(rs, block + ii * 256, uint32_t(lane * ES), uint32_t(ii * 64 * ES));
     };
     auto dma_chunk = [&](int k, int slot) {        // u, delta, B, C of chunk k into ring slot `slot`
-        char* ru = lds + Lds::off_ru + slot * 2 * Lds::RX;
-        char* rbc = lds + Lds::off_rbc + slot * 2 * Lds::RBC;
+        // (LDS offsets formed here: hoisted, the 3 ring slots' dozen
+        // destination addresses would not fit the scalar registers.)
+        const lds_ptr ru = lds3 + opaque_scalar(Lds::off_ru + slot * 2 * Lds::RX);
+        const lds_ptr rbc = lds3 + opaque_scalar(Lds::off_rbc + slot * 2 * Lds::RBC);
         if (kFastLoads && whole_chunk(k)) {
-            // (LDS offsets formed here: hoisted, the 3 ring slots' dozen
-            // destination addresses would not fit the scalar registers.)
-            const lds_ptr ru3 = lds3 + opaque_scalar(Lds::off_ru + slot * 2 * Lds::RX);
-            const lds_ptr rbc3 = lds3 + opaque_scalar(Lds::off_rbc + slot * 2 * Lds::RBC);
-            fast_x(static_cast<const TIn*>(p.u), ru3, k);
-            fast_x(static_cast<const TIn*>(p.delta), ru3 + Lds::RX, k);
-            fast_bc(static_cast<const TIn*>(p.B), rbc3, k);
-            fast_bc(static_cast<const TIn*>(p.C), rbc3 + Lds::RBC, k);
+            fast_x(static_cast<const TIn*>(p.u), ru, k);
+            fast_x(static_cast<const TIn*>(p.delta), ru + Lds::RX, k);
+            fast_bc(static_cast<const TIn*>(p.B), rbc, k);
+            fast_bc(static_cast<const TIn*>(p.C), rbc + Lds::RBC, k);
         } else {
             dma_x(static_cast<const TIn*>(p.u), ru, k, true);
             dma_x(static_cast<const TIn*>(p.delta), ru + Lds::RX, k, false);
@@ -510,10 +505,9 @@ __global__ __launch_bounds__((SC + kSeqElemWaves + 1) * 64) void scan_seq(const 
     };
     auto dma_z = [&](int k, int slot) {
         if (!GATE) return;
-        if (kFastLoads && whole_chunk(k))
-            fast_x(static_cast<const TIn*>(p.z), lds3 + opaque_scalar(Lds::off_rz + slot * Lds::RX), k);
-        else
-            dma_x(static_cast<const TIn*>(p.z), lds + Lds::off_rz + slot * Lds::RX, k, false);
+        const lds_ptr tile = lds3 + opaque_scalar(Lds::off_rz + slot * Lds::RX);
+        if (kFastLoads && whole_chunk(k)) fast_x(static_cast<const TIn*>(p.z), tile, k);
+        else dma_x(static_cast<const TIn*>(p.z), tile, k, false);
     };
 
     // ---- element waves

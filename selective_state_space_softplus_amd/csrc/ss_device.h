@@ -47,31 +47,17 @@ __device__ __forceinline__ void barrier_lds() {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
-// Direct-to-LDS load: every lane reads BYTES bytes at `src` and the wave's data
-// lands in LDS at `lds_dst` + lane * max(BYTES, 4), without passing through
-// registers.  Completion is tracked by the vector-memory counter.
-template <int BYTES>
-__device__ __forceinline__ void load_to_lds(const void* src, void* lds_dst) {
-    static_assert(BYTES == 2 || BYTES == 4 || BYTES == 16, "direct-to-LDS load size");
-    if constexpr (BYTES == 16) __builtin_amdgcn_global_load_lds(src, lds_dst, 16, 0, 0);
-    else if constexpr (BYTES == 4) __builtin_amdgcn_global_load_lds(src, lds_dst, 4, 0, 0);
-    else __builtin_amdgcn_global_load_lds(src, lds_dst, 2, 0, 0);
-}
-
-// Direct-to-LDS load through a buffer descriptor: every lane reads BYTES bytes
-// at byte offset voff + soff of the descriptor's base and the wave's data
-// lands in LDS at `lds_dst` + lane * max(BYTES, 4).  `soff` is wave-uniform
-// (a scalar register), so a stream of such loads whose per-lane offsets are
-// fixed costs no vector instruction.  Lanes whose voff is at or beyond the
-// descriptor's byte count read zeros instead of memory.
+// An LDS-space pointer (the direct-to-LDS loads take their destination so).
 using lds_ptr = __attribute__((address_space(3))) char*;
 
-// LDS-space pointer to the start of a kernel's dynamic LDS (extern
-// __shared__), which begins where the static allocation ends; a kernel that
-// declares no static LDS gets 0.  Formed from the LDS address itself: a cast
-// of the generic pointer would add a null check of it.
+// LDS-space pointer to the start of a kernel's dynamic LDS (extern __shared__
+// __align__(16)), which begins at the end of the static allocation rounded up
+// to that alignment; the kernels here declare no static LDS, so it is 0.
+// Formed from the LDS address itself: converting a generic pointer to LDS
+// space adds a null check of it (which the compiler has also been seen to
+// emit as an invalid instruction).
 __device__ __forceinline__ lds_ptr dynamic_lds_base() {
-    return (lds_ptr)(uintptr_t)__builtin_amdgcn_groupstaticsize();
+    return (lds_ptr)(uintptr_t)((__builtin_amdgcn_groupstaticsize() + 15u) & ~15u);
 }
 
 // `v` unchanged, but opaque to the optimiser: a constant passed through here
@@ -82,6 +68,23 @@ __device__ __forceinline__ uint32_t opaque_scalar(uint32_t v) {
     return v;
 }
 
+// Direct-to-LDS load: every lane reads BYTES bytes at `src` and the wave's data
+// lands in LDS at `lds_dst` + lane * max(BYTES, 4), without passing through
+// registers.  Completion is tracked by the vector-memory counter.
+template <int BYTES>
+__device__ __forceinline__ void load_to_lds(const void* src, lds_ptr lds_dst) {
+    static_assert(BYTES == 2 || BYTES == 4 || BYTES == 16, "direct-to-LDS load size");
+    auto* dst = (__attribute__((address_space(3))) void*)lds_dst;
+    if constexpr (BYTES == 16) __builtin_amdgcn_global_load_lds(src, dst, 16, 0, 0);
+    else if constexpr (BYTES == 4) __builtin_amdgcn_global_load_lds(src, dst, 4, 0, 0);
+    else __builtin_amdgcn_global_load_lds(src, dst, 2, 0, 0);
+}
+
+// The same through a buffer descriptor: every lane reads BYTES bytes at byte
+// offset voff + soff of the descriptor's base.  `soff` is wave-uniform (a
+// scalar register), so a stream of such loads whose per-lane offsets are
+// fixed costs no vector instruction.  Lanes whose voff is at or beyond the
+// descriptor's byte count read zeros instead of memory.
 template <int BYTES>
 __device__ __forceinline__ void buffer_load_to_lds(__amdgpu_buffer_rsrc_t rsrc, lds_ptr lds_dst, uint32_t voff,
                                                    uint32_t soff) {

@@ -135,7 +135,7 @@ float shfl_xor(float v, int mask, int width);
 #define __builtin_amdgcn_logf(x) ::log2f(x)
 #define __builtin_amdgcn_rcpf(x) (1.0f / (x))
 #define __builtin_amdgcn_groupstaticsize() 0u
-#define __builtin_amdgcn_global_load_lds(src, dst, bytes, off, aux) emu::global_load_lds((src), (dst), (bytes))
+#define __builtin_amdgcn_global_load_lds(src, dst, bytes, off, aux) emu::global_load_lds((src), emu::lds_base() + (uintptr_t)(dst), (bytes))
 #define __builtin_amdgcn_make_buffer_rsrc(p, stride, bytes, flags) \
     emu_rsrc{static_cast<const unsigned char*>(static_cast<const void*>(p)), uint32_t(bytes)}
 #define __builtin_amdgcn_raw_ptr_buffer_load_lds(r, dst, bytes, voff, soff, off, aux) \
