@@ -21,15 +21,20 @@ import numpy as np
 _HERE = os.path.dirname(os.path.abspath(__file__))
 SOURCE = os.path.join(_HERE, "ss_oracle.c")
 LIBRARY = os.path.join(_HERE, "libss_oracle.so")
+# The same source with OpenMP over the independent (batch, channel) loops of
+# the scan and the step: bit-identical results, all host cores.
+LIBRARY_OMP = os.path.join(_HERE, "libss_oracle_omp.so")
 CFLAGS = ["-O2", "-std=c99", "-fPIC", "-shared", "-fno-fast-math"]
 
 _lib = None
+_lib_omp = None
 
 
 def build(source: str = SOURCE, output: str = LIBRARY) -> str:
-    """Compile the oracle with gcc (no HIP, no fast-math).  Returns the path."""
-    cmd = ["gcc", *CFLAGS, "-o", output, source, "-lm"]
-    subprocess.run(cmd, check=True)
+    """Compile the oracle with gcc (no HIP, no fast-math), serially and with OpenMP.  Returns the serial path."""
+    subprocess.run(["gcc", *CFLAGS, "-o", output, source, "-lm"], check=True)
+    omp = os.path.join(os.path.dirname(output), os.path.basename(LIBRARY_OMP)) if output != LIBRARY else LIBRARY_OMP
+    subprocess.run(["gcc", *CFLAGS, "-fopenmp", "-o", omp, source, "-lm"], check=True)
     return output
 
 
@@ -45,6 +50,21 @@ def load(path: str | None = None) -> ctypes.CDLL:
     return _lib
 
 
+def load_parallel() -> ctypes.CDLL:
+    """The OpenMP build (OMP_NUM_THREADS threads; ``threads(lib)`` says how many)."""
+    global _lib_omp
+    if _lib_omp is None:
+        if not os.path.exists(LIBRARY_OMP):
+            build()
+        _lib_omp = _bind(ctypes.CDLL(LIBRARY_OMP))
+    return _lib_omp
+
+
+def threads(lib=None) -> int:
+    """Threads the (batch, channel) loops of ``lib`` use (1 for the serial build)."""
+    return int((lib or load()).ss_oracle_threads())
+
+
 def _bind(lib: ctypes.CDLL) -> ctypes.CDLL:
     P = ctypes.c_void_p
     I64 = ctypes.c_int64
@@ -52,6 +72,8 @@ def _bind(lib: ctypes.CDLL) -> ctypes.CDLL:
     lib.ss_oracle_softplus.argtypes = [ctypes.c_double]
     lib.ss_oracle_silu.restype = ctypes.c_double
     lib.ss_oracle_silu.argtypes = [ctypes.c_double]
+    lib.ss_oracle_threads.restype = ctypes.c_int
+    lib.ss_oracle_threads.argtypes = []
     lib.ss_oracle_scan.restype = ctypes.c_int
     lib.ss_oracle_scan.argtypes = [P] * 8 + [ctypes.c_int, P, P, I64, I64, I64, I64]
     lib.ss_oracle_state_update.restype = ctypes.c_int

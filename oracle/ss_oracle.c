@@ -45,6 +45,13 @@
  * sequence, and the four outputs are added back at the positions they came
  * from.
  *
+ * The scan and the step also build as a second library with OpenMP (the
+ * baseline timed on all host cores): the only difference is the pragma
+ * that hands the independent (batch, channel) recurrences to threads; each
+ * recurrence runs exactly the same arithmetic in the same order, so both
+ * builds give the same results bit for bit.  Without -fopenmp the pragmas
+ * are ignored.
+ *
  * Layouts (row-major, last index fastest):
  *   u, delta, z, y : (b, L, d_in)      B, C : (b, L, n)
  *   A_log          : (d_in, n)         D, delta_bias : (d_in)
@@ -58,6 +65,19 @@
 #include <stddef.h>
 #include <stdint.h>
 #include <stdlib.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+/* Threads the (batch, channel) loops may use: 1 unless built with OpenMP. */
+int ss_oracle_threads(void)
+{
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
 
 /* softplus(x) = log(1 + e^x), evaluated without overflow or cancellation:
  * for x > 0 it is x + log(1 + e^-x).  (mhpn.cn page, section 7: softplus
@@ -111,6 +131,7 @@ int ss_oracle_scan_ex(const double *u, const double *delta, const double *A_log,
     if (b <= 0 || L <= 0 || d_in <= 0 || n <= 0)
         return -2;
 
+    #pragma omp parallel for collapse(2) schedule(dynamic, 16)
     for (int64_t bi = 0; bi < b; bi++) {
         for (int64_t d = 0; d < d_in; d++) {
             /* h starts at zero (section 4 of the mhpn.cn page), or at the
@@ -170,6 +191,7 @@ int ss_oracle_state_update_ex(double *state, const double *x, const double *dt,
     if (b <= 0 || d_in <= 0 || n <= 0)
         return -2;
 
+    #pragma omp parallel for collapse(2) schedule(static)
     for (int64_t bi = 0; bi < b; bi++) {
         for (int64_t d = 0; d < d_in; d++) {
             int64_t e = bi * d_in + d;

@@ -107,16 +107,22 @@ def test_bwd_mid_workload_full(ss):
     print(f"{cfg.name} bwd errors: " + ", ".join(f"{k} {v:.3g}" for k, v in errs.items()))
 
 
+def long_channels(d_in):
+    """One channel in every 64-channel group (a different lane in each) and the last: every (channel group,
+    L segment, batch row) piece of the backward kernel is covered, since each channel spans them all."""
+    return sorted({g * 64 + (g * 37) % 64 for g in range(d_in // 64)} | {d_in - 1})
+
+
 def test_bwd_long_workload_sampled(ss):
-    """scan-long (b=4, L=8192, d_in=5120, n=16, bf16): per-channel gradients on sampled channels, and
-    dA_log, dD, dbias of those channels (sums over the batch rows) -- everything but dB, dC, which sum
-    over all channels and are compared in full at the mid size."""
+    """scan-long (b=4, L=8192, d_in=5120, n=16, bf16): per-channel gradients on one channel of every channel
+    group, and dA_log, dD, dbias of those channels (sums over the batch rows) -- everything but dB, dC, which
+    sum over all channels and are compared in full at the mid size."""
     cfg = workloads.CONFIGS[2]
     say(f"bwd at {cfg.name} size, sampled channels")
     inp = workloads.scan_inputs(2)
     dy, _, _ = extras(cfg.b, cfg.L, cfg.d_in, cfg.n, cfg.dtype, seed=78, h0=False, dlast=False)
     got = grads_gpu(ss, to_dev(inp), dy.to(DEV))
-    for d in (0, 63, 64, 2600, cfg.d_in - 1):
+    for d in long_channels(cfg.d_in):
         sl = lambda t: t[:, :, d:d + 1].contiguous()  # noqa: E731
         ref = oracle.scan_bwd(sl(inp["u"]), sl(inp["delta"]), inp["A_log"][d:d + 1], inp["B"], inp["C"],
                               inp["D"][d:d + 1], sl(inp["z"]), inp["delta_bias"][d:d + 1], True, None, sl(dy), None)
@@ -208,13 +214,13 @@ def test_bwd_zoh_mid_workload_full(ss):
 
 
 def test_bwd_zoh_long_workload_sampled(ss):
-    """scan-long with the zero-order hold: per-channel gradients on sampled channels (as for Euler)."""
+    """scan-long with the zero-order hold: per-channel gradients on one channel of every group (as for Euler)."""
     cfg = workloads.CONFIGS[2]
     say(f"bwd zoh at {cfg.name} size, sampled channels")
     inp = workloads.scan_inputs(2)
     dy, _, _ = extras(cfg.b, cfg.L, cfg.d_in, cfg.n, cfg.dtype, seed=82, h0=False, dlast=False)
     got = grads_gpu(ss, to_dev(inp), dy.to(DEV), zoh=True)
-    for d in (0, 65, 3000, cfg.d_in - 1):
+    for d in long_channels(cfg.d_in):
         sl = lambda t: t[:, :, d:d + 1].contiguous()  # noqa: E731
         ref = oracle.scan_bwd(sl(inp["u"]), sl(inp["delta"]), inp["A_log"][d:d + 1], inp["B"], inp["C"],
                               inp["D"][d:d + 1], sl(inp["z"]), inp["delta_bias"][d:d + 1], True, None, sl(dy), None,

@@ -167,3 +167,34 @@ def test_planted_mistake_is_caught(mutant, tmp_path):
     else:
         failed = failing_pins(oracle.load(so))
     assert failed, f"planted mistake '{desc}' passed every pin"
+
+
+def test_openmp_build_is_bit_identical():
+    """The OpenMP build of the oracle (the all-cores baseline and the full-size parity reference) only hands
+    the independent (batch, channel) recurrences to threads: every output equals the serial build's exactly."""
+    import numpy as np
+    import torch
+
+    import workloads
+
+    ser, par = oracle.load(), oracle.load_parallel()
+    for i, (b, L, d, n, dt, zoh, h0, sp) in enumerate([(3, 97, 70, 16, torch.bfloat16, False, False, True),
+                                                       (2, 50, 33, 5, torch.float32, True, True, True),
+                                                       (4, 20, 130, 1, torch.float32, False, True, False)]):
+        inp = workloads.random_scan_inputs(b, L, d, n, dt, seed=300 + i, gated=i != 2, bias=True)
+        if not sp:
+            inp["delta"] = inp["delta"].float().abs().to(dt)
+            inp["delta_bias"] = inp["delta_bias"].abs()
+        hh = torch.randn(b, d, n, generator=torch.Generator().manual_seed(i)) if h0 else None
+        args = (inp["u"], inp["delta"], inp["A_log"], inp["B"], inp["C"], inp["D"], inp["z"], inp["delta_bias"], sp)
+        y1, l1 = oracle.scan(*args, lib=ser, h0=hh, zoh=zoh)
+        y2, l2 = oracle.scan(*args, lib=par, h0=hh, zoh=zoh)
+        assert np.array_equal(y1, y2) and np.array_equal(l1, l2), f"scan case {i}"
+    dec = workloads.decode_inputs(4, steps=1, b=6)
+    st = dec["state"][:, :300].contiguous()
+    step = (dec["x"][0][:, :300], dec["dt"][0][:, :300], dec["A_log"][:300], dec["B"][0], dec["C"][0],
+            dec["D"][:300], dec["z"][0][:, :300], dec["dt_bias"][:300], True)
+    s1, y1 = oracle.state_update(st, *step, lib=ser)
+    s2, y2 = oracle.state_update(st, *step, lib=par)
+    assert np.array_equal(s1, s2) and np.array_equal(y1, y2)
+    assert oracle.threads(ser) == 1
