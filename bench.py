@@ -9,7 +9,8 @@ algorithmic HBM bandwidth in GB/s; state updates/s and the fraction of the
 8 TB/s HBM peak are reported beside it.  The decode step (b=256, d_in=5120,
 n=16, 64 back-to-back single-token steps) and the convolution step that
 precedes it in a decode step (same b and d_in, width 4, bf16) are timed in the
-same run.
+same run, and so are the other scan workloads (scan-tiny, scan-mid after a
+write that evicts the last-level cache, scan-vmamba as a plain scan).
 
 Algorithmic bytes are what the fused method must move (the (b, L, d_in, n)
 intermediates are never stored):
@@ -125,6 +126,76 @@ def time_scan(ss, torch, g, steps, warmup, last, prewarm_s=0.3):
     wall = time.perf_counter() - wall0
     per = [e0.elapsed_time(e1) for e0, e1 in ev]
     return t_all0.elapsed_time(t_all1) / steps, sum(per) / len(per), wall
+
+
+def other_workloads(ss, torch, workloads, dev, reps=20):
+    """The other scan workloads, each timed with HIP events on the launch stream (median of `reps`):
+    scan-tiny (launch-bound: 200 back-to-back calls), scan-mid (its 203 MB fit the 256 MB last-level
+    cache, so each timed call follows a 512 MB write that evicts it; back-to-back calls reported beside),
+    scan-vmamba as a plain scan of the four unrolled directions (b=64, n=1, fp32, ungated)."""
+    import statistics
+
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    out = {}
+    for idx in (0, 1, 3):
+        cfg = workloads.CONFIGS[idx]
+        inp = workloads.scan_inputs(idx)
+        g = {k: (v.to(dev) if isinstance(v, torch.Tensor) else v) for k, v in inp.items()}
+        s = 2 if cfg.dtype == torch.bfloat16 else 4
+        gated, bias = g["z"] is not None, g["delta_bias"] is not None
+        nbytes = scan_bytes(cfg.b, cfg.L, cfg.d_in, cfg.n, s, gated, bias, True)
+        y = torch.empty_like(g["u"])
+        last = torch.empty((cfg.b, cfg.d_in, cfg.n), dtype=torch.float32, device=dev)
+
+        def call():
+            ss.scan_fwd(g["u"], g["delta"], g["A_log"], g["B"], g["C"], g["D"], g["z"], g["delta_bias"], True,
+                        out=y, last_state=last, return_last_state=True)
+
+        for _ in range(20):
+            call()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        row = {"workload": f"{cfg.name}: b={cfg.b} L={cfg.L} d_in={cfg.d_in} n={cfg.n}, "
+                           f"{'bf16' if s == 2 else 'fp32'}{', gated' if gated else ''}"
+                           f"{', delta bias' if bias else ''}, softplus, last state written",
+               "algorithmic_bytes": nbytes}
+        if idx == 0:
+            k = 200
+            e0.record()
+            for _ in range(k):
+                call()
+            e1.record()
+            torch.cuda.synchronize()
+            us = e0.elapsed_time(e1) * 1e3 / k
+            row["note"] = f"{k} back-to-back calls: launch-bound"
+        else:
+            per = []
+            for _ in range(reps):
+                if idx == 1:
+                    flush.zero_()
+                e0.record()
+                call()
+                e1.record()
+                torch.cuda.synchronize()
+                per.append(e0.elapsed_time(e1) * 1e3)
+            us = statistics.median(per)
+            if idx == 1:
+                row["note"] = "each call after a 512 MB write that evicts the last-level cache"
+                b2b = []
+                for _ in range(reps):
+                    e0.record()
+                    call()
+                    e1.record()
+                    torch.cuda.synchronize()
+                    b2b.append(e0.elapsed_time(e1) * 1e3)
+                row["us_back_to_back"] = round(statistics.median(b2b), 2)
+        row["us"] = round(us, 2)
+        row["GBps"] = round(nbytes / (us * 1e-6) / 1e9, 1)
+        row["hbm_frac"] = round(nbytes / (us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4)
+        row["updates_per_s"] = float(f"{cfg.updates / (us * 1e-6):.4g}")
+        out[cfg.name] = row
+        del g, y, last
+    return out
 
 
 def copy_probe(torch, dev, nbytes=1 << 30, reps=5):
@@ -257,6 +328,7 @@ def main(argv=None):
     ap.add_argument("--no-decode", action="store_true", help="skip the decode-step measurement")
     ap.add_argument("--no-cross", action="store_true", help="skip the VMamba cross-scan measurement")
     ap.add_argument("--no-bwd", action="store_true", help="skip the backward-pass measurement")
+    ap.add_argument("--no-others", action="store_true", help="skip the scan-tiny, scan-mid and scan-vmamba timings")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target duration of the CPU baseline sample")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy (calibrates the HBM byte counters)")
@@ -328,6 +400,9 @@ def main(argv=None):
         "host_wall_s": round(wall, 3),
         "prewarm_s": args.prewarm,
     }
+
+    if not args.no_others:
+        result["other_workloads"] = other_workloads(ss, torch, workloads, dev)
 
     if not args.no_decode:
         dcfg = workloads.CONFIGS[4]
