@@ -361,13 +361,21 @@ SS_EXPORT int ss_state_update_ex(float* state, const void* x, const void* dt, co
     p.zoh = discretization == SS_DISC_ZOH ? 1 : 0;
     hipStream_t st = static_cast<hipStream_t>(stream);
 
-    const int64_t lpc = n / 4;
-    const bool vec = n % 4 == 0 && (lpc == 1 || lpc == 2 || lpc == 4 || lpc == 8 || lpc == 16) &&
+    // The vector kernel takes n = 4 lpc, forms offsets within one batch row
+    // of the state in 32 bits, and covers lpc rows of 256 / lpc channels per
+    // workgroup.
+    const int64_t lpc = n % 4 == 0 ? n / 4 : 0;
+    const bool lpc_ok = lpc == 1 || lpc == 2 || lpc == 4 || lpc == 8 || lpc == 16;
+    const int64_t tiles = lpc_ok ? (d_in * lpc + 255) / 256 : 0, groups = lpc_ok ? (b + lpc - 1) / lpc : 0;
+    const bool vec = lpc_ok && d_in * n < (int64_t(1) << 31) && tiles * groups < (int64_t(1) << 31) &&
                      aligned(state, 16) && aligned(A_log, 16) && aligned(B, 4 * es) && aligned(C, 4 * es);
     if (vec) {
-        const int64_t threads = nch * lpc;
-        const dim3 grid(unsigned((threads + 255) / 256));
-#define SS_STEP_VEC(T_, LPC_) hipLaunchKernelGGL((ss::state_update_vec<T_, LPC_>), grid, dim3(256), 0, st, p)
+        const dim3 grid(unsigned(tiles * groups));
+#define SS_STEP_VEC(T_, LPC_)                                                            \
+    if (p.zoh)                                                                           \
+        hipLaunchKernelGGL((ss::state_update_vec<T_, LPC_, true>), grid, dim3(256), 0, st, p); \
+    else                                                                                 \
+        hipLaunchKernelGGL((ss::state_update_vec<T_, LPC_, false>), grid, dim3(256), 0, st, p)
         if (dtype == SS_BF16) {
             switch (lpc) {
                 case 1: SS_STEP_VEC(uint16_t, 1); break;

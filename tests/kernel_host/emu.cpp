@@ -264,22 +264,44 @@ u32x2 permlane16_swap(unsigned a, unsigned b) {
     return r;
 }
 
-// DPP row_shr:k (controls 0x111 .. 0x11f): lane l takes lane l - k of its row
-// of 16; lanes with no source take 0 when bound_ctrl is set, else `old`.
+// DPP with the controls the kernels use: quad_perm (0x00 .. 0xff: lane l of
+// a quad reads quad position (ctrl >> 2 (l % 4)) & 3), row_shr:k (0x111 ..
+// 0x11f: lane l takes lane l - k of its row of 16; lanes with no source take 0
+// when bound_ctrl is set, else `old`) and row_ror:k (0x121 .. 0x12f: lane l
+// takes lane (l - k) mod 16 of its row).
 int update_dpp(int old, int src, int ctrl, int row_mask, int bank_mask, bool bound_ctrl) {
-    if (ctrl < 0x111 || ctrl > 0x11f) {
+    const bool quad = ctrl >= 0 && ctrl <= 0xff, shr = ctrl >= 0x111 && ctrl <= 0x11f,
+               ror = ctrl >= 0x121 && ctrl <= 0x12f;
+    if (!quad && !shr && !ror) {
         std::fprintf(stderr, "emu: DPP control 0x%x not emulated\n", ctrl);
         std::abort();
     }
-    const int k = ctrl - 0x110;
     int res = old;
     exchange(uint32_t(src), 0, [&](Wave& w) {
         const int l = tl_lane, row = l / 16, bank = (l % 16) / 4;
         if (!((row_mask >> row) & 1) || !((bank_mask >> bank) & 1)) return;
-        if (l % 16 >= k) res = int(w.xa[l - k]);
-        else if (bound_ctrl) res = 0;
+        if (quad) {
+            res = int(w.xa[(l & ~3) + ((ctrl >> (2 * (l % 4))) & 3)]);
+        } else if (ror) {
+            res = int(w.xa[row * 16 + (l % 16 + 16 - (ctrl - 0x120)) % 16]);
+        } else {
+            const int k = ctrl - 0x110;
+            if (l % 16 >= k) res = int(w.xa[l - k]);
+            else if (bound_ctrl) res = 0;
+        }
     });
     return res;
+}
+
+// Lane (l & ~(width - 1)) + (src % width), as the hardware's ds_bpermute
+// form of __shfl computes it.
+float shfl(float v, int src, int width) {
+    float r = v;
+    exchange(__float_as_uint(v), 0, [&](Wave& w) {
+        const int l = tl_lane;
+        r = __uint_as_float(w.xa[(l & ~(width - 1)) + (src & (width - 1))]);
+    });
+    return r;
 }
 
 float shfl_xor(float v, int mask, int width) {

@@ -123,6 +123,7 @@ u32x2 permlane32_swap(unsigned a, unsigned b);
 u32x2 permlane16_swap(unsigned a, unsigned b);
 int update_dpp(int old, int src, int ctrl, int row_mask, int bank_mask, bool bound_ctrl);
 float shfl_xor(float v, int mask, int width);
+float shfl(float v, int src, int width);
 }  // namespace emu
 
 #define __builtin_amdgcn_readfirstlane(x) (x)
@@ -144,6 +145,7 @@ float shfl_xor(float v, int mask, int width);
 #define __builtin_amdgcn_permlane16_swap(a, b, fi, bc) emu::permlane16_swap((a), (b))
 #define __builtin_amdgcn_update_dpp(old, src, ctrl, rm, bm, bc) emu::update_dpp((old), (src), (ctrl), (rm), (bm), (bc))
 #define __shfl_xor(v, m, w) emu::shfl_xor((v), (m), (w))
+#define __shfl(v, s, w) emu::shfl((v), (s), (w))
 
 #define __HIP_MEMORY_SCOPE_AGENT 0
 #define __HIP_MEMORY_SCOPE_WORKGROUP 0

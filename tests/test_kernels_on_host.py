@@ -103,8 +103,13 @@ def test_backward_on_host(case):
         assert_close(got[k], ref[k], dt, f"host {k}")
 
 
-@pytest.mark.parametrize("b,d,n,dt", [(3, 70, 16, BF16), (2, 33, 5, F32)])
-def test_step_on_host(b, d, n, dt):
+# n = 4 LPC runs the vector kernel (LPC lanes per channel, LPC batch rows per
+# workgroup) for LPC = 1, 2, 4, 8, 16; n = 5 and n = 3 run the any-n kernel.  Batch
+# sizes leave a partial row group and channel counts a partial tile.
+@pytest.mark.parametrize("b,d,n,dt,zoh", [(3, 70, 16, BF16, 0), (5, 70, 4, F32, 0), (3, 130, 8, BF16, 1),
+                                          (9, 40, 32, F32, 0), (17, 20, 64, BF16, 1), (2, 33, 5, F32, 1),
+                                          (4, 9, 3, F32, 0)])
+def test_step_on_host(b, d, n, dt, zoh):
     dec = workloads.decode_inputs(4, steps=1, b=b)
     g = torch.Generator().manual_seed(b + d)
     state = torch.randn(b, d, n, generator=g) * 0.1
@@ -113,9 +118,9 @@ def test_step_on_host(b, d, n, dt):
     A_log = workloads.s4d_real_A_log(d, n)
     D, bias = torch.randn(d, generator=g), dec["dt_bias"][:d].contiguous()
     t = dict(state=state, x=x, dt=dtv, A_log=A_log, B=B, C=C, D=D, z=z, dt_bias=bias)
-    got = hk.run("step", t, dict(b=b, d_in=d, n=n, dtype=_code(dt), softplus=1, zoh=0),
+    got = hk.run("step", t, dict(b=b, d_in=d, n=n, dtype=_code(dt), softplus=1, zoh=zoh),
                  dict(y=((b, d), dt), state=((b, d, n), F32)))
-    sr, yr = oracle.state_update(state, x, dtv, A_log, B, C, D, z, bias, True)
+    sr, yr = oracle.state_update(state, x, dtv, A_log, B, C, D, z, bias, True, zoh=bool(zoh))
     assert_close(got["y"], yr, dt, "host step y")
     assert_close(got["state"], sr, dt, "host step state")
 
