@@ -27,7 +27,7 @@ LIBRARY = os.path.join(PKG, "libss_scan.so")
 SOURCES = [os.path.join(CSRC, "ss_scan.hip")]
 INPUT_TYPES = ("uint16_t", "float")
 SEQ_SHAPES = ((1, 2), (4, 2), (4, 4), (8, 2), (8, 4), (8, 8))   # must cover ss_host::seq_shape
-BWD_SHAPES = ((1, 2), (4, 2), (8, 2), (8, 4), (8, 8))           # must cover ss_host::bwd_shape
+BWD_SHAPES = ((1, 2, False), (4, 2, False), (8, 2, False), (8, 2, True))   # must cover ss_host::bwd_shape
 ARCH = os.environ.get("SS_OFFLOAD_ARCH", "gfx950")
 FLAGS = ["-O3", "-std=c++17", "-fPIC", "-fvisibility=hidden", "-Xclang", "-target-feature", "-Xclang",
          "-packed-fp32-ops"]
@@ -60,13 +60,16 @@ def instantiation_units(objdir: str) -> list[str]:
     units = []
     for ty in INPUT_TYPES:
         for header, fn, shapes, sig in (
-                ("launch_seq.h", "launch_seq", SEQ_SHAPES, "ss::ScanParams, SeqMode, void*, size_t, hipStream_t"),
+                ("launch_seq.h", "launch_seq", [(sc, nsw, None) for sc, nsw in SEQ_SHAPES],
+                 "ss::ScanParams, SeqMode, void*, size_t, hipStream_t"),
                 ("launch_bwd.h", "launch_bwd", BWD_SHAPES, "ss::BwdParams, bool, bool, hipStream_t, int*")):
-            for sc, nsw in shapes:
-                path = os.path.join(objdir, f"{fn}_{ty}_{sc}x{nsw}.hip")
+            for sc, nsw, sl in shapes:
+                targs = f"{ty}, {sc}, {nsw}" + ("" if sl is None else f", {'true' if sl else 'false'}")
+                tag = f"{sc}x{nsw}" + ("" if not sl else "_sliced")
+                path = os.path.join(objdir, f"{fn}_{ty}_{tag}.hip")
                 with open(path, "w") as f:
                     f.write(f'#include "{header}"\nnamespace ss_host {{\n'
-                            f"template int {fn}<{ty}, {sc}, {nsw}>({sig});\n}}\n")
+                            f"template int {fn}<{targs}>({sig});\n}}\n")
                 units.append(path)
     return units
 

@@ -6,22 +6,23 @@
 
 namespace ss_host {
 
-// Launches scan_bwd, cut into segments along L as the forward is (same rule:
-// balance the resident workgroups); p.K and p.Lseg are set here and the
-// number of segments is returned in *segments.
-template <typename TIn, int SC, int NSW>
+// Launches scan_bwd (SL: the form for n taken in several slices of states),
+// cut into segments along L as the forward is (same rule: balance the
+// resident workgroups); p.K and p.Lseg are set here and the number of
+// segments is returned in *segments.
+template <typename TIn, int SC, int NSW, bool SL>
 int launch_bwd(ss::BwdParams p, bool gate, bool zoh, hipStream_t st, int* segments) {
     constexpr int threads = (SC + 4) * 64;
     constexpr int T = ss::kCkptSteps;
     using Kern = void (*)(ss::BwdParams);
     static constexpr Kern kernels[8] = {
-        ss::scan_bwd<TIn, SC, NSW, false, false, false>, ss::scan_bwd<TIn, SC, NSW, false, true, false>,
-        ss::scan_bwd<TIn, SC, NSW, true, false, false>,  ss::scan_bwd<TIn, SC, NSW, true, true, false>,
-        ss::scan_bwd<TIn, SC, NSW, false, false, true>,  ss::scan_bwd<TIn, SC, NSW, false, true, true>,
-        ss::scan_bwd<TIn, SC, NSW, true, false, true>,   ss::scan_bwd<TIn, SC, NSW, true, true, true>};
+        ss::scan_bwd<TIn, SC, NSW, SL, false, false, false>, ss::scan_bwd<TIn, SC, NSW, SL, false, true, false>,
+        ss::scan_bwd<TIn, SC, NSW, SL, true, false, false>,  ss::scan_bwd<TIn, SC, NSW, SL, true, true, false>,
+        ss::scan_bwd<TIn, SC, NSW, SL, false, false, true>,  ss::scan_bwd<TIn, SC, NSW, SL, false, true, true>,
+        ss::scan_bwd<TIn, SC, NSW, SL, true, false, true>,   ss::scan_bwd<TIn, SC, NSW, SL, true, true, true>};
     const Kern kern = kernels[(zoh ? 4 : 0) | (p.softplus ? 2 : 0) | (gate ? 1 : 0)];
     const size_t lds = ss::BwdLds<SC, SC * NSW>::bytes;
-    const int64_t G = p.b * p.nblk_d;
+    const int64_t G = p.b * p.nblk_d * p.slices;
     const int cus = device_cus();
     const int per_cu = resident_per_cu(reinterpret_cast<const void*>(kern), threads, lds);
     int K = choose_segments(G, p.L, T, int64_t(std::max(cus, 0)) * per_cu);

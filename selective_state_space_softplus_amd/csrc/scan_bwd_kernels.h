@@ -19,7 +19,8 @@
 // dDelta_t gains a_tk where Euler has 1 in its input term, dB = g beta u, and
 // dA_k gains g_tk B_tk u_t (Delta_t a_tk - beta_tk)/A_k.
 //
-// scan_bwd<TIn, SC, NSW, SP, GATE, ZOH>: one workgroup per (b, 64-channel group,
+// scan_bwd<TIn, SC, NSW, SL, SP, GATE, ZOH>: one workgroup per (slice of NP =
+// SC NSW states (SL: n is taken in several slices), b, 64-channel group,
 // segment of L) walks its segment backwards in chunks of kCkptSteps = 8
 // steps; segments are taken last first, each starting from the adjoint the
 // later one handed on (as the forward hands on states), which balances the
@@ -67,38 +68,34 @@ struct BwdParams {
     float* part_C;            // (nblk_d, b, L, n)
     float* part_A;            // (K, b, d_in, n) dA_log per segment and batch row
     float* part_D;            // (K, b, d_in)
-    float* part_bias;         // (K, b, d_in)
+    float* part_bias;         // (K, slices, b, d_in)
+    float* part_du;           // (slices, b, L, d_in) when slices > 1, else null
+    float* part_dd;           // (slices, b, L, d_in) when slices > 1, else null
     int64_t b, L, d_in, n;
     int nck, nblk_d, softplus;
+    // The states are taken in slices of SC NSW (the kernel's NP) by separate
+    // workgroups; with more than one slice, du and ddelta are sums of the
+    // slices' parts (part_du, part_dd), which reduce_groups adds.
+    int slices;
     // L segments: pieces taken in ticket order, last segment first; a piece
     // starts from the adjoint its successor segment handed on.
     int K;
     int64_t Lseg;             // steps per segment, a multiple of kCkptSteps
     uint32_t* ctl;            // [0] ticket counter, [kFlagOffset + s G + g] flags
-    float* handoff;           // (K - 1, G, n, 64) adjoints handed between segments
+    float* handoff;           // (K - 1, G slices, NP, 64) adjoints handed between segments
     uint32_t* err;            // status words of the call (as ScanParams::err; cleared by the forward pass)
     int spin_limit;           // polls before a segment wait gives up
     int wait_never;           // nonzero: waits poll err[1] (never set) and give up after spin_limit polls
 };
 
-// v moved from another lane of the same row by a DPP control (row_shr);
-// lanes the control leaves out, or whose row is not in ROW_MASK, read 0.
-template <int CTRL, int ROW_MASK>
-__device__ __forceinline__ float dpp_take(float v) {
-    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, ROW_MASK, 0xf, true));
-}
-
-// Sums over the 64 lanes of the wave of four values at once (a transposing
-// butterfly; every lane of the wave must be active):
+// Partial sums over the 64 lanes of the wave of four values at once (the
+// first two steps of a transposing butterfly; every lane of the wave must be
+// active):
 //   1. v_permlane32_swap pairs the lower halves of (v0, v1) and of (v2, v3):
 //      a = [v0_lo + v0_hi | v1_lo + v1_hi], b likewise for v2, v3;
-//   2. v_permlane16_swap pairs odd rows of a with even rows of b: t holds in
-//      its rows 0, 1, 2, 3 partial sums (over 4 lanes) of v0, v2, v1, v3;
-//   3. prefix sums inside each row of 16 lanes (DPP row_shr 1, 2, 4, 8).
-// Lanes 15, 31, 47, 63 then hold the sums of v0, v2, v1, v3 -- 10 VALU
-// instructions instead of 24 for four separate six-step reductions.
-// Steps 1 and 2 alone: rows 0, 1, 2, 3 of the result hold 16 partial sums
-// (over 4 lanes each) of v0, v2, v1, v3.
+//   2. v_permlane16_swap pairs odd rows of a with even rows of b.
+// Rows 0, 1, 2, 3 of the result then hold 16 partial sums (over 4 lanes
+// each) of v0, v2, v1, v3: 6 VALU instructions for the four values.
 __device__ __forceinline__ float wave_part4(float v0, float v1, float v2, float v3) {
     const auto x = __builtin_amdgcn_permlane32_swap(__float_as_uint(v0), __float_as_uint(v1), false, false);
     const auto y = __builtin_amdgcn_permlane32_swap(__float_as_uint(v2), __float_as_uint(v3), false, false);
@@ -108,31 +105,21 @@ __device__ __forceinline__ float wave_part4(float v0, float v1, float v2, float 
     return __uint_as_float(z[0]) + __uint_as_float(z[1]);
 }
 
-__device__ __forceinline__ float wave_sum4(float v0, float v1, float v2, float v3) {
-    float t = wave_part4(v0, v1, v2, v3);
-    t += dpp_take<0x111, 0xf>(t);
-    t += dpp_take<0x112, 0xf>(t);
-    t += dpp_take<0x114, 0xf>(t);
-    t += dpp_take<0x118, 0xf>(t);
-    return t;
-}
-
 // LDS of scan_bwd<SC recurrence waves, NP padded states>, T = 8 steps.
-// RL (NP <= 16): the recurrence waves leave the dB, dC sums over the 64
-// channels at 16 partials per (step, state) -- a row of 16 floats -- and the
-// element waves add them up; above, the sums are finished in the wave (the
-// rows would not fit).
+// The recurrence waves leave the dB, dC sums over the 64 channels at 16
+// partials per (step, state) -- a row of 16 floats -- and the element waves
+// add them up.
 template <int SC, int NP>
 struct BwdLds {
     static constexpr int T = kCkptSteps;
-    static constexpr bool RL = NP <= 16;
+    static_assert(NP <= 16, "states per workgroup (larger n is taken in slices)");
     static constexpr int RS = 18;                             // mean floats per row: pairs of rows padded by 4
     static constexpr int ROWS = T * 2 * NP;                   // (step, state, B or C) rows of a chunk
     static constexpr int PREP = T * 64 * 16;                  // (Delta, w, dy', u) per (step, channel)
     static constexpr int PART = SC * T * 64 * 8;              // (S1, S2) per (wave, step, channel)
     static constexpr int CK = NP * 64 * 4;                    // state entering the chunk
     static constexpr int BC = T * 2 * NP * 4;                 // B, C rows as fp32, grouped per wave
-    static constexpr int DBC = RL ? ROWS * RS * 4 : T * 2 * NP * 4;   // dB, dC partial rows, or sums, of the chunk
+    static constexpr int DBC = ROWS * RS * 4;                 // dB, dC partial rows of the chunk
     // Row g of the partial rows starts at float g 16 + (g / 2) 4: a recurrence
     // wave's four rows are two contiguous 32-float runs (bank-conflict-free
     // writes), and 8 consecutive rows start on 8 different 4-bank groups
@@ -147,7 +134,7 @@ struct BwdLds {
     static constexpr int bytes = off_ticket + 16;
 };
 
-template <typename TIn, int SC, int NSW, bool SP, bool GATE, bool ZOH>
+template <typename TIn, int SC, int NSW, bool SL, bool SP, bool GATE, bool ZOH>
 __global__ __launch_bounds__((SC + 4) * 64) void scan_bwd(const BwdParams p) {
     constexpr int T = kCkptSteps;
     constexpr int NE = 4 * 64;                     // element threads
@@ -167,7 +154,6 @@ __global__ __launch_bounds__((SC + 4) * 64) void scan_bwd(const BwdParams p) {
     float* s_ck = reinterpret_cast<float*>(lds + Lds::off_ck);         // [2][NP][64]
     float* s_bc = reinterpret_cast<float*>(lds + Lds::off_bc);         // [2][T][SC][2][NSW]
     float* s_dbc = reinterpret_cast<float*>(lds + Lds::off_dbc);       // [2][T][2][NP], or [2][ROWS][RS] rows
-    constexpr bool RL = Lds::RL;
     constexpr int RS = Lds::RS, ROWS = Lds::ROWS;
     static_assert(Lds::row_off(4) == 4 * RS && ROWS % 4 == 0, "groups of 4 partial rows at 4 RS floats");
     constexpr int RPT = (ROWS + NE - 1) / NE;      // partial rows each element thread adds up per chunk
@@ -177,7 +163,7 @@ __global__ __launch_bounds__((SC + 4) * 64) void scan_bwd(const BwdParams p) {
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const bool rec = wave < SC;
     const int L = int(p.L), d_in = int(p.d_in), n = int(p.n);
-    const int G = int(p.b) * p.nblk_d;
+    const int G = int(p.b) * p.nblk_d * p.slices;   // (slice, batch row, channel group) triples
     int& s_ticket = *reinterpret_cast<int*>(lds + Lds::off_ticket);
     int ticket;
     if (p.K == 1) {
@@ -193,8 +179,12 @@ __global__ __launch_bounds__((SC + 4) * 64) void scan_bwd(const BwdParams p) {
         gi -= G;
         seg--;
     }
-    const int bi = __builtin_amdgcn_readfirstlane(gi / p.nblk_d);
-    const int grp = __builtin_amdgcn_readfirstlane(gi - bi * p.nblk_d);
+    const int slice = SL ? __builtin_amdgcn_readfirstlane(gi / (int(p.b) * p.nblk_d)) : 0;
+    const int gb = gi - slice * int(p.b) * p.nblk_d;
+    const int bi = __builtin_amdgcn_readfirstlane(gb / p.nblk_d);
+    const int grp = __builtin_amdgcn_readfirstlane(gb - bi * p.nblk_d);
+    const int k0 = slice * NP;                     // first state of the slice
+    const int ns = min(NP, n - k0);                // states of the slice
     const int dbase = grp * 64;
     const int t_begin = seg * int(p.Lseg);
     const int t_end = min(L, t_begin + int(p.Lseg));
@@ -209,11 +199,12 @@ __global__ __launch_bounds__((SC + 4) * 64) void scan_bwd(const BwdParams p) {
     float A2[NSW], An[NSW], g[NSW], dA[NSW], invA[NSW];
 #pragma unroll
     for (int q = 0; q < NSW; q++) {
-        const bool ok = rec && dv && n0 + q < n;
-        A2[q] = ok ? a2_from_alog(p.A_log[int64_t(d) * n + n0 + q]) : 0.0f;
+        const bool ok = rec && dv && n0 + q < ns;
+        const int64_t kq = int64_t(d) * n + k0 + n0 + q;             // (d, state) in A_log
+        A2[q] = ok ? a2_from_alog(p.A_log[kq]) : 0.0f;
         An[q] = A2[q] * kLn2;                                          // A itself
-        invA[q] = (ZOH && ok) ? inv_a_from_alog(p.A_log[int64_t(d) * n + n0 + q]) : 0.0f;
-        g[q] = (ok && p.dlast && seg == p.K - 1) ? p.dlast[(int64_t(bi) * d_in + d) * n + n0 + q] : 0.0f;
+        invA[q] = (ZOH && ok) ? inv_a_from_alog(p.A_log[kq]) : 0.0f;
+        g[q] = (ok && p.dlast && seg == p.K - 1) ? p.dlast[int64_t(bi) * d_in * n + kq] : 0.0f;
         dA[q] = 0.0f;
     }
     if (seg < p.K - 1) {
@@ -228,10 +219,10 @@ __global__ __launch_bounds__((SC + 4) * 64) void scan_bwd(const BwdParams p) {
         __syncthreads();
         const bool timed_out = __builtin_amdgcn_readfirstlane(s_timeout) != 0;
         if (rec) {
-            const uint32_t* src = reinterpret_cast<const uint32_t*>(p.handoff) + (int64_t(seg) * G + gi) * n * 64;
+            const uint32_t* src = reinterpret_cast<const uint32_t*>(p.handoff) + (int64_t(seg) * G + gi) * NP * 64;
 #pragma unroll
             for (int q = 0; q < NSW; q++)
-                if (n0 + q < n)
+                if (n0 + q < ns)
                     g[q] = timed_out ? __builtin_nanf("")
                                      : __uint_as_float(__hip_atomic_load(src + (n0 + q) * 64 + lane,
                                                                          __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
@@ -249,7 +240,7 @@ __global__ __launch_bounds__((SC + 4) * 64) void scan_bwd(const BwdParams p) {
     float Dv[V], bias_v[V], accD[V], accBias[V];
 #pragma unroll
     for (int i = 0; i < V; i++) {
-        Dv[i] = evok[i] ? p.D[dbase + ec + i * TPR] : 0.0f;
+        Dv[i] = evok[i] && slice == 0 ? p.D[dbase + ec + i * TPR] : 0.0f;   // the D term once
         bias_v[i] = (evok[i] && p.bias) ? p.bias[dbase + ec + i * TPR] : 0.0f;
         accD[i] = accBias[i] = 0.0f;
     }
@@ -287,9 +278,9 @@ __global__ __launch_bounds__((SC + 4) * 64) void scan_bwd(const BwdParams p) {
     for (int m = 0; m < EBC; m++) {
         const int f = m * NE + etid;
         const int j = f / NP, kk = f - (f / NP) * NP;
-        const bool ok = !rec && f < T * NP && kk < n;
+        const bool ok = !rec && f < T * NP && kk < ns;
         bc_row[m] = ok ? j : -1;
-        off_bc[m] = ok ? uint32_t((j * n + kk) * ES) : 0u;
+        off_bc[m] = ok ? uint32_t((j * n + k0 + kk) * ES) : 0u;
     }
     uint32_t off_ck[ECK], off_h0[ECK];             // (kk, dd) in a checkpoint and in h0
     bool ck_has[ECK];
@@ -297,23 +288,11 @@ __global__ __launch_bounds__((SC + 4) * 64) void scan_bwd(const BwdParams p) {
     for (int m = 0; m < ECK; m++) {
         const int f = m * NE + etid;
         const int kk = f / 64, dd = dbase + (f & 63);
-        ck_has[m] = !rec && f < NP * 64 && kk < n && dd < d_in;
-        off_ck[m] = ck_has[m] ? uint32_t(kk * d_in + dd) * 4u : 0u;
-        off_h0[m] = ck_has[m] ? uint32_t(dd * n + kk) * 4u : 0u;
+        ck_has[m] = !rec && f < NP * 64 && kk < ns && dd < d_in;
+        off_ck[m] = ck_has[m] ? uint32_t((k0 + kk) * d_in + dd) * 4u : 0u;
+        off_h0[m] = ck_has[m] ? uint32_t(dd * n + k0 + kk) * 4u : 0u;
     }
-    // dB, dC words of a chunk written by this element thread (without the
-    // partial rows): word f = m NE + etid < T n is (step f / n, state f % n).
-    constexpr int PFN = (T * NP + NE - 1) / NE;
-    int pf_j[PFN], pf_kk[PFN];
-    bool pf_has[PFN];
-#pragma unroll
-    for (int m = 0; m < PFN; m++) {
-        const int f = m * NE + etid;
-        pf_j[m] = f / max(n, 1);
-        pf_kk[m] = f - pf_j[m] * max(n, 1);
-        pf_has[m] = !rec && f < T * n;
-    }
-    // RL: partial row g = ((j SC + w) NSW/2 + pair) 4 + r of a chunk holds,
+    // Partial row g = ((j SC + w) NSW/2 + pair) 4 + r of a chunk holds,
     // for r = 0, 1, 2, 3, dB of state 2 pair, its dC, dB of the next state,
     // its dC (the row order of wave_part4); element thread etid adds rows
     // etid, etid + NE, ...
@@ -324,10 +303,10 @@ __global__ __launch_bounds__((SC + 4) * 64) void scan_bwd(const BwdParams p) {
         const int g = m * NE + etid;
         const int r = g & 3, pq = (g >> 2) % (NSW / 2), w = (g / (2 * NSW)) % SC, j = g / (2 * NP);
         const int kk = w * NSW + pq * 2 + (r >> 1);
-        red_ok[m] = RL && !rec && g < ROWS && kk < n;
+        red_ok[m] = !rec && g < ROWS && kk < ns;
         red_c[m] = (r & 1) != 0;
         red_j[m] = j;
-        red_off[m] = j * n + kk;
+        red_off[m] = j * n + k0 + kk;
     }
     // Recurrence lane's place in a group of 4 partial rows: row lane / 16, column lane % 16.
     const int red_lane = lane + (lane >> 5) * 4;
@@ -433,19 +412,26 @@ __global__ __launch_bounds__((SC + 4) * 64) void scan_bwd(const BwdParams p) {
             const float ddl = SP ? dDelta * rcp_hw(1.0f + exp2_hw(-kp.x[i] * kLog2e)) : dDelta;
             const float du = ZOH ? fmaf(pr.z, Dv[i], S1) : fmaf(pr.x, S1, pr.z * Dv[i]);
             if (rv && evok[i]) {
-                auto st = [&](void* base, float v) __attribute__((always_inline)) {
-                    TIn* q = static_cast<TIn*>(base) + rb;
-                    Elem<TIn>::store(reinterpret_cast<TIn*>(reinterpret_cast<char*>(q) + off_row[i]), 0, v);
-                };
-                st(p.du, du);
-                st(p.ddelta, ddl);
-                accD[i] = fmaf(pr.z, pr.w, accD[i]);
+                if constexpr (!SL) {
+                    auto st = [&](void* base, float v) __attribute__((always_inline)) {
+                        TIn* q = static_cast<TIn*>(base) + rb;
+                        Elem<TIn>::store(reinterpret_cast<TIn*>(reinterpret_cast<char*>(q) + off_row[i]), 0, v);
+                    };
+                    st(p.du, du);
+                    st(p.ddelta, ddl);
+                } else {
+                    // This slice's parts of du and ddelta (both are linear in S1, S2).
+                    const int64_t e = int64_t(slice) * p.b * L * d_in + rb + off_row[i] / uint32_t(ES);
+                    p.part_du[e] = du;
+                    p.part_dd[e] = ddl;
+                }
+                if (slice == 0) accD[i] = fmaf(pr.z, pr.w, accD[i]);
                 accBias[i] += ddl;
             }
         }
         // dB, dC of the chunk's rows: T * n consecutive values of each.
         const int64_t ob = ((int64_t(grp) * p.b + bi) * L + int64_t(k) * T) * n;
-        if constexpr (RL) {
+        {
 #pragma unroll
             for (int m = 0; m < RPT; m++) {
                 if (!red_ok[m] || k * T + red_j[m] >= L) continue;
@@ -458,36 +444,20 @@ __global__ __launch_bounds__((SC + 4) * 64) void scan_bwd(const BwdParams p) {
                 sum += e.x; sum += e.y; sum += e.z; sum += e.w;
                 (red_c[m] ? p.part_C : p.part_B)[ob + red_off[m]] = sum;
             }
-        } else {
-#pragma unroll
-            for (int m = 0; m < PFN; m++) {
-                if (!pf_has[m] || k * T + pf_j[m] >= L) continue;
-                p.part_B[ob + m * NE + etid] = s_dbc[((s2 * T + pf_j[m]) * 2 + 0) * NP + pf_kk[m]];
-                p.part_C[ob + m * NE + etid] = s_dbc[((s2 * T + pf_j[m]) * 2 + 1) * NP + pf_kk[m]];
-            }
         }
     };
     // Recurrence waves, chunk c: recompute its states, then the adjoint back through them.
-    // The recurrence waves keep TH steps of states and decays (and hold
-    // weights) in registers at once and run a chunk in T / TH passes, latest
-    // first: each pass recomputes the chunk from its entering state up to the
-    // end of its steps, then takes the adjoint back through them.  TH < T
-    // only with 8 states per wave (n > 32), where a whole chunk's values would
-    // not fit the register file.
-    constexpr int TH = NSW >= 8 ? T / 2 : T;
     auto process = [&](int c, int s3, int s2) __attribute__((always_inline)) {
         float hstart[NSW];
 #pragma unroll
         for (int q = 0; q < NSW; q++) hstart[q] = s_ck[(s2 * NP + n0 + q) * 64 + lane];
         const float* bcw = s_bc + s2 * (T * 2 * NP) + wave * 2 * NSW;
+        float h[NSW];                                               // running state
+        float hs[T][NSW], as[T][NSW], bs[ZOH ? T : 1][NSW];        // states, decays, hold weights of the chunk
 #pragma unroll
-        for (int j0 = T - TH; j0 >= 0; j0 -= TH) {
-        float h[NSW], hin[NSW];                                     // running state; state entering step j0
-        float hs[TH][NSW], as[TH][NSW], bs[ZOH ? TH : 1][NSW];   // states, decays, hold weights of steps j0 ..
+        for (int q = 0; q < NSW; q++) h[q] = hstart[q];
 #pragma unroll
-        for (int q = 0; q < NSW; q++) h[q] = hin[q] = hstart[q];
-#pragma unroll
-        for (int j = 0; j < j0 + TH; j++) {
+        for (int j = 0; j < T; j++) {
             const float4 pr = s_prep[(s3 * T + j) * 64 + lane];
 #pragma unroll
             for (int q = 0; q < NSW; q++) {
@@ -496,38 +466,35 @@ __global__ __launch_bounds__((SC + 4) * 64) void scan_bwd(const BwdParams p) {
                 if constexpr (ZOH) {
                     const float beta = zoh_weight(pr.x, x2, a, invA[q]);
                     h[q] = fmaf(a, h[q], beta * (pr.y * bcw[j * SC * 2 * NSW + q]));
-                    if (j >= j0) bs[j - j0][q] = beta;
+                    bs[j][q] = beta;
                 } else {
                     h[q] = fmaf(a, h[q], pr.y * bcw[j * SC * 2 * NSW + q]);
                 }
-                if (j >= j0) {
-                    hs[j - j0][q] = h[q];
-                    as[j - j0][q] = a;
-                }
-                if (j == j0 - 1) hin[q] = h[q];
+                hs[j][q] = h[q];
+                as[j][q] = a;
             }
         }
 #pragma unroll
-        for (int j = j0 + TH - 1; j >= j0; j--) {
+        for (int j = T - 1; j >= 0; j--) {
             const float4 pr = s_prep[(s3 * T + j) * 64 + lane];
             float S1 = 0.0f, S2 = 0.0f, S3 = 0.0f, dBv[NSW], dCv[NSW];
 #pragma unroll
             for (int q = 0; q < NSW; q++) {
                 const float Bq = bcw[j * SC * 2 * NSW + q], Cq = bcw[j * SC * 2 * NSW + NSW + q];
                 g[q] = fmaf(pr.z, Cq, g[q]);
-                const float hp = j > j0 ? hs[j - j0 - 1][q] : hin[q];
-                const float ga = g[q] * as[j - j0][q];
+                const float hp = j > 0 ? hs[j - 1][q] : hstart[q];
+                const float ga = g[q] * as[j][q];
                 const float gah = ga * hp;
                 S2 = fmaf(gah, An[q], S2);
                 dA[q] = fmaf(gah, pr.x, dA[q]);
-                dCv[q] = pr.z * hs[j - j0][q];
+                dCv[q] = pr.z * hs[j][q];
                 if constexpr (ZOH) {
                     // beta = (a - 1)/A: d beta/dDelta = a, d beta/dA = (Delta a - beta)/A.
-                    const float beta = bs[j - j0][q];
+                    const float beta = bs[j][q];
                     const float gb = g[q] * beta;
                     S1 = fmaf(gb, Bq, S1);
                     S3 = fmaf(ga, Bq, S3);
-                    dA[q] = fmaf(g[q] * (pr.y * Bq), fmaf(pr.x, as[j - j0][q], -beta) * invA[q], dA[q]);
+                    dA[q] = fmaf(g[q] * (pr.y * Bq), fmaf(pr.x, as[j][q], -beta) * invA[q], dA[q]);
                     dBv[q] = gb * pr.y;
                 } else {
                     S1 = fmaf(g[q], Bq, S1);
@@ -537,25 +504,12 @@ __global__ __launch_bounds__((SC + 4) * 64) void scan_bwd(const BwdParams p) {
             }
             if constexpr (ZOH) S2 = fmaf(pr.w, S3, S2);   // the input term of dDelta: u sum g a B
             s_part[((s2 * SC + wave) * T + j) * 64 + lane] = make_float2(S1, S2);
-            // dB, dC of this step over the 64 channels, two states at a time.
-            if constexpr (RL) {
-                // 16 partials each, to LDS for the element waves to add up.
-                float* dst = s_dbc + ((s2 * T + j) * SC + wave) * (NSW / 2) * 4 * RS + red_lane;
+            // dB, dC of this step over the 64 channels, two states at a time:
+            // 16 partials each, to LDS for the element waves to add up.
+            float* dst = s_dbc + ((s2 * T + j) * SC + wave) * (NSW / 2) * 4 * RS + red_lane;
 #pragma unroll
-                for (int q = 0; q < NSW; q += 2)
-                    dst[(q / 2) * 4 * RS] = wave_part4(dBv[q], dBv[q + 1], dCv[q], dCv[q + 1]);
-            } else {
-                // Whole sums: lane 15 holds dB[q], 31 dC[q], 47 dB[q + 1], 63 dC[q + 1].
-#pragma unroll
-                for (int q = 0; q < NSW; q += 2) {
-                    const float sum = wave_sum4(dBv[q], dBv[q + 1], dCv[q], dCv[q + 1]);
-                    if ((lane & 15) == 15) {
-                        const int r = lane >> 4;
-                        s_dbc[((s2 * T + j) * 2 + (r & 1)) * NP + n0 + q + (r >> 1)] = sum;
-                    }
-                }
-            }
-        }
+            for (int q = 0; q < NSW; q += 2)
+                dst[(q / 2) * 4 * RS] = wave_part4(dBv[q], dBv[q + 1], dCv[q], dCv[q + 1]);
         }
     };
 
@@ -614,17 +568,17 @@ __global__ __launch_bounds__((SC + 4) * 64) void scan_bwd(const BwdParams p) {
         if (dv) {
 #pragma unroll
             for (int q = 0; q < NSW; q++) {
-                if (n0 + q >= n) continue;
-                p.part_A[(pb * d_in + d) * n + n0 + q] = dA[q] * An[q];
-                if (p.dh0 && seg == 0) p.dh0[(int64_t(bi) * d_in + d) * n + n0 + q] = g[q];
+                if (n0 + q >= ns) continue;
+                p.part_A[(pb * d_in + d) * n + k0 + n0 + q] = dA[q] * An[q];
+                if (p.dh0 && seg == 0) p.dh0[(int64_t(bi) * d_in + d) * n + k0 + n0 + q] = g[q];
             }
         }
         if (seg > 0) {
             // Hand the adjoint on to the earlier segment.
-            uint32_t* dst = reinterpret_cast<uint32_t*>(p.handoff) + (int64_t(seg - 1) * G + gi) * n * 64;
+            uint32_t* dst = reinterpret_cast<uint32_t*>(p.handoff) + (int64_t(seg - 1) * G + gi) * NP * 64;
 #pragma unroll
             for (int q = 0; q < NSW; q++)
-                if (n0 + q < n)
+                if (n0 + q < ns)
                     __hip_atomic_store(dst + (n0 + q) * 64 + lane, __float_as_uint(g[q]), __ATOMIC_RELAXED,
                                        __HIP_MEMORY_SCOPE_AGENT);
         }
@@ -645,8 +599,8 @@ __global__ __launch_bounds__((SC + 4) * 64) void scan_bwd(const BwdParams p) {
                 sD += s_red[(r * 64 + etid) * 2];
                 sB += s_red[(r * 64 + etid) * 2 + 1];
             }
-            p.part_D[pb * d_in + dbase + etid] = sD;
-            p.part_bias[pb * d_in + dbase + etid] = sB;
+            if (slice == 0) p.part_D[pb * d_in + dbase + etid] = sD;
+            p.part_bias[((int64_t(seg) * p.slices + slice) * p.b + bi) * d_in + dbase + etid] = sB;
         }
         barrier_lds();
     }

@@ -10,6 +10,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace ss {
 
 constexpr float kLog2e = 1.4426950408889634f;
@@ -58,6 +60,15 @@ using lds_ptr = __attribute__((address_space(3))) char*;
 // emit as an invalid instruction).
 __device__ __forceinline__ lds_ptr dynamic_lds_base() {
     return (lds_ptr)(uintptr_t)((__builtin_amdgcn_groupstaticsize() + 15u) & ~15u);
+}
+
+// f(std::integral_constant<int, I>{}) for I = 0 .. N-1, unrolled at compile time.
+template <int I, int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+    if constexpr (I < N) {
+        f(std::integral_constant<int, I>{});
+        static_for<I + 1, N>(f);
+    }
 }
 
 // `v` unchanged, but opaque to the optimiser: a constant passed through here

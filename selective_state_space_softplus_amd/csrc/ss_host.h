@@ -77,12 +77,19 @@ inline SeqShape seq_shape(int64_t n) {
 }
 
 // Recurrence waves and states per wave of scan_bwd (n <= 64).
+// Backward shapes: at most 16 states per workgroup; larger n is taken in
+// slices of 16 states by separate workgroups (bwd_slices), so that each
+// recurrence wave keeps two states' chunk of values in registers.
 inline SeqShape bwd_shape(int64_t n) {
     if (n <= 2) return {1, 2};
     if (n <= 8) return {4, 2};
-    if (n <= 16) return {8, 2};
-    if (n <= 32) return {8, 4};
-    return {8, 8};
+    return {8, 2};
+}
+
+inline int64_t bwd_slices(int64_t n) {
+    const SeqShape sh = bwd_shape(n);
+    const int64_t np = int64_t(sh.SC) * sh.NSW;
+    return (n + np - 1) / np;
 }
 
 // Workspace of scan_seq cut into K segments, in order: control words (ticket
@@ -167,9 +174,9 @@ enum class SeqMode { Euler, Zoh, Cross, Dz, ZohDz };
 template <typename TIn, int SC, int NSW>
 int launch_seq(ss::ScanParams p, SeqMode mode, void* ws, size_t ws_bytes, hipStream_t st);
 
-// Launch scan_bwd<TIn, SC, NSW, ...> for one call (launch_bwd.h); the number
-// of segments along L is returned in *segments.
-template <typename TIn, int SC, int NSW>
+// Launch scan_bwd<TIn, SC, NSW, SL, ...> for one call (launch_bwd.h); the
+// number of segments along L is returned in *segments.
+template <typename TIn, int SC, int NSW, bool SL>
 int launch_bwd(ss::BwdParams p, bool gate, bool zoh, hipStream_t st, int* segments);
 
 }  // namespace ss_host

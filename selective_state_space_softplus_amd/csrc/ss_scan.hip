@@ -554,7 +554,7 @@ using ss::BwdParams;
 // dbias partials per segment and batch row, then the control words and
 // adjoints of the backward's segments.
 struct BwdWorkspace {
-    size_t fwd, ckpt, part_B, part_C, part_A, part_D, part_bias, ctl, handoff, total;
+    size_t fwd, ckpt, part_B, part_C, part_A, part_D, part_bias, part_du, part_dd, ctl, handoff, total;
 };
 
 size_t round256(size_t x) { return (x + 255) / 256 * 256; }
@@ -566,23 +566,28 @@ BwdWorkspace bwd_workspace(int64_t b, int64_t L, int64_t d_in, int64_t n) {
     w.ckpt = round256(size_t(b) * size_t(nck) * size_t(n) * size_t(d_in) * 4);
     w.part_B = w.part_C = round256(size_t(nblk) * size_t(b) * size_t(L) * size_t(n) * 4);
     w.part_A = round256(size_t(kMaxSegments) * size_t(b) * size_t(d_in) * size_t(n) * 4);
-    w.part_D = w.part_bias = round256(size_t(kMaxSegments) * size_t(b) * size_t(d_in) * 4);
-    const int64_t G = b * nblk;
+    const int64_t slices = bwd_slices(n);
+    w.part_D = round256(size_t(kMaxSegments) * size_t(b) * size_t(d_in) * 4);
+    w.part_bias = round256(size_t(kMaxSegments) * size_t(slices) * size_t(b) * size_t(d_in) * 4);
+    // du and ddelta in parts, one per slice of the states, when there are several.
+    w.part_du = w.part_dd = slices > 1 ? round256(size_t(slices) * size_t(b) * size_t(L) * size_t(d_in) * 4) : 0;
+    const int64_t G = b * nblk * slices;
+    const SeqShape sh = bwd_shape(n);
     w.ctl = round256((size_t(ss::kFlagOffset) + size_t(G) * kMaxSegments) * sizeof(uint32_t));
-    w.handoff = round256(size_t(kMaxSegments - 1) * size_t(G) * size_t(n) * 64 * sizeof(float));
+    w.handoff = round256(size_t(kMaxSegments - 1) * size_t(G) * size_t(sh.SC * sh.NSW) * 64 * sizeof(float));
     w.fwd = seq_workspace(b, d_in, n).total;
-    w.total = w.fwd + w.ckpt + w.part_B + w.part_C + w.part_A + w.part_D + w.part_bias + w.ctl + w.handoff;
+    w.total = w.fwd + w.ckpt + w.part_B + w.part_C + w.part_A + w.part_D + w.part_bias + w.part_du + w.part_dd +
+              w.ctl + w.handoff;
     return w;
 }
 
 template <typename TIn>
 int dispatch_bwd(const BwdParams& p, bool gate, bool zoh, hipStream_t st, int* segments) {
     const SeqShape sh = bwd_shape(p.n);
-    if (sh.SC == 1) return launch_bwd<TIn, 1, 2>(p, gate, zoh, st, segments);
-    if (sh.SC == 4) return launch_bwd<TIn, 4, 2>(p, gate, zoh, st, segments);
-    if (sh.NSW == 2) return launch_bwd<TIn, 8, 2>(p, gate, zoh, st, segments);
-    if (sh.NSW == 4) return launch_bwd<TIn, 8, 4>(p, gate, zoh, st, segments);
-    return launch_bwd<TIn, 8, 8>(p, gate, zoh, st, segments);
+    if (p.slices > 1) return launch_bwd<TIn, 8, 2, true>(p, gate, zoh, st, segments);
+    if (sh.SC == 1) return launch_bwd<TIn, 1, 2, false>(p, gate, zoh, st, segments);
+    if (sh.SC == 4) return launch_bwd<TIn, 4, 2, false>(p, gate, zoh, st, segments);
+    return launch_bwd<TIn, 8, 2, false>(p, gate, zoh, st, segments);
 }
 
 template <typename TOut>
@@ -597,7 +602,7 @@ int reduce(const float* part, void* out, int64_t count, int64_t groups, hipStrea
 SS_EXPORT size_t ss_scan_bwd_workspace_bytes(int64_t b, int64_t L, int64_t d_in, int64_t n, int dtype) {
     if (dtype != SS_F32 && dtype != SS_BF16) return 0;
     if (!sizes_ok(b, L, d_in) || n <= 0 || n > SS_MAX_BWD_STATE || d_in > SS_MAX_CHANNELS) return 0;
-    if (b * ((d_in + 63) / 64) > kMaxWorkgroups || L > kMaxLength) return 0;
+    if (b * ((d_in + 63) / 64) * bwd_slices(n) > kMaxWorkgroups || L > kMaxLength) return 0;
     return bwd_workspace(b, L, d_in, n).total;
 }
 
@@ -616,7 +621,7 @@ SS_EXPORT int ss_scan_bwd_ex(const void* u, const void* delta, const float* A_lo
     if (!sizes_ok(b, L, d_in) || n <= 0 || d_in > SS_MAX_CHANNELS) return SS_ERR_SHAPE;
     if (dtype != SS_F32 && dtype != SS_BF16) return SS_ERR_DTYPE;
     if (n > SS_MAX_BWD_STATE) return SS_ERR_UNSUPPORTED;
-    if (b * ((d_in + 63) / 64) > kMaxWorkgroups || L > kMaxLength) return SS_ERR_SHAPE;
+    if (b * ((d_in + 63) / 64) * bwd_slices(n) > kMaxWorkgroups || L > kMaxLength) return SS_ERR_SHAPE;
     const size_t es = elem_size(dtype);
     for (const void* p : {u, delta, B, C, z, dy, static_cast<const void*>(du), static_cast<const void*>(ddelta),
                           static_cast<const void*>(dB), static_cast<const void*>(dC), static_cast<const void*>(dz)})
@@ -661,7 +666,9 @@ SS_EXPORT int ss_scan_bwd_ex(const void* u, const void* delta, const float* A_lo
     float* part_A = reinterpret_cast<float*>(at += w.part_C);
     float* part_D = reinterpret_cast<float*>(at += w.part_A);
     float* part_bias = reinterpret_cast<float*>(at += w.part_D);
-    uint32_t* bctl = reinterpret_cast<uint32_t*>(at += w.part_bias);
+    float* part_du = reinterpret_cast<float*>(at += w.part_bias);
+    float* part_dd = reinterpret_cast<float*>(at += w.part_du);
+    uint32_t* bctl = reinterpret_cast<uint32_t*>(at += w.part_dd);
     float* handoff = reinterpret_cast<float*>(at += w.ctl);
     uint32_t* err = static_cast<uint32_t*>(workspace) + kStatusWord;
     hipStream_t st = static_cast<hipStream_t>(stream);
@@ -722,6 +729,9 @@ SS_EXPORT int ss_scan_bwd_ex(const void* u, const void* delta, const float* A_lo
     p.part_A = part_A;
     p.part_D = part_D;
     p.part_bias = part_bias;
+    p.slices = int(bwd_slices(n));
+    p.part_du = p.slices > 1 ? part_du : nullptr;
+    p.part_dd = p.slices > 1 ? part_dd : nullptr;
     p.b = b;
     p.L = L;
     p.d_in = d_in;
@@ -737,14 +747,24 @@ SS_EXPORT int ss_scan_bwd_ex(const void* u, const void* delta, const float* A_lo
                           : dispatch_bwd<float>(p, z != nullptr, zoh, st, &K);
     if (rc != SS_OK) return rc;
 
-    // 3. Sums over channel groups (dB, dC) and segments and batch rows (dA_log, dD, dbias), in a fixed order.
+    // 3. Sums over state slices (du, ddelta), channel groups (dB, dC) and
+    //    segments, slices and batch rows (dA_log, dD, dbias), in a fixed order.
     const int64_t nbc = b * L * n;
+    if (p.slices > 1) {
+        rc = dtype == SS_BF16 ? reduce<uint16_t>(part_du, du, nel, p.slices, st)
+                              : reduce<float>(part_du, du, nel, p.slices, st);
+        if (rc == SS_OK)
+            rc = dtype == SS_BF16 ? reduce<uint16_t>(part_dd, ddelta, nel, p.slices, st)
+                                  : reduce<float>(part_dd, ddelta, nel, p.slices, st);
+        if (rc != SS_OK) return rc;
+    }
     rc = dtype == SS_BF16 ? reduce<uint16_t>(part_B, dB, nbc, nblk, st) : reduce<float>(part_B, dB, nbc, nblk, st);
     if (rc == SS_OK)
         rc = dtype == SS_BF16 ? reduce<uint16_t>(part_C, dC, nbc, nblk, st) : reduce<float>(part_C, dC, nbc, nblk, st);
     if (rc == SS_OK) rc = reduce<float>(part_A, dA_log, d_in * n, int64_t(K) * b, st);
     if (rc == SS_OK) rc = reduce<float>(part_D, dD, d_in, int64_t(K) * b, st);
-    if (rc == SS_OK && ddelta_bias && delta_bias) rc = reduce<float>(part_bias, ddelta_bias, d_in, int64_t(K) * b, st);
+    if (rc == SS_OK && ddelta_bias && delta_bias)
+        rc = reduce<float>(part_bias, ddelta_bias, d_in, int64_t(K) * p.slices * b, st);
     return rc;
 }
 

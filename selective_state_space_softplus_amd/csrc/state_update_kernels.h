@@ -13,8 +13,6 @@
 //   in a loop.
 #pragma once
 
-#include <type_traits>
-
 #include "ss_device.h"
 
 namespace ss {
@@ -72,15 +70,6 @@ __device__ __forceinline__ float group_bcast(float v) {
         return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), ctrl, 0xf, 0xf, false));
     } else {
         return __shfl(v, J, G);
-    }
-}
-
-// f(std::integral_constant<int, I>{}) for I = 0 .. N-1, unrolled at compile time.
-template <int I, int N, typename F>
-__device__ __forceinline__ void static_for(F&& f) {
-    if constexpr (I < N) {
-        f(std::integral_constant<int, I>{});
-        static_for<I + 1, N>(f);
     }
 }
 

@@ -84,8 +84,10 @@ def test_noalloc_on_host():
     fwd_case(2, 150, 70, 16, BF16, segments=4, seed=5, mode="noalloc")
 
 
-@pytest.mark.parametrize("case", [(1, 64, 96, 32, F32, True), (2, 50, 70, 16, BF16, False), (1, 40, 64, 64, F32, False)],
-                         ids=["n32-f32-zoh", "n16-bf16", "n64-f32"])
+# n above 16 is taken in slices of 16 states (n = 40: slices of 16, 16, 8).
+@pytest.mark.parametrize("case", [(1, 64, 96, 32, F32, True), (2, 50, 70, 16, BF16, False), (1, 40, 64, 64, F32, False),
+                                  (2, 37, 33, 40, BF16, True)],
+                         ids=["n32-f32-zoh", "n16-bf16", "n64-f32", "n40-bf16-zoh"])
 def test_backward_on_host(case):
     b, L, d, n, dt, zoh = case
     inp = workloads.random_scan_inputs(b, L, d, n, dt, seed=11, gated=True, bias=True)
