@@ -590,6 +590,47 @@ def main(argv=None):
             "updates_per_s": float(f"{cfg.updates / (bms * 1e-3):.4g}"),
             "vs_forward": round(bms / ms_step, 2),
         }
+        del bws
+        # The training pair: a forward that keeps the state every 8 steps and
+        # the pre-gate readout (ss_scan_fwd_save), and the backward from them
+        # (ss_scan_bwd_saved), each timed on its own and as one training step.
+        fws = torch.empty(ss.scan_fwd_workspace_bytes(cfg.b, cfg.L, cfg.d_in, cfg.n, 1), dtype=torch.uint8,
+                          device=dev)
+        sws = torch.empty(ss.lib.ss_scan_bwd_saved_workspace_bytes(cfg.b, cfg.L, cfg.d_in, cfg.n, 1),
+                          dtype=torch.uint8, device=dev)
+        saved = {}
+
+        def fwd_save():
+            saved.update(ss.scan_fwd_save(g["u"], g["delta"], g["A_log"], g["B"], g["C"], g["D"], g["z"],
+                                          g["delta_bias"], True, workspace=fws))
+
+        def bwd_saved():
+            ss.scan_bwd(g["u"], g["delta"], g["A_log"], g["B"], g["C"], g["D"], dyb, g["z"], g["delta_bias"], True,
+                        workspace=sws, saved=saved)
+
+        def timed(fn, reps=5):
+            for _ in range(2):
+                fn()
+            torch.cuda.synchronize()
+            b0.record()
+            for _ in range(reps):
+                fn()
+            b1.record()
+            torch.cuda.synchronize()
+            return b0.elapsed_time(b1) / reps
+
+        fms = timed(fwd_save)
+        sms = timed(bwd_saved)
+        result["backward"]["from_saved"] = {
+            "workload": f"{cfg.name}: ss_scan_fwd_save (y, plus the state every 8 steps and the readout before the "
+                        "gate) and ss_scan_bwd_saved (the same gradients, starting from those)",
+            "fwd_save_ms": round(fms, 4),
+            "bwd_saved_ms": round(sms, 4),
+            "bwd_saved_updates_per_s": float(f"{cfg.updates / (sms * 1e-3):.4g}"),
+            "training_step_ms": round(fms + sms, 4),
+            "training_step_ms_recomputing": round(ms_step + bms, 4),
+        }
+        del saved, fws, sws
 
     if not args.no_cross:
         # VMamba's cross scan on the scan-vmamba maps: the fused kernel against

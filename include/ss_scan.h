@@ -322,6 +322,56 @@ int ss_scan_bwd_ex(const void *u, const void *delta, const float *A_log,
                    int64_t b, int64_t L, int64_t d_in, int64_t n, int dtype,
                    void *workspace, size_t workspace_bytes, void *stream);
 
+/*
+ * Training pair: a forward that keeps what the backward needs, and a
+ * backward that starts from it instead of running the forward scan again.
+ *
+ * ss_scan_checkpoint_bytes: bytes of the checkpoint buffer for these sizes,
+ * b * ((L - 1) / 8) * n * d_in * 4 (0 for invalid sizes, and 0 for L <= 8).
+ *
+ * ss_scan_fwd_save: ss_scan_fwd_ex (same arguments, results and workspace)
+ * that also writes
+ *   checkpoints : (b, (L - 1) / 8, n, d_in) fp32, the state after steps
+ *                 8, 16, ... (checkpoint i holds h after step 8 (i + 1));
+ *                 required (SS_ERR_NULL), 4-byte aligned
+ *   y_pre       : (b, L, d_in) dtype, the readout sum_k C h + D u before the
+ *                 gate; required when z is given (SS_ERR_NULL), else ignored
+ * n <= SS_MAX_BWD_STATE.  Neither may overlap an input, another output or
+ * the workspace (SS_ERR_ALIAS).
+ *
+ * ss_scan_bwd_saved: ss_scan_bwd_ex (same arguments and results) given the
+ * checkpoints and y_pre of an ss_scan_fwd_save call on the same inputs; it
+ * does not run the forward scan again and forms dz from y_pre.  Its
+ * workspace is ss_scan_bwd_saved_workspace_bytes() long (smaller than
+ * ss_scan_bwd's: no room for a forward pass or checkpoints) and 256-byte
+ * aligned.  Results agree with ss_scan_bwd_ex: bit for bit with fp32
+ * inputs; with bf16 inputs dz takes y_pre rounded to bf16 where ss_scan_bwd
+ * uses it unrounded.  The checkpoints (for L > 8) and y_pre are not written.
+ * Returns an ss_status.
+ */
+size_t ss_scan_checkpoint_bytes(int64_t b, int64_t L, int64_t d_in, int64_t n);
+
+size_t ss_scan_bwd_saved_workspace_bytes(int64_t b, int64_t L, int64_t d_in, int64_t n, int dtype);
+
+int ss_scan_fwd_save(const void *u, const void *delta, const float *A_log,
+                     const void *B, const void *C, const float *D,
+                     const void *z, const float *delta_bias, int delta_softplus,
+                     const float *initial_state, int discretization,
+                     void *y, float *last_state, float *checkpoints, void *y_pre,
+                     int64_t b, int64_t L, int64_t d_in, int64_t n, int dtype,
+                     void *workspace, size_t workspace_bytes, void *stream);
+
+int ss_scan_bwd_saved(const void *u, const void *delta, const float *A_log,
+                      const void *B, const void *C, const float *D,
+                      const void *z, const float *delta_bias, int delta_softplus,
+                      const float *initial_state, int discretization,
+                      const float *checkpoints, const void *y_pre,
+                      const void *dy, const float *dlast_state,
+                      void *du, void *ddelta, float *dA_log, void *dB, void *dC,
+                      float *dD, void *dz, float *ddelta_bias, float *dinitial_state,
+                      int64_t b, int64_t L, int64_t d_in, int64_t n, int dtype,
+                      void *workspace, size_t workspace_bytes, void *stream);
+
 /* Largest convolution width W of ss_conv_update. */
 #define SS_MAX_CONV_WIDTH 8
 

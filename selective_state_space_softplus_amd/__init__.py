@@ -75,7 +75,8 @@ STATUS = {0: "SS_OK", -1: "SS_ERR_NULL", -2: "SS_ERR_SHAPE", -3: "SS_ERR_DTYPE",
 EXPORTS = ("ss_scan_fwd_workspace_bytes", "ss_scan_fwd", "ss_scan_fwd_ex", "ss_scan_fwd_noalloc", "ss_scan_status",
            "ss_state_update", "ss_state_update_ex", "ss_scan_bwd", "ss_scan_bwd_ex", "ss_scan_bwd_workspace_bytes",
            "ss_cross_scan_fwd", "ss_cross_scan_fwd_workspace_bytes", "ss_conv_update", "ss_status_string",
-           "ss_set_test_plan")
+           "ss_set_test_plan", "ss_scan_checkpoint_bytes", "ss_scan_fwd_save", "ss_scan_bwd_saved",
+           "ss_scan_bwd_saved_workspace_bytes")
 
 
 class SSError(RuntimeError):
@@ -112,6 +113,14 @@ def _load() -> ctypes.CDLL:
     lib.ss_scan_bwd.argtypes = [P] * 8 + [I] + [P] * 12 + [I64, I64, I64, I64, I, P, ctypes.c_size_t, P]
     lib.ss_scan_bwd_ex.restype = I
     lib.ss_scan_bwd_ex.argtypes = [P] * 8 + [I, P, I] + [P] * 11 + [I64, I64, I64, I64, I, P, ctypes.c_size_t, P]
+    lib.ss_scan_checkpoint_bytes.restype = ctypes.c_size_t
+    lib.ss_scan_checkpoint_bytes.argtypes = [I64, I64, I64, I64]
+    lib.ss_scan_bwd_saved_workspace_bytes.restype = ctypes.c_size_t
+    lib.ss_scan_bwd_saved_workspace_bytes.argtypes = [I64, I64, I64, I64, I]
+    lib.ss_scan_fwd_save.restype = I
+    lib.ss_scan_fwd_save.argtypes = [P] * 8 + [I, P, I, P, P, P, P, I64, I64, I64, I64, I, P, ctypes.c_size_t, P]
+    lib.ss_scan_bwd_saved.restype = I
+    lib.ss_scan_bwd_saved.argtypes = [P] * 8 + [I, P, I] + [P] * 13 + [I64, I64, I64, I64, I, P, ctypes.c_size_t, P]
     lib.ss_cross_scan_fwd_workspace_bytes.restype = ctypes.c_size_t
     lib.ss_cross_scan_fwd_workspace_bytes.argtypes = [I64, I64, I64, I64, I64, I]
     lib.ss_cross_scan_fwd.restype = I
@@ -282,6 +291,53 @@ def scan_fwd(u, delta, A_log, B, C, D, z=None, delta_bias=None, delta_softplus=T
     return (y, last_state) if return_last_state else y
 
 
+def scan_fwd_save(u, delta, A_log, B, C, D, z=None, delta_bias=None, delta_softplus=True, initial_state=None,
+                  zoh=False, return_last_state=False, workspace=None, check=False):
+    """Forward for training (ss_scan_fwd_save): returns a dict with y (and last_state if asked) and what
+    scan_bwd(saved=...) starts from: checkpoints (b, (L - 1) // 8, n, d_in) fp32 and, gated, y_pre."""
+    if u.dim() != 3 or A_log.dim() != 2:
+        raise ValueError("u must be (b, L, d_in) and A_log (d_in, n)")
+    b, L, d_in = u.shape
+    n = A_log.shape[1]
+    dev = u.device
+    code = _dtype_code(u.dtype)
+    for t, name, shape, dt in ((u, "u", (b, L, d_in), u.dtype), (delta, "delta", (b, L, d_in), u.dtype),
+                               (A_log, "A_log", (d_in, n), torch.float32), (B, "B", (b, L, n), u.dtype),
+                               (C, "C", (b, L, n), u.dtype), (D, "D", (d_in,), torch.float32),
+                               (z, "z", (b, L, d_in), u.dtype), (delta_bias, "delta_bias", (d_in,), torch.float32),
+                               (initial_state, "initial_state", (b, d_in, n), torch.float32)):
+        _check(t, name, shape, dt, dev)
+    out = dict(y=torch.empty_like(u),
+               checkpoints=torch.empty((b, max(L - 1, 0) // 8, n, d_in), dtype=torch.float32, device=dev))
+    if z is not None:
+        out["y_pre"] = torch.empty_like(u)
+    if return_last_state:
+        out["last_state"] = torch.empty((b, d_in, n), dtype=torch.float32, device=dev)
+    if b == 0 or L == 0 or d_in == 0:
+        # Nothing to scan: no steps leave the initial state as it is, and nothing is saved.
+        if return_last_state:
+            if initial_state is None:
+                out["last_state"].zero_()
+            else:
+                out["last_state"].copy_(initial_state)
+        return out
+    need = scan_fwd_workspace_bytes(b, L, d_in, n, code)
+    if workspace is None:
+        workspace = _workspace(dev, need)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    with torch.cuda.device(dev):
+        rc = lib.ss_scan_fwd_save(_ptr(u), _ptr(delta), _ptr(A_log), _ptr(B), _ptr(C), _ptr(D), _ptr(z),
+                                  _ptr(delta_bias), int(bool(delta_softplus)), _ptr(initial_state),
+                                  SS_DISC_ZOH if zoh else SS_DISC_EULER, _ptr(out["y"]), _ptr(out.get("last_state")),
+                                  _ptr(out["checkpoints"]), _ptr(out.get("y_pre")), b, L, d_in, n, code,
+                                  _ptr(workspace), ws_bytes, _stream(dev))
+    if rc != 0:
+        raise SSError(rc, "ss_scan_fwd_save")
+    if check:
+        _raise_on_timeout(workspace, "ss_scan_fwd_save")
+    return out
+
+
 def state_update(state, x, dt, A_log, B, C, D, z=None, dt_bias=None, dt_softplus=True, out=None, zoh=False):
     """One decode step; updates ``state`` in place and returns y (b, d_in)."""
     if state.dim() != 3:
@@ -384,9 +440,11 @@ def cross_scan_fwd(x, delta, A_log, B, C, D, delta_bias=None, delta_softplus=Tru
 
 
 def scan_bwd(u, delta, A_log, B, C, D, dy, z=None, delta_bias=None, delta_softplus=True, initial_state=None,
-             dlast_state=None, workspace=None, zoh=False, check=False):
+             dlast_state=None, workspace=None, zoh=False, check=False, saved=None):
     """Gradients of the scan for output gradients dy (and dlast_state): the delta' B u input term, or
-    with zoh=True the zero-order hold's (ss_scan_bwd_ex).
+    with zoh=True the zero-order hold's (ss_scan_bwd_ex).  ``saved``: the dict scan_fwd_save returned
+    for these inputs; the backward then starts from it (ss_scan_bwd_saved) instead of running the
+    forward scan again.
 
     Returns a dict: du, ddelta, dz (dtype of u; dz only with z), dA_log, dD, ddelta_bias (fp32; only
     with delta_bias), dB, dC (dtype of u), dinitial_state (fp32; only with initial_state).
@@ -421,7 +479,12 @@ def scan_bwd(u, delta, A_log, B, C, D, dy, z=None, delta_bias=None, delta_softpl
             else:
                 v.zero_()
         return g
-    need = int(lib.ss_scan_bwd_workspace_bytes(b, L, d_in, n, code))
+    if saved is not None:
+        _check(saved["checkpoints"], "checkpoints", (b, (L - 1) // 8, n, d_in), torch.float32, dev)
+        _check(saved.get("y_pre"), "y_pre", (b, L, d_in), u.dtype, dev)
+        need = int(lib.ss_scan_bwd_saved_workspace_bytes(b, L, d_in, n, code))
+    else:
+        need = int(lib.ss_scan_bwd_workspace_bytes(b, L, d_in, n, code))
     if workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=dev) if need else None
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
@@ -431,33 +494,45 @@ def scan_bwd(u, delta, A_log, B, C, D, dy, z=None, delta_bias=None, delta_softpl
         tail = (_ptr(dy), _ptr(dlast_state), _ptr(g["du"]), _ptr(g["ddelta"]), _ptr(g["dA_log"]), _ptr(g["dB"]),
                 _ptr(g["dC"]), _ptr(g["dD"]), _ptr(g.get("dz")), _ptr(g.get("ddelta_bias")),
                 _ptr(g.get("dinitial_state")), b, L, d_in, n, code, _ptr(workspace), ws_bytes, _stream(dev))
-        if zoh:
-            rc = lib.ss_scan_bwd_ex(*head, SS_DISC_ZOH, *tail)
+        disc = SS_DISC_ZOH if zoh else SS_DISC_EULER
+        if saved is not None:
+            where = "ss_scan_bwd_saved"
+            rc = lib.ss_scan_bwd_saved(*head, disc, _ptr(saved["checkpoints"]), _ptr(saved.get("y_pre")), *tail)
+        elif zoh:
+            where = "ss_scan_bwd_ex"
+            rc = lib.ss_scan_bwd_ex(*head, disc, *tail)
         else:
+            where = "ss_scan_bwd"
             rc = lib.ss_scan_bwd(*head, *tail)
     if rc != 0:
-        raise SSError(rc, "ss_scan_bwd_ex" if zoh else "ss_scan_bwd")
+        raise SSError(rc, where)
     if check:
-        _raise_on_timeout(workspace, "ss_scan_bwd_ex" if zoh else "ss_scan_bwd")
+        _raise_on_timeout(workspace, where)
     return g
 
 
 class _SelectiveScan(torch.autograd.Function):
-    """The scan as an autograd function: forward ss_scan_fwd(_ex), backward ss_scan_bwd(_ex)."""
+    """The scan as an autograd function: forward ss_scan_fwd_save, backward ss_scan_bwd_saved (from
+    the checkpoints and pre-gate readout the forward kept)."""
 
     @staticmethod
     def forward(ctx, u, delta, A_log, B, C, D, z, delta_bias, delta_softplus, initial_state, zoh):
-        y = scan_fwd(u, delta, A_log, B, C, D, z, delta_bias, delta_softplus, initial_state=initial_state, zoh=zoh)
+        out = scan_fwd_save(u, delta, A_log, B, C, D, z, delta_bias, delta_softplus, initial_state=initial_state,
+                            zoh=zoh)
         ctx.delta_softplus = delta_softplus
         ctx.zoh = zoh
-        ctx.save_for_backward(u, delta, A_log, B, C, D, z, delta_bias, initial_state)
-        return y
+        ctx.save_for_backward(u, delta, A_log, B, C, D, z, delta_bias, initial_state, out["checkpoints"],
+                              out.get("y_pre"))
+        return out["y"]
 
     @staticmethod
     def backward(ctx, dy):
-        u, delta, A_log, B, C, D, z, delta_bias, initial_state = ctx.saved_tensors
+        u, delta, A_log, B, C, D, z, delta_bias, initial_state, ckpt, y_pre = ctx.saved_tensors
+        saved = dict(checkpoints=ckpt)
+        if y_pre is not None:
+            saved["y_pre"] = y_pre
         g = scan_bwd(u, delta, A_log, B, C, D, dy.contiguous(), z, delta_bias, ctx.delta_softplus, initial_state,
-                     zoh=ctx.zoh)
+                     zoh=ctx.zoh, saved=saved)
         return (g["du"], g["ddelta"], g["dA_log"], g["dB"], g["dC"], g["dD"], g.get("dz"), g.get("ddelta_bias"),
                 None, g.get("dinitial_state"), None)
 

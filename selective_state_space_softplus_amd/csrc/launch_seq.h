@@ -32,6 +32,7 @@ int launch_seq(ss::ScanParams p, SeqMode mode, void* ws, size_t ws_bytes, hipStr
     const bool wide = (p.d_in * int64_t(sizeof(TIn))) % 16 == 0 && aligned(p.u, 16) &&
                       aligned(p.delta, 16) && (!p.z || aligned(p.z, 16)) &&
                       (!dz || aligned(p.dy, 16)) &&
+                      (!p.ypre || aligned(p.ypre, (TW / ss::kSeqElemWaves) * sizeof(TIn))) &&
                       (mode == SeqMode::Cross || aligned(out, (TW / ss::kSeqElemWaves) * sizeof(TIn)));
     const int T = wide ? TW : TN;
     const int variant = mode == SeqMode::Cross   ? 12 + (wide ? 2 : 0) + (p.softplus ? 1 : 0)

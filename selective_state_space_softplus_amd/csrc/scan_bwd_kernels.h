@@ -59,6 +59,8 @@ struct BwdParams {
     const float* bias;
     const float* h0;          // (b, d_in, n) or null
     const void* dy;           // (b, L, d_in)
+    const void* ypre;         // gated, from saved states: the forward's readout before the gate (b, L, d_in), else null
+    void* dz;                 // with ypre: dz is written here
     const float* dlast;       // (b, d_in, n) or null
     const float* ckpt;        // (b, nck, n, d_in): state after steps 8 (i + 1)
     void* du;
@@ -109,24 +111,30 @@ __device__ __forceinline__ float wave_part4(float v0, float v1, float v2, float 
 // The recurrence waves leave the dB, dC sums over the 64 channels at 16
 // partials per (step, state) -- a row of 16 floats -- and the element waves
 // add them up.
+//
+// gfx950's LDS has 64 banks of 4 bytes; a 16-byte access serves 16 lanes a
+// cycle, a 4-byte access all 64.  So: the per-(step, channel) values are
+// kept as four planes of floats, not as float4s, since the recurrence waves
+// read one or two of them at a time (a 4-byte read at a 16-byte lane stride
+// meets each bank four times); and the partial rows are RS = 20 floats apart,
+// so that the 16 rows that one 16-byte read of a row per lane touches in a
+// cycle start on 16 different groups of 4 banks (20 g mod 64, g = 0 .. 15,
+// are distinct multiples of 4).
 template <int SC, int NP>
 struct BwdLds {
     static constexpr int T = kCkptSteps;
     static_assert(NP <= 16, "states per workgroup (larger n is taken in slices)");
-    static constexpr int RS = 18;                             // mean floats per row: pairs of rows padded by 4
+    static constexpr int RS = 20;                             // floats per partial row (16 used)
     static constexpr int ROWS = T * 2 * NP;                   // (step, state, B or C) rows of a chunk
-    static constexpr int PREP = T * 64 * 16;                  // (Delta, w, dy', u) per (step, channel)
+    static constexpr int PLANE = 3 * T * 64 * 4;              // one of Delta, w, dy', u per (slot, step, channel)
+    static constexpr int PREP = 4 * PLANE;                    // the four planes, three ring slots each
     static constexpr int PART = SC * T * 64 * 8;              // (S1, S2) per (wave, step, channel)
     static constexpr int CK = NP * 64 * 4;                    // state entering the chunk
     static constexpr int BC = T * 2 * NP * 4;                 // B, C rows as fp32, grouped per wave
     static constexpr int DBC = ROWS * RS * 4;                 // dB, dC partial rows of the chunk
-    // Row g of the partial rows starts at float g 16 + (g / 2) 4: a recurrence
-    // wave's four rows are two contiguous 32-float runs (bank-conflict-free
-    // writes), and 8 consecutive rows start on 8 different 4-bank groups
-    // (conflict-free 16-byte reads of one row per lane).
-    static constexpr int row_off(int g) { return g * 16 + (g >> 1) * 4; }
-    static constexpr int off_prep = 0;                        // [3]
-    static constexpr int off_part = off_prep + 3 * PREP;      // [2]
+    static constexpr int row_off(int g) { return g * RS; }
+    static constexpr int off_prep = 0;                        // [4 planes][3 slots]
+    static constexpr int off_part = off_prep + PREP;          // [2]
     static constexpr int off_ck = off_part + 2 * PART;        // [2]
     static constexpr int off_bc = off_ck + 2 * CK;            // [2]
     static constexpr int off_dbc = off_bc + 2 * BC;           // [2]
@@ -149,13 +157,15 @@ __global__ __launch_bounds__((SC + 4) * 64) void scan_bwd(const BwdParams p) {
     static_assert(NSW % 2 == 0, "states reduced two at a time");
     extern __shared__ __align__(16) float smem[];
     char* const lds = reinterpret_cast<char*>(smem);
-    float4* s_prep = reinterpret_cast<float4*>(lds + Lds::off_prep);   // [3][T][64]
+    // (Delta, w, dy', u) of (slot, step, channel) at s_prep[plane * PL + (slot T + step) 64 + channel].
+    float* s_prep = reinterpret_cast<float*>(lds + Lds::off_prep);
+    constexpr int PL = Lds::PLANE / 4;
     float2* s_part = reinterpret_cast<float2*>(lds + Lds::off_part);   // [2][SC][T][64]
     float* s_ck = reinterpret_cast<float*>(lds + Lds::off_ck);         // [2][NP][64]
     float* s_bc = reinterpret_cast<float*>(lds + Lds::off_bc);         // [2][T][SC][2][NSW]
     float* s_dbc = reinterpret_cast<float*>(lds + Lds::off_dbc);       // [2][T][2][NP], or [2][ROWS][RS] rows
     constexpr int RS = Lds::RS, ROWS = Lds::ROWS;
-    static_assert(Lds::row_off(4) == 4 * RS && ROWS % 4 == 0, "groups of 4 partial rows at 4 RS floats");
+    static_assert(ROWS % 4 == 0, "groups of 4 partial rows");
     constexpr int RPT = (ROWS + NE - 1) / NE;      // partial rows each element thread adds up per chunk
 
     const int tid = threadIdx.x;
@@ -256,7 +266,7 @@ __global__ __launch_bounds__((SC + 4) * 64) void scan_bwd(const BwdParams p) {
     using Word = typename RawIn::type;
     constexpr int ES = int(sizeof(TIn));
     struct Chunk {
-        Word u[V], dl[V], z[V], dy[V];
+        Word u[V], dl[V], z[V], dy[V], yp[V];
         Word b[EBC], c[EBC];
         float ck[ECK];
     };
@@ -309,7 +319,7 @@ __global__ __launch_bounds__((SC + 4) * 64) void scan_bwd(const BwdParams p) {
         red_off[m] = j * n + k0 + kk;
     }
     // Recurrence lane's place in a group of 4 partial rows: row lane / 16, column lane % 16.
-    const int red_lane = lane + (lane >> 5) * 4;
+    const int red_lane = (lane >> 4) * RS + (lane & 15);
 
     // Uniform bases of chunk k (clamped into the segment, so always inside the tensors).
     auto row_base = [&](int k) __attribute__((always_inline)) {
@@ -336,6 +346,7 @@ __global__ __launch_bounds__((SC + 4) * 64) void scan_bwd(const BwdParams p) {
             r.dl[i] = ld(p.delta, rb, o);
             if (GATE) r.z[i] = ld(p.z, rb, o);
             r.dy[i] = ld(p.dy, rb, o);
+            if (GATE && p.ypre) r.yp[i] = ld(p.ypre, rb, o);
         }
         const int64_t bb = (brow + int64_t(max(k, kc0)) * T) * n;
 #pragma unroll
@@ -364,8 +375,20 @@ __global__ __launch_bounds__((SC + 4) * 64) void scan_bwd(const BwdParams p) {
             const float z = (GATE && ok) ? RawIn::f(r.z[i]) : 0.0f;
             const float dy = ok ? RawIn::f(r.dy[i]) : 0.0f;
             const float dl = ok ? (SP ? softplus(x) : x) : 0.0f;
-            const float dyp = GATE ? dy * silu(z) : dy;
-            s_prep[(s3 * T + er) * 64 + ec + i * TPR] = make_float4(dl, ZOH ? u : dl * u, dyp, u);
+            // dy' = dy silu(z); from saved states also dz = dy y' silu'(z),
+            // silu'(z) = sigmoid(z) (1 + z (1 - sigmoid(z))).
+            const float sg = GATE ? rcp_hw(1.0f + exp2_hw(-z * kLog2e)) : 1.0f;
+            const float dyp = GATE ? dy * (z * sg) : dy;
+            if (GATE && p.ypre && ok) {
+                const float dzv = dy * RawIn::f(r.yp[i]) * sg * fmaf(z, 1.0f - sg, 1.0f);
+                TIn* q = static_cast<TIn*>(p.dz) + row_base(k);
+                Elem<TIn>::store(reinterpret_cast<TIn*>(reinterpret_cast<char*>(q) + off_row[i]), 0, dzv);
+            }
+            const int e = (s3 * T + er) * 64 + ec + i * TPR;
+            s_prep[e] = dl;
+            s_prep[PL + e] = ZOH ? u : dl * u;
+            s_prep[2 * PL + e] = dyp;
+            s_prep[3 * PL + e] = u;
             kp.x[i] = x;
         }
 #pragma unroll
@@ -399,7 +422,8 @@ __global__ __launch_bounds__((SC + 4) * 64) void scan_bwd(const BwdParams p) {
             for (int i = 0; i < V; i++) q[w][i] = pp[w * T * 64 + i * TPR];
 #pragma unroll
         for (int i = 0; i < V; i++) {
-            const float4 pr = s_prep[(s3 * T + er) * 64 + ec + i * TPR];    // (Delta, w, dy', u)
+            const int e = (s3 * T + er) * 64 + ec + i * TPR;
+            const float4 pr = make_float4(s_prep[e], 0.0f, s_prep[2 * PL + e], s_prep[3 * PL + e]);   // (Delta, -, dy', u)
             float S1 = q[0][i].x, S2 = q[0][i].y;
 #pragma unroll
             for (int w = 1; w < SC; w++) {
@@ -458,7 +482,8 @@ __global__ __launch_bounds__((SC + 4) * 64) void scan_bwd(const BwdParams p) {
         for (int q = 0; q < NSW; q++) h[q] = hstart[q];
 #pragma unroll
         for (int j = 0; j < T; j++) {
-            const float4 pr = s_prep[(s3 * T + j) * 64 + lane];
+            const int e = (s3 * T + j) * 64 + lane;
+            const float4 pr = make_float4(s_prep[e], s_prep[PL + e], s_prep[2 * PL + e], ZOH ? s_prep[3 * PL + e] : 0.0f);
 #pragma unroll
             for (int q = 0; q < NSW; q++) {
                 const float x2 = pr.x * A2[q];
@@ -476,7 +501,8 @@ __global__ __launch_bounds__((SC + 4) * 64) void scan_bwd(const BwdParams p) {
         }
 #pragma unroll
         for (int j = T - 1; j >= 0; j--) {
-            const float4 pr = s_prep[(s3 * T + j) * 64 + lane];
+            const int e = (s3 * T + j) * 64 + lane;
+            const float4 pr = make_float4(s_prep[e], s_prep[PL + e], s_prep[2 * PL + e], ZOH ? s_prep[3 * PL + e] : 0.0f);
             float S1 = 0.0f, S2 = 0.0f, S3 = 0.0f, dBv[NSW], dCv[NSW];
 #pragma unroll
             for (int q = 0; q < NSW; q++) {

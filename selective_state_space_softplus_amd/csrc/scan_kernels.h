@@ -58,6 +58,7 @@ struct ScanParams {
     float* ckpt;         // (b, nck, n, d_in) states after every kCkptSteps steps, or null (scan_seq)
     const void* dy;      // gradient of y: with dz, scan_seq writes dz in place of y (gated scans)
     void* dz;
+    void* ypre;          // gated scans: the readout before the gate, (b, L, d_in), or null (scan_seq)
     int nck;             // checkpoints per batch row: (L - 1) / kCkptSteps
     int64_t b, L, d_in, n;
     int softplus;
@@ -459,8 +460,11 @@ __global__ __launch_bounds__((SC + kSeqElemWaves + 1) * 64) void scan_seq(const 
     // staging) are taken by the Euler forward only: in the zero-order-hold
     // and dz forms, whose recurrence waves already fill the register file,
     // they made one fp32 build (8 x 4 states, zero-order hold, dz) compute a
-    // wrong dz, though the same source run on the host is correct.
-    constexpr bool kWholeForms = !ZOH && !DZ && !CROSS;
+    // wrong dz, though the same source run on the host is correct.  Nor by
+    // the 8 x 8 shape (n above 32), which spills registers with them: its
+    // gated bf16 form faulted the GPU in the one run it had (its cause not
+    // found; the same source runs clean on the host).
+    constexpr bool kWholeForms = !ZOH && !DZ && !CROSS && SC * NSW <= 32;
     constexpr bool kFastLoads = WIDE && kWholeForms;
     constexpr int XEPL = 16 / ES, XLPR = 64 / XEPL, XRPI = 64 / XLPR;   // elements, lanes, rows per 16-byte load
     uint32_t vo_x = 0;
@@ -597,13 +601,14 @@ __global__ __launch_bounds__((SC + kSeqElemWaves + 1) * 64) void scan_seq(const 
             for (int i = 0; i < V; i++) ypv[w][i] = src[w * T * 64 + i];
         Row zr;
         if (GATE) zr.read(lds + Lds::off_rz + zslot * Lds::RX, er, ec);
-        float yv[V];
+        float yv[V], ypre[V];
 #pragma unroll
         for (int i = 0; i < V; i++) {
             float acc = ypv[0][i];
 #pragma unroll
             for (int w = 1; w < SC; w++) acc += ypv[w][i];
             acc = fmaf(Dv[i], uvk[i], acc);
+            ypre[i] = acc;
             if constexpr (DZ) {
                 const float z = zr.f(i);
                 const float sg = rcp_hw(1.0f + exp2_hw(-z * kLog2e));
@@ -617,6 +622,12 @@ __global__ __launch_bounds__((SC + kSeqElemWaves + 1) * 64) void scan_seq(const 
         TOut* yp = static_cast<TOut*>(DZ ? p.dz : p.y);
         if (valid > 0 && yp)
             store_span<TOut, V, WIDE>(yp + (brow + t_begin + int64_t(k) * T) * d_in, off_el, yv, valid);
+        if constexpr (GATE && !DZ && !CROSS) {
+            // The readout before the gate, for a backward pass that starts from saved states.
+            if (valid > 0 && p.ypre)
+                store_span<TOut, V, WIDE>(static_cast<TOut*>(p.ypre) + (brow + t_begin + int64_t(k) * T) * d_in,
+                                          off_el, ypre, valid);
+        }
     };
 
     // ---- fill: loads of chunks 0 .. 2 and the gate of chunk 0; phase 1 and

@@ -178,23 +178,29 @@ void* scratch_address() {
 // the workspace is the caller's, which must be as large as the query says;
 // otherwise it is the library's static scratch, and the segment count is
 // lowered until the scan fits in it.
+// save: keep what ss_scan_bwd_saved starts from -- in ckpt the state after
+// every kCkptSteps steps, (b, (L - 1) / kCkptSteps, n, d_in) fp32 (null when
+// there is none, L <= kCkptSteps), and, gated, in ypre the readout before the
+// gate, (b, L, d_in).
 int scan_fwd_impl(const void* u, const void* delta, const float* A_log, const void* B, const void* C,
                   const float* D, const void* z, const float* delta_bias, int delta_softplus,
-                  const float* initial_state, int discretization, void* y, float* last_state, int64_t b, int64_t L,
-                  int64_t d_in, int64_t n, int dtype, void* workspace, size_t workspace_bytes, bool own_ws,
-                  void* stream) {
+                  const float* initial_state, int discretization, void* y, float* last_state, float* ckpt,
+                  void* ypre, int64_t b, int64_t L, int64_t d_in, int64_t n, int dtype, void* workspace,
+                  size_t workspace_bytes, bool own_ws, void* stream, bool save = false) {
     if (!u || !delta || !A_log || !B || !C || !D || !y) return SS_ERR_NULL;
+    if (save && z && !ypre) return SS_ERR_NULL;
+    if (!z) ypre = nullptr;
     if (!sizes_ok(b, L, d_in) || n <= 0 || d_in > SS_MAX_CHANNELS) return SS_ERR_SHAPE;
     if (dtype != SS_F32 && dtype != SS_BF16) return SS_ERR_DTYPE;
     if (n > SS_MAX_STATE) return SS_ERR_UNSUPPORTED;
     if (b * ((d_in + 63) / 64) > kMaxWorkgroups || L > kMaxLength) return SS_ERR_SHAPE;
     if (discretization != SS_DISC_EULER && discretization != SS_DISC_ZOH) return SS_ERR_MODE;
     const size_t es = elem_size(dtype);
-    for (const void* p : {u, delta, B, C, z, static_cast<const void*>(y)})
+    for (const void* p : {u, delta, B, C, z, static_cast<const void*>(y), static_cast<const void*>(ypre)})
         if (p && !aligned(p, es)) return SS_ERR_ALIGN;
     for (const void* p : {static_cast<const void*>(A_log), static_cast<const void*>(D),
                           static_cast<const void*>(delta_bias), static_cast<const void*>(initial_state),
-                          static_cast<const void*>(last_state)})
+                          static_cast<const void*>(last_state), static_cast<const void*>(ckpt)})
         if (p && !aligned(p, 4)) return SS_ERR_ALIGN;
     const int64_t nel = b * L * d_in;
     const Range ins[] = {range_of(u, nel, es), range_of(delta, nel, es), range_of(A_log, d_in * n, 4),
@@ -210,6 +216,14 @@ int scan_fwd_impl(const void* u, const void* delta, const float* A_log, const vo
     for (const Range& r : ins)
         if (overlaps(r, ry) || overlaps(r, rs)) return SS_ERR_ALIAS;
     if (overlaps(ry, rs) || overlaps(rh, ry) || (!in_place && overlaps(rh, rs))) return SS_ERR_ALIAS;
+    // The saved states are outputs too.
+    const Range rc = range_of(ckpt, ckpt ? b * ((L - 1) / ss::kCkptSteps) * n * d_in : 0, 4);
+    const Range rp = range_of(ypre, ypre ? nel : 0, es);
+    for (const Range& r : ins)
+        if (overlaps(r, rc) || overlaps(r, rp)) return SS_ERR_ALIAS;
+    for (const Range& r : {ry, rs, rh})
+        if (overlaps(r, rc) || overlaps(r, rp)) return SS_ERR_ALIAS;
+    if (overlaps(rc, rp)) return SS_ERR_ALIAS;
     if (own_ws) {
         const size_t need = ss_scan_fwd_workspace_bytes(b, L, d_in, n, dtype);
         if (!workspace || workspace_bytes < need) return SS_ERR_WORKSPACE;
@@ -218,7 +232,8 @@ int scan_fwd_impl(const void* u, const void* delta, const float* A_log, const vo
         const Range rw = range_of(workspace, int64_t(workspace_bytes), 1);
         for (const Range& r : ins)
             if (overlaps(r, rw)) return SS_ERR_ALIAS;
-        if (overlaps(ry, rw) || overlaps(rs, rw) || overlaps(rh, rw)) return SS_ERR_ALIAS;
+        if (overlaps(ry, rw) || overlaps(rs, rw) || overlaps(rh, rw) || overlaps(rc, rw) || overlaps(rp, rw))
+            return SS_ERR_ALIAS;
     } else {
         // Validation is done: only now is the device touched.
         workspace = scratch_address();
@@ -239,6 +254,9 @@ int scan_fwd_impl(const void* u, const void* delta, const float* A_log, const vo
     p.y = y;
     p.last_state = last_state;
     p.h0 = initial_state;
+    p.ckpt = ckpt;
+    p.nck = int((L - 1) / ss::kCkptSteps);
+    p.ypre = ypre;
     p.b = b;
     p.L = L;
     p.d_in = d_in;
@@ -251,7 +269,7 @@ int scan_fwd_impl(const void* u, const void* delta, const float* A_log, const vo
     hipStream_t st = static_cast<hipStream_t>(stream);
 
     const bool zoh = discretization == SS_DISC_ZOH;
-    if (choose_kernel(p, zoh) == ScanKernel::Tpar) {
+    if (!save && choose_kernel(p, zoh) == ScanKernel::Tpar) {
         // No segment waits: only the status words need clearing.
         hipLaunchKernelGGL(ss::scan_ctl_reset, dim3(1), dim3(64), 0, st, p.err, int64_t(0), p.err);
         if (hipGetLastError() != hipSuccess) return SS_ERR_HIP;
@@ -270,7 +288,19 @@ SS_EXPORT int ss_scan_fwd_ex(const void* u, const void* delta, const float* A_lo
                              int64_t L, int64_t d_in, int64_t n, int dtype, void* workspace, size_t workspace_bytes,
                              void* stream) {
     return scan_fwd_impl(u, delta, A_log, B, C, D, z, delta_bias, delta_softplus, initial_state, discretization, y,
-                         last_state, b, L, d_in, n, dtype, workspace, workspace_bytes, true, stream);
+                         last_state, nullptr, nullptr, b, L, d_in, n, dtype, workspace, workspace_bytes, true, stream);
+}
+
+SS_EXPORT int ss_scan_fwd_save(const void* u, const void* delta, const float* A_log, const void* B, const void* C,
+                               const float* D, const void* z, const float* delta_bias, int delta_softplus,
+                               const float* initial_state, int discretization, void* y, float* last_state,
+                               float* checkpoints, void* y_pre, int64_t b, int64_t L, int64_t d_in, int64_t n,
+                               int dtype, void* workspace, size_t workspace_bytes, void* stream) {
+    if (!checkpoints && L > ss::kCkptSteps) return SS_ERR_NULL;   // none are kept for L <= 8
+    if (n > SS_MAX_BWD_STATE) return SS_ERR_UNSUPPORTED;
+    return scan_fwd_impl(u, delta, A_log, B, C, D, z, delta_bias, delta_softplus, initial_state, discretization, y,
+                         last_state, L > ss::kCkptSteps ? checkpoints : nullptr, y_pre, b, L, d_in, n, dtype,
+                         workspace, workspace_bytes, true, stream, true);
 }
 
 SS_EXPORT int ss_scan_fwd_noalloc(const void* u, const void* delta, const float* A_log, const void* B,
@@ -279,7 +309,7 @@ SS_EXPORT int ss_scan_fwd_noalloc(const void* u, const void* delta, const float*
                                   float* last_state, int64_t b, int64_t L, int64_t d_in, int64_t n, int dtype,
                                   void* stream) {
     return scan_fwd_impl(u, delta, A_log, B, C, D, z, delta_bias, delta_softplus, initial_state, discretization, y,
-                         last_state, b, L, d_in, n, dtype, nullptr, 0, false, stream);
+                         last_state, nullptr, nullptr, b, L, d_in, n, dtype, nullptr, 0, false, stream);
 }
 
 SS_EXPORT int ss_scan_status(const void* workspace, size_t workspace_bytes, int32_t* status, void* stream) {
@@ -559,11 +589,13 @@ struct BwdWorkspace {
 
 size_t round256(size_t x) { return (x + 255) / 256 * 256; }
 
-BwdWorkspace bwd_workspace(int64_t b, int64_t L, int64_t d_in, int64_t n) {
+// saved: the backward from states the forward saved (no forward pass, no
+// checkpoints of its own; the first 256 bytes hold the status words).
+BwdWorkspace bwd_workspace(int64_t b, int64_t L, int64_t d_in, int64_t n, bool saved = false) {
     const int64_t nck = (L - 1) / ss::kCkptSteps;
     const int64_t nblk = (d_in + 63) / 64;
     BwdWorkspace w;
-    w.ckpt = round256(size_t(b) * size_t(nck) * size_t(n) * size_t(d_in) * 4);
+    w.ckpt = saved ? 0 : round256(size_t(b) * size_t(nck) * size_t(n) * size_t(d_in) * 4);
     w.part_B = w.part_C = round256(size_t(nblk) * size_t(b) * size_t(L) * size_t(n) * 4);
     w.part_A = round256(size_t(kMaxSegments) * size_t(b) * size_t(d_in) * size_t(n) * 4);
     const int64_t slices = bwd_slices(n);
@@ -575,7 +607,7 @@ BwdWorkspace bwd_workspace(int64_t b, int64_t L, int64_t d_in, int64_t n) {
     const SeqShape sh = bwd_shape(n);
     w.ctl = round256((size_t(ss::kFlagOffset) + size_t(G) * kMaxSegments) * sizeof(uint32_t));
     w.handoff = round256(size_t(kMaxSegments - 1) * size_t(G) * size_t(sh.SC * sh.NSW) * 64 * sizeof(float));
-    w.fwd = seq_workspace(b, d_in, n).total;
+    w.fwd = saved ? 256 : seq_workspace(b, d_in, n).total;
     w.total = w.fwd + w.ckpt + w.part_B + w.part_C + w.part_A + w.part_D + w.part_bias + w.part_du + w.part_dd +
               w.ctl + w.handoff;
     return w;
@@ -599,38 +631,64 @@ int reduce(const float* part, void* out, int64_t count, int64_t groups, hipStrea
 
 }  // namespace
 
-SS_EXPORT size_t ss_scan_bwd_workspace_bytes(int64_t b, int64_t L, int64_t d_in, int64_t n, int dtype) {
-    if (dtype != SS_F32 && dtype != SS_BF16) return 0;
-    if (!sizes_ok(b, L, d_in) || n <= 0 || n > SS_MAX_BWD_STATE || d_in > SS_MAX_CHANNELS) return 0;
-    if (b * ((d_in + 63) / 64) * bwd_slices(n) > kMaxWorkgroups || L > kMaxLength) return 0;
-    return bwd_workspace(b, L, d_in, n).total;
+namespace {
+
+bool bwd_sizes_ok(int64_t b, int64_t L, int64_t d_in, int64_t n) {
+    return sizes_ok(b, L, d_in) && n > 0 && n <= SS_MAX_BWD_STATE && d_in <= SS_MAX_CHANNELS &&
+           b * ((d_in + 63) / 64) * bwd_slices(n) <= kMaxWorkgroups && L <= kMaxLength;
 }
 
-SS_EXPORT int ss_scan_bwd_ex(const void* u, const void* delta, const float* A_log, const void* B, const void* C,
-                             const float* D, const void* z, const float* delta_bias, int delta_softplus,
-                             const float* initial_state, int discretization, const void* dy,
-                             const float* dlast_state, void* du, void* ddelta, float* dA_log, void* dB, void* dC,
-                             float* dD, void* dz, float* ddelta_bias, float* dinitial_state, int64_t b, int64_t L,
-                             int64_t d_in, int64_t n, int dtype, void* workspace, size_t workspace_bytes,
-                             void* stream) {
+}  // namespace
+
+SS_EXPORT size_t ss_scan_bwd_workspace_bytes(int64_t b, int64_t L, int64_t d_in, int64_t n, int dtype) {
+    if (dtype != SS_F32 && dtype != SS_BF16) return 0;
+    return bwd_sizes_ok(b, L, d_in, n) ? bwd_workspace(b, L, d_in, n).total : 0;
+}
+
+SS_EXPORT size_t ss_scan_bwd_saved_workspace_bytes(int64_t b, int64_t L, int64_t d_in, int64_t n, int dtype) {
+    if (dtype != SS_F32 && dtype != SS_BF16) return 0;
+    return bwd_sizes_ok(b, L, d_in, n) ? bwd_workspace(b, L, d_in, n, true).total : 0;
+}
+
+SS_EXPORT size_t ss_scan_checkpoint_bytes(int64_t b, int64_t L, int64_t d_in, int64_t n) {
+    if (!bwd_sizes_ok(b, L, d_in, n)) return 0;
+    return size_t(b) * size_t((L - 1) / ss::kCkptSteps) * size_t(n) * size_t(d_in) * 4;
+}
+
+namespace {
+
+// The backward pass.  Without saved states (ckpt_in null) it first runs the
+// forward scan again to save the state every kCkptSteps steps (and, gated,
+// to write dz); with them it starts from the checkpoints and the pre-gate
+// readout y_pre that ss_scan_fwd_save wrote, and forms dz itself.
+int scan_bwd_impl(const void* u, const void* delta, const float* A_log, const void* B, const void* C,
+                  const float* D, const void* z, const float* delta_bias, int delta_softplus,
+                  const float* initial_state, int discretization, const float* ckpt_in, const void* y_pre,
+                  const void* dy, const float* dlast_state, void* du, void* ddelta, float* dA_log, void* dB,
+                  void* dC, float* dD, void* dz, float* ddelta_bias, float* dinitial_state, int64_t b, int64_t L,
+                  int64_t d_in, int64_t n, int dtype, void* workspace, size_t workspace_bytes, bool saved,
+                  void* stream) {
     if (!u || !delta || !A_log || !B || !C || !D || !dy || !du || !ddelta || !dA_log || !dB || !dC || !dD)
         return SS_ERR_NULL;
     if (z && !dz) return SS_ERR_NULL;
+    if (saved && ((!ckpt_in && L > ss::kCkptSteps) || (z && !y_pre))) return SS_ERR_NULL;
     if (discretization != SS_DISC_EULER && discretization != SS_DISC_ZOH) return SS_ERR_MODE;
     const bool zoh = discretization == SS_DISC_ZOH;
     if (!sizes_ok(b, L, d_in) || n <= 0 || d_in > SS_MAX_CHANNELS) return SS_ERR_SHAPE;
     if (dtype != SS_F32 && dtype != SS_BF16) return SS_ERR_DTYPE;
     if (n > SS_MAX_BWD_STATE) return SS_ERR_UNSUPPORTED;
     if (b * ((d_in + 63) / 64) * bwd_slices(n) > kMaxWorkgroups || L > kMaxLength) return SS_ERR_SHAPE;
+    if (!saved) y_pre = nullptr;
     const size_t es = elem_size(dtype);
-    for (const void* p : {u, delta, B, C, z, dy, static_cast<const void*>(du), static_cast<const void*>(ddelta),
-                          static_cast<const void*>(dB), static_cast<const void*>(dC), static_cast<const void*>(dz)})
+    for (const void* p : {u, delta, B, C, z, dy, y_pre, static_cast<const void*>(du),
+                          static_cast<const void*>(ddelta), static_cast<const void*>(dB), static_cast<const void*>(dC),
+                          static_cast<const void*>(dz)})
         if (p && !aligned(p, es)) return SS_ERR_ALIGN;
     for (const void* p : {static_cast<const void*>(A_log), static_cast<const void*>(D),
                           static_cast<const void*>(delta_bias), static_cast<const void*>(initial_state),
                           static_cast<const void*>(dlast_state), static_cast<const void*>(dA_log),
                           static_cast<const void*>(dD), static_cast<const void*>(ddelta_bias),
-                          static_cast<const void*>(dinitial_state)})
+                          static_cast<const void*>(dinitial_state), static_cast<const void*>(ckpt_in)})
         if (p && !aligned(p, 4)) return SS_ERR_ALIGN;
     if (!aligned(workspace, 256)) return workspace ? SS_ERR_ALIGN : SS_ERR_WORKSPACE;
     const int64_t nel = b * L * d_in, nst = b * d_in * n;
@@ -638,12 +696,15 @@ SS_EXPORT int ss_scan_bwd_ex(const void* u, const void* delta, const float* A_lo
                          range_of(B, b * L * n, es), range_of(C, b * L * n, es), range_of(D, d_in, 4),
                          range_of(z, z ? nel : 0, es), range_of(delta_bias, delta_bias ? d_in : 0, 4),
                          range_of(initial_state, initial_state ? nst : 0, 4), range_of(dy, nel, es),
-                         range_of(dlast_state, dlast_state ? nst : 0, 4)};
+                         range_of(dlast_state, dlast_state ? nst : 0, 4),
+                         range_of(ckpt_in, saved ? int64_t(ss_scan_checkpoint_bytes(b, L, d_in, n)) : 0, 1),
+                         range_of(y_pre, y_pre ? nel : 0, es)};
     const Range outs[] = {range_of(du, nel, es), range_of(ddelta, nel, es), range_of(dA_log, d_in * n, 4),
                           range_of(dB, b * L * n, es), range_of(dC, b * L * n, es), range_of(dD, d_in, 4),
                           range_of(dz, z ? nel : 0, es), range_of(ddelta_bias, ddelta_bias ? d_in : 0, 4),
                           range_of(dinitial_state, dinitial_state ? nst : 0, 4)};
-    const size_t need = ss_scan_bwd_workspace_bytes(b, L, d_in, n, dtype);
+    const size_t need = saved ? ss_scan_bwd_saved_workspace_bytes(b, L, d_in, n, dtype)
+                              : ss_scan_bwd_workspace_bytes(b, L, d_in, n, dtype);
     if (!workspace || workspace_bytes < need) return SS_ERR_WORKSPACE;
     const Range rw = range_of(workspace, int64_t(workspace_bytes), 1);
     for (size_t i = 0; i < sizeof(outs) / sizeof(outs[0]); i++) {
@@ -656,11 +717,11 @@ SS_EXPORT int ss_scan_bwd_ex(const void* u, const void* delta, const float* A_lo
     for (const Range& r : ins)
         if (overlaps(r, rw)) return SS_ERR_ALIAS;
 
-    const BwdWorkspace w = bwd_workspace(b, L, d_in, n);
+    const BwdWorkspace w = bwd_workspace(b, L, d_in, n, saved);
     char* const base = static_cast<char*>(workspace);
     void* fwd_ws = base;
     char* at = base + w.fwd;
-    float* ckpt = reinterpret_cast<float*>(at);
+    float* ckpt = saved ? const_cast<float*>(ckpt_in) : reinterpret_cast<float*>(at);
     float* part_B = reinterpret_cast<float*>(at += w.ckpt);
     float* part_C = reinterpret_cast<float*>(at += w.part_B);
     float* part_A = reinterpret_cast<float*>(at += w.part_C);
@@ -677,35 +738,43 @@ SS_EXPORT int ss_scan_bwd_ex(const void* u, const void* delta, const float* A_lo
     // 1. The forward scan again, saving the state every kCkptSteps steps.  No
     //    y; with a gate it writes dz, the one gradient that needs the readout
     //    sum C h + D u (so the backward pass never recomputes the readout).
-    ScanParams f{};
-    f.u = u;
-    f.delta = delta;
-    f.A_log = A_log;
-    f.B = B;
-    f.C = C;
-    f.D = D;
-    f.z = z;
-    f.bias = delta_bias;
-    f.y = nullptr;
-    f.last_state = nullptr;
-    f.h0 = initial_state;
-    f.ckpt = ckpt;
-    f.dy = z ? dy : nullptr;
-    f.dz = z ? dz : nullptr;
-    f.nck = int((L - 1) / ss::kCkptSteps);
-    f.b = b;
-    f.L = L;
-    f.d_in = d_in;
-    f.n = n;
-    f.softplus = delta_softplus ? 1 : 0;
-    f.nblk_d = nblk;
-    f.K = 1;
-    f.Lseg = L;
-    f.err = err;
-    const SeqMode fm = zoh ? (z ? SeqMode::ZohDz : SeqMode::Zoh) : (z ? SeqMode::Dz : SeqMode::Euler);
-    int rc = dtype == SS_BF16 ? dispatch_seq<uint16_t>(f, fm, fwd_ws, w.fwd, st)
+    //    From saved states only the status words are cleared.
+    const int nck = int((L - 1) / ss::kCkptSteps);
+    int rc = SS_OK;
+    if (saved) {
+        hipLaunchKernelGGL(ss::scan_ctl_reset, dim3(1), dim3(64), 0, st, err, int64_t(0), err);
+        if (hipGetLastError() != hipSuccess) return SS_ERR_HIP;
+    } else {
+        ScanParams f{};
+        f.u = u;
+        f.delta = delta;
+        f.A_log = A_log;
+        f.B = B;
+        f.C = C;
+        f.D = D;
+        f.z = z;
+        f.bias = delta_bias;
+        f.y = nullptr;
+        f.last_state = nullptr;
+        f.h0 = initial_state;
+        f.ckpt = ckpt;
+        f.dy = z ? dy : nullptr;
+        f.dz = z ? dz : nullptr;
+        f.nck = nck;
+        f.b = b;
+        f.L = L;
+        f.d_in = d_in;
+        f.n = n;
+        f.softplus = delta_softplus ? 1 : 0;
+        f.nblk_d = nblk;
+        f.K = 1;
+        f.Lseg = L;
+        f.err = err;
+        const SeqMode fm = zoh ? (z ? SeqMode::ZohDz : SeqMode::Zoh) : (z ? SeqMode::Dz : SeqMode::Euler);
+        rc = dtype == SS_BF16 ? dispatch_seq<uint16_t>(f, fm, fwd_ws, w.fwd, st)
                               : dispatch_seq<float>(f, fm, fwd_ws, w.fwd, st);
-    if (rc != SS_OK) return rc;
+        if (rc != SS_OK) return rc;
+    }
 
     // 2. Backward through every chunk.
     BwdParams p{};
@@ -719,6 +788,8 @@ SS_EXPORT int ss_scan_bwd_ex(const void* u, const void* delta, const float* A_lo
     p.bias = delta_bias;
     p.h0 = initial_state;
     p.dy = dy;
+    p.ypre = z ? y_pre : nullptr;
+    p.dz = p.ypre ? dz : nullptr;
     p.dlast = dlast_state;
     p.ckpt = ckpt;
     p.du = du;
@@ -736,9 +807,9 @@ SS_EXPORT int ss_scan_bwd_ex(const void* u, const void* delta, const float* A_lo
     p.L = L;
     p.d_in = d_in;
     p.n = n;
-    p.nck = f.nck;
+    p.nck = nck;
     p.nblk_d = nblk;
-    p.softplus = f.softplus;
+    p.softplus = delta_softplus ? 1 : 0;
     p.ctl = bctl;
     p.handoff = handoff;
     p.err = err;
@@ -766,6 +837,32 @@ SS_EXPORT int ss_scan_bwd_ex(const void* u, const void* delta, const float* A_lo
     if (rc == SS_OK && ddelta_bias && delta_bias)
         rc = reduce<float>(part_bias, ddelta_bias, d_in, int64_t(K) * p.slices * b, st);
     return rc;
+}
+
+}  // namespace
+
+SS_EXPORT int ss_scan_bwd_ex(const void* u, const void* delta, const float* A_log, const void* B, const void* C,
+                             const float* D, const void* z, const float* delta_bias, int delta_softplus,
+                             const float* initial_state, int discretization, const void* dy,
+                             const float* dlast_state, void* du, void* ddelta, float* dA_log, void* dB, void* dC,
+                             float* dD, void* dz, float* ddelta_bias, float* dinitial_state, int64_t b, int64_t L,
+                             int64_t d_in, int64_t n, int dtype, void* workspace, size_t workspace_bytes,
+                             void* stream) {
+    return scan_bwd_impl(u, delta, A_log, B, C, D, z, delta_bias, delta_softplus, initial_state, discretization,
+                         nullptr, nullptr, dy, dlast_state, du, ddelta, dA_log, dB, dC, dD, dz, ddelta_bias,
+                         dinitial_state, b, L, d_in, n, dtype, workspace, workspace_bytes, false, stream);
+}
+
+SS_EXPORT int ss_scan_bwd_saved(const void* u, const void* delta, const float* A_log, const void* B, const void* C,
+                                const float* D, const void* z, const float* delta_bias, int delta_softplus,
+                                const float* initial_state, int discretization, const float* checkpoints,
+                                const void* y_pre, const void* dy, const float* dlast_state, void* du, void* ddelta,
+                                float* dA_log, void* dB, void* dC, float* dD, void* dz, float* ddelta_bias,
+                                float* dinitial_state, int64_t b, int64_t L, int64_t d_in, int64_t n, int dtype,
+                                void* workspace, size_t workspace_bytes, void* stream) {
+    return scan_bwd_impl(u, delta, A_log, B, C, D, z, delta_bias, delta_softplus, initial_state, discretization,
+                         checkpoints, y_pre, dy, dlast_state, du, ddelta, dA_log, dB, dC, dD, dz, ddelta_bias,
+                         dinitial_state, b, L, d_in, n, dtype, workspace, workspace_bytes, true, stream);
 }
 
 SS_EXPORT int ss_scan_bwd(const void* u, const void* delta, const float* A_log, const void* B, const void* C,

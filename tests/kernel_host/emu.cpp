@@ -7,7 +7,8 @@
 // (raw little-endian, the dtype the entry point expects), calls the entry
 // point with exact-size host buffers, and writes the outputs as
 // dir/<name>.out.bin.  Modes: fwd (ss_scan_fwd_ex), noalloc
-// (ss_scan_fwd_noalloc), bwd (ss_scan_bwd_ex), step (ss_state_update_ex),
+// (ss_scan_fwd_noalloc), bwd (ss_scan_bwd_ex), train (ss_scan_fwd_save then
+// ss_scan_bwd_saved), step (ss_state_update_ex),
 // cross (ss_cross_scan_fwd).  Built with AddressSanitizer and
 // UndefinedBehaviorSanitizer, so any access outside a tensor, outside the
 // launch's LDS, or any undefined arithmetic ends the run with a report.
@@ -396,7 +397,8 @@ int run(const std::string& mode) {
         save("last_state", last, nst * 4);
         return 0;
     }
-    if (mode == "bwd") {
+    if (mode == "bwd" || mode == "train") {
+        // train: ss_scan_fwd_save, then ss_scan_bwd_saved from what it kept.
         const long long b = arg("b"), L = arg("L"), d = arg("d_in"), n = arg("n");
         const size_t nel = size_t(b * L * d), nbc = size_t(b * L * n), nst = size_t(b * d * n);
         void* u = load("u", nel * es);
@@ -419,12 +421,36 @@ int run(const std::string& mode) {
         void* dz = z ? output(nel * es) : nullptr;
         float* dbias = bias ? static_cast<float*>(output(size_t(d) * 4)) : nullptr;
         float* dh0 = h0 ? static_cast<float*>(output(nst * 4)) : nullptr;
-        const size_t wsb = ss_scan_bwd_workspace_bytes(b, L, d, n, int(arg("dtype")));
-        void* ws = std::aligned_alloc(256, (wsb + 255) / 256 * 256);
-        const int rc = ss_scan_bwd_ex(u, dl, A, B, C, D, z, bias, int(arg("softplus")), h0, int(arg("zoh")), dy, dlast,
-                                      du, ddl, dA, dB, dC, dD, dz, dbias, dh0, b, L, d, n, int(arg("dtype")), ws, wsb,
-                                      nullptr);
-        std::free(ws);
+        int rc;
+        if (mode == "bwd") {
+            const size_t wsb = ss_scan_bwd_workspace_bytes(b, L, d, n, int(arg("dtype")));
+            void* ws = std::aligned_alloc(256, (wsb + 255) / 256 * 256);
+            rc = ss_scan_bwd_ex(u, dl, A, B, C, D, z, bias, int(arg("softplus")), h0, int(arg("zoh")), dy, dlast, du,
+                                ddl, dA, dB, dC, dD, dz, dbias, dh0, b, L, d, n, int(arg("dtype")), ws, wsb, nullptr);
+            std::free(ws);
+        } else {
+            const size_t ckb = ss_scan_checkpoint_bytes(b, L, d, n);
+            float* ck = static_cast<float*>(output(std::max<size_t>(ckb, 4)));
+            void* ypre = z ? output(nel * es) : nullptr;
+            void* y = output(nel * es);
+            float* last = static_cast<float*>(output(nst * 4));
+            const size_t fwb = ss_scan_fwd_workspace_bytes(b, L, d, n, int(arg("dtype")));
+            void* fws = std::aligned_alloc(256, (fwb + 255) / 256 * 256);
+            rc = ss_scan_fwd_save(u, dl, A, B, C, D, z, bias, int(arg("softplus")), h0, int(arg("zoh")), y, last, ck,
+                                  ypre, b, L, d, n, int(arg("dtype")), fws, fwb, nullptr);
+            std::free(fws);
+            if (rc != SS_OK) return rc;
+            save("y", y, nel * es);
+            save("last_state", last, nst * 4);
+            save("checkpoints", ck, ckb);
+            if (ypre) save("y_pre", ypre, nel * es);
+            const size_t wsb = ss_scan_bwd_saved_workspace_bytes(b, L, d, n, int(arg("dtype")));
+            void* ws = std::aligned_alloc(256, (wsb + 255) / 256 * 256);
+            rc = ss_scan_bwd_saved(u, dl, A, B, C, D, z, bias, int(arg("softplus")), h0, int(arg("zoh")), ck, ypre,
+                                   dy, dlast, du, ddl, dA, dB, dC, dD, dz, dbias, dh0, b, L, d, n,
+                                   int(arg("dtype")), ws, wsb, nullptr);
+            std::free(ws);
+        }
         if (rc != SS_OK) return rc;
         save("du", du, nel * es);
         save("ddelta", ddl, nel * es);
@@ -487,7 +513,7 @@ int run(const std::string& mode) {
 
 int main(int argc, char** argv) {
     if (argc != 3) {
-        std::fprintf(stderr, "usage: scan_host <fwd|noalloc|bwd|step|cross> <dir>\n");
+        std::fprintf(stderr, "usage: scan_host <fwd|noalloc|bwd|train|step|cross> <dir>\n");
         return 2;
     }
     g_dir = argv[2];

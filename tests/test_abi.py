@@ -32,7 +32,9 @@ def test_header_declares_the_entry_points():
                                            "ss_scan_bwd", "ss_scan_bwd_ex", "ss_scan_bwd_workspace_bytes", "ss_scan_fwd",
                                            "ss_scan_fwd_ex", "ss_scan_fwd_noalloc", "ss_scan_status",
                                            "ss_scan_fwd_workspace_bytes", "ss_set_test_plan", "ss_state_update",
-                                           "ss_state_update_ex", "ss_status_string"])
+                                           "ss_state_update_ex", "ss_status_string", "ss_scan_checkpoint_bytes",
+                                           "ss_scan_fwd_save", "ss_scan_bwd_saved",
+                                           "ss_scan_bwd_saved_workspace_bytes"])
 
 
 def test_library_exports_every_declared_symbol(ss):
@@ -365,3 +367,73 @@ def test_bwd_workspace_query(ss):
     q = ss.lib.ss_scan_bwd_workspace_bytes
     assert q(4, 8192, 5120, 16, 1) > 4 * 1023 * 16 * 5120 * 4
     assert q(4, 8192, 5120, 65, 1) == 0 and q(0, 1, 1, 1, 0) == 0 and q(1, 1, 1, 1, 3) == 0
+
+
+# ---- the training pair: ss_scan_fwd_save and ss_scan_bwd_saved
+
+
+def call_fwd_save(ss, a, ck=addr(12), ypre=addr(13), disc=0):
+    return ss.lib.ss_scan_fwd_save(a["u"], a["delta"], a["A_log"], a["B"], a["C"], a["D"], a["z"], a["bias"],
+                                   a["softplus"], None, disc, a["y"], a["last"], ck, ypre, a["b"], a["L"], a["d_in"],
+                                   a["n"], a["dtype"], a["ws"], a["ws_bytes"], a["stream"])
+
+
+@pytest.mark.parametrize("over,ck,ypre,code", [
+    (dict(), None, addr(13), NULL),                       # no checkpoint buffer
+    (dict(), addr(12), None, NULL),                       # gated without y_pre
+    (dict(u=None), addr(12), addr(13), NULL),
+    (dict(n=65), addr(12), addr(13), UNSUP),
+    (dict(b=0), addr(12), addr(13), SHAPE),
+    (dict(), addr(12) + 2, addr(13), ALIGN),
+    (dict(), addr(12), addr(13) + 2, ALIGN),
+    (dict(), addr(1), addr(13), ALIAS),                   # checkpoints over u
+    (dict(), addr(12), addr(9), ALIAS),                   # y_pre over y
+    (dict(), addr(12), addr(12) + 64, ALIAS),             # y_pre over the checkpoints
+    (dict(), addr(11) + 256, addr(13), ALIAS),            # checkpoints in the workspace
+    (dict(ws_bytes=100), addr(12), addr(13), WS),
+])
+def test_fwd_save_rejects(ss, over, ck, ypre, code):
+    assert call_fwd_save(ss, scan_args(**over), ck, ypre) == code
+
+
+def test_fwd_save_without_gate_needs_no_y_pre(ss):
+    # Ungated: y_pre may be NULL; only the dtype error remains.
+    assert call_fwd_save(ss, scan_args(z=None, dtype=5), addr(12), None) == DTYPE
+
+
+def call_bwd_saved(ss, a, ck=addr(22), ypre=addr(23), mode=0):
+    k1 = ("u", "delta", "A_log", "B", "C", "D", "z", "bias", "softplus", "h0")
+    k2 = ("dy", "dlast", "du", "ddelta", "dA", "dB", "dC", "dD", "dz", "dbias", "dh0", "b", "L", "d_in", "n", "dtype",
+          "ws", "ws_bytes", "stream")
+    return ss.lib.ss_scan_bwd_saved(*[a[x] for x in k1], mode, ck, ypre, *[a[x] for x in k2])
+
+
+@pytest.mark.parametrize("over,ck,ypre,code", [
+    (dict(), None, addr(23), NULL), (dict(), addr(22), None, NULL), (dict(u=None), addr(22), addr(23), NULL),
+    (dict(n=65), addr(22), addr(23), UNSUP), (dict(ws_bytes=100), addr(22), addr(23), WS),
+    (dict(), addr(22) + 2, addr(23), ALIGN), (dict(), addr(22), addr(23) + 1, ALIGN),
+    (dict(), addr(12), addr(23), ALIAS),                  # checkpoints over du
+    (dict(), addr(22), addr(18), ALIAS),                  # y_pre over dz
+    (dict(), addr(21) + 256, addr(23), ALIAS),            # checkpoints in the workspace
+])
+def test_bwd_saved_rejects(ss, over, ck, ypre, code):
+    assert call_bwd_saved(ss, bwd_args(**over), ck, ypre) == code
+
+
+def test_bwd_saved_without_gate_needs_no_y_pre(ss):
+    assert call_bwd_saved(ss, bwd_args(z=None, dz=None, dtype=7), addr(22), None) == DTYPE
+
+
+def test_training_pair_queries(ss):
+    lib = ss.lib
+    b, L, d, n = 4, 8192, 5120, 16
+    assert lib.ss_scan_checkpoint_bytes(b, L, d, n) == b * ((L - 1) // 8) * n * d * 4
+    assert lib.ss_scan_checkpoint_bytes(2, 8, 32, 16) == 0            # no checkpoint before step 8 < L
+    assert lib.ss_scan_checkpoint_bytes(2, 9, 32, 16) == 2 * 1 * 16 * 32 * 4
+    saved = lib.ss_scan_bwd_saved_workspace_bytes(b, L, d, n, 1)
+    full = lib.ss_scan_bwd_workspace_bytes(b, L, d, n, 1)
+    # The saved backward needs neither the forward pass's room nor checkpoints of its own.
+    assert 0 < saved <= full - lib.ss_scan_checkpoint_bytes(b, L, d, n)
+    for bad in ((0, 1, 1, 1), (1, 1, 1, 65), (1, 0, 1, 1)):
+        assert lib.ss_scan_checkpoint_bytes(*bad) == 0, bad
+        assert lib.ss_scan_bwd_saved_workspace_bytes(*bad, 0) == 0, bad

@@ -105,6 +105,51 @@ def test_backward_on_host(case):
         assert_close(got[k], ref[k], dt, f"host {k}")
 
 
+# The training pair: the saving forward's outputs (y, last state, the state
+# after every 8 steps, the readout before the gate) and the backward from them.
+@pytest.mark.parametrize("case", [(2, 50, 70, 16, BF16, False, True), (1, 37, 33, 40, F32, True, True),
+                                  (2, 21, 64, 8, F32, False, False)],
+                         ids=["n16-bf16-gated", "n40-f32-zoh-gated", "n8-f32-ungated"])
+def test_training_pair_on_host(case):
+    b, L, d, n, dt, zoh, gated = case
+    inp = workloads.random_scan_inputs(b, L, d, n, dt, seed=21, gated=gated, bias=True)
+    g = torch.Generator().manual_seed(22)
+    dy = torch.randn(b, L, d, generator=g).to(dt)
+    z = inp["z"] if gated else None
+    t = dict(u=inp["u"], delta=inp["delta"], A_log=inp["A_log"], B=inp["B"], C=inp["C"], D=inp["D"], z=z,
+             delta_bias=inp["delta_bias"], dy=dy)
+    args = dict(b=b, L=L, d_in=d, n=n, dtype=_code(dt), softplus=1, zoh=int(zoh), segments=2)
+    nck = (L - 1) // 8
+    grads = dict(du=((b, L, d), dt), ddelta=((b, L, d), dt), dA_log=((d, n), F32), dB=((b, L, n), dt),
+                 dC=((b, L, n), dt), dD=((d,), F32), ddelta_bias=((d,), F32))
+    if gated:
+        grads["dz"] = ((b, L, d), dt)
+    outs = dict(y=((b, L, d), dt), last_state=((b, d, n), F32), checkpoints=((b, nck, n, d), F32),
+                y_pre=((b, L, d), dt), **grads)
+    got = hk.run("train", t, args, outs)
+    y, last = oracle.scan(inp["u"], inp["delta"], inp["A_log"], inp["B"], inp["C"], inp["D"], z, inp["delta_bias"],
+                          True, zoh=zoh)
+    assert_close(got["y"], y, dt, "host y")
+    assert_close(got["last_state"], last, dt, "host last_state")
+    if gated:
+        # The readout before the gate is the ungated scan's output.
+        y_pre, _ = oracle.scan(inp["u"], inp["delta"], inp["A_log"], inp["B"], inp["C"], inp["D"], None,
+                               inp["delta_bias"], True, zoh=zoh)
+        assert_close(got["y_pre"], y_pre, dt, "host y_pre")
+    else:
+        assert "y_pre" not in got
+    for i in range(nck):
+        # Checkpoint i is the state after step 8 (i + 1): the last state of the scan cut there.
+        s = slice(0, 8 * (i + 1))
+        _, h = oracle.scan(inp["u"][:, s], inp["delta"][:, s], inp["A_log"], inp["B"][:, s], inp["C"][:, s],
+                           inp["D"], None, inp["delta_bias"], True, zoh=zoh)
+        assert_close(got["checkpoints"][:, i].transpose(1, 2), h, dt, f"host checkpoint {i}")
+    ref = oracle.scan_bwd(inp["u"], inp["delta"], inp["A_log"], inp["B"], inp["C"], inp["D"], z,
+                          inp["delta_bias"], True, None, dy, None, zoh=zoh)
+    for k in grads:
+        assert_close(got[k], ref[k], dt, f"host {k}")
+
+
 # n = 4 LPC runs the vector kernel (LPC lanes per channel, LPC batch rows per
 # workgroup) for LPC = 1, 2, 4, 8, 16; n = 5 and n = 3 run the any-n kernel.  Batch
 # sizes leave a partial row group and channel counts a partial tile.
