@@ -505,34 +505,39 @@ def pin_scan_bwd(lib):
             assert abs(fd - an) <= 1e-6 * (1 + abs(an)), f"finite differences {kw} zoh={zoh}: {fd} vs {an}"
 
 
-def pin_einsum_transcription(lib):
-    """A second, independent formulation in torch float64: the discretised tensors formed whole with einsum
-    (mhpn.cn page, section 3: exp(delta A) over (b, l, d_in, n) and delta B u), then the update-then-read-out
-    loop of section 4 and the skip of section 5 -- the unfused method the kernels avoid materialising."""
-    import torch
-
-    for seed, kw in enumerate([dict(), dict(n=1, gated=False, bias=False), dict(b=3, L=11, d_in=5, n=6)]):
-        c = random_case(700 + seed, **kw)
-        t = {k: (None if c[k] is None else torch.tensor(c[k])) for k in ("u", "delta", "A_log", "B", "C", "D", "z",
-                                                                        "delta_bias")}
-        dl = t["delta"] + (t["delta_bias"] if t["delta_bias"] is not None else 0.0)
-        dl = torch.nn.functional.softplus(dl)
-        A = -torch.exp(t["A_log"])
-        dA = torch.exp(torch.einsum("bld,dn->bldn", dl, A))
-        dBu = torch.einsum("bld,bln,bld->bldn", dl, t["B"], t["u"])
-        x = torch.zeros(dA.shape[0], dA.shape[2], dA.shape[3], dtype=torch.float64)
-        ys = []
-        for i in range(dA.shape[1]):
-            x = dA[:, i] * x + dBu[:, i]
-            ys.append(torch.einsum("bdn,bn->bd", x, t["C"][:, i]))
-        y = torch.stack(ys, dim=1) + t["u"] * t["D"]
-        if t["z"] is not None:
-            y = y * torch.nn.functional.silu(t["z"])
+def pin_segment_sum_closed_form(lib):
+    """A second formulation with no recurrence at all, in numpy float64: since A is constant in time, the product
+    of the decays exp(delta'_r A) over r = s+1..t is exp(A (S_t - S_s)) with S the cumulative sum of delta' along
+    the sequence, so h_t = sum_{s<=t} exp(A (S_t - S_s)) delta'_s B_s u_s (a lower-triangular matrix of those
+    factors applied to the inputs), and y_t = sum_k C_t,k h_t,k + D u_t, gated.  The oracle's sequential loop
+    (update, then read out) must agree with it, and its last state with h_(L-1)."""
+    for seed, kw in enumerate([dict(), dict(n=1, gated=False, bias=False), dict(b=3, L=11, d_in=5, n=6),
+                               dict(L=40, softplus=False)]):
+        c = random_case(900 + seed, **kw)
+        if not c["delta_softplus"]:
+            # Without the softplus the step size is delta + bias itself: keep it positive.
+            c["delta"] = np.abs(c["delta"]) * 0.1 + 0.01
+            if c["delta_bias"] is not None:
+                c["delta_bias"] = np.abs(c["delta_bias"]) * 0.01
+        x = c["delta"] + (c["delta_bias"] if c["delta_bias"] is not None else 0.0)
+        dl = np.logaddexp(0.0, x) if c["delta_softplus"] else x                   # (b, L, d)
+        A = -np.exp(c["A_log"])                                                   # (d, n)
+        S = np.cumsum(dl, axis=1)                                                 # (b, L, d)
+        L = dl.shape[1]
+        tri = np.tril(np.ones((L, L), bool))                                      # s <= t
+        # E[b, t, s, d, k] = exp(A[d, k] (S[b, t, d] - S[b, s, d])) for s <= t, else 0
+        diff = S[:, :, None, :] - S[:, None, :, :]                                 # (b, t, s, d)
+        E = np.where(tri[None, :, :, None, None], np.exp(diff[..., None] * A[None, None, None]), 0.0)
+        inp = (dl * c["u"])[:, :, :, None] * c["B"][:, :, None, :]                 # (b, s, d, k)
+        h = np.einsum("btsdk,bsdk->btdk", E, inp)                                 # (b, t, d, k)
+        y = np.einsum("btdk,btk->btd", h, c["C"]) + c["D"] * c["u"]
+        if c["z"] is not None:
+            y = y * c["z"] / (1.0 + np.exp(-c["z"]))
         yo, lo = run(c, lib)
-        _close(yo, y.numpy(), rtol=1e-12, atol=1e-13, what=f"einsum transcription y {kw}")
-        _close(lo, x.numpy(), rtol=1e-12, atol=1e-13, what=f"einsum transcription last state {kw}")
+        _close(yo, y, rtol=1e-11, atol=1e-12, what=f"segment-sum closed form y {kw}")
+        _close(lo, h[:, -1], rtol=1e-11, atol=1e-12, what=f"segment-sum closed form last state {kw}")
 
 
 ALL_PINS = [pin_softplus_silu, pin_hand_worked, pin_brute_force, pin_geometric_closed_form, pin_limits,
             pin_skip_and_gate, pin_linearity_causality, pin_step_matches_scan, pin_bias_placement,
-            pin_initial_state, pin_zoh, pin_conv_update, pin_cross_scan, pin_scan_bwd, pin_einsum_transcription]
+            pin_initial_state, pin_zoh, pin_conv_update, pin_cross_scan, pin_scan_bwd, pin_segment_sum_closed_form]
