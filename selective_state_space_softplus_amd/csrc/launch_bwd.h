@@ -15,12 +15,31 @@ int launch_bwd(ss::BwdParams p, bool gate, bool zoh, hipStream_t st, int* segmen
     constexpr int threads = (SC + 4) * 64;
     constexpr int T = ss::kCkptSteps;
     using Kern = void (*)(ss::BwdParams);
-    static constexpr Kern kernels[8] = {
-        ss::scan_bwd<TIn, SC, NSW, SL, false, false, false>, ss::scan_bwd<TIn, SC, NSW, SL, false, true, false>,
-        ss::scan_bwd<TIn, SC, NSW, SL, true, false, false>,  ss::scan_bwd<TIn, SC, NSW, SL, true, true, false>,
-        ss::scan_bwd<TIn, SC, NSW, SL, false, false, true>,  ss::scan_bwd<TIn, SC, NSW, SL, false, true, true>,
-        ss::scan_bwd<TIn, SC, NSW, SL, true, false, true>,   ss::scan_bwd<TIn, SC, NSW, SL, true, true, true>};
-    const Kern kern = kernels[(zoh ? 4 : 0) | (p.softplus ? 2 : 0) | (gate ? 1 : 0)];
+    static constexpr Kern kernels[16] = {
+        ss::scan_bwd<TIn, SC, NSW, SL, false, false, false, false>,
+        ss::scan_bwd<TIn, SC, NSW, SL, false, true, false, false>,
+        ss::scan_bwd<TIn, SC, NSW, SL, true, false, false, false>,
+        ss::scan_bwd<TIn, SC, NSW, SL, true, true, false, false>,
+        ss::scan_bwd<TIn, SC, NSW, SL, false, false, true, false>,
+        ss::scan_bwd<TIn, SC, NSW, SL, false, true, true, false>,
+        ss::scan_bwd<TIn, SC, NSW, SL, true, false, true, false>,
+        ss::scan_bwd<TIn, SC, NSW, SL, true, true, true, false>,
+        ss::scan_bwd<TIn, SC, NSW, SL, false, false, false, true>,
+        ss::scan_bwd<TIn, SC, NSW, SL, false, true, false, true>,
+        ss::scan_bwd<TIn, SC, NSW, SL, true, false, false, true>,
+        ss::scan_bwd<TIn, SC, NSW, SL, true, true, false, true>,
+        ss::scan_bwd<TIn, SC, NSW, SL, false, false, true, true>,
+        ss::scan_bwd<TIn, SC, NSW, SL, false, true, true, true>,
+        ss::scan_bwd<TIn, SC, NSW, SL, true, false, true, true>,
+        ss::scan_bwd<TIn, SC, NSW, SL, true, true, true, true>};
+    // Channel pairs: an element thread's two channels adjacent, so each row's
+    // two elements move in one access; needs d_in even and every per-element
+    // tensor aligned to two elements.
+    auto pair_ok = [](const void* q) { return !q || aligned(q, 2 * sizeof(TIn)); };
+    const bool pr = p.d_in % 2 == 0 && pair_ok(p.u) && pair_ok(p.delta) && (!gate || pair_ok(p.z)) &&
+                    pair_ok(p.dy) && pair_ok(p.ypre) && pair_ok(p.dz) && pair_ok(p.du) && pair_ok(p.ddelta) &&
+                    (!p.part_du || aligned(p.part_du, 8)) && (!p.part_dd || aligned(p.part_dd, 8));
+    const Kern kern = kernels[(pr ? 8 : 0) | (zoh ? 4 : 0) | (p.softplus ? 2 : 0) | (gate ? 1 : 0)];
     const size_t lds = ss::BwdLds<SC, SC * NSW>::bytes;
     const int64_t G = p.b * p.nblk_d * p.slices;
     const int cus = device_cus();

@@ -142,7 +142,7 @@ struct BwdLds {
     static constexpr int bytes = off_ticket + 16;
 };
 
-template <typename TIn, int SC, int NSW, bool SL, bool SP, bool GATE, bool ZOH>
+template <typename TIn, int SC, int NSW, bool SL, bool SP, bool GATE, bool ZOH, bool PR>
 __global__ __launch_bounds__((SC + 4) * 64) void scan_bwd(const BwdParams p) {
     constexpr int T = kCkptSteps;
     constexpr int NE = 4 * 64;                     // element threads
@@ -239,19 +239,25 @@ __global__ __launch_bounds__((SC + 4) * 64) void scan_bwd(const BwdParams p) {
         }
     }
 
-    // Element waves: thread owns step row er of a chunk and channels ec + i TPR
-    // (i < V) of the group, so consecutive lanes take consecutive channels.
+    // Element waves: thread owns step row er of a chunk and channels cofs(i)
+    // (i < V) of the group: ec + i TPR, or with PR (d_in even, every
+    // per-element tensor aligned to two elements) the adjacent pair 2 ec,
+    // 2 ec + 1, whose two elements of a row are one 4-byte (bf16) or 8-byte
+    // (fp32) load or store.  Either way consecutive lanes take consecutive
+    // channels.
+    static_assert(!PR || V == 2, "channel pairs");
     const int etid = rec ? 0 : tid - SC * 64;
     const int er = etid / TPR;
     const int ec = etid - er * TPR;
+    auto cofs = [&](int i) __attribute__((always_inline)) { return PR ? 2 * ec + i : ec + i * TPR; };
     bool evok[V];
 #pragma unroll
-    for (int i = 0; i < V; i++) evok[i] = !rec && dbase + ec + i * TPR < d_in;
+    for (int i = 0; i < V; i++) evok[i] = !rec && dbase + cofs(i) < d_in;
     float Dv[V], bias_v[V], accD[V], accBias[V];
 #pragma unroll
     for (int i = 0; i < V; i++) {
-        Dv[i] = evok[i] && slice == 0 ? p.D[dbase + ec + i * TPR] : 0.0f;   // the D term once
-        bias_v[i] = (evok[i] && p.bias) ? p.bias[dbase + ec + i * TPR] : 0.0f;
+        Dv[i] = evok[i] && slice == 0 ? p.D[dbase + cofs(i)] : 0.0f;   // the D term once
+        bias_v[i] = (evok[i] && p.bias) ? p.bias[dbase + cofs(i)] : 0.0f;
         accD[i] = accBias[i] = 0.0f;
     }
 
@@ -279,9 +285,9 @@ __global__ __launch_bounds__((SC + 4) * 64) void scan_bwd(const BwdParams p) {
 
     // Per-thread parts of the element, B/C and entering-state addresses, and
     // which of them exist whatever the chunk.
-    uint32_t off_row[V];                           // (er, dbase + ec + i TPR) from (chunk row 0, dbase)
+    uint32_t off_row[V];                           // (er, dbase + cofs(i)) from (chunk row 0, dbase)
 #pragma unroll
-    for (int i = 0; i < V; i++) off_row[i] = evok[i] ? uint32_t(er * d_in + ec + i * TPR) * uint32_t(ES) : 0u;
+    for (int i = 0; i < V; i++) off_row[i] = evok[i] ? uint32_t(er * d_in + cofs(i)) * uint32_t(ES) : 0u;
     int bc_row[EBC];                               // step row j of the B/C word, -1 if none
     uint32_t off_bc[EBC];                          // (j, kk) from (chunk row 0, state 0)
 #pragma unroll
@@ -329,6 +335,37 @@ __global__ __launch_bounds__((SC + 4) * 64) void scan_bwd(const BwdParams p) {
         const TIn* q = static_cast<const TIn*>(base) + idx;
         return RawIn::load(reinterpret_cast<const TIn*>(reinterpret_cast<const char*>(q) + boff), 0);
     };
+    // PR: both elements of the thread's row in one access (bf16: the pair's
+    // 32-bit word in w[0]; fp32: the two floats).
+    auto ld_pair = [&](Word* w, const void* base, int64_t idx, uint32_t boff) __attribute__((always_inline)) {
+        const char* q = reinterpret_cast<const char*>(static_cast<const TIn*>(base) + idx) + boff;
+        if constexpr (ES == 2) {
+            w[0] = *reinterpret_cast<const uint32_t*>(q);
+        } else {
+            const float2 v = *reinterpret_cast<const float2*>(q);
+            w[0] = v.x;
+            w[1] = v.y;
+        }
+    };
+    // Element i of a thread's row as loaded, widened to fp32.
+    auto raw_f = [&](const Word* w, int i) __attribute__((always_inline)) -> float {
+        if constexpr (PR && ES == 2) return i == 0 ? __uint_as_float(w[0] << 16) : __uint_as_float(w[0] & 0xffff0000u);
+        else return RawIn::f(w[i]);
+    };
+    // Store of the thread's V values of one row of a (b, L, d_in) tensor
+    // (rb: the chunk's row base), element i only where ok_i.
+    auto store_row = [&](void* base, int64_t rb, const float* v, bool ok0, bool ok1) __attribute__((always_inline)) {
+        TIn* q = static_cast<TIn*>(base) + rb;
+        if constexpr (PR) {
+            if (!ok0) return;
+            char* a = reinterpret_cast<char*>(q) + off_row[0];
+            if constexpr (ES == 2) *reinterpret_cast<uint32_t*>(a) = f32x2_to_bf16x2(v[0], v[1]);
+            else *reinterpret_cast<float2*>(a) = make_float2(v[0], v[1]);
+        } else {
+            if (ok0) Elem<TIn>::store(reinterpret_cast<TIn*>(reinterpret_cast<char*>(q) + off_row[0]), 0, v[0]);
+            if (ok1) Elem<TIn>::store(reinterpret_cast<TIn*>(reinterpret_cast<char*>(q) + off_row[1]), 0, v[1]);
+        }
+    };
     auto row_ok = [&](int k) __attribute__((always_inline)) { return k >= kc0 && k * T + er < L; };
     auto bc_ok = [&](int k, int m) __attribute__((always_inline)) {
         return k >= kc0 && bc_row[m] >= 0 && k * T + bc_row[m] < L;
@@ -339,14 +376,23 @@ __global__ __launch_bounds__((SC + 4) * 64) void scan_bwd(const BwdParams p) {
     auto load_chunk = [&](Chunk& r, int k) __attribute__((always_inline)) {       // issue the global loads of chunk k
         const bool rv = row_ok(k);
         const int64_t rb = row_base(k);
+        if constexpr (PR) {
+            const uint32_t o = rv ? off_row[0] : 0u;
+            ld_pair(r.u, p.u, rb, o);
+            ld_pair(r.dl, p.delta, rb, o);
+            if (GATE) ld_pair(r.z, p.z, rb, o);
+            ld_pair(r.dy, p.dy, rb, o);
+            if (GATE && p.ypre) ld_pair(r.yp, p.ypre, rb, o);
+        } else {
 #pragma unroll
-        for (int i = 0; i < V; i++) {
-            const uint32_t o = rv ? off_row[i] : 0u;
-            r.u[i] = ld(p.u, rb, o);
-            r.dl[i] = ld(p.delta, rb, o);
-            if (GATE) r.z[i] = ld(p.z, rb, o);
-            r.dy[i] = ld(p.dy, rb, o);
-            if (GATE && p.ypre) r.yp[i] = ld(p.ypre, rb, o);
+            for (int i = 0; i < V; i++) {
+                const uint32_t o = rv ? off_row[i] : 0u;
+                r.u[i] = ld(p.u, rb, o);
+                r.dl[i] = ld(p.delta, rb, o);
+                if (GATE) r.z[i] = ld(p.z, rb, o);
+                r.dy[i] = ld(p.dy, rb, o);
+                if (GATE && p.ypre) r.yp[i] = ld(p.ypre, rb, o);
+            }
         }
         const int64_t bb = (brow + int64_t(max(k, kc0)) * T) * n;
 #pragma unroll
@@ -367,30 +413,32 @@ __global__ __launch_bounds__((SC + 4) * 64) void scan_bwd(const BwdParams p) {
     // Prepare chunk k from its raw values: LDS ring slots s3 (of 3) and s2 (of 2).
     auto prepare = [&](const Chunk& r, Keep& kp, int k, int s3, int s2) __attribute__((always_inline)) {
         const bool rv = row_ok(k);
+        float dzv[V];
 #pragma unroll
         for (int i = 0; i < V; i++) {
             const bool ok = rv && evok[i];
-            const float u = ok ? RawIn::f(r.u[i]) : 0.0f;
-            const float x = (ok ? RawIn::f(r.dl[i]) : 0.0f) + bias_v[i];
-            const float z = (GATE && ok) ? RawIn::f(r.z[i]) : 0.0f;
-            const float dy = ok ? RawIn::f(r.dy[i]) : 0.0f;
+            const float u = ok ? raw_f(r.u, i) : 0.0f;
+            const float x = (ok ? raw_f(r.dl, i) : 0.0f) + bias_v[i];
+            const float z = (GATE && ok) ? raw_f(r.z, i) : 0.0f;
+            const float dy = ok ? raw_f(r.dy, i) : 0.0f;
             const float dl = ok ? (SP ? softplus(x) : x) : 0.0f;
             // dy' = dy silu(z); from saved states also dz = dy y' silu'(z),
             // silu'(z) = sigmoid(z) (1 + z (1 - sigmoid(z))).
             const float sg = GATE ? rcp_hw(1.0f + exp2_hw(-z * kLog2e)) : 1.0f;
             const float dyp = GATE ? dy * (z * sg) : dy;
-            if (GATE && p.ypre && ok) {
-                const float dzv = dy * RawIn::f(r.yp[i]) * sg * fmaf(z, 1.0f - sg, 1.0f);
+            dzv[i] = (GATE && p.ypre) ? dy * raw_f(r.yp, i) * sg * fmaf(z, 1.0f - sg, 1.0f) : 0.0f;
+            if (!PR && GATE && p.ypre && ok) {
                 TIn* q = static_cast<TIn*>(p.dz) + row_base(k);
-                Elem<TIn>::store(reinterpret_cast<TIn*>(reinterpret_cast<char*>(q) + off_row[i]), 0, dzv);
+                Elem<TIn>::store(reinterpret_cast<TIn*>(reinterpret_cast<char*>(q) + off_row[i]), 0, dzv[i]);
             }
-            const int e = (s3 * T + er) * 64 + ec + i * TPR;
+            const int e = (s3 * T + er) * 64 + cofs(i);
             s_prep[e] = dl;
             s_prep[PL + e] = ZOH ? u : dl * u;
             s_prep[2 * PL + e] = dyp;
             s_prep[3 * PL + e] = u;
             kp.x[i] = x;
         }
+        if (PR && GATE && p.ypre) store_row(p.dz, row_base(k), dzv, rv && evok[0], rv && evok[V - 1]);
 #pragma unroll
         for (int m = 0; m < EBC; m++) {
             const int f = m * NE + etid;
@@ -414,15 +462,16 @@ __global__ __launch_bounds__((SC + 4) * 64) void scan_bwd(const BwdParams p) {
         const bool rv = row_ok(k);
         const int64_t rb = row_base(k);
         // This thread's (step row, channel) in the partials of wave 0; wave w at + w T 64.
-        const float2* pp = s_part + (s2 * SC * T + er) * 64 + ec;
+        const float2* pp = s_part + (s2 * SC * T + er) * 64;
         float2 q[SC][V];
 #pragma unroll
         for (int w = 0; w < SC; w++)
 #pragma unroll
-            for (int i = 0; i < V; i++) q[w][i] = pp[w * T * 64 + i * TPR];
+            for (int i = 0; i < V; i++) q[w][i] = pp[w * T * 64 + cofs(i)];
+        float du_v[V], dd_v[V];
 #pragma unroll
         for (int i = 0; i < V; i++) {
-            const int e = (s3 * T + er) * 64 + ec + i * TPR;
+            const int e = (s3 * T + er) * 64 + cofs(i);
             const float4 pr = make_float4(s_prep[e], 0.0f, s_prep[2 * PL + e], s_prep[3 * PL + e]);   // (Delta, -, dy', u)
             float S1 = q[0][i].x, S2 = q[0][i].y;
 #pragma unroll
@@ -433,24 +482,42 @@ __global__ __launch_bounds__((SC + 4) * 64) void scan_bwd(const BwdParams p) {
             // Euler: S1 = sum g B, dDelta = S2 + u S1, du = Delta S1 + dy' D; the hold:
             // S1 = sum g beta B, S2 already holds the input term, du = S1 + dy' D.
             const float dDelta = ZOH ? S2 : fmaf(pr.w, S1, S2);
-            const float ddl = SP ? dDelta * rcp_hw(1.0f + exp2_hw(-kp.x[i] * kLog2e)) : dDelta;
+            const float sgx = SP ? rcp_hw(1.0f + exp2_hw(-kp.x[i] * kLog2e)) : 1.0f;   // softplus' = sigmoid
+            const float ddl = SP ? dDelta * sgx : dDelta;
             const float du = ZOH ? fmaf(pr.z, Dv[i], S1) : fmaf(pr.x, S1, pr.z * Dv[i]);
+            du_v[i] = du;
+            dd_v[i] = ddl;
             if (rv && evok[i]) {
-                if constexpr (!SL) {
-                    auto st = [&](void* base, float v) __attribute__((always_inline)) {
-                        TIn* q = static_cast<TIn*>(base) + rb;
-                        Elem<TIn>::store(reinterpret_cast<TIn*>(reinterpret_cast<char*>(q) + off_row[i]), 0, v);
-                    };
-                    st(p.du, du);
-                    st(p.ddelta, ddl);
-                } else {
-                    // This slice's parts of du and ddelta (both are linear in S1, S2).
-                    const int64_t e = int64_t(slice) * p.b * L * d_in + rb + off_row[i] / uint32_t(ES);
-                    p.part_du[e] = du;
-                    p.part_dd[e] = ddl;
+                if constexpr (!PR) {
+                    if constexpr (!SL) {
+                        auto st = [&](void* base, float v) __attribute__((always_inline)) {
+                            TIn* q = static_cast<TIn*>(base) + rb;
+                            Elem<TIn>::store(reinterpret_cast<TIn*>(reinterpret_cast<char*>(q) + off_row[i]), 0, v);
+                        };
+                        st(p.du, du);
+                        st(p.ddelta, ddl);
+                    } else {
+                        // This slice's parts of du and ddelta (both are linear in S1, S2).
+                        const int64_t e = int64_t(slice) * p.b * L * d_in + rb + off_row[i] / uint32_t(ES);
+                        p.part_du[e] = du;
+                        p.part_dd[e] = ddl;
+                    }
                 }
                 if (slice == 0) accD[i] = fmaf(pr.z, pr.w, accD[i]);
-                accBias[i] += ddl;
+                // Written as the FMA it is, so that no kernel form is left to
+                // the compiler's choice of contracting the product into it.
+                accBias[i] = SP ? fmaf(dDelta, sgx, accBias[i]) : accBias[i] + dDelta;
+            }
+        }
+        if constexpr (PR) {
+            const bool ok = rv && evok[0];   // d_in even: both channels or neither
+            if constexpr (!SL) {
+                store_row(p.du, rb, du_v, ok, ok);
+                store_row(p.ddelta, rb, dd_v, ok, ok);
+            } else if (ok) {
+                const int64_t e = int64_t(slice) * p.b * L * d_in + rb + off_row[0] / uint32_t(ES);
+                *reinterpret_cast<float2*>(p.part_du + e) = make_float2(du_v[0], du_v[1]);
+                *reinterpret_cast<float2*>(p.part_dd + e) = make_float2(dd_v[0], dd_v[1]);
             }
         }
         // dB, dC of the chunk's rows: T * n consecutive values of each.
@@ -615,8 +682,8 @@ __global__ __launch_bounds__((SC + 4) * 64) void scan_bwd(const BwdParams p) {
         float* s_red = reinterpret_cast<float*>(lds + Lds::off_prep);   // [T][64][2]
 #pragma unroll
         for (int i = 0; i < V; i++) {
-            s_red[(er * 64 + ec + i * TPR) * 2] = accD[i];
-            s_red[(er * 64 + ec + i * TPR) * 2 + 1] = accBias[i];
+            s_red[(er * 64 + cofs(i)) * 2] = accD[i];
+            s_red[(er * 64 + cofs(i)) * 2 + 1] = accBias[i];
         }
         barrier_lds();
         if (etid < 64 && dbase + etid < d_in) {

@@ -154,6 +154,43 @@ def test_bwd_is_deterministic(ss):
         assert torch.equal(a[k], b[k]), k
 
 
+def _shifted(t):
+    """The same values in a view that starts one element into a larger buffer: element-aligned, but not aligned
+    to two elements, so the backward takes its one-channel-at-a-time element mapping instead of channel pairs."""
+    buf = torch.empty(t.numel() + 1, dtype=t.dtype, device=t.device)
+    v = buf[1:].view(t.shape)
+    v.copy_(t)
+    return v
+
+
+@pytest.mark.parametrize("dtype,zoh,n", [(BF16, False, 16), (F32, False, 16), (BF16, True, 8), (F32, False, 40)])
+def test_bwd_channel_pairs_match_single_channels(ss, dtype, zoh, n):
+    """With d_in even and aligned tensors the element threads take adjacent channel pairs; shifted by one element
+    they take channels one at a time.  Both give the same gradients bit for bit, from recomputation and from
+    saved states."""
+    say(f"bwd channel pairs vs single channels dtype={dtype} zoh={zoh} n={n}")
+    inp = to_dev(workloads.random_scan_inputs(2, 300, 130, n, dtype, seed=80 + n, gated=True, bias=True))
+    dy = torch.randn(2, 300, 130, generator=torch.Generator().manual_seed(81)).to(dtype).to(DEV)
+    sh = dict(inp)
+    for k in ("u", "delta", "z"):
+        sh[k] = _shifted(inp[k])
+    dys = _shifted(dy)
+    a = grads_gpu(ss, inp, dy, zoh=zoh)
+    b = grads_gpu(ss, sh, dys, zoh=zoh)
+    for k in a:
+        if a[k] is not None:
+            assert torch.equal(a[k], b[k]), k
+    args = lambda g: (g["u"], g["delta"], g["A_log"], g["B"], g["C"], g["D"])  # noqa: E731
+    for g, d in ((inp, dy), (sh, dys)):
+        g["saved"] = ss.scan_fwd_save(*args(g), g["z"], g["delta_bias"], True, zoh=zoh)
+    sa = ss.scan_bwd(*args(inp), dy, inp["z"], inp["delta_bias"], True, zoh=zoh, saved=inp["saved"])
+    sb = ss.scan_bwd(*args(sh), dys, sh["z"], sh["delta_bias"], True, zoh=zoh, saved=sh["saved"])
+    torch.cuda.synchronize()
+    for k in sa:
+        if sa[k] is not None:
+            assert torch.equal(sa[k], sb[k]), f"saved {k}"
+
+
 def test_autograd_function(ss):
     """selective_scan under torch autograd: y.backward(dy) gives scan_bwd's gradients."""
     say("autograd function")
