@@ -29,3 +29,16 @@ def test_package_never_refers_to_the_oracle():
             if name.endswith((".py", ".hip", ".h", ".cpp")):
                 text = open(os.path.join(dirpath, name), encoding="utf-8").read()
                 assert "oracle" not in text.lower(), os.path.join(dirpath, name)
+
+
+def test_traffic_record_is_readable_by_the_bench():
+    """profiles/traffic.json holds the counter-measured HBM bytes of the scan kernel under the key bench.py looks up,
+    with the fields it reports; whether its source hash is current is the bench's business (it reports null
+    otherwise)."""
+    import json
+
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    rec = json.load(open(os.path.join(root, "profiles", "traffic.json")))["scan_seq"]
+    for key in ("kernel", "bytes_per_launch", "algorithmic_bytes", "source_hash", "fetch_scale", "write_scale"):
+        assert key in rec, key
+    assert 0.9 < rec["bytes_per_launch"] / rec["algorithmic_bytes"] < 3.0
