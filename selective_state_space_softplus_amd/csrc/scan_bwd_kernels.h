@@ -413,7 +413,7 @@ __global__ __launch_bounds__((SC + 4) * 64) void scan_bwd(const BwdParams p) {
     // Prepare chunk k from its raw values: LDS ring slots s3 (of 3) and s2 (of 2).
     auto prepare = [&](const Chunk& r, Keep& kp, int k, int s3, int s2) __attribute__((always_inline)) {
         const bool rv = row_ok(k);
-        float dzv[V];
+        float dzv[V], pv[4][V];
 #pragma unroll
         for (int i = 0; i < V; i++) {
             const bool ok = rv && evok[i];
@@ -431,12 +431,22 @@ __global__ __launch_bounds__((SC + 4) * 64) void scan_bwd(const BwdParams p) {
                 TIn* q = static_cast<TIn*>(p.dz) + row_base(k);
                 Elem<TIn>::store(reinterpret_cast<TIn*>(reinterpret_cast<char*>(q) + off_row[i]), 0, dzv[i]);
             }
-            const int e = (s3 * T + er) * 64 + cofs(i);
-            s_prep[e] = dl;
-            s_prep[PL + e] = ZOH ? u : dl * u;
-            s_prep[2 * PL + e] = dyp;
-            s_prep[3 * PL + e] = u;
+            pv[0][i] = dl;
+            pv[1][i] = ZOH ? u : dl * u;
+            pv[2][i] = dyp;
+            pv[3][i] = u;
             kp.x[i] = x;
+        }
+        // The four planes: one 8-byte write per plane for a channel pair.
+#pragma unroll
+        for (int pl = 0; pl < 4; pl++) {
+            float* dst = s_prep + pl * PL + (s3 * T + er) * 64;
+            if constexpr (PR) {
+                *reinterpret_cast<float2*>(dst + cofs(0)) = make_float2(pv[pl][0], pv[pl][1]);
+            } else {
+#pragma unroll
+                for (int i = 0; i < V; i++) dst[cofs(i)] = pv[pl][i];
+            }
         }
         if (PR && GATE && p.ypre) store_row(p.dz, row_base(k), dzv, rv && evok[0], rv && evok[V - 1]);
 #pragma unroll
@@ -464,15 +474,36 @@ __global__ __launch_bounds__((SC + 4) * 64) void scan_bwd(const BwdParams p) {
         // This thread's (step row, channel) in the partials of wave 0; wave w at + w T 64.
         const float2* pp = s_part + (s2 * SC * T + er) * 64;
         float2 q[SC][V];
+        float pq[3][V];                            // Delta, dy', u of the thread's elements
+        const float* sp = s_prep + (s3 * T + er) * 64;
+        if constexpr (PR) {
+            // A channel pair's partials and planes as 16- and 8-byte reads.
 #pragma unroll
-        for (int w = 0; w < SC; w++)
+            for (int w = 0; w < SC; w++) {
+                const float4 v = *reinterpret_cast<const float4*>(pp + w * T * 64 + cofs(0));
+                q[w][0] = make_float2(v.x, v.y);
+                q[w][1] = make_float2(v.z, v.w);
+            }
 #pragma unroll
-            for (int i = 0; i < V; i++) q[w][i] = pp[w * T * 64 + cofs(i)];
+            for (int j = 0; j < 3; j++) {
+                const float2 v = *reinterpret_cast<const float2*>(sp + (j == 0 ? 0 : j + 1) * PL + cofs(0));
+                pq[j][0] = v.x;
+                pq[j][1] = v.y;
+            }
+        } else {
+#pragma unroll
+            for (int w = 0; w < SC; w++)
+#pragma unroll
+                for (int i = 0; i < V; i++) q[w][i] = pp[w * T * 64 + cofs(i)];
+#pragma unroll
+            for (int j = 0; j < 3; j++)
+#pragma unroll
+                for (int i = 0; i < V; i++) pq[j][i] = sp[(j == 0 ? 0 : j + 1) * PL + cofs(i)];
+        }
         float du_v[V], dd_v[V];
 #pragma unroll
         for (int i = 0; i < V; i++) {
-            const int e = (s3 * T + er) * 64 + cofs(i);
-            const float4 pr = make_float4(s_prep[e], 0.0f, s_prep[2 * PL + e], s_prep[3 * PL + e]);   // (Delta, -, dy', u)
+            const float4 pr = make_float4(pq[0][i], 0.0f, pq[1][i], pq[2][i]);   // (Delta, -, dy', u)
             float S1 = q[0][i].x, S2 = q[0][i].y;
 #pragma unroll
             for (int w = 1; w < SC; w++) {
