@@ -679,9 +679,17 @@ __global__ __launch_bounds__((SC + kSeqElemWaves + 1) * 64) void scan_seq(const 
 #pragma unroll
     for (int q = 0; q < NSW; q++)
         invA[q] = (ZOH && rec && dv && n0 + q < n) ? inv_a_from_alog(p.A_log[(prow + d) * n + n0 + q]) : 0.0f;
-    // Checkpoints for the backward pass: state n0 of channel dbase in checkpoint 0 (wave-uniform).
-    float* const ck0 = p.ckpt ? p.ckpt + (int64_t(bi) * p.nck * n + n0) * d_in + dbase : nullptr;
+    // Checkpoints for the backward pass.  Checkpoint i holds the state after
+    // step kCkptSteps (i + 1); t_begin and T are multiples of kCkptSteps, so
+    // they fall at fixed steps of every chunk, and the offset of the next one
+    // is kept as a running (wave-uniform) count rather than formed from the
+    // step index at every store.  A checkpoint is written only for steps of
+    // this segment (past its end the state is not its own) and not after the
+    // last step.
+    float* const ck_lane = p.ckpt ? p.ckpt + int64_t(n0) * d_in + dbase + lane : nullptr;
     const int64_t ck_stride = int64_t(n) * d_in;   // floats between consecutive checkpoints
+    int64_t ck_off = (int64_t(bi) * p.nck + t_begin / kCkptSteps - 1) * ck_stride;   // before the segment's first
+    const int ck_last = min(t_end, L - 1);         // checkpoints after steps s <= ck_last are kept
     auto rec_chunk = [&](auto ph, int c) {
         constexpr int PH = decltype(ph)::value;
         constexpr int K0 = PH, K1 = (PH + 1) % 3;    // ring slots of chunks c, c+1
@@ -732,12 +740,10 @@ __global__ __launch_bounds__((SC + kSeqElemWaves + 1) * 64) void scan_seq(const 
             } else {
                 ylast = acc;
             }
-            if (j % kCkptSteps == kCkptSteps - 1 && ck0) {
-                // The state after step t + 1 = kCkptSteps (i + 1), for the backward pass;
-                // only for steps of this segment (past its end the state is not its own).
-                const int t = t_begin + c * T + j;
-                if (t < t_end && t + 1 < L && dv) {
-                    float* dst = ck0 + int64_t((t + 1) / kCkptSteps - 1) * ck_stride + lane;
+            if (j % kCkptSteps == kCkptSteps - 1 && ck_lane) {
+                ck_off += ck_stride;                       // the checkpoint after step t_begin + c T + j + 1
+                if (t_begin + c * T + j + 1 <= ck_last && dv) {
+                    float* dst = ck_lane + ck_off;
 #pragma unroll
                     for (int q = 0; q < NSW; q++)
                         if (n0 + q < n) dst[int64_t(q) * d_in] = h[q];
