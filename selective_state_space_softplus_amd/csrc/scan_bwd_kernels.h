@@ -576,12 +576,15 @@ __global__ __launch_bounds__((SC + 4) * 64) void scan_bwd(const BwdParams p) {
         const float* bcw = s_bc + s2 * (T * 2 * NP) + wave * 2 * NSW;
         float h[NSW];                                               // running state
         float hs[T][NSW], as[T][NSW], bs[ZOH ? T : 1][NSW];        // states, decays, hold weights of the chunk
+        float dls[T], wvs[T];                                       // Delta and w of the chunk's steps, read once
 #pragma unroll
         for (int q = 0; q < NSW; q++) h[q] = hstart[q];
 #pragma unroll
         for (int j = 0; j < T; j++) {
             const int e = (s3 * T + j) * 64 + lane;
-            const float4 pr = make_float4(s_prep[e], s_prep[PL + e], s_prep[2 * PL + e], ZOH ? s_prep[3 * PL + e] : 0.0f);
+            const float4 pr = make_float4(s_prep[e], s_prep[PL + e], 0.0f, 0.0f);
+            dls[j] = pr.x;
+            wvs[j] = pr.y;
 #pragma unroll
             for (int q = 0; q < NSW; q++) {
                 const float x2 = pr.x * A2[q];
@@ -600,7 +603,7 @@ __global__ __launch_bounds__((SC + 4) * 64) void scan_bwd(const BwdParams p) {
 #pragma unroll
         for (int j = T - 1; j >= 0; j--) {
             const int e = (s3 * T + j) * 64 + lane;
-            const float4 pr = make_float4(s_prep[e], s_prep[PL + e], s_prep[2 * PL + e], ZOH ? s_prep[3 * PL + e] : 0.0f);
+            const float4 pr = make_float4(dls[j], wvs[j], s_prep[2 * PL + e], ZOH ? s_prep[3 * PL + e] : 0.0f);
             float S1 = 0.0f, S2 = 0.0f, S3 = 0.0f, dBv[NSW], dCv[NSW];
 #pragma unroll
             for (int q = 0; q < NSW; q++) {
