@@ -19,7 +19,7 @@
 // dDelta_t gains a_tk where Euler has 1 in its input term, dB = g beta u, and
 // dA_k gains g_tk B_tk u_t (Delta_t a_tk - beta_tk)/A_k.
 //
-// scan_bwd<TIn, SC, NSW, SL, SP, GATE, ZOH>: one workgroup per (slice of NP =
+// scan_bwd<TIn, SC, NSW, SL, SP, GATE, ZOH, PR>: one workgroup per (slice of NP =
 // SC NSW states (SL: n is taken in several slices), b, 64-channel group,
 // segment of L) walks its segment backwards in chunks of kCkptSteps = 8
 // steps; segments are taken last first, each starting from the adjoint the
@@ -32,9 +32,12 @@
 // chunk (delta', delta' u, dy', the fp32 B and C rows, the entering state;
 // their global loads are issued one chunk earlier still), and finish the
 // previous one (sums of the waves' S1, S2 partials, du, ddelta, and the
-// chunk's dB, dC rows).  dz needs the readout y'_t and nothing else does:
-// the forward pass that saves the states writes it (scan_seq with DZ), so
-// the readout is never recomputed here.  Sums over the 64 channels (dB, dC) are
+// chunk's dB, dC rows).  PR: each element thread owns two adjacent channels
+// (d_in even, tensors aligned), so a row's two elements move in one access.
+// dz needs the readout y'_t and nothing else does: the forward pass that
+// saves the states writes it (scan_seq with DZ), or, from saved states, the
+// element waves form it from the saved pre-gate readout; the readout is
+// never recomputed here.  Sums over the 64 channels (dB, dC) are
 // cross-lane reductions inside each recurrence wave; sums over the channel groups,
 // batch rows and time (dB, dC, dA_log, dD, dbias) go through per-workgroup
 // partials that reduce_groups adds in a fixed order, so every gradient is
