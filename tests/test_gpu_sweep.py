@@ -53,7 +53,7 @@ def dev(t):
     return None if t is None else t.to(DEV)
 
 
-@pytest.mark.parametrize("seed", range(3000, 3200))
+@pytest.mark.parametrize("seed", range(3000, 3400))
 def test_scan_sweep(ss, seed):
     c = draw(seed)
     say(f"scan sweep seed={seed} {c}")
@@ -69,7 +69,7 @@ def test_scan_sweep(ss, seed):
     assert_close(last, lr, c["dtype"], f"seed {seed} last_state")
 
 
-@pytest.mark.parametrize("seed", range(4000, 4120))
+@pytest.mark.parametrize("seed", range(4000, 4400))
 def test_bwd_sweep(ss, seed):
     c = draw(seed)
     say(f"bwd sweep seed={seed} {c}")
