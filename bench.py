@@ -670,16 +670,20 @@ def main(argv=None):
             return a0.elapsed_time(a1) / reps
 
         ms_f, ms_u, ms_s = timed(fused), timed(unfused), timed(scan_only)
+        with ss.test_plan(cross_two_pass=1):
+            ms_2 = timed(fused)
         xb = cross_bytes(maps, L, d, n, 4)
         result["vmamba_cross"] = {
             "workload": f"{vcfg.name}: {maps} maps of {H}x{H}x{d}, 4 traversal orders, n={n}, fp32, softplus, no gate",
             "fused_ms": round(ms_f, 4),
             "fused_GBps": round(xb / (ms_f * 1e-3) / 1e9, 1),
             "algorithmic_bytes": xb,
+            "two_pass_ms": round(ms_2, 4),
             "unfused_ms": round(ms_u, 4),
             "unfused_scan_only_ms": round(ms_s, 4),
-            "note": "unfused = four traversal copies made with torch + ss_scan_fwd + torch merge; "
-                    "scan_only = ss_scan_fwd on copies made beforehand",
+            "note": "fused = one kernel, the four directions summed in LDS; two_pass = the directions' outputs "
+                    "through a workspace, then a merge kernel; unfused = four traversal copies made with torch + "
+                    "ss_scan_fwd + torch merge; scan_only = ss_scan_fwd on copies made beforehand",
         }
 
     if not args.no_cpu:

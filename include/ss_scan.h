@@ -236,9 +236,14 @@ int ss_state_update_ex(float *state, const void *x, const void *dt,
  * one batch row (zero initial state, delta' B u input term, no gate), and the
  * four outputs are added back at the positions they came from:
  *     y[m, p, d] = sum_k y_k[m, t_k(p), d]
- * The map is read in place by every direction (no unrolled copies); the
- * four outputs go to workspace and a second kernel adds them back, in the
- * order k = 0, 1, 2, 3, so y is the same bit for bit on every run.
+ * The map is read in place by every direction (no unrolled copies).  For
+ * n <= 4 and maps whose sum fits in LDS (L = H * W up to 4096 steps for
+ * n <= 2, a little less for n = 3, 4) one kernel scans the four directions of a map and 8
+ * channels together and adds their outputs into that sum, writing y once;
+ * every position takes its four terms in the order of the chunks of 64 steps
+ * in which they were formed (direction order within a chunk).  Otherwise
+ * the four outputs go to workspace and a second kernel adds them back in the
+ * order k = 0, 1, 2, 3.  Either way y is the same bit for bit on every run.
  *
  *   x          : (maps, H, W, d_in)    dtype; u of all four directions
  *   delta      : (maps, 4, L, d_in)    dtype; direction k's values in its own step order
@@ -250,9 +255,10 @@ int ss_state_update_ex(float *state, const void *x, const void *dt,
  *   y          : (maps, H, W, d_in)    fp32 output (whatever dtype the inputs have)
  *   last_state : (maps, 4, d_in, n)    fp32 output, or NULL
  *   workspace  : device memory of ss_cross_scan_fwd_workspace_bytes() bytes,
- *                256-byte aligned (SS_ERR_ALIGN otherwise); it holds the four
- *                directions' outputs, 16 * maps * L * d_in bytes, and the
- *                scan's own workspace.
+ *                256-byte aligned (SS_ERR_ALIGN otherwise): 256 bytes (the
+ *                status words) for the one-kernel form; for the two-pass
+ *                form the four directions' outputs, 16 * maps * L * d_in
+ *                bytes, and the scan's own workspace.
  * Sizes: those of ss_scan_fwd with b = 4 * maps and L = H * W.  Errors as
  * for ss_scan_fwd.
  */
@@ -413,11 +419,15 @@ const char *ss_status_string(int status);
  *   spin_limit    : polls before a segment wait gives up
  *   wait_never    : 1 = segment waits poll a word nothing sets, so each
  *                   gives up after spin_limit polls (exercises SS_ERR_TIMEOUT)
+ *   cross_two_pass: 1 = ss_cross_scan_fwd in its two-pass form (per-direction
+ *                   outputs in the workspace, then the merge) at every size
+ *                   (its workspace query then asks for that form's size)
  * Results agree with the default within the stated tolerances (the order of
  * fp32 additions may change) and are deterministic for each setting.
  * Returns SS_OK, or SS_ERR_SHAPE for an argument out of range.
  */
-int ss_set_test_plan(int segments, int waves, int time_parallel, int spin_limit, int wait_never);
+int ss_set_test_plan(int segments, int waves, int time_parallel, int spin_limit, int wait_never,
+                     int cross_two_pass);
 
 #ifdef __cplusplus
 }

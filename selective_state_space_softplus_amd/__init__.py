@@ -25,7 +25,7 @@ Entry points mirror the C ABI (``include/ss_scan.h``):
   scan_fwd_workspace_bytes(b, L, d_in, n, dtype) -> int
   scan_status(workspace) -> int    (SS_OK, or SS_ERR_TIMEOUT if a segment wait gave up)
   status_string(code) -> str
-  test_plan(segments=0, waves=0, time_parallel=0, spin_limit=0, wait_never=0)
+  test_plan(segments=0, waves=0, time_parallel=0, spin_limit=0, wait_never=0, cross_two_pass=0)
                                              context manager over ss_set_test_plan (tests, tuning)
 
 scan_fwd, cross_scan_fwd and scan_bwd take ``check=True`` to synchronise and
@@ -102,7 +102,7 @@ def _load() -> ctypes.CDLL:
     lib.ss_scan_status.restype = I
     lib.ss_scan_status.argtypes = [P, ctypes.c_size_t, P, P]
     lib.ss_set_test_plan.restype = I
-    lib.ss_set_test_plan.argtypes = [I, I, I, I, I]
+    lib.ss_set_test_plan.argtypes = [I, I, I, I, I, I]
     lib.ss_state_update.restype = I
     lib.ss_state_update.argtypes = [P, P, P, P, P, P, P, P, P, I, P, I64, I64, I64, I, P]
     lib.ss_state_update_ex.restype = I
@@ -194,15 +194,16 @@ def _raise_on_timeout(workspace, where, device=None):
 
 
 @contextlib.contextmanager
-def test_plan(segments=0, waves=0, time_parallel=0, spin_limit=0, wait_never=0):
+def test_plan(segments=0, waves=0, time_parallel=0, spin_limit=0, wait_never=0, cross_two_pass=0):
     """Override how the scans split their work (ss_set_test_plan) inside a with block."""
-    rc = lib.ss_set_test_plan(int(segments), int(waves), int(time_parallel), int(spin_limit), int(wait_never))
+    rc = lib.ss_set_test_plan(int(segments), int(waves), int(time_parallel), int(spin_limit), int(wait_never),
+                              int(cross_two_pass))
     if rc != 0:
         raise SSError(rc, "ss_set_test_plan")
     try:
         yield
     finally:
-        lib.ss_set_test_plan(0, 0, 0, 0, 0)
+        lib.ss_set_test_plan(0, 0, 0, 0, 0, 0)
 
 
 _workspaces: dict = {}

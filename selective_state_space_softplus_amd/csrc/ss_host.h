@@ -27,6 +27,8 @@ constexpr int kTparWaves = 8;
 constexpr int64_t kMaxWorkgroups = (int64_t(1) << 22) - 1;
 // Longest sequence: per-segment time indices of scan_seq are 32-bit.
 constexpr int64_t kMaxLength = (int64_t(1) << 31) - 1024;
+// LDS one workgroup may take on gfx950.
+constexpr size_t kMaxLdsBytes = 160 * 1024;
 // Largest b * d_in of the decode step (up to 16 threads per channel in one launch).
 constexpr int64_t kMaxStepChannels = (int64_t(1) << 28) - 1;
 
@@ -48,6 +50,7 @@ struct TestPlan {
     std::atomic<int> tpar{0};        // 1: scan_tpar for n <= 2 (zero initial state, Euler)
     std::atomic<int> spin_limit{0};  // polls before a segment wait gives up
     std::atomic<int> wait_never{0};  // 1: segment waits poll a word nothing sets (they all give up)
+    std::atomic<int> cross_two_pass{0};  // 1: the cross scan through workspace outputs and a merge pass
 };
 
 inline TestPlan& test_plan() {

@@ -15,6 +15,7 @@
 
 #include "ss_scan.h"
 #include "conv_kernels.h"
+#include "cross_kernels.h"
 #include "scan_bwd_kernels.h"
 #include "scan_kernels.h"
 #include "ss_host.h"
@@ -327,9 +328,11 @@ SS_EXPORT int ss_scan_status(const void* workspace, size_t workspace_bytes, int3
     return hipGetLastError() == hipSuccess ? SS_OK : SS_ERR_HIP;
 }
 
-SS_EXPORT int ss_set_test_plan(int segments, int waves, int time_parallel, int spin_limit, int wait_never) {
+SS_EXPORT int ss_set_test_plan(int segments, int waves, int time_parallel, int spin_limit, int wait_never,
+                               int cross_two_pass) {
     if (segments < 0 || segments > kMaxSegments || (waves != 0 && waves != 4) || spin_limit < 0 ||
-        (time_parallel != 0 && time_parallel != 1) || (wait_never != 0 && wait_never != 1))
+        (time_parallel != 0 && time_parallel != 1) || (wait_never != 0 && wait_never != 1) ||
+        (cross_two_pass != 0 && cross_two_pass != 1))
         return SS_ERR_SHAPE;
     TestPlan& t = test_plan();
     t.segments.store(segments);
@@ -337,6 +340,7 @@ SS_EXPORT int ss_set_test_plan(int segments, int waves, int time_parallel, int s
     t.tpar.store(time_parallel);
     t.spin_limit.store(spin_limit);
     t.wait_never.store(wait_never);
+    t.cross_two_pass.store(cross_two_pass);
     return SS_OK;
 }
 
@@ -491,11 +495,38 @@ bool cross_sizes_ok(int64_t maps, int64_t H, int64_t W, int64_t d_in, int64_t n)
     return sizes_ok(b, L, d_in) && b * ((d_in + 63) / 64) <= kMaxWorkgroups && L <= kMaxLength;
 }
 
+// State slots of cross_fused for state size n (0: not taken there).
+int cross_fused_ns(int64_t n) { return n == 1 ? 1 : n == 2 ? 2 : n <= 4 ? 4 : 0; }
+
+// The one-pass cross scan (cross_fused) takes n <= 4 and maps whose sum fits
+// in LDS next to its staging areas, with positions below 2^16 (the exact
+// 32-bit division by H and W) and a map slice whose byte offsets, two chunks
+// past its end included, stay below 2^31; the two-pass form takes the rest.
+bool cross_one_pass(int64_t L, int64_t d_in, int64_t n) {
+    if (test_plan().cross_two_pass.load(std::memory_order_relaxed)) return false;
+    const int ns = cross_fused_ns(n);
+    return ns > 0 && L < (int64_t(1) << 16) && ss::cross_lds_bytes(int(L), ns) <= kMaxLdsBytes &&
+           (L + 2 * ss::kCrossChunk) * d_in * 4 < (int64_t(1) << 31);   // byte offsets of its buffer loads
+}
+
 SS_EXPORT size_t ss_cross_scan_fwd_workspace_bytes(int64_t maps, int64_t H, int64_t W, int64_t d_in, int64_t n,
                                                    int dtype) {
     if (dtype != SS_F32 && dtype != SS_BF16) return 0;
     if (!cross_sizes_ok(maps, H, W, d_in, n) || n > SS_MAX_STATE) return 0;
+    if (cross_one_pass(H * W, d_in, n)) return 256;   // the call's status words only
     return ss_scan_fwd_workspace_bytes(4 * maps, H * W, d_in, n, dtype) + cross_ys_bytes(maps, H * W, d_in);
+}
+
+template <typename TIn>
+void launch_cross_fused(const ss::CrossParams& p, int ns, hipStream_t st) {
+    const dim3 grid(unsigned(int64_t(p.maps) * p.ncb));
+    const size_t lds = ss::cross_lds_bytes(p.L, ns);
+    using Kern = void (*)(ss::CrossParams);
+    static constexpr Kern kernels[2][3] = {
+        {ss::cross_fused<TIn, 1, false>, ss::cross_fused<TIn, 2, false>, ss::cross_fused<TIn, 4, false>},
+        {ss::cross_fused<TIn, 1, true>, ss::cross_fused<TIn, 2, true>, ss::cross_fused<TIn, 4, true>}};
+    const Kern kern = kernels[p.softplus ? 1 : 0][ns == 1 ? 0 : ns == 2 ? 1 : 2];
+    hipLaunchKernelGGL(kern, grid, dim3(256), lds, st, p);
 }
 
 SS_EXPORT int ss_cross_scan_fwd(const void* x, const void* delta, const float* A_log, const void* B, const void* C,
@@ -530,8 +561,39 @@ SS_EXPORT int ss_cross_scan_fwd(const void* x, const void* delta, const float* A
         if (overlaps(r, rw)) return SS_ERR_ALIAS;
     if (overlaps(ry, rw) || overlaps(rs, rw)) return SS_ERR_ALIAS;
 
-    // The scan's own workspace first (so the status words lead the workspace),
-    // then the four directions' outputs.
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    if (cross_one_pass(L, d_in, n)) {
+        ss::CrossParams c{};
+        c.x = x;
+        c.delta = delta;
+        c.A_log = A_log;
+        c.B = B;
+        c.C = C;
+        c.D = D;
+        c.bias = delta_bias;
+        c.y = y;
+        c.last_state = last_state;
+        c.err = static_cast<uint32_t*>(workspace) + kStatusWord;
+        c.maps = int(maps);
+        c.H = int(H);
+        c.W = int(W);
+        c.L = int(L);
+        c.d_in = int(d_in);
+        c.n = int(n);
+        c.softplus = delta_softplus ? 1 : 0;
+        c.ncb = int((d_in + ss::kCrossCh - 1) / ss::kCrossCh);
+        c.vec_y = d_in % 4 == 0 && aligned(y, 16);
+        c.magic_h = H > 1 ? uint32_t(((uint64_t(1) << 32) + uint64_t(H) - 1) / uint64_t(H)) : 0u;
+        c.magic_w = W > 1 ? uint32_t(((uint64_t(1) << 32) + uint64_t(W) - 1) / uint64_t(W)) : 0u;
+        if (dtype == SS_BF16)
+            launch_cross_fused<uint16_t>(c, cross_fused_ns(n), st);
+        else
+            launch_cross_fused<float>(c, cross_fused_ns(n), st);
+        return hipGetLastError() == hipSuccess ? SS_OK : SS_ERR_HIP;
+    }
+
+    // Two passes: the scan's own workspace first (so the status words lead
+    // the workspace), then the four directions' outputs.
     const size_t scan_ws_bytes = ss_scan_fwd_workspace_bytes(b, L, d_in, n, dtype);
     float* ys = reinterpret_cast<float*>(static_cast<char*>(workspace) + scan_ws_bytes);
     ScanParams p{};
@@ -556,7 +618,6 @@ SS_EXPORT int ss_cross_scan_fwd(const void* x, const void* delta, const float* A
     p.K = 1;
     p.Lseg = L;
     p.err = static_cast<uint32_t*>(workspace) + kStatusWord;
-    hipStream_t st = static_cast<hipStream_t>(stream);
     const int rc = dtype == SS_BF16 ? dispatch_seq<uint16_t>(p, SeqMode::Cross, workspace, scan_ws_bytes, st)
                                     : dispatch_seq<float>(p, SeqMode::Cross, workspace, scan_ws_bytes, st);
     if (rc != SS_OK) return rc;

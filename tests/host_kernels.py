@@ -15,6 +15,7 @@ their timing.
 from __future__ import annotations
 
 import concurrent.futures
+import fcntl
 import hashlib
 import os
 import subprocess
@@ -56,8 +57,6 @@ def _sources() -> dict[str, str]:
 
 def build(verbose: bool = False) -> str:
     """Path of the scan_host executable, compiled once per version of the sources."""
-    import importlib.util
-
     srcs = _sources()
     key = hashlib.sha256(("".join(k + v for k, v in sorted(srcs.items())) + " ".join(FLAGS)).encode()).hexdigest()[:16]
     cache = os.path.join(tempfile.gettempdir(), f"ss_scan_host_{key}")
@@ -65,6 +64,18 @@ def build(verbose: bool = False) -> str:
     if os.path.exists(exe):
         return exe
     os.makedirs(cache, exist_ok=True)
+    # One builder per cache directory (pytest-xdist workers share it): a
+    # source rewritten under a running compiler would break that compile.
+    with open(os.path.join(cache, ".lock"), "w") as lock:
+        fcntl.flock(lock, fcntl.LOCK_EX)
+        if os.path.exists(exe):
+            return exe
+        return _build_locked(srcs, cache, exe)
+
+
+def _build_locked(srcs: dict, cache: str, exe: str) -> str:
+    import importlib.util
+
     for name, text in srcs.items():
         if ":" not in name:
             with open(os.path.join(cache, name), "w") as f:

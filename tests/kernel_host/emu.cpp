@@ -89,6 +89,7 @@ static std::vector<Wave*> g_waves;
 static Wave& my_wave() { return *g_waves[tl_thread.x / 64]; }
 
 void block_barrier() { g_block_bar.arrive_and_wait(); }
+void wave_barrier() { my_wave().bar.arrive_and_wait(); }
 void sleep_a_little() { std::this_thread::yield(); }
 unsigned char* lds_base() { return g_lds; }
 
@@ -226,6 +227,17 @@ void buffer_load_lds(emu_rsrc r, uintptr_t lds_off, int bytes, uint32_t voff, ui
         std::abort();
     }
     global_load_lds(r.base + at, g_lds + lds_off, bytes);
+}
+
+// A buffer load into registers: `bytes` bytes at voff + soff, or 0 where they
+// do not lie inside the descriptor's range (as the hardware's range check of
+// an untyped buffer returns 0 for such lanes).
+uint32_t buffer_load(emu_rsrc r, uint32_t voff, uint32_t soff, int bytes) {
+    const uint64_t at = uint64_t(soff) + voff;
+    if (at + uint64_t(bytes) > r.bytes) return 0u;
+    uint32_t v = 0;
+    std::memcpy(&v, r.base + at, size_t(bytes));
+    return v;
 }
 
 // Cross-lane exchanges: every lane publishes, the wave meets, every lane
@@ -366,7 +378,7 @@ void save(const char* name, const void* p, size_t bytes) {
 int run(const std::string& mode) {
     const long long es = arg("dtype") == SS_BF16 ? 2 : 4;
     ss_set_test_plan(int(g_args.count("segments") ? arg("segments") : 0), int(g_args.count("waves") ? arg("waves") : 0),
-                     0, 0, 0);
+                     0, 0, 0, int(g_args.count("cross_two_pass") ? arg("cross_two_pass") : 0));
     if (mode == "fwd" || mode == "noalloc") {
         const long long b = arg("b"), L = arg("L"), d = arg("d_in"), n = arg("n");
         const size_t nel = size_t(b * L * d), nbc = size_t(b * L * n), nst = size_t(b * d * n);

@@ -48,6 +48,7 @@ hipError_t occupancy(int* nb, const void* fn, int threads, size_t lds);
 hipError_t symbol_address(void** p, const void* sym);
 void run_grid(dim3 grid, dim3 block, size_t lds, void (*body)(void*), void* ctx);
 void block_barrier();
+void wave_barrier();
 void sleep_a_little();
 unsigned char* lds_base();
 
@@ -101,6 +102,7 @@ inline float __uint_as_float(unsigned u) { return __builtin_bit_cast(float, u); 
 inline unsigned __float_as_uint(float f) { return __builtin_bit_cast(unsigned, f); }
 inline float __int_as_float(int u) { return __builtin_bit_cast(float, u); }
 inline int __float_as_int(float f) { return __builtin_bit_cast(int, f); }
+inline unsigned __umulhi(unsigned a, unsigned b) { return unsigned((uint64_t(a) * b) >> 32); }
 
 template <typename A, typename B>
 inline auto min(A a, B b) -> std::common_type_t<A, B> { return a < b ? a : b; }
@@ -118,6 +120,7 @@ struct emu_rsrc {
 namespace emu {
 void global_load_lds(const void* src, void* lds_dst, int bytes);
 void buffer_load_lds(emu_rsrc r, uintptr_t lds_off, int bytes, uint32_t voff, uint32_t soff, uint32_t off);
+uint32_t buffer_load(emu_rsrc r, uint32_t voff, uint32_t soff, int bytes);
 typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
 u32x2 permlane32_swap(unsigned a, unsigned b);
 u32x2 permlane16_swap(unsigned a, unsigned b);
@@ -128,6 +131,7 @@ float shfl(float v, int src, int width);
 
 #define __builtin_amdgcn_readfirstlane(x) (x)
 #define __builtin_amdgcn_s_barrier() emu::block_barrier()
+#define __builtin_amdgcn_wave_barrier() emu::wave_barrier()
 #define __syncthreads() emu::block_barrier()
 #define __builtin_amdgcn_s_waitcnt(x) ((void)(x))
 #define __builtin_amdgcn_s_sleep(x) emu::sleep_a_little()
@@ -141,6 +145,8 @@ float shfl(float v, int src, int width);
     emu_rsrc{static_cast<const unsigned char*>(static_cast<const void*>(p)), uint32_t(bytes)}
 #define __builtin_amdgcn_raw_ptr_buffer_load_lds(r, dst, bytes, voff, soff, off, aux) \
     emu::buffer_load_lds((r), (uintptr_t)(dst), (bytes), (voff), (soff), (off))
+#define __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, aux) emu::buffer_load((r), uint32_t(voff), uint32_t(soff), 4)
+#define __builtin_amdgcn_raw_buffer_load_b16(r, voff, soff, aux) ((unsigned short)emu::buffer_load((r), uint32_t(voff), uint32_t(soff), 2))
 #define __builtin_amdgcn_permlane32_swap(a, b, fi, bc) emu::permlane32_swap((a), (b))
 #define __builtin_amdgcn_permlane16_swap(a, b, fi, bc) emu::permlane16_swap((a), (b))
 #define __builtin_amdgcn_update_dpp(old, src, ctrl, rm, bm, bc) emu::update_dpp((old), (src), (ctrl), (rm), (bm), (bc))

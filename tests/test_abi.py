@@ -139,11 +139,12 @@ def test_scan_status_rejects(ss):
 
 
 def test_test_plan_validates_and_resets(ss):
-    bad = ((-1, 0, 0, 0, 0), (17, 0, 0, 0, 0), (0, 2, 0, 0, 0), (0, 0, 2, 0, 0), (0, 0, 0, -5, 0), (0, 0, 0, 0, 3))
+    bad = ((-1, 0, 0, 0, 0, 0), (17, 0, 0, 0, 0, 0), (0, 2, 0, 0, 0, 0), (0, 0, 2, 0, 0, 0), (0, 0, 0, -5, 0, 0),
+           (0, 0, 0, 0, 3, 0), (0, 0, 0, 0, 0, 2))
     for args in bad:
         assert ss.lib.ss_set_test_plan(*args) == SHAPE, args
-    assert ss.lib.ss_set_test_plan(4, 4, 1, 100, 1) == OK
-    assert ss.lib.ss_set_test_plan(0, 0, 0, 0, 0) == OK
+    assert ss.lib.ss_set_test_plan(4, 4, 1, 100, 1, 1) == OK
+    assert ss.lib.ss_set_test_plan(0, 0, 0, 0, 0, 0) == OK
     with ss.test_plan(segments=3):
         pass
     with pytest.raises(ss.SSError):
@@ -286,7 +287,8 @@ def call_cross(ss, a):
     (dict(maps=0), SHAPE), (dict(H=0), SHAPE), (dict(W=-2), SHAPE), (dict(d_in=0), SHAPE), (dict(n=0), SHAPE),
     (dict(H=1 << 16, W=1 << 16), SHAPE), (dict(maps=1 << 45), SHAPE),
     (dict(dtype=3), DTYPE), (dict(n=65), UNSUP),
-    (dict(ws=None), WS), (dict(ws_bytes=10), WS), (dict(ws_bytes=16 * 16 * 3136 * 384 - 1), WS),
+    (dict(ws=None), WS), (dict(ws_bytes=10), WS), (dict(ws_bytes=255), WS),
+    (dict(n=5, ws_bytes=16 * 16 * 3136 * 384 - 1), WS), (dict(H=64, W=67, ws_bytes=16 * 16 * 64 * 67 * 384 - 1), WS),
     (dict(x=addr(1) + 2), ALIGN), (dict(y=addr(8) + 2), ALIGN), (dict(last=addr(9) + 1), ALIGN),
     (dict(ws=addr(10) + 16), ALIGN),
     (dict(y=addr(1)), ALIAS), (dict(last=addr(3)), ALIAS), (dict(y=addr(9)), ALIAS), (dict(ws=addr(8)), ALIAS),
@@ -303,9 +305,14 @@ def test_cross_optional_pointers_may_be_null(ss):
 def test_cross_workspace_query(ss):
     q = ss.lib.ss_cross_scan_fwd_workspace_bytes
     q.restype = ctypes.c_size_t
-    full = q(16, 56, 56, 384, 1, 0)
-    assert full >= 16 * 16 * 3136 * 384 + ss.scan_fwd_workspace_bytes(64, 3136, 384, 1, 0)
-    assert full == q(16, 56, 56, 384, 1, 1)
+    # One kernel (n <= 4, the map's sum in LDS): the status words only.
+    assert q(16, 56, 56, 384, 1, 0) == 256 == q(16, 56, 56, 384, 4, 1) == q(3, 64, 64, 8, 2, 0)
+    # Two passes: n > 4, a map too large for LDS (64 x 67 at n = 1; 64 x 64 at n = 3, 4), or forced.
+    two = 16 * 16 * 3136 * 384 + ss.scan_fwd_workspace_bytes(64, 3136, 384, 5, 0)
+    assert q(16, 56, 56, 384, 5, 0) >= two
+    assert q(1, 64, 67, 8, 1, 0) > 256 and q(1, 64, 64, 8, 3, 0) > 256 and q(1, 64, 64, 8, 2, 0) == 256
+    with ss.test_plan(cross_two_pass=1):
+        assert q(16, 56, 56, 384, 1, 0) >= 16 * 16 * 3136 * 384 + ss.scan_fwd_workspace_bytes(64, 3136, 384, 1, 0)
     for bad in ((0, 5, 5, 8, 1, 0), (1, 0, 5, 8, 1, 0), (1, 5, 5, 8, 65, 0), (1, 5, 5, 8, 1, 2)):
         assert q(*bad) == 0, bad
 

@@ -5,9 +5,12 @@ both backwards) and the four outputs are added back at their positions
 (githubissues.com VMamba issue 206: CrossScan / CrossMerge only arrange the
 sequence).  The output map is fp32 whatever the input dtype, and the oracle
 sees the same (bf16-exact) inputs, so every case is held to the fp32 bound,
-max relative error 1e-4; last states likewise.  Against the unfused path on
-the GPU (torch-made traversal copies, ss_scan_fwd, torch merge) the result is
-identical bit for bit.
+max relative error 1e-4; last states likewise.  Both forms of the call are
+covered: one kernel that adds the directions into an LDS sum (n <= 4, maps up
+to about 4096 positions; the default there) and the two-pass form
+(per-direction outputs in the workspace, then a merge), which the test plan
+can force.  The two-pass form is identical bit for bit to the unfused path on
+the GPU (torch-made traversal copies, ss_scan_fwd, torch merge).
 """
 import numpy as np
 import pytest
@@ -51,22 +54,30 @@ def run_gpu(ss, c, softplus=True):
     return y, last
 
 
-def check(ss, c, what, softplus=True):
-    y, last = run_gpu(ss, c, softplus)
+def check(ss, c, what, softplus=True, two_pass=False):
+    with ss.test_plan(cross_two_pass=int(two_pass)):
+        y, last = run_gpu(ss, c, softplus)
     yr, lr = oracle.cross_scan(c["x"], c["delta"], c["A_log"], c["B"], c["C"], c["D"], c["delta_bias"], softplus)
     e1 = assert_close(y, yr, F32, f"{what} y")
     e2 = assert_close(last, lr, F32, f"{what} last_state")
     return e1, e2
 
 
-@pytest.mark.parametrize("maps,H,W,d_in,n,dtype", [
+SMALL = [
     (2, 7, 5, 40, 1, F32), (1, 9, 6, 64, 1, F32), (2, 4, 13, 70, 2, BF16), (1, 5, 8, 64, 16, BF16),
     (2, 6, 3, 33, 5, F32), (1, 1, 17, 20, 1, F32), (1, 11, 1, 20, 3, F32), (1, 1, 1, 8, 1, F32),
-    (1, 6, 7, 24, 40, F32), (2, 8, 8, 128, 16, F32),
-])
-def test_cross_small(ss, maps, H, W, d_in, n, dtype):
-    say(f"cross maps={maps} {H}x{W} d_in={d_in} n={n} {dtype}")
-    check(ss, cross_inputs(maps, H, W, d_in, n, dtype, seed=maps + H * 7 + W * 11 + n), f"{H}x{W} n={n}")
+    (1, 6, 7, 24, 40, F32), (2, 8, 8, 128, 16, F32), (1, 12, 11, 9, 4, BF16), (3, 17, 19, 24, 2, F32),
+    (1, 1, 300, 16, 1, BF16), (1, 128, 1, 8, 3, F32), (2, 64, 64, 16, 1, F32), (1, 64, 64, 8, 4, F32),
+    (1, 65, 66, 8, 1, F32),
+]
+
+
+@pytest.mark.parametrize("two_pass", [False, True])
+@pytest.mark.parametrize("maps,H,W,d_in,n,dtype", SMALL)
+def test_cross_small(ss, maps, H, W, d_in, n, dtype, two_pass):
+    say(f"cross maps={maps} {H}x{W} d_in={d_in} n={n} {dtype} two_pass={two_pass}")
+    check(ss, cross_inputs(maps, H, W, d_in, n, dtype, seed=maps + H * 7 + W * 11 + n), f"{H}x{W} n={n}",
+          two_pass=two_pass)
 
 
 def test_cross_without_softplus_or_bias(ss):
@@ -78,27 +89,32 @@ def test_cross_without_softplus_or_bias(ss):
 
 @pytest.mark.parametrize("segments,n", [(3, 1), (5, 16)])
 def test_cross_segments(ss, segments, n):
+    """The two-pass form with L cut into segments."""
     say(f"cross with {segments} segments n={n}")
     c = cross_inputs(1, 20, 30, 64, n, F32, seed=9 + n)
     with plan(segments=segments):
-        check(ss, c, f"segments={segments}")
+        check(ss, c, f"segments={segments}", two_pass=True)
 
 
-def test_cross_vmamba_workload_full(ss):
+@pytest.mark.parametrize("two_pass", [False, True])
+def test_cross_vmamba_workload_full(ss, two_pass):
     """The scan-vmamba workload (16 maps of 56 x 56 x 384, n = 1, fp32), compared in full."""
     cfg = workloads.CONFIGS[3]
-    say(f"cross scan at {cfg.name} size, full compare")
+    say(f"cross scan at {cfg.name} size, full compare, two_pass={two_pass}")
     c = workloads.cross_scan_inputs(3)
-    e1, e2 = check(ss, c, cfg.name)
-    print(f"{cfg.name} fused cross scan: y err {e1:.3g}, last_state err {e2:.3g}")
+    e1, e2 = check(ss, c, cfg.name, two_pass=two_pass)
+    print(f"{cfg.name} cross scan (two_pass={two_pass}): y err {e1:.3g}, last_state err {e2:.3g}")
 
 
 def test_cross_equals_unrolled_scan_and_merge(ss):
-    """Unrolled on the GPU with torch, scanned by ss_scan_fwd, merged with torch: the same map."""
+    """Unrolled on the GPU with torch, scanned by ss_scan_fwd, merged with torch: the same map as the
+    two-pass form, and the one-kernel form within the fp32 bound of both."""
     say("fused cross scan vs unrolled scan + merge")
     maps, H, W, d_in, n = 3, 12, 9, 96, 1
     c = cross_inputs(maps, H, W, d_in, n, F32, seed=17, shared_params=True)
-    y, last = run_gpu(ss, c)
+    y1, last1 = run_gpu(ss, c)
+    with ss.test_plan(cross_two_pass=1):
+        y, last = run_gpu(ss, c)
     g = {k: (v.to(DEV) if isinstance(v, torch.Tensor) else v) for k, v in c.items()}
     L = H * W
     u = workloads.vmamba_unroll(g["x"])                                       # (maps*4, L, d_in)
@@ -110,13 +126,17 @@ def test_cross_equals_unrolled_scan_and_merge(ss):
               + yd[:, 2].flip(1).reshape(maps, H, W, d_in) + yd[:, 3].flip(1).reshape(maps, W, H, d_in).transpose(1, 2))
     torch.cuda.synchronize()
     # Same per-direction arithmetic and the same order of the four additions: bit for bit.
-    assert torch.equal(y, merged), "fused vs unrolled"
+    assert torch.equal(y, merged), "two-pass vs unrolled"
     assert torch.equal(last, ld.reshape(maps, 4, d_in, n))
+    assert_close(y1, merged, F32, "one kernel vs unrolled")
+    assert_close(last1, last, F32, "one kernel vs unrolled, last_state")
 
 
-def test_cross_is_deterministic(ss):
-    say("cross scan run-to-run determinism")
-    c = cross_inputs(2, 10, 9, 72, 16, BF16, seed=23)
+@pytest.mark.parametrize("n,dtype", [(16, BF16), (1, F32), (2, BF16)])
+def test_cross_is_deterministic(ss, n, dtype):
+    say(f"cross scan run-to-run determinism n={n}")
+    c = cross_inputs(2, 40, 39, 72, n, dtype, seed=23)
     y1, l1 = run_gpu(ss, c)
-    y2, l2 = run_gpu(ss, c)
-    assert torch.equal(y1, y2) and torch.equal(l1, l2)
+    for _ in range(3):
+        y2, l2 = run_gpu(ss, c)
+        assert torch.equal(y1, y2) and torch.equal(l1, l2)

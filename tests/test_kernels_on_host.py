@@ -172,17 +172,31 @@ def test_step_on_host(b, d, n, dt, zoh):
     assert_close(got["state"], sr, dt, "host step state")
 
 
-def test_cross_on_host():
-    maps, H, W, d, n = 2, 5, 7, 24, 1
-    g = torch.Generator().manual_seed(3)
-    x = torch.randn(maps, H, W, d, generator=g)
-    delta = torch.randn(maps, 4, H * W, d, generator=g) - 2
-    B, C = (torch.randn(maps, 4, H * W, n, generator=g) for _ in range(2))
-    A_log = torch.zeros(4, d, n)
+CROSS = [
+    # maps, H, W, d_in, n, dtype, bias, two_pass
+    (2, 5, 7, 24, 1, F32, False, True),      # the two-pass form (workspace outputs + merge), two segments
+    (2, 5, 7, 24, 1, F32, True, False),      # one pass, L = 35: a single ragged chunk
+    (1, 9, 15, 20, 1, F32, True, False),     # L = 135: three chunks, the last ragged; d_in not a multiple of 8
+    (1, 1, 70, 8, 2, BF16, True, False),     # H = 1: the column-major order is the row-major one
+    (1, 66, 1, 12, 3, F32, False, False),    # W = 1, n = 3 in four state slots
+    (2, 8, 16, 16, 4, BF16, True, False),    # L = 128: two whole chunks, n = 4
+]
+
+
+@pytest.mark.parametrize("maps,H,W,d,n,dt,bias,two_pass", CROSS)
+def test_cross_on_host(maps, H, W, d, n, dt, bias, two_pass):
+    g = torch.Generator().manual_seed(3 + H + W + n)
+    L = H * W
+    x = torch.randn(maps, H, W, d, generator=g).to(dt)
+    delta = (torch.randn(maps, 4, L, d, generator=g) - 2).to(dt)
+    B, C = (torch.randn(maps, 4, L, n, generator=g).to(dt) for _ in range(2))
+    A_log = torch.rand(4, d, n, generator=g) * 2 - 1
     D = torch.randn(4, d, generator=g)
-    t = dict(x=x, delta=delta, A_log=A_log, B=B, C=C, D=D)
-    got = hk.run("cross", t, dict(maps=maps, H=H, W=W, d_in=d, n=n, dtype=0, softplus=1, segments=2),
+    db = (torch.rand(4, d, generator=g) - 0.5) if bias else None
+    t = dict(x=x, delta=delta, A_log=A_log, B=B, C=C, D=D, delta_bias=db)
+    got = hk.run("cross", t, dict(maps=maps, H=H, W=W, d_in=d, n=n, dtype=_code(dt), softplus=1,
+                                  segments=2 if two_pass else 0, cross_two_pass=int(two_pass)),
                  dict(y=((maps, H, W, d), F32), last_state=((maps, 4, d, n), F32)))
-    yr, lr = oracle.cross_scan(x, delta, A_log, B, C, D, None, True)
+    yr, lr = oracle.cross_scan(x, delta, A_log, B, C, D, db, True)
     assert_close(got["y"], yr, F32, "host cross y")
     assert_close(got["last_state"], lr, F32, "host cross last_state")
