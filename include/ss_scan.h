@@ -89,6 +89,13 @@ typedef enum {
     SS_DISC_ZOH = 1          /* (exp(delta' * A) - 1) / A * B * u, the zero-order hold */
 } ss_discretization;
 
+/* How ss_cross_scan_fwd_ex merges the four directions of a map. */
+typedef enum {
+    SS_CROSS_AUTO = 0,       /* the library's choice: the two-pass form              */
+    SS_CROSS_ONE_PASS = 1,   /* one kernel, the directions summed in LDS (n <= 4)    */
+    SS_CROSS_TWO_PASS = 2    /* per-direction outputs in the workspace, then a merge  */
+} ss_cross_form;
+
 /* Largest state size n the kernels are built for. */
 #define SS_MAX_STATE 64
 
@@ -160,7 +167,7 @@ int ss_scan_fwd_ex(const void *u, const void *delta, const float *A_log,
  * call, in stream order) to *status, one int32 in device memory (or host
  * memory the device can write): SS_OK, or SS_ERR_TIMEOUT when a wait between
  * segments of L gave up, in which case the outputs of that call hold NaN.
- * workspace is the workspace passed to ss_scan_fwd(_ex), ss_cross_scan_fwd
+ * workspace is the workspace passed to ss_scan_fwd(_ex), ss_cross_scan_fwd(_ex)
  * or ss_scan_bwd(_ex); NULL reads the static scratch of the last
  * ss_scan_fwd_noalloc call on the current device.  Returns an ss_status.
  */
@@ -236,14 +243,10 @@ int ss_state_update_ex(float *state, const void *x, const void *dt,
  * one batch row (zero initial state, delta' B u input term, no gate), and the
  * four outputs are added back at the positions they came from:
  *     y[m, p, d] = sum_k y_k[m, t_k(p), d]
- * The map is read in place by every direction (no unrolled copies).  For
- * n <= 4 and maps whose sum fits in LDS (L = H * W up to 4096 steps for
- * n <= 2, a little less for n = 3, 4) one kernel scans the four directions of a map and 8
- * channels together and adds their outputs into that sum, writing y once;
- * every position takes its four terms in the order of the chunks of 64 steps
- * in which they were formed (direction order within a chunk).  Otherwise
- * the four outputs go to workspace and a second kernel adds them back in the
- * order k = 0, 1, 2, 3.  Either way y is the same bit for bit on every run.
+ * The map is read in place by every direction (no unrolled copies); the
+ * four outputs go to workspace and a second kernel adds them back, in the
+ * order k = 0, 1, 2, 3, so y is the same bit for bit on every run.  This is
+ * ss_cross_scan_fwd_ex with SS_CROSS_AUTO.
  *
  *   x          : (maps, H, W, d_in)    dtype; u of all four directions
  *   delta      : (maps, 4, L, d_in)    dtype; direction k's values in its own step order
@@ -255,10 +258,9 @@ int ss_state_update_ex(float *state, const void *x, const void *dt,
  *   y          : (maps, H, W, d_in)    fp32 output (whatever dtype the inputs have)
  *   last_state : (maps, 4, d_in, n)    fp32 output, or NULL
  *   workspace  : device memory of ss_cross_scan_fwd_workspace_bytes() bytes,
- *                256-byte aligned (SS_ERR_ALIGN otherwise): 256 bytes (the
- *                status words) for the one-kernel form; for the two-pass
- *                form the four directions' outputs, 16 * maps * L * d_in
- *                bytes, and the scan's own workspace.
+ *                256-byte aligned (SS_ERR_ALIGN otherwise); it holds the four
+ *                directions' outputs, 16 * maps * L * d_in bytes, and the
+ *                scan's own workspace.
  * Sizes: those of ss_scan_fwd with b = 4 * maps and L = H * W.  Errors as
  * for ss_scan_fwd.
  */
@@ -271,6 +273,33 @@ int ss_cross_scan_fwd(const void *x, const void *delta, const float *A_log,
                       float *y, float *last_state,
                       int64_t maps, int64_t H, int64_t W, int64_t d_in, int64_t n,
                       int dtype, void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * ss_cross_scan_fwd with the merge chosen by `form` (an ss_cross_form value,
+ * else SS_ERR_MODE):
+ *   SS_CROSS_TWO_PASS (and SS_CROSS_AUTO): as ss_cross_scan_fwd.
+ *   SS_CROSS_ONE_PASS: one kernel scans the four directions of a map and 8
+ *     channels together and adds their outputs into that map slice's sum in
+ *     LDS, writing y once; the per-direction outputs never reach memory
+ *     (about 2.3x fewer bytes moved).  Each position takes its four terms in
+ *     the order of the 64-step chunks in which they were formed, direction
+ *     order within a chunk, so y is the same bit for bit on every run (and
+ *     within fp32 rounding of the two-pass form).  It takes n <= 4 and maps
+ *     whose sum fits in LDS, L = H * W up to 4265 at n = 1, 4205 at n = 2
+ *     and 4084 at n = 3 and 4; other shapes return SS_ERR_UNSUPPORTED.
+ * The workspace is ss_cross_scan_fwd_ex_workspace_bytes(..., form) bytes
+ * (256 for the one-pass form: its status words), 256-byte aligned.  Other
+ * arguments, sizes and errors as for ss_cross_scan_fwd.
+ */
+size_t ss_cross_scan_fwd_ex_workspace_bytes(int64_t maps, int64_t H, int64_t W,
+                                            int64_t d_in, int64_t n, int dtype, int form);
+
+int ss_cross_scan_fwd_ex(const void *x, const void *delta, const float *A_log,
+                         const void *B, const void *C, const float *D,
+                         const float *delta_bias, int delta_softplus,
+                         float *y, float *last_state,
+                         int64_t maps, int64_t H, int64_t W, int64_t d_in, int64_t n,
+                         int dtype, int form, void *workspace, size_t workspace_bytes, void *stream);
 
 /* Largest state size n of ss_scan_bwd. */
 #define SS_MAX_BWD_STATE 64
@@ -419,15 +448,11 @@ const char *ss_status_string(int status);
  *   spin_limit    : polls before a segment wait gives up
  *   wait_never    : 1 = segment waits poll a word nothing sets, so each
  *                   gives up after spin_limit polls (exercises SS_ERR_TIMEOUT)
- *   cross_two_pass: 1 = ss_cross_scan_fwd in its two-pass form (per-direction
- *                   outputs in the workspace, then the merge) at every size
- *                   (its workspace query then asks for that form's size)
  * Results agree with the default within the stated tolerances (the order of
  * fp32 additions may change) and are deterministic for each setting.
  * Returns SS_OK, or SS_ERR_SHAPE for an argument out of range.
  */
-int ss_set_test_plan(int segments, int waves, int time_parallel, int spin_limit, int wait_never,
-                     int cross_two_pass);
+int ss_set_test_plan(int segments, int waves, int time_parallel, int spin_limit, int wait_never);
 
 #ifdef __cplusplus
 }

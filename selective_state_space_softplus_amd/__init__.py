@@ -19,13 +19,14 @@ Entry points mirror the C ABI (``include/ss_scan.h``):
                  initial_state=None, zoh=False) -> y, differentiable (torch.autograd.Function
                                                  calling scan_fwd / scan_bwd)
   cross_scan_fwd(x, delta, A_log, B, C, D, delta_bias=None, delta_softplus=True,
-                 return_last_state=False)    -> y (maps, H, W, d_in) fp32  or  (y, last_state)
+                 return_last_state=False, form="auto")
+                                             -> y (maps, H, W, d_in) fp32  or  (y, last_state)
   conv_update(conv_state, x, weight, bias=None, silu=True)
                                              -> out (b, d_in)  (conv_state is updated in place)
   scan_fwd_workspace_bytes(b, L, d_in, n, dtype) -> int
   scan_status(workspace) -> int    (SS_OK, or SS_ERR_TIMEOUT if a segment wait gave up)
   status_string(code) -> str
-  test_plan(segments=0, waves=0, time_parallel=0, spin_limit=0, wait_never=0, cross_two_pass=0)
+  test_plan(segments=0, waves=0, time_parallel=0, spin_limit=0, wait_never=0)
                                              context manager over ss_set_test_plan (tests, tuning)
 
 scan_fwd, cross_scan_fwd and scan_bwd take ``check=True`` to synchronise and
@@ -74,7 +75,8 @@ STATUS = {0: "SS_OK", -1: "SS_ERR_NULL", -2: "SS_ERR_SHAPE", -3: "SS_ERR_DTYPE",
           -10: "SS_ERR_TIMEOUT"}
 EXPORTS = ("ss_scan_fwd_workspace_bytes", "ss_scan_fwd", "ss_scan_fwd_ex", "ss_scan_fwd_noalloc", "ss_scan_status",
            "ss_state_update", "ss_state_update_ex", "ss_scan_bwd", "ss_scan_bwd_ex", "ss_scan_bwd_workspace_bytes",
-           "ss_cross_scan_fwd", "ss_cross_scan_fwd_workspace_bytes", "ss_conv_update", "ss_status_string",
+           "ss_cross_scan_fwd", "ss_cross_scan_fwd_workspace_bytes", "ss_cross_scan_fwd_ex",
+           "ss_cross_scan_fwd_ex_workspace_bytes", "ss_conv_update", "ss_status_string",
            "ss_set_test_plan", "ss_scan_checkpoint_bytes", "ss_scan_fwd_save", "ss_scan_bwd_saved",
            "ss_scan_bwd_saved_workspace_bytes")
 
@@ -102,7 +104,7 @@ def _load() -> ctypes.CDLL:
     lib.ss_scan_status.restype = I
     lib.ss_scan_status.argtypes = [P, ctypes.c_size_t, P, P]
     lib.ss_set_test_plan.restype = I
-    lib.ss_set_test_plan.argtypes = [I, I, I, I, I, I]
+    lib.ss_set_test_plan.argtypes = [I, I, I, I, I]
     lib.ss_state_update.restype = I
     lib.ss_state_update.argtypes = [P, P, P, P, P, P, P, P, P, I, P, I64, I64, I64, I, P]
     lib.ss_state_update_ex.restype = I
@@ -125,6 +127,11 @@ def _load() -> ctypes.CDLL:
     lib.ss_cross_scan_fwd_workspace_bytes.argtypes = [I64, I64, I64, I64, I64, I]
     lib.ss_cross_scan_fwd.restype = I
     lib.ss_cross_scan_fwd.argtypes = [P, P, P, P, P, P, P, I, P, P, I64, I64, I64, I64, I64, I, P, ctypes.c_size_t, P]
+    lib.ss_cross_scan_fwd_ex_workspace_bytes.restype = ctypes.c_size_t
+    lib.ss_cross_scan_fwd_ex_workspace_bytes.argtypes = [I64, I64, I64, I64, I64, I, I]
+    lib.ss_cross_scan_fwd_ex.restype = I
+    lib.ss_cross_scan_fwd_ex.argtypes = [P, P, P, P, P, P, P, I, P, P, I64, I64, I64, I64, I64, I, I, P,
+                                         ctypes.c_size_t, P]
     lib.ss_conv_update.restype = I
     lib.ss_conv_update.argtypes = [P, P, P, P, I, P, I64, I64, I64, I, P]
     lib.ss_status_string.restype = ctypes.c_char_p
@@ -194,16 +201,15 @@ def _raise_on_timeout(workspace, where, device=None):
 
 
 @contextlib.contextmanager
-def test_plan(segments=0, waves=0, time_parallel=0, spin_limit=0, wait_never=0, cross_two_pass=0):
+def test_plan(segments=0, waves=0, time_parallel=0, spin_limit=0, wait_never=0):
     """Override how the scans split their work (ss_set_test_plan) inside a with block."""
-    rc = lib.ss_set_test_plan(int(segments), int(waves), int(time_parallel), int(spin_limit), int(wait_never),
-                              int(cross_two_pass))
+    rc = lib.ss_set_test_plan(int(segments), int(waves), int(time_parallel), int(spin_limit), int(wait_never))
     if rc != 0:
         raise SSError(rc, "ss_set_test_plan")
     try:
         yield
     finally:
-        lib.ss_set_test_plan(0, 0, 0, 0, 0, 0)
+        lib.ss_set_test_plan(0, 0, 0, 0, 0)
 
 
 _workspaces: dict = {}
@@ -398,9 +404,19 @@ def conv_update(conv_state, x, weight, bias=None, silu=True, out=None):
     return y
 
 
+CROSS_FORMS = {"auto": 0, "one_pass": 1, "two_pass": 2}
+
+
 def cross_scan_fwd(x, delta, A_log, B, C, D, delta_bias=None, delta_softplus=True, return_last_state=False,
-                   out=None, last_state=None, workspace=None, check=False):
-    """VMamba cross scan + merge on the GPU; returns y (maps, H, W, d_in) fp32 (and last_state (maps, 4, d_in, n))."""
+                   out=None, last_state=None, workspace=None, check=False, form="auto"):
+    """VMamba cross scan + merge on the GPU; returns y (maps, H, W, d_in) fp32 (and last_state (maps, 4, d_in, n)).
+
+    form: "auto" (the library's choice), "one_pass" (the four directions summed in LDS by one kernel; n <= 4 and
+    maps of up to about 4000 positions, else SSError(SS_ERR_UNSUPPORTED)) or "two_pass" (per-direction outputs in
+    the workspace, then a merge kernel)."""
+    if form not in CROSS_FORMS:
+        raise ValueError(f"form must be one of {sorted(CROSS_FORMS)}")
+    fcode = CROSS_FORMS[form]
     if x.dim() != 4 or A_log.dim() != 3:
         raise ValueError("x must be (maps, H, W, d_in) and A_log (4, d_in, n)")
     maps, H, W, d_in = x.shape
@@ -425,16 +441,16 @@ def cross_scan_fwd(x, delta, A_log, B, C, D, delta_bias=None, delta_softplus=Tru
         if last_state is not None:
             last_state.zero_()
         return (y, last_state) if return_last_state else y
-    need = int(lib.ss_cross_scan_fwd_workspace_bytes(maps, H, W, d_in, n, code))
+    need = int(lib.ss_cross_scan_fwd_ex_workspace_bytes(maps, H, W, d_in, n, code, fcode))
     if workspace is None:
         workspace = _workspace(dev, need)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     with torch.cuda.device(dev):
-        rc = lib.ss_cross_scan_fwd(_ptr(x), _ptr(delta), _ptr(A_log), _ptr(B), _ptr(C), _ptr(D), _ptr(delta_bias),
-                                   int(bool(delta_softplus)), _ptr(y), _ptr(last_state), maps, H, W, d_in, n, code,
-                                   _ptr(workspace), ws_bytes, _stream(dev))
+        rc = lib.ss_cross_scan_fwd_ex(_ptr(x), _ptr(delta), _ptr(A_log), _ptr(B), _ptr(C), _ptr(D),
+                                      _ptr(delta_bias), int(bool(delta_softplus)), _ptr(y), _ptr(last_state), maps, H,
+                                      W, d_in, n, code, fcode, _ptr(workspace), ws_bytes, _stream(dev))
     if rc != 0:
-        raise SSError(rc, "ss_cross_scan_fwd")
+        raise SSError(rc, "ss_cross_scan_fwd_ex")
     if check:
         _raise_on_timeout(workspace, "ss_cross_scan_fwd")
     return (y, last_state) if return_last_state else y

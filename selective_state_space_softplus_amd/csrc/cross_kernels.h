@@ -62,6 +62,7 @@ struct CrossParams {
 
 constexpr int kCrossCh = 8;          // channels per workgroup
 constexpr int kCrossChunk = 64;      // steps per chunk
+constexpr int kCrossAhead = 2;       // chunks whose loads are in flight ahead of the computed one
 constexpr int kCrossStage = 520;     // words of one staged chunk: 8 channels x 65 (one word of padding)
 
 // Words of the LDS sum of a map slice: 8 per position, and 4 more after every
@@ -319,15 +320,14 @@ __global__ __launch_bounds__(256) void cross_fused(CrossParams p) {
         *reinterpret_cast<float4*>(row + 4) = v1;
     };
 
-    // Two chunks of loads in flight ahead of the one being computed.
-    CrossTile<TIn, NS> tiles[3];
-    load_tile(tiles[0], 0);
-    load_tile(tiles[1], 1);
-    for (int c0 = 0; c0 < nch; c0 += 3) {
-        static_for<0, 3>([&](auto I) __attribute__((always_inline)) {
+    // kCrossAhead chunks of loads in flight ahead of the one being computed.
+    CrossTile<TIn, NS> tiles[kCrossAhead + 1];
+    static_for<0, kCrossAhead>([&](auto I) __attribute__((always_inline)) { load_tile(tiles[decltype(I)::value], decltype(I)::value); });
+    for (int c0 = 0; c0 < nch; c0 += kCrossAhead + 1) {
+        static_for<0, kCrossAhead + 1>([&](auto I) __attribute__((always_inline)) {
             constexpr int i = decltype(I)::value;
             const int c = c0 + i;
-            load_tile(tiles[(i + 2) % 3], c + 2);
+            load_tile(tiles[(i + kCrossAhead) % (kCrossAhead + 1)], c + kCrossAhead);
             if (c + 1 < nch) process(tiles[i], c, std::false_type{});
             else if (c + 1 == nch) {
                 if (L % kCrossChunk == 0) process(tiles[i], c, std::false_type{});

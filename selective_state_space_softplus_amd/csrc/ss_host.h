@@ -50,7 +50,6 @@ struct TestPlan {
     std::atomic<int> tpar{0};        // 1: scan_tpar for n <= 2 (zero initial state, Euler)
     std::atomic<int> spin_limit{0};  // polls before a segment wait gives up
     std::atomic<int> wait_never{0};  // 1: segment waits poll a word nothing sets (they all give up)
-    std::atomic<int> cross_two_pass{0};  // 1: the cross scan through workspace outputs and a merge pass
 };
 
 inline TestPlan& test_plan() {

@@ -328,11 +328,9 @@ SS_EXPORT int ss_scan_status(const void* workspace, size_t workspace_bytes, int3
     return hipGetLastError() == hipSuccess ? SS_OK : SS_ERR_HIP;
 }
 
-SS_EXPORT int ss_set_test_plan(int segments, int waves, int time_parallel, int spin_limit, int wait_never,
-                               int cross_two_pass) {
+SS_EXPORT int ss_set_test_plan(int segments, int waves, int time_parallel, int spin_limit, int wait_never) {
     if (segments < 0 || segments > kMaxSegments || (waves != 0 && waves != 4) || spin_limit < 0 ||
-        (time_parallel != 0 && time_parallel != 1) || (wait_never != 0 && wait_never != 1) ||
-        (cross_two_pass != 0 && cross_two_pass != 1))
+        (time_parallel != 0 && time_parallel != 1) || (wait_never != 0 && wait_never != 1))
         return SS_ERR_SHAPE;
     TestPlan& t = test_plan();
     t.segments.store(segments);
@@ -340,7 +338,6 @@ SS_EXPORT int ss_set_test_plan(int segments, int waves, int time_parallel, int s
     t.tpar.store(time_parallel);
     t.spin_limit.store(spin_limit);
     t.wait_never.store(wait_never);
-    t.cross_two_pass.store(cross_two_pass);
     return SS_OK;
 }
 
@@ -500,21 +497,38 @@ int cross_fused_ns(int64_t n) { return n == 1 ? 1 : n == 2 ? 2 : n <= 4 ? 4 : 0;
 
 // The one-pass cross scan (cross_fused) takes n <= 4 and maps whose sum fits
 // in LDS next to its staging areas, with positions below 2^16 (the exact
-// 32-bit division by H and W) and a map slice whose byte offsets, two chunks
-// past its end included, stay below 2^31; the two-pass form takes the rest.
-bool cross_one_pass(int64_t L, int64_t d_in, int64_t n) {
-    if (test_plan().cross_two_pass.load(std::memory_order_relaxed)) return false;
+// 32-bit division by H and W) and a map slice whose byte offsets, the chunks
+// loaded past its end included, stay below 2^31.
+bool cross_one_pass_fits(int64_t L, int64_t d_in, int64_t n) {
     const int ns = cross_fused_ns(n);
     return ns > 0 && L < (int64_t(1) << 16) && ss::cross_lds_bytes(int(L), ns) <= kMaxLdsBytes &&
-           (L + 2 * ss::kCrossChunk) * d_in * 4 < (int64_t(1) << 31);   // byte offsets of its buffer loads
+           (L + (ss::kCrossAhead + 1) * ss::kCrossChunk) * d_in * 4 < (int64_t(1) << 31);
+}
+
+// The form a call runs: SS_CROSS_AUTO is the two-pass form, the faster of the
+// two on MI355X at every size measured (the one-pass form moves 2.3x fewer
+// bytes at scan-vmamba but takes 1.24x as long: with 8 channels per
+// workgroup, the most its LDS sum allows, it is bound by its memory requests
+// and the per-chunk synchronisation, not by bandwidth).  0: not runnable.
+int cross_form(int form, int64_t L, int64_t d_in, int64_t n) {
+    if (form == SS_CROSS_AUTO || form == SS_CROSS_TWO_PASS) return SS_CROSS_TWO_PASS;
+    if (form == SS_CROSS_ONE_PASS) return cross_one_pass_fits(L, d_in, n) ? SS_CROSS_ONE_PASS : 0;
+    return 0;
+}
+
+SS_EXPORT size_t ss_cross_scan_fwd_ex_workspace_bytes(int64_t maps, int64_t H, int64_t W, int64_t d_in, int64_t n,
+                                                      int dtype, int form) {
+    if (dtype != SS_F32 && dtype != SS_BF16) return 0;
+    if (!cross_sizes_ok(maps, H, W, d_in, n) || n > SS_MAX_STATE) return 0;
+    const int f = cross_form(form, H * W, d_in, n);
+    if (f == 0) return 0;
+    if (f == SS_CROSS_ONE_PASS) return 256;   // the call's status words only
+    return ss_scan_fwd_workspace_bytes(4 * maps, H * W, d_in, n, dtype) + cross_ys_bytes(maps, H * W, d_in);
 }
 
 SS_EXPORT size_t ss_cross_scan_fwd_workspace_bytes(int64_t maps, int64_t H, int64_t W, int64_t d_in, int64_t n,
                                                    int dtype) {
-    if (dtype != SS_F32 && dtype != SS_BF16) return 0;
-    if (!cross_sizes_ok(maps, H, W, d_in, n) || n > SS_MAX_STATE) return 0;
-    if (cross_one_pass(H * W, d_in, n)) return 256;   // the call's status words only
-    return ss_scan_fwd_workspace_bytes(4 * maps, H * W, d_in, n, dtype) + cross_ys_bytes(maps, H * W, d_in);
+    return ss_cross_scan_fwd_ex_workspace_bytes(maps, H, W, d_in, n, dtype, SS_CROSS_AUTO);
 }
 
 template <typename TIn>
@@ -529,14 +543,16 @@ void launch_cross_fused(const ss::CrossParams& p, int ns, hipStream_t st) {
     hipLaunchKernelGGL(kern, grid, dim3(256), lds, st, p);
 }
 
-SS_EXPORT int ss_cross_scan_fwd(const void* x, const void* delta, const float* A_log, const void* B, const void* C,
-                                const float* D, const float* delta_bias, int delta_softplus, float* y,
-                                float* last_state, int64_t maps, int64_t H, int64_t W, int64_t d_in, int64_t n,
-                                int dtype, void* workspace, size_t workspace_bytes, void* stream) {
+SS_EXPORT int ss_cross_scan_fwd_ex(const void* x, const void* delta, const float* A_log, const void* B,
+                                   const void* C, const float* D, const float* delta_bias, int delta_softplus,
+                                   float* y, float* last_state, int64_t maps, int64_t H, int64_t W, int64_t d_in,
+                                   int64_t n, int dtype, int form, void* workspace, size_t workspace_bytes,
+                                   void* stream) {
     if (!x || !delta || !A_log || !B || !C || !D || !y) return SS_ERR_NULL;
     if (!cross_sizes_ok(maps, H, W, d_in, n)) return SS_ERR_SHAPE;
     if (dtype != SS_F32 && dtype != SS_BF16) return SS_ERR_DTYPE;
-    if (n > SS_MAX_STATE) return SS_ERR_UNSUPPORTED;
+    if (form != SS_CROSS_AUTO && form != SS_CROSS_ONE_PASS && form != SS_CROSS_TWO_PASS) return SS_ERR_MODE;
+    if (n > SS_MAX_STATE || cross_form(form, H * W, d_in, n) == 0) return SS_ERR_UNSUPPORTED;
     const int64_t b = 4 * maps, L = H * W;
     const size_t es = elem_size(dtype);
     for (const void* p : {x, delta, B, C})
@@ -554,7 +570,7 @@ SS_EXPORT int ss_cross_scan_fwd(const void* x, const void* delta, const float* A
     for (const Range& r : ins)
         if (overlaps(r, ry) || overlaps(r, rs)) return SS_ERR_ALIAS;
     if (overlaps(ry, rs)) return SS_ERR_ALIAS;
-    const size_t need = ss_cross_scan_fwd_workspace_bytes(maps, H, W, d_in, n, dtype);
+    const size_t need = ss_cross_scan_fwd_ex_workspace_bytes(maps, H, W, d_in, n, dtype, form);
     if (!workspace || workspace_bytes < need) return SS_ERR_WORKSPACE;
     const Range rw = range_of(workspace, int64_t(workspace_bytes), 1);
     for (const Range& r : ins)
@@ -562,7 +578,7 @@ SS_EXPORT int ss_cross_scan_fwd(const void* x, const void* delta, const float* A
     if (overlaps(ry, rw) || overlaps(rs, rw)) return SS_ERR_ALIAS;
 
     hipStream_t st = static_cast<hipStream_t>(stream);
-    if (cross_one_pass(L, d_in, n)) {
+    if (cross_form(form, L, d_in, n) == SS_CROSS_ONE_PASS) {
         ss::CrossParams c{};
         c.x = x;
         c.delta = delta;
@@ -630,6 +646,14 @@ SS_EXPORT int ss_cross_scan_fwd(const void* x, const void* delta, const float* A
     else
         hipLaunchKernelGGL((ss::cross_merge<1>), grid, dim3(256), 0, st, ys, y, maps, int(H), int(W), d_in);
     return hipGetLastError() == hipSuccess ? SS_OK : SS_ERR_HIP;
+}
+
+SS_EXPORT int ss_cross_scan_fwd(const void* x, const void* delta, const float* A_log, const void* B, const void* C,
+                                const float* D, const float* delta_bias, int delta_softplus, float* y,
+                                float* last_state, int64_t maps, int64_t H, int64_t W, int64_t d_in, int64_t n,
+                                int dtype, void* workspace, size_t workspace_bytes, void* stream) {
+    return ss_cross_scan_fwd_ex(x, delta, A_log, B, C, D, delta_bias, delta_softplus, y, last_state, maps, H, W,
+                                d_in, n, dtype, SS_CROSS_AUTO, workspace, workspace_bytes, stream);
 }
 
 // ============================================================================= backward

@@ -378,7 +378,7 @@ void save(const char* name, const void* p, size_t bytes) {
 int run(const std::string& mode) {
     const long long es = arg("dtype") == SS_BF16 ? 2 : 4;
     ss_set_test_plan(int(g_args.count("segments") ? arg("segments") : 0), int(g_args.count("waves") ? arg("waves") : 0),
-                     0, 0, 0, int(g_args.count("cross_two_pass") ? arg("cross_two_pass") : 0));
+                     0, 0, 0);
     if (mode == "fwd" || mode == "noalloc") {
         const long long b = arg("b"), L = arg("L"), d = arg("d_in"), n = arg("n");
         const size_t nel = size_t(b * L * d), nbc = size_t(b * L * n), nst = size_t(b * d * n);
@@ -507,10 +507,11 @@ int run(const std::string& mode) {
         float* bias = static_cast<float*>(load("delta_bias", size_t(4 * d) * 4, true));
         float* y = static_cast<float*>(output(size_t(maps * L * d) * 4));
         float* last = static_cast<float*>(output(size_t(b * d * n) * 4));
-        const size_t wsb = ss_cross_scan_fwd_workspace_bytes(maps, H, W, d, n, int(arg("dtype")));
+        const int form = int(g_args.count("form") ? arg("form") : SS_CROSS_AUTO);
+        const size_t wsb = ss_cross_scan_fwd_ex_workspace_bytes(maps, H, W, d, n, int(arg("dtype")), form);
         void* ws = std::aligned_alloc(256, (wsb + 255) / 256 * 256);
-        const int rc = ss_cross_scan_fwd(x, dl, A, B, C, D, bias, int(arg("softplus")), y, last, maps, H, W, d, n,
-                                         int(arg("dtype")), ws, wsb, nullptr);
+        const int rc = ss_cross_scan_fwd_ex(x, dl, A, B, C, D, bias, int(arg("softplus")), y, last, maps, H, W, d, n,
+                                            int(arg("dtype")), form, ws, wsb, nullptr);
         std::free(ws);
         if (rc != SS_OK) return rc;
         save("y", y, size_t(maps * L * d) * 4);

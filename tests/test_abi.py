@@ -29,6 +29,7 @@ def declared_functions():
 
 def test_header_declares_the_entry_points():
     assert declared_functions() == sorted(["ss_conv_update", "ss_cross_scan_fwd", "ss_cross_scan_fwd_workspace_bytes",
+                                           "ss_cross_scan_fwd_ex", "ss_cross_scan_fwd_ex_workspace_bytes",
                                            "ss_scan_bwd", "ss_scan_bwd_ex", "ss_scan_bwd_workspace_bytes", "ss_scan_fwd",
                                            "ss_scan_fwd_ex", "ss_scan_fwd_noalloc", "ss_scan_status",
                                            "ss_scan_fwd_workspace_bytes", "ss_set_test_plan", "ss_state_update",
@@ -139,12 +140,11 @@ def test_scan_status_rejects(ss):
 
 
 def test_test_plan_validates_and_resets(ss):
-    bad = ((-1, 0, 0, 0, 0, 0), (17, 0, 0, 0, 0, 0), (0, 2, 0, 0, 0, 0), (0, 0, 2, 0, 0, 0), (0, 0, 0, -5, 0, 0),
-           (0, 0, 0, 0, 3, 0), (0, 0, 0, 0, 0, 2))
+    bad = ((-1, 0, 0, 0, 0), (17, 0, 0, 0, 0), (0, 2, 0, 0, 0), (0, 0, 2, 0, 0), (0, 0, 0, -5, 0), (0, 0, 0, 0, 3))
     for args in bad:
         assert ss.lib.ss_set_test_plan(*args) == SHAPE, args
-    assert ss.lib.ss_set_test_plan(4, 4, 1, 100, 1, 1) == OK
-    assert ss.lib.ss_set_test_plan(0, 0, 0, 0, 0, 0) == OK
+    assert ss.lib.ss_set_test_plan(4, 4, 1, 100, 1) == OK
+    assert ss.lib.ss_set_test_plan(0, 0, 0, 0, 0) == OK
     with ss.test_plan(segments=3):
         pass
     with pytest.raises(ss.SSError):
@@ -269,16 +269,19 @@ def test_conv_bias_is_optional(ss):
 
 def cross_args(**over):
     a = dict(x=addr(1), delta=addr(2), A_log=addr(3), B=addr(4), C=addr(5), D=addr(6), bias=addr(7), softplus=1,
-             y=addr(8), last=addr(9), maps=16, H=56, W=56, d_in=384, n=1, dtype=0, ws=addr(10), ws_bytes=1 << 30,
-             stream=None)
+             y=addr(8), last=addr(9), maps=16, H=56, W=56, d_in=384, n=1, dtype=0, form=0, ws=addr(10),
+             ws_bytes=1 << 30, stream=None)
     a.update(over)
     return a
 
 
 def call_cross(ss, a):
-    return ss.lib.ss_cross_scan_fwd(a["x"], a["delta"], a["A_log"], a["B"], a["C"], a["D"], a["bias"], a["softplus"],
-                                    a["y"], a["last"], a["maps"], a["H"], a["W"], a["d_in"], a["n"], a["dtype"],
-                                    a["ws"], a["ws_bytes"], a["stream"])
+    return ss.lib.ss_cross_scan_fwd_ex(a["x"], a["delta"], a["A_log"], a["B"], a["C"], a["D"], a["bias"],
+                                       a["softplus"], a["y"], a["last"], a["maps"], a["H"], a["W"], a["d_in"], a["n"],
+                                       a["dtype"], a["form"], a["ws"], a["ws_bytes"], a["stream"])
+
+
+TWO_PASS_WS = 16 * 16 * 3136 * 384
 
 
 @pytest.mark.parametrize("over,code", [
@@ -286,16 +289,24 @@ def call_cross(ss, a):
     (dict(C=None), NULL), (dict(D=None), NULL), (dict(y=None), NULL),
     (dict(maps=0), SHAPE), (dict(H=0), SHAPE), (dict(W=-2), SHAPE), (dict(d_in=0), SHAPE), (dict(n=0), SHAPE),
     (dict(H=1 << 16, W=1 << 16), SHAPE), (dict(maps=1 << 45), SHAPE),
-    (dict(dtype=3), DTYPE), (dict(n=65), UNSUP),
-    (dict(ws=None), WS), (dict(ws_bytes=10), WS), (dict(ws_bytes=255), WS),
-    (dict(n=5, ws_bytes=16 * 16 * 3136 * 384 - 1), WS), (dict(H=64, W=67, ws_bytes=16 * 16 * 64 * 67 * 384 - 1), WS),
+    (dict(dtype=3), DTYPE), (dict(n=65), UNSUP), (dict(form=3), MODE), (dict(form=-1), MODE),
+    (dict(form=1, n=5), UNSUP), (dict(form=1, H=64, W=67), UNSUP), (dict(form=1, H=64, W=64, n=3), UNSUP),
+    (dict(ws=None), WS), (dict(ws_bytes=10), WS), (dict(ws_bytes=TWO_PASS_WS - 1), WS),
+    (dict(form=2, ws_bytes=TWO_PASS_WS - 1), WS), (dict(form=1, ws_bytes=255), WS),
     (dict(x=addr(1) + 2), ALIGN), (dict(y=addr(8) + 2), ALIGN), (dict(last=addr(9) + 1), ALIGN),
-    (dict(ws=addr(10) + 16), ALIGN),
+    (dict(ws=addr(10) + 16), ALIGN), (dict(form=1, ws=addr(10) + 16), ALIGN),
     (dict(y=addr(1)), ALIAS), (dict(last=addr(3)), ALIAS), (dict(y=addr(9)), ALIAS), (dict(ws=addr(8)), ALIAS),
-    (dict(bias=addr(9) + 8), ALIAS),
+    (dict(bias=addr(9) + 8), ALIAS), (dict(form=1, y=addr(1)), ALIAS),
 ])
 def test_cross_rejects(ss, over, code):
     assert call_cross(ss, cross_args(**over)) == code
+
+
+def test_cross_plain_entry_is_the_auto_form(ss):
+    a = cross_args(ws_bytes=TWO_PASS_WS - 1)
+    assert ss.lib.ss_cross_scan_fwd(a["x"], a["delta"], a["A_log"], a["B"], a["C"], a["D"], a["bias"], a["softplus"],
+                                    a["y"], a["last"], a["maps"], a["H"], a["W"], a["d_in"], a["n"], a["dtype"],
+                                    a["ws"], a["ws_bytes"], a["stream"]) == WS
 
 
 def test_cross_optional_pointers_may_be_null(ss):
@@ -304,17 +315,20 @@ def test_cross_optional_pointers_may_be_null(ss):
 
 def test_cross_workspace_query(ss):
     q = ss.lib.ss_cross_scan_fwd_workspace_bytes
-    q.restype = ctypes.c_size_t
-    # One kernel (n <= 4, the map's sum in LDS): the status words only.
-    assert q(16, 56, 56, 384, 1, 0) == 256 == q(16, 56, 56, 384, 4, 1) == q(3, 64, 64, 8, 2, 0)
-    # Two passes: n > 4, a map too large for LDS (64 x 67 at n = 1; 64 x 64 at n = 3, 4), or forced.
-    two = 16 * 16 * 3136 * 384 + ss.scan_fwd_workspace_bytes(64, 3136, 384, 5, 0)
-    assert q(16, 56, 56, 384, 5, 0) >= two
-    assert q(1, 64, 67, 8, 1, 0) > 256 and q(1, 64, 64, 8, 3, 0) > 256 and q(1, 64, 64, 8, 2, 0) == 256
-    with ss.test_plan(cross_two_pass=1):
-        assert q(16, 56, 56, 384, 1, 0) >= 16 * 16 * 3136 * 384 + ss.scan_fwd_workspace_bytes(64, 3136, 384, 1, 0)
+    qx = ss.lib.ss_cross_scan_fwd_ex_workspace_bytes
+    full = q(16, 56, 56, 384, 1, 0)
+    assert full >= TWO_PASS_WS + ss.scan_fwd_workspace_bytes(64, 3136, 384, 1, 0)
+    assert full == q(16, 56, 56, 384, 1, 1) == qx(16, 56, 56, 384, 1, 0, 0) == qx(16, 56, 56, 384, 1, 0, 2)
+    # One pass: the status words only, where the map's sum fits in LDS (n <= 4).
+    assert qx(16, 56, 56, 384, 1, 0, 1) == 256 == qx(16, 56, 56, 384, 4, 1, 1) == qx(3, 64, 65, 8, 2, 0, 1)
+    assert qx(1, 4265, 1, 8, 1, 0, 1) == 256 and qx(1, 4266, 1, 8, 1, 0, 1) == 0
+    assert qx(1, 4205, 1, 8, 2, 0, 1) == 256 and qx(1, 4206, 1, 8, 2, 0, 1) == 0
+    assert qx(1, 4084, 1, 8, 3, 0, 1) == 256 and qx(1, 4085, 1, 8, 4, 0, 1) == 0
+    assert qx(1, 5, 5, 8, 5, 0, 1) == 0
     for bad in ((0, 5, 5, 8, 1, 0), (1, 0, 5, 8, 1, 0), (1, 5, 5, 8, 65, 0), (1, 5, 5, 8, 1, 2)):
         assert q(*bad) == 0, bad
+        assert qx(*bad, 1) == 0, bad
+    assert qx(1, 5, 5, 8, 1, 0, 7) == 0
 
 
 def bwd_args(**over):

@@ -6,11 +6,12 @@ both backwards) and the four outputs are added back at their positions
 sequence).  The output map is fp32 whatever the input dtype, and the oracle
 sees the same (bf16-exact) inputs, so every case is held to the fp32 bound,
 max relative error 1e-4; last states likewise.  Both forms of the call are
-covered: one kernel that adds the directions into an LDS sum (n <= 4, maps up
-to about 4096 positions; the default there) and the two-pass form
-(per-direction outputs in the workspace, then a merge), which the test plan
-can force.  The two-pass form is identical bit for bit to the unfused path on
-the GPU (torch-made traversal copies, ss_scan_fwd, torch merge).
+covered: the two-pass form (per-direction outputs in the workspace, then a
+merge; the default) and the one-pass form (one kernel that adds the
+directions into an LDS sum; n <= 4 and maps of up to 4084..4265 positions,
+beyond which it returns SS_ERR_UNSUPPORTED).  The two-pass form is identical
+bit for bit to the unfused path on the GPU (torch-made traversal copies,
+ss_scan_fwd, torch merge).
 """
 import numpy as np
 import pytest
@@ -46,17 +47,32 @@ def cross_inputs(maps, H, W, d_in, n, dtype, seed, bias=True, shared_params=Fals
                 B=r(maps, 4, L, n).to(dtype), C=r(maps, 4, L, n).to(dtype), D=D, delta_bias=db)
 
 
-def run_gpu(ss, c, softplus=True):
+# Largest map (positions) the one-pass form takes, by state size: its LDS sum
+# (8.5 words a position), staging and B, C areas within 160 KB.
+ONE_PASS_MAX_L = {1: 4265, 2: 4205, 3: 4084, 4: 4084}
+
+
+def one_pass_fits(H, W, n):
+    return n in ONE_PASS_MAX_L and H * W <= ONE_PASS_MAX_L[n]
+
+
+def run_gpu(ss, c, softplus=True, form="auto"):
     g = {k: (v.to(DEV) if isinstance(v, torch.Tensor) else v) for k, v in c.items()}
     y, last = ss.cross_scan_fwd(g["x"], g["delta"], g["A_log"], g["B"], g["C"], g["D"], g["delta_bias"], softplus,
-                                return_last_state=True)
+                                return_last_state=True, form=form)
     torch.cuda.synchronize()
     return y, last
 
 
-def check(ss, c, what, softplus=True, two_pass=False):
-    with ss.test_plan(cross_two_pass=int(two_pass)):
-        y, last = run_gpu(ss, c, softplus)
+def check(ss, c, what, softplus=True, form="auto"):
+    maps, H, W, _ = c["x"].shape
+    n = c["A_log"].shape[2]
+    if form == "one_pass" and not one_pass_fits(H, W, n):
+        with pytest.raises(ss.SSError) as e:
+            run_gpu(ss, c, softplus, form)
+        assert ss.STATUS[e.value.code] == "SS_ERR_UNSUPPORTED"
+        return 0.0, 0.0
+    y, last = run_gpu(ss, c, softplus, form)
     yr, lr = oracle.cross_scan(c["x"], c["delta"], c["A_log"], c["B"], c["C"], c["D"], c["delta_bias"], softplus)
     e1 = assert_close(y, yr, F32, f"{what} y")
     e2 = assert_close(last, lr, F32, f"{what} last_state")
@@ -72,19 +88,26 @@ SMALL = [
 ]
 
 
-@pytest.mark.parametrize("two_pass", [False, True])
+@pytest.mark.parametrize("form", ["auto", "one_pass"])
 @pytest.mark.parametrize("maps,H,W,d_in,n,dtype", SMALL)
-def test_cross_small(ss, maps, H, W, d_in, n, dtype, two_pass):
-    say(f"cross maps={maps} {H}x{W} d_in={d_in} n={n} {dtype} two_pass={two_pass}")
+def test_cross_small(ss, maps, H, W, d_in, n, dtype, form):
+    say(f"cross maps={maps} {H}x{W} d_in={d_in} n={n} {dtype} form={form}")
     check(ss, cross_inputs(maps, H, W, d_in, n, dtype, seed=maps + H * 7 + W * 11 + n), f"{H}x{W} n={n}",
-          two_pass=two_pass)
+          form=form)
 
 
-def test_cross_without_softplus_or_bias(ss):
-    say("cross without softplus or bias")
+@pytest.mark.parametrize("form", ["auto", "one_pass"])
+def test_cross_without_softplus_or_bias(ss, form):
+    say(f"cross without softplus or bias, form={form}")
     c = cross_inputs(2, 6, 5, 40, 1, F32, seed=3, bias=False)
     c["delta"] = c["delta"].abs() * 0.1 + 0.01
-    check(ss, c, "no softplus", softplus=False)
+    check(ss, c, "no softplus", softplus=False, form=form)
+
+
+def test_cross_rejects_an_unknown_form(ss):
+    c = cross_inputs(1, 4, 4, 8, 1, F32, seed=1)
+    with pytest.raises(ValueError):
+        run_gpu(ss, c, form="three_pass")
 
 
 @pytest.mark.parametrize("segments,n", [(3, 1), (5, 16)])
@@ -93,17 +116,17 @@ def test_cross_segments(ss, segments, n):
     say(f"cross with {segments} segments n={n}")
     c = cross_inputs(1, 20, 30, 64, n, F32, seed=9 + n)
     with plan(segments=segments):
-        check(ss, c, f"segments={segments}", two_pass=True)
+        check(ss, c, f"segments={segments}", form="two_pass")
 
 
-@pytest.mark.parametrize("two_pass", [False, True])
-def test_cross_vmamba_workload_full(ss, two_pass):
+@pytest.mark.parametrize("form", ["two_pass", "one_pass"])
+def test_cross_vmamba_workload_full(ss, form):
     """The scan-vmamba workload (16 maps of 56 x 56 x 384, n = 1, fp32), compared in full."""
     cfg = workloads.CONFIGS[3]
-    say(f"cross scan at {cfg.name} size, full compare, two_pass={two_pass}")
+    say(f"cross scan at {cfg.name} size, full compare, form={form}")
     c = workloads.cross_scan_inputs(3)
-    e1, e2 = check(ss, c, cfg.name, two_pass=two_pass)
-    print(f"{cfg.name} cross scan (two_pass={two_pass}): y err {e1:.3g}, last_state err {e2:.3g}")
+    e1, e2 = check(ss, c, cfg.name, form=form)
+    print(f"{cfg.name} cross scan ({form}): y err {e1:.3g}, last_state err {e2:.3g}")
 
 
 def test_cross_equals_unrolled_scan_and_merge(ss):
@@ -112,9 +135,8 @@ def test_cross_equals_unrolled_scan_and_merge(ss):
     say("fused cross scan vs unrolled scan + merge")
     maps, H, W, d_in, n = 3, 12, 9, 96, 1
     c = cross_inputs(maps, H, W, d_in, n, F32, seed=17, shared_params=True)
-    y1, last1 = run_gpu(ss, c)
-    with ss.test_plan(cross_two_pass=1):
-        y, last = run_gpu(ss, c)
+    y1, last1 = run_gpu(ss, c, form="one_pass")
+    y, last = run_gpu(ss, c)
     g = {k: (v.to(DEV) if isinstance(v, torch.Tensor) else v) for k, v in c.items()}
     L = H * W
     u = workloads.vmamba_unroll(g["x"])                                       # (maps*4, L, d_in)
@@ -132,11 +154,12 @@ def test_cross_equals_unrolled_scan_and_merge(ss):
     assert_close(last1, last, F32, "one kernel vs unrolled, last_state")
 
 
-@pytest.mark.parametrize("n,dtype", [(16, BF16), (1, F32), (2, BF16)])
-def test_cross_is_deterministic(ss, n, dtype):
-    say(f"cross scan run-to-run determinism n={n}")
+@pytest.mark.parametrize("n,dtype,form", [(16, BF16, "auto"), (1, F32, "auto"), (1, F32, "one_pass"),
+                                          (2, BF16, "one_pass"), (4, F32, "one_pass")])
+def test_cross_is_deterministic(ss, n, dtype, form):
+    say(f"cross scan run-to-run determinism n={n} form={form}")
     c = cross_inputs(2, 40, 39, 72, n, dtype, seed=23)
-    y1, l1 = run_gpu(ss, c)
+    y1, l1 = run_gpu(ss, c, form=form)
     for _ in range(3):
-        y2, l2 = run_gpu(ss, c)
+        y2, l2 = run_gpu(ss, c, form=form)
         assert torch.equal(y1, y2) and torch.equal(l1, l2)

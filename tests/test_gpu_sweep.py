@@ -113,6 +113,6 @@ def test_cross_sweep(ss, seed):
     H, W = (r.randint(1, 70), r.randint(1, 70)) if r.random() < 0.25 else (r.randint(1, 12), r.randint(1, 12))
     n = r.choice([1, 1, 2, 3, 4] + STATES[:8])
     d_in = r.choice(CHANNELS) if H * W * n < 2000 else r.choice(CHANNELS[:5])
-    dtype, bias, two_pass = r.choice([F32, BF16]), r.random() < 0.6, r.random() < 0.25
-    say(f"cross sweep seed={seed} maps={maps} {H}x{W} d_in={d_in} n={n} {dtype} bias={bias} two_pass={two_pass}")
-    cross_check(ss, cross_inputs(maps, H, W, d_in, n, dtype, seed, bias=bias), f"seed {seed}", two_pass=two_pass)
+    dtype, bias, form = r.choice([F32, BF16]), r.random() < 0.6, r.choice(["auto", "one_pass", "one_pass"])
+    say(f"cross sweep seed={seed} maps={maps} {H}x{W} d_in={d_in} n={n} {dtype} bias={bias} form={form}")
+    cross_check(ss, cross_inputs(maps, H, W, d_in, n, dtype, seed, bias=bias), f"seed {seed}", form=form)

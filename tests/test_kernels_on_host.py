@@ -173,7 +173,7 @@ def test_step_on_host(b, d, n, dt, zoh):
 
 
 CROSS = [
-    # maps, H, W, d_in, n, dtype, bias, two_pass
+    # maps, H, W, d_in, n, dtype, bias, two_pass (else the one-pass form)
     (2, 5, 7, 24, 1, F32, False, True),      # the two-pass form (workspace outputs + merge), two segments
     (2, 5, 7, 24, 1, F32, True, False),      # one pass, L = 35: a single ragged chunk
     (1, 9, 15, 20, 1, F32, True, False),     # L = 135: three chunks, the last ragged; d_in not a multiple of 8
@@ -195,7 +195,7 @@ def test_cross_on_host(maps, H, W, d, n, dt, bias, two_pass):
     db = (torch.rand(4, d, generator=g) - 0.5) if bias else None
     t = dict(x=x, delta=delta, A_log=A_log, B=B, C=C, D=D, delta_bias=db)
     got = hk.run("cross", t, dict(maps=maps, H=H, W=W, d_in=d, n=n, dtype=_code(dt), softplus=1,
-                                  segments=2 if two_pass else 0, cross_two_pass=int(two_pass)),
+                                  segments=2 if two_pass else 0, form=2 if two_pass else 1),
                  dict(y=((maps, H, W, d), F32), last_state=((maps, 4, d, n), F32)))
     yr, lr = oracle.cross_scan(x, delta, A_log, B, C, D, db, True)
     assert_close(got["y"], yr, F32, "host cross y")
