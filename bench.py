@@ -198,6 +198,52 @@ def other_workloads(ss, torch, workloads, dev, reps=20):
     return out
 
 
+def valu_probe(torch, dev, iters=16384, reps=10, settle_s=0.3):
+    """Issue rates of fp32 FMA, multiply and exp2 chains (libss_probe.so) at 8, 4 and 2 waves per SIMD.
+
+    Each work-item runs `iters` steps of 8 independent chains; a step is one
+    v_fma_f32 (mix 0), one v_mul_f32 (mix 1), one v_exp_f32 plus one
+    v_mul_f32 (mix 2) or one v_exp_f32 (mix 3).  The issue cost of
+    v_exp_f32, in multiplies, is t3 / t1 alone and t2 / t1 - 1 mixed.  The
+    probe first runs untimed for `settle_s` seconds so the clocks settle.
+    """
+    import ctypes
+
+    lib = ctypes.CDLL(os.path.join(ROOT, "selective_state_space_softplus_amd", "libss_probe.so"))
+    lib.ss_probe_valu.restype = ctypes.c_int
+    lib.ss_probe_valu.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    out = torch.empty(cus * 8 * 256, device=dev)
+    stream = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+    run = lambda mix, blocks: lib.ss_probe_valu(mix, blocks, iters, ctypes.c_void_p(out.data_ptr()), stream)  # noqa: E731
+    t0 = time.time()
+    while time.time() - t0 < settle_s:
+        assert run(0, cus * 4) == 0
+        torch.cuda.synchronize()
+    res = {"metric": "VALU issue rates (probe)", "cus": cus, "iters": iters, "chains_per_work_item": 8}
+    for waves_per_simd in (8, 4, 2):
+        blocks = cus * waves_per_simd     # 256 work-items = 4 waves a block, one per SIMD
+        row = {}
+        for mix, name, instr in ((0, "fma", 1), (1, "mul", 1), (2, "exp2+mul", 2), (3, "exp2", 1)):
+            assert run(mix, blocks) == 0
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(reps):
+                run(mix, blocks)
+            e1.record()
+            torch.cuda.synchronize()
+            ms = e0.elapsed_time(e1) / reps
+            lane_instr = blocks * 256 * iters * 8 * instr
+            row[name] = {"ms": round(ms, 4), "lane_instr_per_s_T": round(lane_instr / (ms * 1e-3) / 1e12, 2)}
+        row["exp2_cost_in_muls_alone"] = round(row["exp2"]["ms"] / row["mul"]["ms"], 3)
+        row["exp2_cost_in_muls_mixed"] = round(row["exp2+mul"]["ms"] / row["mul"]["ms"] - 1.0, 3)
+        res[f"{waves_per_simd}_waves_per_simd"] = row
+    res["fp32_vector_peak_T"] = round(cus * 4 * 16 * 2.4e9 / 1e12, 2)
+    print(json.dumps(res), flush=True)
+    return 0
+
+
 def copy_probe(torch, dev, nbytes=1 << 30, reps=5):
     """A plain device copy of known size: each launch reads and writes nbytes."""
     src = torch.ones(nbytes // 4, dtype=torch.float32, device=dev)
@@ -330,6 +376,8 @@ def main(argv=None):
     ap.add_argument("--no-bwd", action="store_true", help="skip the backward-pass measurement")
     ap.add_argument("--no-others", action="store_true", help="skip the scan-tiny, scan-mid and scan-vmamba timings")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target duration of the CPU baseline sample")
+    ap.add_argument("--valu-probe", action="store_true",
+                    help="only time the VALU issue-rate probe (fma, mul, exp2 chains) and print its JSON line")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy (calibrates the HBM byte counters)")
     ap.add_argument("--sweep", action="store_true",
@@ -349,6 +397,8 @@ def main(argv=None):
     torch.cuda.set_device(0)
     if args.copy_probe:
         return copy_probe(torch, dev)
+    if args.valu_probe:
+        return valu_probe(torch, dev)
     if args.sweep:
         return shape_sweep(torch, ss, workloads, dev)
     cfg = workloads.CONFIGS[2]

@@ -20,6 +20,9 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIBRARY = os.path.join(PKG, "libss_scan.so")
+# The VALU issue-rate probe that bench.py --valu-probe runs (a measurement aid).
+PROBE_SOURCE = os.path.join(CSRC, "valu_probe.hip")
+PROBE_LIBRARY = os.path.join(PKG, "libss_probe.so")
 # The C ABI and the small kernels in one translation unit; the scan_seq and
 # scan_bwd launchers (launch_seq.h, launch_bwd.h) are instantiated once per
 # input type and launch shape, each in a small generated unit of its own, so
@@ -89,6 +92,11 @@ def build(output: str = LIBRARY, verbose: bool = False) -> str:
         tmp = output + ".tmp"
         _run(link_command(objects, tmp), verbose)
         os.replace(tmp, output)
+        if output == LIBRARY:
+            probe_obj = os.path.join(objdir, "valu_probe.hip.o")
+            _run(compile_command(PROBE_SOURCE, probe_obj), verbose)
+            _run(link_command([probe_obj], PROBE_LIBRARY + ".tmp"), verbose)
+            os.replace(PROBE_LIBRARY + ".tmp", PROBE_LIBRARY)
     finally:
         shutil.rmtree(objdir, ignore_errors=True)
     return output
