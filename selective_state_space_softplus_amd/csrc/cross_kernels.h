@@ -30,8 +30,9 @@
 // that the compiler sees every load issued and waits only for the oldest).
 //
 // The outputs of a chunk go to a staging area in LDS (one per direction,
-// double-buffered); after one barrier, thread (k, i) adds step i of direction
-// k into the sum of its map position, together with the contributions of the
+// double-buffered); after the barrier that ends the chunk's iteration, the
+// next iteration (once it has computed its own chunk) has thread (k, i) add
+// step i of direction k into the sum of its map position, together with the contributions of the
 // other directions that visited the same position in the same chunk -- the
 // thread of the lowest such direction does all of them, the others skip it.
 // So every position is updated by one thread per chunk, in the order (chunk,
@@ -282,7 +283,12 @@ __global__ __launch_bounds__(256) void cross_fused(CrossParams p) {
         float* st = stage + ((c & 1) * 4 + k) * kCrossStage + ci * 65 + s * 8;
 #pragma unroll
         for (int j = 0; j < 8; j++) st[j] = yv[j];
-        barrier_lds();
+    };
+
+    // The sums of chunk c's positions, from its staged outputs (after the
+    // barrier that follows the chunk's computation).
+    auto add_chunk = [&](int c, auto tail) __attribute__((always_inline)) {
+        constexpr bool TAIL = decltype(tail)::value;
         // Thread (k, lane): the position pp of step c*64 + lane of direction k.
         // Its other visits are at steps pp and L-1-pp (row-major) and tc and
         // L-1-tc (column-major); every direction visiting pp in this chunk is
@@ -321,6 +327,9 @@ __global__ __launch_bounds__(256) void cross_fused(CrossParams p) {
     };
 
     // kCrossAhead chunks of loads in flight ahead of the one being computed.
+    // Iteration c computes chunk c and then adds chunk c - 1, whose outputs
+    // every wave staged before the last barrier: one barrier an iteration, and
+    // a wave's adds overlap its own and the other waves' computation.
     CrossTile<TIn, NS> tiles[kCrossAhead + 1];
     static_for<0, kCrossAhead>([&](auto I) __attribute__((always_inline)) { load_tile(tiles[decltype(I)::value], decltype(I)::value); });
     for (int c0 = 0; c0 < nch; c0 += kCrossAhead + 1) {
@@ -328,13 +337,16 @@ __global__ __launch_bounds__(256) void cross_fused(CrossParams p) {
             constexpr int i = decltype(I)::value;
             const int c = c0 + i;
             load_tile(tiles[(i + kCrossAhead) % (kCrossAhead + 1)], c + kCrossAhead);
-            if (c + 1 < nch) process(tiles[i], c, std::false_type{});
-            else if (c + 1 == nch) {
-                if (L % kCrossChunk == 0) process(tiles[i], c, std::false_type{});
+            if (c < nch) {
+                if (c + 1 < nch || L % kCrossChunk == 0) process(tiles[i], c, std::false_type{});
                 else process(tiles[i], c, std::true_type{});
+                if (c > 0) add_chunk(c - 1, std::false_type{});
+                barrier_lds();
             }
         });
     }
+    if (L % kCrossChunk == 0) add_chunk(nch - 1, std::false_type{});
+    else add_chunk(nch - 1, std::true_type{});
 
     if (p.last_state && cv && s == 0) {
 #pragma unroll
