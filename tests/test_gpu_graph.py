@@ -79,3 +79,30 @@ def test_scan_bwd_graph_replays(ss, zoh):
             torch.cuda.synchronize()
             for k in ref:
                 assert torch.equal(got[k], ref[k]), f"{k}, replay {rep}"
+
+
+@pytest.mark.parametrize("form", ["two_pass", "one_pass"])
+def test_cross_scan_graph_replays(ss, form):
+    say(f"cross scan in a HIP graph, form={form}")
+    c = to_dev(workloads.cross_scan_inputs(3, seed=41))
+    args = (c["x"][:3].contiguous(), c["delta"][:3].contiguous(), c["A_log"], c["B"][:3].contiguous(),
+            c["C"][:3].contiguous(), c["D"], c["delta_bias"], True)
+    other = (c["x"][3:5].contiguous(), c["delta"][3:5].contiguous(), c["A_log"], c["B"][3:5].contiguous(),
+             c["C"][3:5].contiguous(), c["D"], c["delta_bias"], True)
+    maps, H, W, d_in = args[0].shape
+    with plan(segments=3):
+        y_e, last_e = ss.cross_scan_fwd(*args, return_last_state=True, form=form)
+        y_g, last_g = torch.empty_like(y_e), torch.empty_like(last_e)
+        code = {"two_pass": 2, "one_pass": 1}[form]
+        ws = torch.empty(ss.lib.ss_cross_scan_fwd_ex_workspace_bytes(maps, H, W, d_in, 1, 0, code),
+                         dtype=torch.uint8, device=DEV)
+        graph, _ = _capture(lambda: ss.cross_scan_fwd(*args, return_last_state=True, out=y_g, last_state=last_g,
+                                                      workspace=ws, form=form))
+        for rep in range(3):
+            y_g.zero_()
+            last_g.zero_()
+            ss.cross_scan_fwd(*other, form=form)
+            torch.cuda.synchronize()
+            graph.replay()
+            torch.cuda.synchronize()
+            assert torch.equal(y_g, y_e) and torch.equal(last_g, last_e), f"replay {rep}"

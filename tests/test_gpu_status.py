@@ -81,3 +81,20 @@ def test_forced_timeout_backward_and_cross(ss):
             ss.cross_scan_fwd(*args, check=True)
         assert e.value.code == ss.SS_ERR_TIMEOUT
     assert torch.equal(ss.cross_scan_fwd(*args, check=True), y_ok)
+
+
+def test_one_pass_cross_clears_a_stale_status(ss):
+    """The one-pass cross scan waits on nothing, so it clears the status words a timed-out call left."""
+    say("one-pass cross scan after a forced timeout in the same workspace")
+    c = to_dev(workloads.cross_scan_inputs(3, seed=9))
+    args = (c["x"][:2].contiguous(), c["delta"][:2].contiguous(), c["A_log"], c["B"][:2].contiguous(),
+            c["C"][:2].contiguous(), c["D"], c["delta_bias"], True)
+    maps, H, W, d_in = args[0].shape
+    ws = torch.empty(ss.lib.ss_cross_scan_fwd_ex_workspace_bytes(maps, H, W, d_in, 1, 0, 2), dtype=torch.uint8,
+                     device=DEV)
+    with ss.test_plan(segments=4, spin_limit=20, wait_never=1):
+        ss.cross_scan_fwd(*args, workspace=ws, form="two_pass")
+        assert ss.scan_status(ws) == ss.SS_ERR_TIMEOUT
+    y1 = ss.cross_scan_fwd(*args, workspace=ws, form="one_pass", check=True)
+    assert ss.scan_status(ws) == 0
+    assert torch.equal(y1, ss.cross_scan_fwd(*args, form="one_pass"))
