@@ -21,22 +21,28 @@
 // them into the pair (P, H) = (prod a_j, state after the 8 steps from zero),
 // and the 8 sub-chunks of a channel (8 neighbouring lanes) are combined by an
 // inclusive scan over s with DPP row shifts, (P1, H1) then (P2, H2) ->
-// (P1 P2, P2 H1 + H2), which gives
-// every lane the state entering its sub-chunk from the chunk's carried state;
-// it then walks its 8 steps again from there, producing the outputs.  The
-// decays and inputs stay in registers between the two walks, so the second
-// costs one FMA per step and state.  Each chunk's inputs are loaded two
-// chunks ahead (unconditionally, past the end at a clamped chunk index, so
-// that the compiler sees every load issued and waits only for the oldest).
+// (P1 P2, P2 H1 + H2), which gives every lane the state entering its
+// sub-chunk from the chunk's carried state; it then walks its 8 steps again
+// from there, producing the outputs.  The decays and inputs stay in
+// registers between the two walks, so the second costs one FMA per step and
+// state.  Each chunk's inputs are loaded two chunks ahead by buffer loads
+// (issued unconditionally: past the end they read 0, so the compiler sees
+// every load issued and waits only for the oldest).
 //
 // The outputs of a chunk go to a staging area in LDS (one per direction,
-// double-buffered); after the barrier that ends the chunk's iteration, the
-// next iteration (once it has computed its own chunk) has thread (k, i) add
-// step i of direction k into the sum of its map position, together with the contributions of the
-// other directions that visited the same position in the same chunk -- the
-// thread of the lowest such direction does all of them, the others skip it.
-// So every position is updated by one thread per chunk, in the order (chunk,
-// direction): no atomics, and the same bits on every run.
+// double-buffered).  After the barrier that ends the chunk's iteration, the
+// next iteration, once it has computed its own chunk, has thread (k, i) add
+// step i of direction k into the sum of its map position, together with the
+// contributions of the other directions that visited the same position in
+// the same chunk -- the thread of the lowest such direction does all of
+// them, the others skip it.  So every position is updated by one thread per
+// chunk, in the order (chunk, direction): no atomics, and the same bits on
+// every run.
+//
+// ss_cross_scan_fwd_ex selects this kernel for SS_CROSS_ONE_PASS.  It moves
+// 2.3x fewer bytes than the two-pass form but is slower on MI355X (8
+// channels per workgroup, all its LDS allows, means 32-byte row segments and
+// one workgroup per compute unit), so the two-pass form is the default.
 #pragma once
 
 #include "ss_device.h"
