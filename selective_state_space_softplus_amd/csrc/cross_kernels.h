@@ -25,9 +25,11 @@
 // sub-chunk from the chunk's carried state; it then walks its 8 steps again
 // from there, producing the outputs.  The decays and inputs stay in
 // registers between the two walks, so the second costs one FMA per step and
-// state.  Each chunk's inputs are loaded two chunks ahead by buffer loads
-// (issued unconditionally: past the end they read 0, so the compiler sees
-// every load issued and waits only for the oldest).
+// state.  The first half (all but the carried state) of chunk c + 1 runs
+// beside the second half of chunk c.  Each chunk's inputs are loaded two
+// iterations ahead by buffer loads (issued unconditionally: past the end they
+// read 0, so the compiler sees every load issued and waits only for the
+// oldest).
 //
 // The outputs of a chunk go to a staging area in LDS (one per direction,
 // double-buffered).  After the barrier that ends the chunk's iteration, the
@@ -69,7 +71,7 @@ struct CrossParams {
 
 constexpr int kCrossCh = 8;          // channels per workgroup
 constexpr int kCrossChunk = 64;      // steps per chunk
-constexpr int kCrossAhead = 2;       // chunks whose loads are in flight ahead of the computed one
+constexpr int kCrossAhead = 2;       // iterations a chunk's loads are issued ahead of their use
 constexpr int kCrossStage = 520;     // words of one staged chunk: 8 channels x 65 (one word of padding)
 
 // Words of the LDS sum of a map slice: 8 per position, and 4 more after every
@@ -228,10 +230,16 @@ __global__ __launch_bounds__(256) void cross_fused(CrossParams p) {
 
     float* spare = bcw + 2 * kCrossChunk * NS * (4 - k) + k * 8;   // this wave's spare row (after all B, C areas)
 
-    // One chunk.  TAIL: the last chunk, which ends past L (steps past the end
-    // then decay by 1 and add nothing, and have no position to add to).
-    auto process = [&](const CrossTile<TIn, NS>& tl, int c, auto tail) __attribute__((always_inline)) {
-        constexpr bool TAIL = decltype(tail)::value;
+    // A chunk in two halves.  local(): what needs no carried state -- the
+    // step sizes, decays and inputs of the lane's 8 steps, its sub-chunk's
+    // (P, H) from a zero state and their scan over the 8 sub-chunks (steps
+    // past L decay by 1 and add nothing).  finish(): the carried state applied,
+    // the 8 steps walked again, the outputs staged.  The loop below runs
+    // chunk c + 1's local() beside chunk c's finish(): two independent chains.
+    struct Local {
+        float a[8][NS], bu[8][NS], cc[8][NS], yv[8], P[NS], Hh[NS];
+    };
+    auto local = [&](const CrossTile<TIn, NS>& tl, int c, Local& r) __attribute__((always_inline)) {
         const int t0 = c * kCrossChunk + s * 8;
         // B and C of the chunk through this wave's LDS: [step][state].
 #pragma unroll
@@ -242,32 +250,30 @@ __global__ __launch_bounds__(256) void cross_fused(CrossParams p) {
         // The wave's own lanes read what the others wrote: LDS accesses of one
         // wave complete in order, so only the compiler must keep them so.
         __builtin_amdgcn_wave_barrier();
-        float a[8][NS], bu[8][NS];
         float dsum = 0.0f;
 #pragma unroll
         for (int j = 0; j < 8; j++) {
             float dl = RT::f(tl.dl[j]) + bias;
             if constexpr (SP) dl = softplus(dl);
-            const bool ok = !TAIL || t0 + j < L;
-            if constexpr (TAIL) dl = ok ? dl : 0.0f;
-            const float du = dl * RT::f(tl.u[j]);
+            const bool ok = t0 + j < L;
+            dl = ok ? dl : 0.0f;
+            const float u = RT::f(tl.u[j]);
+            const float du = dl * u;
             dsum += dl;
+            r.yv[j] = Dv * u;
 #pragma unroll
             for (int q = 0; q < NS; q++) {
-                a[j][q] = exp2_hw(dl * A2[q]);
+                r.a[j][q] = exp2_hw(dl * A2[q]);
                 const float b = du * bcw[(s * 8 + j) * NS + q];
-                bu[j][q] = TAIL ? (ok ? b : 0.0f) : b;
+                r.bu[j][q] = ok ? b : 0.0f;
+                r.cc[j][q] = bcw[kCrossChunk * NS + (s * 8 + j) * NS + q];
             }
         }
-        float yv[8];
-#pragma unroll
-        for (int j = 0; j < 8; j++) yv[j] = Dv * RT::f(tl.u[j]);
 #pragma unroll
         for (int q = 0; q < NS; q++) {
-            // This lane's sub-chunk from a zero state, then the scan over the 8 sub-chunks.
             float P = exp2_hw(dsum * A2[q]), Hh = 0.0f;
 #pragma unroll
-            for (int j = 0; j < 8; j++) Hh = fmaf(a[j][q], Hh, bu[j][q]);
+            for (int j = 0; j < 8; j++) Hh = fmaf(r.a[j][q], Hh, r.bu[j][q]);
             static_for<0, 3>([&](auto I) __attribute__((always_inline)) {
                 constexpr int off = 1 << decltype(I)::value;
                 const float Pp = dpp_row_shr<off>(P), Hp = dpp_row_shr<off>(Hh);
@@ -276,14 +282,24 @@ __global__ __launch_bounds__(256) void cross_fused(CrossParams p) {
                 Hh = in ? Hn : Hh;
                 P = in ? Pn : P;
             });
-            const float hend = fmaf(P, hc[q], Hh);          // state after sub-chunk s
+            r.P[q] = P;
+            r.Hh[q] = Hh;
+        }
+    };
+    auto finish = [&](const Local& r, int c) __attribute__((always_inline)) {
+        float yv[8];
+#pragma unroll
+        for (int j = 0; j < 8; j++) yv[j] = r.yv[j];
+#pragma unroll
+        for (int q = 0; q < NS; q++) {
+            const float hend = fmaf(r.P[q], hc[q], r.Hh[q]);    // state after sub-chunk s
             const float hprev = dpp_row_shr<1>(hend);
-            float h = s == 0 ? hc[q] : hprev;               // state entering sub-chunk s
-            hc[q] = __shfl(hend, ci * 8 + 7, 64);           // state after the chunk
+            float h = s == 0 ? hc[q] : hprev;                   // state entering sub-chunk s
+            hc[q] = __shfl(hend, ci * 8 + 7, 64);               // state after the chunk
 #pragma unroll
             for (int j = 0; j < 8; j++) {
-                h = fmaf(a[j][q], h, bu[j][q]);
-                yv[j] = fmaf(bcw[kCrossChunk * NS + (s * 8 + j) * NS + q], h, yv[j]);
+                h = fmaf(r.a[j][q], h, r.bu[j][q]);
+                yv[j] = fmaf(r.cc[j][q], h, yv[j]);
             }
         }
         float* st = stage + ((c & 1) * 4 + k) * kCrossStage + ci * 65 + s * 8;
@@ -332,20 +348,25 @@ __global__ __launch_bounds__(256) void cross_fused(CrossParams p) {
         *reinterpret_cast<float4*>(row + 4) = v1;
     };
 
-    // kCrossAhead chunks of loads in flight ahead of the one being computed.
-    // Iteration c computes chunk c and then adds chunk c - 1, whose outputs
-    // every wave staged before the last barrier: one barrier an iteration, and
-    // a wave's adds overlap its own and the other waves' computation.
-    CrossTile<TIn, NS> tiles[kCrossAhead + 1];
-    static_for<0, kCrossAhead>([&](auto I) __attribute__((always_inline)) { load_tile(tiles[decltype(I)::value], decltype(I)::value); });
-    for (int c0 = 0; c0 < nch; c0 += kCrossAhead + 1) {
-        static_for<0, kCrossAhead + 1>([&](auto I) __attribute__((always_inline)) {
+    // Iteration c: the loads of chunk c + 3, chunk c + 1's local(), chunk c's
+    // finish(), then the adds of chunk c - 1, whose outputs every wave staged
+    // before the last barrier: one barrier an iteration.  Loads run two
+    // iterations ahead of their use (a ring of three tiles).
+    static_assert(kCrossAhead == 2, "the loop below keeps three tiles");
+    CrossTile<TIn, NS> tiles[3];
+    load_tile(tiles[0], 0);
+    load_tile(tiles[1], 1);
+    load_tile(tiles[2], 2);
+    Local lc[2];
+    local(tiles[0], 0, lc[0]);
+    for (int c0 = 0; c0 < nch; c0 += 6) {
+        static_for<0, 6>([&](auto I) __attribute__((always_inline)) {
             constexpr int i = decltype(I)::value;
             const int c = c0 + i;
-            load_tile(tiles[(i + kCrossAhead) % (kCrossAhead + 1)], c + kCrossAhead);
             if (c < nch) {
-                if (c + 1 < nch || L % kCrossChunk == 0) process(tiles[i], c, std::false_type{});
-                else process(tiles[i], c, std::true_type{});
+                load_tile(tiles[i % 3], c + 3);
+                local(tiles[(i + 1) % 3], c + 1, lc[(i + 1) % 2]);
+                finish(lc[i % 2], c);
                 if (c > 0) add_chunk(c - 1, std::false_type{});
                 barrier_lds();
             }

@@ -502,7 +502,7 @@ int cross_fused_ns(int64_t n) { return n == 1 ? 1 : n == 2 ? 2 : n <= 4 ? 4 : 0;
 bool cross_one_pass_fits(int64_t L, int64_t d_in, int64_t n) {
     const int ns = cross_fused_ns(n);
     return ns > 0 && L < (int64_t(1) << 16) && ss::cross_lds_bytes(int(L), ns) <= kMaxLdsBytes &&
-           (L + (ss::kCrossAhead + 1) * ss::kCrossChunk) * d_in * 4 < (int64_t(1) << 31);
+           (L + (ss::kCrossAhead + 2) * ss::kCrossChunk) * d_in * 4 < (int64_t(1) << 31);
 }
 
 // The form a call runs: SS_CROSS_AUTO is the two-pass form, the faster of the
