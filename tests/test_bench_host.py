@@ -39,3 +39,19 @@ def test_conv_step_bytes():
     # fp32 weights (d_in x 4) and bias.
     assert bench.conv_bytes(256, 5120, 4, 2) == 2 * 256 * 5120 * (2 * 4 + 2) + 4 * (5120 * 4 + 5120)
     assert bench.conv_bytes(256, 5120, 4, 2) == 26_316_800
+
+
+def test_valu_probe_library_loads_and_validates():
+    """libss_probe.so (built beside libss_scan.so) exports the probe and rejects bad arguments before any launch."""
+    import ctypes
+    import os
+
+    path = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
+                        "selective_state_space_softplus_amd", "libss_probe.so")
+    lib = ctypes.CDLL(path)
+    f = lib.ss_probe_valu
+    f.restype = ctypes.c_int
+    f.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    buf = ctypes.c_void_p(16)
+    for mix, blocks, iters, out in ((4, 1, 1, buf), (-1, 1, 1, buf), (0, 0, 1, buf), (0, 1, 0, buf), (0, 1, 1, None)):
+        assert f(mix, blocks, iters, out, None) == -1, (mix, blocks, iters, out)
