@@ -163,3 +163,21 @@ def test_cross_is_deterministic(ss, n, dtype, form):
     for _ in range(3):
         y2, l2 = run_gpu(ss, c, form=form)
         assert torch.equal(y1, y2) and torch.equal(l1, l2)
+
+
+def test_cross_vmamba_workload_bf16_one_pass(ss):
+    """The scan-vmamba maps with bf16 inputs through the one-pass form, compared in full (the oracle sees the same
+    bf16 values; the output is fp32, so the fp32 bound holds)."""
+    say("cross scan at scan-vmamba size, bf16 inputs, one pass")
+    c = workloads.cross_scan_inputs(3)
+    for key in ("x", "delta", "B", "C"):
+        c[key] = c[key].to(BF16)
+    e1, e2 = check(ss, c, "scan-vmamba bf16", form="one_pass")
+    print(f"scan-vmamba bf16 one pass: y err {e1:.3g}, last_state err {e2:.3g}")
+
+
+@pytest.mark.parametrize("n,form", [(2, "one_pass"), (4, "one_pass"), (4, "auto")])
+def test_cross_mid_maps(ss, n, form):
+    """8 maps of 40 x 40 x 256 (25 chunks of 64 steps, none ragged) with n = 2 and 4."""
+    say(f"cross 8 maps 40x40x256 n={n} form={form}")
+    check(ss, cross_inputs(8, 40, 40, 256, n, F32, seed=77 + n), f"40x40 n={n}", form=form)
